@@ -1,0 +1,35 @@
+"""Float64 CPU oracle for the fused scaled-masked softmax and its backward.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path imports, calls or loads
+this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it. It shares no code with the HIP
+library (``attention_softmax_amd``) and never imports it.
+
+What it computes is the plain definition of the operation, evaluated in float64
+from the exact values of the typed inputs (every fp32, fp16 and bf16 value is
+exactly representable as a float64):
+
+* forward  -- lmnt.cn "Custom fused Softmax operator in CUDA, wrapped into
+  PyTorch", sec. 1.2 (score = x*scale + mask, softmax over keys) and sec. 2.1
+  (subtract the row maximum before exponentiating); the causal rule (key j > query
+  i is masked) from sec. 1.2, applied after the additive mask as in sec. 3.1;
+* backward -- the same page, sec. 3.3: dx_i = scale * y_i * (dy_i - sum_j dy_j*y_j);
+* fully-masked rows -- pnsm.cn article on a custom ScaledMaskSoftmax operator,
+  sec. 4.2 / 4.3: such a row must not divide 0 by 0; it returns all zeros.
+
+Every function here is pinned by tests in ``tests/test_oracle_pins.py``
+(closed forms, invariants, brute force, finite differences, the explicit
+Jacobian). Nothing in this package is "parity unpinned".
+"""
+
+from .softmax import (  # noqa: F401
+    DTYPES,
+    decode,
+    forward,
+    forward_row,
+    forward_rows,
+    backward,
+    backward_row,
+    backward_rows,
+    row_index,
+)

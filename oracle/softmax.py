@@ -1,0 +1,178 @@
+"""Plain float64 reference of y = softmax(x*scale + mask) and its backward.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring). Slow and obvious on
+purpose: one row at a time, the definition written out, no blocking or fusion.
+
+Conventions
+-----------
+* ``x`` has shape [B, H, Sq, Sk]; softmax runs over the last axis (keys).
+* Typed inputs are numpy arrays: ``float32`` for fp32, ``float16`` for fp16 and
+  ``uint16`` holding the raw bit patterns for bf16 (numpy has no bfloat16).
+  The ``dtype`` argument ("f32", "f16", "bf16") says which.
+* ``mask`` is ``None`` or a 4-D array whose every axis has the length of the
+  matching axis of ``x`` or length 1 (length 1 = broadcast over that axis).
+  It holds additive values (0 keeps, a large negative value or -inf masks),
+  in the same dtype as ``x`` -- lmnt.cn "Custom fused Softmax operator in CUDA,
+  wrapped into PyTorch", sec. 2.2 (additive mask) and sec. 4.2 (mask passed with
+  the input's element type).
+* ``scale`` is rounded to fp32 first, because the operation receives it as a
+  32-bit float (same page, sec. 4.2: the wrapper casts it to float).
+* Outputs are float64 arrays, unrounded.
+"""
+
+import math
+
+import numpy as np
+
+DTYPES = ("f32", "f16", "bf16")
+
+
+def decode(a, dtype):
+    """Exact float64 values of a typed array (bf16 given as uint16 bit patterns)."""
+    a = np.asarray(a)
+    if dtype == "f32":
+        if a.dtype != np.float32:
+            raise TypeError("f32 data must be a float32 array")
+        return a.astype(np.float64)
+    if dtype == "f16":
+        if a.dtype != np.float16:
+            raise TypeError("f16 data must be a float16 array")
+        return a.astype(np.float64)
+    if dtype == "bf16":
+        if a.dtype != np.uint16:
+            raise TypeError("bf16 data must be a uint16 array of bit patterns")
+        # A bf16 value is the upper half of an IEEE binary32 value.
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _fp32(v):
+    return float(np.float32(v))
+
+
+def _check_mask_shape(mask, shape):
+    if mask is None:
+        return
+    if mask.ndim != 4:
+        raise ValueError("mask must be 4-D with length-1 axes for broadcast")
+    for m, n in zip(mask.shape, shape):
+        if m not in (1, n):
+            raise ValueError(f"mask shape {mask.shape} does not broadcast to {shape}")
+
+
+def row_index(shape, r):
+    """Flat row number r -> (b, h, q) for x of shape [B, H, Sq, Sk]."""
+    B, H, Sq, _ = shape
+    if not 0 <= r < B * H * Sq:
+        raise IndexError(r)
+    q = r % Sq
+    h = (r // Sq) % H
+    b = r // (Sq * H)
+    return b, h, q
+
+
+def _mask_row(maskd, b, h, q):
+    # Broadcast axes have length 1: index 0 there.
+    mb = b if maskd.shape[0] > 1 else 0
+    mh = h if maskd.shape[1] > 1 else 0
+    mq = q if maskd.shape[2] > 1 else 0
+    return maskd[mb, mh, mq, :]
+
+
+def _forward_one_row(xrow, mrow, sc, causal, q):
+    """Softmax of one row of scores, in float64."""
+    n = xrow.shape[0]
+    # score_k = x_k*scale + mask_k
+    s = xrow * sc
+    if mrow is not None:
+        s = s + mrow
+    # Causal: keys after the query position are masked, after the additive mask.
+    if causal:
+        s = s.copy()
+        s[np.arange(n) > q] = -math.inf
+    m = s.max() if n else -math.inf
+    if m == -math.inf:
+        # Every key is masked: the row is all zeros (nothing to normalise).
+        return np.zeros(n, dtype=np.float64)
+    e = np.exp(s - m)  # exp(-inf) is exactly 0
+    z = e.sum()
+    return e / z
+
+
+def forward_row(xrow, dtype, mrow=None, scale=1.0, is_causal=False, q=0):
+    """Forward of one typed row of x (length Sk) with its typed mask row or None.
+
+    ``q`` is the row's query position; it matters only when ``is_causal``.
+    """
+    xd = decode(np.asarray(xrow), dtype)
+    md = decode(np.asarray(mrow), dtype) if mrow is not None else None
+    if xd.ndim != 1 or (md is not None and md.shape != xd.shape):
+        raise ValueError("rows must be 1-D and of one length")
+    return _forward_one_row(xd, md, _fp32(scale), bool(is_causal), int(q))
+
+
+def forward_rows(x, dtype, rows, mask=None, scale=1.0, is_causal=False):
+    """Forward on a list of flat row numbers; returns float64 [len(rows), Sk]."""
+    x = np.asarray(x)
+    if x.ndim != 4:
+        raise ValueError("x must be 4-D [B, H, Sq, Sk]")
+    _check_mask_shape(mask, x.shape)
+    xd_all = x  # decoded per row to keep memory bounded at large sizes
+    maskd = decode(mask, dtype) if mask is not None else None
+    sc = _fp32(scale)
+    out = np.empty((len(rows), x.shape[3]), dtype=np.float64)
+    for i, r in enumerate(rows):
+        b, h, q = row_index(x.shape, int(r))
+        xrow = decode(xd_all[b, h, q, :], dtype)
+        mrow = _mask_row(maskd, b, h, q) if maskd is not None else None
+        out[i] = _forward_one_row(xrow, mrow, sc, bool(is_causal), q)
+    return out
+
+
+def forward(x, dtype, mask=None, scale=1.0, is_causal=False):
+    """Forward over the whole tensor; returns float64 of x's shape."""
+    x = np.asarray(x)
+    B, H, Sq, Sk = x.shape
+    rows = range(B * H * Sq)
+    return forward_rows(x, dtype, rows, mask, scale, is_causal).reshape(B, H, Sq, Sk)
+
+
+def _backward_one_row(yrow, dyrow, sc):
+    # dot = sum_j dy_j * y_j ; dx_i = scale * y_i * (dy_i - dot)
+    dot = float(np.dot(dyrow, yrow))
+    return sc * yrow * (dyrow - dot)
+
+
+def backward_row(yrow, dyrow, dtype, scale=1.0):
+    """Backward of one typed row (y and dy of length Sk)."""
+    yd = decode(np.asarray(yrow), dtype)
+    dyd = decode(np.asarray(dyrow), dtype)
+    if yd.ndim != 1 or yd.shape != dyd.shape:
+        raise ValueError("rows must be 1-D and of one length")
+    return _backward_one_row(yd, dyd, _fp32(scale))
+
+
+def backward_rows(y, dy, dtype, rows, scale=1.0):
+    """Backward on a list of flat row numbers; returns float64 [len(rows), Sk].
+
+    ``y`` is the typed forward output the backward receives and ``dy`` the typed
+    upstream gradient; neither the mask nor the causal flag enters the formula.
+    """
+    y = np.asarray(y)
+    dy = np.asarray(dy)
+    if y.shape != dy.shape or y.ndim != 4:
+        raise ValueError("y and dy must be 4-D and of one shape")
+    sc = _fp32(scale)
+    out = np.empty((len(rows), y.shape[3]), dtype=np.float64)
+    for i, r in enumerate(rows):
+        b, h, q = row_index(y.shape, int(r))
+        out[i] = _backward_one_row(decode(y[b, h, q, :], dtype),
+                                   decode(dy[b, h, q, :], dtype), sc)
+    return out
+
+
+def backward(y, dy, dtype, scale=1.0):
+    """Backward over the whole tensor; returns float64 of y's shape."""
+    y = np.asarray(y)
+    B, H, Sq, Sk = y.shape
+    return backward_rows(y, dy, dtype, range(B * H * Sq), scale).reshape(B, H, Sq, Sk)

@@ -1,0 +1,327 @@
+"""Checks that pin the float64 oracle to facts outside itself.
+
+Each check raises AssertionError when the oracle disagrees with a closed form,
+an invariant of the definition, a library routine on a special case, a brute
+force second formulation, finite differences or the explicit Jacobian. The
+checks call the oracle through ``oracle.softmax`` attributes at call time, so
+``tests/test_oracle_pins.py`` can also run them against deliberately broken
+copies of the oracle (planted on the CPU) and require that each is caught.
+
+Sources of the facts: the operation's definition -- lmnt.cn "Custom fused
+Softmax operator in CUDA, wrapped into PyTorch", sec. 1.2 (score = x*scale +
+mask, softmax over keys; causal masks key j > query i), sec. 2.1 (max
+subtraction leaves the result unchanged), sec. 3.3 (backward formula and its
+Jacobian derivation); pnsm.cn ScaledMaskSoftmax article sec. 4.2/4.3 (a fully
+masked row must not produce NaN; zeros chosen).
+"""
+
+import itertools
+import math
+
+import numpy as np
+
+import oracle.softmax as S
+
+F32, F16 = np.float32, np.float16
+NINF = -math.inf
+
+
+def _close(got, want, atol=0.0, rtol=1e-15, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    with np.errstate(invalid="ignore"):
+        ok = (np.abs(got - want) <= atol + rtol * np.abs(want)) | (got == want)
+    bad = ~ok  # NaN anywhere counts as a mismatch
+    assert not bad.any(), f"{what}: got {got[bad][:4]} want {want[bad][:4]}"
+
+
+def _logistic(a):
+    """1 / (1 + e^-a), written so it never overflows."""
+    if a >= 0:
+        return 1.0 / (1.0 + math.exp(-a))
+    ea = math.exp(a)
+    return ea / (1.0 + ea)
+
+
+# ---------------------------------------------------------------- forward pins
+
+def pin_two_element_closed_form():
+    """softmax([s0, s1]) = [logistic(s0-s1), logistic(s1-s0)] for any s0, s1."""
+    vals = [-30.0, -7.25, -1.0, 0.0, 0.5, 3.0, 12.0, 40.0]
+    for s0, s1 in itertools.product(vals, vals):
+        y = S.forward_row(np.array([s0, s1], F32), "f32")
+        _close(y, [_logistic(s0 - s1), _logistic(s1 - s0)], rtol=4e-16, what="two-element")
+    # Large, equal-ish scores: the naive exp(1000) overflows; the definition does not.
+    y = S.forward_row(np.array([1000.0, 1001.0], F32), "f32")
+    _close(y, [1.0 / (1.0 + math.e), math.e / (1.0 + math.e)], rtol=4e-16, what="[1000,1001]")
+
+
+def pin_hand_rows():
+    """Rows worked by hand from the definition."""
+    # [0, ln 3] -> [1/4, 3/4] up to the fp32 rounding of ln 3
+    l3 = float(F32(math.log(3.0)))
+    y = S.forward_row(np.array([0.0, l3], F32), "f32")
+    _close(y, [1 / (1 + math.exp(l3)), math.exp(l3) / (1 + math.exp(l3))], rtol=4e-16)
+    _close(y, [0.25, 0.75], rtol=2e-7, what="[0, ln3]")
+    # constant row -> uniform, exactly
+    for n in (1, 2, 3, 4, 7, 64, 1000):
+        y = S.forward_row(np.full(n, 0.75, F32), "f32")
+        _close(y, np.full(n, 1.0 / n), rtol=1e-15, what=f"uniform n={n}")
+    # geometric row: s = [0.375, 0.125, -0.125] after scale 1/8; ratios r = e^0.25
+    y = S.forward_row(np.array([3.0, 1.0, -1.0], F32), "f32", scale=0.125)
+    r = math.exp(0.25)
+    z = r * r + r + 1.0
+    _close(y, [r * r / z, r / z, 1.0 / z], rtol=4e-16, what="geometric")
+    # additive -inf mask entry is exactly 0 and the rest renormalise
+    y = S.forward_row(np.array([2.0, 2.0, 5.0], F32), "f32", mrow=np.array([0, 0, NINF], F32))
+    assert y.tolist() == [0.5, 0.5, 0.0], y
+    # causal, query q=1: keys 2, 3 are masked (key j > query i), key 1 is kept
+    y = S.forward_row(np.array([1.0, 2.0, 3.0, 4.0], F32), "f32", scale=0.5, is_causal=True, q=1)
+    _close(y[:2], [_logistic(-0.5), _logistic(0.5)], rtol=4e-16, what="causal q=1")
+    assert y[2] == 0.0 and y[3] == 0.0
+    # causal q=0: only key 0 survives, its probability is exactly 1
+    y = S.forward_row(np.array([9.0, -3.0, 1.0], F32), "f32", is_causal=True, q=0)
+    assert y.tolist() == [1.0, 0.0, 0.0], y
+    # fp16 row whose small probability is an fp16 subnormal: [0, -12]
+    y = S.forward_row(np.array([0.0, -12.0], F16), "f16")
+    _close(y, [_logistic(12.0), _logistic(-12.0)], rtol=4e-16, what="[0,-12]")
+
+
+def pin_fully_masked_rows():
+    """All keys masked (by the additive mask, by causality or both): all zeros."""
+    n = 5
+    y = S.forward_row(np.arange(n, dtype=F32), "f32", mrow=np.full(n, NINF, F32))
+    assert y.tolist() == [0.0] * n and not np.isnan(y).any()
+    m = np.zeros(n, F32)
+    m[0] = NINF
+    y = S.forward_row(np.arange(n, dtype=F32), "f32", mrow=m, is_causal=True, q=0)
+    assert y.tolist() == [0.0] * n
+    # one surviving key gets probability exactly 1
+    m = np.full(n, NINF, F32)
+    m[3] = 0.0
+    y = S.forward_row(np.arange(n, dtype=F32), "f32", mrow=m)
+    assert y.tolist() == [0.0, 0.0, 0.0, 1.0, 0.0]
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def pin_invariants():
+    """Sum to one; masked entries exactly zero; shift invariance; permutation."""
+    rng = _rng(7)
+    for trial in range(40):
+        n = int(rng.integers(1, 300))
+        x = (rng.standard_normal(n) * 4).astype(F32)
+        m = np.where(rng.random(n) < 0.3, NINF, 0.0).astype(F32)
+        q = int(rng.integers(0, n))
+        causal = bool(trial % 2)
+        y = S.forward_row(x, "f32", mrow=m, scale=0.3, is_causal=causal, q=q)
+        dead = np.isinf(m) | ((np.arange(n) > q) if causal else False)
+        assert (y[dead] == 0.0).all()
+        if not dead.all():
+            assert abs(math.fsum(y) - 1.0) < 1e-14
+            assert (y[~dead] > 0).all()
+        # shift: x + c with c a multiple of 2^-4 and |x| < 2^8 is exact in fp32
+        xq = np.round(x * 16) / 16
+        c = float(rng.integers(-64, 64)) / 16.0
+        y0 = S.forward_row(xq.astype(F32), "f32", mrow=m, scale=1.0, is_causal=causal, q=q)
+        y1 = S.forward_row((xq + c).astype(F32), "f32", mrow=m, scale=1.0, is_causal=causal, q=q)
+        _close(y1, y0, atol=1e-15, rtol=1e-13, what="shift")
+        # key permutation (no causal): output permutes with the input
+        p = rng.permutation(n)
+        ya = S.forward_row(x, "f32", mrow=m, scale=0.3)
+        yb = S.forward_row(x[p], "f32", mrow=m[p], scale=0.3)
+        _close(yb, ya[p], atol=1e-17, rtol=1e-14, what="permutation")
+    # scale 0 -> uniform over the unmasked keys
+    x = (rng.standard_normal(50) * 9).astype(F32)
+    m = np.where(np.arange(50) % 3 == 0, NINF, 0.0).astype(F32)
+    y = S.forward_row(x, "f32", mrow=m, scale=0.0)
+    keep = ~np.isinf(m)
+    _close(y[keep], np.full(keep.sum(), 1.0 / keep.sum()), rtol=1e-15, what="scale 0")
+    # monotone: a larger score never gets a smaller probability
+    x = (rng.standard_normal(200) * 3).astype(F32)
+    y = S.forward_row(x, "f32", scale=0.7)
+    o = np.argsort(x, kind="stable")
+    assert (np.diff(y[o]) >= 0).all()
+
+
+def pin_library_special_case():
+    """No mask, no causal, scale 1: the library softmax in float64."""
+    import scipy.special
+    import torch
+    rng = _rng(11)
+    x = (rng.standard_normal((2, 3, 5, 37)) * 3).astype(F32)
+    y = S.forward(x, "f32")
+    _close(y, scipy.special.softmax(x.astype(np.float64), axis=-1), atol=1e-17, rtol=1e-14,
+           what="scipy")
+    t = torch.softmax(torch.from_numpy(x.astype(np.float64)), dim=-1).numpy()
+    _close(y, t, atol=1e-17, rtol=1e-14, what="torch")
+
+
+def _brute_row(svals):
+    """Second formulation: exp(s_k) / sum_j exp(s_j) without the max shift,
+    with math.fsum, on small scores only; masked keys are None."""
+    keep = [v for v in svals if v is not None]
+    if not keep:
+        return [0.0] * len(svals)
+    z = math.fsum(math.exp(v) for v in keep)
+    return [0.0 if v is None else math.exp(v) / z for v in svals]
+
+
+def pin_brute_force_exhaustive():
+    """All 2^n mask patterns x causal x query position, n <= 6, on an exact grid."""
+    rng = _rng(3)
+    for n in range(1, 7):
+        x = (rng.integers(-16, 17, n) * 0.25).astype(F32)  # exact grid in [-4, 4]
+        for bits in range(1 << n):
+            m = np.array([NINF if (bits >> k) & 1 else 0.0 for k in range(n)], F32)
+            for causal in (False, True):
+                for q in (range(n) if causal else [0]):
+                    y = S.forward_row(x, "f32", mrow=m, scale=0.5, is_causal=causal, q=q)
+                    s = [None if (np.isinf(m[k]) or (causal and k > q)) else 0.5 * float(x[k])
+                         for k in range(n)]
+                    _close(y, _brute_row(s), atol=1e-17, rtol=1e-14, what=f"brute n={n}")
+
+
+def _mask_index(mode, b, h, q):
+    return {"sq_sk": (0, 0, q), "b_sq_sk": (b, 0, q), "b_1_sk": (b, 0, 0),
+            "full": (b, h, q)}[mode]
+
+
+def pin_tensor_indexing():
+    """Whole-tensor forward against an explicit per-(b,h,q) loop for every
+    broadcast mode, with a mask that differs along every axis it has."""
+    rng = _rng(5)
+    B, H, Sq, Sk = 2, 3, 4, 6
+    x = (rng.integers(-12, 13, (B, H, Sq, Sk)) * 0.25).astype(F32)
+    shapes4 = {"sq_sk": (1, 1, Sq, Sk), "b_sq_sk": (B, 1, Sq, Sk), "b_1_sk": (B, 1, 1, Sk),
+               "full": (B, H, Sq, Sk)}
+    for mode, ms in shapes4.items():
+        mask = (rng.integers(-8, 9, ms) * 0.5).astype(F32)
+        mask[rng.random(ms) < 0.2] = NINF
+        for causal in (False, True):
+            y = S.forward(x, "f32", mask=mask, scale=0.75, is_causal=causal)
+            for b, h, q in itertools.product(range(B), range(H), range(Sq)):
+                mb, mh, mq = _mask_index(mode, b, h, q)
+                s = []
+                for k in range(Sk):
+                    mv = float(mask[mb, mh, mq, k])
+                    dead = math.isinf(mv) or (causal and k > q)
+                    s.append(None if dead else 0.75 * float(x[b, h, q, k]) + mv)
+                _close(y[b, h, q], _brute_row(s), atol=1e-17, rtol=1e-14,
+                       what=f"indexing {mode} causal={causal} ({b},{h},{q})")
+            # the row-subset entry point agrees with the whole-tensor one
+            rows = [0, B * H * Sq - 1, 5]
+            yr = S.forward_rows(x, "f32", rows, mask=mask, scale=0.75, is_causal=causal)
+            for i, r in enumerate(rows):
+                b, h, q = S.row_index(x.shape, r)
+                assert (yr[i] == y[b, h, q]).all()
+
+
+def pin_decode():
+    """Exact decoding of typed inputs, from the formats' definitions."""
+    bf = np.array([0x3F80, 0xC000, 0x3FC0, 0x0001, 0x8000, 0x7F80, 0xFF80, 0x4049, 0x0080],
+                  np.uint16)
+    want = [1.0, -2.0, 1.5, 2.0 ** -133, -0.0, math.inf, -math.inf,
+            3.140625, 2.0 ** -126]
+    got = S.decode(bf, "bf16")
+    assert got.tolist() == want, got
+    h = np.array([1.0, 2.0 ** -24, 65504.0, -0.5], F16)
+    assert S.decode(h, "f16").tolist() == [1.0, 2.0 ** -24, 65504.0, -0.5]
+    # the bf16 and fp32 paths of the oracle agree on bf16-representable rows
+    v = np.array([0.5, -1.25, 3.0, 0.0], F32)
+    bits = (v.view(np.uint32) >> 16).astype(np.uint16)
+    _close(S.forward_row(bits, "bf16", scale=0.9), S.forward_row(v, "f32", scale=0.9),
+           rtol=0, what="bf16 vs f32")
+
+
+def pin_scale_rounding():
+    """scale enters as the fp32 value nearest to it."""
+    s = 1.0 / math.sqrt(128.0)
+    y = S.forward_row(np.array([0.0, 1.0], F32), "f32", scale=s)
+    _close(y, [_logistic(-float(F32(s))), _logistic(float(F32(s)))], rtol=4e-16)
+
+
+# --------------------------------------------------------------- backward pins
+
+def _fd_grad(x, m, sc, causal, q, dy, h=1e-6):
+    """Central differences of L(x) = sum_k dy_k * y_k(x) on the float64 forward core."""
+    g = np.zeros_like(x)
+    for j in range(x.size):
+        hp = h * max(1.0, abs(x[j]))
+        xp = x.copy()
+        xm = x.copy()
+        xp[j] += hp
+        xm[j] -= hp
+        lp = float(np.dot(dy, S._forward_one_row(xp, m, sc, causal, q)))
+        lm = float(np.dot(dy, S._forward_one_row(xm, m, sc, causal, q)))
+        g[j] = (lp - lm) / (2 * hp)
+    return g
+
+
+def pin_backward_finite_differences():
+    rng = _rng(13)
+    for trial in range(24):
+        n = int(rng.integers(1, 17))
+        x = rng.standard_normal(n) * 2.0
+        m = np.where(rng.random(n) < 0.25, NINF, 0.0)
+        causal = bool(trial % 3 == 0)
+        q = int(rng.integers(0, n))
+        sc = float(F32([0.125, 0.5, 1.0, 2.5][trial % 4]))
+        dy = rng.standard_normal(n)
+        y = S._forward_one_row(x, m, sc, causal, q)
+        dx = S._backward_one_row(y, dy, sc)
+        fd = _fd_grad(x, m, sc, causal, q, dy)
+        _close(dx, fd, atol=2e-8, rtol=1e-6, what=f"FD trial {trial}")
+
+
+def pin_backward_jacobian():
+    """dx = scale * J^T dy with J = diag(y) - y y^T (the softmax Jacobian)."""
+    rng = _rng(17)
+    for n in (1, 2, 3, 8, 16):
+        x = (rng.standard_normal(n) * 3).astype(F32)
+        y = S.forward_row(x, "f32", scale=0.5).astype(F32)   # a typed y, as the op receives
+        dy = rng.standard_normal(n).astype(F32)
+        yd, dyd = y.astype(np.float64), dy.astype(np.float64)
+        J = np.diag(yd) - np.outer(yd, yd)
+        _close(S.backward_row(y, dy, "f32", scale=0.5), 0.5 * (J.T @ dyd), atol=1e-16,
+               rtol=1e-12, what=f"Jacobian n={n}")
+    # worked example: y = softmax([1,2,3]), dy = e_0, scale 1/2
+    y = S._forward_one_row(np.array([1.0, 2.0, 3.0]), None, 1.0, False, 0)
+    dx = S._backward_one_row(y, np.array([1.0, 0.0, 0.0]), 0.5)
+    want = [0.5 * y[0] * (1 - y[0]), -0.5 * y[0] * y[1], -0.5 * y[0] * y[2]]
+    _close(dx, want, rtol=1e-15, what="worked Jacobian")
+
+
+def pin_backward_invariants():
+    rng = _rng(19)
+    for trial in range(20):
+        n = int(rng.integers(2, 200))
+        x = rng.standard_normal(n) * 2
+        m = np.where(rng.random(n) < 0.3, NINF, 0.0)
+        m[int(rng.integers(0, n))] = 0.0
+        sc = 0.25 + trial * 0.1
+        y = S._forward_one_row(x, m, sc, False, 0)
+        dy = rng.standard_normal(n)
+        dx = S._backward_one_row(y, dy, sc)
+        assert abs(math.fsum(dx)) < 1e-14 * max(1.0, np.abs(dy).max())   # sum dx = 0
+        assert (dx[y == 0.0] == 0.0).all()                               # masked -> 0
+        dc = S._backward_one_row(y, np.full(n, 1.7), sc)                  # constant dy -> 0
+        assert np.abs(dc).max() < 1e-15
+        dyy = S._backward_one_row(y, y, sc)                               # dy = y
+        _close(dyy, sc * y * (y - float(np.dot(y, y))), atol=1e-18, rtol=1e-12)
+    # typed wrapper decodes y and dy before the formula
+    y = np.array([0.25, 0.75], F16)
+    dy = np.array([1.0, -1.0], F16)
+    _close(S.backward_row(y, dy, "f16", scale=2.0), [2 * 0.25 * (1 - (-0.5)),
+                                                     2 * 0.75 * (-1 - (-0.5))], rtol=0)
+
+
+FORWARD_PINS = [pin_two_element_closed_form, pin_hand_rows, pin_fully_masked_rows,
+                pin_invariants, pin_library_special_case, pin_brute_force_exhaustive,
+                pin_tensor_indexing, pin_decode, pin_scale_rounding]
+BACKWARD_PINS = [pin_backward_finite_differences, pin_backward_jacobian,
+                 pin_backward_invariants]
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS

@@ -1,0 +1,140 @@
+"""The float64 oracle against its pins (CPU only), and planted mistakes.
+
+The second half plants plausible mistakes in a copy of the oracle (on the CPU,
+through monkeypatch) and requires that at least one pin fails for each: that
+is the evidence that the pins constrain every step of the oracle.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle.softmax as S
+from tests import oracle_pins as P
+
+
+@pytest.mark.parametrize("pin", P.ALL_PINS, ids=lambda f: f.__name__)
+def test_oracle_pin(pin):
+    pin()
+
+
+# ----------------------------------------------------------- planted mistakes
+
+_orig_fwd = S._forward_one_row
+_orig_bwd = S._backward_one_row
+_orig_decode = S.decode
+_orig_mask_row = S._mask_row
+_orig_row_index = S.row_index
+
+
+def _fwd_generic(xrow, mrow, sc, causal, q, *, use_scale=True, causal_ge=False,
+                 mask_scaled=False, shift=True, full_mask="zeros", causal_first_only=False):
+    n = xrow.shape[0]
+    s = xrow * (sc if use_scale else 1.0)
+    if mrow is not None:
+        s = s + (mrow * sc if mask_scaled else mrow)
+    if causal:
+        s = s.copy()
+        k = np.arange(n)
+        s[(k >= q) if causal_ge else (k > q)] = -math.inf
+        if causal_first_only:
+            s[k > q + 1] = -math.inf
+    m = s.max() if n else -math.inf
+    if m == -math.inf:
+        if full_mask == "zeros":
+            return np.zeros(n)
+        if full_mask == "uniform":
+            return np.full(n, 1.0 / n)
+        with np.errstate(invalid="ignore"):
+            e = np.exp(s - m)
+            return e / e.sum()
+    with np.errstate(over="ignore", invalid="ignore"):
+        e = np.exp(s - m) if shift else np.exp(s)
+        return e / e.sum()
+
+
+def _bwd_generic(y, dy, sc, *, use_scale=True, sign=1.0, use_dot=True, dot_sq=False):
+    dot = float(np.dot(dy, y)) if use_dot else 0.0
+    if dot_sq:
+        dot = float(np.dot(y, y))
+    return (sc if use_scale else 1.0) * y * (dy - sign * dot)
+
+
+FWD_MUTANTS = {
+    "scale dropped": dict(use_scale=False),
+    "causal masks the diagonal too": dict(causal_ge=True),
+    "causal mask one key late": dict(causal_first_only=False, causal_ge=False) | {"_late": True},
+    "mask multiplied by scale": dict(mask_scaled=True),
+    "no max subtraction": dict(shift=False),
+    "fully masked row uniform": dict(full_mask="uniform"),
+    "fully masked row NaN": dict(full_mask="nan"),
+}
+
+BWD_MUTANTS = {
+    "backward scale dropped": dict(use_scale=False),
+    "backward sign of dot flipped": dict(sign=-1.0),
+    "backward dot dropped": dict(use_dot=False),
+    "backward uses sum y^2": dict(dot_sq=True),
+}
+
+
+def _late_causal(xrow, mrow, sc, causal, q):
+    # keys up to q+1 kept (off by one in the other direction)
+    return _orig_fwd(xrow, mrow, sc, causal, q + 1 if causal else q)
+
+
+def _run_all_pins():
+    failures = []
+    for pin in P.ALL_PINS:
+        try:
+            pin()
+        except AssertionError as e:
+            failures.append((pin.__name__, str(e)[:80]))
+        except (FloatingPointError, ValueError, IndexError) as e:
+            failures.append((pin.__name__, repr(e)[:80]))
+    return failures
+
+
+@pytest.mark.parametrize("name", sorted(FWD_MUTANTS))
+def test_planted_forward_mistake_is_caught(name, monkeypatch):
+    kw = dict(FWD_MUTANTS[name])
+    if kw.pop("_late", False):
+        monkeypatch.setattr(S, "_forward_one_row", _late_causal)
+    else:
+        monkeypatch.setattr(S, "_forward_one_row",
+                            lambda xr, mr, sc, c, q: _fwd_generic(xr, mr, sc, c, q, **kw))
+    assert _run_all_pins(), f"planted mistake '{name}' passed every pin"
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_planted_backward_mistake_is_caught(name, monkeypatch):
+    kw = BWD_MUTANTS[name]
+    monkeypatch.setattr(S, "_backward_one_row", lambda y, dy, sc: _bwd_generic(y, dy, sc, **kw))
+    assert _run_all_pins(), f"planted mistake '{name}' passed every pin"
+
+
+def test_planted_indexing_mistakes_are_caught(monkeypatch):
+    # mask broadcast taken along heads instead of batches
+    def mask_row_h(maskd, b, h, q):
+        return _orig_mask_row(maskd, h % maskd.shape[0], b % max(maskd.shape[1], 1), q)
+    monkeypatch.setattr(S, "_mask_row", mask_row_h)
+    assert _run_all_pins()
+    monkeypatch.setattr(S, "_mask_row", _orig_mask_row)
+
+    # row order (b, q, h) instead of (b, h, q)
+    def row_index_swapped(shape, r):
+        B, H, Sq, _ = shape
+        return r // (Sq * H), r % H, (r // H) % Sq
+    monkeypatch.setattr(S, "row_index", row_index_swapped)
+    assert _run_all_pins()
+
+
+def test_planted_decode_mistake_is_caught(monkeypatch):
+    def decode_bad(a, dtype):
+        if dtype == "bf16":
+            a = np.asarray(a)
+            return (a.astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
+        return _orig_decode(a, dtype)
+    monkeypatch.setattr(S, "decode", decode_bad)
+    assert _run_all_pins()
