@@ -1,0 +1,607 @@
+// kernels.hpp -- HIP kernels of the fused scaled-masked softmax for gfx950.
+//
+// Forward, per row (b, h, q) of x[B,H,Sq,Sk]: s_k = x_k*scale + mask_k, keys
+// k > q masked when causal, y_k = exp(s_k - max s) / sum exp(s - max s)
+// (lmnt.cn "Custom fused Softmax operator in CUDA, wrapped into PyTorch",
+// sec. 1.2 and 2.1; causal after the additive mask as in sec. 3.1). A fully
+// masked row is written as zeros (pnsm.cn ScaledMaskSoftmax article, sec. 4.3).
+// Backward: dx_k = scale * y_k * (dy_k - sum_j dy_j y_j) (lmnt.cn page, sec. 3.3).
+//
+// Mapping. A row is owned by TPR consecutive lanes. TPR <= 64 packs 64/TPR rows
+// into each wavefront (four wavefronts per 256-thread workgroup); TPR >= 128
+// gives one row to a workgroup of TPR/64 wavefronts. Each lane holds NV 16-byte
+// vectors of the row in VGPRs: vector v = j*TPR + lane (j < NV), so one wave
+// instruction moves TPR*16 contiguous bytes. The row is read from HBM once,
+// reduced in registers and written once; exponentials are computed once per
+// element and kept in the same registers.
+//
+// Reductions. Within a wavefront: DPP quad_perm / row_half_mirror / row_mirror
+// steps reduce 4, 8 and 16 lanes, then the gfx950 lane-swap instructions
+// v_permlane16_swap and v_permlane32_swap combine rows of 16 and halves of 32.
+// No LDS traffic and no barrier. Across the wavefronts of a workgroup: one LDS
+// slot per wavefront and one barrier per reduction (max and sum use distinct
+// slots, so the forward takes exactly two barriers).
+//
+// Alignment. Vector v covers the row's elements [v*E - a, v*E - a + E), where a
+// is the row start's element offset inside its 16-byte line, so full vectors
+// are 16-byte aligned in the input. The first and last vectors of a row may be
+// partial: those elements are read and written one at a time. An operand whose
+// row has a different offset than the input's uses element accesses.
+//
+// Causal rows read keys 0..q only; later vectors are neither loaded nor
+// exponentiated, and are stored as zeros.
+
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define SMS_DEV __device__ __forceinline__
+
+namespace sms {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_inff();
+
+// ----------------------------------------------------------------- formats
+
+struct Fp32 {
+  static constexpr int kBytes = 4;
+  static constexpr int kE = 4;  // elements per 16-byte vector
+  SMS_DEV static void unpack(const uint4& u, float (&f)[kE]) {
+    f[0] = __uint_as_float(u.x);
+    f[1] = __uint_as_float(u.y);
+    f[2] = __uint_as_float(u.z);
+    f[3] = __uint_as_float(u.w);
+  }
+  SMS_DEV static uint4 pack(const float (&f)[kE]) {
+    return uint4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                 __float_as_uint(f[3])};
+  }
+  SMS_DEV static float ld(const char* p) { return *reinterpret_cast<const float*>(p); }
+  SMS_DEV static void st(char* p, float v) { *reinterpret_cast<float*>(p) = v; }
+  // Outputs are fp32: a flushed subnormal exponential is below any fp32
+  // tolerance, so the bare hardware exp2 serves.
+  SMS_DEV static float exp2(float t) { return __builtin_amdgcn_exp2f(t); }
+  // fp32 products are not exact in fp32: widen before multiplying.
+  SMS_DEV static double prod(float a, float b) { return (double)a * (double)b; }
+};
+
+struct Fp16 {
+  static constexpr int kBytes = 2;
+  static constexpr int kE = 8;
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  SMS_DEV static void unpack(const uint4& u, float (&f)[kE]) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const h2 h = __builtin_bit_cast(h2, w[i]);
+      f[2 * i] = (float)h.x;
+      f[2 * i + 1] = (float)h.y;
+    }
+  }
+  SMS_DEV static uint4 pack(const float (&f)[kE]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h2 h;
+      h.x = (_Float16)f[2 * i];  // round to nearest even, subnormals kept
+      h.y = (_Float16)f[2 * i + 1];
+      w[i] = __builtin_bit_cast(uint32_t, h);
+    }
+    return uint4{w[0], w[1], w[2], w[3]};
+  }
+  SMS_DEV static float ld(const char* p) { return (float)*reinterpret_cast<const _Float16*>(p); }
+  SMS_DEV static void st(char* p, float v) { *reinterpret_cast<_Float16*>(p) = (_Float16)v; }
+  // The smallest fp16 subnormal (2^-24) is a normal fp32 number: bare exp2.
+  SMS_DEV static float exp2(float t) { return __builtin_amdgcn_exp2f(t); }
+  // Product of two fp16 values (11-bit significands) is exact in fp32.
+  SMS_DEV static double prod(float a, float b) { return (double)(a * b); }
+};
+
+struct Bf16 {
+  static constexpr int kBytes = 2;
+  static constexpr int kE = 8;
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  SMS_DEV static void unpack(const uint4& u, float (&f)[kE]) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  SMS_DEV static uint4 pack(const float (&f)[kE]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      b2 b;
+      b.x = (__bf16)f[2 * i];  // v_cvt_pk_bf16_f32: round to nearest even
+      b.y = (__bf16)f[2 * i + 1];
+      w[i] = __builtin_bit_cast(uint32_t, b);
+    }
+    return uint4{w[0], w[1], w[2], w[3]};
+  }
+  SMS_DEV static float ld(const char* p) {
+    return __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t*>(p)) << 16);
+  }
+  SMS_DEV static void st(char* p, float v) { *reinterpret_cast<__bf16*>(p) = (__bf16)v; }
+  // bf16 shares fp32's exponent range, so bf16 outputs can be fp32 subnormals:
+  // use the library exp2f, which keeps subnormal results.
+  SMS_DEV static float exp2(float t) { return exp2f(t); }
+  SMS_DEV static double prod(float a, float b) { return (double)(a * b); }  // exact
+};
+
+// ------------------------------------------------------ wavefront reductions
+
+template <int CTRL>
+SMS_DEV float dpp(float v) {
+  const int i = __float_as_int(v);
+  return __int_as_float(__builtin_amdgcn_update_dpp(i, i, CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+SMS_DEV double dpp(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
+  const uint32_t lo2 = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xF, 0xF, false);
+  const uint32_t hi2 = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi2 << 32) | lo2);
+}
+
+// The pair of values a lane sees after exchanging rows of 16 lanes (SWAP32 =
+// false) or halves of 32 lanes (true) with itself: its own and its partner's.
+template <bool SWAP32>
+SMS_DEV void swap_pair(float v, float& a, float& b) {
+  const uint32_t u = __float_as_uint(v);
+  if constexpr (SWAP32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  }
+}
+
+template <bool SWAP32>
+SMS_DEV void swap_pair(double v, double& a, double& b) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+  uint32_t lo_a, lo_b, hi_a, hi_b;
+  if constexpr (SWAP32) {
+    const auto rl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto rh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    lo_a = rl[0]; lo_b = rl[1]; hi_a = rh[0]; hi_b = rh[1];
+  } else {
+    const auto rl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto rh = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    lo_a = rl[0]; lo_b = rl[1]; hi_a = rh[0]; hi_b = rh[1];
+  }
+  a = __builtin_bit_cast(double, ((uint64_t)hi_a << 32) | lo_a);
+  b = __builtin_bit_cast(double, ((uint64_t)hi_b << 32) | lo_b);
+}
+
+struct OpMax {
+  SMS_DEV float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct OpAdd {
+  template <class T>
+  SMS_DEV T operator()(T a, T b) const { return a + b; }
+};
+
+// All-reduce over aligned groups of G lanes (G a power of two, <= 64); every
+// lane of a group ends with the group's result. Fixed order: deterministic.
+template <int G, class T, class Op>
+SMS_DEV T group_reduce(T v, Op op) {
+  if constexpr (G > 1) v = op(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]: lane ^ 1
+  if constexpr (G > 2) v = op(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (G > 4) v = op(v, dpp<0x141>(v));  // row_half_mirror: other quad of 8
+  if constexpr (G > 8) v = op(v, dpp<0x140>(v));  // row_mirror: other half of 16
+  if constexpr (G > 16) {
+    T a, b;
+    swap_pair<false>(v, a, b);  // rows 0<->1 and 2<->3
+    v = op(a, b);
+  }
+  if constexpr (G > 32) {
+    T a, b;
+    swap_pair<true>(v, a, b);   // lanes 0-31 <-> 32-63
+    v = op(a, b);
+  }
+  return v;
+}
+
+// Reduction over the TPR lanes that own a row. For TPR > 64 the wavefronts of
+// the workgroup meet in LDS (`slots` holds TPR/64 values) behind one barrier.
+template <int TPR, class T, class Op>
+SMS_DEV T row_reduce(T v, Op op, T* slots) {
+  if constexpr (TPR <= 64) {
+    return group_reduce<TPR>(v, op);
+  } else {
+    constexpr int W = TPR / 64;
+    v = group_reduce<64>(v, op);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) slots[wave] = v;
+    __syncthreads();
+    T r = slots[0];
+#pragma unroll
+    for (int i = 1; i < W; ++i) r = op(r, slots[i]);
+    return r;
+  }
+}
+
+// -------------------------------------------------------------- row mapping
+
+// Row order. ORDER_ROWS: flat row r -> (b, h, q) with q fastest. The grouped
+// orders put the rows that share one mask row on consecutive workgroups of the
+// same XCD (workgroup w runs on XCD w % xcds), so the mask row is fetched from
+// HBM once and then hits that XCD's L2:
+//   ORDER_HEADS:   group (b, q), members h      (mask [B,Sq,Sk])
+//   ORDER_SAMPLES: group q, members (b, h)      (mask [Sq,Sk])
+enum : uint32_t { ORDER_ROWS = 0, ORDER_HEADS = 1, ORDER_SAMPLES = 2 };
+
+struct RowGeom {
+  uint32_t B, H, Sq, Sk;
+  uint32_t rows;     // B*H*Sq
+  uint32_t order;    // ORDER_*
+  uint32_t xcds;     // XCDs the workgroups are dealt over
+  uint32_t members;  // rows per group in a grouped order
+};
+
+template <int RPB>
+SMS_DEV bool row_coords(const RowGeom& g, uint32_t w, uint32_t local, uint32_t& b, uint32_t& h,
+                        uint32_t& q) {
+  if (g.order == ORDER_ROWS) {
+    const uint32_t r = w * RPB + local;
+    if (r >= g.rows) return false;
+    q = r % g.Sq;
+    const uint32_t t = r / g.Sq;
+    h = t % g.H;
+    b = t / g.H;
+    return true;
+  }
+  // The host only picks a grouped order when members % RPB == 0 and the number
+  // of groups is a multiple of xcds, so every workgroup maps to real rows.
+  const uint32_t xcd = w % g.xcds;
+  const uint32_t s = w / g.xcds;
+  const uint32_t bpg = g.members / RPB;  // workgroups per group
+  const uint32_t grp = (s / bpg) * g.xcds + xcd;
+  const uint32_t m = (s % bpg) * RPB + local;
+  if (g.order == ORDER_HEADS) {
+    b = grp / g.Sq;
+    q = grp % g.Sq;
+    h = m;
+  } else {
+    q = grp;
+    b = m / g.H;
+    h = m % g.H;
+  }
+  return true;
+}
+
+constexpr int block_of(int tpr) { return tpr <= 64 ? 256 : tpr; }
+
+// ------------------------------------------------------------------ forward
+
+struct FwdParams {
+  const char* x;
+  const char* mask;
+  char* y;
+  int64_t sx_b, sx_h, sx_q;  // element strides of x
+  int64_t sy_b, sy_h, sy_q;  // element strides of y
+  int64_t sm_b, sm_h, sm_q;  // element strides of the mask, 0 on broadcast axes
+  RowGeom g;
+  float scale;
+  int causal;
+  int has_mask;
+};
+
+template <class F, int TPR, int NV>
+__global__ void __launch_bounds__(block_of(TPR)) sms_fwd_kernel(FwdParams p) {
+  constexpr int E = F::kE;
+  constexpr int BY = F::kBytes;
+  constexpr int RPB = block_of(TPR) / TPR;
+  __shared__ float slots[2][TPR > 64 ? TPR / 64 : 1];
+
+  const uint32_t lane = threadIdx.x % TPR;
+  uint32_t b, h, q;
+  if (!row_coords<RPB>(p.g, blockIdx.x, threadIdx.x / TPR, b, h, q)) return;
+
+  const int Sk = (int)p.g.Sk;
+  const char* xrow = p.x + ((int64_t)b * p.sx_b + (int64_t)h * p.sx_h + (int64_t)q * p.sx_q) * BY;
+  char* yrow = p.y + ((int64_t)b * p.sy_b + (int64_t)h * p.sy_h + (int64_t)q * p.sy_q) * BY;
+  const int ax = (int)(((uintptr_t)xrow & 15) / BY);
+  const bool yvec = ((((uintptr_t)yrow & 15) / BY) == (uintptr_t)ax);
+  const char* xbase = xrow - ax * BY;  // 16-byte aligned
+  char* ybase = yrow - ax * BY;        // 16-byte aligned when yvec
+  // Keys [0, kload) are read; later keys are causal-future (or past the row).
+  const int kload = p.causal ? (int)min((int64_t)q + 1, (int64_t)Sk) : Sk;
+
+  float s[NV][E];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int v = j * TPR + (int)lane;
+    const int k0 = v * E - ax;
+    if (k0 >= kload || k0 + E <= 0) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) s[j][e] = kNegInf;
+    } else if (k0 >= 0 && k0 + E <= kload) {
+      const uint4 u = *reinterpret_cast<const uint4*>(xbase + (int64_t)v * 16);
+      F::unpack(u, s[j]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int k = k0 + e;
+        s[j][e] = (k >= 0 && k < kload) ? F::ld(xrow + (int64_t)k * BY) : kNegInf;
+      }
+    }
+  }
+
+  // score = x*scale + mask on the keys that were read; the rest stay -inf.
+  const float scale = p.scale;
+  if (p.has_mask) {
+    const char* mrow =
+        p.mask + ((int64_t)b * p.sm_b + (int64_t)h * p.sm_h + (int64_t)q * p.sm_q) * BY;
+    const bool mvec = ((((uintptr_t)mrow & 15) / BY) == (uintptr_t)ax);
+    const char* mbase = mrow - ax * BY;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int v = j * TPR + (int)lane;
+      const int k0 = v * E - ax;
+      if (k0 >= kload || k0 + E <= 0) continue;
+      if (k0 >= 0 && k0 + E <= kload) {
+        float m[E];
+        if (mvec) {
+          F::unpack(*reinterpret_cast<const uint4*>(mbase + (int64_t)v * 16), m);
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) m[e] = F::ld(mrow + (int64_t)(k0 + e) * BY);
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[j][e] = fmaf(s[j][e], scale, m[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int k = k0 + e;
+          if (k >= 0 && k < kload) s[j][e] = fmaf(s[j][e], scale, F::ld(mrow + (int64_t)k * BY));
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int v = j * TPR + (int)lane;
+      const int k0 = v * E - ax;
+      if (k0 >= kload || k0 + E <= 0) continue;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int k = k0 + e;
+        if (k >= 0 && k < kload) s[j][e] *= scale;
+      }
+    }
+  }
+
+  // Row maximum.
+  float mx = kNegInf;
+#pragma unroll
+  for (int j = 0; j < NV; ++j)
+#pragma unroll
+    for (int e = 0; e < E; ++e) mx = fmaxf(mx, s[j][e]);
+  mx = row_reduce<TPR>(mx, OpMax(), slots[0]);
+  // Every key masked: exponentiate against 0 so every term is exp(-inf) = 0.
+  const float mref = (mx == kNegInf) ? 0.0f : mx;
+
+  // Exponentials (kept in place) and their sum.
+  float sum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int k0 = (j * TPR + (int)lane) * E - ax;
+    if (k0 >= kload) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) s[j][e] = 0.0f;
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        s[j][e] = F::exp2((s[j][e] - mref) * kLog2e);
+        sum += s[j][e];
+      }
+    }
+  }
+  sum = row_reduce<TPR>(sum, OpAdd(), slots[1]);
+  const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;  // fully masked row -> zeros
+
+  // Write the whole row, zeros included.
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int v = j * TPR + (int)lane;
+    const int k0 = v * E - ax;
+    if (k0 >= Sk || k0 + E <= 0) continue;
+    float o[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = s[j][e] * inv;
+    if (yvec && k0 >= 0 && k0 + E <= Sk) {
+      *reinterpret_cast<uint4*>(ybase + (int64_t)v * 16) = F::pack(o);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int k = k0 + e;
+        if (k >= 0 && k < Sk) F::st(yrow + (int64_t)k * BY, o[e]);
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------- backward
+
+struct BwdParams {
+  const char* y;
+  const char* dy;
+  char* dx;
+  int64_t sy_b, sy_h, sy_q;
+  int64_t sd_b, sd_h, sd_q;  // dy
+  int64_t sx_b, sx_h, sx_q;  // dx
+  RowGeom g;
+  float scale;
+  int causal;
+};
+
+template <class F, int TPR, int NV>
+__global__ void __launch_bounds__(block_of(TPR)) sms_bwd_kernel(BwdParams p) {
+  constexpr int E = F::kE;
+  constexpr int BY = F::kBytes;
+  constexpr int RPB = block_of(TPR) / TPR;
+  __shared__ double slots[TPR > 64 ? TPR / 64 : 1];
+
+  const uint32_t lane = threadIdx.x % TPR;
+  uint32_t b, h, q;
+  if (!row_coords<RPB>(p.g, blockIdx.x, threadIdx.x / TPR, b, h, q)) return;
+
+  const int Sk = (int)p.g.Sk;
+  const char* yrow = p.y + ((int64_t)b * p.sy_b + (int64_t)h * p.sy_h + (int64_t)q * p.sy_q) * BY;
+  const char* drow = p.dy + ((int64_t)b * p.sd_b + (int64_t)h * p.sd_h + (int64_t)q * p.sd_q) * BY;
+  char* xrow = p.dx + ((int64_t)b * p.sx_b + (int64_t)h * p.sx_h + (int64_t)q * p.sx_q) * BY;
+  const int ay = (int)(((uintptr_t)yrow & 15) / BY);
+  const bool dvec = ((((uintptr_t)drow & 15) / BY) == (uintptr_t)ay);
+  const bool xvec = ((((uintptr_t)xrow & 15) / BY) == (uintptr_t)ay);
+  const char* ybase = yrow - ay * BY;
+  const char* dbase = drow - ay * BY;
+  char* xbase = xrow - ay * BY;
+  // With the causal promise, y is 0 after key q: those keys are not read.
+  const int kload = p.causal ? (int)min((int64_t)q + 1, (int64_t)Sk) : Sk;
+
+  float yv[NV][E], gv[NV][E];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int v = j * TPR + (int)lane;
+    const int k0 = v * E - ay;
+    if (k0 >= kload || k0 + E <= 0) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) yv[j][e] = gv[j][e] = 0.0f;
+    } else if (k0 >= 0 && k0 + E <= kload) {
+      F::unpack(*reinterpret_cast<const uint4*>(ybase + (int64_t)v * 16), yv[j]);
+      if (dvec) {
+        F::unpack(*reinterpret_cast<const uint4*>(dbase + (int64_t)v * 16), gv[j]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) gv[j][e] = F::ld(drow + (int64_t)(k0 + e) * BY);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int k = k0 + e;
+        const bool in = (k >= 0 && k < kload);
+        yv[j][e] = in ? F::ld(yrow + (int64_t)k * BY) : 0.0f;
+        gv[j][e] = in ? F::ld(drow + (int64_t)k * BY) : 0.0f;
+      }
+    }
+  }
+
+  // dot = sum_k dy_k * y_k, accumulated in fp64 (no cancellation loss when
+  // dy_k - dot is small).
+  double acc = 0.0;
+#pragma unroll
+  for (int j = 0; j < NV; ++j)
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc += F::prod(yv[j][e], gv[j][e]);
+  acc = row_reduce<TPR>(acc, OpAdd(), slots);
+  const float dot_hi = (float)acc;
+  const float dot_lo = (float)(acc - (double)dot_hi);
+
+  const float scale = p.scale;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int v = j * TPR + (int)lane;
+    const int k0 = v * E - ay;
+    if (k0 >= Sk || k0 + E <= 0) continue;
+    float o[E];
+    if (k0 >= kload) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] = 0.0f;
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] = (yv[j][e] * scale) * ((gv[j][e] - dot_hi) - dot_lo);
+    }
+    if (xvec && k0 >= 0 && k0 + E <= Sk) {
+      *reinterpret_cast<uint4*>(xbase + (int64_t)v * 16) = F::pack(o);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int k = k0 + e;
+        if (k >= 0 && k < Sk) F::st(xrow + (int64_t)k * BY, o[e]);
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------- launchers
+
+// TPR and NV values the library is built with.
+constexpr int kTprList[] = {4, 8, 16, 32, 64, 128, 256, 512, 1024};
+constexpr int kNvList[] = {1, 2, 4};
+
+template <class F, int TPR>
+hipError_t launch_fwd_tpr(const FwdParams& p, int nv, uint32_t blocks, hipStream_t st) {
+  const dim3 grid(blocks), block(block_of(TPR));
+  switch (nv) {
+    case 1: hipLaunchKernelGGL((sms_fwd_kernel<F, TPR, 1>), grid, block, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((sms_fwd_kernel<F, TPR, 2>), grid, block, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((sms_fwd_kernel<F, TPR, 4>), grid, block, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <class F, int TPR>
+hipError_t launch_bwd_tpr(const BwdParams& p, int nv, uint32_t blocks, hipStream_t st) {
+  const dim3 grid(blocks), block(block_of(TPR));
+  switch (nv) {
+    case 1: hipLaunchKernelGGL((sms_bwd_kernel<F, TPR, 1>), grid, block, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((sms_bwd_kernel<F, TPR, 2>), grid, block, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((sms_bwd_kernel<F, TPR, 4>), grid, block, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <class F>
+hipError_t launch_fwd(const FwdParams& p, int tpr, int nv, uint32_t blocks, hipStream_t st) {
+  switch (tpr) {
+    case 4: return launch_fwd_tpr<F, 4>(p, nv, blocks, st);
+    case 8: return launch_fwd_tpr<F, 8>(p, nv, blocks, st);
+    case 16: return launch_fwd_tpr<F, 16>(p, nv, blocks, st);
+    case 32: return launch_fwd_tpr<F, 32>(p, nv, blocks, st);
+    case 64: return launch_fwd_tpr<F, 64>(p, nv, blocks, st);
+    case 128: return launch_fwd_tpr<F, 128>(p, nv, blocks, st);
+    case 256: return launch_fwd_tpr<F, 256>(p, nv, blocks, st);
+    case 512: return launch_fwd_tpr<F, 512>(p, nv, blocks, st);
+    case 1024: return launch_fwd_tpr<F, 1024>(p, nv, blocks, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <class F>
+hipError_t launch_bwd(const BwdParams& p, int tpr, int nv, uint32_t blocks, hipStream_t st) {
+  switch (tpr) {
+    case 4: return launch_bwd_tpr<F, 4>(p, nv, blocks, st);
+    case 8: return launch_bwd_tpr<F, 8>(p, nv, blocks, st);
+    case 16: return launch_bwd_tpr<F, 16>(p, nv, blocks, st);
+    case 32: return launch_bwd_tpr<F, 32>(p, nv, blocks, st);
+    case 64: return launch_bwd_tpr<F, 64>(p, nv, blocks, st);
+    case 128: return launch_bwd_tpr<F, 128>(p, nv, blocks, st);
+    case 256: return launch_bwd_tpr<F, 256>(p, nv, blocks, st);
+    case 512: return launch_bwd_tpr<F, 512>(p, nv, blocks, st);
+    case 1024: return launch_bwd_tpr<F, 1024>(p, nv, blocks, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace sms
+
+// Per-format launch entry points, one translation unit each (inst_*.hip).
+hipError_t sms_launch_fwd_f32(const sms::FwdParams&, int tpr, int nv, uint32_t blocks, hipStream_t);
+hipError_t sms_launch_fwd_f16(const sms::FwdParams&, int tpr, int nv, uint32_t blocks, hipStream_t);
+hipError_t sms_launch_fwd_bf16(const sms::FwdParams&, int tpr, int nv, uint32_t blocks, hipStream_t);
+hipError_t sms_launch_bwd_f32(const sms::BwdParams&, int tpr, int nv, uint32_t blocks, hipStream_t);
+hipError_t sms_launch_bwd_f16(const sms::BwdParams&, int tpr, int nv, uint32_t blocks, hipStream_t);
+hipError_t sms_launch_bwd_bf16(const sms::BwdParams&, int tpr, int nv, uint32_t blocks, hipStream_t);

@@ -1,0 +1,173 @@
+"""Tensor-level binding of sms_forward / sms_backward and the autograd wrapper.
+
+Argument marshalling only: shapes, strides, dtype, mask mode and the current
+stream are read from the tensors and passed to libsms.so. Nothing here computes
+any part of the softmax, and there is no CPU path: a tensor that is not on the
+GPU is an error.
+"""
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+
+
+def _dtype_code(t, what):
+    try:
+        return _lib.DTYPE_CODES[_DTYPES[t.dtype]]
+    except KeyError:
+        raise TypeError(f"{what}: dtype {t.dtype} is not float32, float16 or bfloat16") from None
+
+
+def _require_gpu(t, what):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a GPU tensor (there is no CPU path)")
+
+
+def _require_4d_rows(t, what):
+    if t.dim() != 4:
+        raise ValueError(f"{what} must be 4-D [B, H, Sq, Sk], got shape {tuple(t.shape)}")
+    if t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{what}: the key axis must be contiguous (stride 1)")
+
+
+def _strides(t):
+    st = list(t.stride())
+    if t.shape[-1] <= 1:
+        st[-1] = 1
+    return _lib.strides4(st)
+
+
+def mask_mode_of(mask, shape):
+    """Mask-broadcast mode for an additive mask of ``mask.shape`` against x of ``shape``.
+
+    [Sq,Sk] or [1,1,Sq,Sk] -> "sq_sk"; [B,Sq,Sk] or [B,1,Sq,Sk] -> "b_sq_sk";
+    [B,1,Sk] or [B,1,1,Sk] -> "b_1_sk"; [B,H,Sq,Sk] -> "full".
+    """
+    if mask is None:
+        return "none"
+    B, H, Sq, Sk = shape
+    ms = tuple(mask.shape)
+    table = [
+        ((Sq, Sk), "sq_sk"), ((1, 1, Sq, Sk), "sq_sk"),
+        ((B, Sq, Sk), "b_sq_sk"), ((B, 1, Sq, Sk), "b_sq_sk"),
+        ((B, 1, Sk), "b_1_sk"), ((B, 1, 1, Sk), "b_1_sk"),
+        ((B, H, Sq, Sk), "full"),
+    ]
+    for s, mode in table:
+        if ms == s:
+            return mode
+    raise ValueError(f"mask shape {ms} is none of [Sq,Sk], [B,Sq,Sk], [B,1,Sk], [B,H,Sq,Sk] "
+                     f"for x of shape {tuple(shape)}")
+
+
+def _stream_handle(device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return s.cuda_stream
+
+
+def sms_forward(x, mask, y, scale=1.0, is_causal=False, stream=None):
+    """y <- softmax(x*scale + mask) over the last axis (C ABI sms_forward).
+
+    x, y: 4-D GPU tensors of one shape and dtype (float32/float16/bfloat16), key
+    axis contiguous; y may be x itself (in place). mask: None or an additive mask
+    of x's dtype, contiguous, in one of the shapes ``mask_mode_of`` accepts.
+    Enqueued on ``stream`` (default: the current stream); returns y.
+    """
+    _require_gpu(x, "x")
+    _require_gpu(y, "y")
+    _require_4d_rows(x, "x")
+    _require_4d_rows(y, "y")
+    if y.shape != x.shape or y.dtype != x.dtype or y.device != x.device:
+        raise ValueError("y must have x's shape, dtype and device")
+    code = _dtype_code(x, "x")
+    mode = mask_mode_of(mask, tuple(x.shape))
+    mptr = None
+    if mask is not None:
+        _require_gpu(mask, "mask")
+        if mask.dtype != x.dtype:
+            raise TypeError(f"mask dtype {mask.dtype} must equal x dtype {x.dtype} "
+                            "(an additive mask; convert boolean masks to 0/-inf first)")
+        if mask.device != x.device:
+            raise ValueError("mask must be on x's device")
+        if not mask.is_contiguous():
+            raise ValueError("mask must be contiguous in its own shape")
+        mptr = mask.data_ptr()
+    B, H, Sq, Sk = x.shape
+    L = _lib.lib()
+    with torch.cuda.device(x.device):
+        st = L.sms_forward(x.data_ptr(), _strides(x), mptr, _lib.MASK_MODES[mode], y.data_ptr(),
+                           _strides(y), code, B, H, Sq, Sk, float(scale), int(bool(is_causal)),
+                           _stream_handle(x.device, stream))
+    _lib.check("sms_forward", st)
+    return y
+
+
+def sms_backward(y, dy, dx, scale=1.0, is_causal=False, stream=None):
+    """dx <- scale * y * (dy - sum_k dy_k y_k) row by row (C ABI sms_backward).
+
+    y, dy, dx: 4-D GPU tensors of one shape and dtype, key axis contiguous; dx
+    may be dy or y itself. ``is_causal`` promises y == 0 at keys after the query
+    (true for y from a causal forward); those keys are then skipped.
+    """
+    for t, n in ((y, "y"), (dy, "dy"), (dx, "dx")):
+        _require_gpu(t, n)
+        _require_4d_rows(t, n)
+        if t.shape != y.shape or t.dtype != y.dtype or t.device != y.device:
+            raise ValueError("y, dy and dx must share shape, dtype and device")
+    code = _dtype_code(y, "y")
+    B, H, Sq, Sk = y.shape
+    L = _lib.lib()
+    with torch.cuda.device(y.device):
+        st = L.sms_backward(y.data_ptr(), _strides(y), dy.data_ptr(), _strides(dy), dx.data_ptr(),
+                            _strides(dx), code, B, H, Sq, Sk, float(scale),
+                            int(bool(is_causal)), _stream_handle(y.device, stream))
+    _lib.check("sms_backward", st)
+    return dx
+
+
+def sms_max_sk(dtype):
+    """Largest key length the library runs for a torch dtype."""
+    return int(_lib.lib().sms_max_sk(_lib.DTYPE_CODES[_DTYPES[dtype]]))
+
+
+def sms_path(dtype, Sk, backward=False):
+    """Kernel family for (dtype, Sk): 0 rows-per-wave, 1 wave-per-row, 2 multi-wave."""
+    return int(_lib.lib().sms_path(_lib.DTYPE_CODES[_DTYPES[dtype]], int(Sk), int(backward)))
+
+
+def _rows_view(t):
+    """t itself when its key axis is contiguous, else a contiguous copy."""
+    return t if (t.shape[-1] <= 1 or t.stride(-1) == 1) else t.contiguous()
+
+
+class ScaledMaskSoftmaxFunction(torch.autograd.Function):
+    """Autograd wrapper: forward saves y only; backward returns (dx, None, None, None)."""
+
+    @staticmethod
+    def forward(ctx, x, mask, scale, is_causal):
+        x = _rows_view(x)
+        if mask is not None and not mask.is_contiguous():
+            mask = mask.contiguous()
+        y = torch.empty_like(x, memory_format=torch.contiguous_format)
+        sms_forward(x, mask, y, scale, is_causal)
+        ctx.scale = float(scale)
+        ctx.is_causal = bool(is_causal)
+        ctx.save_for_backward(y)
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        (y,) = ctx.saved_tensors
+        dy = _rows_view(dy)
+        dx = torch.empty_like(y)
+        sms_backward(y, dy, dx, ctx.scale, ctx.is_causal)
+        return dx, None, None, None
+
+
+def scaled_mask_softmax(x, mask=None, scale=1.0, is_causal=False):
+    """softmax(x*scale + mask) over the last axis of a 4-D GPU tensor, differentiable in x."""
+    return ScaledMaskSoftmaxFunction.apply(x, mask, scale, is_causal)

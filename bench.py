@@ -1,0 +1,240 @@
+"""Throughput of the fused scaled-masked softmax, forward + backward, on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+
+A step is one forward (y = softmax(x*scale + mask), causal rule if the workload
+has it) and one backward (dx = scale*y*(dy - sum dy*y)) over the whole synthetic
+batch, through the C ABI, with every input already in HBM. The default workload
+is fp32 x[8,32,1024,1024] ~ N(0,4), scale 1/8, additive key-padding mask
+[8,1,1024] (0 before a per-batch length L_b ~ U{256..1024}, -10000 after);
+dy ~ N(0,1) fp32.
+
+value = algorithmic bytes of a step / time of a step (GB/s), where algorithmic
+bytes count x and the mask once where the result depends on them, y and dy
+where y can be nonzero, and every y and dx written. One JSON line on stdout;
+diagnostics on stderr.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kept_keys(Sq, Sk, causal):
+    """Keys per (b, h) plane the result depends on: all, or q+1 per row if causal."""
+    if not causal:
+        return Sq * Sk
+    return sum(min(q + 1, Sk) for q in range(Sq)) if Sq <= 1 << 16 else None
+
+
+def min_bytes(shape, dtype_bytes, mode, causal):
+    """Algorithmic bytes of one forward and one backward launch."""
+    B, H, Sq, Sk = shape
+    full = B * H * Sq * Sk
+    plane = kept_keys(Sq, Sk, causal)
+    x_read = B * H * plane
+    if mode == "none":
+        m_read = 0
+    elif mode == "b_1_sk":
+        m_read = B * (min(Sk, Sq) if causal else Sk)
+    elif mode == "sq_sk":
+        m_read = plane
+    elif mode == "b_sq_sk":
+        m_read = B * plane
+    else:
+        m_read = B * H * plane
+    fwd = (x_read + m_read + full) * dtype_bytes
+    bwd = (2 * B * H * plane + full) * dtype_bytes
+    return fwd, bwd
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="time budget of the oracle CPU baseline sample (0 = skip)")
+    ap.add_argument("--no-copy", action="store_true", help="skip the plain-copy reference")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with rocprofv3 FETCH/WRITE bytes per launch (profiles/)")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, y, dy, step_bytes, rows_total, budget_s):
+    """The float64 oracle, as it stands, over a bounded sample of the same rows."""
+    import numpy as np
+
+    import oracle
+    from tests.parity import gather_mask_rows, gather_rows
+
+    B, H, Sq, Sk = w["x"].shape
+    dt = w["dtype"]
+    done = 0
+    spent = 0.0
+    chunk = 64
+    r0 = 0
+    while spent < budget_s and r0 < rows_total:
+        rows = list(range(r0, min(r0 + chunk, rows_total)))
+        xr = gather_rows(w["x"], rows)
+        mr = gather_mask_rows(w["mask"], w["mode"], w["x"].shape, rows)
+        yr, dyr = gather_rows(y, rows), gather_rows(dy, rows)
+        t0 = time.perf_counter()
+        for i, r in enumerate(rows):
+            oracle.forward_row(xr[i], dt, None if mr is None else mr[i], w["scale"], w["causal"],
+                               r % Sq)
+            oracle.backward_row(yr[i], dyr[i], dt, w["scale"])
+        spent += time.perf_counter() - t0
+        done += len(rows)
+        r0 += chunk
+    per_row = step_bytes / rows_total
+    gbps = done * per_row / spent / 1e9
+    del np
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"forward+backward of rows 0..{done - 1} ({done} of {rows_total} rows, "
+                      f"{spent:.1f} s, one thread, float64 numpy oracle)",
+            "rows_per_s": round(done / spent, 1)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): rows are "
+              "independent, so a multi-GPU run is the same kernel on each GPU's share", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from attention_softmax_amd import sms_backward, sms_forward, sms_path
+    from attention_softmax_amd.workloads import CONFIGS, make_config
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = CONFIGS[args.workload]
+    w = make_config(args.workload, dev, with_dy=True)
+    x, mask, dy = w["x"], w["mask"], w["dy"]
+    B, H, Sq, Sk = x.shape
+    rows = B * H * Sq
+    dbytes = x.element_size()
+    fwd_b, bwd_b = min_bytes(x.shape, dbytes, w["mode"], w["causal"])
+    step_b = fwd_b + bwd_b
+    y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    stream = torch.cuda.current_stream(dev)
+    log(f"workload {args.workload}: {cfg['name']}; path fwd={sms_path(x.dtype, Sk)}")
+
+    def step():
+        sms_forward(x, mask, y, w["scale"], w["causal"], stream=stream)
+        sms_backward(y, dy, dx, w["scale"], w["causal"], stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps, HIP events between the two launches on their stream.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        sms_forward(x, mask, y, w["scale"], w["causal"], stream=stream)
+        ev[i][1].record(stream)
+        sms_backward(y, dy, dx, w["scale"], w["causal"], stream=stream)
+        ev[i][2].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    value = step_b / (ms_step * 1e-3) / 1e9
+    kern = {
+        "forward": {"avg_us": round(fwd_ms * 1e3, 2), "bytes": fwd_b,
+                    "GBps": round(fwd_b / (fwd_ms * 1e-3) / 1e9, 1)},
+        "backward": {"avg_us": round(bwd_ms * 1e3, 2), "bytes": bwd_b,
+                     "GBps": round(bwd_b / (bwd_ms * 1e-3) / 1e9, 1)},
+    }
+    for k in kern.values():
+        k["frac_hbm_peak"] = round(k["GBps"] / HBM_PEAK_GBPS, 4)
+    dom = "forward" if fwd_ms >= bwd_ms else "backward"
+
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            t = json.load(f)
+        key = f"workload{args.workload}_{dom}"
+        if key in t:
+            traffic = t[key]
+
+    copy = None
+    if not args.no_copy:
+        # A plain device copy moving the forward's byte count: the achievable ceiling.
+        n = fwd_b // 2
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(10):
+            dst.copy_(src)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        cms = c0.elapsed_time(c1) / 10
+        copy = {"bytes": 2 * n, "avg_us": round(cms * 1e3, 2),
+                "GBps": round(2 * n / (cms * 1e-3) / 1e9, 1)}
+        del src, dst
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(w, y, dy, step_b, rows, args.cpu_seconds)
+
+    out = {
+        "metric": "fused masked-softmax GB/s and % of HBM peak, fwd+bwd, 1 MI355X",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "f16": "f16", "bf16": "bf16"}[w["dtype"]],
+        "data": "synthetic",
+        "config": {"workload": cfg["name"], "shape": [B, H, Sq, Sk], "mask": w["mode"],
+                   "causal": w["causal"], "scale": w["scale"], "pass": "forward+backward",
+                   "dy": "N(0,1)"},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "rows_per_s": round(rows / (ms_step * 1e-3), 1),
+        "step_bytes": step_b,
+        "kernels": kern,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["GBps"],
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": kern[dom]["frac_hbm_peak"], "traffic": traffic},
+        "copy_reference": copy,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,153 @@
+/*
+ * sms.h -- C ABI of the fused scaled-masked softmax library (libsms.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation, for every row (b, h, q) of a score tensor x[B, H, Sq, Sk]:
+ *
+ *     s_k = x[b,h,q,k] * scale + mask[.., k]        (mask optional, additive)
+ *     s_k = -inf                 if is_causal and k > q
+ *     y[b,h,q,k] = exp(s_k - max_j s_j) / sum_j exp(s_j - max_j s_j)
+ *
+ * as defined in lmnt.cn "Custom fused Softmax operator in CUDA, wrapped into
+ * PyTorch", sec. 1.2 (scaled scores plus an additive mask, softmax over the key
+ * axis; causal hides key j > query i) and sec. 2.1 (subtract the row maximum);
+ * the causal rule is applied after the additive mask (sec. 3.1). A row whose
+ * every key is masked is written as all zeros instead of 0/0 (pnsm.cn article on
+ * a custom ScaledMaskSoftmax operator, sec. 4.2 and 4.3).
+ *
+ * The backward (same lmnt.cn page, sec. 3.3) is
+ *
+ *     dx[b,h,q,k] = scale * y_k * (dy_k - sum_j dy_j * y_j)
+ *
+ * which needs only the forward's output y, the upstream gradient dy and scale.
+ *
+ * Arithmetic: inputs of every dtype are widened to fp32; the row maximum, the
+ * exponentials, the normaliser and the normalisation are fp32; the backward's
+ * row dot product is accumulated in fp64. Outputs are rounded to the I/O dtype
+ * with round-to-nearest-even, keeping subnormals.
+ *
+ * Common rules for both entry points
+ * ----------------------------------
+ * - All tensor pointers are DEVICE pointers (memory of the current HIP device),
+ *   owned by the caller. The library allocates nothing, keeps no state between
+ *   calls and never synchronises: work is enqueued on `stream` (a hipStream_t;
+ *   NULL = the null stream) and the call returns before it runs.
+ * - Strides are in ELEMENTS, for the axes (B, H, Sq, Sk) in that order. The key
+ *   axis must be contiguous (stride[3] == 1); other strides are any value >= 0.
+ * - Every pointer must be aligned to its element size. Rows whose start is
+ *   16-byte aligned in every operand take 128-bit loads and stores; other rows
+ *   are still correct (element accesses for the unaligned head and tail).
+ * - Outputs must not overlap inputs, except exactly in place: y == x with
+ *   identical strides (forward), or dx == dy (or dx == y) with identical
+ *   strides (backward). Each row is read completely before any of it is written.
+ * - A size of zero in any dimension is a successful no-op.
+ * - On any error nothing is launched and a status other than SMS_OK is
+ *   returned; no function throws or aborts. SMS_ERR_HIP reports a failure the
+ *   HIP runtime gave for the launch (hipGetLastError after enqueueing).
+ */
+#ifndef SMS_H
+#define SMS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SMS_ABI_VERSION 1
+
+typedef enum {
+  SMS_OK = 0,
+  SMS_ERR_NULL = 1,      /* a required pointer is NULL                            */
+  SMS_ERR_SHAPE = 2,     /* negative dim, or a size beyond what the library runs  */
+  SMS_ERR_STRIDE = 3,    /* stride[3] != 1 or a negative stride                   */
+  SMS_ERR_DTYPE = 4,     /* unknown dtype                                         */
+  SMS_ERR_MASK_MODE = 5, /* unknown mask mode                                     */
+  SMS_ERR_ALIGN = 6,     /* a pointer not aligned to its element size             */
+  SMS_ERR_HIP = 7        /* the HIP runtime reported an error for the launch      */
+} sms_status;
+
+typedef enum {
+  SMS_F32 = 0,  /* IEEE binary32                                */
+  SMS_F16 = 1,  /* IEEE binary16                                */
+  SMS_BF16 = 2  /* bfloat16 (upper 16 bits of a binary32 value) */
+} sms_dtype;
+
+/* The additive mask's own shape; it has x's dtype and is contiguous (row-major)
+ * in that shape. Axes it lacks are broadcast. The shapes follow the pnsm.cn
+ * ScaledMaskSoftmax article, sec. 2.1 ([Sq,Sk] shared by all samples, or
+ * [B,Sq,Sk] per sample), the lmnt.cn page's full mask (sec. 5.1 test), and a
+ * per-batch key-padding mask [B,1,Sk]. */
+typedef enum {
+  SMS_MASK_NONE = 0,    /* no mask; the mask pointer is ignored                */
+  SMS_MASK_SQ_SK = 1,   /* [Sq, Sk],     broadcast over B and H                */
+  SMS_MASK_B_SQ_SK = 2, /* [B, Sq, Sk],  broadcast over H                      */
+  SMS_MASK_B_1_SK = 3,  /* [B, 1, Sk],   broadcast over H and Sq (key padding) */
+  SMS_MASK_FULL = 4     /* [B, H, Sq, Sk]                                      */
+} sms_mask_mode;
+
+/*
+ * sms_forward -- y = softmax(x * scale + mask) over the key axis, with the
+ * optional causal rule (key k > query q masked, q = the row's index on the Sq
+ * axis).
+ *
+ *   x, x_strides   input scores [B,H,Sq,Sk] (dtype), device memory
+ *   mask           additive mask in the shape `mask_mode` names (dtype, device,
+ *                  contiguous); may be NULL only with SMS_MASK_NONE. Values are
+ *                  finite or -inf.
+ *   y, y_strides   output [B,H,Sq,Sk] (dtype), device memory; every element of
+ *                  every row is written (0 where masked or causal-future, all
+ *                  zeros for a row with every key masked)
+ *   scale          multiplier applied to x before the mask (e.g. 1/sqrt(d_k))
+ *   is_causal      nonzero: keys k > q are masked after the additive mask
+ *   stream         hipStream_t to enqueue on
+ *
+ * Limits: B*H*Sq < 2^32 rows and Sk <= sms_max_sk(dtype).
+ */
+sms_status sms_forward(const void* x, const int64_t x_strides[4],
+                       const void* mask, sms_mask_mode mask_mode,
+                       void* y, const int64_t y_strides[4],
+                       sms_dtype dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk,
+                       float scale, int is_causal, void* stream);
+
+/*
+ * sms_backward -- dx = scale * y * (dy - sum_k dy_k * y_k), row by row.
+ *
+ *   y, y_strides     the forward's output (dtype), device memory
+ *   dy, dy_strides   upstream gradient (dtype), device memory
+ *   dx, dx_strides   output gradient (dtype), device memory; every element written
+ *   scale            the forward's scale
+ *   is_causal        nonzero: a promise that y is 0 at keys k > q (true of any y
+ *                    sms_forward wrote with is_causal set); those y and dy are
+ *                    then not read and dx there is written as 0. Zero is always
+ *                    correct.
+ *   stream           hipStream_t to enqueue on
+ *
+ * Limits as for sms_forward.
+ */
+sms_status sms_backward(const void* y, const int64_t y_strides[4],
+                        const void* dy, const int64_t dy_strides[4],
+                        void* dx, const int64_t dx_strides[4],
+                        sms_dtype dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk,
+                        float scale, int is_causal, void* stream);
+
+/* Largest key length Sk the library runs for `dtype` (0 for an unknown dtype). */
+int64_t sms_max_sk(sms_dtype dtype);
+
+/* Which kernel family a call with these sizes takes: 0 = several rows per
+ * wavefront, 1 = one wavefront per row, 2 = several wavefronts per row (LDS
+ * cross-wave reduction). -1 for an unsupported size or dtype. `backward`
+ * selects the backward's choice. Host-only; launches nothing. */
+int sms_path(sms_dtype dtype, int64_t Sk, int backward);
+
+/* Static text naming a status code. */
+const char* sms_status_str(sms_status s);
+
+/* SMS_ABI_VERSION of the library that was loaded. */
+int sms_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMS_H */

@@ -1,0 +1,131 @@
+"""The C ABI loads and exports what include/sms.h declares; host-side argument
+checks. CPU only: every call here fails validation (or is a zero-size no-op)
+before the library would launch anything."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from attention_softmax_amd import _lib, mask_mode_of
+from attention_softmax_amd.workloads import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sms.h")
+
+# A non-NULL, 16-byte aligned address that is never dereferenced: every call
+# that receives it is rejected by the host-side checks first.
+FAKE = 0x10000
+FAKE_ODD = 0x10001
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sms_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_status_text(L):
+    assert L.sms_abi_version() == _lib.ABI_VERSION
+    for code, name in _lib.STATUS_NAMES.items():
+        text = L.sms_status_str(code).decode()
+        assert text and text != "unknown status", (code, name)
+    assert L.sms_status_str(99).decode() == "unknown status"
+
+
+def _fwd(L, x=FAKE, xs=(64, 64, 64, 1), mask=None, mode=0, y=FAKE, ys=(64, 64, 64, 1),
+         dtype=0, B=1, H=1, Sq=1, Sk=64, scale=1.0, causal=0):
+    return L.sms_forward(x, _lib.strides4(xs) if xs is not None else None, mask, mode, y,
+                         _lib.strides4(ys) if ys is not None else None, dtype, B, H, Sq, Sk,
+                         scale, causal, None)
+
+
+def _bwd(L, y=FAKE, dy=FAKE, dx=FAKE, st=(64, 64, 64, 1), dtype=0, B=1, H=1, Sq=1, Sk=64):
+    s = _lib.strides4(st)
+    return L.sms_backward(y, s, dy, s, dx, s, dtype, B, H, Sq, Sk, 1.0, 0, None)
+
+
+def test_forward_argument_checks(L):
+    assert _fwd(L, dtype=7) == 4                                  # dtype
+    assert _fwd(L, mode=9) == 5                                   # mask mode
+    assert _fwd(L, B=-1) == 2 and _fwd(L, Sk=-3) == 2             # negative dims
+    assert _fwd(L, x=None) == 1 and _fwd(L, y=None) == 1          # NULL tensors
+    assert _fwd(L, mode=1, mask=None) == 1                        # mask required by mode
+    assert _fwd(L, xs=None) == 1                                  # NULL strides
+    assert _fwd(L, xs=(64, 64, 64, 2)) == 3                       # key axis not contiguous
+    assert _fwd(L, ys=(64, -64, 64, 1)) == 3                      # negative stride
+    assert _fwd(L, x=FAKE_ODD) == 6                               # misaligned fp32 pointer
+    assert _fwd(L, dtype=1, y=FAKE_ODD) == 6                      # misaligned fp16 pointer
+    assert _fwd(L, mode=2, mask=FAKE_ODD) == 6                    # misaligned mask
+    assert _fwd(L, Sk=L.sms_max_sk(0) + 1) == 2                   # too long a row
+    assert _fwd(L, B=1 << 20, H=1 << 10, Sq=1 << 3) == 2          # 2^33 rows
+    assert _fwd(L, Sk=1 << 31) == 2
+
+
+def test_zero_sizes_are_noops(L):
+    # NULL pointers are fine when there is nothing to do.
+    for dims in ((0, 1, 1, 8), (1, 0, 1, 8), (1, 1, 0, 8), (1, 1, 1, 0)):
+        B, H, Sq, Sk = dims
+        assert _fwd(L, x=None, y=None, B=B, H=H, Sq=Sq, Sk=Sk) == 0
+        assert _bwd(L, y=None, dy=None, dx=None, B=B, H=H, Sq=Sq, Sk=Sk) == 0
+
+
+def test_backward_argument_checks(L):
+    assert _bwd(L, dtype=3) == 4
+    assert _bwd(L, dy=None) == 1 and _bwd(L, dx=None) == 1
+    assert _bwd(L, st=(64, 64, 64, 0)) == 3
+    assert _bwd(L, dx=FAKE_ODD) == 6
+    assert _bwd(L, Sk=L.sms_max_sk(2) + 1, dtype=2) == 2
+
+
+def test_max_sk_and_paths(L):
+    assert L.sms_max_sk(0) == 4096 * 4 - 3
+    assert L.sms_max_sk(1) == L.sms_max_sk(2) == 4096 * 8 - 7
+    assert L.sms_max_sk(5) == 0
+    # the benchmark workloads: rows-per-wave, wave-per-row and multi-wave families
+    expect = {1: 0, 2: 1, 3: 1, 4: 2, 5: 0}
+    code = {"f32": 0, "f16": 1, "bf16": 2}
+    for i, c in CONFIGS.items():
+        assert L.sms_path(code[c["dtype"]], c["shape"][3], 0) == expect[i], i
+    assert L.sms_path(1, 1 << 20, 0) == -1
+
+
+def test_mask_mode_inference():
+    shape = (2, 3, 5, 7)
+    z = lambda *s: torch.empty(s)  # noqa: E731
+    assert mask_mode_of(None, shape) == "none"
+    assert mask_mode_of(z(5, 7), shape) == "sq_sk"
+    assert mask_mode_of(z(1, 1, 5, 7), shape) == "sq_sk"
+    assert mask_mode_of(z(2, 5, 7), shape) == "b_sq_sk"
+    assert mask_mode_of(z(2, 1, 5, 7), shape) == "b_sq_sk"
+    assert mask_mode_of(z(2, 1, 7), shape) == "b_1_sk"
+    assert mask_mode_of(z(2, 1, 1, 7), shape) == "b_1_sk"
+    assert mask_mode_of(z(2, 3, 5, 7), shape) == "full"
+    for bad in ((3, 5, 7), (5, 6), (2, 3, 1, 7), (7,)):
+        with pytest.raises(ValueError):
+            mask_mode_of(z(*bad), shape)
+
+
+def test_binding_refuses_cpu_tensors():
+    from attention_softmax_amd import sms_forward, sms_backward, scaled_mask_softmax
+    x = torch.zeros(1, 1, 2, 8)
+    with pytest.raises(ValueError, match="GPU"):
+        sms_forward(x, None, torch.empty_like(x))
+    with pytest.raises(ValueError, match="GPU"):
+        sms_backward(x, x, torch.empty_like(x))
+    with pytest.raises(ValueError, match="GPU"):
+        scaled_mask_softmax(x)

@@ -1,0 +1,371 @@
+"""HIP path against the float64 oracle, through the C ABI (via the binding).
+
+Small shapes are checked element by element on every row; the benchmark
+workloads at full size are checked on sampled rows (oracle one row at a time)
+plus properties over every row: exact zeros where keys are masked or
+causal-future, and row sums.
+"""
+
+import math
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attention_softmax_amd import (SmsError, scaled_mask_softmax, sms_backward, sms_forward,
+                                   sms_max_sk)
+from attention_softmax_amd.workloads import CONFIGS, TORCH_DTYPE, draw_mask, draw_x, make_config
+from tests.parity import (compare, decoded, gather_mask_rows, gather_rows, mask_4d,
+                          sample_rows, to_np)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def fwd(x, mask=None, scale=1.0, causal=False, y=None):
+    y = torch.empty_like(x) if y is None else y
+    sms_forward(x, mask, y, scale, causal)
+    torch.cuda.synchronize()
+    return y
+
+
+def bwd(y, dy, scale=1.0, causal=False, dx=None):
+    dx = torch.empty_like(y) if dx is None else dx
+    sms_backward(y, dy, dx, scale, causal)
+    torch.cuda.synchronize()
+    return dx
+
+
+def oracle_fwd(x, mask, mode, scale, causal):
+    dt = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[x.dtype]
+    return oracle.forward(to_np(x), dt, mask_4d(mask, mode), scale, causal)
+
+
+def dtname(t):
+    return {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[t.dtype]
+
+
+# ------------------------------------------------------------ shape sweep
+
+SK_SWEEP = [1, 3, 7, 8, 63, 64, 65, 77, 127, 128, 1000, 1001, 1024, 2047, 2048, 2049, 4095,
+            4096, 4097, 8192]
+MODES = ["none", "sq_sk", "b_sq_sk", "b_1_sk", "full"]
+
+
+def _mask_kind(mode):
+    return ("normal", 2.0) if mode in ("b_1_sk",) else ("bernoulli_neginf", 0.25)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("Sk", SK_SWEEP)
+def test_sweep_all_modes(dtype, Sk):
+    """Every mask mode, non-causal and causal, on a few rows of each length."""
+    say(f"sweep dtype={dtype} Sk={Sk}")
+    for mode in MODES:
+        for causal in (False, True):
+            shape = (2, 2, 3, Sk)
+            seed = zlib.crc32(f"{dtype}/{Sk}/{mode}/{causal}".encode()) % 10000
+            x = draw_x(shape, dtype, ("normal", 3.0), seed, DEV)
+            mask = draw_mask(shape, mode, dtype, _mask_kind(mode), seed + 1, DEV)
+            y = fwd(x, mask, 0.3, causal)
+            ref = oracle_fwd(x, mask, mode, 0.3, causal)
+            compare(decoded(y), ref, dtype, f"{dtype} Sk={Sk} {mode} causal={causal}",
+                    rowsum=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("Sk", [5, 64, 200, 1000, 1030, 4096])
+def test_causal_square(dtype, Sk):
+    """Sq = Sk causal: every query position, sampled rows against the oracle and
+    exact zeros after the diagonal on every row."""
+    say(f"causal square dtype={dtype} Sk={Sk}")
+    shape = (1, 2, Sk, Sk)
+    x = draw_x(shape, dtype, ("normal", 8.0), Sk, DEV)
+    mask = draw_mask(shape, "sq_sk", dtype, ("bernoulli_neginf", 0.1), Sk + 7, DEV)
+    y = fwd(x, mask, 1 / math.sqrt(128), True)
+    fut = torch.triu(torch.ones(Sk, Sk, dtype=torch.bool, device=DEV), diagonal=1)
+    assert (y[:, :, fut] == 0).all()
+    rows = sample_rows(2 * Sk, Sk, k=min(2 * Sk, 160), seed=Sk)
+    xr, mr = gather_rows(x, rows), gather_mask_rows(mask, "sq_sk", shape, rows)
+    yr = oracle.decode(gather_rows(y, rows), dtype)
+    for i, r in enumerate(rows):
+        q = r % Sk
+        ref = oracle.forward_row(xr[i], dtype, mr[i], 1 / math.sqrt(128), True, q)
+        compare(yr[i], ref, dtype, f"row {r}")
+
+
+# ------------------------------------------------ workloads, reduced sizes
+
+SMALL = {1: (1, 2, 64, 64), 2: (2, 4, 64, 1024), 3: (1, 2, 2048, 2048),
+         4: (1, 2, 4096, 4096), 5: (2, 2, 1000, 1000)}
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_workload_recipe_small(cfg):
+    """Each workload's recipe (dtype, distributions, mask mode, causal, scale) at
+    a size the oracle covers on every row; forward and backward."""
+    say(f"workload {cfg} small shape {SMALL[cfg]}")
+    w = make_config(cfg, DEV, shape=SMALL[cfg], with_dy=True)
+    x, mask, mode, dt = w["x"], w["mask"], w["mode"], w["dtype"]
+    y = fwd(x, mask, w["scale"], w["causal"])
+    ref = oracle_fwd(x, mask, mode, w["scale"], w["causal"])
+    compare(decoded(y), ref, dt, f"cfg{cfg} fwd", rowsum=True)
+    dx = bwd(y, w["dy"], w["scale"], w["causal"])
+    refb = oracle.backward(to_np(y), to_np(w["dy"]), dt, w["scale"])
+    compare(decoded(dx), refb, dt, f"cfg{cfg} bwd")
+    # the causal promise changes nothing when it holds
+    if w["causal"]:
+        dx0 = bwd(y, w["dy"], w["scale"], False)
+        compare(decoded(dx0), refb, dt, f"cfg{cfg} bwd without the causal promise")
+
+
+# -------------------------------------------------- workloads, full sizes
+
+def _full_forward_check(cfg):
+    c = CONFIGS[cfg]
+    say(f"workload {cfg} full {c['shape']}")
+    w = make_config(cfg, DEV)
+    x, mask, mode, dt = w["x"], w["mask"], w["mode"], w["dtype"]
+    B, H, Sq, Sk = x.shape
+    y = fwd(x, mask, w["scale"], w["causal"])
+    rows = sample_rows(B * H * Sq, Sq, k=256, seed=cfg)
+    xr = gather_rows(x, rows)
+    mr = gather_mask_rows(mask, mode, x.shape, rows)
+    yr = oracle.decode(gather_rows(y, rows), dt)
+    for i, r in enumerate(rows):
+        ref = oracle.forward_row(xr[i], dt, None if mr is None else mr[i], w["scale"],
+                                 w["causal"], r % Sq)
+        compare(yr[i], ref, dt, f"cfg{cfg} row {r}", rowsum=True)
+    # every row: masked / causal-future keys exactly 0, row sums near 1. For
+    # fp16/bf16 the bound follows from 2 ulp per element: sum_k 2 ulp(y_k) <=
+    # 2^-(p-2) * sum_k y_k plus 2 subnormal ulps per element.
+    p, emin = {"f32": (24, -126), "f16": (11, -14), "bf16": (8, -126)}[dt]
+    tol = 1e-5 if dt == "f32" else 2.0 ** -(p - 2) + Sk * 2.0 ** (emin - p + 2)
+    for b in range(B):
+        yb = y[b]
+        if w["causal"]:
+            fut = torch.triu(torch.ones(Sq, Sk, dtype=torch.bool, device=DEV), diagonal=1)
+            assert not ((yb != 0) & fut).any(), f"cfg{cfg} b={b}: causal-future key not 0"
+        if mask is not None:
+            mb = {"sq_sk": mask, "b_sq_sk": mask[b], "b_1_sk": mask[b], "full": mask[b]}[mode]
+            assert not ((yb != 0) & torch.isinf(mb)).any(), f"cfg{cfg} b={b}: masked key not 0"
+        s = yb.double().sum(-1)
+        assert (s - 1).abs().max().item() <= tol, f"cfg{cfg} b={b} row sum"
+    return w, y, rows
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_workload_full_size(cfg):
+    w, y, rows = _full_forward_check(cfg)
+    if CONFIGS[cfg]["backward"]:
+        dt = w["dtype"]
+        say(f"workload {cfg} full backward")
+        dx = bwd(y, w["dy"], w["scale"], w["causal"])
+        yr, dyr = gather_rows(y, rows), gather_rows(w["dy"], rows)
+        dxr = oracle.decode(gather_rows(dx, rows), dt)
+        for i, r in enumerate(rows):
+            ref = oracle.backward_row(yr[i], dyr[i], dt, w["scale"])
+            compare(dxr[i], ref, dt, f"cfg{cfg} bwd row {r}")
+        # sum_k dx_k ~ 0 on every row (sum_k y_k ~ 1)
+        s = dx.double().sum(-1).abs().max().item()
+        assert s < 1e-2, s
+        del dx
+    del w, y
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------- strides, alignment, in place
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("Sk,pad,xoff,yoff,moff", [
+    (1000, 0, 1, 1, 0),    # rows start mid-line, x and y alike
+    (1000, 0, 1, 0, 0),    # x and y with different offsets -> element stores
+    (1001, 0, 0, 0, 0),    # odd length: rows alternate alignment
+    (1001, 7, 0, 0, 3),    # padded strides with a scalar tail; mask offset
+    (256, 8, 0, 0, 1),     # aligned rows, misaligned mask rows
+    (77, 3, 2, 5, 1),
+])
+def test_strided_and_misaligned(dtype, Sk, pad, xoff, yoff, moff):
+    say(f"strided dtype={dtype} Sk={Sk} pad={pad} xoff={xoff} yoff={yoff} moff={moff}")
+    B, H, Sq = 2, 3, 4
+    td = TORCH_DTYPE[dtype]
+    n = B * H * Sq * (Sk + pad)
+    xs = draw_x((xoff + n,), dtype, ("normal", 3.0), Sk + pad, DEV)
+    x = xs[xoff:].view(B, H, Sq, Sk + pad)[..., :Sk]
+    ys = torch.full((yoff + n,), 7.0, dtype=td, device=DEV)
+    y = ys[yoff:].view(B, H, Sq, Sk + pad)[..., :Sk]
+    ms = draw_mask((1, 1, 1, moff + B * Sq * Sk), "full", dtype, ("bernoulli_neginf", 0.2), 5,
+                   DEV).reshape(-1)
+    mask = ms[moff:].view(B, Sq, Sk)
+    fwd(x, mask, 0.5, True, y=y)
+    ref = oracle_fwd(x.contiguous(), mask, "b_sq_sk", 0.5, True)
+    compare(decoded(y), ref, dtype, "strided fwd", rowsum=True)
+    if pad:  # the padding between rows is untouched
+        gaps = ys[yoff:].view(B, H, Sq, Sk + pad)[..., Sk:]
+        assert (gaps == 7.0).all()
+    # backward with the same strided layout
+    dys = draw_x((xoff + n,), dtype, ("normal", 1.0), 99, DEV)
+    dy = dys[xoff:].view(B, H, Sq, Sk + pad)[..., :Sk]
+    dxs = torch.zeros((yoff + n,), dtype=td, device=DEV)
+    dx = dxs[yoff:].view(B, H, Sq, Sk + pad)[..., :Sk]
+    bwd(y, dy, 0.5, True, dx=dx)
+    refb = oracle.backward(to_np(y), to_np(dy), dtype, 0.5)
+    compare(decoded(dx), refb, dtype, "strided bwd")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_permuted_strides_and_in_place(dtype):
+    say(f"permuted/in-place dtype={dtype}")
+    base = draw_x((2, 5, 3, 512), dtype, ("normal", 2.0), 3, DEV)  # [B, Sq, H, Sk] storage
+    x = base.permute(0, 2, 1, 3)                                   # [B, H, Sq, Sk] view
+    ref = oracle_fwd(x.contiguous(), None, "none", 0.7, False)
+    y = fwd(x, None, 0.7, False)
+    compare(decoded(y), ref, dtype, "permuted")
+    xi = x.clone()
+    fwd(xi, None, 0.7, False, y=xi)                                # in place
+    assert torch.equal(xi, y)
+    dy = draw_x(tuple(y.shape), dtype, ("normal", 1.0), 4, DEV)
+    refb = oracle.backward(to_np(y), to_np(dy), dtype, 0.7)
+    g = dy.clone()
+    bwd(y, g, 0.7, False, dx=g)                                    # dx == dy in place
+    compare(decoded(g), refb, dtype, "in-place bwd")
+
+
+# ------------------------------------------------------ forced kernel shapes
+
+@pytest.mark.parametrize("tpr", [4, 8, 16, 32, 64, 128, 256, 512, 1024])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_every_lanes_per_row(tpr, dtype, monkeypatch):
+    """Each row width (rows per wave, one wave, 2..16 waves per row) on a row
+    length it can hold, against the oracle."""
+    E = 4 if dtype == "f32" else 8
+    Sk = min(4 * tpr * E - E + 1, 3 * tpr * E + 5)
+    say(f"forced TPR={tpr} dtype={dtype} Sk={Sk}")
+    monkeypatch.setenv("SMS_FORCE_TPR", str(tpr))
+    shape = (1, 3, 5, Sk)
+    x = draw_x(shape, dtype, ("normal", 4.0), tpr, DEV)
+    mask = draw_mask(shape, "b_sq_sk", dtype, ("bernoulli_neginf", 0.3), tpr + 1, DEV)
+    for causal in (False, True):
+        y = fwd(x, mask, 0.25, causal)
+        compare(decoded(y), oracle_fwd(x, mask, "b_sq_sk", 0.25, causal), dtype,
+                f"TPR={tpr} causal={causal}", rowsum=True)
+    dy = draw_x(shape, dtype, ("normal", 1.0), tpr + 2, DEV)
+    dx = bwd(y, dy, 0.25, True)
+    compare(decoded(dx), oracle.backward(to_np(y), to_np(dy), dtype, 0.25), dtype,
+            f"TPR={tpr} bwd")
+
+
+def test_forced_width_too_small_is_an_error(monkeypatch):
+    monkeypatch.setenv("SMS_FORCE_TPR", "4")
+    x = torch.zeros(1, 1, 2, 4096, device=DEV)
+    with pytest.raises(SmsError, match="SHAPE"):
+        sms_forward(x, None, torch.empty_like(x))
+
+
+@pytest.mark.parametrize("order", ["rows", "grouped"])
+def test_row_orders_agree(order, monkeypatch):
+    """The XCD-grouped row order is a permutation of rows: identical bits."""
+    monkeypatch.setenv("SMS_ORDER", order)
+    for Sk, mode in ((2048, "b_sq_sk"), (4096, "b_sq_sk"), (2048, "sq_sk"), (4096, "sq_sk")):
+        shape = (2, 4, 64, Sk)  # 4 heads: a multiple of the rows per workgroup
+        x = draw_x(shape, "f16", ("normal", 8.0), 1, DEV)
+        mask = draw_mask(shape, mode, "f16", ("bernoulli_neginf", 0.1), 2, DEV)
+        y = fwd(x, mask, 0.125, True)
+        monkeypatch.setenv("SMS_ORDER", "rows")
+        y0 = fwd(x, mask, 0.125, True)
+        monkeypatch.setenv("SMS_ORDER", order)
+        assert torch.equal(y, y0)
+        compare(decoded(y), oracle_fwd(x, mask, mode, 0.125, True), "f16", f"order {order}")
+
+
+# ------------------------------------------------------------------ edges
+
+def test_edge_rows():
+    say("edge rows")
+    # fully masked rows (by mask, and by causal + mask at key 0 for q = 0) -> zeros
+    x = draw_x((1, 2, 4, 300), "f16", ("normal", 1.0), 0, DEV)
+    mask = torch.zeros(4, 300, dtype=torch.float16, device=DEV)
+    mask[1] = -math.inf
+    mask[0, 0] = -math.inf
+    y = fwd(x, mask, 1.0, True)
+    assert (y[:, :, 0] == 0).all() and (y[:, :, 1] == 0).all()
+    assert not torch.isnan(y).any()
+    compare(decoded(y), oracle_fwd(x, mask, "sq_sk", 1.0, True), "f16", "fully masked")
+    dy = torch.randn_like(y)
+    dx = bwd(y, dy, 1.0, True)
+    assert (dx[:, :, :2] == 0).all()
+    # Sk = 1: probability exactly 1 (or 0 when masked)
+    x1 = torch.randn(2, 2, 3, 1, device=DEV)
+    assert (fwd(x1) == 1).all()
+    # large equal-ish scores; an fp16 probability that is a subnormal
+    xs = torch.tensor([[[[1000.0, 1001.0]]]], device=DEV)
+    compare(decoded(fwd(xs)), [[[[1 / (1 + math.e), math.e / (1 + math.e)]]]], "f32", "[1000,1001]")
+    xh = torch.tensor([[[[0.0, -12.0]]]], device=DEV, dtype=torch.float16)
+    yh = fwd(xh)
+    assert yh[0, 0, 0, 1].item() == 103 * 2.0 ** -24  # RNE of 6.1442e-06, kept subnormal
+    # scale 0 -> uniform over unmasked keys; negative scale flips the order
+    xu = draw_x((1, 1, 2, 100), "f32", ("normal", 5.0), 3, DEV)
+    yu = fwd(xu, None, 0.0)
+    assert torch.allclose(yu, torch.full_like(yu, 0.01), atol=1e-9, rtol=0)
+    compare(decoded(fwd(xu, None, -0.5)), oracle_fwd(xu, None, "none", -0.5, False), "f32",
+            "negative scale")
+
+
+def test_zero_size_and_errors():
+    x = torch.empty(2, 0, 3, 8, device=DEV)
+    fwd(x)
+    bwd(x, x)
+    x = torch.randn(1, 1, 2, 8, device=DEV)
+    with pytest.raises(TypeError):
+        sms_forward(x, torch.zeros(2, 8, dtype=torch.float16, device=DEV), torch.empty_like(x))
+    with pytest.raises(ValueError):
+        sms_forward(x, None, torch.empty(1, 1, 2, 9, device=DEV))
+    with pytest.raises(SmsError, match="SHAPE"):
+        big = torch.empty(1, 1, 1, sms_max_sk(torch.float32) + 1, device=DEV)
+        sms_forward(big, None, big)
+
+
+def test_deterministic():
+    w = make_config(5, DEV, shape=(2, 4, 1000, 1000), with_dy=True)
+    y1 = fwd(w["x"], w["mask"], w["scale"], False)
+    y2 = fwd(w["x"], w["mask"], w["scale"], False)
+    assert torch.equal(y1, y2)
+    d1 = bwd(y1, w["dy"], w["scale"])
+    d2 = bwd(y1, w["dy"], w["scale"])
+    assert torch.equal(d1, d2)
+
+
+# --------------------------------------------------------------- autograd
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_autograd_and_streams(dtype):
+    say(f"autograd dtype={dtype}")
+    shape = (2, 3, 17, 130)
+    x = draw_x(shape, dtype, ("normal", 3.0), 1, DEV).requires_grad_(True)
+    mask = draw_mask(shape, "b_sq_sk", dtype, ("bernoulli_neginf", 0.2), 2, DEV)
+    dy = draw_x(shape, dtype, ("normal", 1.0), 3, DEV)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        y = scaled_mask_softmax(x, mask, 0.35, True)
+        (y * dy).sum().backward() if dtype == "f32" else y.backward(dy)
+    torch.cuda.synchronize()
+    compare(decoded(y.detach()), oracle_fwd(x.detach(), mask, "b_sq_sk", 0.35, True), dtype,
+            "autograd fwd")
+    refb = oracle.backward(to_np(y.detach()), to_np(dy), dtype, 0.35)
+    compare(decoded(x.grad), refb, dtype, "autograd bwd")
+    # non-contiguous upstream gradient
+    x.grad = None
+    y = scaled_mask_softmax(x, mask, 0.35, True)
+    g = torch.cat([dy, dy], dim=-1)[..., ::2]
+    y.backward(g)
+    torch.cuda.synchronize()
+    compare(decoded(x.grad), oracle.backward(to_np(y.detach()), to_np(g.contiguous()), dtype,
+                                             0.35), dtype, "autograd strided dy")
