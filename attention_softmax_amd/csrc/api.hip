@@ -23,8 +23,11 @@ using sms::RowGeom;
 
 // Workgroups are dealt round-robin over the XCDs of an MI355X.
 constexpr uint32_t kXcds = 8;
-// A broadcast mask larger than this is worth a grouped row order.
-constexpr int64_t kGroupedOrderMaskBytes = 16ll << 20;
+// The grouped row order (rows sharing a mask row on one XCD, back to back) is
+// available on request (SMS_ORDER=grouped); by default rows run in memory
+// order, which measured faster on MI355X even for a 128 MB [B,Sq,Sk] mask:
+// the x / y streams keep their DRAM-page locality and the re-read mask rows
+// are served by the 256 MB Infinity Cache.
 
 int dtype_bytes(sms_dtype d) {
   switch (d) {
@@ -65,18 +68,29 @@ int64_t vectors_per_row(int64_t Sk, int E, bool aligned) {
   return aligned ? (Sk + E - 1) / E : (Sk + 2 * E - 2) / E;
 }
 
-// Fewest lanes per row that hold the row in at most 4 vectors per lane, then
-// the fewest vectors per lane that cover it.
-bool choose_plan(int64_t nvec, Plan& out) {
+// Fewest lanes per row that hold the row in at most `want` vectors per lane,
+// then the fewest vectors that cover it; rows too long for 1024 lanes at that
+// count take up to 4. Measured on MI355X: the forward runs best at 2 vectors
+// per lane up to 256 vectors per row and at 4 beyond; the backward (two input
+// streams) at 2 below 256 vectors per row and at 1 from there.
+int vectors_per_lane(int64_t nvec, bool backward) {
+  if (backward) return nvec >= 256 ? 1 : 2;
+  return nvec > 256 ? 4 : 2;
+}
+
+bool choose_plan(int64_t nvec, bool backward, Plan& out) {
   const int force = forced_tpr();
-  for (int tpr : sms::kTprList) {
-    if (force && tpr != force) continue;
-    if (!force && (int64_t)tpr * 4 < nvec) continue;
-    for (int nv : sms::kNvList) {
-      if ((int64_t)tpr * nv >= nvec) {
-        out.tpr = tpr;
-        out.nv = nv;
-        return true;
+  const int want = vectors_per_lane(nvec, backward);
+  for (int per_lane : {want, 2, 4}) {
+    for (int tpr : sms::kTprList) {
+      if (force && tpr != force) continue;
+      if (!force && (int64_t)tpr * per_lane < nvec) continue;
+      for (int nv : sms::kNvList) {
+        if ((int64_t)tpr * nv >= nvec) {
+          out.tpr = tpr;
+          out.nv = nv;
+          return true;
+        }
       }
     }
   }
@@ -121,6 +135,23 @@ sms_status check_sizes(int64_t B, int64_t H, int64_t Sq, int64_t Sk) {
 
 bool aligned_to(const void* p, int bytes) { return ((uintptr_t)p % (uintptr_t)bytes) == 0; }
 
+int env_int(const char* name, int dflt) {
+  const char* s = getenv(name);
+  return s ? atoi(s) : dflt;
+}
+
+// The fast path needs whole 16-byte vectors everywhere: every row of every
+// operand starts on a 16-byte line and the row length is a multiple of 16
+// bytes. SMS_FAST=0 turns it off (tests of the general kernels).
+bool fast_ok(int64_t Sk, int bytes) {
+  return ((Sk * bytes) & 15) == 0 && env_int("SMS_FAST", 1) != 0;
+}
+
+// Cache hints of the fast path: nontemporal loads of the streamed inputs and
+// nontemporal stores of the outputs (SMS_CACHE_POLICY overrides: bit 1 loads,
+// bit 2 stores).
+constexpr int kDefaultPolicy = sms::POL_NT_LOAD | sms::POL_NT_STORE;
+
 // Grid for `rows` rows at `tpr` lanes per row; false if it exceeds what one
 // dispatch can hold (2^31-1 workgroups, 2^32-1 work-items).
 bool grid_for(int64_t rows, int tpr, uint32_t& blocks) {
@@ -161,11 +192,10 @@ int64_t sms_max_sk(sms_dtype dtype) {
 }
 
 int sms_path(sms_dtype dtype, int64_t Sk, int backward) {
-  (void)backward;  // forward and backward share the choice
   const int bytes = dtype_bytes(dtype);
   if (!bytes || Sk < 0 || Sk > sms_max_sk(dtype)) return -1;
   Plan pl;
-  if (!choose_plan(vectors_per_row(Sk, 16 / bytes, true), pl)) return -1;
+  if (!choose_plan(vectors_per_row(Sk, 16 / bytes, true), backward != 0, pl)) return -1;
   return pl.tpr < 64 ? 0 : (pl.tpr == 64 ? 1 : 2);
 }
 
@@ -191,7 +221,7 @@ sms_status sms_forward(const void* x, const int64_t x_strides[4], const void* ma
   const int E = 16 / bytes;
   Plan pl;
   const bool aligned = rows_aligned16(x, x_strides, B, H, Sq, bytes);
-  if (!choose_plan(vectors_per_row(Sk, E, aligned), pl)) return SMS_ERR_SHAPE;
+  if (!choose_plan(vectors_per_row(Sk, E, aligned), false, pl)) return SMS_ERR_SHAPE;
 
   FwdParams p;
   p.x = static_cast<const char*>(x);
@@ -200,12 +230,11 @@ sms_status sms_forward(const void* x, const int64_t x_strides[4], const void* ma
   p.sx_b = x_strides[0]; p.sx_h = x_strides[1]; p.sx_q = x_strides[2];
   p.sy_b = y_strides[0]; p.sy_h = y_strides[1]; p.sy_q = y_strides[2];
   p.sm_b = p.sm_h = p.sm_q = 0;
-  int64_t mask_elems = 0;
   switch (mask_mode) {
-    case SMS_MASK_SQ_SK: p.sm_q = Sk; mask_elems = Sq * Sk; break;
-    case SMS_MASK_B_SQ_SK: p.sm_b = Sq * Sk; p.sm_q = Sk; mask_elems = B * Sq * Sk; break;
-    case SMS_MASK_B_1_SK: p.sm_b = Sk; mask_elems = B * Sk; break;
-    case SMS_MASK_FULL: p.sm_b = H * Sq * Sk; p.sm_h = Sq * Sk; p.sm_q = Sk; mask_elems = B * H * Sq * Sk; break;
+    case SMS_MASK_SQ_SK: p.sm_q = Sk; break;
+    case SMS_MASK_B_SQ_SK: p.sm_b = Sq * Sk; p.sm_q = Sk; break;
+    case SMS_MASK_B_1_SK: p.sm_b = Sk; break;
+    case SMS_MASK_FULL: p.sm_b = H * Sq * Sk; p.sm_h = Sq * Sk; p.sm_q = Sk; break;
     default: break;
   }
   p.scale = scale;
@@ -226,7 +255,7 @@ sms_status sms_forward(const void* x, const int64_t x_strides[4], const void* ma
   if (mask_mode == SMS_MASK_B_SQ_SK) { members = H; groups = B * Sq; order = sms::ORDER_HEADS; }
   if (mask_mode == SMS_MASK_SQ_SK) { members = B * H; groups = Sq; order = sms::ORDER_SAMPLES; }
   const int fo = forced_order();
-  const bool want = fo == 1 || (fo == -1 && mask_elems * bytes > kGroupedOrderMaskBytes);
+  const bool want = fo == 1;
   if (want && members > 1 && members % rpb == 0 && groups % kXcds == 0) {
     g.order = order;
     g.members = (uint32_t)members;
@@ -236,6 +265,18 @@ sms_status sms_forward(const void* x, const int64_t x_strides[4], const void* ma
   if (!grid_for(g.rows, pl.tpr, blocks)) return SMS_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
+  if (fast_ok(Sk, bytes) && aligned && rows_aligned16(y, y_strides, B, H, Sq, bytes) &&
+      (!has_mask || ((uintptr_t)mask & 15) == 0)) {
+    sms::FastFwdArgs fa;
+    fa.p = p;
+    fa.policy = env_int("SMS_CACHE_POLICY", kDefaultPolicy);
+    switch (dtype) {
+      case SMS_F32: e = sms_launch_fast_f32(&fa, nullptr, pl.tpr, pl.nv, blocks, s); break;
+      case SMS_F16: e = sms_launch_fast_f16(&fa, nullptr, pl.tpr, pl.nv, blocks, s); break;
+      default: e = sms_launch_fast_bf16(&fa, nullptr, pl.tpr, pl.nv, blocks, s); break;
+    }
+    return e == hipSuccess ? SMS_OK : SMS_ERR_HIP;
+  }
   switch (dtype) {
     case SMS_F32: e = sms_launch_fwd_f32(p, pl.tpr, pl.nv, blocks, s); break;
     case SMS_F16: e = sms_launch_fwd_f16(p, pl.tpr, pl.nv, blocks, s); break;
@@ -264,7 +305,7 @@ sms_status sms_backward(const void* y, const int64_t y_strides[4], const void* d
 
   Plan pl;
   const bool aligned = rows_aligned16(y, y_strides, B, H, Sq, bytes);
-  if (!choose_plan(vectors_per_row(Sk, 16 / bytes, aligned), pl)) return SMS_ERR_SHAPE;
+  if (!choose_plan(vectors_per_row(Sk, 16 / bytes, aligned), true, pl)) return SMS_ERR_SHAPE;
 
   BwdParams p;
   p.y = static_cast<const char*>(y);
@@ -286,6 +327,18 @@ sms_status sms_backward(const void* y, const int64_t y_strides[4], const void* d
   if (!grid_for(g.rows, pl.tpr, blocks)) return SMS_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
+  if (fast_ok(Sk, bytes) && aligned && rows_aligned16(dy, dy_strides, B, H, Sq, bytes) &&
+      rows_aligned16(dx, dx_strides, B, H, Sq, bytes)) {
+    sms::FastBwdArgs ba;
+    ba.p = p;
+    ba.policy = env_int("SMS_CACHE_POLICY", kDefaultPolicy);
+    switch (dtype) {
+      case SMS_F32: e = sms_launch_fast_f32(nullptr, &ba, pl.tpr, pl.nv, blocks, s); break;
+      case SMS_F16: e = sms_launch_fast_f16(nullptr, &ba, pl.tpr, pl.nv, blocks, s); break;
+      default: e = sms_launch_fast_bf16(nullptr, &ba, pl.tpr, pl.nv, blocks, s); break;
+    }
+    return e == hipSuccess ? SMS_OK : SMS_ERR_HIP;
+  }
   switch (dtype) {
     case SMS_F32: e = sms_launch_bwd_f32(p, pl.tpr, pl.nv, blocks, s); break;
     case SMS_F16: e = sms_launch_bwd_f16(p, pl.tpr, pl.nv, blocks, s); break;

@@ -10,3 +10,8 @@ hipError_t sms_launch_bwd_bf16(const sms::BwdParams& p, int tpr, int nv, uint32_
                              hipStream_t st) {
   return sms::launch_bwd<sms::Bf16>(p, tpr, nv, blocks, st);
 }
+
+hipError_t sms_launch_fast_bf16(const sms::FastFwdArgs* fa, const sms::FastBwdArgs* ba, int tpr,
+                              int nv, uint32_t blocks, hipStream_t st) {
+  return sms::launch_fast<sms::Bf16>(fa, ba, tpr, nv, blocks, st);
+}

@@ -10,3 +10,8 @@ hipError_t sms_launch_bwd_f16(const sms::BwdParams& p, int tpr, int nv, uint32_t
                              hipStream_t st) {
   return sms::launch_bwd<sms::Fp16>(p, tpr, nv, blocks, st);
 }
+
+hipError_t sms_launch_fast_f16(const sms::FastFwdArgs* fa, const sms::FastBwdArgs* ba, int tpr,
+                              int nv, uint32_t blocks, hipStream_t st) {
+  return sms::launch_fast<sms::Fp16>(fa, ba, tpr, nv, blocks, st);
+}

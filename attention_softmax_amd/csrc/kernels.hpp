@@ -40,29 +40,39 @@
 
 namespace sms {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
+
+// Exponentials are taken as 2^64 * exp(s - m) = v_exp_f32((s - m)*log2(e) + 64):
+// the bias rides in the same FMA, and it keeps every exponential that can
+// matter in the normal fp32 range (the hardware exp2 does not return
+// subnormals, while bf16 and fp32 outputs reach down to 2^-133 and 2^-149).
+// The row sum carries the same 2^64 (at most 2^64 * Sk, far from overflow),
+// so y = e' / sum' equals e / sum with the power of two cancelled exactly.
+constexpr float kExpBias = 64.0f;
+SMS_DEV float exp_biased(float s, float m) {
+  return __builtin_amdgcn_exp2f(fmaf(s - m, kLog2e, kExpBias));
+}
 
 // ----------------------------------------------------------------- formats
 
 struct Fp32 {
   static constexpr int kBytes = 4;
   static constexpr int kE = 4;  // elements per 16-byte vector
-  SMS_DEV static void unpack(const uint4& u, float (&f)[kE]) {
+  SMS_DEV static void unpack(const u32x4& u, float (&f)[kE]) {
     f[0] = __uint_as_float(u.x);
     f[1] = __uint_as_float(u.y);
     f[2] = __uint_as_float(u.z);
     f[3] = __uint_as_float(u.w);
   }
-  SMS_DEV static uint4 pack(const float (&f)[kE]) {
-    return uint4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+  SMS_DEV static u32x4 pack(const float (&f)[kE]) {
+    return u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
                  __float_as_uint(f[3])};
   }
   SMS_DEV static float ld(const char* p) { return *reinterpret_cast<const float*>(p); }
   SMS_DEV static void st(char* p, float v) { *reinterpret_cast<float*>(p) = v; }
-  // Outputs are fp32: a flushed subnormal exponential is below any fp32
-  // tolerance, so the bare hardware exp2 serves.
-  SMS_DEV static float exp2(float t) { return __builtin_amdgcn_exp2f(t); }
   // fp32 products are not exact in fp32: widen before multiplying.
   SMS_DEV static double prod(float a, float b) { return (double)a * (double)b; }
 };
@@ -71,7 +81,7 @@ struct Fp16 {
   static constexpr int kBytes = 2;
   static constexpr int kE = 8;
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  SMS_DEV static void unpack(const uint4& u, float (&f)[kE]) {
+  SMS_DEV static void unpack(const u32x4& u, float (&f)[kE]) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -80,7 +90,7 @@ struct Fp16 {
       f[2 * i + 1] = (float)h.y;
     }
   }
-  SMS_DEV static uint4 pack(const float (&f)[kE]) {
+  SMS_DEV static u32x4 pack(const float (&f)[kE]) {
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -89,12 +99,10 @@ struct Fp16 {
       h.y = (_Float16)f[2 * i + 1];
       w[i] = __builtin_bit_cast(uint32_t, h);
     }
-    return uint4{w[0], w[1], w[2], w[3]};
+    return u32x4{w[0], w[1], w[2], w[3]};
   }
   SMS_DEV static float ld(const char* p) { return (float)*reinterpret_cast<const _Float16*>(p); }
   SMS_DEV static void st(char* p, float v) { *reinterpret_cast<_Float16*>(p) = (_Float16)v; }
-  // The smallest fp16 subnormal (2^-24) is a normal fp32 number: bare exp2.
-  SMS_DEV static float exp2(float t) { return __builtin_amdgcn_exp2f(t); }
   // Product of two fp16 values (11-bit significands) is exact in fp32.
   SMS_DEV static double prod(float a, float b) { return (double)(a * b); }
 };
@@ -103,7 +111,7 @@ struct Bf16 {
   static constexpr int kBytes = 2;
   static constexpr int kE = 8;
   typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-  SMS_DEV static void unpack(const uint4& u, float (&f)[kE]) {
+  SMS_DEV static void unpack(const u32x4& u, float (&f)[kE]) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -111,7 +119,7 @@ struct Bf16 {
       f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   }
-  SMS_DEV static uint4 pack(const float (&f)[kE]) {
+  SMS_DEV static u32x4 pack(const float (&f)[kE]) {
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -120,15 +128,12 @@ struct Bf16 {
       b.y = (__bf16)f[2 * i + 1];
       w[i] = __builtin_bit_cast(uint32_t, b);
     }
-    return uint4{w[0], w[1], w[2], w[3]};
+    return u32x4{w[0], w[1], w[2], w[3]};
   }
   SMS_DEV static float ld(const char* p) {
     return __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t*>(p)) << 16);
   }
   SMS_DEV static void st(char* p, float v) { *reinterpret_cast<__bf16*>(p) = (__bf16)v; }
-  // bf16 shares fp32's exponent range, so bf16 outputs can be fp32 subnormals:
-  // use the library exp2f, which keeps subnormal results.
-  SMS_DEV static float exp2(float t) { return exp2f(t); }
   SMS_DEV static double prod(float a, float b) { return (double)(a * b); }  // exact
 };
 
@@ -327,7 +332,7 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int e = 0; e < E; ++e) s[j][e] = kNegInf;
     } else if (k0 >= 0 && k0 + E <= kload) {
-      const uint4 u = *reinterpret_cast<const uint4*>(xbase + (int64_t)v * 16);
+      const u32x4 u = *reinterpret_cast<const u32x4*>(xbase + (int64_t)v * 16);
       F::unpack(u, s[j]);
     } else {
 #pragma unroll
@@ -353,7 +358,7 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_fwd_kernel(FwdParams p) {
       if (k0 >= 0 && k0 + E <= kload) {
         float m[E];
         if (mvec) {
-          F::unpack(*reinterpret_cast<const uint4*>(mbase + (int64_t)v * 16), m);
+          F::unpack(*reinterpret_cast<const u32x4*>(mbase + (int64_t)v * 16), m);
         } else {
 #pragma unroll
           for (int e = 0; e < E; ++e) m[e] = F::ld(mrow + (int64_t)(k0 + e) * BY);
@@ -403,7 +408,7 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_fwd_kernel(FwdParams p) {
     } else {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        s[j][e] = F::exp2((s[j][e] - mref) * kLog2e);
+        s[j][e] = exp_biased(s[j][e], mref);
         sum += s[j][e];
       }
     }
@@ -421,7 +426,7 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int e = 0; e < E; ++e) o[e] = s[j][e] * inv;
     if (yvec && k0 >= 0 && k0 + E <= Sk) {
-      *reinterpret_cast<uint4*>(ybase + (int64_t)v * 16) = F::pack(o);
+      *reinterpret_cast<u32x4*>(ybase + (int64_t)v * 16) = F::pack(o);
     } else {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
@@ -479,9 +484,9 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_bwd_kernel(BwdParams p) {
 #pragma unroll
       for (int e = 0; e < E; ++e) yv[j][e] = gv[j][e] = 0.0f;
     } else if (k0 >= 0 && k0 + E <= kload) {
-      F::unpack(*reinterpret_cast<const uint4*>(ybase + (int64_t)v * 16), yv[j]);
+      F::unpack(*reinterpret_cast<const u32x4*>(ybase + (int64_t)v * 16), yv[j]);
       if (dvec) {
-        F::unpack(*reinterpret_cast<const uint4*>(dbase + (int64_t)v * 16), gv[j]);
+        F::unpack(*reinterpret_cast<const u32x4*>(dbase + (int64_t)v * 16), gv[j]);
       } else {
 #pragma unroll
         for (int e = 0; e < E; ++e) gv[j][e] = F::ld(drow + (int64_t)(k0 + e) * BY);
@@ -523,7 +528,7 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_bwd_kernel(BwdParams p) {
       for (int e = 0; e < E; ++e) o[e] = (yv[j][e] * scale) * ((gv[j][e] - dot_hi) - dot_lo);
     }
     if (xvec && k0 >= 0 && k0 + E <= Sk) {
-      *reinterpret_cast<uint4*>(xbase + (int64_t)v * 16) = F::pack(o);
+      *reinterpret_cast<u32x4*>(xbase + (int64_t)v * 16) = F::pack(o);
     } else {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
@@ -534,6 +539,263 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_bwd_kernel(BwdParams p) {
   }
 }
 
+
+// ------------------------------------------------ fast path: aligned rows
+//
+// When every row of every operand starts on a 16-byte line and Sk is a
+// multiple of E, every vector of a row is whole: no element accesses remain,
+// and the causal boundary inside a vector is a register select. One workgroup
+// per slot (RPB rows), launched once: short-lived workgroups dealt in order
+// keep the set of DRAM pages in use compact, which measured faster on MI355X
+// than a persistent grid with next-row prefetch.
+//
+// The score and output streams are touched once, so they are loaded and
+// stored with the nontemporal hint; the mask, which other rows read again,
+// goes through the caches normally.
+
+// Cache policy bits for the fast path: 1 = nontemporal x / y / dy loads,
+// 2 = nontemporal y / dx stores.
+enum : int { POL_NT_LOAD = 1, POL_NT_STORE = 2 };
+
+SMS_DEV u32x4 ld16(const char* p, bool nt) {
+  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+  return nt ? __builtin_nontemporal_load(q) : *q;
+}
+SMS_DEV void st16(char* p, u32x4 v, bool nt) {
+  u32x4* q = reinterpret_cast<u32x4*>(p);
+  if (nt) __builtin_nontemporal_store(v, q); else *q = v;
+}
+
+struct FastFwdArgs {
+  FwdParams p;
+  int policy;
+};
+
+struct FastRow {
+  const char* x;
+  const char* m;
+  char* y;
+  int kload;
+  bool valid;
+};
+
+template <class F, int RPB>
+SMS_DEV FastRow fast_fwd_row(const FwdParams& p, uint32_t slot, uint32_t local) {
+  FastRow r;
+  uint32_t b = 0, h = 0, q = 0;
+  r.valid = row_coords<RPB>(p.g, slot, local, b, h, q);
+  constexpr int BY = F::kBytes;
+  const int Sk = (int)p.g.Sk;
+  r.x = p.x + ((int64_t)b * p.sx_b + (int64_t)h * p.sx_h + (int64_t)q * p.sx_q) * BY;
+  r.y = p.y + ((int64_t)b * p.sy_b + (int64_t)h * p.sy_h + (int64_t)q * p.sy_q) * BY;
+  r.m = p.mask + ((int64_t)b * p.sm_b + (int64_t)h * p.sm_h + (int64_t)q * p.sm_q) * BY;
+  r.kload = !r.valid ? 0 : (p.causal ? (int)min((int64_t)q + 1, (int64_t)Sk) : Sk);
+  return r;
+}
+
+template <class F, int TPR, int NV>
+SMS_DEV void fast_fwd_load(const FwdParams& p, const FastRow& r, uint32_t lane, bool nt,
+                           u32x4 (&xr)[NV], u32x4 (&mr)[NV]) {
+  constexpr int E = F::kE;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int v = j * TPR + (int)lane;
+    if (v * E < r.kload) {
+      xr[j] = ld16(r.x + (int64_t)v * 16, nt);
+      if (p.has_mask) mr[j] = ld16(r.m + (int64_t)v * 16, false);
+    }
+  }
+}
+
+template <class F, int TPR, int NV>
+SMS_DEV void fast_fwd_compute(const FwdParams& p, const FastRow& r, uint32_t lane, bool nt,
+                              const u32x4 (&xr)[NV], const u32x4 (&mr)[NV], float* smax,
+                              float* ssum) {
+  constexpr int E = F::kE;
+  const int Sk = (int)p.g.Sk;
+  const int kload = r.kload;
+  const float scale = p.scale;
+  float s[NV][E];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int k0 = (j * TPR + (int)lane) * E;
+    if (k0 < kload) {
+      F::unpack(xr[j], s[j]);
+      if (p.has_mask) {
+        float m[E];
+        F::unpack(mr[j], m);
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[j][e] = fmaf(s[j][e], scale, m[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[j][e] *= scale;
+      }
+      if (k0 + E > kload) {  // the vector that holds the causal boundary
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (k0 + e >= kload) s[j][e] = kNegInf;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) s[j][e] = kNegInf;
+    }
+  }
+  float mx = kNegInf;
+#pragma unroll
+  for (int j = 0; j < NV; ++j)
+#pragma unroll
+    for (int e = 0; e < E; ++e) mx = fmaxf(mx, s[j][e]);
+  mx = row_reduce<TPR>(mx, OpMax(), smax);
+  const float mref = (mx == kNegInf) ? 0.0f : mx;
+  float sum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int k0 = (j * TPR + (int)lane) * E;
+    if (k0 < kload) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        s[j][e] = exp_biased(s[j][e], mref);
+        sum += s[j][e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) s[j][e] = 0.0f;
+    }
+  }
+  sum = row_reduce<TPR>(sum, OpAdd(), ssum);
+  const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int v = j * TPR + (int)lane;
+    if (v * E < Sk) {
+      float o[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] = s[j][e] * inv;
+      st16(r.y + (int64_t)v * 16, F::pack(o), nt);
+    }
+  }
+}
+
+template <class F, int TPR, int NV>
+__global__ void __launch_bounds__(block_of(TPR)) sms_fwd_fast_kernel(FastFwdArgs a) {
+  constexpr int RPB = block_of(TPR) / TPR;
+  constexpr int W = TPR > 64 ? TPR / 64 : 1;
+  __shared__ float red[2][W];
+  const uint32_t lane = threadIdx.x % TPR;
+  const FastRow r = fast_fwd_row<F, RPB>(a.p, blockIdx.x, threadIdx.x / TPR);
+  if (!r.valid) return;  // only a tail group of a TPR <= 64 launch, which has no barrier
+  u32x4 xr[NV], mr[NV];
+  fast_fwd_load<F, TPR, NV>(a.p, r, lane, (a.policy & POL_NT_LOAD) != 0, xr, mr);
+  fast_fwd_compute<F, TPR, NV>(a.p, r, lane, (a.policy & POL_NT_STORE) != 0, xr, mr, red[0],
+                               red[1]);
+}
+
+struct FastBwdArgs {
+  BwdParams p;
+  int policy;
+};
+
+struct FastBwdRow {
+  const char* y;
+  const char* d;
+  char* x;
+  int kload;
+  bool valid;
+};
+
+template <class F, int RPB>
+SMS_DEV FastBwdRow fast_bwd_row(const BwdParams& p, uint32_t slot, uint32_t local) {
+  FastBwdRow r;
+  uint32_t b = 0, h = 0, q = 0;
+  r.valid = row_coords<RPB>(p.g, slot, local, b, h, q);
+  constexpr int BY = F::kBytes;
+  const int Sk = (int)p.g.Sk;
+  r.y = p.y + ((int64_t)b * p.sy_b + (int64_t)h * p.sy_h + (int64_t)q * p.sy_q) * BY;
+  r.d = p.dy + ((int64_t)b * p.sd_b + (int64_t)h * p.sd_h + (int64_t)q * p.sd_q) * BY;
+  r.x = p.dx + ((int64_t)b * p.sx_b + (int64_t)h * p.sx_h + (int64_t)q * p.sx_q) * BY;
+  r.kload = !r.valid ? 0 : (p.causal ? (int)min((int64_t)q + 1, (int64_t)Sk) : Sk);
+  return r;
+}
+
+template <class F, int TPR, int NV>
+SMS_DEV void fast_bwd_load(const FastBwdRow& r, uint32_t lane, bool nt, u32x4 (&yr)[NV],
+                           u32x4 (&dr)[NV]) {
+  constexpr int E = F::kE;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int v = j * TPR + (int)lane;
+    if (v * E < r.kload) {
+      yr[j] = ld16(r.y + (int64_t)v * 16, nt);
+      dr[j] = ld16(r.d + (int64_t)v * 16, nt);
+    }
+  }
+}
+
+template <class F, int TPR, int NV>
+SMS_DEV void fast_bwd_compute(const BwdParams& p, const FastBwdRow& r, uint32_t lane, bool nt,
+                              const u32x4 (&yr)[NV], const u32x4 (&dr)[NV], double* red) {
+  constexpr int E = F::kE;
+  const int Sk = (int)p.g.Sk;
+  const int kload = r.kload;
+  double acc = 0.0;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int k0 = (j * TPR + (int)lane) * E;
+    if (k0 < kload) {
+      float yv[E], gv[E];
+      F::unpack(yr[j], yv);
+      F::unpack(dr[j], gv);
+      if (k0 + E > kload) {  // keys past the causal boundary are not used
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (k0 + e >= kload) yv[e] = 0.0f;
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc += F::prod(yv[e], gv[e]);
+    }
+  }
+  acc = row_reduce<TPR>(acc, OpAdd(), red);
+  const float dot_hi = (float)acc;
+  const float dot_lo = (float)(acc - (double)dot_hi);
+  const float scale = p.scale;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int v = j * TPR + (int)lane;
+    const int k0 = v * E;
+    if (k0 < Sk) {
+      float o[E];
+      if (k0 < kload) {
+        float yv[E], gv[E];
+        F::unpack(yr[j], yv);
+        F::unpack(dr[j], gv);
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = (yv[e] * scale) * ((gv[e] - dot_hi) - dot_lo);
+        if (k0 + E > kload) {
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            if (k0 + e >= kload) o[e] = 0.0f;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = 0.0f;
+      }
+      st16(r.x + (int64_t)v * 16, F::pack(o), nt);
+    }
+  }
+}
+
+template <class F, int TPR, int NV>
+__global__ void __launch_bounds__(block_of(TPR)) sms_bwd_fast_kernel(FastBwdArgs a) {
+  constexpr int RPB = block_of(TPR) / TPR;
+  constexpr int W = TPR > 64 ? TPR / 64 : 1;
+  __shared__ double red[W];
+  const uint32_t lane = threadIdx.x % TPR;
+  const FastBwdRow r = fast_bwd_row<F, RPB>(a.p, blockIdx.x, threadIdx.x / TPR);
+  if (!r.valid) return;
+  u32x4 yr[NV], dr[NV];
+  fast_bwd_load<F, TPR, NV>(r, lane, (a.policy & POL_NT_LOAD) != 0, yr, dr);
+  fast_bwd_compute<F, TPR, NV>(a.p, r, lane, (a.policy & POL_NT_STORE) != 0, yr, dr, red);
+}
 // --------------------------------------------------------------- launchers
 
 // TPR and NV values the library is built with.
@@ -562,6 +824,50 @@ hipError_t launch_bwd_tpr(const BwdParams& p, int nv, uint32_t blocks, hipStream
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <class F, int TPR, int NV>
+hipError_t launch_fwd_fast_nv(const FastFwdArgs& a, uint32_t blocks, hipStream_t st) {
+  hipLaunchKernelGGL((sms_fwd_fast_kernel<F, TPR, NV>), dim3(blocks), dim3(block_of(TPR)), 0, st, a);
+  return hipGetLastError();
+}
+
+template <class F, int TPR, int NV>
+hipError_t launch_bwd_fast_nv(const FastBwdArgs& a, uint32_t blocks, hipStream_t st) {
+  hipLaunchKernelGGL((sms_bwd_fast_kernel<F, TPR, NV>), dim3(blocks), dim3(block_of(TPR)), 0, st, a);
+  return hipGetLastError();
+}
+
+template <class F, int TPR>
+hipError_t launch_fast_tpr(const FastFwdArgs* fa, const FastBwdArgs* ba, int nv, uint32_t blocks,
+                           hipStream_t st) {
+  switch (nv) {
+    case 1: return fa ? launch_fwd_fast_nv<F, TPR, 1>(*fa, blocks, st)
+                      : launch_bwd_fast_nv<F, TPR, 1>(*ba, blocks, st);
+    case 2: return fa ? launch_fwd_fast_nv<F, TPR, 2>(*fa, blocks, st)
+                      : launch_bwd_fast_nv<F, TPR, 2>(*ba, blocks, st);
+    case 4: return fa ? launch_fwd_fast_nv<F, TPR, 4>(*fa, blocks, st)
+                      : launch_bwd_fast_nv<F, TPR, 4>(*ba, blocks, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Fast path (aligned rows): exactly one of fa / ba is non-null.
+template <class F>
+hipError_t launch_fast(const FastFwdArgs* fa, const FastBwdArgs* ba, int tpr, int nv,
+                       uint32_t blocks, hipStream_t st) {
+  switch (tpr) {
+    case 4: return launch_fast_tpr<F, 4>(fa, ba, nv, blocks, st);
+    case 8: return launch_fast_tpr<F, 8>(fa, ba, nv, blocks, st);
+    case 16: return launch_fast_tpr<F, 16>(fa, ba, nv, blocks, st);
+    case 32: return launch_fast_tpr<F, 32>(fa, ba, nv, blocks, st);
+    case 64: return launch_fast_tpr<F, 64>(fa, ba, nv, blocks, st);
+    case 128: return launch_fast_tpr<F, 128>(fa, ba, nv, blocks, st);
+    case 256: return launch_fast_tpr<F, 256>(fa, ba, nv, blocks, st);
+    case 512: return launch_fast_tpr<F, 512>(fa, ba, nv, blocks, st);
+    case 1024: return launch_fast_tpr<F, 1024>(fa, ba, nv, blocks, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <class F>
@@ -605,3 +911,9 @@ hipError_t sms_launch_fwd_bf16(const sms::FwdParams&, int tpr, int nv, uint32_t 
 hipError_t sms_launch_bwd_f32(const sms::BwdParams&, int tpr, int nv, uint32_t blocks, hipStream_t);
 hipError_t sms_launch_bwd_f16(const sms::BwdParams&, int tpr, int nv, uint32_t blocks, hipStream_t);
 hipError_t sms_launch_bwd_bf16(const sms::BwdParams&, int tpr, int nv, uint32_t blocks, hipStream_t);
+hipError_t sms_launch_fast_f32(const sms::FastFwdArgs*, const sms::FastBwdArgs*, int tpr, int nv,
+                               uint32_t blocks, hipStream_t);
+hipError_t sms_launch_fast_f16(const sms::FastFwdArgs*, const sms::FastBwdArgs*, int tpr, int nv,
+                               uint32_t blocks, hipStream_t);
+hipError_t sms_launch_fast_bf16(const sms::FastFwdArgs*, const sms::FastBwdArgs*, int tpr, int nv,
+                                uint32_t blocks, hipStream_t);

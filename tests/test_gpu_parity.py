@@ -108,11 +108,14 @@ SMALL = {1: (1, 2, 64, 64), 2: (2, 4, 64, 1024), 3: (1, 2, 2048, 2048),
          4: (1, 2, 4096, 4096), 5: (2, 2, 1000, 1000)}
 
 
+@pytest.mark.parametrize("fast", ["1", "0"])
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
-def test_workload_recipe_small(cfg):
+def test_workload_recipe_small(cfg, fast, monkeypatch):
     """Each workload's recipe (dtype, distributions, mask mode, causal, scale) at
-    a size the oracle covers on every row; forward and backward."""
-    say(f"workload {cfg} small shape {SMALL[cfg]}")
+    a size the oracle covers on every row; forward and backward; through the
+    aligned-row persistent kernels (fast=1) and the general kernels (fast=0)."""
+    monkeypatch.setenv("SMS_FAST", fast)
+    say(f"workload {cfg} small shape {SMALL[cfg]} fast={fast}")
     w = make_config(cfg, DEV, shape=SMALL[cfg], with_dy=True)
     x, mask, mode, dt = w["x"], w["mask"], w["mode"], w["dtype"]
     y = fwd(x, mask, w["scale"], w["causal"])
@@ -241,13 +244,17 @@ def test_permuted_strides_and_in_place(dtype):
 
 # ------------------------------------------------------ forced kernel shapes
 
+@pytest.mark.parametrize("aligned", [False, True])
 @pytest.mark.parametrize("tpr", [4, 8, 16, 32, 64, 128, 256, 512, 1024])
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
-def test_every_lanes_per_row(tpr, dtype, monkeypatch):
+def test_every_lanes_per_row(tpr, dtype, aligned, monkeypatch):
     """Each row width (rows per wave, one wave, 2..16 waves per row) on a row
-    length it can hold, against the oracle."""
+    length it can hold, against the oracle: an odd length (general kernels) and
+    a whole number of 16-byte vectors (persistent aligned-row kernels)."""
     E = 4 if dtype == "f32" else 8
     Sk = min(4 * tpr * E - E + 1, 3 * tpr * E + 5)
+    if aligned:
+        Sk = 3 * tpr * E + E
     say(f"forced TPR={tpr} dtype={dtype} Sk={Sk}")
     monkeypatch.setenv("SMS_FORCE_TPR", str(tpr))
     shape = (1, 3, 5, Sk)
