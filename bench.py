@@ -16,9 +16,12 @@ diagnostics on stderr.
 """
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
-import math
 import os
+import statistics
 import sys
 import time
 
@@ -27,6 +30,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_KERNEL = "__amd_rocclr_copyBuffer"  # torch's device copy, timed as the copy reference
 
 
 def log(*a):
@@ -70,9 +75,105 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the oracle CPU baseline sample (0 = skip)")
     ap.add_argument("--no-copy", action="store_true", help="skip the plain-copy reference")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON file with rocprofv3 FETCH/WRITE bytes per launch (profiles/)")
+    ap.add_argument("--traffic", default=TRAFFIC_JSON,
+                    help="HBM bytes per launch from rocprofv3 counters (see --ingest)")
+    ap.add_argument("--ingest", default=None, metavar="DIR",
+                    help="read rocprofv3 output under DIR (kt/, fetch/, write/) of a run of "
+                         "this script, update --traffic and print a summary; no GPU work")
     return ap.parse_args()
+
+
+def csrc_sha():
+    """Hash of the kernel sources: counters taken on other sources are stale."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "attention_softmax_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "sms.h"))
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _kernel_role(name):
+    if "sms_fwd" in name:
+        return "forward"
+    if "sms_bwd" in name:
+        return "backward"
+    if COPY_KERNEL in name:
+        return "copy"
+    return None
+
+
+def ingest(args):
+    """Counters of one bench run -> HBM bytes per launch of each kernel.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch, from two --pmc runs) are scaled
+    by what they read for the plain copy kernel of known size in the same run
+    (copy_reference moves n bytes each way).
+    """
+    d = args.ingest
+    stats = glob.glob(os.path.join(d, "kt", "*kernel_stats.csv"))
+    trace_json = glob.glob(os.path.join(d, "kt_bench.json"))
+    run = json.load(open(trace_json[0])) if trace_json else None
+    avg = {}
+    for row in csv.DictReader(open(stats[0])):
+        role = _kernel_role(row["Name"])
+        if role:
+            avg[role] = (row["Name"], int(row["Calls"]), float(row["AverageNs"]) / 1e3)
+
+    def counter(sub):
+        vals = {}
+        for f in glob.glob(os.path.join(d, sub, "*counter_collection.csv")):
+            for row in csv.DictReader(open(f)):
+                role = _kernel_role(row["Kernel_Name"])
+                if role:
+                    vals.setdefault(role, []).append(float(row["Counter_Value"]) * 1024.0)
+        return {k: statistics.median(v) for k, v in vals.items()}
+
+    fetch, write = counter("fetch"), counter("write")
+    copy_bytes = run["copy_reference"]["bytes"] // 2 if run else None
+    fscale = copy_bytes / fetch["copy"] if copy_bytes and fetch.get("copy") else None
+    wscale = copy_bytes / write["copy"] if copy_bytes and write.get("copy") else None
+    wl = run["config"]["workload"] if run else "?"
+    key_wl = args.workload
+    table = json.load(open(args.traffic)) if os.path.exists(args.traffic) else {}
+    table.setdefault("workloads", {})
+    sha = csrc_sha()
+    lines = [f"workload {key_wl}: {wl}",
+             f"copy kernel {COPY_KERNEL}: {copy_bytes} B each way; FETCH_SIZE scale "
+             f"{fscale:.4f}, WRITE_SIZE scale {wscale:.4f}" if fscale and wscale else "no copy",
+             "", "| kernel | calls | avg us (rocprofv3) | avg us (HIP events) | algorithmic B | "
+             "FETCH B (scaled) | WRITE B (scaled) | traffic / algorithmic |", "|---|---|---|---|---|---|---|---|"]
+    for role in ("forward", "backward"):
+        if role not in avg:
+            continue
+        name, calls, us = avg[role]
+        f_b = fetch.get(role, 0.0) * (fscale or 1.0)
+        w_b = write.get(role, 0.0) * (wscale or 1.0)
+        alg = run["kernels"][role]["bytes"] if run else None
+        ev = run["kernels"][role]["avg_us"] if run else None
+        table["workloads"][f"{key_wl}_{role}"] = {
+            "kernel": name, "fetch_bytes": round(f_b), "write_bytes": round(w_b),
+            "traffic": round(f_b + w_b), "algorithmic_bytes": alg, "rocprof_avg_us": round(us, 2),
+            "fetch_scale": fscale, "write_scale": wscale, "csrc_sha": sha}
+        ratio = (f_b + w_b) / alg if alg else float("nan")
+        lines.append(f"| `{name}` | {calls} | {us:.2f} | {ev} | {alg} | {f_b:.0f} | {w_b:.0f} | "
+                     f"{ratio:.4f} |")
+    os.makedirs(os.path.dirname(args.traffic), exist_ok=True)
+    with open(args.traffic, "w") as fh:
+        json.dump(table, fh, indent=1, sort_keys=True)
+    print("\n".join(lines))
+
+
+def load_traffic(path, workload, role):
+    """Traffic bytes per launch if measured on the current kernel sources, else None."""
+    if not path or not os.path.exists(path):
+        return None
+    e = json.load(open(path)).get("workloads", {}).get(f"{workload}_{role}")
+    if not e or e.get("csrc_sha") != csrc_sha():
+        return None
+    return e["traffic"]
 
 
 def cpu_baseline(w, y, dy, step_bytes, rows_total, budget_s):
@@ -112,6 +213,9 @@ def cpu_baseline(w, y, dy, step_bytes, rows_total, budget_s):
 
 def main():
     args = parse()
+    if args.ingest:
+        ingest(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): rows are "
               "independent, so a multi-GPU run is the same kernel on each GPU's share", file=sys.stderr)
@@ -175,13 +279,7 @@ def main():
         k["frac_hbm_peak"] = round(k["GBps"] / HBM_PEAK_GBPS, 4)
     dom = "forward" if fwd_ms >= bwd_ms else "backward"
 
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            t = json.load(f)
-        key = f"workload{args.workload}_{dom}"
-        if key in t:
-            traffic = t[key]
+    traffic = load_traffic(args.traffic, args.workload, dom)
 
     copy = None
     if not args.no_copy:
