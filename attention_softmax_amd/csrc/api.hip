@@ -12,6 +12,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "kernels.hpp"
 #include "sms.h"
 
@@ -23,6 +25,8 @@ using sms::RowGeom;
 
 // Workgroups are dealt round-robin over the XCDs of an MI355X.
 constexpr uint32_t kXcds = 8;
+// Query rows per group in a grouped row order (SMS_QBLOCK overrides).
+constexpr int kDefaultQBlock = 16;
 // The grouped row order (rows sharing a mask row on one XCD, back to back) is
 // available on request (SMS_ORDER=grouped); by default rows run in memory
 // order, which measured faster on MI355X even for a 128 MB [B,Sq,Sk] mask:
@@ -247,18 +251,23 @@ sms_status sms_forward(const void* x, const int64_t x_strides[4], const void* ma
   g.order = sms::ORDER_ROWS;
   g.xcds = kXcds;
   g.members = 1;
+  g.qblock = 1;
 
-  // Grouped order: rows that read the same mask row run back to back on one XCD.
+  // Grouped order: rows that read the same block of mask rows run back to back
+  // on one XCD.
   const int rpb = sms::block_of(pl.tpr) / pl.tpr;
+  const int64_t Q = std::max(1, env_int("SMS_QBLOCK", kDefaultQBlock));
   int64_t members = 0, groups = 0;
   uint32_t order = sms::ORDER_ROWS;
-  if (mask_mode == SMS_MASK_B_SQ_SK) { members = H; groups = B * Sq; order = sms::ORDER_HEADS; }
-  if (mask_mode == SMS_MASK_SQ_SK) { members = B * H; groups = Sq; order = sms::ORDER_SAMPLES; }
+  if (mask_mode == SMS_MASK_B_SQ_SK) { members = H * Q; groups = B * (Sq / Q); order = sms::ORDER_HEADS; }
+  if (mask_mode == SMS_MASK_SQ_SK) { members = B * H * Q; groups = Sq / Q; order = sms::ORDER_SAMPLES; }
   const int fo = forced_order();
   const bool want = fo == 1;
-  if (want && members > 1 && members % rpb == 0 && groups % kXcds == 0) {
+  if (want && members > 1 && Sq % Q == 0 && members % rpb == 0 && groups > 0 &&
+      groups % kXcds == 0 && members <= UINT32_MAX) {
     g.order = order;
     g.members = (uint32_t)members;
+    g.qblock = (uint32_t)Q;
   }
 
   uint32_t blocks = 0;
@@ -322,6 +331,7 @@ sms_status sms_backward(const void* y, const int64_t y_strides[4], const void* d
   g.order = sms::ORDER_ROWS;
   g.xcds = kXcds;
   g.members = 1;
+  g.qblock = 1;
 
   uint32_t blocks = 0;
   if (!grid_for(g.rows, pl.tpr, blocks)) return SMS_ERR_SHAPE;

@@ -239,11 +239,12 @@ SMS_DEV T row_reduce(T v, Op op, T* slots) {
 // -------------------------------------------------------------- row mapping
 
 // Row order. ORDER_ROWS: flat row r -> (b, h, q) with q fastest. The grouped
-// orders put the rows that share one mask row on consecutive workgroups of the
-// same XCD (workgroup w runs on XCD w % xcds), so the mask row is fetched from
-// HBM once and then hits that XCD's L2:
-//   ORDER_HEADS:   group (b, q), members h      (mask [B,Sq,Sk])
-//   ORDER_SAMPLES: group q, members (b, h)      (mask [Sq,Sk])
+// orders put the rows that read one block of Q mask rows on consecutive
+// workgroups of the same XCD (workgroup w runs on XCD w % xcds), so the block
+// is fetched once and then hits that XCD's L2; inside a group each head takes
+// Q consecutive rows, which keeps the x / y streams contiguous in Q-row runs:
+//   ORDER_HEADS:   group (b, query block), members (h, q in block)    (mask [B,Sq,Sk])
+//   ORDER_SAMPLES: group (query block), members (b, h, q in block)    (mask [Sq,Sk])
 enum : uint32_t { ORDER_ROWS = 0, ORDER_HEADS = 1, ORDER_SAMPLES = 2 };
 
 struct RowGeom {
@@ -252,6 +253,7 @@ struct RowGeom {
   uint32_t order;    // ORDER_*
   uint32_t xcds;     // XCDs the workgroups are dealt over
   uint32_t members;  // rows per group in a grouped order
+  uint32_t qblock;   // query rows per group in a grouped order (divides Sq)
 };
 
 template <int RPB>
@@ -266,21 +268,25 @@ SMS_DEV bool row_coords(const RowGeom& g, uint32_t w, uint32_t local, uint32_t& 
     b = t / g.H;
     return true;
   }
-  // The host only picks a grouped order when members % RPB == 0 and the number
-  // of groups is a multiple of xcds, so every workgroup maps to real rows.
+  // The host only picks a grouped order when members % RPB == 0, Sq % qblock
+  // == 0 and the number of groups is a multiple of xcds, so every workgroup
+  // maps to one real row per local index.
   const uint32_t xcd = w % g.xcds;
   const uint32_t s = w / g.xcds;
   const uint32_t bpg = g.members / RPB;  // workgroups per group
   const uint32_t grp = (s / bpg) * g.xcds + xcd;
   const uint32_t m = (s % bpg) * RPB + local;
+  const uint32_t qi = m % g.qblock;
+  const uint32_t mm = m / g.qblock;
+  const uint32_t nqb = g.Sq / g.qblock;
   if (g.order == ORDER_HEADS) {
-    b = grp / g.Sq;
-    q = grp % g.Sq;
-    h = m;
+    b = grp / nqb;
+    q = (grp % nqb) * g.qblock + qi;
+    h = mm;
   } else {
-    q = grp;
-    b = m / g.H;
-    h = m % g.H;
+    q = grp * g.qblock + qi;
+    b = mm / g.H;
+    h = mm % g.H;
   }
   return true;
 }

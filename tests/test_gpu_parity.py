@@ -277,10 +277,12 @@ def test_forced_width_too_small_is_an_error(monkeypatch):
         sms_forward(x, None, torch.empty_like(x))
 
 
-@pytest.mark.parametrize("order", ["rows", "grouped"])
-def test_row_orders_agree(order, monkeypatch):
-    """The XCD-grouped row order is a permutation of rows: identical bits."""
+@pytest.mark.parametrize("order,qblock", [("rows", 1), ("grouped", 1), ("grouped", 4),
+                                          ("grouped", 16)])
+def test_row_orders_agree(order, qblock, monkeypatch):
+    """The XCD-grouped row orders are permutations of rows: identical bits."""
     monkeypatch.setenv("SMS_ORDER", order)
+    monkeypatch.setenv("SMS_QBLOCK", str(qblock))
     for Sk, mode in ((2048, "b_sq_sk"), (4096, "b_sq_sk"), (2048, "sq_sk"), (4096, "sq_sk")):
         shape = (2, 4, 64, Sk)  # 4 heads: a multiple of the rows per workgroup
         x = draw_x(shape, "f16", ("normal", 8.0), 1, DEV)
