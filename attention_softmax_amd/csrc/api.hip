@@ -42,8 +42,11 @@ int dtype_bytes(sms_dtype d) {
   }
 }
 
-// Largest vectors-per-row a (TPR, NV) pair in the build covers.
+// Largest vectors-per-row a (TPR, NV) pair in the build covers; longer rows
+// take the streaming kernels (one workgroup per row, two passes).
 constexpr int64_t kMaxVecPerRow = 1024 * 4;
+// Longest row: keeps every in-kernel element index far inside int32.
+constexpr int64_t kMaxSk = int64_t(1) << 30;
 
 // Optional override of the lanes per row, for tests and tuning:
 // SMS_FORCE_TPR=<4..1024>. Unset or 0 = automatic.
@@ -151,6 +154,12 @@ bool fast_ok(int64_t Sk, int bytes) {
   return ((Sk * bytes) & 15) == 0 && env_int("SMS_FAST", 1) != 0;
 }
 
+// Rows beyond the register-resident kernels' reach stream; SMS_FORCE_STREAM=1
+// sends every row there (tests of the streaming kernels on short rows).
+bool use_stream(int64_t nvec) {
+  return nvec > kMaxVecPerRow || env_int("SMS_FORCE_STREAM", 0) != 0;
+}
+
 // Cache hints of the fast path: nontemporal loads of the streamed inputs and
 // nontemporal stores of the outputs (SMS_CACHE_POLICY overrides: bit 1 loads,
 // bit 2 stores).
@@ -187,19 +196,15 @@ const char* sms_status_str(sms_status s) {
   }
 }
 
-int64_t sms_max_sk(sms_dtype dtype) {
-  const int bytes = dtype_bytes(dtype);
-  if (!bytes) return 0;
-  const int E = 16 / bytes;
-  // Any alignment: ceil((Sk + E - 1)/E) <= kMaxVecPerRow.
-  return kMaxVecPerRow * E - (E - 1);
-}
+int64_t sms_max_sk(sms_dtype dtype) { return dtype_bytes(dtype) ? kMaxSk : 0; }
 
 int sms_path(sms_dtype dtype, int64_t Sk, int backward) {
   const int bytes = dtype_bytes(dtype);
-  if (!bytes || Sk < 0 || Sk > sms_max_sk(dtype)) return -1;
+  if (!bytes || Sk < 0 || Sk > kMaxSk) return -1;
+  const int64_t nvec = vectors_per_row(Sk, 16 / bytes, true);
+  if (use_stream(nvec)) return 3;
   Plan pl;
-  if (!choose_plan(vectors_per_row(Sk, 16 / bytes, true), backward != 0, pl)) return -1;
+  if (!choose_plan(nvec, backward != 0, pl)) return -1;
   return pl.tpr < 64 ? 0 : (pl.tpr == 64 ? 1 : 2);
 }
 
@@ -220,12 +225,19 @@ sms_status sms_forward(const void* x, const int64_t x_strides[4], const void* ma
   const int bytes = dtype_bytes(dtype);
   if (!aligned_to(x, bytes) || !aligned_to(y, bytes) || (has_mask && !aligned_to(mask, bytes)))
     return SMS_ERR_ALIGN;
-  if (Sk > sms_max_sk(dtype)) return SMS_ERR_SHAPE;
+  if (Sk > kMaxSk) return SMS_ERR_SHAPE;
 
   const int E = 16 / bytes;
-  Plan pl;
   const bool aligned = rows_aligned16(x, x_strides, B, H, Sq, bytes);
-  if (!choose_plan(vectors_per_row(Sk, E, aligned), false, pl)) return SMS_ERR_SHAPE;
+  const int64_t nvec = vectors_per_row(Sk, E, aligned);
+  const bool streaming = use_stream(nvec);
+  Plan pl;
+  if (streaming) {
+    pl.tpr = sms::kStreamTpr;
+    pl.nv = 0;
+  } else if (!choose_plan(nvec, false, pl)) {
+    return SMS_ERR_SHAPE;
+  }
 
   FwdParams p;
   p.x = static_cast<const char*>(x);
@@ -274,6 +286,15 @@ sms_status sms_forward(const void* x, const int64_t x_strides[4], const void* ma
   if (!grid_for(g.rows, pl.tpr, blocks)) return SMS_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
+  if (streaming) {
+    g.order = sms::ORDER_ROWS;
+    switch (dtype) {
+      case SMS_F32: e = sms_launch_stream_f32(&p, nullptr, blocks, s); break;
+      case SMS_F16: e = sms_launch_stream_f16(&p, nullptr, blocks, s); break;
+      default: e = sms_launch_stream_bf16(&p, nullptr, blocks, s); break;
+    }
+    return e == hipSuccess ? SMS_OK : SMS_ERR_HIP;
+  }
   if (fast_ok(Sk, bytes) && aligned && rows_aligned16(y, y_strides, B, H, Sq, bytes) &&
       (!has_mask || ((uintptr_t)mask & 15) == 0)) {
     sms::FastFwdArgs fa;
@@ -310,11 +331,18 @@ sms_status sms_backward(const void* y, const int64_t y_strides[4], const void* d
   const int bytes = dtype_bytes(dtype);
   if (!aligned_to(y, bytes) || !aligned_to(dy, bytes) || !aligned_to(dx, bytes))
     return SMS_ERR_ALIGN;
-  if (Sk > sms_max_sk(dtype)) return SMS_ERR_SHAPE;
+  if (Sk > kMaxSk) return SMS_ERR_SHAPE;
 
-  Plan pl;
   const bool aligned = rows_aligned16(y, y_strides, B, H, Sq, bytes);
-  if (!choose_plan(vectors_per_row(Sk, 16 / bytes, aligned), true, pl)) return SMS_ERR_SHAPE;
+  const int64_t nvec = vectors_per_row(Sk, 16 / bytes, aligned);
+  const bool streaming = use_stream(nvec);
+  Plan pl;
+  if (streaming) {
+    pl.tpr = sms::kStreamTpr;
+    pl.nv = 0;
+  } else if (!choose_plan(nvec, true, pl)) {
+    return SMS_ERR_SHAPE;
+  }
 
   BwdParams p;
   p.y = static_cast<const char*>(y);
@@ -337,6 +365,14 @@ sms_status sms_backward(const void* y, const int64_t y_strides[4], const void* d
   if (!grid_for(g.rows, pl.tpr, blocks)) return SMS_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
+  if (streaming) {
+    switch (dtype) {
+      case SMS_F32: e = sms_launch_stream_f32(nullptr, &p, blocks, s); break;
+      case SMS_F16: e = sms_launch_stream_f16(nullptr, &p, blocks, s); break;
+      default: e = sms_launch_stream_bf16(nullptr, &p, blocks, s); break;
+    }
+    return e == hipSuccess ? SMS_OK : SMS_ERR_HIP;
+  }
   if (fast_ok(Sk, bytes) && aligned && rows_aligned16(dy, dy_strides, B, H, Sq, bytes) &&
       rows_aligned16(dx, dx_strides, B, H, Sq, bytes)) {
     sms::FastBwdArgs ba;

@@ -15,3 +15,8 @@ hipError_t sms_launch_fast_bf16(const sms::FastFwdArgs* fa, const sms::FastBwdAr
                               int nv, uint32_t blocks, hipStream_t st) {
   return sms::launch_fast<sms::Bf16>(fa, ba, tpr, nv, blocks, st);
 }
+
+hipError_t sms_launch_stream_bf16(const sms::FwdParams* fp, const sms::BwdParams* bp, uint32_t rows,
+                                    hipStream_t st) {
+  return sms::launch_stream<sms::Bf16>(fp, bp, rows, st);
+}

@@ -15,3 +15,8 @@ hipError_t sms_launch_fast_f32(const sms::FastFwdArgs* fa, const sms::FastBwdArg
                               int nv, uint32_t blocks, hipStream_t st) {
   return sms::launch_fast<sms::Fp32>(fa, ba, tpr, nv, blocks, st);
 }
+
+hipError_t sms_launch_stream_f32(const sms::FwdParams* fp, const sms::BwdParams* bp, uint32_t rows,
+                                   hipStream_t st) {
+  return sms::launch_stream<sms::Fp32>(fp, bp, rows, st);
+}

@@ -802,6 +802,259 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_bwd_fast_kernel(FastBwdArgs
   fast_bwd_load<F, TPR, NV>(r, lane, (a.policy & POL_NT_LOAD) != 0, yr, dr);
   fast_bwd_compute<F, TPR, NV>(a.p, r, lane, (a.policy & POL_NT_STORE) != 0, yr, dr, red);
 }
+
+// ------------------------------------------------------ long rows: streaming
+//
+// Rows longer than a workgroup's registers hold (more than 4096 vectors) run
+// one 1024-lane workgroup per row in two passes. Pass 1 reads the row in
+// chunks of kStreamCv vectors per lane and keeps, per lane, a running maximum
+// and a running sum of exponentials, rescaled by exp(m_old - m_new) whenever
+// the maximum grows -- the online softmax of the 0539edu.com notes (fused
+// attention section) applied to one row; the lanes' (max, sum) pairs are then
+// merged across the workgroup. Pass 2 reads the row again and writes y. The
+// backward likewise accumulates the row's dot product in pass 1 and writes dx
+// in pass 2. The second read of a row usually hits the L2 or the Infinity
+// Cache; the HBM traffic grows by at most the re-read.
+//
+// Any alignment: vector v covers elements [v*E - a, v*E - a + E) of the row as
+// in the general kernels, with element accesses for partial vectors.
+
+constexpr int kStreamTpr = 1024;
+constexpr int kStreamCv = 4;
+
+// Scores of vector v of a row: x*scale + mask for keys [0, kload), -inf else.
+template <class F>
+SMS_DEV void row_scores(const char* xrow, const char* mrow, bool has_mask, bool mvec, int ax,
+                        int v, int kload, float scale, float (&s)[F::kE]) {
+  constexpr int E = F::kE;
+  constexpr int BY = F::kBytes;
+  const int k0 = v * E - ax;
+  if (k0 >= kload || k0 + E <= 0) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) s[e] = kNegInf;
+    return;
+  }
+  if (k0 >= 0 && k0 + E <= kload) {
+    // xrow + k0*BY sits on a 16-byte line: k0 + ax is a multiple of E.
+    F::unpack(*reinterpret_cast<const u32x4*>(xrow + (int64_t)k0 * BY), s);
+    if (has_mask) {
+      float m[E];
+      if (mvec) {
+        F::unpack(*reinterpret_cast<const u32x4*>(mrow + (int64_t)k0 * BY), m);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) m[e] = F::ld(mrow + (int64_t)(k0 + e) * BY);
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) s[e] = fmaf(s[e], scale, m[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) s[e] *= scale;
+    }
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int k = k0 + e;
+    if (k >= 0 && k < kload) {
+      const float xv = F::ld(xrow + (int64_t)k * BY);
+      s[e] = has_mask ? fmaf(xv, scale, F::ld(mrow + (int64_t)k * BY)) : xv * scale;
+    } else {
+      s[e] = kNegInf;
+    }
+  }
+}
+
+// y and dy of vector v for keys [0, kload), zeros elsewhere.
+template <class F>
+SMS_DEV void row_pair(const char* yrow, const char* drow, bool dvec, int ay, int v, int kload,
+                      float (&yv)[F::kE], float (&gv)[F::kE]) {
+  constexpr int E = F::kE;
+  constexpr int BY = F::kBytes;
+  const int k0 = v * E - ay;
+  if (k0 >= kload || k0 + E <= 0) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) yv[e] = gv[e] = 0.0f;
+    return;
+  }
+  if (k0 >= 0 && k0 + E <= kload) {
+    F::unpack(*reinterpret_cast<const u32x4*>(yrow + (int64_t)k0 * BY), yv);
+    if (dvec) {
+      F::unpack(*reinterpret_cast<const u32x4*>(drow + (int64_t)k0 * BY), gv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) gv[e] = F::ld(drow + (int64_t)(k0 + e) * BY);
+    }
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int k = k0 + e;
+    const bool in = (k >= 0 && k < kload);
+    yv[e] = in ? F::ld(yrow + (int64_t)k * BY) : 0.0f;
+    gv[e] = in ? F::ld(drow + (int64_t)k * BY) : 0.0f;
+  }
+}
+
+// Stores vector v of an output row (keys [0, Sk)); whole vectors go out as one
+// 16-byte store when the output row has the input row's alignment.
+template <class F>
+SMS_DEV void row_store(char* orow, bool ovec, int ax, int v, int Sk, const float (&o)[F::kE]) {
+  constexpr int E = F::kE;
+  constexpr int BY = F::kBytes;
+  const int k0 = v * E - ax;
+  if (k0 >= Sk || k0 + E <= 0) return;
+  if (ovec && k0 >= 0 && k0 + E <= Sk) {
+    *reinterpret_cast<u32x4*>(orow + (int64_t)k0 * BY) = F::pack(o);
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int k = k0 + e;
+    if (k >= 0 && k < Sk) F::st(orow + (int64_t)k * BY, o[e]);
+  }
+}
+
+template <class F>
+__global__ void __launch_bounds__(kStreamTpr) sms_fwd_stream_kernel(FwdParams p) {
+  constexpr int E = F::kE;
+  constexpr int BY = F::kBytes;
+  constexpr int TPR = kStreamTpr;
+  constexpr int CV = kStreamCv;
+  __shared__ float red[2][TPR / 64];
+  uint32_t b, h, q;
+  row_coords<1>(p.g, blockIdx.x, 0, b, h, q);  // one row per workgroup, grid = rows
+  const int Sk = (int)p.g.Sk;
+  const int lane = (int)threadIdx.x;
+  const char* xrow = p.x + ((int64_t)b * p.sx_b + (int64_t)h * p.sx_h + (int64_t)q * p.sx_q) * BY;
+  char* yrow = p.y + ((int64_t)b * p.sy_b + (int64_t)h * p.sy_h + (int64_t)q * p.sy_q) * BY;
+  const char* mrow =
+      p.mask + ((int64_t)b * p.sm_b + (int64_t)h * p.sm_h + (int64_t)q * p.sm_q) * BY;
+  const int ax = (int)(((uintptr_t)xrow & 15) / BY);
+  const bool yvec = ((((uintptr_t)yrow & 15) / BY) == (uintptr_t)ax);
+  const bool mvec = p.has_mask && ((((uintptr_t)mrow & 15) / BY) == (uintptr_t)ax);
+  const bool has_mask = p.has_mask != 0;
+  const int kload = p.causal ? (int)min((int64_t)q + 1, (int64_t)Sk) : Sk;
+  const int nvec = (int)(((int64_t)ax + kload + E - 1) / E);  // vectors holding read keys
+  const int nvec_out = (int)(((int64_t)ax + Sk + E - 1) / E);
+  const float scale = p.scale;
+
+  // Pass 1: per-lane running (max, rescaled sum).
+  float m_run = kNegInf, l_run = 0.0f;
+  for (int base = 0; base < nvec; base += TPR * CV) {
+    float s[CV][E];
+#pragma unroll
+    for (int j = 0; j < CV; ++j)
+      row_scores<F>(xrow, mrow, has_mask, mvec, ax, base + j * TPR + lane, kload, scale, s[j]);
+    float cm = kNegInf;
+#pragma unroll
+    for (int j = 0; j < CV; ++j)
+#pragma unroll
+      for (int e = 0; e < E; ++e) cm = fmaxf(cm, s[j][e]);
+    if (cm > m_run) {
+      l_run = (m_run == kNegInf) ? 0.0f : l_run * __builtin_amdgcn_exp2f((m_run - cm) * kLog2e);
+      m_run = cm;
+    }
+    if (m_run != kNegInf) {
+#pragma unroll
+      for (int j = 0; j < CV; ++j)
+#pragma unroll
+        for (int e = 0; e < E; ++e) l_run += exp_biased(s[j][e], m_run);
+    }
+  }
+  const float M = row_reduce<TPR>(m_run, OpMax(), red[0]);
+  const float mine =
+      (m_run == kNegInf) ? 0.0f : l_run * __builtin_amdgcn_exp2f((m_run - M) * kLog2e);
+  const float L = row_reduce<TPR>(mine, OpAdd(), red[1]);
+  const float mref = (M == kNegInf) ? 0.0f : M;
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;  // fully masked row -> zeros
+
+  // Pass 2: y over the whole row.
+  for (int base = 0; base < nvec_out; base += TPR * CV) {
+#pragma unroll
+    for (int j = 0; j < CV; ++j) {
+      const int v = base + j * TPR + lane;
+      float o[E];
+      if (v * E - ax >= kload) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = 0.0f;
+      } else {
+        row_scores<F>(xrow, mrow, has_mask, mvec, ax, v, kload, scale, o);
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = exp_biased(o[e], mref) * inv;
+      }
+      row_store<F>(yrow, yvec, ax, v, Sk, o);
+    }
+  }
+}
+
+template <class F>
+__global__ void __launch_bounds__(kStreamTpr) sms_bwd_stream_kernel(BwdParams p) {
+  constexpr int E = F::kE;
+  constexpr int BY = F::kBytes;
+  constexpr int TPR = kStreamTpr;
+  constexpr int CV = kStreamCv;
+  __shared__ double red[TPR / 64];
+  uint32_t b, h, q;
+  row_coords<1>(p.g, blockIdx.x, 0, b, h, q);
+  const int Sk = (int)p.g.Sk;
+  const int lane = (int)threadIdx.x;
+  const char* yrow = p.y + ((int64_t)b * p.sy_b + (int64_t)h * p.sy_h + (int64_t)q * p.sy_q) * BY;
+  const char* drow = p.dy + ((int64_t)b * p.sd_b + (int64_t)h * p.sd_h + (int64_t)q * p.sd_q) * BY;
+  char* xrow = p.dx + ((int64_t)b * p.sx_b + (int64_t)h * p.sx_h + (int64_t)q * p.sx_q) * BY;
+  const int ay = (int)(((uintptr_t)yrow & 15) / BY);
+  const bool dvec = ((((uintptr_t)drow & 15) / BY) == (uintptr_t)ay);
+  const bool xvec = ((((uintptr_t)xrow & 15) / BY) == (uintptr_t)ay);
+  const int kload = p.causal ? (int)min((int64_t)q + 1, (int64_t)Sk) : Sk;
+  const int nvec = (int)(((int64_t)ay + kload + E - 1) / E);
+  const int nvec_out = (int)(((int64_t)ay + Sk + E - 1) / E);
+
+  // Pass 1: the row's dot product, in fp64.
+  double acc = 0.0;
+  for (int base = 0; base < nvec; base += TPR * CV) {
+#pragma unroll
+    for (int j = 0; j < CV; ++j) {
+      float yv[E], gv[E];
+      row_pair<F>(yrow, drow, dvec, ay, base + j * TPR + lane, kload, yv, gv);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc += F::prod(yv[e], gv[e]);
+    }
+  }
+  acc = row_reduce<TPR>(acc, OpAdd(), red);
+  const float dot_hi = (float)acc;
+  const float dot_lo = (float)(acc - (double)dot_hi);
+  const float scale = p.scale;
+
+  // Pass 2: dx over the whole row.
+  for (int base = 0; base < nvec_out; base += TPR * CV) {
+#pragma unroll
+    for (int j = 0; j < CV; ++j) {
+      const int v = base + j * TPR + lane;
+      float o[E];
+      if (v * E - ay >= kload) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = 0.0f;
+      } else {
+        float yv[E], gv[E];
+        row_pair<F>(yrow, drow, dvec, ay, v, kload, yv, gv);
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = (yv[e] * scale) * ((gv[e] - dot_hi) - dot_lo);
+      }
+      row_store<F>(xrow, xvec, ay, v, Sk, o);
+    }
+  }
+}
+
+template <class F>
+hipError_t launch_stream(const FwdParams* fp, const BwdParams* bp, uint32_t rows,
+                         hipStream_t st) {
+  if (fp)
+    hipLaunchKernelGGL((sms_fwd_stream_kernel<F>), dim3(rows), dim3(kStreamTpr), 0, st, *fp);
+  else
+    hipLaunchKernelGGL((sms_bwd_stream_kernel<F>), dim3(rows), dim3(kStreamTpr), 0, st, *bp);
+  return hipGetLastError();
+}
+
 // --------------------------------------------------------------- launchers
 
 // TPR and NV values the library is built with.
@@ -917,6 +1170,12 @@ hipError_t sms_launch_fwd_bf16(const sms::FwdParams&, int tpr, int nv, uint32_t 
 hipError_t sms_launch_bwd_f32(const sms::BwdParams&, int tpr, int nv, uint32_t blocks, hipStream_t);
 hipError_t sms_launch_bwd_f16(const sms::BwdParams&, int tpr, int nv, uint32_t blocks, hipStream_t);
 hipError_t sms_launch_bwd_bf16(const sms::BwdParams&, int tpr, int nv, uint32_t blocks, hipStream_t);
+hipError_t sms_launch_stream_f32(const sms::FwdParams*, const sms::BwdParams*, uint32_t rows,
+                                 hipStream_t);
+hipError_t sms_launch_stream_f16(const sms::FwdParams*, const sms::BwdParams*, uint32_t rows,
+                                 hipStream_t);
+hipError_t sms_launch_stream_bf16(const sms::FwdParams*, const sms::BwdParams*, uint32_t rows,
+                                  hipStream_t);
 hipError_t sms_launch_fast_f32(const sms::FastFwdArgs*, const sms::FastBwdArgs*, int tpr, int nv,
                                uint32_t blocks, hipStream_t);
 hipError_t sms_launch_fast_f16(const sms::FastFwdArgs*, const sms::FastBwdArgs*, int tpr, int nv,

@@ -39,7 +39,8 @@
  *   are still correct (element accesses for the unaligned head and tail).
  * - Outputs must not overlap inputs, except exactly in place: y == x with
  *   identical strides (forward), or dx == dy (or dx == y) with identical
- *   strides (backward). Each row is read completely before any of it is written.
+ *   strides (backward). Every element is read before it is written, by the same
+ *   thread, and rows do not share elements, so exact in-place use is safe.
  * - A size of zero in any dimension is a successful no-op.
  * - On any error nothing is launched and a status other than SMS_OK is
  *   returned; no function throws or aborts. SMS_ERR_HIP reports a failure the
@@ -102,7 +103,10 @@ typedef enum {
  *   is_causal      nonzero: keys k > q are masked after the additive mask
  *   stream         hipStream_t to enqueue on
  *
- * Limits: B*H*Sq < 2^32 rows and Sk <= sms_max_sk(dtype).
+ * Limits: B*H*Sq < 2^32 rows, Sk <= sms_max_sk(dtype) = 2^30, and at most
+ * 2^32 - 1 work-items per launch (rows of more than 4096 16-byte vectors take
+ * one 1024-lane workgroup each, so at most 4194303 such rows per call).
+ * Longer rows cost a second read of the row (two passes).
  */
 sms_status sms_forward(const void* x, const int64_t x_strides[4],
                        const void* mask, sms_mask_mode mask_mode,
@@ -131,13 +135,16 @@ sms_status sms_backward(const void* y, const int64_t y_strides[4],
                         sms_dtype dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk,
                         float scale, int is_causal, void* stream);
 
-/* Largest key length Sk the library runs for `dtype` (0 for an unknown dtype). */
+/* Largest key length Sk the library runs for `dtype` (2^30; 0 for an unknown
+ * dtype). */
 int64_t sms_max_sk(sms_dtype dtype);
 
-/* Which kernel family a call with these sizes takes: 0 = several rows per
- * wavefront, 1 = one wavefront per row, 2 = several wavefronts per row (LDS
- * cross-wave reduction). -1 for an unsupported size or dtype. `backward`
- * selects the backward's choice. Host-only; launches nothing. */
+/* Which kernel family a call with these sizes takes (rows 16-byte aligned):
+ * 0 = several rows per wavefront, 1 = one wavefront per row, 2 = several
+ * wavefronts per row (LDS cross-wave reduction), 3 = streaming (one 1024-lane
+ * workgroup per row, two passes: online max/sum, then normalise; for rows of
+ * more than 4096 16-byte vectors). -1 for an unsupported size or dtype.
+ * `backward` selects the backward's choice. Host-only; launches nothing. */
 int sms_path(sms_dtype dtype, int64_t Sk, int backward);
 
 /* Static text naming a status code. */

@@ -16,9 +16,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sms.h")
 
 # A non-NULL, 16-byte aligned address that is never dereferenced: every call
-# that receives it is rejected by the host-side checks first.
+# that receives it is rejected by the host-side checks first. The tests that
+# pass it run only where no GPU is visible, so that no mistake in a check can
+# ever turn one of them into a launch on a real device.
 FAKE = 0x10000
 FAKE_ODD = 0x10001
+no_device = pytest.mark.skipif(torch.cuda.is_available(),
+                               reason="passes fake device pointers; host-only test")
 
 
 def declared_functions():
@@ -59,6 +63,7 @@ def _bwd(L, y=FAKE, dy=FAKE, dx=FAKE, st=(64, 64, 64, 1), dtype=0, B=1, H=1, Sq=
     return L.sms_backward(y, s, dy, s, dx, s, dtype, B, H, Sq, Sk, 1.0, 0, None)
 
 
+@no_device
 def test_forward_argument_checks(L):
     assert _fwd(L, dtype=7) == 4                                  # dtype
     assert _fwd(L, mode=9) == 5                                   # mask mode
@@ -73,9 +78,11 @@ def test_forward_argument_checks(L):
     assert _fwd(L, mode=2, mask=FAKE_ODD) == 6                    # misaligned mask
     assert _fwd(L, Sk=L.sms_max_sk(0) + 1) == 2                   # too long a row
     assert _fwd(L, B=1 << 20, H=1 << 10, Sq=1 << 3) == 2          # 2^33 rows
+    assert _fwd(L, Sq=1 << 23, Sk=1 << 20) == 2                   # 2^23 streamed rows: > 2^32 lanes
     assert _fwd(L, Sk=1 << 31) == 2
 
 
+@no_device
 def test_zero_sizes_are_noops(L):
     # NULL pointers are fine when there is nothing to do.
     for dims in ((0, 1, 1, 8), (1, 0, 1, 8), (1, 1, 0, 8), (1, 1, 1, 0)):
@@ -84,6 +91,7 @@ def test_zero_sizes_are_noops(L):
         assert _bwd(L, y=None, dy=None, dx=None, B=B, H=H, Sq=Sq, Sk=Sk) == 0
 
 
+@no_device
 def test_backward_argument_checks(L):
     assert _bwd(L, dtype=3) == 4
     assert _bwd(L, dy=None) == 1 and _bwd(L, dx=None) == 1
@@ -93,15 +101,17 @@ def test_backward_argument_checks(L):
 
 
 def test_max_sk_and_paths(L):
-    assert L.sms_max_sk(0) == 4096 * 4 - 3
-    assert L.sms_max_sk(1) == L.sms_max_sk(2) == 4096 * 8 - 7
+    assert L.sms_max_sk(0) == L.sms_max_sk(1) == L.sms_max_sk(2) == 1 << 30
     assert L.sms_max_sk(5) == 0
     # the benchmark workloads: rows-per-wave, wave-per-row and multi-wave families
     expect = {1: 0, 2: 2, 3: 2, 4: 2, 5: 1}
     code = {"f32": 0, "f16": 1, "bf16": 2}
     for i, c in CONFIGS.items():
         assert L.sms_path(code[c["dtype"]], c["shape"][3], 0) == expect[i], i
-    assert L.sms_path(1, 1 << 20, 0) == -1
+    # rows beyond 4096 16-byte vectors stream; beyond 2^30 keys: unsupported
+    assert L.sms_path(0, 4096 * 4, 0) == 2 and L.sms_path(0, 4096 * 4 + 1, 0) == 3
+    assert L.sms_path(1, 4096 * 8, 1) == 2 and L.sms_path(1, 4096 * 8 + 1, 1) == 3
+    assert L.sms_path(2, 1 << 30, 0) == 3 and L.sms_path(2, (1 << 30) + 1, 0) == -1
 
 
 def test_mask_mode_inference():

@@ -378,3 +378,74 @@ def test_autograd_and_streams(dtype):
     torch.cuda.synchronize()
     compare(decoded(x.grad), oracle.backward(to_np(y.detach()), to_np(g.contiguous()), dtype,
                                              0.35), dtype, "autograd strided dy")
+
+
+# ------------------------------------------------- long rows (streaming)
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("Sk", [1, 7, 64, 77, 1000, 1001, 4096, 5000])
+def test_streaming_kernels_on_short_rows(dtype, Sk, monkeypatch):
+    """The two-pass streaming kernels, forced onto short rows: every mask mode,
+    causal or not, aligned or not, forward and backward, against the oracle."""
+    monkeypatch.setenv("SMS_FORCE_STREAM", "1")
+    say(f"stream forced dtype={dtype} Sk={Sk}")
+    for mode in MODES:
+        for causal in (False, True):
+            shape = (2, 2, 3, Sk)
+            seed = zlib.crc32(f"s/{dtype}/{Sk}/{mode}/{causal}".encode()) % 10000
+            x = draw_x(shape, dtype, ("normal", 3.0), seed, DEV)
+            mask = draw_mask(shape, mode, dtype, _mask_kind(mode), seed + 1, DEV)
+            y = fwd(x, mask, 0.3, causal)
+            compare(decoded(y), oracle_fwd(x, mask, mode, 0.3, causal), dtype,
+                    f"stream {dtype} Sk={Sk} {mode} causal={causal}", rowsum=True)
+            dy = draw_x(shape, dtype, ("normal", 1.0), seed + 2, DEV)
+            dx = bwd(y, dy, 0.3, causal)
+            compare(decoded(dx), oracle.backward(to_np(y), to_np(dy), dtype, 0.3), dtype,
+                    f"stream bwd {dtype} Sk={Sk} {mode} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype,Sk,mode", [
+    ("f32", 16385, "b_1_sk"),      # one past the register-resident fp32 reach
+    ("f32", 262144, "none"),       # 1 MB rows
+    ("f16", 32769, "sq_sk"),       # one past the fp16 reach
+    ("f16", 40000, "b_sq_sk"),
+    ("bf16", 100003, "full"),      # odd length: unaligned rows, element head/tail
+])
+def test_long_rows(dtype, Sk, mode):
+    """Rows beyond one workgroup's registers take the streaming kernels; sampled
+    rows against the oracle, row sums on every row."""
+    say(f"long rows dtype={dtype} Sk={Sk} mode={mode}")
+    shape = (1, 2, 4, Sk)
+    x = draw_x(shape, dtype, ("normal", 4.0), Sk, DEV)
+    mask = draw_mask(shape, mode, dtype, _mask_kind(mode), Sk + 1, DEV)
+    for causal in (False, True):
+        y = fwd(x, mask, 0.25, causal)
+        ref = oracle_fwd(x, mask, mode, 0.25, causal)
+        compare(decoded(y), ref, dtype, f"long fwd causal={causal}", rowsum=True)
+        dy = draw_x(shape, dtype, ("normal", 1.0), Sk + 2, DEV)
+        dx = bwd(y, dy, 0.25, causal)
+        compare(decoded(dx), oracle.backward(to_np(y), to_np(dy), dtype, 0.25), dtype,
+                f"long bwd causal={causal}")
+
+
+def test_long_causal_square():
+    """Causal with Sq = Sk = 40000 (fp16): query positions across the whole
+    streamed row; sampled rows against the oracle, zeros after the diagonal."""
+    Sk = 40000
+    say(f"long causal square Sk={Sk}")
+    shape = (1, 1, Sk, Sk)
+    x = draw_x(shape, "f16", ("normal", 8.0), 5, DEV)
+    y = fwd(x, None, 1 / math.sqrt(128), True)
+    rows = sample_rows(Sk, Sk, k=48, seed=5) + [Sk - 1, 32767, 32768]
+    xr = gather_rows(x, rows)
+    yr = oracle.decode(gather_rows(y, rows), "f16")
+    for i, r in enumerate(rows):
+        ref = oracle.forward_row(xr[i], "f16", None, 1 / math.sqrt(128), True, r % Sk)
+        compare(yr[i], ref, "f16", f"row {r}")
+    for q0 in range(0, Sk, 8192):
+        blk = y[0, 0, q0:q0 + 8192]
+        k = torch.arange(Sk, device=DEV)
+        fut = k.view(1, -1) > torch.arange(q0, q0 + blk.shape[0], device=DEV).view(-1, 1)
+        assert not ((blk != 0) & fut).any()
+    del x, y
+    torch.cuda.empty_cache()
