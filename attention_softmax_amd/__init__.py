@@ -14,6 +14,8 @@ computation runs in the HIP kernels. ``scaled_mask_softmax`` wraps them in a
 from ._lib import SmsError, lib  # noqa: F401
 from .ops import (  # noqa: F401
     ScaledMaskSoftmaxFunction,
+    causal_code,
+    mask_kind_of,
     mask_mode_of,
     scaled_mask_softmax,
     sms_backward,

@@ -1,22 +1,7 @@
 // Kernel instantiations for one I/O format (bf16); see kernels.hpp.
 #include "kernels.hpp"
 
-hipError_t sms_launch_fwd_bf16(const sms::FwdParams& p, int tpr, int nv, uint32_t blocks,
-                             hipStream_t st) {
-  return sms::launch_fwd<sms::Bf16>(p, tpr, nv, blocks, st);
-}
-
-hipError_t sms_launch_bwd_bf16(const sms::BwdParams& p, int tpr, int nv, uint32_t blocks,
-                             hipStream_t st) {
-  return sms::launch_bwd<sms::Bf16>(p, tpr, nv, blocks, st);
-}
-
-hipError_t sms_launch_fast_bf16(const sms::FastFwdArgs* fa, const sms::FastBwdArgs* ba, int tpr,
+hipError_t sms_launch_bf16(const sms::FwdParams* fp, const sms::BwdParams* bp, int family, int tpr,
                               int nv, uint32_t blocks, hipStream_t st) {
-  return sms::launch_fast<sms::Bf16>(fa, ba, tpr, nv, blocks, st);
-}
-
-hipError_t sms_launch_stream_bf16(const sms::FwdParams* fp, const sms::BwdParams* bp, uint32_t rows,
-                                    hipStream_t st) {
-  return sms::launch_stream<sms::Bf16>(fp, bp, rows, st);
+  return sms::launch<sms::Bf16>(fp, bp, family, tpr, nv, blocks, st);
 }

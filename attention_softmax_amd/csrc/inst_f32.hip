@@ -1,22 +1,7 @@
 // Kernel instantiations for one I/O format (f32); see kernels.hpp.
 #include "kernels.hpp"
 
-hipError_t sms_launch_fwd_f32(const sms::FwdParams& p, int tpr, int nv, uint32_t blocks,
-                             hipStream_t st) {
-  return sms::launch_fwd<sms::Fp32>(p, tpr, nv, blocks, st);
-}
-
-hipError_t sms_launch_bwd_f32(const sms::BwdParams& p, int tpr, int nv, uint32_t blocks,
-                             hipStream_t st) {
-  return sms::launch_bwd<sms::Fp32>(p, tpr, nv, blocks, st);
-}
-
-hipError_t sms_launch_fast_f32(const sms::FastFwdArgs* fa, const sms::FastBwdArgs* ba, int tpr,
-                              int nv, uint32_t blocks, hipStream_t st) {
-  return sms::launch_fast<sms::Fp32>(fa, ba, tpr, nv, blocks, st);
-}
-
-hipError_t sms_launch_stream_f32(const sms::FwdParams* fp, const sms::BwdParams* bp, uint32_t rows,
-                                   hipStream_t st) {
-  return sms::launch_stream<sms::Fp32>(fp, bp, rows, st);
+hipError_t sms_launch_f32(const sms::FwdParams* fp, const sms::BwdParams* bp, int family, int tpr,
+                             int nv, uint32_t blocks, hipStream_t st) {
+  return sms::launch<sms::Fp32>(fp, bp, family, tpr, nv, blocks, st);
 }

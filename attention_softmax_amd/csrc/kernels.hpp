@@ -1,11 +1,19 @@
 // kernels.hpp -- HIP kernels of the fused scaled-masked softmax for gfx950.
 //
 // Forward, per row (b, h, q) of x[B,H,Sq,Sk]: s_k = x_k*scale + mask_k, keys
-// k > q masked when causal, y_k = exp(s_k - max s) / sum exp(s - max s)
+// after the causal bound masked, y_k = exp(s_k - max s) / sum exp(s - max s)
 // (lmnt.cn "Custom fused Softmax operator in CUDA, wrapped into PyTorch",
 // sec. 1.2 and 2.1; causal after the additive mask as in sec. 3.1). A fully
 // masked row is written as zeros (pnsm.cn ScaledMaskSoftmax article, sec. 4.3).
 // Backward: dx_k = scale * y_k * (dy_k - sum_j dy_j y_j) (lmnt.cn page, sec. 3.3).
+//
+// Masks: additive (x's dtype), boolean (one byte per key, nonzero = excluded,
+// turned into -inf inside the kernel as the pnsm.cn article, sec. 2.3,
+// suggests), or per-batch key lengths (keys k >= len[b] excluded; nothing per
+// key is read). Causal: key k is excluded when k > q (top-left alignment) or
+// k > q + Sk - Sq (bottom-right alignment, for Sq != Sk). Key lengths and both
+// causal rules are one bound per row, kload: keys [0, kload) are read, the
+// rest are neither loaded nor exponentiated and are written as zeros.
 //
 // Mapping. A row is owned by TPR consecutive lanes. TPR <= 64 packs 64/TPR rows
 // into each wavefront (four wavefronts per 256-thread workgroup); TPR >= 128
@@ -13,7 +21,8 @@
 // vectors of the row in VGPRs: vector v = j*TPR + lane (j < NV), so one wave
 // instruction moves TPR*16 contiguous bytes. The row is read from HBM once,
 // reduced in registers and written once; exponentials are computed once per
-// element and kept in the same registers.
+// element and kept in the same registers. Rows too long for that stream (two
+// passes, one workgroup per row; see the streaming kernels).
 //
 // Reductions. Within a wavefront: DPP quad_perm / row_half_mirror / row_mirror
 // steps reduce 4, 8 and 16 lanes, then the gfx950 lane-swap instructions
@@ -23,13 +32,12 @@
 // slots, so the forward takes exactly two barriers).
 //
 // Alignment. Vector v covers the row's elements [v*E - a, v*E - a + E), where a
-// is the row start's element offset inside its 16-byte line, so full vectors
-// are 16-byte aligned in the input. The first and last vectors of a row may be
-// partial: those elements are read and written one at a time. An operand whose
-// row has a different offset than the input's uses element accesses.
-//
-// Causal rows read keys 0..q only; later vectors are neither loaded nor
-// exponentiated, and are stored as zeros.
+// is the input row start's element offset inside its 16-byte line, so full
+// vectors are 16-byte aligned in the input. The general kernels read and write
+// the partial first and last vectors of a row one element at a time, and use
+// element accesses for any operand whose rows sit at another offset. The
+// aligned-row kernels serve the common case where every operand's rows start
+// on 16-byte lines and hold whole vectors.
 
 #pragma once
 
@@ -293,157 +301,28 @@ SMS_DEV bool row_coords(const RowGeom& g, uint32_t w, uint32_t local, uint32_t& 
 
 constexpr int block_of(int tpr) { return tpr <= 64 ? 256 : tpr; }
 
-// ------------------------------------------------------------------ forward
+// ------------------------------------------------------------- parameters
+
+enum : int { MASK_NONE = 0, MASK_ADD = 1, MASK_BOOL = 2, MASK_LEN = 3 };
+enum : int { CAUSAL_NONE = 0, CAUSAL_TOP_LEFT = 1, CAUSAL_BOTTOM_RIGHT = 2 };
+// Cache policy bits: 1 = nontemporal loads of x / y / dy, 2 = nontemporal
+// stores of y / dx. The score and output streams are touched once; the mask,
+// which other rows read again, always goes through the caches.
+enum : int { POL_NT_LOAD = 1, POL_NT_STORE = 2 };
 
 struct FwdParams {
   const char* x;
-  const char* mask;
+  const char* mask;          // additive (x's dtype), bool (bytes) or int32 lengths [B]
   char* y;
   int64_t sx_b, sx_h, sx_q;  // element strides of x
   int64_t sy_b, sy_h, sy_q;  // element strides of y
   int64_t sm_b, sm_h, sm_q;  // element strides of the mask, 0 on broadcast axes
   RowGeom g;
   float scale;
-  int causal;
-  int has_mask;
+  int causal;     // CAUSAL_*
+  int mask_kind;  // MASK_*
+  int policy;     // POL_*
 };
-
-template <class F, int TPR, int NV>
-__global__ void __launch_bounds__(block_of(TPR)) sms_fwd_kernel(FwdParams p) {
-  constexpr int E = F::kE;
-  constexpr int BY = F::kBytes;
-  constexpr int RPB = block_of(TPR) / TPR;
-  __shared__ float slots[2][TPR > 64 ? TPR / 64 : 1];
-
-  const uint32_t lane = threadIdx.x % TPR;
-  uint32_t b, h, q;
-  if (!row_coords<RPB>(p.g, blockIdx.x, threadIdx.x / TPR, b, h, q)) return;
-
-  const int Sk = (int)p.g.Sk;
-  const char* xrow = p.x + ((int64_t)b * p.sx_b + (int64_t)h * p.sx_h + (int64_t)q * p.sx_q) * BY;
-  char* yrow = p.y + ((int64_t)b * p.sy_b + (int64_t)h * p.sy_h + (int64_t)q * p.sy_q) * BY;
-  const int ax = (int)(((uintptr_t)xrow & 15) / BY);
-  const bool yvec = ((((uintptr_t)yrow & 15) / BY) == (uintptr_t)ax);
-  const char* xbase = xrow - ax * BY;  // 16-byte aligned
-  char* ybase = yrow - ax * BY;        // 16-byte aligned when yvec
-  // Keys [0, kload) are read; later keys are causal-future (or past the row).
-  const int kload = p.causal ? (int)min((int64_t)q + 1, (int64_t)Sk) : Sk;
-
-  float s[NV][E];
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int v = j * TPR + (int)lane;
-    const int k0 = v * E - ax;
-    if (k0 >= kload || k0 + E <= 0) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) s[j][e] = kNegInf;
-    } else if (k0 >= 0 && k0 + E <= kload) {
-      const u32x4 u = *reinterpret_cast<const u32x4*>(xbase + (int64_t)v * 16);
-      F::unpack(u, s[j]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int k = k0 + e;
-        s[j][e] = (k >= 0 && k < kload) ? F::ld(xrow + (int64_t)k * BY) : kNegInf;
-      }
-    }
-  }
-
-  // score = x*scale + mask on the keys that were read; the rest stay -inf.
-  const float scale = p.scale;
-  if (p.has_mask) {
-    const char* mrow =
-        p.mask + ((int64_t)b * p.sm_b + (int64_t)h * p.sm_h + (int64_t)q * p.sm_q) * BY;
-    const bool mvec = ((((uintptr_t)mrow & 15) / BY) == (uintptr_t)ax);
-    const char* mbase = mrow - ax * BY;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int v = j * TPR + (int)lane;
-      const int k0 = v * E - ax;
-      if (k0 >= kload || k0 + E <= 0) continue;
-      if (k0 >= 0 && k0 + E <= kload) {
-        float m[E];
-        if (mvec) {
-          F::unpack(*reinterpret_cast<const u32x4*>(mbase + (int64_t)v * 16), m);
-        } else {
-#pragma unroll
-          for (int e = 0; e < E; ++e) m[e] = F::ld(mrow + (int64_t)(k0 + e) * BY);
-        }
-#pragma unroll
-        for (int e = 0; e < E; ++e) s[j][e] = fmaf(s[j][e], scale, m[e]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int k = k0 + e;
-          if (k >= 0 && k < kload) s[j][e] = fmaf(s[j][e], scale, F::ld(mrow + (int64_t)k * BY));
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int v = j * TPR + (int)lane;
-      const int k0 = v * E - ax;
-      if (k0 >= kload || k0 + E <= 0) continue;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int k = k0 + e;
-        if (k >= 0 && k < kload) s[j][e] *= scale;
-      }
-    }
-  }
-
-  // Row maximum.
-  float mx = kNegInf;
-#pragma unroll
-  for (int j = 0; j < NV; ++j)
-#pragma unroll
-    for (int e = 0; e < E; ++e) mx = fmaxf(mx, s[j][e]);
-  mx = row_reduce<TPR>(mx, OpMax(), slots[0]);
-  // Every key masked: exponentiate against 0 so every term is exp(-inf) = 0.
-  const float mref = (mx == kNegInf) ? 0.0f : mx;
-
-  // Exponentials (kept in place) and their sum.
-  float sum = 0.0f;
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int k0 = (j * TPR + (int)lane) * E - ax;
-    if (k0 >= kload) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) s[j][e] = 0.0f;
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        s[j][e] = exp_biased(s[j][e], mref);
-        sum += s[j][e];
-      }
-    }
-  }
-  sum = row_reduce<TPR>(sum, OpAdd(), slots[1]);
-  const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;  // fully masked row -> zeros
-
-  // Write the whole row, zeros included.
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int v = j * TPR + (int)lane;
-    const int k0 = v * E - ax;
-    if (k0 >= Sk || k0 + E <= 0) continue;
-    float o[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) o[e] = s[j][e] * inv;
-    if (yvec && k0 >= 0 && k0 + E <= Sk) {
-      *reinterpret_cast<u32x4*>(ybase + (int64_t)v * 16) = F::pack(o);
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int k = k0 + e;
-        if (k >= 0 && k < Sk) F::st(yrow + (int64_t)k * BY, o[e]);
-      }
-    }
-  }
-}
-
-// ----------------------------------------------------------------- backward
 
 struct BwdParams {
   const char* y;
@@ -454,114 +333,17 @@ struct BwdParams {
   int64_t sx_b, sx_h, sx_q;  // dx
   RowGeom g;
   float scale;
-  int causal;
+  int causal;  // CAUSAL_*: a promise that y is 0 past the bound
+  int policy;  // POL_*
 };
 
-template <class F, int TPR, int NV>
-__global__ void __launch_bounds__(block_of(TPR)) sms_bwd_kernel(BwdParams p) {
-  constexpr int E = F::kE;
-  constexpr int BY = F::kBytes;
-  constexpr int RPB = block_of(TPR) / TPR;
-  __shared__ double slots[TPR > 64 ? TPR / 64 : 1];
-
-  const uint32_t lane = threadIdx.x % TPR;
-  uint32_t b, h, q;
-  if (!row_coords<RPB>(p.g, blockIdx.x, threadIdx.x / TPR, b, h, q)) return;
-
-  const int Sk = (int)p.g.Sk;
-  const char* yrow = p.y + ((int64_t)b * p.sy_b + (int64_t)h * p.sy_h + (int64_t)q * p.sy_q) * BY;
-  const char* drow = p.dy + ((int64_t)b * p.sd_b + (int64_t)h * p.sd_h + (int64_t)q * p.sd_q) * BY;
-  char* xrow = p.dx + ((int64_t)b * p.sx_b + (int64_t)h * p.sx_h + (int64_t)q * p.sx_q) * BY;
-  const int ay = (int)(((uintptr_t)yrow & 15) / BY);
-  const bool dvec = ((((uintptr_t)drow & 15) / BY) == (uintptr_t)ay);
-  const bool xvec = ((((uintptr_t)xrow & 15) / BY) == (uintptr_t)ay);
-  const char* ybase = yrow - ay * BY;
-  const char* dbase = drow - ay * BY;
-  char* xbase = xrow - ay * BY;
-  // With the causal promise, y is 0 after key q: those keys are not read.
-  const int kload = p.causal ? (int)min((int64_t)q + 1, (int64_t)Sk) : Sk;
-
-  float yv[NV][E], gv[NV][E];
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int v = j * TPR + (int)lane;
-    const int k0 = v * E - ay;
-    if (k0 >= kload || k0 + E <= 0) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) yv[j][e] = gv[j][e] = 0.0f;
-    } else if (k0 >= 0 && k0 + E <= kload) {
-      F::unpack(*reinterpret_cast<const u32x4*>(ybase + (int64_t)v * 16), yv[j]);
-      if (dvec) {
-        F::unpack(*reinterpret_cast<const u32x4*>(dbase + (int64_t)v * 16), gv[j]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) gv[j][e] = F::ld(drow + (int64_t)(k0 + e) * BY);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int k = k0 + e;
-        const bool in = (k >= 0 && k < kload);
-        yv[j][e] = in ? F::ld(yrow + (int64_t)k * BY) : 0.0f;
-        gv[j][e] = in ? F::ld(drow + (int64_t)k * BY) : 0.0f;
-      }
-    }
-  }
-
-  // dot = sum_k dy_k * y_k, accumulated in fp64 (no cancellation loss when
-  // dy_k - dot is small).
-  double acc = 0.0;
-#pragma unroll
-  for (int j = 0; j < NV; ++j)
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc += F::prod(yv[j][e], gv[j][e]);
-  acc = row_reduce<TPR>(acc, OpAdd(), slots);
-  const float dot_hi = (float)acc;
-  const float dot_lo = (float)(acc - (double)dot_hi);
-
-  const float scale = p.scale;
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int v = j * TPR + (int)lane;
-    const int k0 = v * E - ay;
-    if (k0 >= Sk || k0 + E <= 0) continue;
-    float o[E];
-    if (k0 >= kload) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) o[e] = 0.0f;
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) o[e] = (yv[j][e] * scale) * ((gv[j][e] - dot_hi) - dot_lo);
-    }
-    if (xvec && k0 >= 0 && k0 + E <= Sk) {
-      *reinterpret_cast<u32x4*>(xbase + (int64_t)v * 16) = F::pack(o);
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int k = k0 + e;
-        if (k >= 0 && k < Sk) F::st(xrow + (int64_t)k * BY, o[e]);
-      }
-    }
-  }
+// Keys [0, bound) of row q survive the causal rule.
+SMS_DEV int causal_bound(int causal, uint32_t q, uint32_t Sq, int Sk) {
+  int64_t c = Sk;
+  if (causal == CAUSAL_TOP_LEFT) c = (int64_t)q + 1;
+  if (causal == CAUSAL_BOTTOM_RIGHT) c = (int64_t)q + 1 + (int64_t)Sk - (int64_t)Sq;
+  return (int)(c < 0 ? 0 : (c > Sk ? Sk : c));
 }
-
-
-// ------------------------------------------------ fast path: aligned rows
-//
-// When every row of every operand starts on a 16-byte line and Sk is a
-// multiple of E, every vector of a row is whole: no element accesses remain,
-// and the causal boundary inside a vector is a register select. One workgroup
-// per slot (RPB rows), launched once: short-lived workgroups dealt in order
-// keep the set of DRAM pages in use compact, which measured faster on MI355X
-// than a persistent grid with next-row prefetch.
-//
-// The score and output streams are touched once, so they are loaded and
-// stored with the nontemporal hint; the mask, which other rows read again,
-// goes through the caches normally.
-
-// Cache policy bits for the fast path: 1 = nontemporal x / y / dy loads,
-// 2 = nontemporal y / dx stores.
-enum : int { POL_NT_LOAD = 1, POL_NT_STORE = 2 };
 
 SMS_DEV u32x4 ld16(const char* p, bool nt) {
   const u32x4* q = reinterpret_cast<const u32x4*>(p);
@@ -572,91 +354,204 @@ SMS_DEV void st16(char* p, u32x4 v, bool nt) {
   if (nt) __builtin_nontemporal_store(v, q); else *q = v;
 }
 
-struct FastFwdArgs {
-  FwdParams p;
-  int policy;
-};
+// E mask bytes starting at p (aligned to E), zero-extended.
+template <int E>
+SMS_DEV uint64_t ld_bits(const char* p) {
+  if constexpr (E == 8) return *reinterpret_cast<const uint64_t*>(p);
+  else return *reinterpret_cast<const uint32_t*>(p);
+}
+SMS_DEV bool bit_set(uint64_t bits, int e) { return ((bits >> (8 * e)) & 0xffu) != 0; }
 
-struct FastRow {
+// ----------------------------------------------------------- row descriptors
+
+struct FwdRow {
   const char* x;
-  const char* m;
+  const char* m;  // the row's mask row (additive / bool), unused otherwise
   char* y;
-  int kload;
+  int ax;         // elements from x's row start back to its 16-byte line
+  int kload;      // keys [0, kload) are read
+  bool yvec;      // y's row sits at x's offset: whole-vector stores
+  bool mvec;      // the mask row sits at x's offset: whole-vector mask loads
   bool valid;
 };
 
 template <class F, int RPB>
-SMS_DEV FastRow fast_fwd_row(const FwdParams& p, uint32_t slot, uint32_t local) {
-  FastRow r;
-  uint32_t b = 0, h = 0, q = 0;
-  r.valid = row_coords<RPB>(p.g, slot, local, b, h, q);
+SMS_DEV FwdRow fwd_row(const FwdParams& p, uint32_t w, uint32_t local) {
   constexpr int BY = F::kBytes;
+  constexpr int E = F::kE;
+  FwdRow r;
+  uint32_t b = 0, h = 0, q = 0;
+  r.valid = row_coords<RPB>(p.g, w, local, b, h, q);
   const int Sk = (int)p.g.Sk;
   r.x = p.x + ((int64_t)b * p.sx_b + (int64_t)h * p.sx_h + (int64_t)q * p.sx_q) * BY;
   r.y = p.y + ((int64_t)b * p.sy_b + (int64_t)h * p.sy_h + (int64_t)q * p.sy_q) * BY;
-  r.m = p.mask + ((int64_t)b * p.sm_b + (int64_t)h * p.sm_h + (int64_t)q * p.sm_q) * BY;
-  r.kload = !r.valid ? 0 : (p.causal ? (int)min((int64_t)q + 1, (int64_t)Sk) : Sk);
+  r.ax = (int)(((uintptr_t)r.x & 15) / BY);
+  r.yvec = ((((uintptr_t)r.y & 15) / BY) == (uintptr_t)r.ax);
+  int kload = causal_bound(p.causal, q, p.g.Sq, Sk);
+  const int64_t moff = (int64_t)b * p.sm_b + (int64_t)h * p.sm_h + (int64_t)q * p.sm_q;
+  r.m = nullptr;
+  r.mvec = false;
+  if (p.mask_kind == MASK_ADD) {
+    r.m = p.mask + moff * BY;
+    r.mvec = ((((uintptr_t)r.m & 15) / BY) == (uintptr_t)r.ax);
+  } else if (p.mask_kind == MASK_BOOL) {
+    r.m = p.mask + moff;
+    r.mvec = ((((uintptr_t)r.m - (uintptr_t)r.ax) & (E - 1)) == 0);
+  } else if (p.mask_kind == MASK_LEN && r.valid) {
+    const int len = reinterpret_cast<const int32_t*>(p.mask)[b];
+    kload = min(kload, max(len, 0));
+  }
+  r.kload = r.valid ? kload : 0;
   return r;
 }
 
-template <class F, int TPR, int NV>
-SMS_DEV void fast_fwd_load(const FwdParams& p, const FastRow& r, uint32_t lane, bool nt,
-                           u32x4 (&xr)[NV], u32x4 (&mr)[NV]) {
+struct BwdRow {
+  const char* y;
+  const char* d;
+  char* x;
+  int ay;      // elements from y's row start back to its 16-byte line
+  int kload;   // keys [0, kload) are read
+  bool dvec;   // dy's row at y's offset
+  bool xvec;   // dx's row at y's offset
+  bool valid;
+};
+
+template <class F, int RPB>
+SMS_DEV BwdRow bwd_row(const BwdParams& p, uint32_t w, uint32_t local) {
+  constexpr int BY = F::kBytes;
+  BwdRow r;
+  uint32_t b = 0, h = 0, q = 0;
+  r.valid = row_coords<RPB>(p.g, w, local, b, h, q);
+  r.y = p.y + ((int64_t)b * p.sy_b + (int64_t)h * p.sy_h + (int64_t)q * p.sy_q) * BY;
+  r.d = p.dy + ((int64_t)b * p.sd_b + (int64_t)h * p.sd_h + (int64_t)q * p.sd_q) * BY;
+  r.x = p.dx + ((int64_t)b * p.sx_b + (int64_t)h * p.sx_h + (int64_t)q * p.sx_q) * BY;
+  r.ay = (int)(((uintptr_t)r.y & 15) / BY);
+  r.dvec = ((((uintptr_t)r.d & 15) / BY) == (uintptr_t)r.ay);
+  r.xvec = ((((uintptr_t)r.x & 15) / BY) == (uintptr_t)r.ay);
+  r.kload = r.valid ? causal_bound(p.causal, q, p.g.Sq, (int)p.g.Sk) : 0;
+  return r;
+}
+
+// ------------------------------------------------ element and vector access
+
+// Scores of vector v of a row: x*scale + mask for keys [0, kload), -inf for
+// every other key. Any alignment.
+template <class F>
+SMS_DEV void row_scores(const FwdRow& r, int kind, int v, float scale, float (&s)[F::kE]) {
   constexpr int E = F::kE;
+  constexpr int BY = F::kBytes;
+  const int k0 = v * E - r.ax;
+  if (k0 >= 0 && k0 + E <= r.kload) {
+    // x + k0*BY sits on a 16-byte line: k0 + ax is a multiple of E.
+    F::unpack(*reinterpret_cast<const u32x4*>(r.x + (int64_t)k0 * BY), s);
+    if (kind == MASK_ADD) {
+      float m[E];
+      if (r.mvec) {
+        F::unpack(*reinterpret_cast<const u32x4*>(r.m + (int64_t)k0 * BY), m);
+      } else {
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int v = j * TPR + (int)lane;
-    if (v * E < r.kload) {
-      xr[j] = ld16(r.x + (int64_t)v * 16, nt);
-      if (p.has_mask) mr[j] = ld16(r.m + (int64_t)v * 16, false);
+        for (int e = 0; e < E; ++e) m[e] = F::ld(r.m + (int64_t)(k0 + e) * BY);
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) s[e] = fmaf(s[e], scale, m[e]);
+    } else if (kind == MASK_BOOL) {
+      uint64_t bits = 0;
+      if (r.mvec) {
+        bits = ld_bits<E>(r.m + k0);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          bits |= (uint64_t)(uint8_t)r.m[k0 + e] << (8 * e);
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) s[e] = bit_set(bits, e) ? kNegInf : s[e] * scale;
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) s[e] *= scale;
+    }
+  } else {
+    // A partial vector (row head or tail, or the key bound inside it), or none
+    // of the vector's keys read: element by element, -inf outside [0, kload).
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int k = k0 + e;
+      float v2 = kNegInf;
+      if (k >= 0 && k < r.kload) {
+        const float xv = F::ld(r.x + (int64_t)k * BY);
+        if (kind == MASK_ADD) v2 = fmaf(xv, scale, F::ld(r.m + (int64_t)k * BY));
+        else if (kind == MASK_BOOL) v2 = r.m[k] ? kNegInf : xv * scale;
+        else v2 = xv * scale;
+      }
+      s[e] = v2;
     }
   }
 }
 
-template <class F, int TPR, int NV>
-SMS_DEV void fast_fwd_compute(const FwdParams& p, const FastRow& r, uint32_t lane, bool nt,
-                              const u32x4 (&xr)[NV], const u32x4 (&mr)[NV], float* smax,
-                              float* ssum) {
+// y and dy of vector v for keys [0, kload), zeros elsewhere. Any alignment.
+template <class F>
+SMS_DEV void row_pair(const BwdRow& r, int v, float (&yv)[F::kE], float (&gv)[F::kE]) {
   constexpr int E = F::kE;
-  const int Sk = (int)p.g.Sk;
-  const int kload = r.kload;
-  const float scale = p.scale;
-  float s[NV][E];
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int k0 = (j * TPR + (int)lane) * E;
-    if (k0 < kload) {
-      F::unpack(xr[j], s[j]);
-      if (p.has_mask) {
-        float m[E];
-        F::unpack(mr[j], m);
-#pragma unroll
-        for (int e = 0; e < E; ++e) s[j][e] = fmaf(s[j][e], scale, m[e]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) s[j][e] *= scale;
-      }
-      if (k0 + E > kload) {  // the vector that holds the causal boundary
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-          if (k0 + e >= kload) s[j][e] = kNegInf;
-      }
+  constexpr int BY = F::kBytes;
+  const int k0 = v * E - r.ay;
+  if (k0 >= 0 && k0 + E <= r.kload) {
+    F::unpack(*reinterpret_cast<const u32x4*>(r.y + (int64_t)k0 * BY), yv);
+    if (r.dvec) {
+      F::unpack(*reinterpret_cast<const u32x4*>(r.d + (int64_t)k0 * BY), gv);
     } else {
 #pragma unroll
-      for (int e = 0; e < E; ++e) s[j][e] = kNegInf;
+      for (int e = 0; e < E; ++e) gv[e] = F::ld(r.d + (int64_t)(k0 + e) * BY);
+    }
+  } else {
+    // A partial vector (row head or tail, or the key bound inside it), or none
+    // of the vector's keys read: element by element, zeros outside [0, kload).
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int k = k0 + e;
+      const bool in = (k >= 0 && k < r.kload);
+      yv[e] = in ? F::ld(r.y + (int64_t)k * BY) : 0.0f;
+      gv[e] = in ? F::ld(r.d + (int64_t)k * BY) : 0.0f;
     }
   }
+}
+
+// Stores vector v of an output row (keys [0, Sk)); a whole vector goes out as
+// one 16-byte store when the output row sits at the input row's offset.
+template <class F>
+SMS_DEV void row_store(char* orow, bool ovec, int a, int v, int Sk, const float (&o)[F::kE],
+                       bool nt) {
+  constexpr int E = F::kE;
+  constexpr int BY = F::kBytes;
+  const int k0 = v * E - a;
+  if (k0 >= Sk || k0 + E <= 0) return;
+  if (ovec && k0 >= 0 && k0 + E <= Sk) {
+    st16(orow + (int64_t)k0 * BY, F::pack(o), nt);
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int k = k0 + e;
+    if (k >= 0 && k < Sk) F::st(orow + (int64_t)k * BY, o[e]);
+  }
+}
+
+// Max, exponentials (in place) and normalisation of a row held as s[NV][E];
+// k0 of vector j is (j*TPR + lane)*E - a. Returns the reciprocal sum through
+// the values: s becomes y.
+template <int TPR, int NV, int E>
+SMS_DEV void softmax_in_registers(float (&s)[NV][E], int lane, int a, int kload, float* smax,
+                                  float* ssum) {
   float mx = kNegInf;
 #pragma unroll
   for (int j = 0; j < NV; ++j)
 #pragma unroll
     for (int e = 0; e < E; ++e) mx = fmaxf(mx, s[j][e]);
   mx = row_reduce<TPR>(mx, OpMax(), smax);
+  // Every key masked: exponentiate against 0 so every term is exp(-inf) = 0.
   const float mref = (mx == kNegInf) ? 0.0f : mx;
   float sum = 0.0f;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int k0 = (j * TPR + (int)lane) * E;
+    const int k0 = (j * TPR + lane) * E - a;
     if (k0 < kload) {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
@@ -669,89 +564,169 @@ SMS_DEV void fast_fwd_compute(const FwdParams& p, const FastRow& r, uint32_t lan
     }
   }
   sum = row_reduce<TPR>(sum, OpAdd(), ssum);
-  const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;
+  const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;  // fully masked row -> zeros
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int v = j * TPR + (int)lane;
-    if (v * E < Sk) {
-      float o[E];
+  for (int j = 0; j < NV; ++j)
 #pragma unroll
-      for (int e = 0; e < E; ++e) o[e] = s[j][e] * inv;
-      st16(r.y + (int64_t)v * 16, F::pack(o), nt);
-    }
-  }
+    for (int e = 0; e < E; ++e) s[j][e] *= inv;
 }
 
+// -------------------------------------------------- general kernels (any alignment)
+
 template <class F, int TPR, int NV>
-__global__ void __launch_bounds__(block_of(TPR)) sms_fwd_fast_kernel(FastFwdArgs a) {
+__global__ void __launch_bounds__(block_of(TPR)) sms_fwd_kernel(FwdParams p) {
+  constexpr int E = F::kE;
   constexpr int RPB = block_of(TPR) / TPR;
-  constexpr int W = TPR > 64 ? TPR / 64 : 1;
-  __shared__ float red[2][W];
-  const uint32_t lane = threadIdx.x % TPR;
-  const FastRow r = fast_fwd_row<F, RPB>(a.p, blockIdx.x, threadIdx.x / TPR);
+  __shared__ float red[2][TPR > 64 ? TPR / 64 : 1];
+  const int lane = (int)(threadIdx.x % TPR);
+  const FwdRow r = fwd_row<F, RPB>(p, blockIdx.x, threadIdx.x / TPR);
   if (!r.valid) return;  // only a tail group of a TPR <= 64 launch, which has no barrier
-  u32x4 xr[NV], mr[NV];
-  fast_fwd_load<F, TPR, NV>(a.p, r, lane, (a.policy & POL_NT_LOAD) != 0, xr, mr);
-  fast_fwd_compute<F, TPR, NV>(a.p, r, lane, (a.policy & POL_NT_STORE) != 0, xr, mr, red[0],
-                               red[1]);
-}
-
-struct FastBwdArgs {
-  BwdParams p;
-  int policy;
-};
-
-struct FastBwdRow {
-  const char* y;
-  const char* d;
-  char* x;
-  int kload;
-  bool valid;
-};
-
-template <class F, int RPB>
-SMS_DEV FastBwdRow fast_bwd_row(const BwdParams& p, uint32_t slot, uint32_t local) {
-  FastBwdRow r;
-  uint32_t b = 0, h = 0, q = 0;
-  r.valid = row_coords<RPB>(p.g, slot, local, b, h, q);
-  constexpr int BY = F::kBytes;
-  const int Sk = (int)p.g.Sk;
-  r.y = p.y + ((int64_t)b * p.sy_b + (int64_t)h * p.sy_h + (int64_t)q * p.sy_q) * BY;
-  r.d = p.dy + ((int64_t)b * p.sd_b + (int64_t)h * p.sd_h + (int64_t)q * p.sd_q) * BY;
-  r.x = p.dx + ((int64_t)b * p.sx_b + (int64_t)h * p.sx_h + (int64_t)q * p.sx_q) * BY;
-  r.kload = !r.valid ? 0 : (p.causal ? (int)min((int64_t)q + 1, (int64_t)Sk) : Sk);
-  return r;
+  float s[NV][E];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) row_scores<F>(r, p.mask_kind, j * TPR + lane, p.scale, s[j]);
+  softmax_in_registers<TPR, NV, E>(s, lane, r.ax, r.kload, red[0], red[1]);
+  const bool nt = (p.policy & POL_NT_STORE) != 0;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) row_store<F>(r.y, r.yvec, r.ax, j * TPR + lane, (int)p.g.Sk, s[j], nt);
 }
 
 template <class F, int TPR, int NV>
-SMS_DEV void fast_bwd_load(const FastBwdRow& r, uint32_t lane, bool nt, u32x4 (&yr)[NV],
-                           u32x4 (&dr)[NV]) {
+__global__ void __launch_bounds__(block_of(TPR)) sms_bwd_kernel(BwdParams p) {
   constexpr int E = F::kE;
+  constexpr int RPB = block_of(TPR) / TPR;
+  __shared__ double red[TPR > 64 ? TPR / 64 : 1];
+  const int lane = (int)(threadIdx.x % TPR);
+  const BwdRow r = bwd_row<F, RPB>(p, blockIdx.x, threadIdx.x / TPR);
+  if (!r.valid) return;
+  float yv[NV][E], gv[NV][E];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) row_pair<F>(r, j * TPR + lane, yv[j], gv[j]);
+  // dot = sum_k dy_k * y_k, accumulated in fp64 (no cancellation loss when
+  // dy_k - dot is small).
+  double acc = 0.0;
+#pragma unroll
+  for (int j = 0; j < NV; ++j)
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc += F::prod(yv[j][e], gv[j][e]);
+  acc = row_reduce<TPR>(acc, OpAdd(), red);
+  const float dot_hi = (float)acc;
+  const float dot_lo = (float)(acc - (double)dot_hi);
+  const float scale = p.scale;
+  const bool nt = (p.policy & POL_NT_STORE) != 0;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int v = j * TPR + (int)lane;
-    if (v * E < r.kload) {
-      yr[j] = ld16(r.y + (int64_t)v * 16, nt);
-      dr[j] = ld16(r.d + (int64_t)v * 16, nt);
+    const int v = j * TPR + lane;
+    float o[E];
+    if (v * E - r.ay >= r.kload) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] = 0.0f;
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] = (yv[j][e] * scale) * ((gv[j][e] - dot_hi) - dot_lo);
     }
+    row_store<F>(r.x, r.xvec, r.ay, v, (int)p.g.Sk, o, nt);
+  }
+}
+
+// ---------------------------------------------------- aligned-row kernels
+//
+// When every row of every operand starts on a 16-byte line and Sk is a
+// multiple of E, every vector of a row is whole: no element accesses remain,
+// and a bound inside a vector is a register select. One workgroup per slot
+// (RPB rows), launched once: short-lived workgroups dealt in order keep the
+// set of DRAM pages in use compact, which measured faster on MI355X than a
+// persistent grid with next-row prefetch.
+
+template <class F, int TPR, int NV>
+__global__ void __launch_bounds__(block_of(TPR)) sms_fwd_fast_kernel(FwdParams p) {
+  constexpr int E = F::kE;
+  constexpr int RPB = block_of(TPR) / TPR;
+  __shared__ float red[2][TPR > 64 ? TPR / 64 : 1];
+  const int lane = (int)(threadIdx.x % TPR);
+  const FwdRow r = fwd_row<F, RPB>(p, blockIdx.x, threadIdx.x / TPR);
+  if (!r.valid) return;
+  // Host-checked: r.ax == 0 and whole-vector y and mask rows.
+  const bool ntl = (p.policy & POL_NT_LOAD) != 0;
+  const int kind = p.mask_kind;
+  const int kload = r.kload;
+  u32x4 xr[NV], mr[NV];
+  uint64_t mb[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int v = j * TPR + lane;
+    if (v * E < kload) {
+      xr[j] = ld16(r.x + (int64_t)v * 16, ntl);
+      if (kind == MASK_ADD) mr[j] = ld16(r.m + (int64_t)v * 16, false);
+      if (kind == MASK_BOOL) mb[j] = ld_bits<E>(r.m + (int64_t)v * E);
+    }
+  }
+  const float scale = p.scale;
+  float s[NV][E];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int k0 = (j * TPR + lane) * E;
+    if (k0 < kload) {
+      F::unpack(xr[j], s[j]);
+      if (kind == MASK_ADD) {
+        float m[E];
+        F::unpack(mr[j], m);
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[j][e] = fmaf(s[j][e], scale, m[e]);
+      } else if (kind == MASK_BOOL) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[j][e] = bit_set(mb[j], e) ? kNegInf : s[j][e] * scale;
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[j][e] *= scale;
+      }
+      if (k0 + E > kload) {  // the vector that holds the row's key bound
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (k0 + e >= kload) s[j][e] = kNegInf;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) s[j][e] = kNegInf;
+    }
+  }
+  softmax_in_registers<TPR, NV, E>(s, lane, 0, kload, red[0], red[1]);
+  const bool nts = (p.policy & POL_NT_STORE) != 0;
+  const int Sk = (int)p.g.Sk;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int v = j * TPR + lane;
+    if (v * E < Sk) st16(r.y + (int64_t)v * 16, F::pack(s[j]), nts);
   }
 }
 
 template <class F, int TPR, int NV>
-SMS_DEV void fast_bwd_compute(const BwdParams& p, const FastBwdRow& r, uint32_t lane, bool nt,
-                              const u32x4 (&yr)[NV], const u32x4 (&dr)[NV], double* red) {
+__global__ void __launch_bounds__(block_of(TPR)) sms_bwd_fast_kernel(BwdParams p) {
   constexpr int E = F::kE;
-  const int Sk = (int)p.g.Sk;
+  constexpr int RPB = block_of(TPR) / TPR;
+  __shared__ double red[TPR > 64 ? TPR / 64 : 1];
+  const int lane = (int)(threadIdx.x % TPR);
+  const BwdRow r = bwd_row<F, RPB>(p, blockIdx.x, threadIdx.x / TPR);
+  if (!r.valid) return;
+  const bool ntl = (p.policy & POL_NT_LOAD) != 0;
   const int kload = r.kload;
+  u32x4 yr[NV], dr[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int v = j * TPR + lane;
+    if (v * E < kload) {
+      yr[j] = ld16(r.y + (int64_t)v * 16, ntl);
+      dr[j] = ld16(r.d + (int64_t)v * 16, ntl);
+    }
+  }
   double acc = 0.0;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int k0 = (j * TPR + (int)lane) * E;
+    const int k0 = (j * TPR + lane) * E;
     if (k0 < kload) {
       float yv[E], gv[E];
       F::unpack(yr[j], yv);
       F::unpack(dr[j], gv);
-      if (k0 + E > kload) {  // keys past the causal boundary are not used
+      if (k0 + E > kload) {  // keys past the bound are not used
 #pragma unroll
         for (int e = 0; e < E; ++e)
           if (k0 + e >= kload) yv[e] = 0.0f;
@@ -764,9 +739,11 @@ SMS_DEV void fast_bwd_compute(const BwdParams& p, const FastBwdRow& r, uint32_t 
   const float dot_hi = (float)acc;
   const float dot_lo = (float)(acc - (double)dot_hi);
   const float scale = p.scale;
+  const bool nts = (p.policy & POL_NT_STORE) != 0;
+  const int Sk = (int)p.g.Sk;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int v = j * TPR + (int)lane;
+    const int v = j * TPR + lane;
     const int k0 = v * E;
     if (k0 < Sk) {
       float o[E];
@@ -785,22 +762,9 @@ SMS_DEV void fast_bwd_compute(const BwdParams& p, const FastBwdRow& r, uint32_t 
 #pragma unroll
         for (int e = 0; e < E; ++e) o[e] = 0.0f;
       }
-      st16(r.x + (int64_t)v * 16, F::pack(o), nt);
+      st16(r.x + (int64_t)v * 16, F::pack(o), nts);
     }
   }
-}
-
-template <class F, int TPR, int NV>
-__global__ void __launch_bounds__(block_of(TPR)) sms_bwd_fast_kernel(FastBwdArgs a) {
-  constexpr int RPB = block_of(TPR) / TPR;
-  constexpr int W = TPR > 64 ? TPR / 64 : 1;
-  __shared__ double red[W];
-  const uint32_t lane = threadIdx.x % TPR;
-  const FastBwdRow r = fast_bwd_row<F, RPB>(a.p, blockIdx.x, threadIdx.x / TPR);
-  if (!r.valid) return;
-  u32x4 yr[NV], dr[NV];
-  fast_bwd_load<F, TPR, NV>(r, lane, (a.policy & POL_NT_LOAD) != 0, yr, dr);
-  fast_bwd_compute<F, TPR, NV>(a.p, r, lane, (a.policy & POL_NT_STORE) != 0, yr, dr, red);
 }
 
 // ------------------------------------------------------ long rows: streaming
@@ -814,138 +778,31 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_bwd_fast_kernel(FastBwdArgs
 // merged across the workgroup. Pass 2 reads the row again and writes y. The
 // backward likewise accumulates the row's dot product in pass 1 and writes dx
 // in pass 2. The second read of a row usually hits the L2 or the Infinity
-// Cache; the HBM traffic grows by at most the re-read.
-//
-// Any alignment: vector v covers elements [v*E - a, v*E - a + E) of the row as
-// in the general kernels, with element accesses for partial vectors.
+// Cache; the HBM traffic grows by at most the re-read. Any alignment.
 
 constexpr int kStreamTpr = 1024;
 constexpr int kStreamCv = 4;
 
-// Scores of vector v of a row: x*scale + mask for keys [0, kload), -inf else.
-template <class F>
-SMS_DEV void row_scores(const char* xrow, const char* mrow, bool has_mask, bool mvec, int ax,
-                        int v, int kload, float scale, float (&s)[F::kE]) {
-  constexpr int E = F::kE;
-  constexpr int BY = F::kBytes;
-  const int k0 = v * E - ax;
-  if (k0 >= kload || k0 + E <= 0) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) s[e] = kNegInf;
-    return;
-  }
-  if (k0 >= 0 && k0 + E <= kload) {
-    // xrow + k0*BY sits on a 16-byte line: k0 + ax is a multiple of E.
-    F::unpack(*reinterpret_cast<const u32x4*>(xrow + (int64_t)k0 * BY), s);
-    if (has_mask) {
-      float m[E];
-      if (mvec) {
-        F::unpack(*reinterpret_cast<const u32x4*>(mrow + (int64_t)k0 * BY), m);
-      } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) m[e] = F::ld(mrow + (int64_t)(k0 + e) * BY);
-      }
-#pragma unroll
-      for (int e = 0; e < E; ++e) s[e] = fmaf(s[e], scale, m[e]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) s[e] *= scale;
-    }
-    return;
-  }
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int k = k0 + e;
-    if (k >= 0 && k < kload) {
-      const float xv = F::ld(xrow + (int64_t)k * BY);
-      s[e] = has_mask ? fmaf(xv, scale, F::ld(mrow + (int64_t)k * BY)) : xv * scale;
-    } else {
-      s[e] = kNegInf;
-    }
-  }
-}
-
-// y and dy of vector v for keys [0, kload), zeros elsewhere.
-template <class F>
-SMS_DEV void row_pair(const char* yrow, const char* drow, bool dvec, int ay, int v, int kload,
-                      float (&yv)[F::kE], float (&gv)[F::kE]) {
-  constexpr int E = F::kE;
-  constexpr int BY = F::kBytes;
-  const int k0 = v * E - ay;
-  if (k0 >= kload || k0 + E <= 0) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) yv[e] = gv[e] = 0.0f;
-    return;
-  }
-  if (k0 >= 0 && k0 + E <= kload) {
-    F::unpack(*reinterpret_cast<const u32x4*>(yrow + (int64_t)k0 * BY), yv);
-    if (dvec) {
-      F::unpack(*reinterpret_cast<const u32x4*>(drow + (int64_t)k0 * BY), gv);
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) gv[e] = F::ld(drow + (int64_t)(k0 + e) * BY);
-    }
-    return;
-  }
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int k = k0 + e;
-    const bool in = (k >= 0 && k < kload);
-    yv[e] = in ? F::ld(yrow + (int64_t)k * BY) : 0.0f;
-    gv[e] = in ? F::ld(drow + (int64_t)k * BY) : 0.0f;
-  }
-}
-
-// Stores vector v of an output row (keys [0, Sk)); whole vectors go out as one
-// 16-byte store when the output row has the input row's alignment.
-template <class F>
-SMS_DEV void row_store(char* orow, bool ovec, int ax, int v, int Sk, const float (&o)[F::kE]) {
-  constexpr int E = F::kE;
-  constexpr int BY = F::kBytes;
-  const int k0 = v * E - ax;
-  if (k0 >= Sk || k0 + E <= 0) return;
-  if (ovec && k0 >= 0 && k0 + E <= Sk) {
-    *reinterpret_cast<u32x4*>(orow + (int64_t)k0 * BY) = F::pack(o);
-    return;
-  }
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int k = k0 + e;
-    if (k >= 0 && k < Sk) F::st(orow + (int64_t)k * BY, o[e]);
-  }
-}
-
 template <class F>
 __global__ void __launch_bounds__(kStreamTpr) sms_fwd_stream_kernel(FwdParams p) {
   constexpr int E = F::kE;
-  constexpr int BY = F::kBytes;
   constexpr int TPR = kStreamTpr;
   constexpr int CV = kStreamCv;
   __shared__ float red[2][TPR / 64];
-  uint32_t b, h, q;
-  row_coords<1>(p.g, blockIdx.x, 0, b, h, q);  // one row per workgroup, grid = rows
+  const FwdRow r = fwd_row<F, 1>(p, blockIdx.x, 0);  // one row per workgroup, grid = rows
   const int Sk = (int)p.g.Sk;
   const int lane = (int)threadIdx.x;
-  const char* xrow = p.x + ((int64_t)b * p.sx_b + (int64_t)h * p.sx_h + (int64_t)q * p.sx_q) * BY;
-  char* yrow = p.y + ((int64_t)b * p.sy_b + (int64_t)h * p.sy_h + (int64_t)q * p.sy_q) * BY;
-  const char* mrow =
-      p.mask + ((int64_t)b * p.sm_b + (int64_t)h * p.sm_h + (int64_t)q * p.sm_q) * BY;
-  const int ax = (int)(((uintptr_t)xrow & 15) / BY);
-  const bool yvec = ((((uintptr_t)yrow & 15) / BY) == (uintptr_t)ax);
-  const bool mvec = p.has_mask && ((((uintptr_t)mrow & 15) / BY) == (uintptr_t)ax);
-  const bool has_mask = p.has_mask != 0;
-  const int kload = p.causal ? (int)min((int64_t)q + 1, (int64_t)Sk) : Sk;
-  const int nvec = (int)(((int64_t)ax + kload + E - 1) / E);  // vectors holding read keys
-  const int nvec_out = (int)(((int64_t)ax + Sk + E - 1) / E);
+  const int kind = p.mask_kind;
   const float scale = p.scale;
+  const int nvec = (int)(((int64_t)r.ax + r.kload + E - 1) / E);  // vectors holding read keys
+  const int nvec_out = (int)(((int64_t)r.ax + Sk + E - 1) / E);
 
   // Pass 1: per-lane running (max, rescaled sum).
   float m_run = kNegInf, l_run = 0.0f;
   for (int base = 0; base < nvec; base += TPR * CV) {
     float s[CV][E];
 #pragma unroll
-    for (int j = 0; j < CV; ++j)
-      row_scores<F>(xrow, mrow, has_mask, mvec, ax, base + j * TPR + lane, kload, scale, s[j]);
+    for (int j = 0; j < CV; ++j) row_scores<F>(r, kind, base + j * TPR + lane, scale, s[j]);
     float cm = kNegInf;
 #pragma unroll
     for (int j = 0; j < CV; ++j)
@@ -970,20 +827,21 @@ __global__ void __launch_bounds__(kStreamTpr) sms_fwd_stream_kernel(FwdParams p)
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;  // fully masked row -> zeros
 
   // Pass 2: y over the whole row.
+  const bool nt = (p.policy & POL_NT_STORE) != 0;
   for (int base = 0; base < nvec_out; base += TPR * CV) {
 #pragma unroll
     for (int j = 0; j < CV; ++j) {
       const int v = base + j * TPR + lane;
       float o[E];
-      if (v * E - ax >= kload) {
+      if (v * E - r.ax >= r.kload) {
 #pragma unroll
         for (int e = 0; e < E; ++e) o[e] = 0.0f;
       } else {
-        row_scores<F>(xrow, mrow, has_mask, mvec, ax, v, kload, scale, o);
+        row_scores<F>(r, kind, v, scale, o);
 #pragma unroll
         for (int e = 0; e < E; ++e) o[e] = exp_biased(o[e], mref) * inv;
       }
-      row_store<F>(yrow, yvec, ax, v, Sk, o);
+      row_store<F>(r.y, r.yvec, r.ax, v, Sk, o, nt);
     }
   }
 }
@@ -991,23 +849,14 @@ __global__ void __launch_bounds__(kStreamTpr) sms_fwd_stream_kernel(FwdParams p)
 template <class F>
 __global__ void __launch_bounds__(kStreamTpr) sms_bwd_stream_kernel(BwdParams p) {
   constexpr int E = F::kE;
-  constexpr int BY = F::kBytes;
   constexpr int TPR = kStreamTpr;
   constexpr int CV = kStreamCv;
   __shared__ double red[TPR / 64];
-  uint32_t b, h, q;
-  row_coords<1>(p.g, blockIdx.x, 0, b, h, q);
+  const BwdRow r = bwd_row<F, 1>(p, blockIdx.x, 0);
   const int Sk = (int)p.g.Sk;
   const int lane = (int)threadIdx.x;
-  const char* yrow = p.y + ((int64_t)b * p.sy_b + (int64_t)h * p.sy_h + (int64_t)q * p.sy_q) * BY;
-  const char* drow = p.dy + ((int64_t)b * p.sd_b + (int64_t)h * p.sd_h + (int64_t)q * p.sd_q) * BY;
-  char* xrow = p.dx + ((int64_t)b * p.sx_b + (int64_t)h * p.sx_h + (int64_t)q * p.sx_q) * BY;
-  const int ay = (int)(((uintptr_t)yrow & 15) / BY);
-  const bool dvec = ((((uintptr_t)drow & 15) / BY) == (uintptr_t)ay);
-  const bool xvec = ((((uintptr_t)xrow & 15) / BY) == (uintptr_t)ay);
-  const int kload = p.causal ? (int)min((int64_t)q + 1, (int64_t)Sk) : Sk;
-  const int nvec = (int)(((int64_t)ay + kload + E - 1) / E);
-  const int nvec_out = (int)(((int64_t)ay + Sk + E - 1) / E);
+  const int nvec = (int)(((int64_t)r.ay + r.kload + E - 1) / E);
+  const int nvec_out = (int)(((int64_t)r.ay + Sk + E - 1) / E);
 
   // Pass 1: the row's dot product, in fp64.
   double acc = 0.0;
@@ -1015,7 +864,7 @@ __global__ void __launch_bounds__(kStreamTpr) sms_bwd_stream_kernel(BwdParams p)
 #pragma unroll
     for (int j = 0; j < CV; ++j) {
       float yv[E], gv[E];
-      row_pair<F>(yrow, drow, dvec, ay, base + j * TPR + lane, kload, yv, gv);
+      row_pair<F>(r, base + j * TPR + lane, yv, gv);
 #pragma unroll
       for (int e = 0; e < E; ++e) acc += F::prod(yv[e], gv[e]);
     }
@@ -1026,137 +875,86 @@ __global__ void __launch_bounds__(kStreamTpr) sms_bwd_stream_kernel(BwdParams p)
   const float scale = p.scale;
 
   // Pass 2: dx over the whole row.
+  const bool nt = (p.policy & POL_NT_STORE) != 0;
   for (int base = 0; base < nvec_out; base += TPR * CV) {
 #pragma unroll
     for (int j = 0; j < CV; ++j) {
       const int v = base + j * TPR + lane;
       float o[E];
-      if (v * E - ay >= kload) {
+      if (v * E - r.ay >= r.kload) {
 #pragma unroll
         for (int e = 0; e < E; ++e) o[e] = 0.0f;
       } else {
         float yv[E], gv[E];
-        row_pair<F>(yrow, drow, dvec, ay, v, kload, yv, gv);
+        row_pair<F>(r, v, yv, gv);
 #pragma unroll
         for (int e = 0; e < E; ++e) o[e] = (yv[e] * scale) * ((gv[e] - dot_hi) - dot_lo);
       }
-      row_store<F>(xrow, xvec, ay, v, Sk, o);
+      row_store<F>(r.x, r.xvec, r.ay, v, Sk, o, nt);
     }
   }
 }
 
-template <class F>
-hipError_t launch_stream(const FwdParams* fp, const BwdParams* bp, uint32_t rows,
-                         hipStream_t st) {
-  if (fp)
-    hipLaunchKernelGGL((sms_fwd_stream_kernel<F>), dim3(rows), dim3(kStreamTpr), 0, st, *fp);
-  else
-    hipLaunchKernelGGL((sms_bwd_stream_kernel<F>), dim3(rows), dim3(kStreamTpr), 0, st, *bp);
-  return hipGetLastError();
-}
-
 // --------------------------------------------------------------- launchers
+
+// Kernel families.
+enum : int { FAMILY_GENERAL = 0, FAMILY_ALIGNED = 1, FAMILY_STREAM = 2 };
 
 // TPR and NV values the library is built with.
 constexpr int kTprList[] = {4, 8, 16, 32, 64, 128, 256, 512, 1024};
 constexpr int kNvList[] = {1, 2, 4};
 
-template <class F, int TPR>
-hipError_t launch_fwd_tpr(const FwdParams& p, int nv, uint32_t blocks, hipStream_t st) {
-  const dim3 grid(blocks), block(block_of(TPR));
-  switch (nv) {
-    case 1: hipLaunchKernelGGL((sms_fwd_kernel<F, TPR, 1>), grid, block, 0, st, p); break;
-    case 2: hipLaunchKernelGGL((sms_fwd_kernel<F, TPR, 2>), grid, block, 0, st, p); break;
-    case 4: hipLaunchKernelGGL((sms_fwd_kernel<F, TPR, 4>), grid, block, 0, st, p); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-template <class F, int TPR>
-hipError_t launch_bwd_tpr(const BwdParams& p, int nv, uint32_t blocks, hipStream_t st) {
-  const dim3 grid(blocks), block(block_of(TPR));
-  switch (nv) {
-    case 1: hipLaunchKernelGGL((sms_bwd_kernel<F, TPR, 1>), grid, block, 0, st, p); break;
-    case 2: hipLaunchKernelGGL((sms_bwd_kernel<F, TPR, 2>), grid, block, 0, st, p); break;
-    case 4: hipLaunchKernelGGL((sms_bwd_kernel<F, TPR, 4>), grid, block, 0, st, p); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
 template <class F, int TPR, int NV>
-hipError_t launch_fwd_fast_nv(const FastFwdArgs& a, uint32_t blocks, hipStream_t st) {
-  hipLaunchKernelGGL((sms_fwd_fast_kernel<F, TPR, NV>), dim3(blocks), dim3(block_of(TPR)), 0, st, a);
-  return hipGetLastError();
-}
-
-template <class F, int TPR, int NV>
-hipError_t launch_bwd_fast_nv(const FastBwdArgs& a, uint32_t blocks, hipStream_t st) {
-  hipLaunchKernelGGL((sms_bwd_fast_kernel<F, TPR, NV>), dim3(blocks), dim3(block_of(TPR)), 0, st, a);
+hipError_t launch_nv(const FwdParams* fp, const BwdParams* bp, int family, uint32_t blocks,
+                     hipStream_t st) {
+  const dim3 grid(blocks), block(block_of(TPR));
+  if (fp) {
+    if (family == FAMILY_ALIGNED)
+      hipLaunchKernelGGL((sms_fwd_fast_kernel<F, TPR, NV>), grid, block, 0, st, *fp);
+    else
+      hipLaunchKernelGGL((sms_fwd_kernel<F, TPR, NV>), grid, block, 0, st, *fp);
+  } else {
+    if (family == FAMILY_ALIGNED)
+      hipLaunchKernelGGL((sms_bwd_fast_kernel<F, TPR, NV>), grid, block, 0, st, *bp);
+    else
+      hipLaunchKernelGGL((sms_bwd_kernel<F, TPR, NV>), grid, block, 0, st, *bp);
+  }
   return hipGetLastError();
 }
 
 template <class F, int TPR>
-hipError_t launch_fast_tpr(const FastFwdArgs* fa, const FastBwdArgs* ba, int nv, uint32_t blocks,
-                           hipStream_t st) {
+hipError_t launch_tpr(const FwdParams* fp, const BwdParams* bp, int family, int nv,
+                      uint32_t blocks, hipStream_t st) {
   switch (nv) {
-    case 1: return fa ? launch_fwd_fast_nv<F, TPR, 1>(*fa, blocks, st)
-                      : launch_bwd_fast_nv<F, TPR, 1>(*ba, blocks, st);
-    case 2: return fa ? launch_fwd_fast_nv<F, TPR, 2>(*fa, blocks, st)
-                      : launch_bwd_fast_nv<F, TPR, 2>(*ba, blocks, st);
-    case 4: return fa ? launch_fwd_fast_nv<F, TPR, 4>(*fa, blocks, st)
-                      : launch_bwd_fast_nv<F, TPR, 4>(*ba, blocks, st);
+    case 1: return launch_nv<F, TPR, 1>(fp, bp, family, blocks, st);
+    case 2: return launch_nv<F, TPR, 2>(fp, bp, family, blocks, st);
+    case 4: return launch_nv<F, TPR, 4>(fp, bp, family, blocks, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-// Fast path (aligned rows): exactly one of fa / ba is non-null.
+// One launch: exactly one of fp / bp is non-null. The streaming family
+// ignores tpr / nv and takes one workgroup per row (blocks = rows).
 template <class F>
-hipError_t launch_fast(const FastFwdArgs* fa, const FastBwdArgs* ba, int tpr, int nv,
-                       uint32_t blocks, hipStream_t st) {
-  switch (tpr) {
-    case 4: return launch_fast_tpr<F, 4>(fa, ba, nv, blocks, st);
-    case 8: return launch_fast_tpr<F, 8>(fa, ba, nv, blocks, st);
-    case 16: return launch_fast_tpr<F, 16>(fa, ba, nv, blocks, st);
-    case 32: return launch_fast_tpr<F, 32>(fa, ba, nv, blocks, st);
-    case 64: return launch_fast_tpr<F, 64>(fa, ba, nv, blocks, st);
-    case 128: return launch_fast_tpr<F, 128>(fa, ba, nv, blocks, st);
-    case 256: return launch_fast_tpr<F, 256>(fa, ba, nv, blocks, st);
-    case 512: return launch_fast_tpr<F, 512>(fa, ba, nv, blocks, st);
-    case 1024: return launch_fast_tpr<F, 1024>(fa, ba, nv, blocks, st);
-    default: return hipErrorInvalidValue;
+hipError_t launch(const FwdParams* fp, const BwdParams* bp, int family, int tpr, int nv,
+                  uint32_t blocks, hipStream_t st) {
+  if (family == FAMILY_STREAM) {
+    if (fp)
+      hipLaunchKernelGGL((sms_fwd_stream_kernel<F>), dim3(blocks), dim3(kStreamTpr), 0, st, *fp);
+    else
+      hipLaunchKernelGGL((sms_bwd_stream_kernel<F>), dim3(blocks), dim3(kStreamTpr), 0, st, *bp);
+    return hipGetLastError();
   }
-}
-
-template <class F>
-hipError_t launch_fwd(const FwdParams& p, int tpr, int nv, uint32_t blocks, hipStream_t st) {
   switch (tpr) {
-    case 4: return launch_fwd_tpr<F, 4>(p, nv, blocks, st);
-    case 8: return launch_fwd_tpr<F, 8>(p, nv, blocks, st);
-    case 16: return launch_fwd_tpr<F, 16>(p, nv, blocks, st);
-    case 32: return launch_fwd_tpr<F, 32>(p, nv, blocks, st);
-    case 64: return launch_fwd_tpr<F, 64>(p, nv, blocks, st);
-    case 128: return launch_fwd_tpr<F, 128>(p, nv, blocks, st);
-    case 256: return launch_fwd_tpr<F, 256>(p, nv, blocks, st);
-    case 512: return launch_fwd_tpr<F, 512>(p, nv, blocks, st);
-    case 1024: return launch_fwd_tpr<F, 1024>(p, nv, blocks, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-template <class F>
-hipError_t launch_bwd(const BwdParams& p, int tpr, int nv, uint32_t blocks, hipStream_t st) {
-  switch (tpr) {
-    case 4: return launch_bwd_tpr<F, 4>(p, nv, blocks, st);
-    case 8: return launch_bwd_tpr<F, 8>(p, nv, blocks, st);
-    case 16: return launch_bwd_tpr<F, 16>(p, nv, blocks, st);
-    case 32: return launch_bwd_tpr<F, 32>(p, nv, blocks, st);
-    case 64: return launch_bwd_tpr<F, 64>(p, nv, blocks, st);
-    case 128: return launch_bwd_tpr<F, 128>(p, nv, blocks, st);
-    case 256: return launch_bwd_tpr<F, 256>(p, nv, blocks, st);
-    case 512: return launch_bwd_tpr<F, 512>(p, nv, blocks, st);
-    case 1024: return launch_bwd_tpr<F, 1024>(p, nv, blocks, st);
+    case 4: return launch_tpr<F, 4>(fp, bp, family, nv, blocks, st);
+    case 8: return launch_tpr<F, 8>(fp, bp, family, nv, blocks, st);
+    case 16: return launch_tpr<F, 16>(fp, bp, family, nv, blocks, st);
+    case 32: return launch_tpr<F, 32>(fp, bp, family, nv, blocks, st);
+    case 64: return launch_tpr<F, 64>(fp, bp, family, nv, blocks, st);
+    case 128: return launch_tpr<F, 128>(fp, bp, family, nv, blocks, st);
+    case 256: return launch_tpr<F, 256>(fp, bp, family, nv, blocks, st);
+    case 512: return launch_tpr<F, 512>(fp, bp, family, nv, blocks, st);
+    case 1024: return launch_tpr<F, 1024>(fp, bp, family, nv, blocks, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1164,21 +962,9 @@ hipError_t launch_bwd(const BwdParams& p, int tpr, int nv, uint32_t blocks, hipS
 }  // namespace sms
 
 // Per-format launch entry points, one translation unit each (inst_*.hip).
-hipError_t sms_launch_fwd_f32(const sms::FwdParams&, int tpr, int nv, uint32_t blocks, hipStream_t);
-hipError_t sms_launch_fwd_f16(const sms::FwdParams&, int tpr, int nv, uint32_t blocks, hipStream_t);
-hipError_t sms_launch_fwd_bf16(const sms::FwdParams&, int tpr, int nv, uint32_t blocks, hipStream_t);
-hipError_t sms_launch_bwd_f32(const sms::BwdParams&, int tpr, int nv, uint32_t blocks, hipStream_t);
-hipError_t sms_launch_bwd_f16(const sms::BwdParams&, int tpr, int nv, uint32_t blocks, hipStream_t);
-hipError_t sms_launch_bwd_bf16(const sms::BwdParams&, int tpr, int nv, uint32_t blocks, hipStream_t);
-hipError_t sms_launch_stream_f32(const sms::FwdParams*, const sms::BwdParams*, uint32_t rows,
-                                 hipStream_t);
-hipError_t sms_launch_stream_f16(const sms::FwdParams*, const sms::BwdParams*, uint32_t rows,
-                                 hipStream_t);
-hipError_t sms_launch_stream_bf16(const sms::FwdParams*, const sms::BwdParams*, uint32_t rows,
-                                  hipStream_t);
-hipError_t sms_launch_fast_f32(const sms::FastFwdArgs*, const sms::FastBwdArgs*, int tpr, int nv,
-                               uint32_t blocks, hipStream_t);
-hipError_t sms_launch_fast_f16(const sms::FastFwdArgs*, const sms::FastBwdArgs*, int tpr, int nv,
-                               uint32_t blocks, hipStream_t);
-hipError_t sms_launch_fast_bf16(const sms::FastFwdArgs*, const sms::FastBwdArgs*, int tpr, int nv,
-                                uint32_t blocks, hipStream_t);
+hipError_t sms_launch_f32(const sms::FwdParams*, const sms::BwdParams*, int family, int tpr,
+                          int nv, uint32_t blocks, hipStream_t);
+hipError_t sms_launch_f16(const sms::FwdParams*, const sms::BwdParams*, int family, int tpr,
+                          int nv, uint32_t blocks, hipStream_t);
+hipError_t sms_launch_bf16(const sms::FwdParams*, const sms::BwdParams*, int family, int tpr,
+                           int nv, uint32_t blocks, hipStream_t);

@@ -41,16 +41,37 @@ def _strides(t):
     return _lib.strides4(st)
 
 
+_INT_DTYPES = (torch.int32, torch.int64)
+_BOOL_DTYPES = (torch.bool, torch.uint8)
+
+
+def mask_kind_of(mask):
+    """"none", "bool" (torch.bool / uint8: nonzero excludes the key), "lengths"
+    (an integer tensor of per-batch key lengths) or "additive"."""
+    if mask is None:
+        return "none"
+    if mask.dtype in _BOOL_DTYPES:
+        return "bool"
+    if mask.dtype in _INT_DTYPES:
+        return "lengths"
+    return "additive"
+
+
 def mask_mode_of(mask, shape):
-    """Mask-broadcast mode for an additive mask of ``mask.shape`` against x of ``shape``.
+    """Mask shape mode for ``mask`` against x of ``shape``.
 
     [Sq,Sk] or [1,1,Sq,Sk] -> "sq_sk"; [B,Sq,Sk] or [B,1,Sq,Sk] -> "b_sq_sk";
-    [B,1,Sk] or [B,1,1,Sk] -> "b_1_sk"; [B,H,Sq,Sk] -> "full".
+    [B,1,Sk] or [B,1,1,Sk] -> "b_1_sk"; [B,H,Sq,Sk] -> "full"; an integer
+    tensor of shape [B] -> "key_lengths".
     """
     if mask is None:
         return "none"
     B, H, Sq, Sk = shape
     ms = tuple(mask.shape)
+    if mask_kind_of(mask) == "lengths":
+        if ms != (B,):
+            raise ValueError(f"key lengths must have shape [B] = ({B},), got {ms}")
+        return "key_lengths"
     table = [
         ((Sq, Sk), "sq_sk"), ((1, 1, Sq, Sk), "sq_sk"),
         ((B, Sq, Sk), "b_sq_sk"), ((B, 1, Sq, Sk), "b_sq_sk"),
@@ -64,6 +85,21 @@ def mask_mode_of(mask, shape):
                      f"for x of shape {tuple(shape)}")
 
 
+def causal_code(is_causal):
+    """False / None / "none" -> 0; True / "top_left" -> 1 (key k > q excluded);
+    "bottom_right" -> 2 (key k > q + Sk - Sq excluded)."""
+    if is_causal is None or is_causal is False:
+        return 0
+    if is_causal is True:
+        return 1
+    if isinstance(is_causal, str) and is_causal in _lib.CAUSAL_CODES:
+        return _lib.CAUSAL_CODES[is_causal]
+    if isinstance(is_causal, int) and is_causal in (0, 1, 2):
+        return is_causal
+    raise ValueError(f"is_causal must be False, True, 'top_left' or 'bottom_right', "
+                     f"got {is_causal!r}")
+
+
 def _stream_handle(device, stream):
     s = stream if stream is not None else torch.cuda.current_stream(device)
     return s.cuda_stream
@@ -73,9 +109,11 @@ def sms_forward(x, mask, y, scale=1.0, is_causal=False, stream=None):
     """y <- softmax(x*scale + mask) over the last axis (C ABI sms_forward).
 
     x, y: 4-D GPU tensors of one shape and dtype (float32/float16/bfloat16), key
-    axis contiguous; y may be x itself (in place). mask: None or an additive mask
-    of x's dtype, contiguous, in one of the shapes ``mask_mode_of`` accepts.
-    Enqueued on ``stream`` (default: the current stream); returns y.
+    axis contiguous; y may be x itself (in place). mask: None; an additive mask
+    of x's dtype; a boolean mask (torch.bool or uint8, nonzero = key excluded);
+    both contiguous, in one of the shapes ``mask_mode_of`` accepts; or int32 key
+    lengths of shape [B]. is_causal: see ``causal_code``. Enqueued on ``stream``
+    (default: the current stream); returns y.
     """
     _require_gpu(x, "x")
     _require_gpu(y, "y")
@@ -85,12 +123,17 @@ def sms_forward(x, mask, y, scale=1.0, is_causal=False, stream=None):
         raise ValueError("y must have x's shape, dtype and device")
     code = _dtype_code(x, "x")
     mode = mask_mode_of(mask, tuple(x.shape))
+    kind = mask_kind_of(mask)
+    mode_code = _lib.MASK_MODES[mode]
     mptr = None
     if mask is not None:
         _require_gpu(mask, "mask")
-        if mask.dtype != x.dtype:
-            raise TypeError(f"mask dtype {mask.dtype} must equal x dtype {x.dtype} "
-                            "(an additive mask; convert boolean masks to 0/-inf first)")
+        if kind == "additive" and mask.dtype != x.dtype:
+            raise TypeError(f"additive mask dtype {mask.dtype} must equal x dtype {x.dtype}")
+        if kind == "lengths" and mask.dtype != torch.int32:
+            raise TypeError("key lengths must be int32")
+        if kind == "bool":
+            mode_code |= _lib.MASK_BOOL
         if mask.device != x.device:
             raise ValueError("mask must be on x's device")
         if not mask.is_contiguous():
@@ -99,8 +142,8 @@ def sms_forward(x, mask, y, scale=1.0, is_causal=False, stream=None):
     B, H, Sq, Sk = x.shape
     L = _lib.lib()
     with torch.cuda.device(x.device):
-        st = L.sms_forward(x.data_ptr(), _strides(x), mptr, _lib.MASK_MODES[mode], y.data_ptr(),
-                           _strides(y), code, B, H, Sq, Sk, float(scale), int(bool(is_causal)),
+        st = L.sms_forward(x.data_ptr(), _strides(x), mptr, mode_code, y.data_ptr(),
+                           _strides(y), code, B, H, Sq, Sk, float(scale), causal_code(is_causal),
                            _stream_handle(x.device, stream))
     _lib.check("sms_forward", st)
     return y
@@ -110,8 +153,9 @@ def sms_backward(y, dy, dx, scale=1.0, is_causal=False, stream=None):
     """dx <- scale * y * (dy - sum_k dy_k y_k) row by row (C ABI sms_backward).
 
     y, dy, dx: 4-D GPU tensors of one shape and dtype, key axis contiguous; dx
-    may be dy or y itself. ``is_causal`` promises y == 0 at keys after the query
-    (true for y from a causal forward); those keys are then skipped.
+    may be dy or y itself. A causal ``is_causal`` (see ``causal_code``) promises
+    y == 0 at the keys that rule excludes (true for y from a forward with the
+    same rule); those keys are then skipped.
     """
     for t, n in ((y, "y"), (dy, "dy"), (dx, "dx")):
         _require_gpu(t, n)
@@ -124,7 +168,7 @@ def sms_backward(y, dy, dx, scale=1.0, is_causal=False, stream=None):
     with torch.cuda.device(y.device):
         st = L.sms_backward(y.data_ptr(), _strides(y), dy.data_ptr(), _strides(dy), dx.data_ptr(),
                             _strides(dx), code, B, H, Sq, Sk, float(scale),
-                            int(bool(is_causal)), _stream_handle(y.device, stream))
+                            causal_code(is_causal), _stream_handle(y.device, stream))
     _lib.check("sms_backward", st)
     return dx
 
@@ -150,12 +194,15 @@ class ScaledMaskSoftmaxFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x, mask, scale, is_causal):
         x = _rows_view(x)
-        if mask is not None and not mask.is_contiguous():
-            mask = mask.contiguous()
+        if mask is not None:
+            if mask.dtype == torch.int64:  # key lengths: the C ABI takes int32
+                mask = mask.to(torch.int32)
+            if not mask.is_contiguous():
+                mask = mask.contiguous()
         y = torch.empty_like(x, memory_format=torch.contiguous_format)
         sms_forward(x, mask, y, scale, is_causal)
         ctx.scale = float(scale)
-        ctx.is_causal = bool(is_causal)
+        ctx.is_causal = causal_code(is_causal)
         ctx.save_for_backward(y)
         return y
 
@@ -169,5 +216,10 @@ class ScaledMaskSoftmaxFunction(torch.autograd.Function):
 
 
 def scaled_mask_softmax(x, mask=None, scale=1.0, is_causal=False):
-    """softmax(x*scale + mask) over the last axis of a 4-D GPU tensor, differentiable in x."""
+    """softmax(x*scale + mask) over the last axis of a 4-D GPU tensor, differentiable in x.
+
+    mask: None, an additive mask (x's dtype), a boolean mask (True = excluded)
+    or integer key lengths [B]; is_causal: False, True ("top_left") or
+    "bottom_right".
+    """
     return ScaledMaskSoftmaxFunction.apply(x, mask, scale, is_causal)

@@ -86,6 +86,8 @@ def draw_mask(shape4, mode, dtype, kind, seed, device):
     kind = ("bernoulli_neginf", p): -inf with probability p at each position,
       0 elsewhere; the diagonal (key == query) is never masked.
     kind = ("normal", sigma): finite N(0, sigma^2) values (a generic additive bias).
+    kind = ("bool", p): a boolean mask, True (key excluded) with probability p,
+      the diagonal never excluded; ``dtype`` is ignored.
     """
     if mode == "none":
         return None
@@ -117,7 +119,24 @@ def draw_mask(shape4, mode, dtype, kind, seed, device):
     if kind[0] == "normal":
         v = torch.randn(mshape, generator=g, device=device, dtype=torch.float32)
         return v.mul_(kind[1]).to(td)
+    if kind[0] == "bool":
+        # True (excluded) with probability p; the diagonal is never excluded.
+        p = kind[1]
+        u = torch.rand(mshape, generator=g, device=device, dtype=torch.float32)
+        m = u < p
+        if mode in ("sq_sk", "b_sq_sk", "full"):
+            n = min(Sq, Sk)
+            idx = torch.arange(n, device=device)
+            m[..., idx, idx] = False
+        return m
     raise ValueError(kind)
+
+
+def draw_lengths(B, lo, hi, seed, device):
+    """Per-batch key lengths, integers drawn uniformly from lo..hi inclusive (int32)."""
+    g = _gen(seed, device)
+    return torch.randint(lo, hi + 1, (B,), generator=g, device=device, dtype=torch.int64).to(
+        torch.int32)
 
 
 def draw_dy(shape, dtype, seed, device):

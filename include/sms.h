@@ -5,15 +5,18 @@
  * The operation, for every row (b, h, q) of a score tensor x[B, H, Sq, Sk]:
  *
  *     s_k = x[b,h,q,k] * scale + mask[.., k]        (mask optional, additive)
- *     s_k = -inf                 if is_causal and k > q
+ *     s_k = -inf                 if key k is excluded (boolean mask, key
+ *                                length, or the causal rule)
  *     y[b,h,q,k] = exp(s_k - max_j s_j) / sum_j exp(s_j - max_j s_j)
  *
  * as defined in lmnt.cn "Custom fused Softmax operator in CUDA, wrapped into
  * PyTorch", sec. 1.2 (scaled scores plus an additive mask, softmax over the key
  * axis; causal hides key j > query i) and sec. 2.1 (subtract the row maximum);
- * the causal rule is applied after the additive mask (sec. 3.1). A row whose
- * every key is masked is written as all zeros instead of 0/0 (pnsm.cn article on
- * a custom ScaledMaskSoftmax operator, sec. 4.2 and 4.3).
+ * the causal rule is applied after the additive mask (sec. 3.1). A boolean mask
+ * excludes keys inside the kernel instead of adding a large negative value
+ * (pnsm.cn article on a custom ScaledMaskSoftmax operator, sec. 2.3). A row whose
+ * every key is excluded is written as all zeros instead of 0/0 (same article,
+ * sec. 4.2 and 4.3).
  *
  * The backward (same lmnt.cn page, sec. 3.3) is
  *
@@ -55,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SMS_ABI_VERSION 1
+#define SMS_ABI_VERSION 2
 
 typedef enum {
   SMS_OK = 0,
@@ -65,7 +68,8 @@ typedef enum {
   SMS_ERR_DTYPE = 4,     /* unknown dtype                                         */
   SMS_ERR_MASK_MODE = 5, /* unknown mask mode                                     */
   SMS_ERR_ALIGN = 6,     /* a pointer not aligned to its element size             */
-  SMS_ERR_HIP = 7        /* the HIP runtime reported an error for the launch      */
+  SMS_ERR_HIP = 7,       /* the HIP runtime reported an error for the launch      */
+  SMS_ERR_CAUSAL = 8     /* unknown causal mode                                   */
 } sms_status;
 
 typedef enum {
@@ -74,33 +78,53 @@ typedef enum {
   SMS_BF16 = 2  /* bfloat16 (upper 16 bits of a binary32 value) */
 } sms_dtype;
 
-/* The additive mask's own shape; it has x's dtype and is contiguous (row-major)
- * in that shape. Axes it lacks are broadcast. The shapes follow the pnsm.cn
- * ScaledMaskSoftmax article, sec. 2.1 ([Sq,Sk] shared by all samples, or
- * [B,Sq,Sk] per sample), the lmnt.cn page's full mask (sec. 5.1 test), and a
- * per-batch key-padding mask [B,1,Sk]. */
+/* The mask's own shape; the mask is contiguous (row-major) in that shape and
+ * axes it lacks are broadcast. The shapes follow the pnsm.cn ScaledMaskSoftmax
+ * article, sec. 2.1 ([Sq,Sk] shared by all samples, or [B,Sq,Sk] per sample),
+ * the lmnt.cn page's full mask (sec. 5.1 test), a per-batch key-padding mask
+ * [B,1,Sk], and key padding given as lengths.
+ *
+ * Modes 1-4 alone: an ADDITIVE mask with x's dtype (0 keeps a key; a large
+ * negative value or -inf masks it). Modes 1-4 OR'ed with SMS_MASK_BOOL: a
+ * BOOLEAN mask of one byte per key, nonzero = the key is excluded (score
+ * -inf), zero = kept. SMS_MASK_KEY_LENGTHS: `mask` points to int32 lengths[B];
+ * keys k >= lengths[b] are excluded (lengths <= 0 exclude every key, lengths
+ * >= Sk none), and no per-key mask is read. */
 typedef enum {
-  SMS_MASK_NONE = 0,    /* no mask; the mask pointer is ignored                */
-  SMS_MASK_SQ_SK = 1,   /* [Sq, Sk],     broadcast over B and H                */
-  SMS_MASK_B_SQ_SK = 2, /* [B, Sq, Sk],  broadcast over H                      */
-  SMS_MASK_B_1_SK = 3,  /* [B, 1, Sk],   broadcast over H and Sq (key padding) */
-  SMS_MASK_FULL = 4     /* [B, H, Sq, Sk]                                      */
+  SMS_MASK_NONE = 0,        /* no mask; the mask pointer is ignored                */
+  SMS_MASK_SQ_SK = 1,       /* [Sq, Sk],     broadcast over B and H                */
+  SMS_MASK_B_SQ_SK = 2,     /* [B, Sq, Sk],  broadcast over H                      */
+  SMS_MASK_B_1_SK = 3,      /* [B, 1, Sk],   broadcast over H and Sq (key padding) */
+  SMS_MASK_FULL = 4,        /* [B, H, Sq, Sk]                                      */
+  SMS_MASK_KEY_LENGTHS = 5  /* int32 lengths [B]: keys k >= lengths[b] excluded    */
 } sms_mask_mode;
+
+#define SMS_MASK_BOOL 0x10  /* OR with modes 1-4: uint8 mask, nonzero = excluded */
+
+/* Causal rule: key k of row (b, h, q) is excluded when k > q (TOP_LEFT: query q
+ * sees keys 0..q, as on the lmnt.cn page, sec. 1.2) or when k > q + Sk - Sq
+ * (BOTTOM_RIGHT: the last query sees every key; for Sq != Sk, e.g. queries that
+ * continue a longer key sequence). Both are the same rule when Sq == Sk. */
+typedef enum {
+  SMS_CAUSAL_NONE = 0,
+  SMS_CAUSAL_TOP_LEFT = 1,
+  SMS_CAUSAL_BOTTOM_RIGHT = 2
+} sms_causal;
 
 /*
  * sms_forward -- y = softmax(x * scale + mask) over the key axis, with the
- * optional causal rule (key k > query q masked, q = the row's index on the Sq
- * axis).
+ * optional causal rule (q = the row's index on the Sq axis).
  *
  *   x, x_strides   input scores [B,H,Sq,Sk] (dtype), device memory
- *   mask           additive mask in the shape `mask_mode` names (dtype, device,
- *                  contiguous); may be NULL only with SMS_MASK_NONE. Values are
- *                  finite or -inf.
+ *   mask           device memory as `mask_mode` describes (additive: dtype,
+ *                  values finite or -inf; boolean: uint8; lengths: int32);
+ *                  may be NULL only with SMS_MASK_NONE
+ *   mask_mode      an sms_mask_mode, modes 1-4 optionally OR'ed with SMS_MASK_BOOL
  *   y, y_strides   output [B,H,Sq,Sk] (dtype), device memory; every element of
- *                  every row is written (0 where masked or causal-future, all
- *                  zeros for a row with every key masked)
+ *                  every row is written (0 where excluded, all zeros for a row
+ *                  with every key excluded)
  *   scale          multiplier applied to x before the mask (e.g. 1/sqrt(d_k))
- *   is_causal      nonzero: keys k > q are masked after the additive mask
+ *   is_causal      an sms_causal value; the causal rule is applied after the mask
  *   stream         hipStream_t to enqueue on
  *
  * Limits: B*H*Sq < 2^32 rows, Sk <= sms_max_sk(dtype) = 2^30, and at most
@@ -109,7 +133,7 @@ typedef enum {
  * Longer rows cost a second read of the row (two passes).
  */
 sms_status sms_forward(const void* x, const int64_t x_strides[4],
-                       const void* mask, sms_mask_mode mask_mode,
+                       const void* mask, int mask_mode,
                        void* y, const int64_t y_strides[4],
                        sms_dtype dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk,
                        float scale, int is_causal, void* stream);
@@ -121,9 +145,10 @@ sms_status sms_forward(const void* x, const int64_t x_strides[4],
  *   dy, dy_strides   upstream gradient (dtype), device memory
  *   dx, dx_strides   output gradient (dtype), device memory; every element written
  *   scale            the forward's scale
- *   is_causal        nonzero: a promise that y is 0 at keys k > q (true of any y
- *                    sms_forward wrote with is_causal set); those y and dy are
- *                    then not read and dx there is written as 0. Zero is always
+ *   is_causal        an sms_causal value other than NONE is a promise that y is
+ *                    0 at the keys that rule excludes (true of any y sms_forward
+ *                    wrote with the same rule); those y and dy are then not read
+ *                    and dx there is written as 0. SMS_CAUSAL_NONE is always
  *                    correct.
  *   stream           hipStream_t to enqueue on
  *

@@ -12,7 +12,10 @@ exactly representable as a float64):
 * forward  -- lmnt.cn "Custom fused Softmax operator in CUDA, wrapped into
   PyTorch", sec. 1.2 (score = x*scale + mask, softmax over keys) and sec. 2.1
   (subtract the row maximum before exponentiating); the causal rule (key j > query
-  i is masked) from sec. 1.2, applied after the additive mask as in sec. 3.1;
+  i is masked) from sec. 1.2, applied after the additive mask as in sec. 3.1,
+  with a bottom-right variant (offset Sk - Sq) for Sq != Sk; boolean masks
+  that exclude keys inside the operator (pnsm.cn ScaledMaskSoftmax article,
+  sec. 2.3) and key padding given as per-batch lengths;
 * backward -- the same page, sec. 3.3: dx_i = scale * y_i * (dy_i - sum_j dy_j*y_j);
 * fully-masked rows -- pnsm.cn article on a custom ScaledMaskSoftmax operator,
   sec. 4.2 / 4.3: such a row must not divide 0 by 0; it returns all zeros.
@@ -24,6 +27,7 @@ Jacobian). Nothing in this package is "parity unpinned".
 
 from .softmax import (  # noqa: F401
     DTYPES,
+    causal_offset,
     decode,
     forward,
     forward_row,

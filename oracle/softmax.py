@@ -15,6 +15,15 @@ Conventions
   in the same dtype as ``x`` -- lmnt.cn "Custom fused Softmax operator in CUDA,
   wrapped into PyTorch", sec. 2.2 (additive mask) and sec. 4.2 (mask passed with
   the input's element type).
+* ``mask_kind="bool"``: the mask holds booleans (numpy bool or uint8); a
+  nonzero entry excludes the key (its score is -inf), as in the pnsm.cn
+  ScaledMaskSoftmax article, sec. 2.3 (mask value 1 marks an illegal position,
+  handled inside the operator).
+* ``mask_kind="lengths"``: ``key_lengths`` holds one integer per batch; keys
+  k >= key_lengths[b] are excluded (key padding given as lengths).
+* Causal: key k of query q is excluded when k > q + offset, with offset 0 for
+  the top-left rule of lmnt.cn sec. 1.2 (key j > query i) and Sk - Sq for the
+  bottom-right rule (the last query sees every key).
 * ``scale`` is rounded to fp32 first, because the operation receives it as a
   32-bit float (same page, sec. 4.2: the wrapper casts it to float).
 * Outputs are float64 arrays, unrounded.
@@ -79,17 +88,31 @@ def _mask_row(maskd, b, h, q):
     return maskd[mb, mh, mq, :]
 
 
-def _forward_one_row(xrow, mrow, sc, causal, q):
-    """Softmax of one row of scores, in float64."""
+def causal_offset(mode, Sq, Sk):
+    """Offset of the causal bound: key k is excluded when k > q + offset."""
+    if mode in (False, None, 0, "none"):
+        return None
+    if mode in (True, 1, "top_left"):
+        return 0
+    if mode in (2, "bottom_right"):
+        return Sk - Sq
+    raise ValueError(f"unknown causal mode {mode!r}")
+
+
+def _forward_one_row(xrow, mrow, sc, causal, q, excluded=None, offset=0):
+    """Softmax of one row of scores, in float64. ``excluded`` is a boolean
+    array of keys that take score -inf (boolean mask, key lengths)."""
     n = xrow.shape[0]
     # score_k = x_k*scale + mask_k
     s = xrow * sc
     if mrow is not None:
         s = s + mrow
-    # Causal: keys after the query position are masked, after the additive mask.
+    if excluded is not None:
+        s = np.where(excluded, -math.inf, s)
+    # Causal: keys after the bound are masked, after the additive mask.
     if causal:
         s = s.copy()
-        s[np.arange(n) > q] = -math.inf
+        s[np.arange(n) > q + offset] = -math.inf
     m = s.max() if n else -math.inf
     if m == -math.inf:
         # Every key is masked: the row is all zeros (nothing to normalise).
@@ -99,42 +122,80 @@ def _forward_one_row(xrow, mrow, sc, causal, q):
     return e / z
 
 
-def forward_row(xrow, dtype, mrow=None, scale=1.0, is_causal=False, q=0):
-    """Forward of one typed row of x (length Sk) with its typed mask row or None.
+def _excluded(n, mrow_bool=None, key_len=None):
+    ex = None
+    if mrow_bool is not None:
+        ex = np.asarray(mrow_bool) != 0
+    if key_len is not None:
+        lk = np.arange(n) >= int(key_len)
+        ex = lk if ex is None else (ex | lk)
+    return ex
 
-    ``q`` is the row's query position; it matters only when ``is_causal``.
+
+def forward_row(xrow, dtype, mrow=None, scale=1.0, is_causal=False, q=0, mask_kind="additive",
+                key_len=None, causal_offset=0):
+    """Forward of one typed row of x (length Sk) with its mask row or None.
+
+    ``q`` is the row's query position; with ``is_causal`` keys k > q +
+    ``causal_offset`` are excluded. ``mask_kind`` is "additive" (``mrow`` typed
+    like x) or "bool" (``mrow`` booleans, nonzero = excluded); ``key_len``
+    excludes keys k >= key_len.
     """
     xd = decode(np.asarray(xrow), dtype)
-    md = decode(np.asarray(mrow), dtype) if mrow is not None else None
-    if xd.ndim != 1 or (md is not None and md.shape != xd.shape):
+    md, mb = None, None
+    if mrow is not None:
+        if mask_kind == "additive":
+            md = decode(np.asarray(mrow), dtype)
+        elif mask_kind == "bool":
+            mb = np.asarray(mrow)
+        else:
+            raise ValueError(f"unknown mask kind {mask_kind!r}")
+    if xd.ndim != 1 or any(m is not None and m.shape != xd.shape for m in (md, mb)):
         raise ValueError("rows must be 1-D and of one length")
-    return _forward_one_row(xd, md, _fp32(scale), bool(is_causal), int(q))
+    return _forward_one_row(xd, md, _fp32(scale), bool(is_causal), int(q),
+                            _excluded(xd.shape[0], mb, key_len), int(causal_offset))
 
 
-def forward_rows(x, dtype, rows, mask=None, scale=1.0, is_causal=False):
-    """Forward on a list of flat row numbers; returns float64 [len(rows), Sk]."""
+def forward_rows(x, dtype, rows, mask=None, scale=1.0, is_causal=False, mask_kind="additive",
+                 key_lengths=None):
+    """Forward on a list of flat row numbers; returns float64 [len(rows), Sk].
+
+    ``is_causal``: False, True / "top_left" or "bottom_right". ``mask``: 4-D
+    with length-1 broadcast axes (additive or boolean per ``mask_kind``).
+    ``key_lengths``: one integer per batch, or None.
+    """
     x = np.asarray(x)
     if x.ndim != 4:
         raise ValueError("x must be 4-D [B, H, Sq, Sk]")
+    B, H, Sq, Sk = x.shape
     _check_mask_shape(mask, x.shape)
-    xd_all = x  # decoded per row to keep memory bounded at large sizes
-    maskd = decode(mask, dtype) if mask is not None else None
+    off = causal_offset(is_causal, Sq, Sk)
+    maskd = None
+    if mask is not None:
+        maskd = decode(mask, dtype) if mask_kind == "additive" else np.asarray(mask)
+    if key_lengths is not None and len(key_lengths) != B:
+        raise ValueError("key_lengths needs one entry per batch")
     sc = _fp32(scale)
-    out = np.empty((len(rows), x.shape[3]), dtype=np.float64)
+    out = np.empty((len(rows), Sk), dtype=np.float64)
     for i, r in enumerate(rows):
         b, h, q = row_index(x.shape, int(r))
-        xrow = decode(xd_all[b, h, q, :], dtype)
+        xrow = decode(x[b, h, q, :], dtype)  # decoded per row: memory stays bounded
         mrow = _mask_row(maskd, b, h, q) if maskd is not None else None
-        out[i] = _forward_one_row(xrow, mrow, sc, bool(is_causal), q)
+        add = mrow if mask_kind == "additive" else None
+        ex = _excluded(Sk, mrow if mask_kind == "bool" else None,
+                       key_lengths[b] if key_lengths is not None else None)
+        out[i] = _forward_one_row(xrow, add, sc, off is not None, q, ex, off or 0)
     return out
 
 
-def forward(x, dtype, mask=None, scale=1.0, is_causal=False):
+def forward(x, dtype, mask=None, scale=1.0, is_causal=False, mask_kind="additive",
+            key_lengths=None):
     """Forward over the whole tensor; returns float64 of x's shape."""
     x = np.asarray(x)
     B, H, Sq, Sk = x.shape
     rows = range(B * H * Sq)
-    return forward_rows(x, dtype, rows, mask, scale, is_causal).reshape(B, H, Sq, Sk)
+    return forward_rows(x, dtype, rows, mask, scale, is_causal, mask_kind,
+                        key_lengths).reshape(B, H, Sq, Sk)
 
 
 def _backward_one_row(yrow, dyrow, sc):

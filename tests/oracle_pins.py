@@ -319,9 +319,74 @@ def pin_backward_invariants():
                                                      2 * 0.75 * (-1 - (-0.5))], rtol=0)
 
 
+def pin_bool_masks():
+    """Boolean masks: nonzero excludes the key (score -inf); exhaustive brute
+    force over every pattern for n <= 6 and a hand row fixing the polarity."""
+    y = S.forward_row(np.array([1.0, 2.0, 3.0], F32), "f32",
+                      mrow=np.array([0, 1, 0], np.uint8), mask_kind="bool")
+    _close(y, [_logistic(-2.0), 0.0, _logistic(2.0)], rtol=4e-16, what="bool polarity")
+    assert y[1] == 0.0
+    rng = _rng(23)
+    for n in range(1, 7):
+        x = (rng.integers(-16, 17, n) * 0.25).astype(F32)
+        for bits in range(1 << n):
+            m = np.array([(bits >> k) & 1 for k in range(n)], np.bool_)
+            for causal in (False, True):
+                for q in (range(n) if causal else [0]):
+                    y = S.forward_row(x, "f32", mrow=m, scale=0.5, is_causal=causal, q=q,
+                                      mask_kind="bool")
+                    s = [None if (m[k] or (causal and k > q)) else 0.5 * float(x[k])
+                         for k in range(n)]
+                    _close(y, _brute_row(s), atol=1e-17, rtol=1e-14, what=f"bool brute n={n}")
+
+
+def pin_key_lengths():
+    """Key lengths: keys k >= L excluded; L = 0 gives zeros, L >= Sk nothing."""
+    x = np.array([1.0, 2.0, 3.0, 4.0], F32)
+    _close(S.forward_row(x, "f32", key_len=2), [_logistic(-1.0), _logistic(1.0), 0, 0],
+           rtol=4e-16, what="L=2")
+    assert S.forward_row(x, "f32", key_len=0).tolist() == [0.0] * 4
+    assert S.forward_row(x, "f32", key_len=1).tolist() == [1.0, 0.0, 0.0, 0.0]
+    _close(S.forward_row(x, "f32", key_len=9), S.forward_row(x, "f32"), rtol=0)
+    # tensor level: one length per batch, against a per-row brute force
+    rng = _rng(29)
+    B, H, Sq, Sk = 3, 2, 3, 7
+    xt = (rng.integers(-12, 13, (B, H, Sq, Sk)) * 0.25).astype(F32)
+    lens = np.array([0, 3, 7])
+    for causal in (False, True):
+        y = S.forward(xt, "f32", scale=0.5, is_causal=causal, mask_kind="lengths",
+                      key_lengths=lens)
+        for b, h, q in itertools.product(range(B), range(H), range(Sq)):
+            s = [None if (k >= lens[b] or (causal and k > q)) else 0.5 * float(xt[b, h, q, k])
+                 for k in range(Sk)]
+            _close(y[b, h, q], _brute_row(s), atol=1e-17, rtol=1e-14, what="lengths tensor")
+
+
+def pin_causal_alignments():
+    """Top-left: query q keeps keys 0..q. Bottom-right: keys 0..q+Sk-Sq, so the
+    last query keeps every key; Sq > Sk leaves the first Sq-Sk rows empty."""
+    x = np.zeros((1, 1, 2, 4), F32)  # equal scores: uniform over the kept keys
+    y = S.forward(x, "f32", is_causal="bottom_right")
+    _close(y[0, 0, 0], [1 / 3, 1 / 3, 1 / 3, 0], rtol=1e-15, what="BR q=0")
+    _close(y[0, 0, 1], [0.25] * 4, rtol=1e-15, what="BR q=1")
+    y = S.forward(x, "f32", is_causal="top_left")
+    _close(y[0, 0, 0], [1, 0, 0, 0], rtol=0, what="TL q=0")
+    _close(y[0, 0, 1], [0.5, 0.5, 0, 0], rtol=1e-15, what="TL q=1")
+    x = np.zeros((1, 1, 4, 2), F32)
+    y = S.forward(x, "f32", is_causal="bottom_right")
+    assert y[0, 0, 0].tolist() == [0.0, 0.0] and y[0, 0, 1].tolist() == [0.0, 0.0]
+    assert y[0, 0, 2].tolist() == [1.0, 0.0]
+    _close(y[0, 0, 3], [0.5, 0.5], rtol=1e-15, what="BR Sq>Sk last")
+    # square tensors: both rules agree
+    xs = (_rng(31).standard_normal((1, 2, 5, 5)) * 2).astype(F32)
+    _close(S.forward(xs, "f32", is_causal="bottom_right"), S.forward(xs, "f32", is_causal=True),
+           rtol=0)
+
+
 FORWARD_PINS = [pin_two_element_closed_form, pin_hand_rows, pin_fully_masked_rows,
                 pin_invariants, pin_library_special_case, pin_brute_force_exhaustive,
-                pin_tensor_indexing, pin_decode, pin_scale_rounding]
+                pin_tensor_indexing, pin_decode, pin_scale_rounding, pin_bool_masks,
+                pin_key_lengths, pin_causal_alignments]
 BACKWARD_PINS = [pin_backward_finite_differences, pin_backward_jacobian,
                  pin_backward_invariants]
 ALL_PINS = FORWARD_PINS + BACKWARD_PINS

@@ -9,7 +9,7 @@ import re
 import pytest
 import torch
 
-from attention_softmax_amd import _lib, mask_mode_of
+from attention_softmax_amd import _lib, causal_code, mask_kind_of, mask_mode_of
 from attention_softmax_amd.workloads import CONFIGS
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -80,6 +80,11 @@ def test_forward_argument_checks(L):
     assert _fwd(L, B=1 << 20, H=1 << 10, Sq=1 << 3) == 2          # 2^33 rows
     assert _fwd(L, Sq=1 << 23, Sk=1 << 20) == 2                   # 2^23 streamed rows: > 2^32 lanes
     assert _fwd(L, Sk=1 << 31) == 2
+    assert _fwd(L, mode=0x10) == 5                                # boolean flag without a shape
+    assert _fwd(L, mode=0x15, mask=FAKE) == 5                     # boolean key lengths
+    assert _fwd(L, mode=6, mask=FAKE) == 5
+    assert _fwd(L, causal=3) == 8 and _fwd(L, causal=-1) == 8     # unknown causal mode
+    assert _fwd(L, mode=5, mask=FAKE_ODD) == 6                    # int32 lengths misaligned
 
 
 @no_device
@@ -98,6 +103,8 @@ def test_backward_argument_checks(L):
     assert _bwd(L, st=(64, 64, 64, 0)) == 3
     assert _bwd(L, dx=FAKE_ODD) == 6
     assert _bwd(L, Sk=L.sms_max_sk(2) + 1, dtype=2) == 2
+    s = _lib.strides4((64, 64, 64, 1))
+    assert L.sms_backward(FAKE, s, FAKE, s, FAKE, s, 0, 1, 1, 1, 64, 1.0, 4, None) == 8
 
 
 def test_max_sk_and_paths(L):
@@ -128,6 +135,17 @@ def test_mask_mode_inference():
     for bad in ((3, 5, 7), (5, 6), (2, 3, 1, 7), (7,)):
         with pytest.raises(ValueError):
             mask_mode_of(z(*bad), shape)
+    assert mask_mode_of(torch.zeros(2, dtype=torch.int32), shape) == "key_lengths"
+    with pytest.raises(ValueError):
+        mask_mode_of(torch.zeros(3, dtype=torch.int32), shape)
+    assert mask_kind_of(torch.zeros(5, 7, dtype=torch.bool)) == "bool"
+    assert mask_kind_of(torch.zeros(5, 7, dtype=torch.uint8)) == "bool"
+    assert mask_kind_of(torch.zeros(2, dtype=torch.int64)) == "lengths"
+    assert mask_kind_of(torch.zeros(5, 7, dtype=torch.bfloat16)) == "additive"
+    assert [causal_code(c) for c in (False, True, "top_left", "bottom_right", None, 2)] == \
+        [0, 1, 1, 2, 0, 2]
+    with pytest.raises(ValueError):
+        causal_code("diagonal")
 
 
 def test_binding_refuses_cpu_tensors():

@@ -17,7 +17,8 @@ import torch
 import oracle
 from attention_softmax_amd import (SmsError, scaled_mask_softmax, sms_backward, sms_forward,
                                    sms_max_sk)
-from attention_softmax_amd.workloads import CONFIGS, TORCH_DTYPE, draw_mask, draw_x, make_config
+from attention_softmax_amd.workloads import (CONFIGS, TORCH_DTYPE, draw_lengths, draw_mask,
+                                             draw_x, make_config)
 from tests.parity import (compare, decoded, gather_mask_rows, gather_rows, mask_4d,
                           sample_rows, to_np)
 
@@ -44,9 +45,11 @@ def bwd(y, dy, scale=1.0, causal=False, dx=None):
     return dx
 
 
-def oracle_fwd(x, mask, mode, scale, causal):
+def oracle_fwd(x, mask, mode, scale, causal, kind="additive"):
     dt = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[x.dtype]
-    return oracle.forward(to_np(x), dt, mask_4d(mask, mode), scale, causal)
+    if mask is not None and kind == "lengths":
+        return oracle.forward(to_np(x), dt, None, scale, causal, "lengths", to_np(mask))
+    return oracle.forward(to_np(x), dt, mask_4d(mask, mode), scale, causal, kind)
 
 
 def dtname(t):
@@ -64,21 +67,70 @@ def _mask_kind(mode):
     return ("normal", 2.0) if mode in ("b_1_sk",) else ("bernoulli_neginf", 0.25)
 
 
+# (shape mode, kind): every additive and boolean shape, key lengths, none
+MASK_CASES = ([("none", "none")] + [(m, "additive") for m in MODES[1:]] +
+              [(m, "bool") for m in MODES[1:]] + [("key_lengths", "lengths")])
+CAUSALS = (False, True, "bottom_right")
+
+
+def make_mask(shape, mode, kind, dtype, seed):
+    """A mask of the given shape mode and kind for x of ``shape``."""
+    if kind == "none":
+        return None
+    if kind == "lengths":
+        return draw_lengths(shape[0], 0, shape[3] + 2, seed, DEV)  # 0 .. beyond Sk
+    if kind == "bool":
+        return draw_mask(shape, mode, dtype, ("bool", 0.3), seed, DEV)
+    return draw_mask(shape, mode, dtype, _mask_kind(mode), seed, DEV)
+
+
+def check_fwd_bwd(x, mask, mode, kind, scale, causal, what, dy_seed=None):
+    dtype = dtname(x)
+    y = fwd(x, mask, scale, causal)
+    compare(decoded(y), oracle_fwd(x, mask, mode, scale, causal, kind), dtype, what, rowsum=True)
+    if dy_seed is not None:
+        dy = draw_x(tuple(x.shape), dtype, ("normal", 1.0), dy_seed, DEV)
+        dx = bwd(y, dy, scale, causal)
+        compare(decoded(dx), oracle.backward(to_np(y), to_np(dy), dtype, scale), dtype,
+                what + " bwd")
+    return y
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("Sk", SK_SWEEP)
 def test_sweep_all_modes(dtype, Sk):
-    """Every mask mode, non-causal and causal, on a few rows of each length."""
+    """Every mask shape and kind (additive, boolean, key lengths), no causal rule
+    and both causal alignments (Sq = 3 < Sk), on a few rows of each length;
+    forward, and backward with the same causal promise."""
     say(f"sweep dtype={dtype} Sk={Sk}")
-    for mode in MODES:
-        for causal in (False, True):
-            shape = (2, 2, 3, Sk)
-            seed = zlib.crc32(f"{dtype}/{Sk}/{mode}/{causal}".encode()) % 10000
+    shape = (2, 2, 3, Sk)
+    for mode, kind in MASK_CASES:
+        for causal in CAUSALS:
+            seed = zlib.crc32(f"{dtype}/{Sk}/{mode}/{kind}/{causal}".encode()) % 10000
             x = draw_x(shape, dtype, ("normal", 3.0), seed, DEV)
-            mask = draw_mask(shape, mode, dtype, _mask_kind(mode), seed + 1, DEV)
-            y = fwd(x, mask, 0.3, causal)
-            ref = oracle_fwd(x, mask, mode, 0.3, causal)
-            compare(decoded(y), ref, dtype, f"{dtype} Sk={Sk} {mode} causal={causal}",
-                    rowsum=True)
+            mask = make_mask(shape, mode, kind, dtype, seed + 1)
+            check_fwd_bwd(x, mask, mode, kind, 0.3, causal,
+                          f"{dtype} Sk={Sk} {mode}/{kind} causal={causal}",
+                          dy_seed=seed + 2 if causal else None)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("Sk", [1, 8, 77, 1000, 2048])
+def test_bottom_right_causal_more_queries_than_keys(dtype, Sk, monkeypatch):
+    """Sq > Sk with the bottom-right rule: the first Sq - Sk rows have no key and
+    are all zeros; through both the general and the aligned-row kernels."""
+    say(f"bottom-right Sq>Sk dtype={dtype} Sk={Sk}")
+    shape = (1, 2, Sk + 5, Sk)
+    for fast in ("1", "0"):
+        monkeypatch.setenv("SMS_FAST", fast)
+        for mode, kind in (("none", "none"), ("sq_sk", "bool"), ("key_lengths", "lengths"),
+                           ("b_sq_sk", "additive")):
+            seed = zlib.crc32(f"br/{dtype}/{Sk}/{mode}/{kind}".encode()) % 10000
+            x = draw_x(shape, dtype, ("normal", 3.0), seed, DEV)
+            mask = make_mask(shape, mode, kind, dtype, seed + 1)
+            y = check_fwd_bwd(x, mask, mode, kind, 0.5, "bottom_right",
+                              f"BR {dtype} Sk={Sk} {mode}/{kind} fast={fast}", dy_seed=seed + 2)
+            assert (y[:, :, :5] == 0).all()
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
@@ -389,43 +441,55 @@ def test_streaming_kernels_on_short_rows(dtype, Sk, monkeypatch):
     causal or not, aligned or not, forward and backward, against the oracle."""
     monkeypatch.setenv("SMS_FORCE_STREAM", "1")
     say(f"stream forced dtype={dtype} Sk={Sk}")
-    for mode in MODES:
-        for causal in (False, True):
+    for mode, kind in MASK_CASES:
+        for causal in CAUSALS:
             shape = (2, 2, 3, Sk)
-            seed = zlib.crc32(f"s/{dtype}/{Sk}/{mode}/{causal}".encode()) % 10000
+            seed = zlib.crc32(f"s/{dtype}/{Sk}/{mode}/{kind}/{causal}".encode()) % 10000
             x = draw_x(shape, dtype, ("normal", 3.0), seed, DEV)
-            mask = draw_mask(shape, mode, dtype, _mask_kind(mode), seed + 1, DEV)
-            y = fwd(x, mask, 0.3, causal)
-            compare(decoded(y), oracle_fwd(x, mask, mode, 0.3, causal), dtype,
-                    f"stream {dtype} Sk={Sk} {mode} causal={causal}", rowsum=True)
-            dy = draw_x(shape, dtype, ("normal", 1.0), seed + 2, DEV)
-            dx = bwd(y, dy, 0.3, causal)
-            compare(decoded(dx), oracle.backward(to_np(y), to_np(dy), dtype, 0.3), dtype,
-                    f"stream bwd {dtype} Sk={Sk} {mode} causal={causal}")
+            mask = make_mask(shape, mode, kind, dtype, seed + 1)
+            check_fwd_bwd(x, mask, mode, kind, 0.3, causal,
+                          f"stream {dtype} Sk={Sk} {mode}/{kind} causal={causal}",
+                          dy_seed=seed + 2)
 
 
-@pytest.mark.parametrize("dtype,Sk,mode", [
-    ("f32", 16385, "b_1_sk"),      # one past the register-resident fp32 reach
-    ("f32", 262144, "none"),       # 1 MB rows
-    ("f16", 32769, "sq_sk"),       # one past the fp16 reach
-    ("f16", 40000, "b_sq_sk"),
-    ("bf16", 100003, "full"),      # odd length: unaligned rows, element head/tail
+@pytest.mark.parametrize("dtype,Sk,mode,kind", [
+    ("f32", 16385, "b_1_sk", "additive"),   # one past the register-resident fp32 reach
+    ("f32", 262144, "none", "none"),        # 1 MB rows
+    ("f32", 20000, "sq_sk", "bool"),
+    ("f16", 32769, "sq_sk", "additive"),    # one past the fp16 reach
+    ("f16", 40000, "b_sq_sk", "additive"),
+    ("bf16", 100003, "full", "additive"),   # odd length: unaligned rows, element head/tail
+    ("bf16", 50001, "key_lengths", "lengths"),
 ])
-def test_long_rows(dtype, Sk, mode):
-    """Rows beyond one workgroup's registers take the streaming kernels; sampled
-    rows against the oracle, row sums on every row."""
-    say(f"long rows dtype={dtype} Sk={Sk} mode={mode}")
+def test_long_rows(dtype, Sk, mode, kind):
+    """Rows beyond one workgroup's registers take the streaming kernels; every
+    row against the oracle, for no causal rule and both alignments."""
+    say(f"long rows dtype={dtype} Sk={Sk} mode={mode} kind={kind}")
     shape = (1, 2, 4, Sk)
     x = draw_x(shape, dtype, ("normal", 4.0), Sk, DEV)
-    mask = draw_mask(shape, mode, dtype, _mask_kind(mode), Sk + 1, DEV)
-    for causal in (False, True):
-        y = fwd(x, mask, 0.25, causal)
-        ref = oracle_fwd(x, mask, mode, 0.25, causal)
-        compare(decoded(y), ref, dtype, f"long fwd causal={causal}", rowsum=True)
-        dy = draw_x(shape, dtype, ("normal", 1.0), Sk + 2, DEV)
-        dx = bwd(y, dy, 0.25, causal)
-        compare(decoded(dx), oracle.backward(to_np(y), to_np(dy), dtype, 0.25), dtype,
-                f"long bwd causal={causal}")
+    if kind == "lengths":
+        mask = torch.tensor([Sk // 3], dtype=torch.int32, device=DEV)
+    else:
+        mask = make_mask(shape, mode, kind, dtype, Sk + 1)
+    for causal in CAUSALS:
+        check_fwd_bwd(x, mask, mode, kind, 0.25, causal, f"long causal={causal}",
+                      dy_seed=Sk + 2)
+
+
+@pytest.mark.parametrize("moff", [1, 3, 5])
+@pytest.mark.parametrize("dtype,Sk", [("f16", 1000), ("f32", 256), ("bf16", 77)])
+def test_bool_mask_at_odd_offsets(dtype, Sk, moff):
+    """Boolean mask rows that do not sit on a vector boundary: byte-wise mask
+    loads in the general kernels, against the oracle."""
+    say(f"bool mask offset dtype={dtype} Sk={Sk} moff={moff}")
+    B, H, Sq = 2, 2, 5
+    shape = (B, H, Sq, Sk)
+    x = draw_x(shape, dtype, ("normal", 3.0), moff, DEV)
+    full = draw_mask((1, 1, 1, moff + B * Sq * Sk), "full", dtype, ("bool", 0.3), moff + 1,
+                     DEV).reshape(-1)
+    mask = full[moff:].view(B, Sq, Sk)
+    for causal in CAUSALS:
+        check_fwd_bwd(x, mask, "b_sq_sk", "bool", 0.7, causal, f"bool moff={moff} {causal}")
 
 
 def test_long_causal_square():

@@ -28,18 +28,21 @@ _orig_mask_row = S._mask_row
 _orig_row_index = S.row_index
 
 
-def _fwd_generic(xrow, mrow, sc, causal, q, *, use_scale=True, causal_ge=False,
-                 mask_scaled=False, shift=True, full_mask="zeros", causal_first_only=False):
+def _fwd_generic(xrow, mrow, sc, causal, q, excluded=None, offset=0, *, use_scale=True,
+                 causal_ge=False, mask_scaled=False, shift=True, full_mask="zeros",
+                 causal_first_only=False):
     n = xrow.shape[0]
     s = xrow * (sc if use_scale else 1.0)
     if mrow is not None:
         s = s + (mrow * sc if mask_scaled else mrow)
+    if excluded is not None:
+        s = np.where(excluded, -math.inf, s)
     if causal:
         s = s.copy()
         k = np.arange(n)
-        s[(k >= q) if causal_ge else (k > q)] = -math.inf
+        s[(k >= q + offset) if causal_ge else (k > q + offset)] = -math.inf
         if causal_first_only:
-            s[k > q + 1] = -math.inf
+            s[k > q + offset + 1] = -math.inf
     m = s.max() if n else -math.inf
     if m == -math.inf:
         if full_mask == "zeros":
@@ -79,9 +82,9 @@ BWD_MUTANTS = {
 }
 
 
-def _late_causal(xrow, mrow, sc, causal, q):
+def _late_causal(xrow, mrow, sc, causal, q, excluded=None, offset=0):
     # keys up to q+1 kept (off by one in the other direction)
-    return _orig_fwd(xrow, mrow, sc, causal, q + 1 if causal else q)
+    return _orig_fwd(xrow, mrow, sc, causal, q + 1 if causal else q, excluded, offset)
 
 
 def _run_all_pins():
@@ -103,7 +106,8 @@ def test_planted_forward_mistake_is_caught(name, monkeypatch):
         monkeypatch.setattr(S, "_forward_one_row", _late_causal)
     else:
         monkeypatch.setattr(S, "_forward_one_row",
-                            lambda xr, mr, sc, c, q: _fwd_generic(xr, mr, sc, c, q, **kw))
+                            lambda xr, mr, sc, c, q, ex=None, off=0:
+                            _fwd_generic(xr, mr, sc, c, q, ex, off, **kw))
     assert _run_all_pins(), f"planted mistake '{name}' passed every pin"
 
 
@@ -137,4 +141,33 @@ def test_planted_decode_mistake_is_caught(monkeypatch):
             return (a.astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
         return _orig_decode(a, dtype)
     monkeypatch.setattr(S, "decode", decode_bad)
+    assert _run_all_pins()
+
+
+_orig_excluded = S._excluded
+_orig_offset = S.causal_offset
+
+
+def test_planted_mask_kind_mistakes_are_caught(monkeypatch):
+    # boolean mask polarity inverted (zero taken as "excluded")
+    def excluded_inverted(n, mrow_bool=None, key_len=None):
+        if mrow_bool is not None:
+            mrow_bool = (np.asarray(mrow_bool) == 0)
+        return _orig_excluded(n, mrow_bool, key_len)
+    monkeypatch.setattr(S, "_excluded", excluded_inverted)
+    assert _run_all_pins()
+    monkeypatch.setattr(S, "_excluded", _orig_excluded)
+
+    # key length off by one (keys k > L excluded instead of k >= L)
+    def excluded_len_late(n, mrow_bool=None, key_len=None):
+        return _orig_excluded(n, mrow_bool, None if key_len is None else key_len + 1)
+    monkeypatch.setattr(S, "_excluded", excluded_len_late)
+    assert _run_all_pins()
+    monkeypatch.setattr(S, "_excluded", _orig_excluded)
+
+    # bottom-right offset with the wrong sign
+    def offset_flipped(mode, Sq, Sk):
+        o = _orig_offset(mode, Sq, Sk)
+        return -o if o else o
+    monkeypatch.setattr(S, "causal_offset", offset_flipped)
     assert _run_all_pins()
