@@ -1,6 +1,5 @@
 // api.hip -- the C ABI declared in include/sms.h: argument checks, the choice
-// of kernel family and shape (lanes per row, vectors per lane, row order) and
-// the launch.
+// of kernel family and shape (lanes per row, vectors per lane) and the launch.
 //
 // Interface after lmnt.cn "Custom fused Softmax operator in CUDA, wrapped into
 // PyTorch", sec. 4.2 (forward takes x, an optional mask, scale and is_causal;
@@ -11,9 +10,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
-#include <string.h>
-
-#include <algorithm>
 
 #include "kernels.hpp"
 #include "sms.h"
@@ -24,10 +20,6 @@ using sms::BwdParams;
 using sms::FwdParams;
 using sms::RowGeom;
 
-// Workgroups are dealt round-robin over the XCDs of an MI355X.
-constexpr uint32_t kXcds = 8;
-// Query rows per group in a grouped row order (SMS_QBLOCK overrides).
-constexpr int kDefaultQBlock = 16;
 // Largest vectors-per-row a (TPR, NV) pair in the build covers; longer rows
 // take the streaming kernels (one workgroup per row, two passes).
 constexpr int64_t kMaxVecPerRow = 1024 * 4;
@@ -53,17 +45,8 @@ int env_int(const char* name, int dflt) {
 
 // Tuning and test overrides, read per call:
 //   SMS_FORCE_TPR=<4..1024>  lanes per row (0 = automatic)
-//   SMS_ORDER=rows|grouped   row order (unset = memory order), SMS_QBLOCK=<Q>
 //   SMS_FAST=0               never take the aligned-row kernels
 //   SMS_FORCE_STREAM=1       take the streaming kernels for every row
-int forced_order() {
-  const char* s = getenv("SMS_ORDER");
-  if (!s) return -1;
-  if (!strcmp(s, "rows")) return 0;
-  if (!strcmp(s, "grouped")) return 1;
-  return -1;
-}
-
 struct Plan {
   int family = sms::FAMILY_GENERAL;
   int tpr = 0;
@@ -171,10 +154,8 @@ void fill_geom(RowGeom& g, int64_t B, int64_t H, int64_t Sq, int64_t Sk) {
   g.Sq = (uint32_t)Sq;
   g.Sk = (uint32_t)Sk;
   g.rows = (uint32_t)(B * H * Sq);
-  g.order = sms::ORDER_ROWS;
-  g.xcds = kXcds;
-  g.members = 1;
-  g.qblock = 1;
+  g.div_sq = sms::make_fastdiv(g.Sq);
+  g.div_h = sms::make_fastdiv(g.H);
 }
 
 hipError_t launch(sms_dtype dtype, const FwdParams* fp, const BwdParams* bp, const Plan& pl,
@@ -270,20 +251,6 @@ sms_status sms_forward(const void* x, const int64_t x_strides[4], const void* ma
   fill_geom(p.g, B, H, Sq, Sk);
 
   if (pl.family != sms::FAMILY_STREAM) {
-    // Grouped order: rows that read the same block of mask rows run back to
-    // back on one XCD. Opt-in: memory order measured faster on MI355X.
-    const int rpb = sms::block_of(pl.tpr) / pl.tpr;
-    const int64_t Q = std::max(1, env_int("SMS_QBLOCK", kDefaultQBlock));
-    int64_t members = 0, groups = 0;
-    uint32_t order = sms::ORDER_ROWS;
-    if (shape_mode == SMS_MASK_B_SQ_SK) { members = H * Q; groups = B * (Sq / Q); order = sms::ORDER_HEADS; }
-    if (shape_mode == SMS_MASK_SQ_SK) { members = B * H * Q; groups = Sq / Q; order = sms::ORDER_SAMPLES; }
-    if (forced_order() == 1 && members > 1 && Sq % Q == 0 && members % rpb == 0 && groups > 0 &&
-        groups % kXcds == 0 && members <= UINT32_MAX) {
-      p.g.order = order;
-      p.g.members = (uint32_t)members;
-      p.g.qblock = (uint32_t)Q;
-    }
     // Aligned-row kernels: every operand's rows on 16-byte lines, whole vectors.
     const bool mask_whole = !has_mask || p.mask_kind == sms::MASK_LEN ||
                             (p.mask_kind == sms::MASK_ADD && ((uintptr_t)mask & 15) == 0) ||

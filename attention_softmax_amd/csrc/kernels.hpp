@@ -44,6 +44,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fastdiv.hpp"
+
 #define SMS_DEV __device__ __forceinline__
 
 namespace sms {
@@ -246,60 +248,44 @@ SMS_DEV T row_reduce(T v, Op op, T* slots) {
 
 // -------------------------------------------------------------- row mapping
 
-// Row order. ORDER_ROWS: flat row r -> (b, h, q) with q fastest. The grouped
-// orders put the rows that read one block of Q mask rows on consecutive
-// workgroups of the same XCD (workgroup w runs on XCD w % xcds), so the block
-// is fetched once and then hits that XCD's L2; inside a group each head takes
-// Q consecutive rows, which keeps the x / y streams contiguous in Q-row runs:
-//   ORDER_HEADS:   group (b, query block), members (h, q in block)    (mask [B,Sq,Sk])
-//   ORDER_SAMPLES: group (query block), members (b, h, q in block)    (mask [Sq,Sk])
-enum : uint32_t { ORDER_ROWS = 0, ORDER_HEADS = 1, ORDER_SAMPLES = 2 };
-
+// Rows are numbered r = (b*H + h)*Sq + q (q fastest) and run in that order:
+// consecutive workgroups take consecutive rows, which keeps the x / y streams
+// contiguous in memory. (b, h, q) come from two divisions by launch-time
+// constants (fastdiv.hpp); a row starts at b*s_b + h*s_h + q*s_q. With 64 or
+// more lanes per row all of it is scalar work, once per wave, free of branches
+// so that the kernel-argument loads it needs are issued together.
 struct RowGeom {
   uint32_t B, H, Sq, Sk;
   uint32_t rows;     // B*H*Sq
-  uint32_t order;    // ORDER_*
-  uint32_t xcds;     // XCDs the workgroups are dealt over
-  uint32_t members;  // rows per group in a grouped order
-  uint32_t qblock;   // query rows per group in a grouped order (divides Sq)
+  FastDiv div_sq;    // by Sq
+  FastDiv div_h;     // by H
 };
 
-template <int RPB>
-SMS_DEV bool row_coords(const RowGeom& g, uint32_t w, uint32_t local, uint32_t& b, uint32_t& h,
-                        uint32_t& q) {
-  if (g.order == ORDER_ROWS) {
-    const uint32_t r = w * RPB + local;
-    if (r >= g.rows) return false;
-    q = r % g.Sq;
-    const uint32_t t = r / g.Sq;
-    h = t % g.H;
-    b = t / g.H;
-    return true;
-  }
-  // The host only picks a grouped order when members % RPB == 0, Sq % qblock
-  // == 0 and the number of groups is a multiple of xcds, so every workgroup
-  // maps to one real row per local index.
-  const uint32_t xcd = w % g.xcds;
-  const uint32_t s = w / g.xcds;
-  const uint32_t bpg = g.members / RPB;  // workgroups per group
-  const uint32_t grp = (s / bpg) * g.xcds + xcd;
-  const uint32_t m = (s % bpg) * RPB + local;
-  const uint32_t qi = m % g.qblock;
-  const uint32_t mm = m / g.qblock;
-  const uint32_t nqb = g.Sq / g.qblock;
-  if (g.order == ORDER_HEADS) {
-    b = grp / nqb;
-    q = (grp % nqb) * g.qblock + qi;
-    h = mm;
-  } else {
-    q = grp * g.qblock + qi;
-    b = mm / g.H;
-    h = mm % g.H;
-  }
-  return true;
+SMS_DEV void row_bhq(const RowGeom& g, uint32_t r, uint32_t& b, uint32_t& h, uint32_t& q) {
+  const uint32_t t = fast_div(r, g.div_sq);
+  q = r - t * g.Sq;
+  b = fast_div(t, g.div_h);
+  h = t - b * g.H;
+}
+
+// Element offset of row (b, h, q) of an operand with strides (sb, sh, sq).
+SMS_DEV int64_t row_offset(uint32_t b, uint32_t h, uint32_t q, int64_t sb, int64_t sh,
+                           int64_t sq) {
+  return (int64_t)b * sb + (int64_t)h * sh + (int64_t)q * sq;
 }
 
 constexpr int block_of(int tpr) { return tpr <= 64 ? 256 : tpr; }
+
+// Index of this thread's row inside its workgroup. With 64 or more lanes per
+// row it is the same for the whole wavefront, and readfirstlane says so: the
+// row's coordinates, offsets and key bound are then computed once per wave in
+// scalar registers instead of per lane (integer division and 64-bit products
+// on the vector unit measured ~9 % of a bandwidth-bound backward).
+template <int TPR>
+SMS_DEV uint32_t local_row() {
+  if constexpr (TPR >= 64) return __builtin_amdgcn_readfirstlane(threadIdx.x / TPR);
+  else return threadIdx.x / TPR;
+}
 
 // ------------------------------------------------------------- parameters
 
@@ -380,11 +366,13 @@ SMS_DEV FwdRow fwd_row(const FwdParams& p, uint32_t w, uint32_t local) {
   constexpr int BY = F::kBytes;
   constexpr int E = F::kE;
   FwdRow r;
-  uint32_t b = 0, h = 0, q = 0;
-  r.valid = row_coords<RPB>(p.g, w, local, b, h, q);
+  const uint32_t row = w * RPB + local;
+  r.valid = RPB == 1 || row < p.g.rows;  // RPB == 1: the grid is exactly the rows
+  uint32_t b, h, q;
+  row_bhq(p.g, row, b, h, q);
   const int Sk = (int)p.g.Sk;
-  r.x = p.x + ((int64_t)b * p.sx_b + (int64_t)h * p.sx_h + (int64_t)q * p.sx_q) * BY;
-  r.y = p.y + ((int64_t)b * p.sy_b + (int64_t)h * p.sy_h + (int64_t)q * p.sy_q) * BY;
+  r.x = p.x + row_offset(b, h, q, p.sx_b, p.sx_h, p.sx_q) * BY;
+  r.y = p.y + row_offset(b, h, q, p.sy_b, p.sy_h, p.sy_q) * BY;
   r.ax = (int)(((uintptr_t)r.x & 15) / BY);
   r.yvec = ((((uintptr_t)r.y & 15) / BY) == (uintptr_t)r.ax);
   int kload = causal_bound(p.causal, q, p.g.Sq, Sk);
@@ -420,11 +408,13 @@ template <class F, int RPB>
 SMS_DEV BwdRow bwd_row(const BwdParams& p, uint32_t w, uint32_t local) {
   constexpr int BY = F::kBytes;
   BwdRow r;
-  uint32_t b = 0, h = 0, q = 0;
-  r.valid = row_coords<RPB>(p.g, w, local, b, h, q);
-  r.y = p.y + ((int64_t)b * p.sy_b + (int64_t)h * p.sy_h + (int64_t)q * p.sy_q) * BY;
-  r.d = p.dy + ((int64_t)b * p.sd_b + (int64_t)h * p.sd_h + (int64_t)q * p.sd_q) * BY;
-  r.x = p.dx + ((int64_t)b * p.sx_b + (int64_t)h * p.sx_h + (int64_t)q * p.sx_q) * BY;
+  const uint32_t row = w * RPB + local;
+  r.valid = RPB == 1 || row < p.g.rows;
+  uint32_t b, h, q;
+  row_bhq(p.g, row, b, h, q);
+  r.y = p.y + row_offset(b, h, q, p.sy_b, p.sy_h, p.sy_q) * BY;
+  r.d = p.dy + row_offset(b, h, q, p.sd_b, p.sd_h, p.sd_q) * BY;
+  r.x = p.dx + row_offset(b, h, q, p.sx_b, p.sx_h, p.sx_q) * BY;
   r.ay = (int)(((uintptr_t)r.y & 15) / BY);
   r.dvec = ((((uintptr_t)r.d & 15) / BY) == (uintptr_t)r.ay);
   r.xvec = ((((uintptr_t)r.x & 15) / BY) == (uintptr_t)r.ay);
@@ -579,7 +569,7 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_fwd_kernel(FwdParams p) {
   constexpr int RPB = block_of(TPR) / TPR;
   __shared__ float red[2][TPR > 64 ? TPR / 64 : 1];
   const int lane = (int)(threadIdx.x % TPR);
-  const FwdRow r = fwd_row<F, RPB>(p, blockIdx.x, threadIdx.x / TPR);
+  const FwdRow r = fwd_row<F, RPB>(p, blockIdx.x, local_row<TPR>());
   if (!r.valid) return;  // only a tail group of a TPR <= 64 launch, which has no barrier
   float s[NV][E];
 #pragma unroll
@@ -596,7 +586,7 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_bwd_kernel(BwdParams p) {
   constexpr int RPB = block_of(TPR) / TPR;
   __shared__ double red[TPR > 64 ? TPR / 64 : 1];
   const int lane = (int)(threadIdx.x % TPR);
-  const BwdRow r = bwd_row<F, RPB>(p, blockIdx.x, threadIdx.x / TPR);
+  const BwdRow r = bwd_row<F, RPB>(p, blockIdx.x, local_row<TPR>());
   if (!r.valid) return;
   float yv[NV][E], gv[NV][E];
 #pragma unroll
@@ -649,13 +639,15 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_fwd_fast_kernel(FwdParams p
   constexpr int RPB = block_of(TPR) / TPR;
   __shared__ float red[2][TPR > 64 ? TPR / 64 : 1];
   const int lane = (int)(threadIdx.x % TPR);
+  const uint32_t row = blockIdx.x * RPB + local_row<TPR>();
+  if (RPB > 1 && row >= p.g.rows) return;  // a tail group of a TPR <= 64 launch (no barrier)
   uint32_t b, h, q;
-  if (!row_coords<RPB>(p.g, blockIdx.x, threadIdx.x / TPR, b, h, q)) return;
+  row_bhq(p.g, row, b, h, q);
   // Host-checked: every row of x, y and the mask starts on a 16-byte line (an
   // E-byte line for a boolean mask) and holds whole vectors.
   const int Sk = (int)p.g.Sk;
-  const char* xrow = p.x + ((int64_t)b * p.sx_b + (int64_t)h * p.sx_h + (int64_t)q * p.sx_q) * BY;
-  char* yrow = p.y + ((int64_t)b * p.sy_b + (int64_t)h * p.sy_h + (int64_t)q * p.sy_q) * BY;
+  const char* xrow = p.x + row_offset(b, h, q, p.sx_b, p.sx_h, p.sx_q) * BY;
+  char* yrow = p.y + row_offset(b, h, q, p.sy_b, p.sy_h, p.sy_q) * BY;
   int kload = p.causal ? causal_bound(p.causal, q, p.g.Sq, Sk) : Sk;
   const char* mrow = nullptr;
   if constexpr (KIND != FAST_PLAIN) {
@@ -721,7 +713,7 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_bwd_fast_kernel(BwdParams p
   constexpr int RPB = block_of(TPR) / TPR;
   __shared__ double red[TPR > 64 ? TPR / 64 : 1];
   const int lane = (int)(threadIdx.x % TPR);
-  const BwdRow r = bwd_row<F, RPB>(p, blockIdx.x, threadIdx.x / TPR);
+  const BwdRow r = bwd_row<F, RPB>(p, blockIdx.x, local_row<TPR>());
   if (!r.valid) return;
   const bool ntl = (p.policy & POL_NT_LOAD) != 0;
   const int kload = r.kload;

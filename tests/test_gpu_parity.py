@@ -17,8 +17,8 @@ import torch
 import oracle
 from attention_softmax_amd import (SmsError, scaled_mask_softmax, sms_backward, sms_forward,
                                    sms_max_sk)
-from attention_softmax_amd.workloads import (CONFIGS, TORCH_DTYPE, draw_lengths, draw_mask,
-                                             draw_x, make_config)
+from attention_softmax_amd.workloads import (CONFIGS, TORCH_DTYPE, draw_dy, draw_lengths,
+                                             draw_mask, draw_x, make_config)
 from tests.parity import (compare, decoded, gather_mask_rows, gather_rows, mask_4d,
                           sample_rows, to_np)
 
@@ -329,22 +329,27 @@ def test_forced_width_too_small_is_an_error(monkeypatch):
         sms_forward(x, None, torch.empty_like(x))
 
 
-@pytest.mark.parametrize("order,qblock", [("rows", 1), ("grouped", 1), ("grouped", 4),
-                                          ("grouped", 16)])
-def test_row_orders_agree(order, qblock, monkeypatch):
-    """The XCD-grouped row orders are permutations of rows: identical bits."""
-    monkeypatch.setenv("SMS_ORDER", order)
-    monkeypatch.setenv("SMS_QBLOCK", str(qblock))
-    for Sk, mode in ((2048, "b_sq_sk"), (4096, "b_sq_sk"), (2048, "sq_sk"), (4096, "sq_sk")):
-        shape = (2, 4, 64, Sk)  # 4 heads: a multiple of the rows per workgroup
-        x = draw_x(shape, "f16", ("normal", 8.0), 1, DEV)
-        mask = draw_mask(shape, mode, "f16", ("bernoulli_neginf", 0.1), 2, DEV)
-        y = fwd(x, mask, 0.125, True)
-        monkeypatch.setenv("SMS_ORDER", "rows")
-        y0 = fwd(x, mask, 0.125, True)
-        monkeypatch.setenv("SMS_ORDER", order)
-        assert torch.equal(y, y0)
-        compare(decoded(y), oracle_fwd(x, mask, mode, 0.125, True), "f16", f"order {order}")
+@pytest.mark.parametrize("shape", [(2, 3, 5, 1024), (3, 1, 1, 2048), (1, 4, 1, 512),
+                                   (2, 1, 7, 256), (1, 1, 1, 4096)])
+def test_padded_and_permuted_rows_agree(shape):
+    """Contiguous, padded-row and [H,B]-ordered operands give identical bits,
+    including shapes with size-1 axes (row coordinates from the fast divisions)."""
+    B, H, Sq, Sk = shape
+    x = draw_x(shape, "f16", ("normal", 4.0), 7, DEV)
+    dy = draw_dy(shape, "f16", 8, DEV)
+    y0 = fwd(x, None, 0.25, True)
+    dx0 = bwd(y0, dy, 0.25, True)
+    # padded rows (row stride Sk + 8, still 16-byte aligned) and a [H,B] storage order
+    for make in (lambda t: torch.zeros(B, H, Sq, Sk + 8, dtype=t.dtype, device=DEV)[..., :Sk],
+                 lambda t: torch.zeros(H, B, Sq, Sk, dtype=t.dtype, device=DEV).transpose(0, 1)):
+        xs, dys = make(x), make(dy)
+        xs.copy_(x)
+        dys.copy_(dy)
+        ys, dxs = make(x), make(x)
+        sms_forward(xs, None, ys, 0.25, True)
+        sms_backward(ys, dys, dxs, 0.25, True)
+        assert torch.equal(ys, y0) and torch.equal(dxs, dx0)
+    compare(decoded(y0), oracle_fwd(x, None, "none", 0.25, True), "f16", f"flat {shape}")
 
 
 # ------------------------------------------------------------------ edges
