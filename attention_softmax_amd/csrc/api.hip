@@ -25,9 +25,6 @@ using sms::RowGeom;
 constexpr int64_t kMaxVecPerRow = 1024 * 4;
 // Longest row: keeps every in-kernel element index far inside int32.
 constexpr int64_t kMaxSk = int64_t(1) << 30;
-// Cache hints: nontemporal loads of the streamed inputs and nontemporal
-// stores of the outputs (SMS_CACHE_POLICY overrides: bit 1 loads, bit 2 stores).
-constexpr int kDefaultPolicy = sms::POL_NT_LOAD | sms::POL_NT_STORE;
 
 int dtype_bytes(sms_dtype d) {
   switch (d) {
@@ -247,7 +244,6 @@ sms_status sms_forward(const void* x, const int64_t x_strides[4], const void* ma
   p.mask_kind = !has_mask ? sms::MASK_NONE
                 : shape_mode == SMS_MASK_KEY_LENGTHS ? sms::MASK_LEN
                 : is_bool ? sms::MASK_BOOL : sms::MASK_ADD;
-  p.policy = env_int("SMS_CACHE_POLICY", kDefaultPolicy);
   fill_geom(p.g, B, H, Sq, Sk);
 
   if (pl.family != sms::FAMILY_STREAM) {
@@ -296,7 +292,6 @@ sms_status sms_backward(const void* y, const int64_t y_strides[4], const void* d
   p.sx_b = dx_strides[0]; p.sx_h = dx_strides[1]; p.sx_q = dx_strides[2];
   p.scale = scale;
   p.causal = is_causal;
-  p.policy = env_int("SMS_CACHE_POLICY", kDefaultPolicy);
   fill_geom(p.g, B, H, Sq, Sk);
 
   if (pl.family != sms::FAMILY_STREAM && ((Sk * bytes) & 15) == 0 &&

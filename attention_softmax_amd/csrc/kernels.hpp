@@ -291,10 +291,18 @@ SMS_DEV uint32_t local_row() {
 
 enum : int { MASK_NONE = 0, MASK_ADD = 1, MASK_BOOL = 2, MASK_LEN = 3 };
 enum : int { CAUSAL_NONE = 0, CAUSAL_TOP_LEFT = 1, CAUSAL_BOTTOM_RIGHT = 2 };
-// Cache policy bits: 1 = nontemporal loads of x / y / dy, 2 = nontemporal
-// stores of y / dx. The score and output streams are touched once; the mask,
-// which other rows read again, always goes through the caches.
-enum : int { POL_NT_LOAD = 1, POL_NT_STORE = 2 };
+// Cache hints, fixed at build time. The score and output streams (x, y, dy,
+// dx) are touched once: their 16-byte vectors are loaded and stored with the
+// nontemporal hint. The mask, which other rows read again, goes through the
+// caches. Building with SMS_NT_LOADS=0 / SMS_NT_STORES=0 drops the hints.
+#ifndef SMS_NT_LOADS
+#define SMS_NT_LOADS 1
+#endif
+#ifndef SMS_NT_STORES
+#define SMS_NT_STORES 1
+#endif
+constexpr bool kNtLoads = SMS_NT_LOADS != 0;
+constexpr bool kNtStores = SMS_NT_STORES != 0;
 
 struct FwdParams {
   const char* x;
@@ -307,7 +315,6 @@ struct FwdParams {
   float scale;
   int causal;     // CAUSAL_*
   int mask_kind;  // MASK_*
-  int policy;     // POL_*
 };
 
 struct BwdParams {
@@ -320,7 +327,6 @@ struct BwdParams {
   RowGeom g;
   float scale;
   int causal;  // CAUSAL_*: a promise that y is 0 past the bound
-  int policy;  // POL_*
 };
 
 // Keys [0, bound) of row q survive the causal rule.
@@ -331,13 +337,19 @@ SMS_DEV int causal_bound(int causal, uint32_t q, uint32_t Sq, int Sk) {
   return (int)(c < 0 ? 0 : (c > Sk ? Sk : c));
 }
 
-SMS_DEV u32x4 ld16(const char* p, bool nt) {
+// 16-byte vector of a streamed operand (x, y, dy) / of the mask, and a
+// 16-byte store to an output row (y, dx).
+template <bool NT = kNtLoads>
+SMS_DEV u32x4 ld_stream(const char* p) {
   const u32x4* q = reinterpret_cast<const u32x4*>(p);
-  return nt ? __builtin_nontemporal_load(q) : *q;
+  if constexpr (NT) return __builtin_nontemporal_load(q);
+  else return *q;
 }
-SMS_DEV void st16(char* p, u32x4 v, bool nt) {
+SMS_DEV u32x4 ld_cached(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
+SMS_DEV void st_stream(char* p, u32x4 v) {
   u32x4* q = reinterpret_cast<u32x4*>(p);
-  if (nt) __builtin_nontemporal_store(v, q); else *q = v;
+  if constexpr (kNtStores) __builtin_nontemporal_store(v, q);
+  else *q = v;
 }
 
 // E mask bytes starting at p (aligned to E), zero-extended.
@@ -425,19 +437,20 @@ SMS_DEV BwdRow bwd_row(const BwdParams& p, uint32_t w, uint32_t local) {
 // ------------------------------------------------ element and vector access
 
 // Scores of vector v of a row: x*scale + mask for keys [0, kload), -inf for
-// every other key. Any alignment.
-template <class F>
+// every other key. Any alignment. NT: nontemporal vector loads of x (off for a
+// first pass over a row that is read again).
+template <class F, bool NT = kNtLoads>
 SMS_DEV void row_scores(const FwdRow& r, int kind, int v, float scale, float (&s)[F::kE]) {
   constexpr int E = F::kE;
   constexpr int BY = F::kBytes;
   const int k0 = v * E - r.ax;
   if (k0 >= 0 && k0 + E <= r.kload) {
     // x + k0*BY sits on a 16-byte line: k0 + ax is a multiple of E.
-    F::unpack(*reinterpret_cast<const u32x4*>(r.x + (int64_t)k0 * BY), s);
+    F::unpack(ld_stream<NT>(r.x + (int64_t)k0 * BY), s);
     if (kind == MASK_ADD) {
       float m[E];
       if (r.mvec) {
-        F::unpack(*reinterpret_cast<const u32x4*>(r.m + (int64_t)k0 * BY), m);
+        F::unpack(ld_cached(r.m + (int64_t)k0 * BY), m);
       } else {
 #pragma unroll
         for (int e = 0; e < E; ++e) m[e] = F::ld(r.m + (int64_t)(k0 + e) * BY);
@@ -478,15 +491,15 @@ SMS_DEV void row_scores(const FwdRow& r, int kind, int v, float scale, float (&s
 }
 
 // y and dy of vector v for keys [0, kload), zeros elsewhere. Any alignment.
-template <class F>
+template <class F, bool NT = kNtLoads>
 SMS_DEV void row_pair(const BwdRow& r, int v, float (&yv)[F::kE], float (&gv)[F::kE]) {
   constexpr int E = F::kE;
   constexpr int BY = F::kBytes;
   const int k0 = v * E - r.ay;
   if (k0 >= 0 && k0 + E <= r.kload) {
-    F::unpack(*reinterpret_cast<const u32x4*>(r.y + (int64_t)k0 * BY), yv);
+    F::unpack(ld_stream<NT>(r.y + (int64_t)k0 * BY), yv);
     if (r.dvec) {
-      F::unpack(*reinterpret_cast<const u32x4*>(r.d + (int64_t)k0 * BY), gv);
+      F::unpack(ld_stream<NT>(r.d + (int64_t)k0 * BY), gv);
     } else {
 #pragma unroll
       for (int e = 0; e < E; ++e) gv[e] = F::ld(r.d + (int64_t)(k0 + e) * BY);
@@ -507,14 +520,13 @@ SMS_DEV void row_pair(const BwdRow& r, int v, float (&yv)[F::kE], float (&gv)[F:
 // Stores vector v of an output row (keys [0, Sk)); a whole vector goes out as
 // one 16-byte store when the output row sits at the input row's offset.
 template <class F>
-SMS_DEV void row_store(char* orow, bool ovec, int a, int v, int Sk, const float (&o)[F::kE],
-                       bool nt) {
+SMS_DEV void row_store(char* orow, bool ovec, int a, int v, int Sk, const float (&o)[F::kE]) {
   constexpr int E = F::kE;
   constexpr int BY = F::kBytes;
   const int k0 = v * E - a;
   if (k0 >= Sk || k0 + E <= 0) return;
   if (ovec && k0 >= 0 && k0 + E <= Sk) {
-    st16(orow + (int64_t)k0 * BY, F::pack(o), nt);
+    st_stream(orow + (int64_t)k0 * BY, F::pack(o));
     return;
   }
 #pragma unroll
@@ -575,9 +587,8 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int j = 0; j < NV; ++j) row_scores<F>(r, p.mask_kind, j * TPR + lane, p.scale, s[j]);
   softmax_in_registers<TPR, NV, E>(s, lane, r.ax, r.kload, red[0], red[1]);
-  const bool nt = (p.policy & POL_NT_STORE) != 0;
 #pragma unroll
-  for (int j = 0; j < NV; ++j) row_store<F>(r.y, r.yvec, r.ax, j * TPR + lane, (int)p.g.Sk, s[j], nt);
+  for (int j = 0; j < NV; ++j) row_store<F>(r.y, r.yvec, r.ax, j * TPR + lane, (int)p.g.Sk, s[j]);
 }
 
 template <class F, int TPR, int NV>
@@ -602,7 +613,6 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_bwd_kernel(BwdParams p) {
   const float dot_hi = (float)acc;
   const float dot_lo = (float)(acc - (double)dot_hi);
   const float scale = p.scale;
-  const bool nt = (p.policy & POL_NT_STORE) != 0;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int v = j * TPR + lane;
@@ -614,7 +624,7 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_bwd_kernel(BwdParams p) {
 #pragma unroll
       for (int e = 0; e < E; ++e) o[e] = (yv[j][e] * scale) * ((gv[j][e] - dot_hi) - dot_lo);
     }
-    row_store<F>(r.x, r.xvec, r.ay, v, (int)p.g.Sk, o, nt);
+    row_store<F>(r.x, r.xvec, r.ay, v, (int)p.g.Sk, o);
   }
 }
 
@@ -657,15 +667,14 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_fwd_fast_kernel(FwdParams p
     if (p.mask_kind == MASK_LEN)
       kload = min(kload, max(reinterpret_cast<const int32_t*>(p.mask)[b], 0));
   }
-  const bool ntl = (p.policy & POL_NT_LOAD) != 0;
   u32x4 xr[NV], mr[NV];
   uint64_t mb[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int v = j * TPR + lane;
     if (v * E < kload) {
-      xr[j] = ld16(xrow + (int64_t)v * 16, ntl);
-      if constexpr (KIND == FAST_ADD) mr[j] = ld16(mrow + (int64_t)v * 16, false);
+      xr[j] = ld_stream(xrow + (int64_t)v * 16);
+      if constexpr (KIND == FAST_ADD) mr[j] = ld_cached(mrow + (int64_t)v * 16);
       if constexpr (KIND == FAST_BOOL) mb[j] = ld_bits<E>(mrow + (int64_t)v * E);
     }
   }
@@ -699,11 +708,10 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_fwd_fast_kernel(FwdParams p
     }
   }
   softmax_in_registers<TPR, NV, E>(s, lane, 0, kload, red[0], red[1]);
-  const bool nts = (p.policy & POL_NT_STORE) != 0;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int v = j * TPR + lane;
-    if (v * E < Sk) st16(yrow + (int64_t)v * 16, F::pack(s[j]), nts);
+    if (v * E < Sk) st_stream(yrow + (int64_t)v * 16, F::pack(s[j]));
   }
 }
 
@@ -715,15 +723,14 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_bwd_fast_kernel(BwdParams p
   const int lane = (int)(threadIdx.x % TPR);
   const BwdRow r = bwd_row<F, RPB>(p, blockIdx.x, local_row<TPR>());
   if (!r.valid) return;
-  const bool ntl = (p.policy & POL_NT_LOAD) != 0;
   const int kload = r.kload;
   u32x4 yr[NV], dr[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int v = j * TPR + lane;
     if (v * E < kload) {
-      yr[j] = ld16(r.y + (int64_t)v * 16, ntl);
-      dr[j] = ld16(r.d + (int64_t)v * 16, ntl);
+      yr[j] = ld_stream(r.y + (int64_t)v * 16);
+      dr[j] = ld_stream(r.d + (int64_t)v * 16);
     }
   }
   double acc = 0.0;
@@ -747,7 +754,6 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_bwd_fast_kernel(BwdParams p
   const float dot_hi = (float)acc;
   const float dot_lo = (float)(acc - (double)dot_hi);
   const float scale = p.scale;
-  const bool nts = (p.policy & POL_NT_STORE) != 0;
   const int Sk = (int)p.g.Sk;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
@@ -770,7 +776,7 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_bwd_fast_kernel(BwdParams p
 #pragma unroll
         for (int e = 0; e < E; ++e) o[e] = 0.0f;
       }
-      st16(r.x + (int64_t)v * 16, F::pack(o), nts);
+      st_stream(r.x + (int64_t)v * 16, F::pack(o));
     }
   }
 }
@@ -810,7 +816,7 @@ __global__ void __launch_bounds__(kStreamTpr) sms_fwd_stream_kernel(FwdParams p)
   for (int base = 0; base < nvec; base += TPR * CV) {
     float s[CV][E];
 #pragma unroll
-    for (int j = 0; j < CV; ++j) row_scores<F>(r, kind, base + j * TPR + lane, scale, s[j]);
+    for (int j = 0; j < CV; ++j) row_scores<F, false>(r, kind, base + j * TPR + lane, scale, s[j]);
     float cm = kNegInf;
 #pragma unroll
     for (int j = 0; j < CV; ++j)
@@ -835,7 +841,6 @@ __global__ void __launch_bounds__(kStreamTpr) sms_fwd_stream_kernel(FwdParams p)
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;  // fully masked row -> zeros
 
   // Pass 2: y over the whole row.
-  const bool nt = (p.policy & POL_NT_STORE) != 0;
   for (int base = 0; base < nvec_out; base += TPR * CV) {
 #pragma unroll
     for (int j = 0; j < CV; ++j) {
@@ -849,7 +854,7 @@ __global__ void __launch_bounds__(kStreamTpr) sms_fwd_stream_kernel(FwdParams p)
 #pragma unroll
         for (int e = 0; e < E; ++e) o[e] = exp_biased(o[e], mref) * inv;
       }
-      row_store<F>(r.y, r.yvec, r.ax, v, Sk, o, nt);
+      row_store<F>(r.y, r.yvec, r.ax, v, Sk, o);
     }
   }
 }
@@ -872,7 +877,7 @@ __global__ void __launch_bounds__(kStreamTpr) sms_bwd_stream_kernel(BwdParams p)
 #pragma unroll
     for (int j = 0; j < CV; ++j) {
       float yv[E], gv[E];
-      row_pair<F>(r, base + j * TPR + lane, yv, gv);
+      row_pair<F, false>(r, base + j * TPR + lane, yv, gv);
 #pragma unroll
       for (int e = 0; e < E; ++e) acc += F::prod(yv[e], gv[e]);
     }
@@ -883,7 +888,6 @@ __global__ void __launch_bounds__(kStreamTpr) sms_bwd_stream_kernel(BwdParams p)
   const float scale = p.scale;
 
   // Pass 2: dx over the whole row.
-  const bool nt = (p.policy & POL_NT_STORE) != 0;
   for (int base = 0; base < nvec_out; base += TPR * CV) {
 #pragma unroll
     for (int j = 0; j < CV; ++j) {
@@ -898,7 +902,7 @@ __global__ void __launch_bounds__(kStreamTpr) sms_bwd_stream_kernel(BwdParams p)
 #pragma unroll
         for (int e = 0; e < E; ++e) o[e] = (yv[e] * scale) * ((gv[e] - dot_hi) - dot_lo);
       }
-      row_store<F>(r.x, r.xvec, r.ay, v, Sk, o, nt);
+      row_store<F>(r.x, r.xvec, r.ay, v, Sk, o);
     }
   }
 }
