@@ -1,25 +1,15 @@
-"""Comparison of GPU results with the float64 oracle, and the tolerances.
+"""GPU tensors to the oracle's typed numpy arrays, row gathering and sampling.
 
-Tolerances (stated for the operation's outputs):
-* fp32: max |y - y_ref| <= 1e-6, and |sum_k y_k - 1| <= 1e-5 for every row
-  with at least one unmasked key (sum taken in float64 over the fp32 outputs);
-  the backward uses the same 1e-6 absolute bound.
-* fp16 / bf16: |y - y_ref| <= 2 ulp of the output dtype at y_ref, per element,
-  with ulp_T(v) = 2^(max(floor(log2|v|), e_min) - (p - 1)) (fp16: p = 11,
-  e_min = -14; bf16: p = 8, e_min = -126). Same for the backward's dx.
-* everywhere: where the oracle's value is exactly 0 (masked key, causal-future
-  key, fully masked row) the GPU value must be exactly 0.
+The tolerances and ``compare`` live in tests/tolerance.py (numpy only) and are
+re-exported here.
 """
 
 import numpy as np
 import torch
 
 import oracle
+from tests.tolerance import F32_ABS, F32_ROWSUM, ULPS, compare, ulp  # noqa: F401
 
-F32_ABS = 1e-6
-F32_ROWSUM = 1e-5
-ULPS = 2.0
-_PREC = {"f16": (11, -14), "bf16": (8, -126)}
 DTYPE_OF = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
 
 
@@ -48,49 +38,6 @@ def mask_4d(mask, mode):
     if mode == "b_1_sk":
         return m.reshape(m.shape[0], 1, 1, m.shape[-1])
     return m
-
-
-def ulp(ref, dtype):
-    p, emin = _PREC[dtype]
-    a = np.abs(ref)
-    with np.errstate(divide="ignore"):
-        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
-    e = np.where(a > 0, np.maximum(e, emin), emin)
-    return np.exp2(e - (p - 1))
-
-
-def compare(got, ref, dtype, what="", rowsum=False, live_rows=None):
-    """Raise AssertionError unless ``got`` (float64 of the typed GPU output)
-    matches ``ref`` (oracle float64) to the dtype's tolerance. Returns stats."""
-    got = np.asarray(got, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
-    assert got.shape == ref.shape, (what, got.shape, ref.shape)
-    assert np.isfinite(got).all(), f"{what}: non-finite GPU output"
-    zero = ref == 0.0
-    nz_bad = int(np.count_nonzero(got[zero] != 0.0))
-    assert nz_bad == 0, f"{what}: {nz_bad} elements must be exactly 0"
-    err = np.abs(got - ref)
-    stats = {"max_abs": float(err.max()) if err.size else 0.0}
-    if dtype == "f32":
-        bad = err > F32_ABS
-        assert not bad.any(), (f"{what}: max abs err {err.max():.3e} > {F32_ABS} "
-                               f"({int(bad.sum())} elements)")
-        if rowsum and got.size:
-            s = got.reshape(-1, got.shape[-1]).sum(axis=1)
-            live = ref.reshape(-1, ref.shape[-1]).sum(axis=1) > 0 if live_rows is None else live_rows
-            dev = np.abs(s[live] - 1.0)
-            stats["max_rowsum_err"] = float(dev.max()) if dev.size else 0.0
-            assert (dev <= F32_ROWSUM).all(), f"{what}: row sum off by {dev.max():.3e}"
-    else:
-        u = ulp(ref, dtype)
-        r = err / u
-        stats["max_ulp"] = float(r.max()) if r.size else 0.0
-        bad = r > ULPS
-        if bad.any():
-            i = np.argmax(r)
-            raise AssertionError(f"{what}: {int(bad.sum())} elements beyond {ULPS} ulp; worst "
-                                 f"{r.flat[i]:.2f} ulp (got {got.flat[i]!r} want {ref.flat[i]!r})")
-    return stats
 
 
 def sample_rows(n_rows, Sq, k=192, seed=0):

@@ -1,9 +1,10 @@
 """HIP path against the float64 oracle, through the C ABI (via the binding).
 
 Small shapes are checked element by element on every row; the benchmark
-workloads at full size are checked on sampled rows (oracle one row at a time)
-plus properties over every row: exact zeros where keys are masked or
-causal-future, and row sums.
+workloads at full size are checked here on sampled rows (oracle one row at a
+time) plus properties over every row: exact zeros where keys are masked or
+causal-future, and row sums. tests/test_gpu_every_row.py checks every row of
+them against the oracle.
 """
 
 import math
