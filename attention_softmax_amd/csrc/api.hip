@@ -133,6 +133,18 @@ sms_status check_sizes(int64_t B, int64_t H, int64_t Sq, int64_t Sk) {
 
 bool aligned_to(const void* p, int bytes) { return ((uintptr_t)p % (uintptr_t)bytes) == 0; }
 
+// Every row (b, h, q) of the tensor starts on a 128-byte line and fills whole
+// lines: the base, every stride of a non-trivial axis and the row length are
+// multiples of 128 bytes.
+bool rows_line_exact(const void* p, const int64_t st[4], int64_t B, int64_t H, int64_t Sq,
+                     int64_t Sk, int bytes) {
+  if (((uintptr_t)p & 127) != 0 || ((Sk * bytes) & 127) != 0) return false;
+  if (B > 1 && ((st[0] * bytes) & 127) != 0) return false;
+  if (H > 1 && ((st[1] * bytes) & 127) != 0) return false;
+  if (Sq > 1 && ((st[2] * bytes) & 127) != 0) return false;
+  return true;
+}
+
 // Grid for `rows` rows; false if it exceeds what one dispatch holds (2^31-1
 // workgroups, 2^32-1 work-items).
 bool grid_for(int64_t rows, const Plan& pl, uint32_t& blocks) {
@@ -241,6 +253,8 @@ sms_status sms_forward(const void* x, const int64_t x_strides[4], const void* ma
   }
   p.scale = scale;
   p.causal = is_causal;
+  p.lines = rows_line_exact(x, x_strides, B, H, Sq, Sk, bytes) &&
+            rows_line_exact(y, y_strides, B, H, Sq, Sk, bytes);
   p.mask_kind = !has_mask ? sms::MASK_NONE
                 : shape_mode == SMS_MASK_KEY_LENGTHS ? sms::MASK_LEN
                 : is_bool ? sms::MASK_BOOL : sms::MASK_ADD;
@@ -292,6 +306,9 @@ sms_status sms_backward(const void* y, const int64_t y_strides[4], const void* d
   p.sx_b = dx_strides[0]; p.sx_h = dx_strides[1]; p.sx_q = dx_strides[2];
   p.scale = scale;
   p.causal = is_causal;
+  p.lines = rows_line_exact(y, y_strides, B, H, Sq, Sk, bytes) &&
+            rows_line_exact(dy, dy_strides, B, H, Sq, Sk, bytes) &&
+            rows_line_exact(dx, dx_strides, B, H, Sq, Sk, bytes);
   fill_geom(p.g, B, H, Sq, Sk);
 
   if (pl.family != sms::FAMILY_STREAM && ((Sk * bytes) & 15) == 0 &&
