@@ -65,12 +65,18 @@ bool use_stream(int64_t nvec) {
 // count take up to 4. Measured on MI355X: the forward runs best at 2 vectors
 // per lane up to 256 vectors per row and at 4 beyond; the backward (two input
 // streams) at 2 below 256 vectors per row and at 1 from there.
-int vectors_per_lane(int64_t nvec, bool backward) {
-  if (backward) return nvec >= 256 ? 1 : 2;
-  return nvec > 256 ? 4 : 2;
+// 16-byte vectors per lane for a row of nvec vectors, from sweeps of every
+// width on MI355X (fp32/fp16/bf16 rows of 125 to 1024 vectors, causal and
+// not): one vector per lane (the widest workgroup) wins for the backward up to
+// 512 vectors and for the forward up to 128, and up to 512 when no causal
+// bound cuts the loads short; causal forward rows keep two vectors per lane,
+// which halves the lanes that only store zeros. Longer rows: two, then four.
+int vectors_per_lane(int64_t nvec, bool backward, bool causal) {
+  if (nvec <= 128 || (nvec <= 512 && (backward || !causal))) return 1;
+  return nvec <= 2048 ? 2 : 4;
 }
 
-bool choose_plan(int64_t nvec, bool backward, Plan& out) {
+bool choose_plan(int64_t nvec, bool backward, bool causal, Plan& out) {
   if (use_stream(nvec)) {
     out.family = sms::FAMILY_STREAM;
     out.tpr = sms::kStreamTpr;
@@ -78,7 +84,7 @@ bool choose_plan(int64_t nvec, bool backward, Plan& out) {
     return true;
   }
   const int force = env_int("SMS_FORCE_TPR", 0);
-  const int want = vectors_per_lane(nvec, backward);
+  const int want = vectors_per_lane(nvec, backward, causal);
   for (int per_lane : {want, 2, 4}) {
     for (int tpr : sms::kTprList) {
       if (force && tpr != force) continue;
@@ -203,7 +209,7 @@ int sms_path(sms_dtype dtype, int64_t Sk, int backward) {
   const int bytes = dtype_bytes(dtype);
   if (!bytes || Sk < 0 || Sk > kMaxSk) return -1;
   Plan pl;
-  if (!choose_plan(vectors_per_row(Sk, 16 / bytes, true), backward != 0, pl)) return -1;
+  if (!choose_plan(vectors_per_row(Sk, 16 / bytes, true), backward != 0, false, pl)) return -1;
   if (pl.family == sms::FAMILY_STREAM) return 3;
   return pl.tpr < 64 ? 0 : (pl.tpr == 64 ? 1 : 2);
 }
@@ -235,7 +241,8 @@ sms_status sms_forward(const void* x, const int64_t x_strides[4], const void* ma
   const int E = 16 / bytes;
   const bool aligned = rows_aligned16(x, x_strides, B, H, Sq, bytes);
   Plan pl;
-  if (!choose_plan(vectors_per_row(Sk, E, aligned), false, pl)) return SMS_ERR_SHAPE;
+  if (!choose_plan(vectors_per_row(Sk, E, aligned), false, is_causal != 0, pl))
+    return SMS_ERR_SHAPE;
 
   FwdParams p;
   p.x = static_cast<const char*>(x);
@@ -295,7 +302,8 @@ sms_status sms_backward(const void* y, const int64_t y_strides[4], const void* d
 
   const bool aligned = rows_aligned16(y, y_strides, B, H, Sq, bytes);
   Plan pl;
-  if (!choose_plan(vectors_per_row(Sk, 16 / bytes, aligned), true, pl)) return SMS_ERR_SHAPE;
+  if (!choose_plan(vectors_per_row(Sk, 16 / bytes, aligned), true, is_causal != 0, pl))
+    return SMS_ERR_SHAPE;
 
   BwdParams p;
   p.y = static_cast<const char*>(y);

@@ -164,7 +164,8 @@ sms_status sms_backward(const void* y, const int64_t y_strides[4],
  * dtype). */
 int64_t sms_max_sk(sms_dtype dtype);
 
-/* Which kernel family a call with these sizes takes (rows 16-byte aligned):
+/* Which kernel family a call with these sizes takes (rows 16-byte aligned, no
+ * causal rule; a causal forward may take narrower workgroups):
  * 0 = several rows per wavefront, 1 = one wavefront per row, 2 = several
  * wavefronts per row (LDS cross-wave reduction), 3 = streaming (one 1024-lane
  * workgroup per row, two passes: online max/sum, then normalise; for rows of
