@@ -407,10 +407,23 @@ SMS_DEV void rs_store(const RowStream& s, uint32_t off, u32x4 v) {
   else buf_store<kAuxDefault>(s, off, v);
 }
 
+
 SMS_DEV void st_stream(char* p, u32x4 v) {
   u32x4* q = reinterpret_cast<u32x4*>(p);
   if constexpr (kNtStores) __builtin_nontemporal_store(v, q);
   else *q = v;
+}
+
+// 16-byte store of vector v of an aligned output row: through the row's
+// buffer resource (BUF; line-exact launch or not) or a nontemporal global store.
+template <bool BUF>
+SMS_DEV void out_store(const RowStream& rs, char* row, bool exact, int v, u32x4 val) {
+  if constexpr (BUF) {
+    if (exact) buf_store<kAuxNtDevice>(rs, (uint32_t)v * 16, val);
+    else rs_store(rs, (uint32_t)v * 16, val);
+  } else {
+    st_stream(row + (int64_t)v * 16, val);
+  }
 }
 
 // E mask bytes starting at p (aligned to E), zero-extended.
@@ -777,26 +790,10 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_fwd_fast_kernel(FwdParams p
     }
   }
   softmax_in_registers<TPR, NV, E>(s, lane, 0, kload, red[0], red[1]);
-  if constexpr (kBuf) {
-    if (exact) {
 #pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        const int v = j * TPR + lane;
-        if (v * E < Sk) buf_store<kAuxNtDevice>(ys, (uint32_t)v * 16, F::pack(s[j]));
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        const int v = j * TPR + lane;
-        if (v * E < Sk) rs_store(ys, (uint32_t)v * 16, F::pack(s[j]));
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int v = j * TPR + lane;
-      if (v * E < Sk) st_stream(yrow + (int64_t)v * 16, F::pack(s[j]));
-    }
+  for (int j = 0; j < NV; ++j) {
+    const int v = j * TPR + lane;
+    if (v * E < Sk) out_store<kBuf>(ys, yrow, exact, v, F::pack(s[j]));
   }
 }
 
@@ -875,12 +872,7 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_bwd_fast_kernel(BwdParams p
 #pragma unroll
         for (int e = 0; e < E; ++e) o[e] = 0.0f;
       }
-      if constexpr (kBuf) {
-        if (exact) buf_store<kAuxNtDevice>(xs, (uint32_t)v * 16, F::pack(o));
-        else rs_store(xs, (uint32_t)v * 16, F::pack(o));
-      } else {
-        st_stream(r.x + (int64_t)v * 16, F::pack(o));
-      }
+      out_store<kBuf>(xs, r.x, exact, v, F::pack(o));
     }
   }
 }
