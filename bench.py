@@ -77,6 +77,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the oracle CPU baseline sample (0 = skip)")
     ap.add_argument("--no-copy", action="store_true", help="skip the plain-copy reference")
+    ap.add_argument("--no-torch", action="store_true",
+                    help="skip the unfused PyTorch reference (context only)")
     ap.add_argument("--traffic", default=TRAFFIC_JSON,
                     help="HBM bytes per launch from rocprofv3 counters (see --ingest)")
     ap.add_argument("--ingest", default=None, metavar="DIR",
@@ -231,6 +233,57 @@ def cpu_baseline(w, y, dy, step_bytes, rows_total, budget_s):
             "rows_per_s": round(done / spent, 1)}
 
 
+def torch_reference(torch, w, stream, fwd_b, bwd_b, fwd_ms, bwd_ms):
+    """Unfused PyTorch on the same inputs, as context: softmax(x*scale + mask)
+    with torch's own kernels (scale, mask add and softmax as separate passes;
+    the mask broadcast as a view), and torch's softmax backward times scale."""
+    x, dy, scale = w["x"], w["dy"], w["scale"]
+    B, H, Sq, Sk = x.shape
+    m = w["mask"]
+    if m is not None:
+        m = {"sq_sk": lambda t: t.view(1, 1, Sq, Sk), "b_sq_sk": lambda t: t.view(B, 1, Sq, Sk),
+             "b_1_sk": lambda t: t.view(B, 1, 1, Sk), "full": lambda t: t}[w["mode"]](m)
+    causal = None
+    if w["causal"]:
+        causal = torch.triu(torch.ones(Sq, Sk, dtype=torch.bool, device=x.device), diagonal=1)
+
+    def fwd():
+        s = x * scale
+        if m is not None:
+            s = s + m
+        if causal is not None:
+            s = s.masked_fill(causal, float("-inf"))
+        return torch.softmax(s, dim=-1)
+
+    def bwd(yt):
+        return torch._softmax_backward_data(dy, yt, -1, x.dtype) * scale
+
+    yt = fwd()
+    for _ in range(2):
+        fwd()
+        bwd(yt)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    n = 5
+    e[0].record(stream)
+    for _ in range(n):
+        fwd()
+    e[1].record(stream)
+    for _ in range(n):
+        bwd(yt)
+    e[2].record(stream)
+    torch.cuda.synchronize()
+    tf = e[0].elapsed_time(e[1]) / n
+    tb = e[1].elapsed_time(e[2]) / n
+    del yt
+    torch.cuda.empty_cache()
+    return {"what": "unfused PyTorch: x*scale (+mask) (masked_fill causal) softmax; "
+                    "_softmax_backward_data * scale",
+            "forward_us": round(tf * 1e3, 1), "backward_us": round(tb * 1e3, 1),
+            "forward_GBps_algorithmic": round(fwd_b / (tf * 1e-3) / 1e9, 1),
+            "backward_GBps_algorithmic": round(bwd_b / (tb * 1e-3) / 1e9, 1),
+            "speedup_forward": round(tf / fwd_ms, 2), "speedup_backward": round(tb / bwd_ms, 2)}
+
+
 def main():
     args = parse()
     if args.ingest:
@@ -320,6 +373,10 @@ def main():
                 "GBps": round(2 * n / (cms * 1e-3) / 1e9, 1)}
         del src, dst
 
+    torch_ref = None
+    if not args.no_torch:
+        torch_ref = torch_reference(torch, w, stream, fwd_b, bwd_b, fwd_ms, bwd_ms)
+
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(w, y, dy, step_b, rows, args.cpu_seconds)
@@ -348,6 +405,7 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": kern[dom]["frac_hbm_peak"], "traffic": traffic},
         "copy_reference": copy,
+        "torch_reference": torch_ref,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }
