@@ -22,4 +22,5 @@ from .ops import (  # noqa: F401
     sms_forward,
     sms_max_sk,
     sms_path,
+    sms_workspace_bytes,
 )

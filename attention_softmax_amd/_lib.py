@@ -19,14 +19,14 @@ LIB_PATH = os.path.join(HERE, "libsms.so")
 SMS_OK = 0
 STATUS_NAMES = {0: "SMS_OK", 1: "SMS_ERR_NULL", 2: "SMS_ERR_SHAPE", 3: "SMS_ERR_STRIDE",
                 4: "SMS_ERR_DTYPE", 5: "SMS_ERR_MASK_MODE", 6: "SMS_ERR_ALIGN", 7: "SMS_ERR_HIP",
-                8: "SMS_ERR_CAUSAL"}
+                8: "SMS_ERR_CAUSAL", 9: "SMS_ERR_WORKSPACE"}
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 MASK_MODES = {"none": 0, "sq_sk": 1, "b_sq_sk": 2, "b_1_sk": 3, "full": 4, "key_lengths": 5}
 MASK_BOOL = 0x10
 CAUSAL_CODES = {"none": 0, "top_left": 1, "bottom_right": 2}
-EXPORTS = ("sms_forward", "sms_backward", "sms_max_sk", "sms_path", "sms_status_str",
-           "sms_abi_version")
-ABI_VERSION = 2
+EXPORTS = ("sms_forward", "sms_backward", "sms_forward_ws", "sms_backward_ws",
+           "sms_workspace_bytes", "sms_max_sk", "sms_path", "sms_status_str", "sms_abi_version")
+ABI_VERSION = 3
 
 _lock = threading.Lock()
 _lib = None
@@ -49,6 +49,14 @@ def _declare(L):
     L.sms_backward.argtypes = [vp, strides, vp, strides, vp, strides, i32, i64, i64, i64, i64,
                                f32, i32, vp]
     L.sms_backward.restype = i32
+    L.sms_forward_ws.argtypes = [vp, strides, vp, i32, vp, strides, i32, i64, i64, i64, i64, f32,
+                                 i32, vp, i64, vp]
+    L.sms_forward_ws.restype = i32
+    L.sms_backward_ws.argtypes = [vp, strides, vp, strides, vp, strides, i32, i64, i64, i64, i64,
+                                  f32, i32, vp, i64, vp]
+    L.sms_backward_ws.restype = i32
+    L.sms_workspace_bytes.argtypes = [i32, i64, i64, i64, i64, i32]
+    L.sms_workspace_bytes.restype = i64
     L.sms_max_sk.argtypes = [i32]
     L.sms_max_sk.restype = i64
     L.sms_path.argtypes = [i32, i64, i32]

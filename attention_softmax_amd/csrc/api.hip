@@ -11,6 +11,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include "kernels.hpp"
 #include "sms.h"
 
@@ -25,6 +27,20 @@ using sms::RowGeom;
 constexpr int64_t kMaxVecPerRow = 1024 * 4;
 // Longest row: keeps every in-kernel element index far inside int32.
 constexpr int64_t kMaxSk = int64_t(1) << 30;
+// Split rows (calls with a workspace): rows are split when there are fewer
+// than kSplitRowsBelow of them (one workgroup per row would leave CUs idle)
+// and each holds at least kSplitMinVec vectors (256 KB; shorter rows finish
+// sooner at one workgroup each than the split's two launches take); chunks of
+// at least kSplitMinChunk vectors (16 KB), aiming at kSplitTargetWgs
+// workgroups in all. The grid's second dimension holds at most kSplitGridRows
+// rows. Measured on MI355X (fp16/bf16/fp32, 1 to 1024 rows of 16K-4M keys):
+// 8 fp16 rows of 2^20 keys 158 -> 25 us, one bf16 row of 2^22 keys 675 ->
+// 25 us; 64 fp32 rows of 16384 keys 13 -> 24 us (hence the length floor).
+constexpr int64_t kSplitRowsBelow = 256;
+constexpr int64_t kSplitMinVec = 16384;
+constexpr int64_t kSplitMinChunk = 1024;
+constexpr int64_t kSplitTargetWgs = 2048;
+constexpr int64_t kSplitGridRows = 65535;
 
 int dtype_bytes(sms_dtype d) {
   switch (d) {
@@ -44,10 +60,13 @@ int env_int(const char* name, int dflt) {
 //   SMS_FORCE_TPR=<4..1024>  lanes per row (0 = automatic)
 //   SMS_FAST=0               never take the aligned-row kernels
 //   SMS_FORCE_STREAM=1       take the streaming kernels for every row
+//   SMS_FORCE_SPLIT=<C>      split every row into C chunks (calls with a workspace)
+//   SMS_SPLIT=0              never split rows
 struct Plan {
   int family = sms::FAMILY_GENERAL;
   int tpr = 0;
   int nv = 0;
+  int64_t chunks = 1, chunk_vec = 0;  // FAMILY_SPLIT
 };
 
 // Vectors a row may span: ceil(Sk/E) when every row starts on a 16-byte line,
@@ -60,11 +79,35 @@ bool use_stream(int64_t nvec) {
   return nvec > kMaxVecPerRow || env_int("SMS_FORCE_STREAM", 0) != 0;
 }
 
-// Fewest lanes per row that hold the row in at most `want` vectors per lane,
-// then the fewest vectors that cover it; rows too long for 1024 lanes at that
-// count take up to 4. Measured on MI355X: the forward runs best at 2 vectors
-// per lane up to 256 vectors per row and at 4 beyond; the backward (two input
-// streams) at 2 below 256 vectors per row and at 1 from there.
+// Chunks per row for `rows` rows of up to `nvec` vectors: 1 = no split.
+int64_t split_chunks(int64_t rows, int64_t nvec) {
+  if (rows > kSplitGridRows || nvec < 1) return 1;
+  const int force = env_int("SMS_FORCE_SPLIT", 0);
+  if (force > 0) return std::min<int64_t>(force, nvec);
+  if (env_int("SMS_SPLIT", 1) == 0 || rows >= kSplitRowsBelow || nvec < kSplitMinVec) return 1;
+  const int64_t want = (kSplitTargetWgs + rows - 1) / rows;
+  return std::max<int64_t>(1, std::min(want, nvec / kSplitMinChunk));
+}
+
+// Vectors per chunk for `chunks` chunks of a row of nvec vectors: a multiple
+// of the workgroup width (unless forced), then the chunk count that covers
+// the row at that size (never more than asked for).
+void split_shape(int64_t nvec, int64_t chunks, Plan& pl) {
+  int64_t cv = (nvec + chunks - 1) / chunks;
+  if (env_int("SMS_FORCE_SPLIT", 0) <= 0)
+    cv = (cv + sms::kSplitTpr - 1) / sms::kSplitTpr * sms::kSplitTpr;
+  pl.family = sms::FAMILY_SPLIT;
+  pl.chunk_vec = cv;
+  pl.chunks = (nvec + cv - 1) / cv;
+}
+
+// Workspace bytes of a split launch: 8 per (row, chunk); 0 without a split.
+// Sized for unaligned rows, which span the most vectors.
+int64_t workspace_bytes(int64_t rows, int64_t Sk, int E) {
+  const int64_t c = split_chunks(rows, vectors_per_row(Sk, E, false));
+  return c > 1 ? rows * c * 8 : 0;
+}
+
 // 16-byte vectors per lane for a row of nvec vectors, from sweeps of every
 // width on MI355X (fp32/fp16/bf16 rows of 125 to 1024 vectors, causal and
 // not): one vector per lane (the widest workgroup) wins for the backward up to
@@ -76,6 +119,9 @@ int vectors_per_lane(int64_t nvec, bool backward, bool causal) {
   return nvec <= 2048 ? 2 : 4;
 }
 
+// Fewest lanes per row that hold the row at vectors_per_lane() vectors per
+// lane, then the fewest vectors that cover it; rows too long for 1024 lanes at
+// that count take up to 4.
 bool choose_plan(int64_t nvec, bool backward, bool causal, Plan& out) {
   if (use_stream(nvec)) {
     out.family = sms::FAMILY_STREAM;
@@ -154,6 +200,12 @@ bool rows_line_exact(const void* p, const int64_t st[4], int64_t B, int64_t H, i
 // Grid for `rows` rows; false if it exceeds what one dispatch holds (2^31-1
 // workgroups, 2^32-1 work-items).
 bool grid_for(int64_t rows, const Plan& pl, uint32_t& blocks) {
+  if (pl.family == sms::FAMILY_SPLIT) {  // grid chunks x rows, 256 lanes
+    if (rows > kSplitGridRows || pl.chunks * rows * sms::kSplitTpr > (int64_t)UINT32_MAX)
+      return false;
+    blocks = (uint32_t)rows;
+    return true;
+  }
   const bool st = pl.family == sms::FAMILY_STREAM;
   const int block = st ? sms::kStreamTpr : sms::block_of(pl.tpr);
   const int rpb = st ? 1 : block / pl.tpr;
@@ -199,6 +251,7 @@ const char* sms_status_str(sms_status s) {
     case SMS_ERR_ALIGN: return "pointer not aligned to its element size";
     case SMS_ERR_HIP: return "HIP runtime error at launch";
     case SMS_ERR_CAUSAL: return "unknown causal mode";
+    case SMS_ERR_WORKSPACE: return "workspace smaller than sms_workspace_bytes() asks for";
     default: return "unknown status";
   }
 }
@@ -214,10 +267,29 @@ int sms_path(sms_dtype dtype, int64_t Sk, int backward) {
   return pl.tpr < 64 ? 0 : (pl.tpr == 64 ? 1 : 2);
 }
 
+int64_t sms_workspace_bytes(sms_dtype dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk,
+                            int backward) {
+  (void)backward;  // 8 bytes per (row, chunk) either way
+  const int bytes = dtype_bytes(dtype);
+  if (!bytes || B < 0 || H < 0 || Sq < 0 || Sk < 0) return -1;
+  if (B == 0 || H == 0 || Sq == 0 || Sk == 0) return 0;
+  if (check_sizes(B, H, Sq, Sk) != SMS_OK) return -1;
+  return workspace_bytes(B * H * Sq, Sk, 16 / bytes);
+}
+
 sms_status sms_forward(const void* x, const int64_t x_strides[4], const void* mask,
                        int mask_mode, void* y, const int64_t y_strides[4], sms_dtype dtype,
                        int64_t B, int64_t H, int64_t Sq, int64_t Sk, float scale, int is_causal,
                        void* stream) {
+  return sms_forward_ws(x, x_strides, mask, mask_mode, y, y_strides, dtype, B, H, Sq, Sk, scale,
+                        is_causal, nullptr, 0, stream);
+}
+
+sms_status sms_forward_ws(const void* x, const int64_t x_strides[4], const void* mask,
+                          int mask_mode, void* y, const int64_t y_strides[4], sms_dtype dtype,
+                          int64_t B, int64_t H, int64_t Sq, int64_t Sk, float scale,
+                          int is_causal, void* workspace, int64_t workspace_bytes_given,
+                          void* stream) {
   bool empty = false;
   sms_status st = check_common(dtype, B, H, Sq, Sk, is_causal, empty);
   if (st != SMS_OK) return st;
@@ -237,12 +309,17 @@ sms_status sms_forward(const void* x, const int64_t x_strides[4], const void* ma
   if (!aligned_to(x, bytes) || !aligned_to(y, bytes) ||
       (has_mask && !aligned_to(mask, mask_bytes)))
     return SMS_ERR_ALIGN;
-
   const int E = 16 / bytes;
+  const int64_t need = workspace ? workspace_bytes(B * H * Sq, Sk, E) : 0;
+  if (need > 0 && (workspace_bytes_given < need || !aligned_to(workspace, 8)))
+    return SMS_ERR_WORKSPACE;
+
   const bool aligned = rows_aligned16(x, x_strides, B, H, Sq, bytes);
+  const int64_t nvec = vectors_per_row(Sk, E, aligned);
   Plan pl;
-  if (!choose_plan(vectors_per_row(Sk, E, aligned), false, is_causal != 0, pl))
-    return SMS_ERR_SHAPE;
+  if (!choose_plan(nvec, false, is_causal != 0, pl)) return SMS_ERR_SHAPE;
+  const int64_t chunks = need > 0 ? split_chunks(B * H * Sq, nvec) : 1;
+  if (chunks > 1) split_shape(nvec, chunks, pl);
 
   FwdParams p;
   p.x = static_cast<const char*>(x);
@@ -266,8 +343,11 @@ sms_status sms_forward(const void* x, const int64_t x_strides[4], const void* ma
                 : shape_mode == SMS_MASK_KEY_LENGTHS ? sms::MASK_LEN
                 : is_bool ? sms::MASK_BOOL : sms::MASK_ADD;
   fill_geom(p.g, B, H, Sq, Sk);
+  p.chunks = (uint32_t)pl.chunks;
+  p.chunk_vec = (uint32_t)pl.chunk_vec;
+  p.ws = static_cast<float2*>(workspace);
 
-  if (pl.family != sms::FAMILY_STREAM) {
+  if (pl.family != sms::FAMILY_STREAM && pl.family != sms::FAMILY_SPLIT) {
     // Aligned-row kernels: every operand's rows on 16-byte lines, whole vectors.
     const bool mask_whole = !has_mask || p.mask_kind == sms::MASK_LEN ||
                             (p.mask_kind == sms::MASK_ADD && ((uintptr_t)mask & 15) == 0) ||
@@ -287,6 +367,15 @@ sms_status sms_backward(const void* y, const int64_t y_strides[4], const void* d
                         const int64_t dy_strides[4], void* dx, const int64_t dx_strides[4],
                         sms_dtype dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, float scale,
                         int is_causal, void* stream) {
+  return sms_backward_ws(y, y_strides, dy, dy_strides, dx, dx_strides, dtype, B, H, Sq, Sk, scale,
+                         is_causal, nullptr, 0, stream);
+}
+
+sms_status sms_backward_ws(const void* y, const int64_t y_strides[4], const void* dy,
+                           const int64_t dy_strides[4], void* dx, const int64_t dx_strides[4],
+                           sms_dtype dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk,
+                           float scale, int is_causal, void* workspace,
+                           int64_t workspace_bytes_given, void* stream) {
   bool empty = false;
   sms_status st = check_common(dtype, B, H, Sq, Sk, is_causal, empty);
   if (st != SMS_OK) return st;
@@ -299,11 +388,17 @@ sms_status sms_backward(const void* y, const int64_t y_strides[4], const void* d
   const int bytes = dtype_bytes(dtype);
   if (!aligned_to(y, bytes) || !aligned_to(dy, bytes) || !aligned_to(dx, bytes))
     return SMS_ERR_ALIGN;
+  const int E = 16 / bytes;
+  const int64_t need = workspace ? workspace_bytes(B * H * Sq, Sk, E) : 0;
+  if (need > 0 && (workspace_bytes_given < need || !aligned_to(workspace, 8)))
+    return SMS_ERR_WORKSPACE;
 
   const bool aligned = rows_aligned16(y, y_strides, B, H, Sq, bytes);
+  const int64_t nvec = vectors_per_row(Sk, E, aligned);
   Plan pl;
-  if (!choose_plan(vectors_per_row(Sk, 16 / bytes, aligned), true, is_causal != 0, pl))
-    return SMS_ERR_SHAPE;
+  if (!choose_plan(nvec, true, is_causal != 0, pl)) return SMS_ERR_SHAPE;
+  const int64_t chunks = need > 0 ? split_chunks(B * H * Sq, nvec) : 1;
+  if (chunks > 1) split_shape(nvec, chunks, pl);
 
   BwdParams p;
   p.y = static_cast<const char*>(y);
@@ -318,8 +413,12 @@ sms_status sms_backward(const void* y, const int64_t y_strides[4], const void* d
             rows_line_exact(dy, dy_strides, B, H, Sq, Sk, bytes) &&
             rows_line_exact(dx, dx_strides, B, H, Sq, Sk, bytes);
   fill_geom(p.g, B, H, Sq, Sk);
+  p.chunks = (uint32_t)pl.chunks;
+  p.chunk_vec = (uint32_t)pl.chunk_vec;
+  p.ws = static_cast<double*>(workspace);
 
-  if (pl.family != sms::FAMILY_STREAM && ((Sk * bytes) & 15) == 0 &&
+  if (pl.family != sms::FAMILY_STREAM && pl.family != sms::FAMILY_SPLIT &&
+      ((Sk * bytes) & 15) == 0 &&
       env_int("SMS_FAST", 1) != 0 && aligned &&
       rows_aligned16(dy, dy_strides, B, H, Sq, bytes) &&
       rows_aligned16(dx, dx_strides, B, H, Sq, bytes))

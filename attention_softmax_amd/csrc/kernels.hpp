@@ -316,6 +316,10 @@ struct FwdParams {
   int causal;     // CAUSAL_*
   int mask_kind;  // MASK_*
   int lines;      // every row of x and y starts on a 128-byte line and fills whole lines
+  // Split rows (FAMILY_SPLIT): chunks per row, vectors per chunk, and the
+  // workspace of rows * chunks (max, sum) pairs.
+  uint32_t chunks, chunk_vec;
+  float2* ws;
 };
 
 struct BwdParams {
@@ -329,6 +333,10 @@ struct BwdParams {
   float scale;
   int causal;  // CAUSAL_*: a promise that y is 0 past the bound
   int lines;   // every row of y, dy and dx starts on a 128-byte line and fills whole lines
+  // Split rows (FAMILY_SPLIT): chunks per row, vectors per chunk, and the
+  // workspace of rows * chunks partial dot products.
+  uint32_t chunks, chunk_vec;
+  double* ws;
 };
 
 // Keys [0, bound) of row q survive the causal rule.
@@ -893,26 +901,44 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_bwd_fast_kernel(BwdParams p
 constexpr int kStreamTpr = 1024;
 constexpr int kStreamCv = 4;
 
-template <class F>
-__global__ void __launch_bounds__(kStreamTpr) sms_fwd_stream_kernel(FwdParams p) {
-  constexpr int E = F::kE;
-  constexpr int TPR = kStreamTpr;
-  constexpr int CV = kStreamCv;
-  __shared__ float red[2][TPR / 64];
-  const FwdRow r = fwd_row<F, 1>(p, blockIdx.x, 0);  // one row per workgroup, grid = rows
-  const int Sk = (int)p.g.Sk;
-  const int lane = (int)threadIdx.x;
-  const int kind = p.mask_kind;
-  const float scale = p.scale;
-  const int nvec = (int)(((int64_t)r.ax + r.kload + E - 1) / E);  // vectors holding read keys
-  const int nvec_out = (int)(((int64_t)r.ax + Sk + E - 1) / E);
+// Folds the (max, biased sum) pair (pm, pl) into (m, l).
+SMS_DEV void merge_ml(float& m, float& l, float pm, float pl) {
+  if (pm == kNegInf) return;
+  if (pm > m) {
+    l = (m == kNegInf) ? pl : l * __builtin_amdgcn_exp2f((m - pm) * kLog2e) + pl;
+    m = pm;
+  } else {
+    l += pl * __builtin_amdgcn_exp2f((pm - m) * kLog2e);
+  }
+}
 
-  // Pass 1: per-lane running (max, rescaled sum).
-  float m_run = kNegInf, l_run = 0.0f;
-  for (int base = 0; base < nvec; base += TPR * CV) {
+// The workgroup's (max, biased sum) from every lane's pair, in a fixed order.
+template <int TPR>
+SMS_DEV void block_ml(float m, float l, float (&red)[2][TPR / 64], float& M, float& L) {
+  M = row_reduce<TPR>(m, OpMax(), red[0]);
+  const float mine = (m == kNegInf) ? 0.0f : l * __builtin_amdgcn_exp2f((m - M) * kLog2e);
+  L = row_reduce<TPR>(mine, OpAdd(), red[1]);
+}
+
+// Pass 1 over vectors [v0, v1) of a row: this lane's running (max, biased sum).
+template <class F, int TPR>
+SMS_DEV void online_ml(const FwdRow& r, int kind, float scale, int v0, int v1, float& m_run,
+                       float& l_run) {
+  constexpr int E = F::kE;
+  constexpr int CV = kStreamCv;
+  const int lane = (int)(threadIdx.x % TPR);
+  for (int base = v0; base < v1; base += TPR * CV) {
     float s[CV][E];
 #pragma unroll
-    for (int j = 0; j < CV; ++j) row_scores<F, false>(r, kind, base + j * TPR + lane, scale, s[j]);
+    for (int j = 0; j < CV; ++j) {
+      const int v = base + j * TPR + lane;
+      if (v < v1) {
+        row_scores<F, false>(r, kind, v, scale, s[j]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[j][e] = kNegInf;
+      }
+    }
     float cm = kNegInf;
 #pragma unroll
     for (int j = 0; j < CV; ++j)
@@ -929,84 +955,196 @@ __global__ void __launch_bounds__(kStreamTpr) sms_fwd_stream_kernel(FwdParams p)
         for (int e = 0; e < E; ++e) l_run += exp_biased(s[j][e], m_run);
     }
   }
-  const float M = row_reduce<TPR>(m_run, OpMax(), red[0]);
-  const float mine =
-      (m_run == kNegInf) ? 0.0f : l_run * __builtin_amdgcn_exp2f((m_run - M) * kLog2e);
-  const float L = row_reduce<TPR>(mine, OpAdd(), red[1]);
-  const float mref = (M == kNegInf) ? 0.0f : M;
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;  // fully masked row -> zeros
+}
 
-  // Pass 2: y over the whole row.
-  for (int base = 0; base < nvec_out; base += TPR * CV) {
+// Pass 2 over vectors [v0, v1) of a row: y = exp(s - M) / L, zeros past the bound.
+template <class F, int TPR>
+SMS_DEV void write_probs(const FwdRow& r, int kind, float scale, float mref, float inv, int v0,
+                         int v1, int Sk) {
+  constexpr int E = F::kE;
+  constexpr int CV = kStreamCv;
+  const int lane = (int)(threadIdx.x % TPR);
+  for (int base = v0; base < v1; base += TPR * CV) {
 #pragma unroll
     for (int j = 0; j < CV; ++j) {
       const int v = base + j * TPR + lane;
-      float o[E];
-      if (v * E - r.ax >= r.kload) {
+      if (v < v1) {
+        float o[E];
+        if (v * E - r.ax >= r.kload) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = 0.0f;
-      } else {
-        row_scores<F>(r, kind, v, scale, o);
+          for (int e = 0; e < E; ++e) o[e] = 0.0f;
+        } else {
+          row_scores<F>(r, kind, v, scale, o);
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = exp_biased(o[e], mref) * inv;
+          for (int e = 0; e < E; ++e) o[e] = exp_biased(o[e], mref) * inv;
+        }
+        row_store<F>(r.y, r.yvec, r.ax, v, Sk, o);
       }
-      row_store<F>(r.y, r.yvec, r.ax, v, Sk, o);
     }
   }
+}
+
+// Pass 1 of the backward over vectors [v0, v1): this lane's part of sum dy*y.
+template <class F, int TPR>
+SMS_DEV double dot_part(const BwdRow& r, int v0, int v1) {
+  constexpr int E = F::kE;
+  constexpr int CV = kStreamCv;
+  const int lane = (int)(threadIdx.x % TPR);
+  double acc = 0.0;
+  for (int base = v0; base < v1; base += TPR * CV) {
+#pragma unroll
+    for (int j = 0; j < CV; ++j) {
+      const int v = base + j * TPR + lane;
+      if (v < v1) {
+        float yv[E], gv[E];
+        row_pair<F, false>(r, v, yv, gv);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc += F::prod(yv[e], gv[e]);
+      }
+    }
+  }
+  return acc;
+}
+
+// Pass 2 of the backward over vectors [v0, v1): dx = scale*y*(dy - dot).
+template <class F, int TPR>
+SMS_DEV void write_grads(const BwdRow& r, float scale, double dot, int v0, int v1, int Sk) {
+  constexpr int E = F::kE;
+  constexpr int CV = kStreamCv;
+  const int lane = (int)(threadIdx.x % TPR);
+  const float dot_hi = (float)dot;
+  const float dot_lo = (float)(dot - (double)dot_hi);
+  for (int base = v0; base < v1; base += TPR * CV) {
+#pragma unroll
+    for (int j = 0; j < CV; ++j) {
+      const int v = base + j * TPR + lane;
+      if (v < v1) {
+        float o[E];
+        if (v * E - r.ay >= r.kload) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) o[e] = 0.0f;
+        } else {
+          float yv[E], gv[E];
+          row_pair<F>(r, v, yv, gv);
+#pragma unroll
+          for (int e = 0; e < E; ++e) o[e] = (yv[e] * scale) * ((gv[e] - dot_hi) - dot_lo);
+        }
+        row_store<F>(r.x, r.xvec, r.ay, v, Sk, o);
+      }
+    }
+  }
+}
+
+template <class F>
+__global__ void __launch_bounds__(kStreamTpr) sms_fwd_stream_kernel(FwdParams p) {
+  constexpr int E = F::kE;
+  constexpr int TPR = kStreamTpr;
+  __shared__ float red[2][TPR / 64];
+  const FwdRow r = fwd_row<F, 1>(p, blockIdx.x, 0);  // one row per workgroup, grid = rows
+  const int Sk = (int)p.g.Sk;
+  const int nvec = (int)(((int64_t)r.ax + r.kload + E - 1) / E);  // vectors holding read keys
+  const int nvec_out = (int)(((int64_t)r.ax + Sk + E - 1) / E);
+  float m = kNegInf, l = 0.0f, M, L;
+  online_ml<F, TPR>(r, p.mask_kind, p.scale, 0, nvec, m, l);
+  block_ml<TPR>(m, l, red, M, L);
+  const float mref = (M == kNegInf) ? 0.0f : M;
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;  // fully masked row -> zeros
+  write_probs<F, TPR>(r, p.mask_kind, p.scale, mref, inv, 0, nvec_out, Sk);
 }
 
 template <class F>
 __global__ void __launch_bounds__(kStreamTpr) sms_bwd_stream_kernel(BwdParams p) {
   constexpr int E = F::kE;
   constexpr int TPR = kStreamTpr;
-  constexpr int CV = kStreamCv;
   __shared__ double red[TPR / 64];
   const BwdRow r = bwd_row<F, 1>(p, blockIdx.x, 0);
   const int Sk = (int)p.g.Sk;
-  const int lane = (int)threadIdx.x;
   const int nvec = (int)(((int64_t)r.ay + r.kload + E - 1) / E);
   const int nvec_out = (int)(((int64_t)r.ay + Sk + E - 1) / E);
+  const double dot = row_reduce<TPR>(dot_part<F, TPR>(r, 0, nvec), OpAdd(), red);
+  write_grads<F, TPR>(r, p.scale, dot, 0, nvec_out, Sk);
+}
 
-  // Pass 1: the row's dot product, in fp64.
-  double acc = 0.0;
-  for (int base = 0; base < nvec; base += TPR * CV) {
-#pragma unroll
-    for (int j = 0; j < CV; ++j) {
-      float yv[E], gv[E];
-      row_pair<F, false>(r, base + j * TPR + lane, yv, gv);
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc += F::prod(yv[e], gv[e]);
-    }
-  }
-  acc = row_reduce<TPR>(acc, OpAdd(), red);
-  const float dot_hi = (float)acc;
-  const float dot_lo = (float)(acc - (double)dot_hi);
-  const float scale = p.scale;
+// ------------------------------------------------- long rows, few of them: split
+//
+// With too few rows to fill the GPU at one workgroup per row, each row is cut
+// into `chunks` chunks of `chunk_vec` vectors and every (chunk, row) pair gets
+// a 256-lane workgroup (grid chunks x rows), in two launches. The first writes
+// each chunk's (max, biased sum) -- the backward: its partial dot product -- to
+// the workspace; the second merges the row's partials lane-strided and then
+// across the workgroup, in a fixed order (deterministic), and writes its
+// chunk's outputs, reading the chunk's inputs again (from the caches when the
+// rows fit in them). The per-chunk pairs merge as in the streaming pass 1.
 
-  // Pass 2: dx over the whole row.
-  for (int base = 0; base < nvec_out; base += TPR * CV) {
-#pragma unroll
-    for (int j = 0; j < CV; ++j) {
-      const int v = base + j * TPR + lane;
-      float o[E];
-      if (v * E - r.ay >= r.kload) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = 0.0f;
-      } else {
-        float yv[E], gv[E];
-        row_pair<F>(r, v, yv, gv);
-#pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = (yv[e] * scale) * ((gv[e] - dot_hi) - dot_lo);
-      }
-      row_store<F>(r.x, r.xvec, r.ay, v, Sk, o);
-    }
+constexpr int kSplitTpr = 256;
+
+template <class F>
+__global__ void __launch_bounds__(kSplitTpr) sms_fwd_split_partial_kernel(FwdParams p) {
+  constexpr int E = F::kE;
+  __shared__ float red[2][kSplitTpr / 64];
+  const FwdRow r = fwd_row<F, 1>(p, blockIdx.y, 0);  // grid.y = rows
+  const int nvec = (int)(((int64_t)r.ax + r.kload + E - 1) / E);
+  const int v0 = (int)(blockIdx.x * p.chunk_vec);
+  const int v1 = min(v0 + (int)p.chunk_vec, nvec);
+  float m = kNegInf, l = 0.0f, M, L;
+  online_ml<F, kSplitTpr>(r, p.mask_kind, p.scale, v0, v1, m, l);
+  block_ml<kSplitTpr>(m, l, red, M, L);
+  if (threadIdx.x == 0) p.ws[(size_t)blockIdx.y * p.chunks + blockIdx.x] = make_float2(M, L);
+}
+
+template <class F>
+__global__ void __launch_bounds__(kSplitTpr) sms_fwd_split_final_kernel(FwdParams p) {
+  constexpr int E = F::kE;
+  __shared__ float red[2][kSplitTpr / 64];
+  const FwdRow r = fwd_row<F, 1>(p, blockIdx.y, 0);
+  const int Sk = (int)p.g.Sk;
+  const float2* part = p.ws + (size_t)blockIdx.y * p.chunks;
+  float m = kNegInf, l = 0.0f, M, L;
+  for (uint32_t c = threadIdx.x; c < p.chunks; c += kSplitTpr) {
+    const float2 pc = part[c];
+    merge_ml(m, l, pc.x, pc.y);
   }
+  block_ml<kSplitTpr>(m, l, red, M, L);
+  const float mref = (M == kNegInf) ? 0.0f : M;
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  const int nvec_out = (int)(((int64_t)r.ax + Sk + E - 1) / E);
+  const int v0 = (int)(blockIdx.x * p.chunk_vec);
+  const int v1 = min(v0 + (int)p.chunk_vec, nvec_out);
+  write_probs<F, kSplitTpr>(r, p.mask_kind, p.scale, mref, inv, v0, v1, Sk);
+}
+
+template <class F>
+__global__ void __launch_bounds__(kSplitTpr) sms_bwd_split_partial_kernel(BwdParams p) {
+  constexpr int E = F::kE;
+  __shared__ double red[kSplitTpr / 64];
+  const BwdRow r = bwd_row<F, 1>(p, blockIdx.y, 0);
+  const int nvec = (int)(((int64_t)r.ay + r.kload + E - 1) / E);
+  const int v0 = (int)(blockIdx.x * p.chunk_vec);
+  const int v1 = min(v0 + (int)p.chunk_vec, nvec);
+  const double d = row_reduce<kSplitTpr>(dot_part<F, kSplitTpr>(r, v0, v1), OpAdd(), red);
+  if (threadIdx.x == 0) p.ws[(size_t)blockIdx.y * p.chunks + blockIdx.x] = d;
+}
+
+template <class F>
+__global__ void __launch_bounds__(kSplitTpr) sms_bwd_split_final_kernel(BwdParams p) {
+  constexpr int E = F::kE;
+  __shared__ double red[kSplitTpr / 64];
+  const BwdRow r = bwd_row<F, 1>(p, blockIdx.y, 0);
+  const int Sk = (int)p.g.Sk;
+  const double* part = p.ws + (size_t)blockIdx.y * p.chunks;
+  double d = 0.0;
+  for (uint32_t c = threadIdx.x; c < p.chunks; c += kSplitTpr) d += part[c];
+  const double dot = row_reduce<kSplitTpr>(d, OpAdd(), red);
+  const int nvec_out = (int)(((int64_t)r.ay + Sk + E - 1) / E);
+  const int v0 = (int)(blockIdx.x * p.chunk_vec);
+  const int v1 = min(v0 + (int)p.chunk_vec, nvec_out);
+  write_grads<F, kSplitTpr>(r, p.scale, dot, v0, v1, Sk);
 }
 
 // --------------------------------------------------------------- launchers
 
 // Kernel families.
-enum : int { FAMILY_GENERAL = 0, FAMILY_ALIGNED = 1, FAMILY_STREAM = 2 };
+enum : int { FAMILY_GENERAL = 0, FAMILY_ALIGNED = 1, FAMILY_STREAM = 2, FAMILY_SPLIT = 3 };
 
 // TPR and NV values the library is built with.
 constexpr int kTprList[] = {4, 8, 16, 32, 64, 128, 256, 512, 1024};
@@ -1048,10 +1186,21 @@ hipError_t launch_tpr(const FwdParams* fp, const BwdParams* bp, int family, int 
 }
 
 // One launch: exactly one of fp / bp is non-null. The streaming family
-// ignores tpr / nv and takes one workgroup per row (blocks = rows).
+// ignores tpr / nv and takes one workgroup per row (blocks = rows); the split
+// family launches twice over a grid of chunks x rows (blocks = rows).
 template <class F>
 hipError_t launch(const FwdParams* fp, const BwdParams* bp, int family, int tpr, int nv,
                   uint32_t blocks, hipStream_t st) {
+  if (family == FAMILY_SPLIT) {
+    const dim3 grid(fp ? fp->chunks : bp->chunks, blocks), block(kSplitTpr);
+    if (fp) hipLaunchKernelGGL((sms_fwd_split_partial_kernel<F>), grid, block, 0, st, *fp);
+    else hipLaunchKernelGGL((sms_bwd_split_partial_kernel<F>), grid, block, 0, st, *bp);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (fp) hipLaunchKernelGGL((sms_fwd_split_final_kernel<F>), grid, block, 0, st, *fp);
+    else hipLaunchKernelGGL((sms_bwd_split_final_kernel<F>), grid, block, 0, st, *bp);
+    return hipGetLastError();
+  }
   if (family == FAMILY_STREAM) {
     if (fp)
       hipLaunchKernelGGL((sms_fwd_stream_kernel<F>), dim3(blocks), dim3(kStreamTpr), 0, st, *fp);

@@ -100,20 +100,50 @@ def causal_code(is_causal):
                      f"got {is_causal!r}")
 
 
-def _stream_handle(device, stream):
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    return s.cuda_stream
+def _stream_of(device, stream):
+    return stream if stream is not None else torch.cuda.current_stream(device)
 
 
-def sms_forward(x, mask, y, scale=1.0, is_causal=False, stream=None):
-    """y <- softmax(x*scale + mask) over the last axis (C ABI sms_forward).
+def sms_workspace_bytes(dtype, shape, backward=False):
+    """Workspace bytes sms_forward / sms_backward use for split rows (0: none)."""
+    B, H, Sq, Sk = shape
+    n = int(_lib.lib().sms_workspace_bytes(_lib.DTYPE_CODES[_DTYPES[dtype]], B, H, Sq, Sk,
+                                           int(backward)))
+    if n < 0:
+        raise ValueError(f"no workspace size for dtype {dtype} and shape {tuple(shape)}")
+    return n
+
+
+def _workspace(dtype, shape, backward, device, stream, workspace):
+    """(pointer, bytes) of the workspace for a call: the caller's tensor, or a
+    fresh one from torch's allocator on the launch stream when rows split."""
+    if workspace is not None:
+        _require_gpu(workspace, "workspace")
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        return workspace, workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    B, H, Sq, Sk = shape
+    need = int(_lib.lib().sms_workspace_bytes(_lib.DTYPE_CODES[_DTYPES[dtype]], B, H, Sq, Sk,
+                                              int(backward)))
+    if need <= 0:  # no split; invalid sizes are reported by the call itself
+        return None, None, 0
+    with torch.cuda.stream(stream):
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return ws, ws.data_ptr(), need
+
+
+def sms_forward(x, mask, y, scale=1.0, is_causal=False, stream=None, workspace=None):
+    """y <- softmax(x*scale + mask) over the last axis (C ABI sms_forward_ws).
 
     x, y: 4-D GPU tensors of one shape and dtype (float32/float16/bfloat16), key
     axis contiguous; y may be x itself (in place). mask: None; an additive mask
     of x's dtype; a boolean mask (torch.bool or uint8, nonzero = key excluded);
     both contiguous, in one of the shapes ``mask_mode_of`` accepts; or int32 key
     lengths of shape [B]. is_causal: see ``causal_code``. Enqueued on ``stream``
-    (default: the current stream); returns y.
+    (default: the current stream); returns y. Few long rows are split across
+    workgroups through a workspace: ``workspace`` (a GPU tensor of at least
+    ``sms_workspace_bytes`` bytes) or, by default, one taken from torch's
+    allocator on the launch stream.
     """
     _require_gpu(x, "x")
     _require_gpu(y, "y")
@@ -142,20 +172,23 @@ def sms_forward(x, mask, y, scale=1.0, is_causal=False, stream=None):
     B, H, Sq, Sk = x.shape
     L = _lib.lib()
     with torch.cuda.device(x.device):
-        st = L.sms_forward(x.data_ptr(), _strides(x), mptr, mode_code, y.data_ptr(),
-                           _strides(y), code, B, H, Sq, Sk, float(scale), causal_code(is_causal),
-                           _stream_handle(x.device, stream))
+        s = _stream_of(x.device, stream)
+        keep, wptr, wbytes = _workspace(x.dtype, x.shape, False, x.device, s, workspace)
+        st = L.sms_forward_ws(x.data_ptr(), _strides(x), mptr, mode_code, y.data_ptr(),
+                              _strides(y), code, B, H, Sq, Sk, float(scale),
+                              causal_code(is_causal), wptr, wbytes, s.cuda_stream)
+        del keep  # torch reuses the block only for later work on this stream, after the launch
     _lib.check("sms_forward", st)
     return y
 
 
-def sms_backward(y, dy, dx, scale=1.0, is_causal=False, stream=None):
-    """dx <- scale * y * (dy - sum_k dy_k y_k) row by row (C ABI sms_backward).
+def sms_backward(y, dy, dx, scale=1.0, is_causal=False, stream=None, workspace=None):
+    """dx <- scale * y * (dy - sum_k dy_k y_k) row by row (C ABI sms_backward_ws).
 
     y, dy, dx: 4-D GPU tensors of one shape and dtype, key axis contiguous; dx
     may be dy or y itself. A causal ``is_causal`` (see ``causal_code``) promises
     y == 0 at the keys that rule excludes (true for y from a forward with the
-    same rule); those keys are then skipped.
+    same rule); those keys are then skipped. ``workspace``: as for sms_forward.
     """
     for t, n in ((y, "y"), (dy, "dy"), (dx, "dx")):
         _require_gpu(t, n)
@@ -166,9 +199,12 @@ def sms_backward(y, dy, dx, scale=1.0, is_causal=False, stream=None):
     B, H, Sq, Sk = y.shape
     L = _lib.lib()
     with torch.cuda.device(y.device):
-        st = L.sms_backward(y.data_ptr(), _strides(y), dy.data_ptr(), _strides(dy), dx.data_ptr(),
-                            _strides(dx), code, B, H, Sq, Sk, float(scale),
-                            causal_code(is_causal), _stream_handle(y.device, stream))
+        s = _stream_of(y.device, stream)
+        keep, wptr, wbytes = _workspace(y.dtype, y.shape, True, y.device, s, workspace)
+        st = L.sms_backward_ws(y.data_ptr(), _strides(y), dy.data_ptr(), _strides(dy),
+                               dx.data_ptr(), _strides(dx), code, B, H, Sq, Sk, float(scale),
+                               causal_code(is_causal), wptr, wbytes, s.cuda_stream)
+        del keep
     _lib.check("sms_backward", st)
     return dx
 

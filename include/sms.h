@@ -32,7 +32,8 @@
  * Common rules for both entry points
  * ----------------------------------
  * - All tensor pointers are DEVICE pointers (memory of the current HIP device),
- *   owned by the caller. The library allocates nothing, keeps no state between
+ *   owned by the caller. The library allocates nothing (the split-row entry
+ *   points take their workspace from the caller), keeps no state between
  *   calls and never synchronises: work is enqueued on `stream` (a hipStream_t;
  *   NULL = the null stream) and the call returns before it runs.
  * - Strides are in ELEMENTS, for the axes (B, H, Sq, Sk) in that order. The key
@@ -58,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SMS_ABI_VERSION 2
+#define SMS_ABI_VERSION 3
 
 typedef enum {
   SMS_OK = 0,
@@ -69,7 +70,9 @@ typedef enum {
   SMS_ERR_MASK_MODE = 5, /* unknown mask mode                                     */
   SMS_ERR_ALIGN = 6,     /* a pointer not aligned to its element size             */
   SMS_ERR_HIP = 7,       /* the HIP runtime reported an error for the launch      */
-  SMS_ERR_CAUSAL = 8     /* unknown causal mode                                   */
+  SMS_ERR_CAUSAL = 8,    /* unknown causal mode                                   */
+  SMS_ERR_WORKSPACE = 9  /* workspace smaller than sms_workspace_bytes(), or not
+                            8-byte aligned                                       */
 } sms_status;
 
 typedef enum {
@@ -130,7 +133,8 @@ typedef enum {
  * Limits: B*H*Sq < 2^32 rows, Sk <= sms_max_sk(dtype) = 2^30, and at most
  * 2^32 - 1 work-items per launch (rows of more than 4096 16-byte vectors take
  * one 1024-lane workgroup each, so at most 4194303 such rows per call).
- * Longer rows cost a second read of the row (two passes).
+ * Longer rows cost a second read of the row (two passes). sms_forward never
+ * splits a row across workgroups (see sms_forward_ws).
  */
 sms_status sms_forward(const void* x, const int64_t x_strides[4],
                        const void* mask, int mask_mode,
@@ -159,6 +163,52 @@ sms_status sms_backward(const void* y, const int64_t y_strides[4],
                         void* dx, const int64_t dx_strides[4],
                         sms_dtype dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk,
                         float scale, int is_causal, void* stream);
+
+/*
+ * Split rows. When a call has too few rows to fill the GPU at one workgroup
+ * per row (fewer than 256) and its rows are long (at least 16384 16-byte
+ * vectors, 256 KB), each row is
+ * cut into chunks with a workgroup each, in two launches: per-chunk partial
+ * results -- (running max, sum of exponentials) forward, the partial dot
+ * product backward -- go to a caller-provided workspace, and the second launch
+ * merges a row's partials (the online-softmax merge of two (max, sum) pairs,
+ * 0539edu.com notes, fused-attention section, where a row shared by several
+ * blocks needs their statistics combined) and writes its chunk, re-reading
+ * the chunk's inputs. The pnsm.cn ScaledMaskSoftmax article, sec. 2.2, cuts
+ * rows beyond 4096 keys into blocks for the same reason of size.
+ *
+ * sms_workspace_bytes -- bytes of device workspace a call of sms_forward_ws
+ * (backward = 0) or sms_backward_ws (backward = 1) with these sizes may use:
+ * 0 when it would not split rows (any workspace, NULL included, is then
+ * ignored), -1 for invalid sizes or dtype. It depends only on the arguments
+ * and on the SMS_SPLIT / SMS_FORCE_SPLIT environment overrides; 8 bytes per
+ * (row, chunk), a few KB to tens of KB in practice.
+ */
+int64_t sms_workspace_bytes(sms_dtype dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk,
+                            int backward);
+
+/*
+ * sms_forward_ws / sms_backward_ws -- sms_forward / sms_backward with a
+ * workspace (device memory owned by the caller, 8-byte aligned, of
+ * `workspace_bytes` bytes, not shared with any call that may run at the same
+ * time). With workspace == NULL they are exactly sms_forward / sms_backward.
+ * Otherwise, if sms_workspace_bytes() > 0, rows are split as described above
+ * and workspace_bytes must be at least that (else SMS_ERR_WORKSPACE, nothing
+ * launched). The workspace holds no state between calls: its contents on entry
+ * do not matter and are garbage on exit.
+ */
+sms_status sms_forward_ws(const void* x, const int64_t x_strides[4],
+                          const void* mask, int mask_mode,
+                          void* y, const int64_t y_strides[4],
+                          sms_dtype dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk,
+                          float scale, int is_causal, void* workspace, int64_t workspace_bytes,
+                          void* stream);
+sms_status sms_backward_ws(const void* y, const int64_t y_strides[4],
+                           const void* dy, const int64_t dy_strides[4],
+                           void* dx, const int64_t dx_strides[4],
+                           sms_dtype dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk,
+                           float scale, int is_causal, void* workspace, int64_t workspace_bytes,
+                           void* stream);
 
 /* Largest key length Sk the library runs for `dtype` (2^30; 0 for an unknown
  * dtype). */

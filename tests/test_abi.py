@@ -107,6 +107,47 @@ def test_backward_argument_checks(L):
     assert L.sms_backward(FAKE, s, FAKE, s, FAKE, s, 0, 1, 1, 1, 64, 1.0, 4, None) == 8
 
 
+def test_workspace_sizes(L, monkeypatch):
+    """8 bytes per (row, chunk); chunks = min(ceil(2048 / rows), vectors // 1024)
+    for fewer than 256 rows of at least 16384 vectors, else no split (0); -1 for
+    invalid arguments."""
+    monkeypatch.delenv("SMS_FORCE_SPLIT", raising=False)
+    monkeypatch.delenv("SMS_SPLIT", raising=False)
+    ws = L.sms_workspace_bytes
+    # fp16, 8 rows of 2^20 keys: unaligned rows span (2^20 + 14) // 8 = 131073
+    # vectors -> min(256, 128) = 128 chunks
+    assert ws(1, 1, 1, 8, 1 << 20, 0) == 8 * 128 * 8
+    assert ws(1, 1, 1, 8, 1 << 20, 1) == 8 * 128 * 8
+    assert ws(0, 1, 2, 1, 1 << 16, 0) == 2 * 16 * 8       # fp32: 16385 vectors -> 16 chunks
+    assert ws(0, 1, 1, 255, 1 << 16, 0) == 255 * 9 * 8     # 255 rows -> 9 chunks
+    assert ws(0, 1, 1, 256, 1 << 16, 0) == 0               # 256 rows: one workgroup each
+    assert ws(1, 1, 1, 4, 1024, 0) == 0                    # 129 vectors: short rows
+    assert ws(1, 1, 1, 1, 16383 * 8 - 14, 0) == 0          # 16382 vectors: short rows
+    assert ws(1, 1, 1, 1, 16384 * 8 - 14, 0) == 16 * 8     # 16384 vectors: 16 chunks
+    assert ws(1, 0, 1, 1, 1 << 20, 0) == 0                 # empty
+    assert ws(7, 1, 1, 1, 64, 0) == -1 and ws(0, -1, 1, 1, 64, 0) == -1
+    assert ws(0, 1, 1, 1, (1 << 30) + 1, 0) == -1
+    monkeypatch.setenv("SMS_FORCE_SPLIT", "3")
+    assert ws(0, 2, 3, 4, 100, 0) == 24 * 3 * 8            # forced: any shape
+    monkeypatch.setenv("SMS_FORCE_SPLIT", "0")
+    monkeypatch.setenv("SMS_SPLIT", "0")
+    assert ws(1, 1, 1, 8, 1 << 20, 0) == 0
+
+
+@no_device
+def test_workspace_argument_checks(L):
+    s = _lib.strides4((1 << 20, 1 << 20, 1 << 20, 1))
+    need = L.sms_workspace_bytes(1, 1, 1, 8, 1 << 20, 0)
+    args = (FAKE, s, None, 0, FAKE, s, 1, 1, 1, 8, 1 << 20, 1.0, 0)
+    assert L.sms_forward_ws(*args, FAKE, need - 1, None) == 9     # too small
+    assert L.sms_forward_ws(*args, FAKE + 4, need, None) == 9     # not 8-byte aligned
+    bargs = (FAKE, s, FAKE, s, FAKE, s, 1, 1, 1, 8, 1 << 20, 1.0, 0)
+    assert L.sms_backward_ws(*bargs, FAKE, 8, None) == 9
+    # argument errors are still reported first
+    assert L.sms_forward_ws(FAKE, s, None, 0, None, s, 1, 1, 1, 8, 1 << 20, 1.0, 0, FAKE, 8,
+                            None) == 1
+
+
 def test_max_sk_and_paths(L):
     assert L.sms_max_sk(0) == L.sms_max_sk(1) == L.sms_max_sk(2) == 1 << 30
     assert L.sms_max_sk(5) == 0

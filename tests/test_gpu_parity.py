@@ -17,7 +17,7 @@ import torch
 
 import oracle
 from attention_softmax_amd import (SmsError, scaled_mask_softmax, sms_backward, sms_forward,
-                                   sms_max_sk)
+                                   sms_max_sk, sms_workspace_bytes)
 from attention_softmax_amd.workloads import (CONFIGS, TORCH_DTYPE, draw_dy, draw_lengths,
                                              draw_mask, draw_x, make_config)
 from tests.parity import (compare, decoded, gather_mask_rows, gather_rows, mask_4d,
@@ -513,11 +513,18 @@ def test_streaming_kernels_on_short_rows(dtype, Sk, monkeypatch):
     ("f16", 40000, "b_sq_sk", "additive"),
     ("bf16", 100003, "full", "additive"),   # odd length: unaligned rows, element head/tail
     ("bf16", 50001, "key_lengths", "lengths"),
+    ("f16", 140001, "b_sq_sk", "bool"),       # rows of >= 16384 vectors: split when auto
+    ("bf16", 262147, "key_lengths", "lengths"),
+    ("f32", 65537, "full", "additive"),
 ])
-def test_long_rows(dtype, Sk, mode, kind):
-    """Rows beyond one workgroup's registers take the streaming kernels; every
-    row against the oracle, for no causal rule and both alignments."""
-    say(f"long rows dtype={dtype} Sk={Sk} mode={mode} kind={kind}")
+@pytest.mark.parametrize("split", ["auto", "off"])
+def test_long_rows(dtype, Sk, mode, kind, split, monkeypatch):
+    """Rows beyond one workgroup's registers: eight of them are split across
+    workgroups (through a workspace) or, with splitting off, take the streaming
+    kernels; every row against the oracle, every causal rule, both alignments."""
+    if split == "off":
+        monkeypatch.setenv("SMS_SPLIT", "0")
+    say(f"long rows dtype={dtype} Sk={Sk} mode={mode} kind={kind} split={split}")
     shape = (1, 2, 4, Sk)
     x = draw_x(shape, dtype, ("normal", 4.0), Sk, DEV)
     if kind == "lengths":
@@ -527,6 +534,59 @@ def test_long_rows(dtype, Sk, mode, kind):
     for causal in CAUSALS:
         check_fwd_bwd(x, mask, mode, kind, 0.25, causal, f"long causal={causal}",
                       dy_seed=Sk + 2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("Sk", [7, 77, 1001, 4097])
+@pytest.mark.parametrize("chunks", [2, 7])
+def test_split_forced_on_short_rows(dtype, Sk, chunks, monkeypatch):
+    """The split kernels forced onto short rows with chunk boundaries at odd
+    vectors (including chunks wholly past a causal bound or beyond the row):
+    every mask shape and kind, every causal rule, against the oracle."""
+    monkeypatch.setenv("SMS_FORCE_SPLIT", str(chunks))
+    say(f"split forced dtype={dtype} Sk={Sk} chunks={chunks}")
+    for mode, kind in MASK_CASES:
+        for causal in CAUSALS:
+            shape = (2, 2, 3, Sk)
+            seed = zlib.crc32(f"p/{dtype}/{Sk}/{chunks}/{mode}/{kind}/{causal}".encode()) % 10000
+            x = draw_x(shape, dtype, ("normal", 3.0), seed, DEV)
+            mask = make_mask(shape, mode, kind, dtype, seed + 1)
+            check_fwd_bwd(x, mask, mode, kind, 0.3, causal,
+                          f"split {dtype} Sk={Sk} C={chunks} {mode}/{kind} causal={causal}",
+                          dy_seed=seed + 2)
+
+
+@pytest.mark.parametrize("dtype,Sk", [("f16", 200003), ("f32", 65536)])
+def test_split_rows_in_place_deterministic_workspace(dtype, Sk):
+    """Split rows: in place (y = x, dx = dy) equals out of place, two runs are
+    bitwise equal, a caller workspace equals the default one, a short workspace
+    is an error, and the result matches the streaming kernels within tolerance."""
+    say(f"split properties dtype={dtype} Sk={Sk}")
+    shape = (1, 1, 3, Sk)
+    td = TORCH_DTYPE[dtype]
+    assert sms_workspace_bytes(td, shape) > 0
+    x = draw_x(shape, dtype, ("normal", 4.0), 21, DEV)
+    dy = draw_dy(shape, dtype, 22, DEV)
+    y = fwd(x, None, 0.5, "bottom_right")
+    dx = bwd(y, dy, 0.5, "bottom_right")
+    assert torch.equal(fwd(x, None, 0.5, "bottom_right"), y)
+    assert torch.equal(bwd(y, dy, 0.5, "bottom_right"), dx)
+    xi = x.clone()
+    sms_forward(xi, None, xi, 0.5, "bottom_right")
+    dyi = dy.clone()
+    sms_backward(y, dyi, dyi, 0.5, "bottom_right")
+    torch.cuda.synchronize()
+    assert torch.equal(xi, y) and torch.equal(dyi, dx)
+    ws = torch.empty(sms_workspace_bytes(td, shape), dtype=torch.uint8, device=DEV)
+    yw = torch.empty_like(x)
+    sms_forward(x, None, yw, 0.5, "bottom_right", workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(yw, y)
+    with pytest.raises(SmsError, match="WORKSPACE"):
+        sms_forward(x, None, yw, 0.5, "bottom_right", workspace=ws[:8])
+    compare(decoded(y), oracle_fwd(x, None, "none", 0.5, "bottom_right"), dtype, "split fwd",
+            rowsum=True)
+    compare(decoded(dx), oracle.backward(to_np(y), to_np(dy), dtype, 0.5), dtype, "split bwd")
 
 
 @pytest.mark.parametrize("moff", [1, 3, 5])
