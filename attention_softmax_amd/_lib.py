@@ -20,7 +20,7 @@ SMS_OK = 0
 STATUS_NAMES = {0: "SMS_OK", 1: "SMS_ERR_NULL", 2: "SMS_ERR_SHAPE", 3: "SMS_ERR_STRIDE",
                 4: "SMS_ERR_DTYPE", 5: "SMS_ERR_MASK_MODE", 6: "SMS_ERR_ALIGN", 7: "SMS_ERR_HIP",
                 8: "SMS_ERR_CAUSAL", 9: "SMS_ERR_WORKSPACE"}
-DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "f64": 3}
 MASK_MODES = {"none": 0, "sq_sk": 1, "b_sq_sk": 2, "b_1_sk": 3, "full": 4, "key_lengths": 5}
 MASK_BOOL = 0x10
 CAUSAL_CODES = {"none": 0, "top_left": 1, "bottom_right": 2}

@@ -47,6 +47,7 @@ int dtype_bytes(sms_dtype d) {
     case SMS_F32: return 4;
     case SMS_F16: return 2;
     case SMS_BF16: return 2;
+    case SMS_F64: return 8;
     default: return 0;
   }
 }
@@ -227,6 +228,7 @@ void fill_geom(RowGeom& g, int64_t B, int64_t H, int64_t Sq, int64_t Sk) {
 
 hipError_t launch(sms_dtype dtype, const FwdParams* fp, const BwdParams* bp, const Plan& pl,
                   uint32_t blocks, hipStream_t s) {
+  if (pl.family == sms::FAMILY_F64) return sms_launch_f64(fp, bp, pl.tpr, blocks, s);
   switch (dtype) {
     case SMS_F32: return sms_launch_f32(fp, bp, pl.family, pl.tpr, pl.nv, blocks, s);
     case SMS_F16: return sms_launch_f16(fp, bp, pl.family, pl.tpr, pl.nv, blocks, s);
@@ -261,6 +263,7 @@ int64_t sms_max_sk(sms_dtype dtype) { return dtype_bytes(dtype) ? kMaxSk : 0; }
 int sms_path(sms_dtype dtype, int64_t Sk, int backward) {
   const int bytes = dtype_bytes(dtype);
   if (!bytes || Sk < 0 || Sk > kMaxSk) return -1;
+  if (dtype == SMS_F64) return 4;
   Plan pl;
   if (!choose_plan(vectors_per_row(Sk, 16 / bytes, true), backward != 0, false, pl)) return -1;
   if (pl.family == sms::FAMILY_STREAM) return 3;
@@ -274,6 +277,7 @@ int64_t sms_workspace_bytes(sms_dtype dtype, int64_t B, int64_t H, int64_t Sq, i
   if (!bytes || B < 0 || H < 0 || Sq < 0 || Sk < 0) return -1;
   if (B == 0 || H == 0 || Sq == 0 || Sk == 0) return 0;
   if (check_sizes(B, H, Sq, Sk) != SMS_OK) return -1;
+  if (dtype == SMS_F64) return 0;  // the fp64 kernels never split rows
   return workspace_bytes(B * H * Sq, Sk, 16 / bytes);
 }
 
@@ -310,14 +314,20 @@ sms_status sms_forward_ws(const void* x, const int64_t x_strides[4], const void*
       (has_mask && !aligned_to(mask, mask_bytes)))
     return SMS_ERR_ALIGN;
   const int E = 16 / bytes;
-  const int64_t need = workspace ? workspace_bytes(B * H * Sq, Sk, E) : 0;
+  const bool f64 = dtype == SMS_F64;
+  const int64_t need = workspace && !f64 ? workspace_bytes(B * H * Sq, Sk, E) : 0;
   if (need > 0 && (workspace_bytes_given < need || !aligned_to(workspace, 8)))
     return SMS_ERR_WORKSPACE;
 
   const bool aligned = rows_aligned16(x, x_strides, B, H, Sq, bytes);
   const int64_t nvec = vectors_per_row(Sk, E, aligned);
   Plan pl;
-  if (!choose_plan(nvec, false, is_causal != 0, pl)) return SMS_ERR_SHAPE;
+  if (f64) {
+    pl.family = sms::FAMILY_F64;
+    pl.tpr = sms::f64_tpr(Sk);
+  } else if (!choose_plan(nvec, false, is_causal != 0, pl)) {
+    return SMS_ERR_SHAPE;
+  }
   const int64_t chunks = need > 0 ? split_chunks(B * H * Sq, nvec) : 1;
   if (chunks > 1) split_shape(nvec, chunks, pl);
 
@@ -347,7 +357,7 @@ sms_status sms_forward_ws(const void* x, const int64_t x_strides[4], const void*
   p.chunk_vec = (uint32_t)pl.chunk_vec;
   p.ws = static_cast<float2*>(workspace);
 
-  if (pl.family != sms::FAMILY_STREAM && pl.family != sms::FAMILY_SPLIT) {
+  if (pl.family != sms::FAMILY_STREAM && pl.family != sms::FAMILY_SPLIT && !f64) {
     // Aligned-row kernels: every operand's rows on 16-byte lines, whole vectors.
     const bool mask_whole = !has_mask || p.mask_kind == sms::MASK_LEN ||
                             (p.mask_kind == sms::MASK_ADD && ((uintptr_t)mask & 15) == 0) ||
@@ -389,14 +399,20 @@ sms_status sms_backward_ws(const void* y, const int64_t y_strides[4], const void
   if (!aligned_to(y, bytes) || !aligned_to(dy, bytes) || !aligned_to(dx, bytes))
     return SMS_ERR_ALIGN;
   const int E = 16 / bytes;
-  const int64_t need = workspace ? workspace_bytes(B * H * Sq, Sk, E) : 0;
+  const bool f64 = dtype == SMS_F64;
+  const int64_t need = workspace && !f64 ? workspace_bytes(B * H * Sq, Sk, E) : 0;
   if (need > 0 && (workspace_bytes_given < need || !aligned_to(workspace, 8)))
     return SMS_ERR_WORKSPACE;
 
   const bool aligned = rows_aligned16(y, y_strides, B, H, Sq, bytes);
   const int64_t nvec = vectors_per_row(Sk, E, aligned);
   Plan pl;
-  if (!choose_plan(nvec, true, is_causal != 0, pl)) return SMS_ERR_SHAPE;
+  if (f64) {
+    pl.family = sms::FAMILY_F64;
+    pl.tpr = sms::f64_tpr(Sk);
+  } else if (!choose_plan(nvec, true, is_causal != 0, pl)) {
+    return SMS_ERR_SHAPE;
+  }
   const int64_t chunks = need > 0 ? split_chunks(B * H * Sq, nvec) : 1;
   if (chunks > 1) split_shape(nvec, chunks, pl);
 
@@ -417,7 +433,7 @@ sms_status sms_backward_ws(const void* y, const int64_t y_strides[4], const void
   p.chunk_vec = (uint32_t)pl.chunk_vec;
   p.ws = static_cast<double*>(workspace);
 
-  if (pl.family != sms::FAMILY_STREAM && pl.family != sms::FAMILY_SPLIT &&
+  if (pl.family != sms::FAMILY_STREAM && pl.family != sms::FAMILY_SPLIT && !f64 &&
       ((Sk * bytes) & 15) == 0 &&
       env_int("SMS_FAST", 1) != 0 && aligned &&
       rows_aligned16(dy, dy_strides, B, H, Sq, bytes) &&

@@ -200,6 +200,7 @@ SMS_DEV void swap_pair(double v, double& a, double& b) {
 
 struct OpMax {
   SMS_DEV float operator()(float a, float b) const { return fmaxf(a, b); }
+  SMS_DEV double operator()(double a, double b) const { return fmax(a, b); }
 };
 struct OpAdd {
   template <class T>
@@ -1141,10 +1142,119 @@ __global__ void __launch_bounds__(kSplitTpr) sms_bwd_split_final_kernel(BwdParam
   write_grads<F, kSplitTpr>(r, p.scale, dot, v0, v1, Sk);
 }
 
+// ------------------------------------------------------- double precision
+//
+// fp64 inputs are computed in fp64 throughout (the lmnt.cn page's wrapper
+// dispatches float, double and half; widening double to fp32 would lose the
+// precision the caller asked for). One kernel pair for every row length and
+// alignment: TPR lanes per row, lane k takes keys k, k + TPR, ...: 8-byte
+// loads and stores, coalesced across the wavefront. Forward: pass 1 keeps a
+// per-lane running (max, sum of exp(s - max)), merged across the row; pass 2
+// reads the row again and writes exp(s - M) / L (fp64 exp from the device math
+// library). Backward: pass 1 the fp64 dot product, pass 2 dx.
+
+struct Fp64 {  // row geometry only (fwd_row / bwd_row)
+  static constexpr int kBytes = 8;
+  static constexpr int kE = 2;
+};
+
+constexpr double kNegInfD = -__builtin_inf();
+
+// Score of key k < kload of a row: x*scale (+ additive mask), -inf if excluded.
+SMS_DEV double score_f64(const FwdRow& r, int kind, double scale, int k, bool nt) {
+  const double* xp = reinterpret_cast<const double*>(r.x) + k;
+  const double xv = nt ? __builtin_nontemporal_load(xp) : *xp;
+  if (kind == MASK_ADD) return fma(xv, scale, reinterpret_cast<const double*>(r.m)[k]);
+  if (kind == MASK_BOOL && r.m[k] != 0) return kNegInfD;
+  return xv * scale;
+}
+
+template <int TPR>
+__global__ void __launch_bounds__(block_of(TPR)) sms_fwd_f64_kernel(FwdParams p) {
+  constexpr int RPB = block_of(TPR) / TPR;
+  __shared__ double red[2][TPR > 64 ? TPR / 64 : 1];
+  const int lane = (int)(threadIdx.x % TPR);
+  const FwdRow r = fwd_row<Fp64, RPB>(p, blockIdx.x, local_row<TPR>());
+  if (!r.valid) return;  // only a tail group of a TPR <= 64 launch, which has no barrier
+  const int Sk = (int)p.g.Sk;
+  const int kind = p.mask_kind;
+  const double scale = p.scale;
+  double m = kNegInfD, l = 0.0;
+  for (int k = lane; k < r.kload; k += TPR) {
+    const double s = score_f64(r, kind, scale, k, false);
+    if (s > m) {
+      l = (m == kNegInfD) ? 0.0 : l * exp(m - s);
+      m = s;
+    }
+    if (s != kNegInfD) l += exp(s - m);
+  }
+  const double M = row_reduce<TPR>(m, OpMax(), red[0]);
+  const double mine = (m == kNegInfD) ? 0.0 : l * exp(m - M);
+  const double L = row_reduce<TPR>(mine, OpAdd(), red[1]);
+  const double inv = L > 0.0 ? 1.0 / L : 0.0;  // fully masked row -> zeros
+  double* yp = reinterpret_cast<double*>(r.y);
+  for (int k = lane; k < Sk; k += TPR) {
+    double o = 0.0;
+    if (k < r.kload && inv != 0.0) o = exp(score_f64(r, kind, scale, k, true) - M) * inv;
+    __builtin_nontemporal_store(o, yp + k);
+  }
+}
+
+template <int TPR>
+__global__ void __launch_bounds__(block_of(TPR)) sms_bwd_f64_kernel(BwdParams p) {
+  constexpr int RPB = block_of(TPR) / TPR;
+  __shared__ double red[TPR > 64 ? TPR / 64 : 1];
+  const int lane = (int)(threadIdx.x % TPR);
+  const BwdRow r = bwd_row<Fp64, RPB>(p, blockIdx.x, local_row<TPR>());
+  if (!r.valid) return;
+  const int Sk = (int)p.g.Sk;
+  const double* yp = reinterpret_cast<const double*>(r.y);
+  const double* dp = reinterpret_cast<const double*>(r.d);
+  double acc = 0.0;
+  for (int k = lane; k < r.kload; k += TPR) acc = fma(yp[k], dp[k], acc);
+  const double dot = row_reduce<TPR>(acc, OpAdd(), red);
+  const double scale = p.scale;
+  double* xp = reinterpret_cast<double*>(r.x);
+  for (int k = lane; k < Sk; k += TPR) {
+    double o = 0.0;
+    if (k < r.kload) {
+      const double yv = __builtin_nontemporal_load(yp + k);
+      const double dv = __builtin_nontemporal_load(dp + k);
+      o = (yv * scale) * (dv - dot);
+    }
+    __builtin_nontemporal_store(o, xp + k);
+  }
+}
+
+// Lanes per fp64 row: one wavefront for rows up to 256 keys (four rows per
+// workgroup), else 256.
+constexpr int f64_tpr(int64_t Sk) { return Sk <= 256 ? 64 : 256; }
+
+inline hipError_t launch_f64(const FwdParams* fp, const BwdParams* bp, int tpr, uint32_t blocks,
+                             hipStream_t st) {
+  const dim3 grid(blocks), block(256);
+  if (tpr == 64) {
+    if (fp) hipLaunchKernelGGL((sms_fwd_f64_kernel<64>), grid, block, 0, st, *fp);
+    else hipLaunchKernelGGL((sms_bwd_f64_kernel<64>), grid, block, 0, st, *bp);
+  } else if (tpr == 256) {
+    if (fp) hipLaunchKernelGGL((sms_fwd_f64_kernel<256>), grid, block, 0, st, *fp);
+    else hipLaunchKernelGGL((sms_bwd_f64_kernel<256>), grid, block, 0, st, *bp);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 // --------------------------------------------------------------- launchers
 
 // Kernel families.
-enum : int { FAMILY_GENERAL = 0, FAMILY_ALIGNED = 1, FAMILY_STREAM = 2, FAMILY_SPLIT = 3 };
+enum : int {
+  FAMILY_GENERAL = 0,
+  FAMILY_ALIGNED = 1,
+  FAMILY_STREAM = 2,
+  FAMILY_SPLIT = 3,
+  FAMILY_F64 = 4
+};
 
 // TPR and NV values the library is built with.
 constexpr int kTprList[] = {4, 8, 16, 32, 64, 128, 256, 512, 1024};
@@ -1231,3 +1341,5 @@ hipError_t sms_launch_f16(const sms::FwdParams*, const sms::BwdParams*, int fami
                           int nv, uint32_t blocks, hipStream_t);
 hipError_t sms_launch_bf16(const sms::FwdParams*, const sms::BwdParams*, int family, int tpr,
                            int nv, uint32_t blocks, hipStream_t);
+hipError_t sms_launch_f64(const sms::FwdParams*, const sms::BwdParams*, int tpr, uint32_t blocks,
+                          hipStream_t);

@@ -10,14 +10,16 @@ import torch
 
 from . import _lib
 
-_DTYPES = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+_DTYPES = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16",
+           torch.float64: "f64"}
 
 
 def _dtype_code(t, what):
     try:
         return _lib.DTYPE_CODES[_DTYPES[t.dtype]]
     except KeyError:
-        raise TypeError(f"{what}: dtype {t.dtype} is not float32, float16 or bfloat16") from None
+        raise TypeError(
+            f"{what}: dtype {t.dtype} is not float32, float16, bfloat16 or float64") from None
 
 
 def _require_gpu(t, what):

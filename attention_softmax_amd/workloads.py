@@ -15,14 +15,15 @@ tensor of the pnsm.cn ScaledMaskSoftmax article, sec. 1.3), bf16
 
 Distributions: N(mu, sigma^2) notation, so "N(0,4)" has sigma = 2. Random
 values are drawn in fp32 and rounded to the working dtype by round-to-nearest-
-even (torch's ``Tensor.to``). Mask positions are independent Bernoulli draws.
+even (torch's ``Tensor.to``); fp64 tensors are drawn in fp64. Mask positions are independent Bernoulli draws.
 """
 
 import math
 
 import torch
 
-TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+               "f64": torch.float64}
 
 # Mask broadcast modes, named by the mask's own shape.
 MASK_SHAPES = {
@@ -62,15 +63,17 @@ def _gen(seed, device):
 
 
 def draw_x(shape, dtype, dist, seed, device):
-    """x drawn in fp32 from ``dist`` then rounded to ``dtype``."""
+    """x drawn in fp32 (fp64 for an fp64 ``dtype``) from ``dist``, then rounded
+    to ``dtype``."""
     g = _gen(seed, device)
     kind, p = dist
+    draw_dt = torch.float64 if dtype == "f64" else torch.float32
     if kind == "normal":
-        v = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        v = torch.randn(shape, generator=g, device=device, dtype=draw_dt)
         if p != 1.0:
             v.mul_(p)
     elif kind == "uniform":
-        v = torch.rand(shape, generator=g, device=device, dtype=torch.float32)
+        v = torch.rand(shape, generator=g, device=device, dtype=draw_dt)
         v.mul_(2.0 * p).sub_(p)
     else:
         raise ValueError(kind)

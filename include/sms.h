@@ -24,10 +24,12 @@
  *
  * which needs only the forward's output y, the upstream gradient dy and scale.
  *
- * Arithmetic: inputs of every dtype are widened to fp32; the row maximum, the
- * exponentials, the normaliser and the normalisation are fp32; the backward's
- * row dot product is accumulated in fp64. Outputs are rounded to the I/O dtype
- * with round-to-nearest-even, keeping subnormals.
+ * Arithmetic: fp32, fp16 and bf16 inputs are widened to fp32; the row maximum,
+ * the exponentials, the normaliser and the normalisation are fp32; the
+ * backward's row dot product is accumulated in fp64. Outputs are rounded to the
+ * I/O dtype with round-to-nearest-even, keeping subnormals. fp64 inputs (the
+ * lmnt.cn page's wrapper dispatches float, double and half, sec. 4.2) are
+ * computed in fp64 throughout; `scale` is still a 32-bit float.
  *
  * Common rules for both entry points
  * ----------------------------------
@@ -78,7 +80,8 @@ typedef enum {
 typedef enum {
   SMS_F32 = 0,  /* IEEE binary32                                */
   SMS_F16 = 1,  /* IEEE binary16                                */
-  SMS_BF16 = 2  /* bfloat16 (upper 16 bits of a binary32 value) */
+  SMS_BF16 = 2, /* bfloat16 (upper 16 bits of a binary32 value) */
+  SMS_F64 = 3   /* IEEE binary64, computed in binary64          */
 } sms_dtype;
 
 /* The mask's own shape; the mask is contiguous (row-major) in that shape and
@@ -180,7 +183,8 @@ sms_status sms_backward(const void* y, const int64_t y_strides[4],
  * sms_workspace_bytes -- bytes of device workspace a call of sms_forward_ws
  * (backward = 0) or sms_backward_ws (backward = 1) with these sizes may use:
  * 0 when it would not split rows (any workspace, NULL included, is then
- * ignored), -1 for invalid sizes or dtype. It depends only on the arguments
+ * ignored; always 0 for SMS_F64, whose kernels never split rows), -1 for
+ * invalid sizes or dtype. It depends only on the arguments
  * and on the SMS_SPLIT / SMS_FORCE_SPLIT environment overrides; 8 bytes per
  * (row, chunk), a few KB to tens of KB in practice.
  */
@@ -219,7 +223,8 @@ int64_t sms_max_sk(sms_dtype dtype);
  * 0 = several rows per wavefront, 1 = one wavefront per row, 2 = several
  * wavefronts per row (LDS cross-wave reduction), 3 = streaming (one 1024-lane
  * workgroup per row, two passes: online max/sum, then normalise; for rows of
- * more than 4096 16-byte vectors). -1 for an unsupported size or dtype.
+ * more than 4096 16-byte vectors), 4 = the fp64 kernels (two passes, one
+ * wavefront or 256 lanes per row). -1 for an unsupported size or dtype.
  * `backward` selects the backward's choice. Host-only; launches nothing. */
 int sms_path(sms_dtype dtype, int64_t Sk, int backward);
 

@@ -6,9 +6,11 @@ purpose: one row at a time, the definition written out, no blocking or fusion.
 Conventions
 -----------
 * ``x`` has shape [B, H, Sq, Sk]; softmax runs over the last axis (keys).
-* Typed inputs are numpy arrays: ``float32`` for fp32, ``float16`` for fp16 and
-  ``uint16`` holding the raw bit patterns for bf16 (numpy has no bfloat16).
-  The ``dtype`` argument ("f32", "f16", "bf16") says which.
+* Typed inputs are numpy arrays: ``float32`` for fp32, ``float16`` for fp16,
+  ``float64`` for fp64 and ``uint16`` holding the raw bit patterns for bf16
+  (numpy has no bfloat16). The ``dtype`` argument ("f32", "f16", "bf16",
+  "f64") says which. Every value converts to float64 exactly; for fp64 inputs
+  the oracle computes at the inputs' own precision.
 * ``mask`` is ``None`` or a 4-D array whose every axis has the length of the
   matching axis of ``x`` or length 1 (length 1 = broadcast over that axis).
   It holds additive values (0 keeps, a large negative value or -inf masks),
@@ -33,7 +35,7 @@ import math
 
 import numpy as np
 
-DTYPES = ("f32", "f16", "bf16")
+DTYPES = ("f32", "f16", "bf16", "f64")
 
 
 def decode(a, dtype):
@@ -46,6 +48,10 @@ def decode(a, dtype):
     if dtype == "f16":
         if a.dtype != np.float16:
             raise TypeError("f16 data must be a float16 array")
+        return a.astype(np.float64)
+    if dtype == "f64":
+        if a.dtype != np.float64:
+            raise TypeError("f64 data must be a float64 array")
         return a.astype(np.float64)
     if dtype == "bf16":
         if a.dtype != np.uint16:

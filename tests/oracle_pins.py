@@ -235,6 +235,22 @@ def pin_decode():
     bits = (v.view(np.uint32) >> 16).astype(np.uint16)
     _close(S.forward_row(bits, "bf16", scale=0.9), S.forward_row(v, "f32", scale=0.9),
            rtol=0, what="bf16 vs f32")
+    # fp64 values pass through unchanged, including those no fp32 holds
+    d = np.array([0.1, 1.0 + 2.0 ** -52, -2.0 ** -1074, 1e300], np.float64)
+    assert S.decode(d, "f64").tolist() == d.tolist()
+    # the fp64 path is the same definition: the logistic closed form on a pair
+    # of scores fp32 cannot hold, and equality with the f32 path where it can
+    a, b = 0.1, 0.3
+    y = S.forward_row(np.array([a, b]), "f64", scale=1.0)
+    _close(y, [1 / (1 + math.exp(b - a)), 1 / (1 + math.exp(a - b))], rtol=1e-15, what="f64 pair")
+    _close(S.forward_row(v.astype(np.float64), "f64", scale=0.9),
+           S.forward_row(v, "f32", scale=0.9), rtol=0, what="f64 vs f32")
+    try:
+        S.decode(np.zeros(2, F32), "f64")
+    except TypeError:
+        pass
+    else:
+        raise AssertionError("f64 decode must reject float32 data")
 
 
 def pin_scale_rounding():

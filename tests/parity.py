@@ -10,7 +10,8 @@ import torch
 import oracle
 from tests.tolerance import F32_ABS, F32_ROWSUM, ULPS, compare, ulp  # noqa: F401
 
-DTYPE_OF = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+DTYPE_OF = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16",
+            torch.float64: "f64"}
 
 
 def to_np(t):

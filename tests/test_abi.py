@@ -98,13 +98,25 @@ def test_zero_sizes_are_noops(L):
 
 @no_device
 def test_backward_argument_checks(L):
-    assert _bwd(L, dtype=3) == 4
+    assert _bwd(L, dtype=9) == 4
     assert _bwd(L, dy=None) == 1 and _bwd(L, dx=None) == 1
     assert _bwd(L, st=(64, 64, 64, 0)) == 3
     assert _bwd(L, dx=FAKE_ODD) == 6
     assert _bwd(L, Sk=L.sms_max_sk(2) + 1, dtype=2) == 2
     s = _lib.strides4((64, 64, 64, 1))
     assert L.sms_backward(FAKE, s, FAKE, s, FAKE, s, 0, 1, 1, 1, 64, 1.0, 4, None) == 8
+
+
+def test_f64_queries(L):
+    assert L.sms_max_sk(3) == 1 << 30
+    assert L.sms_path(3, 1000, 0) == 4 and L.sms_path(3, 1 << 20, 1) == 4
+    assert L.sms_workspace_bytes(3, 1, 1, 8, 1 << 20, 0) == 0   # fp64 rows never split
+
+
+@no_device
+def test_f64_alignment(L):
+    assert _fwd(L, dtype=3, x=FAKE + 4) == 6                   # fp64 needs 8-byte alignment
+    assert _bwd(L, dtype=3, dy=FAKE + 4) == 6
 
 
 def test_workspace_sizes(L, monkeypatch):

@@ -20,7 +20,7 @@ from attention_softmax_amd import (SmsError, scaled_mask_softmax, sms_backward, 
                                    sms_max_sk, sms_workspace_bytes)
 from attention_softmax_amd.workloads import (CONFIGS, TORCH_DTYPE, draw_dy, draw_lengths,
                                              draw_mask, draw_x, make_config)
-from tests.parity import (compare, decoded, gather_mask_rows, gather_rows, mask_4d,
+from tests.parity import (DTYPE_OF, compare, decoded, gather_mask_rows, gather_rows, mask_4d,
                           sample_rows, to_np)
 
 pytestmark = pytest.mark.gpu
@@ -47,14 +47,14 @@ def bwd(y, dy, scale=1.0, causal=False, dx=None):
 
 
 def oracle_fwd(x, mask, mode, scale, causal, kind="additive"):
-    dt = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[x.dtype]
+    dt = DTYPE_OF[x.dtype]
     if mask is not None and kind == "lengths":
         return oracle.forward(to_np(x), dt, None, scale, causal, "lengths", to_np(mask))
     return oracle.forward(to_np(x), dt, mask_4d(mask, mode), scale, causal, kind)
 
 
 def dtname(t):
-    return {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[t.dtype]
+    return DTYPE_OF[t.dtype]
 
 
 # ------------------------------------------------------------ shape sweep
@@ -97,7 +97,7 @@ def check_fwd_bwd(x, mask, mode, kind, scale, causal, what, dy_seed=None):
     return y
 
 
-@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "f64"])
 @pytest.mark.parametrize("Sk", SK_SWEEP)
 def test_sweep_all_modes(dtype, Sk):
     """Every mask shape and kind (additive, boolean, key lengths), no causal rule
@@ -240,7 +240,7 @@ def test_workload_full_size(cfg):
 
 # ------------------------------------------- strides, alignment, in place
 
-@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "f64"])
 @pytest.mark.parametrize("Sk,pad,xoff,yoff,moff", [
     (1000, 0, 1, 1, 0),    # rows start mid-line, x and y alike
     (1000, 0, 1, 0, 0),    # x and y with different offsets -> element stores
@@ -412,7 +412,7 @@ def test_deterministic():
 
 # --------------------------------------------------------------- autograd
 
-@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "f64"])
 def test_autograd_and_streams(dtype):
     say(f"autograd dtype={dtype}")
     shape = (2, 3, 17, 130)
@@ -422,7 +422,7 @@ def test_autograd_and_streams(dtype):
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
         y = scaled_mask_softmax(x, mask, 0.35, True)
-        (y * dy).sum().backward() if dtype == "f32" else y.backward(dy)
+        (y * dy).sum().backward() if dtype in ("f32", "f64") else y.backward(dy)
     torch.cuda.synchronize()
     compare(decoded(y.detach()), oracle_fwd(x.detach(), mask, "b_sq_sk", 0.35, True), dtype,
             "autograd fwd")
@@ -516,6 +516,8 @@ def test_streaming_kernels_on_short_rows(dtype, Sk, monkeypatch):
     ("f16", 140001, "b_sq_sk", "bool"),       # rows of >= 16384 vectors: split when auto
     ("bf16", 262147, "key_lengths", "lengths"),
     ("f32", 65537, "full", "additive"),
+    ("f64", 70001, "sq_sk", "additive"),     # fp64: two-pass kernels at every length
+    ("f64", 40000, "b_1_sk", "bool"),
 ])
 @pytest.mark.parametrize("split", ["auto", "off"])
 def test_long_rows(dtype, Sk, mode, kind, split, monkeypatch):
