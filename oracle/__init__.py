@@ -18,13 +18,18 @@ exactly representable as a float64):
   sec. 2.3) and key padding given as per-batch lengths;
 * backward -- the same page, sec. 3.3: dx_i = scale * y_i * (dy_i - sum_j dy_j*y_j);
 * fully-masked rows -- pnsm.cn article on a custom ScaledMaskSoftmax operator,
-  sec. 4.2 / 4.3: such a row must not divide 0 by 0; it returns all zeros.
+  sec. 4.2 / 4.3: such a row must not divide 0 by 0; it returns all zeros;
+* fused attention (``oracle.attention``) -- O = softmax(Q K^T * scale + mask) V
+  and the rows' log-sum-exp, the fusion of the QK^T product into the operator
+  that the pnsm.cn article proposes in sec. 4.4, with the softmax step taken
+  from this package's softmax oracle.
 
 Every function here is pinned by tests in ``tests/test_oracle_pins.py``
 (closed forms, invariants, brute force, finite differences, the explicit
 Jacobian). Nothing in this package is "parity unpinned".
 """
 
+from . import attention  # noqa: F401
 from .softmax import (  # noqa: F401
     DTYPES,
     causal_offset,

@@ -105,9 +105,9 @@ def causal_offset(mode, Sq, Sk):
     raise ValueError(f"unknown causal mode {mode!r}")
 
 
-def _forward_one_row(xrow, mrow, sc, causal, q, excluded=None, offset=0):
-    """Softmax of one row of scores, in float64. ``excluded`` is a boolean
-    array of keys that take score -inf (boolean mask, key lengths)."""
+def _scores_one_row(xrow, mrow, sc, causal, q, excluded=None, offset=0):
+    """The scores of one row, in float64: x*scale + mask, -inf where a key is
+    excluded (``excluded``: boolean mask, key lengths) or past the causal bound."""
     n = xrow.shape[0]
     # score_k = x_k*scale + mask_k
     s = xrow * sc
@@ -119,13 +119,25 @@ def _forward_one_row(xrow, mrow, sc, causal, q, excluded=None, offset=0):
     if causal:
         s = s.copy()
         s[np.arange(n) > q + offset] = -math.inf
+    return s
+
+
+def _softmax_and_lse(s):
+    """softmax(s) and log(sum_k exp(s_k)) of one row of scores, in float64."""
+    n = s.shape[0]
     m = s.max() if n else -math.inf
     if m == -math.inf:
         # Every key is masked: the row is all zeros (nothing to normalise).
-        return np.zeros(n, dtype=np.float64)
+        return np.zeros(n, dtype=np.float64), -math.inf
     e = np.exp(s - m)  # exp(-inf) is exactly 0
     z = e.sum()
-    return e / z
+    return e / z, m + math.log(z)
+
+
+def _forward_one_row(xrow, mrow, sc, causal, q, excluded=None, offset=0):
+    """Softmax of one row of scores, in float64. ``excluded`` is a boolean
+    array of keys that take score -inf (boolean mask, key lengths)."""
+    return _softmax_and_lse(_scores_one_row(xrow, mrow, sc, causal, q, excluded, offset))[0]
 
 
 def _excluded(n, mrow_bool=None, key_len=None):

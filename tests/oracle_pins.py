@@ -12,7 +12,12 @@ Softmax operator in CUDA, wrapped into PyTorch", sec. 1.2 (score = x*scale +
 mask, softmax over keys; causal masks key j > query i), sec. 2.1 (max
 subtraction leaves the result unchanged), sec. 3.3 (backward formula and its
 Jacobian derivation); pnsm.cn ScaledMaskSoftmax article sec. 4.2/4.3 (a fully
-masked row must not produce NaN; zeros chosen).
+masked row must not produce NaN; zeros chosen). For fused attention
+(``oracle.attention``, the QK^T fusion of the pnsm.cn article's sec. 4.4):
+closed forms of one and two keys and of equal scores, a second formulation by
+brute force, invariances of attention under key permutation and key shift,
+grouped-query head mapping, and reduction to the pinned softmax oracle when V
+is the identity.
 """
 
 import itertools
@@ -20,6 +25,7 @@ import math
 
 import numpy as np
 
+import oracle.attention as A
 import oracle.softmax as S
 
 F32, F16 = np.float32, np.float16
@@ -399,10 +405,146 @@ def pin_causal_alignments():
            rtol=0)
 
 
+# ------------------------------------------------------------- attention pins
+
+def _attn_brute(q, k, v, scale, causal_offset=None):
+    """A second formulation for tiny float64 inputs without masks: loops over
+    queries and keys, no max shift, exact sums (math.fsum)."""
+    B, H, Sq, D = q.shape
+    Hk, Sk = k.shape[1], k.shape[2]
+    O = np.zeros((B, H, Sq, D))
+    L = np.zeros((B, H, Sq))
+    for b, h, i in itertools.product(range(B), range(H), range(Sq)):
+        g = h // (H // Hk)
+        keys = [j for j in range(Sk) if causal_offset is None or j <= i + causal_offset]
+        w = [math.exp(scale * math.fsum(q[b, h, i, d] * k[b, g, j, d] for d in range(D)))
+             for j in keys]
+        z = math.fsum(w)
+        L[b, h, i] = math.log(z) if keys else NINF
+        for d in range(D):
+            O[b, h, i, d] = math.fsum(wj * v[b, g, j, d] for wj, j in zip(w, keys)) / z if keys else 0
+    return O, L
+
+
+def _ints(seed, shape, lo=-3, hi=4, dtype=F32):
+    return _rng(seed).integers(lo, hi, size=shape).astype(dtype)
+
+
+def pin_attention_one_and_two_keys():
+    """One key: every query returns that key's value row and LSE = its score.
+    Two keys: O = sigma v0 + (1 - sigma) v1 with sigma = logistic(s0 - s1) and
+    LSE = log(e^s0 + e^s1), scores from integer vectors (exact)."""
+    q, k, v = _ints(1, (1, 2, 3, 4)), _ints(2, (1, 2, 1, 4)), _ints(3, (1, 2, 1, 4))
+    O, L = A.forward(q, k, v, "f32", scale=0.5)
+    for h in range(2):
+        _close(O[0, h], np.repeat(v[0, h].astype(np.float64), 3, axis=0), rtol=1e-15, what="one key O")
+        _close(L[0, h], 0.5 * (q[0, h] @ k[0, h, 0]), rtol=1e-15, what="one key LSE")
+    q, k, v = _ints(4, (1, 1, 3, 4)), _ints(5, (1, 1, 2, 4)), _ints(6, (1, 1, 2, 4))
+    O, L = A.forward(q, k, v, "f32", scale=0.25)
+    for i in range(3):
+        s0 = 0.25 * float(q[0, 0, i] @ k[0, 0, 0])
+        s1 = 0.25 * float(q[0, 0, i] @ k[0, 0, 1])
+        sg = _logistic(s0 - s1)
+        vd = v.astype(np.float64)
+        _close(O[0, 0, i], sg * vd[0, 0, 0] + (1 - sg) * vd[0, 0, 1], rtol=1e-14, what="two keys O")
+        _close(L[0, 0, i], max(s0, s1) + math.log1p(math.exp(-abs(s0 - s1))), rtol=1e-15,
+               what="two keys LSE")
+
+
+def pin_attention_equal_scores():
+    """Q = 0: every score is 0, so O is the mean of the value rows each query
+    may see (all; the first i+1 under the causal rule; the first L_b with key
+    lengths), LSE = log(count); no key at all gives zeros and -inf."""
+    Sq = Sk = 5
+    q = np.zeros((2, 1, Sq, 3), F32)
+    k = _ints(7, (2, 1, Sk, 3))
+    v = _ints(8, (2, 1, Sk, 3))
+    vd = v.astype(np.float64)
+    O, L = A.forward(q, k, v, "f32", scale=0.7)
+    _close(O[:, 0], np.repeat(vd[:, 0].mean(axis=1, keepdims=True), Sq, axis=1), atol=1e-14,
+           rtol=1e-14, what="mean of V")
+    _close(L, np.full((2, 1, Sq), math.log(Sk)), rtol=1e-15, what="LSE log n")
+    O, L = A.forward(q, k, v, "f32", is_causal=True)
+    for i in range(Sq):
+        _close(O[:, 0, i], vd[:, 0, :i + 1].mean(axis=1), atol=1e-14, rtol=1e-14,
+               what="causal prefix mean")
+        _close(L[:, 0, i], [math.log(i + 1)] * 2, rtol=1e-15, what="causal LSE")
+    O, L = A.forward(q, k, v, "f32", mask_kind="lengths", key_lengths=[0, 2])
+    assert (O[0] == 0).all() and (L[0] == NINF).all()
+    _close(O[1, 0], np.repeat(vd[1, 0, :2].mean(axis=0, keepdims=True), Sq, axis=0), atol=1e-14,
+           rtol=1e-14, what="length mean")
+
+
+def pin_attention_brute_force():
+    """Against the loop formulation on random tiny inputs: plain, top-left and
+    bottom-right causal (Sq < Sk), and grouped heads (H = 4 over Hk = 2)."""
+    r = _rng(9)
+    for (B, H, Hk, Sq, Sk, D), causal in itertools.product(
+            [(1, 2, 2, 3, 5, 4), (2, 4, 2, 4, 4, 3), (1, 1, 1, 1, 7, 2)],
+            [False, True, "bottom_right"]):
+        q = r.standard_normal((B, H, Sq, D)).astype(np.float64)
+        k = r.standard_normal((B, Hk, Sk, D)).astype(np.float64)
+        v = r.standard_normal((B, Hk, Sk, D)).astype(np.float64)
+        off = S.causal_offset(causal, Sq, Sk)
+        O, L = A.forward(q, k, v, "f64", scale=0.6, is_causal=causal)
+        Ob, Lb = _attn_brute(q, k, v, float(np.float32(0.6)), off)
+        _close(O, Ob, atol=1e-14, rtol=1e-12, what=f"brute O {causal}")
+        _close(L, Lb, atol=1e-14, rtol=1e-12, what=f"brute LSE {causal}")
+
+
+def pin_attention_invariants():
+    """Permuting keys with their values leaves O unchanged (no causal rule);
+    adding one vector c to every key adds scale*q.c to each row's scores, which
+    leaves O unchanged and shifts LSE by exactly that (integer data: exact)."""
+    q, k, v = _ints(10, (1, 2, 4, 3)), _ints(11, (1, 2, 6, 3)), _ints(12, (1, 2, 6, 3))
+    O, L = A.forward(q, k, v, "f32", scale=0.5)
+    perm = _rng(13).permutation(6)
+    O2, L2 = A.forward(q, k[:, :, perm], v[:, :, perm], "f32", scale=0.5)
+    _close(O2, O, rtol=1e-14, what="key permutation O")
+    _close(L2, L, rtol=1e-14, what="key permutation LSE")
+    c = np.array([1, -2, 3], F32)
+    O3, L3 = A.forward(q, k + c, v, "f32", scale=0.5)
+    _close(O3, O, atol=1e-14, rtol=1e-13, what="key shift O")
+    _close(L3, L + 0.5 * (q.astype(np.float64) @ c.astype(np.float64)), rtol=1e-14,
+           what="key shift LSE")
+
+
+def pin_attention_heads_and_masks():
+    """Grouped heads equal ordinary attention over repeated K/V; with V the
+    identity (D = Sk) O equals the softmax oracle's rows of the scaled masked
+    scores Q K^T (integer data: the scores are exact) for every mask kind and
+    causal rule."""
+    q, k, v = _ints(14, (2, 4, 3, 5)), _ints(15, (2, 2, 6, 5)), _ints(16, (2, 2, 6, 5))
+    O, L = A.forward(q, k, v, "f32", scale=0.3)
+    Or, Lr = A.forward(q, np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1), "f32", scale=0.3)
+    _close(O, Or, rtol=0, what="GQA O")
+    _close(L, Lr, rtol=0, what="GQA LSE")
+    B, H, Sq, Sk = 2, 2, 4, 6
+    q, k = _ints(17, (B, H, Sq, 3)), _ints(18, (B, H, Sk, 3))
+    eye = np.broadcast_to(np.eye(Sk, dtype=F32), (B, H, Sk, Sk)).copy()
+    S4 = (q.astype(np.float64) @ np.swapaxes(k.astype(np.float64), -1, -2)).astype(F32)
+    add = (_rng(19).standard_normal((1, 1, Sq, Sk)) * 2).astype(F32)
+    boolm = _rng(20).random((B, 1, Sq, Sk)) < 0.4
+    lens = [2, 5]
+    for causal in (False, True, "bottom_right"):
+        for mask, kind, kl in ((None, "additive", None), (add, "additive", None),
+                               (boolm, "bool", None), (None, "lengths", lens)):
+            O, _ = A.forward(q, k, eye, "f32", mask=mask, scale=0.4, is_causal=causal,
+                             mask_kind=kind, key_lengths=kl)
+            want = S.forward(S4, "f32", mask=mask, scale=0.4, is_causal=causal, mask_kind=kind,
+                             key_lengths=kl)
+            _close(O, want, atol=1e-16, rtol=1e-14, what=f"V=I {kind} {causal}")
+
+
+ATTENTION_PINS = [pin_attention_one_and_two_keys, pin_attention_equal_scores,
+                  pin_attention_brute_force, pin_attention_invariants,
+                  pin_attention_heads_and_masks]
+
+
 FORWARD_PINS = [pin_two_element_closed_form, pin_hand_rows, pin_fully_masked_rows,
                 pin_invariants, pin_library_special_case, pin_brute_force_exhaustive,
                 pin_tensor_indexing, pin_decode, pin_scale_rounding, pin_bool_masks,
                 pin_key_lengths, pin_causal_alignments]
 BACKWARD_PINS = [pin_backward_finite_differences, pin_backward_jacobian,
                  pin_backward_invariants]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS + ATTENTION_PINS

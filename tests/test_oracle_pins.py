@@ -171,3 +171,47 @@ def test_planted_mask_kind_mistakes_are_caught(monkeypatch):
         return -o if o else o
     monkeypatch.setattr(S, "causal_offset", offset_flipped)
     assert _run_all_pins()
+
+
+# ------------------------------------------------- planted attention mistakes
+
+import oracle.attention as A  # noqa: E402
+
+_orig_kv_head = A.kv_head
+_orig_head_scores = A.head_scores
+_orig_combine = A.combine
+_orig_softmax_lse = S._softmax_and_lse
+
+
+def _attention_pins_fail():
+    """True if at least one attention pin fails."""
+    for pin in P.ATTENTION_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            return True
+    return False
+
+
+@pytest.mark.parametrize("mistake", [
+    "gqa_modulo", "scores_transposed", "probs_transposed", "values_unweighted",
+    "lse_without_max", "no_scale",
+])
+def test_planted_attention_mistakes_are_caught(mistake, monkeypatch):
+    if mistake == "gqa_modulo":  # query head h reads kv head h % Hk
+        monkeypatch.setattr(A, "kv_head", lambda h, H, Hk: h % Hk)
+    elif mistake == "scores_transposed":  # K Q^T in place of Q K^T
+        monkeypatch.setattr(A, "head_scores", lambda qh, kh: (kh @ qh.T).T.T)
+    elif mistake == "probs_transposed":  # P^T V
+        monkeypatch.setattr(A, "combine", lambda P_, vh: P_.T @ vh)
+    elif mistake == "values_unweighted":  # sum of V over the keys that survive
+        monkeypatch.setattr(A, "combine", lambda P_, vh: (P_ > 0).astype(float) @ vh)
+    elif mistake == "lse_without_max":  # log of the shifted sum only
+        def lse_bad(s):
+            p, lse = _orig_softmax_lse(s)
+            m = s.max() if s.size else -math.inf
+            return p, (lse - m) if m != -math.inf else lse
+        monkeypatch.setattr(S, "_softmax_and_lse", lse_bad)
+    elif mistake == "no_scale":
+        monkeypatch.setattr(S, "_fp32", lambda v: 1.0)
+    assert _attention_pins_fail(), mistake
