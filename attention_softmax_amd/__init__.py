@@ -18,6 +18,7 @@ from .ops import (  # noqa: F401
     mask_kind_of,
     mask_mode_of,
     scaled_mask_softmax,
+    sms_attention_forward,
     sms_backward,
     sms_forward,
     sms_max_sk,

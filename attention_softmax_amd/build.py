@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsms.so")
 
-SOURCES = ["api.hip", "inst_f32.hip", "inst_f16.hip", "inst_bf16.hip", "inst_f64.hip"]
+SOURCES = ["api.hip", "inst_f32.hip", "inst_f16.hip", "inst_bf16.hip", "inst_f64.hip",
+           "attention.hip"]
 ARCH = "gfx950"
 
 

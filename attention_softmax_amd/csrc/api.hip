@@ -12,7 +12,9 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <utility>
 
+#include "attention.hpp"
 #include "kernels.hpp"
 #include "sms.h"
 
@@ -443,6 +445,73 @@ sms_status sms_backward_ws(const void* y, const int64_t y_strides[4], const void
   uint32_t blocks = 0;
   if (!grid_for(p.g.rows, pl, blocks)) return SMS_ERR_SHAPE;
   const hipError_t e = launch(dtype, nullptr, &p, pl, blocks, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SMS_OK : SMS_ERR_HIP;
+}
+
+sms_status sms_attention_forward(const void* q, const int64_t q_strides[4], const void* k,
+                                 const int64_t k_strides[4], const void* v,
+                                 const int64_t v_strides[4], const void* mask, int mask_mode,
+                                 void* o, const int64_t o_strides[4], float* lse,
+                                 sms_dtype dtype, int64_t B, int64_t H, int64_t Hk, int64_t Sq,
+                                 int64_t Sk, int64_t D, float scale, int is_causal,
+                                 void* stream) {
+  if (dtype != SMS_F16 && dtype != SMS_BF16) return SMS_ERR_DTYPE;
+  if (B < 0 || H < 0 || Hk < 0 || Sq < 0 || Sk < 0 || D < 0) return SMS_ERR_SHAPE;
+  if (is_causal < SMS_CAUSAL_NONE || is_causal > SMS_CAUSAL_BOTTOM_RIGHT) return SMS_ERR_CAUSAL;
+  const bool is_bool = (mask_mode & SMS_MASK_BOOL) != 0;
+  const int shape_mode = mask_mode & ~SMS_MASK_BOOL;
+  if (shape_mode < SMS_MASK_NONE || shape_mode > SMS_MASK_KEY_LENGTHS) return SMS_ERR_MASK_MODE;
+  if (is_bool && (shape_mode == SMS_MASK_NONE || shape_mode == SMS_MASK_KEY_LENGTHS))
+    return SMS_ERR_MASK_MODE;
+  if (D != 64 && D != 128) return SMS_ERR_SHAPE;
+  if (B == 0 || H == 0 || Sq == 0) return SMS_OK;  // no output row
+  if (Hk < 1 || H % Hk != 0) return SMS_ERR_SHAPE;
+  const bool has_mask = shape_mode != SMS_MASK_NONE;
+  if (!q || !k || !v || !o || (has_mask && !mask)) return SMS_ERR_NULL;
+  sms_status st;
+  for (const int64_t* s : {q_strides, k_strides, v_strides, o_strides})
+    if ((st = check_strides(s)) != SMS_OK) return st;
+  const int64_t nqt = (Sq + sms::kAttnBq - 1) / sms::kAttnBq;
+  if (nqt > INT32_MAX || H > 65535 || B > 65535 || Sq > INT32_MAX || Sk > INT32_MAX)
+    return SMS_ERR_SHAPE;
+  // Every row of Q, K, V and O starts on a 16-byte line (head dims of 8 elements).
+  for (const auto& t : {std::make_pair(q, q_strides), std::make_pair(k, k_strides),
+                        std::make_pair(v, v_strides),
+                        std::make_pair(static_cast<const void*>(o), o_strides)})
+    if (((uintptr_t)t.first & 15) || (t.second[0] & 7) || (t.second[1] & 7) || (t.second[2] & 7))
+      return SMS_ERR_ALIGN;
+  const int mask_bytes = shape_mode == SMS_MASK_KEY_LENGTHS ? 4 : (is_bool ? 1 : 2);
+  if (has_mask && !aligned_to(mask, mask_bytes)) return SMS_ERR_ALIGN;
+  if (((uintptr_t)lse & 3) != 0) return SMS_ERR_ALIGN;
+
+  sms::AttnParams p;
+  p.q = static_cast<const char*>(q);
+  p.k = static_cast<const char*>(k);
+  p.v = static_cast<const char*>(v);
+  p.mask = static_cast<const char*>(mask);
+  p.o = static_cast<char*>(o);
+  p.lse = lse;
+  p.sq_b = q_strides[0]; p.sq_h = q_strides[1]; p.sq_s = q_strides[2];
+  p.sk_b = k_strides[0]; p.sk_h = k_strides[1]; p.sk_s = k_strides[2];
+  p.sv_b = v_strides[0]; p.sv_h = v_strides[1]; p.sv_s = v_strides[2];
+  p.so_b = o_strides[0]; p.so_h = o_strides[1]; p.so_s = o_strides[2];
+  p.sm_b = p.sm_h = p.sm_q = 0;
+  switch (shape_mode) {
+    case SMS_MASK_SQ_SK: p.sm_q = Sk; break;
+    case SMS_MASK_B_SQ_SK: p.sm_b = Sq * Sk; p.sm_q = Sk; break;
+    case SMS_MASK_B_1_SK: p.sm_b = Sk; break;
+    case SMS_MASK_FULL: p.sm_b = H * Sq * Sk; p.sm_h = Sq * Sk; p.sm_q = Sk; break;
+    default: break;
+  }
+  p.B = (uint32_t)B; p.H = (uint32_t)H; p.Hk = (uint32_t)Hk;
+  p.Sq = (uint32_t)Sq; p.Sk = (uint32_t)Sk;
+  p.group = (uint32_t)(H / Hk);
+  p.scale_log2 = scale * sms::kLog2e;
+  p.causal = is_causal;
+  p.mask_kind = !has_mask ? sms::ATTN_MASK_NONE
+                : shape_mode == SMS_MASK_KEY_LENGTHS ? sms::ATTN_MASK_LEN
+                : is_bool ? sms::ATTN_MASK_BOOL : sms::ATTN_MASK_ADD;
+  const hipError_t e = sms_attn_launch(&p, (int)dtype, (int)D, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SMS_OK : SMS_ERR_HIP;
 }
 

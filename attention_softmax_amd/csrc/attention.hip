@@ -1,0 +1,282 @@
+// attention.hip -- fused attention forward on the gfx950 matrix cores:
+//
+//     O = softmax(Q K^T * scale + mask) V,   LSE = log sum_k exp(score_k)
+//
+// per query row, without the score tensor ever reaching memory (the QK^T
+// fusion of the pnsm.cn ScaledMaskSoftmax article, sec. 4.4), with the online
+// softmax of the 0539edu.com notes' fused-attention section: a running row
+// maximum and sum, and the output rescaled by exp(m_old - m_new) whenever the
+// maximum grows.
+//
+// Workgroup: 4 wavefronts x 32 queries = 128 queries of one (batch, head).
+// Keys arrive in tiles of 64 through LDS (K row-major, V transposed). Per tile
+// a wavefront computes S^T = K Q^T (keys x queries) with
+// v_mfma_f32_32x32x16_{f16,bf16}, so each lane holds 16 keys of one query:
+// the row maximum and sum are mostly in-lane plus one swap with the lane 32
+// away (which holds the other 16 keys of the same query). The probabilities
+// are then, register for register, the B operand of O^T += V^T P^T (the
+// contraction over keys in an order that matches the S^T output layout; the
+// A operand reads the matching keys of V^T), so P never leaves registers.
+//
+// MFMA 32x32x16 lane layout (probed on MI355X): A (32x16): lane l holds row
+// l%32, k = 8*(l/32)..+7; B (16x32): lane l holds column l%32, same k; D
+// (32x32): lane l holds column l%32, rows 8*(r/4) + 4*(l/32) + r%4 in its
+// registers r = 0..15.
+
+#include "attention.hpp"
+
+namespace sms {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2eA = 1.4426950408889634f;
+constexpr float kLn2A = 0.6931471805599453f;
+constexpr float kNegInfA = -__builtin_inff();
+
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Two fp32 values to a packed pair of 16-bit values, round to nearest even.
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (BF16) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    b2 v;
+    v.x = (__bf16)a;
+    v.y = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    h2 v;
+    v.x = (_Float16)a;
+    v.y = (_Float16)b;
+    return __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float to_float(uint32_t bits16) {
+  if constexpr (BF16) return __uint_as_float(bits16 << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// The value of lane l ^ 32 (same query, the other 16 keys of a 32-key block).
+__device__ __forceinline__ float other_half_max(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float other_half_sum(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 16-bit element j (0..7) of an 8-element vector.
+__device__ __forceinline__ uint32_t elem(const u32x4& v, int j) {
+  return (v[j >> 1] >> ((j & 1) * 16)) & 0xffffu;
+}
+
+template <bool BF16, int D, int KIND>
+__global__ void __launch_bounds__(256) attn_fwd_kernel(AttnParams p) {
+  constexpr int BK = kAttnBk;
+  constexpr int KP = D + 8;   // K tile row pitch, elements (conflict-free 16-byte reads)
+  constexpr int VP = BK + 4;  // V^T tile row pitch, elements (34 dwords: 8-byte reads spread)
+  __shared__ __align__(16) uint16_t ks[BK * KP];
+  __shared__ __align__(16) uint16_t vt[D * VP];
+
+  const int tid = (int)threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
+  const uint32_t b = blockIdx.z, h = blockIdx.y;
+  const int q0 = (int)((gridDim.x - 1 - blockIdx.x) * kAttnBq);  // longest causal tiles first
+  const int qi = q0 + wave * 32 + c;
+  const int Sq = (int)p.Sq, Sk = (int)p.Sk;
+  const uint32_t hk = h / p.group;
+  const char* qbase = p.q + ((int64_t)b * p.sq_b + (int64_t)h * p.sq_h) * 2;
+  const char* kbase = p.k + ((int64_t)b * p.sk_b + (int64_t)hk * p.sk_h) * 2;
+  const char* vbase = p.v + ((int64_t)b * p.sv_b + (int64_t)hk * p.sv_h) * 2;
+
+  // Keys the workgroup visits ([0, kend)) and this lane's query sees ([0, kq)).
+  const int off = p.causal == 2 ? Sk - Sq : 0;
+  int klen = Sk;
+  if constexpr (KIND == ATTN_MASK_LEN)
+    klen = max(min(reinterpret_cast<const int32_t*>(p.mask)[b], Sk), 0);
+  int kend = klen;
+  if (p.causal) kend = min(kend, max(q0 + kAttnBq + off, 0));
+  int kq = klen;
+  if (p.causal) kq = min(kq, max(qi + off + 1, 0));
+  const bool qvalid = qi < Sq;
+  const int64_t mrow = (int64_t)b * p.sm_b + (int64_t)h * p.sm_h + (int64_t)qi * p.sm_q;
+
+  // Q fragment: the B operand of S^T = K Q^T (query qi, dims ks*16 + 8g .. +7).
+  u32x4 qf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    qf[s] = u32x4{0, 0, 0, 0};
+    if (qvalid)
+      qf[s] = *reinterpret_cast<const u32x4*>(qbase + ((int64_t)qi * p.sq_s + s * 16 + 8 * g) * 2);
+  }
+
+  float m_i = kNegInfA, l_i = 0.0f;
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+
+  for (int kt = 0; kt < kend; kt += BK) {
+    __syncthreads();  // the previous tile's LDS reads are done
+    // K tile, row-major: 16-byte chunks, rows past Sk as zeros.
+    constexpr int KCH = D / 8;
+    for (int idx = tid; idx < BK * KCH; idx += 256) {
+      const int row = idx / KCH, ch = idx - row * KCH;
+      u32x4 val = u32x4{0, 0, 0, 0};
+      if (kt + row < Sk)
+        val = *reinterpret_cast<const u32x4*>(kbase + ((int64_t)(kt + row) * p.sk_s + ch * 8) * 2);
+      *reinterpret_cast<u32x4*>(&ks[row * KP + ch * 8]) = val;
+    }
+    // V tile, transposed: a thread reads 4 keys x 8 dims and writes 8 rows of 4 keys.
+    for (int idx = tid; idx < (BK / 4) * (D / 8); idx += 256) {
+      const int dg = idx % (D / 8), kg = idx / (D / 8);
+      u32x4 rv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = kt + 4 * kg + i;
+        rv[i] = u32x4{0, 0, 0, 0};
+        if (key < Sk)
+          rv[i] = *reinterpret_cast<const u32x4*>(vbase + ((int64_t)key * p.sv_s + dg * 8) * 2);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const u32x2 w{elem(rv[0], j) | (elem(rv[1], j) << 16), elem(rv[2], j) | (elem(rv[3], j) << 16)};
+        *reinterpret_cast<u32x2*>(&vt[(8 * dg + j) * VP + 4 * kg]) = w;
+      }
+    }
+    __syncthreads();
+
+    // S^T for the tile's two 32-key blocks.
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(&ks[(kb * 32 + c) * KP + s * 16 + 8 * g]);
+        sacc[kb] = mfma_32x32x16<BF16>(a, qf[s], sacc[kb]);
+      }
+    }
+
+    // Scores in the log2 domain, the mask and the key bounds.
+    float mloc = kNegInfA;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        float t = sacc[kb][r] * p.scale_log2;
+        if (key >= kq || key >= Sk) {
+          t = kNegInfA;
+        } else if constexpr (KIND == ATTN_MASK_ADD) {
+          if (qvalid) {
+            const uint32_t bits = *reinterpret_cast<const uint16_t*>(p.mask + (mrow + key) * 2);
+            t = fmaf(to_float<BF16>(bits), kLog2eA, t);
+          }
+        } else if constexpr (KIND == ATTN_MASK_BOOL) {
+          if (qvalid && p.mask[mrow + key] != 0) t = kNegInfA;
+        }
+        sacc[kb][r] = t;
+        mloc = fmaxf(mloc, t);
+      }
+    }
+    mloc = other_half_max(mloc);
+    const float m_new = fmaxf(m_i, mloc);
+    const float m_use = (m_new == kNegInfA) ? 0.0f : m_new;  // nothing visible yet
+    const float corr = __builtin_amdgcn_exp2f(m_i - m_use);
+    float psum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = __builtin_amdgcn_exp2f(sacc[kb][r] - m_use);
+        sacc[kb][r] = pv;
+        psum += pv;
+      }
+    l_i = l_i * corr + psum;
+    m_i = m_new;
+    // P as the B operand of O^T += V^T P^T: k-step s takes registers
+    // 8*(s%2) .. +7 of block s/2 (keys 16s + 8*(j/4) + 4g + j%4 for element j).
+    u32x4 pb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int kb = s >> 1, base = 8 * (s & 1);
+      pb[s] = u32x4{pack2<BF16>(sacc[kb][base + 0], sacc[kb][base + 1]),
+                    pack2<BF16>(sacc[kb][base + 2], sacc[kb][base + 3]),
+                    pack2<BF16>(sacc[kb][base + 4], sacc[kb][base + 5]),
+                    pack2<BF16>(sacc[kb][base + 6], sacc[kb][base + 7])};
+    }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= corr;
+      const uint16_t* vrow = &vt[(db * 32 + c) * VP];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x2 a0 = *reinterpret_cast<const u32x2*>(vrow + 16 * s + 4 * g);
+        const u32x2 a1 = *reinterpret_cast<const u32x2*>(vrow + 16 * s + 8 + 4 * g);
+        oacc[db] = mfma_32x32x16<BF16>(u32x4{a0.x, a0.y, a1.x, a1.y}, pb[s], oacc[db]);
+      }
+    }
+  }
+
+  const float L = other_half_sum(l_i);  // both halves of the query's keys
+  if (!qvalid) return;
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;  // no visible key: zeros
+  char* orow = p.o + ((int64_t)b * p.so_b + (int64_t)h * p.so_h + (int64_t)qi * p.so_s) * 2;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const u32x2 w{pack2<BF16>(oacc[db][4 * rg] * inv, oacc[db][4 * rg + 1] * inv),
+                    pack2<BF16>(oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv)};
+      *reinterpret_cast<u32x2*>(orow + (db * 32 + 8 * rg + 4 * g) * 2) = w;
+    }
+  if (p.lse && g == 0)
+    p.lse[((int64_t)b * p.H + h) * Sq + qi] = L > 0.0f ? (m_i + log2f(L)) * kLn2A : kNegInfA;
+}
+
+template <bool BF16, int D>
+hipError_t launch_kind(const AttnParams& p, hipStream_t st) {
+  const dim3 grid((p.Sq + kAttnBq - 1) / kAttnBq, p.H, p.B), block(256);
+  switch (p.mask_kind) {
+    case ATTN_MASK_NONE: hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_NONE>), grid, block, 0, st, p); break;
+    case ATTN_MASK_ADD: hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_ADD>), grid, block, 0, st, p); break;
+    case ATTN_MASK_BOOL: hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_BOOL>), grid, block, 0, st, p); break;
+    case ATTN_MASK_LEN: hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_LEN>), grid, block, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace sms
+
+hipError_t sms_attn_launch(const sms::AttnParams* p, int dtype, int head_dim, hipStream_t st) {
+  if (dtype == 1 && head_dim == 64) return sms::launch_kind<false, 64>(*p, st);
+  if (dtype == 1 && head_dim == 128) return sms::launch_kind<false, 128>(*p, st);
+  if (dtype == 2 && head_dim == 64) return sms::launch_kind<true, 64>(*p, st);
+  if (dtype == 2 && head_dim == 128) return sms::launch_kind<true, 128>(*p, st);
+  return hipErrorInvalidValue;
+}

@@ -211,6 +211,65 @@ def sms_backward(y, dy, dx, scale=1.0, is_causal=False, stream=None, workspace=N
     return dx
 
 
+def sms_attention_forward(q, k, v, mask=None, scale=None, is_causal=False, o=None,
+                          return_lse=False, stream=None):
+    """O = softmax(Q K^T * scale + mask) V, fused on the matrix cores (C ABI
+    sms_attention_forward); forward only.
+
+    q [B,H,Sq,D], k and v [B,Hk,Sk,D] (Hk divides H), float16 or bfloat16 GPU
+    tensors with the head dim contiguous and every row 16-byte aligned; D = 64
+    or 128. ``mask``: as for ``sms_forward`` (shapes over [B,H,Sq,Sk], additive
+    of q's dtype, boolean, or int32 key lengths [B]). ``scale`` defaults to
+    1/sqrt(D). Returns O (``o`` if given), and the fp32 log-sum-exp [B,H,Sq]
+    too when ``return_lse``.
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require_gpu(t, n)
+        if t.dim() != 4 or t.stride(-1) != 1:
+            raise ValueError(f"{n} must be 4-D with a contiguous last axis")
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k and v must share dtype and device")
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("attention takes float16 or bfloat16")
+    B, H, Sq, D = q.shape
+    Bk, Hk, Sk, Dk = k.shape
+    if tuple(v.shape) != (Bk, Hk, Sk, Dk) or Bk != B or Dk != D:
+        raise ValueError(f"shapes q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if o is None:
+        o = torch.empty_like(q, memory_format=torch.contiguous_format)
+    _require_gpu(o, "o")
+    if o.shape != q.shape or o.dtype != q.dtype or o.stride(-1) != 1:
+        raise ValueError("o must have q's shape and dtype, last axis contiguous")
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device) if return_lse else None
+    mode = mask_mode_of(mask, (B, H, Sq, Sk))
+    mode_code = _lib.MASK_MODES[mode]
+    mptr = None
+    if mask is not None:
+        _require_gpu(mask, "mask")
+        kind = mask_kind_of(mask)
+        if kind == "additive" and mask.dtype != q.dtype:
+            raise TypeError("additive mask dtype must equal q's")
+        if kind == "lengths" and mask.dtype != torch.int32:
+            raise TypeError("key lengths must be int32")
+        if kind == "bool":
+            mode_code |= _lib.MASK_BOOL
+        if not mask.is_contiguous():
+            raise ValueError("mask must be contiguous in its own shape")
+        mptr = mask.data_ptr()
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    L = _lib.lib()
+    with torch.cuda.device(q.device):
+        s = _stream_of(q.device, stream)
+        st = L.sms_attention_forward(
+            q.data_ptr(), _strides(q), k.data_ptr(), _strides(k), v.data_ptr(), _strides(v),
+            mptr, mode_code, o.data_ptr(), _strides(o),
+            lse.data_ptr() if lse is not None else None, _dtype_code(q, "q"), B, H, Hk, Sq, Sk,
+            D, float(scale), causal_code(is_causal), s.cuda_stream)
+    _lib.check("sms_attention_forward", st)
+    return (o, lse) if return_lse else o
+
+
 def sms_max_sk(dtype):
     """Largest key length the library runs for a torch dtype."""
     return int(_lib.lib().sms_max_sk(_lib.DTYPE_CODES[_DTYPES[dtype]]))

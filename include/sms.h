@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SMS_ABI_VERSION 3
+#define SMS_ABI_VERSION 4
 
 typedef enum {
   SMS_OK = 0,
@@ -213,6 +213,46 @@ sms_status sms_backward_ws(const void* y, const int64_t y_strides[4],
                            sms_dtype dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk,
                            float scale, int is_causal, void* workspace, int64_t workspace_bytes,
                            void* stream);
+
+/*
+ * sms_attention_forward -- fused attention forward on the matrix cores,
+ *
+ *     O = softmax(Q K^T * scale + mask) V      (over keys, per query row)
+ *
+ * without writing the scores to memory: the fusion of the QK^T product into the
+ * operator that the pnsm.cn ScaledMaskSoftmax article proposes in sec. 4.4
+ * (FlashAttention-style tiling), with the online softmax of the 0539edu.com
+ * notes' fused-attention section. The softmax step is exactly sms_forward's:
+ * same scale, mask modes and kinds, causal rules, and fully-masked rows give
+ * zeros.
+ *
+ *   q, q_strides   queries [B, H, Sq, D] (dtype), device memory
+ *   k, k_strides   keys    [B, Hk, Sk, D]: query head h reads key/value head
+ *                  h / (H / Hk) (grouped-query attention; Hk = H is plain
+ *                  multi-head attention)
+ *   v, v_strides   values  [B, Hk, Sk, D]
+ *   mask, mask_mode  as for sms_forward, over [B, H, Sq, Sk] scores
+ *   o, o_strides   output  [B, H, Sq, D] (dtype); every element written
+ *   lse            NULL, or fp32 [B, H, Sq] contiguous: the natural log of
+ *                  sum_k exp(score_k) over the visible keys (-inf if none), as
+ *                  a backward pass would need it
+ *   dtype          SMS_F16 or SMS_BF16 (products exact, fp32 accumulation; the
+ *                  probabilities enter the P V product rounded to dtype)
+ *   D              head dimension, 64 or 128
+ *   scale, is_causal, stream   as for sms_forward
+ *
+ * Every row of q, k, v and o must start on a 16-byte boundary (base 16-byte
+ * aligned, strides multiples of 8 elements; else SMS_ERR_ALIGN); the head dim
+ * is contiguous (stride[3] == 1). Limits: H, B <= 65535. Forward only.
+ */
+sms_status sms_attention_forward(const void* q, const int64_t q_strides[4],
+                                 const void* k, const int64_t k_strides[4],
+                                 const void* v, const int64_t v_strides[4],
+                                 const void* mask, int mask_mode,
+                                 void* o, const int64_t o_strides[4], float* lse,
+                                 sms_dtype dtype, int64_t B, int64_t H, int64_t Hk,
+                                 int64_t Sq, int64_t Sk, int64_t D,
+                                 float scale, int is_causal, void* stream);
 
 /* Largest key length Sk the library runs for `dtype` (2^30; 0 for an unknown
  * dtype). */

@@ -71,3 +71,47 @@ def compare(got, ref, dtype, what="", rowsum=False, live_rows=None):
             raise AssertionError(f"{what}: {int(bad.sum())} elements beyond {ULPS} ulp; worst "
                                  f"{r.flat[i]:.2f} ulp (got {got.flat[i]!r} want {ref.flat[i]!r})")
     return stats
+
+
+# ------------------------------------------------------- fused attention
+#
+# O = sum_k p_k v_k / L with fp32 scores and sums, the probabilities rounded to
+# the I/O dtype T (unit roundoff u_T = 2^-11 fp16, 2^-8 bf16) for the P V
+# product while L sums them unrounded, and O rounded to T at the end. Per
+# element: |O - O_ref| <= u_T * max_k |v_k| (the rounded probabilities) plus
+# the fp32 score error (below 2^-20 relative for |scores| < 2^4) plus half an
+# ulp of O; the bound allows twice that: 2 u_T max|v| + 2 ulp_T(O_ref). The
+# log-sum-exp is fp32: |LSE - LSE_ref| <= 2^-18 (1 + |LSE_ref|). Rows with no
+# visible key: O exactly 0 and LSE = -inf.
+
+ATTN_U = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+
+
+def compare_attention(got_o, ref_o, vmax, dtype, what="", got_lse=None, ref_lse=None):
+    """``vmax``: per output row, max |v| over the keys of its (batch, kv head),
+    broadcastable to O's shape. Returns stats."""
+    got = np.asarray(got_o, dtype=np.float64)
+    ref = np.asarray(ref_o, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    tol = 2 * ATTN_U[dtype] * np.asarray(vmax, dtype=np.float64) + 2 * ulp(ref, dtype)
+    err = np.abs(got - ref)
+    bad = err > tol
+    stats = {"max_abs": float(err.max()) if err.size else 0.0,
+             "max_err_over_tol": float((err / tol).max()) if err.size else 0.0}
+    if bad.any():
+        i = np.argmax(err / tol)
+        raise AssertionError(f"{what}: {int(bad.sum())} elements beyond tolerance; worst at "
+                             f"{np.unravel_index(i, got.shape)}: got {got.flat[i]!r} want "
+                             f"{ref.flat[i]!r} tol {tol.flat[i]:.3g}")
+    if got_lse is not None:
+        gl = np.asarray(got_lse, dtype=np.float64)
+        rl = np.asarray(ref_lse, dtype=np.float64)
+        none = rl == -np.inf
+        assert (gl[none] == -np.inf).all(), f"{what}: LSE of a row without keys must be -inf"
+        assert (ref[none] == 0).all() and (got[none] == 0).all(), f"{what}: such a row is zeros"
+        d = np.abs(gl[~none] - rl[~none])
+        ltol = 2.0 ** -18 * (1 + np.abs(rl[~none]))
+        assert (d <= ltol).all(), f"{what}: LSE off by {d.max():.3g}"
+        stats["lse_max_abs"] = float(d.max()) if d.size else 0.0
+    return stats
