@@ -37,6 +37,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr float kLog2eA = 1.4426950408889634f;
 constexpr float kLn2A = 0.6931471805599453f;
 constexpr float kNegInfA = -__builtin_inff();
+// Growth of the row maximum (log2 units) that the running output absorbs
+// before it is rescaled; probabilities stay below 2^kLazy.
+constexpr float kLazy = 8.0f;
 
 template <bool BF16>
 __device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
@@ -90,7 +93,8 @@ __device__ __forceinline__ uint32_t elem(const u32x4& v, int j) {
 }
 
 template <bool BF16, int D, int KIND>
-__global__ void __launch_bounds__(256) attn_fwd_kernel(AttnParams p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_fwd_kernel(AttnParams p) {
   constexpr int BK = kAttnBk;
   constexpr int KP = D + 8;   // K tile row pitch, elements (conflict-free 16-byte reads)
   constexpr int VP = BK + 4;  // V^T tile row pitch, elements (34 dwords: 8-byte reads spread)
@@ -202,9 +206,19 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnParams p) {
       }
     }
     mloc = other_half_max(mloc);
-    const float m_new = fmaxf(m_i, mloc);
-    const float m_use = (m_new == kNegInfA) ? 0.0f : m_new;  // nothing visible yet
-    const float corr = __builtin_amdgcn_exp2f(m_i - m_use);
+    // The reference maximum m_i moves only when a score exceeds it by more
+    // than kLazy (log2 units): probabilities then stay below 2^kLazy, far
+    // inside fp16 / bf16 range, and the running output and sum are rescaled
+    // only on those tiles -- and skipped by the whole wavefront when none of
+    // its queries needs it.
+    const bool grow = mloc > m_i + kLazy || (m_i == kNegInfA && mloc != kNegInfA);
+    float corr = 1.0f;
+    if (grow) {
+      corr = __builtin_amdgcn_exp2f(m_i - mloc);  // 0 from the first visible key on
+      m_i = mloc;
+      l_i *= corr;
+    }
+    const float m_use = (m_i == kNegInfA) ? 0.0f : m_i;  // nothing visible yet
     float psum = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -214,8 +228,8 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnParams p) {
         sacc[kb][r] = pv;
         psum += pv;
       }
-    l_i = l_i * corr + psum;
-    m_i = m_new;
+    l_i += psum;
+    const bool rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
     // P as the B operand of O^T += V^T P^T: k-step s takes registers
     // 8*(s%2) .. +7 of block s/2 (keys 16s + 8*(j/4) + 4g + j%4 for element j).
     u32x4 pb[4];
@@ -227,10 +241,14 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnParams p) {
                     pack2<BF16>(sacc[kb][base + 4], sacc[kb][base + 5]),
                     pack2<BF16>(sacc[kb][base + 6], sacc[kb][base + 7])};
     }
+    if (rescale) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= corr;
+    }
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= corr;
       const uint16_t* vrow = &vt[(db * 32 + c) * VP];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
