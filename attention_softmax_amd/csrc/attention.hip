@@ -140,35 +140,54 @@ attn_fwd_kernel(AttnParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
 
-  for (int kt = 0; kt < kend; kt += BK) {
-    __syncthreads();  // the previous tile's LDS reads are done
-    // K tile, row-major: 16-byte chunks, rows past Sk as zeros.
-    constexpr int KCH = D / 8;
-    for (int idx = tid; idx < BK * KCH; idx += 256) {
-      const int row = idx / KCH, ch = idx - row * KCH;
-      u32x4 val = u32x4{0, 0, 0, 0};
-      if (kt + row < Sk)
-        val = *reinterpret_cast<const u32x4*>(kbase + ((int64_t)(kt + row) * p.sk_s + ch * 8) * 2);
-      *reinterpret_cast<u32x4*>(&ks[row * KP + ch * 8]) = val;
-    }
-    // V tile, transposed: a thread reads 4 keys x 8 dims and writes 8 rows of 4 keys.
-    for (int idx = tid; idx < (BK / 4) * (D / 8); idx += 256) {
-      const int dg = idx % (D / 8), kg = idx / (D / 8);
-      u32x4 rv[4];
+  // Key/value tiles are fetched one tile ahead into registers (KC 16-byte
+  // chunks of K and VR rows of V per thread), so their global-memory latency
+  // overlaps the current tile's products; a thread then stores its K chunks
+  // row-major and its 4 keys x 8 dims of V transposed into LDS.
+  constexpr int KCH = D / 8;                     // 16-byte chunks per K row
+  constexpr int KC = BK * KCH / 256;              // K chunks per thread
+  constexpr int VITEMS = (BK / 4) * (D / 8);      // (4 keys x 8 dims) items per tile
+  const int vdg = tid % (D / 8), vkg = tid / (D / 8);
+  const bool vthread = tid < VITEMS;
+  u32x4 kreg[KC], vreg[4];
+  auto fetch = [&](int kt) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kt + 4 * kg + i;
-        rv[i] = u32x4{0, 0, 0, 0};
-        if (key < Sk)
-          rv[i] = *reinterpret_cast<const u32x4*>(vbase + ((int64_t)key * p.sv_s + dg * 8) * 2);
-      }
+    for (int i = 0; i < KC; ++i) {
+      const int idx = tid + 256 * i, row = idx / KCH, ch = idx - row * KCH;
+      kreg[i] = u32x4{0, 0, 0, 0};
+      if (kt + row < Sk)
+        kreg[i] = *reinterpret_cast<const u32x4*>(kbase + ((int64_t)(kt + row) * p.sk_s + ch * 8) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = kt + 4 * vkg + i;
+      vreg[i] = u32x4{0, 0, 0, 0};
+      if (vthread && key < Sk)
+        vreg[i] = *reinterpret_cast<const u32x4*>(vbase + ((int64_t)key * p.sv_s + vdg * 8) * 2);
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      const int idx = tid + 256 * i, row = idx / KCH, ch = idx - row * KCH;
+      *reinterpret_cast<u32x4*>(&ks[row * KP + ch * 8]) = kreg[i];
+    }
+    if (vthread) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const u32x2 w{elem(rv[0], j) | (elem(rv[1], j) << 16), elem(rv[2], j) | (elem(rv[3], j) << 16)};
-        *reinterpret_cast<u32x2*>(&vt[(8 * dg + j) * VP + 4 * kg]) = w;
+        const u32x2 w{elem(vreg[0], j) | (elem(vreg[1], j) << 16),
+                      elem(vreg[2], j) | (elem(vreg[3], j) << 16)};
+        *reinterpret_cast<u32x2*>(&vt[(8 * vdg + j) * VP + 4 * vkg]) = w;
       }
     }
+  };
+  if (kend > 0) fetch(0);
+
+  for (int kt = 0; kt < kend; kt += BK) {
+    __syncthreads();  // the previous tile's LDS reads are done
+    stage();
     __syncthreads();
+    if (kt + BK < kend) fetch(kt + BK);  // in flight during this tile's products
 
     // S^T for the tile's two 32-key blocks.
     f32x16 sacc[2];
