@@ -472,8 +472,7 @@ sms_status sms_attention_forward(const void* q, const int64_t q_strides[4], cons
   for (const int64_t* s : {q_strides, k_strides, v_strides, o_strides})
     if ((st = check_strides(s)) != SMS_OK) return st;
   const int64_t nqt = (Sq + sms::kAttnBq - 1) / sms::kAttnBq;
-  if (nqt > INT32_MAX || H > 65535 || B > 65535 || Sq > INT32_MAX || Sk > INT32_MAX)
-    return SMS_ERR_SHAPE;
+  if (nqt * H * B > INT32_MAX || Sq > INT32_MAX || Sk > INT32_MAX) return SMS_ERR_SHAPE;
   // Every row of Q, K, V and O starts on a 16-byte line (head dims of 8 elements).
   for (const auto& t : {std::make_pair(q, q_strides), std::make_pair(k, k_strides),
                         std::make_pair(v, v_strides),

@@ -42,5 +42,5 @@ constexpr int kAttnBk = 64;
 }  // namespace sms
 
 // Launch of the forward for dtype 1 (fp16) or 2 (bf16) and head dim 64 or 128;
-// hipErrorInvalidValue for anything else. Grid: ceil(Sq / 128) x H x B.
+// hipErrorInvalidValue for anything else. Grid: H * B * ceil(Sq / 128).
 hipError_t sms_attn_launch(const sms::AttnParams* p, int dtype, int head_dim, hipStream_t st);

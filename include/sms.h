@@ -243,7 +243,8 @@ sms_status sms_backward_ws(const void* y, const int64_t y_strides[4],
  *
  * Every row of q, k, v and o must start on a 16-byte boundary (base 16-byte
  * aligned, strides multiples of 8 elements; else SMS_ERR_ALIGN); the head dim
- * is contiguous (stride[3] == 1). Limits: H, B <= 65535. Forward only.
+ * is contiguous (stride[3] == 1). Limits: ceil(Sq / 128) * H * B < 2^31.
+ * Forward only.
  */
 sms_status sms_attention_forward(const void* q, const int64_t q_strides[4],
                                  const void* k, const int64_t k_strides[4],
