@@ -13,6 +13,14 @@ value = algorithmic bytes of a step / time of a step (GB/s), where algorithmic
 bytes count x and the mask once where the result depends on them, y and dy
 where y can be nonzero, and every y and dx written. One JSON line on stdout;
 diagnostics on stderr.
+
+    python bench.py --op attention [--steps K] [--warmup W]
+
+times the fused attention forward instead (O = softmax(Q K^T * scale) V, fp16
+[4,32,4096,128] queries, keys and values, causal): value = the two products'
+flops (halved by the causal rule) / time, in TFLOP/s against the MI355X dense
+fp16 matrix peak. It is a diagnostic line for that kernel; the default
+(softmax) line is the headline metric.
 """
 
 import argparse
@@ -30,6 +38,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 matrix, published
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_KERNEL = "__amd_rocclr_copyBuffer"  # torch's device copy, timed as the copy reference
 
@@ -74,6 +83,8 @@ def parse():
     # its clocks (the forward runs up to 15 % slow meanwhile): warm up past it.
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--op", default="softmax", choices=["softmax", "attention"],
+                    help="softmax (the headline line) or the fused attention forward")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the oracle CPU baseline sample (0 = skip)")
     ap.add_argument("--no-copy", action="store_true", help="skip the plain-copy reference")
@@ -284,6 +295,87 @@ def torch_reference(torch, w, stream, fwd_b, bwd_b, fwd_ms, bwd_ms):
             "speedup_forward": round(tf / fwd_ms, 2), "speedup_backward": round(tb / bwd_ms, 2)}
 
 
+def bench_attention(args):
+    """Fused attention forward: fp16 [4,32,4096,128] Q, K, V, causal, scale 1/sqrt(128)."""
+    import torch
+
+    import oracle
+    from attention_softmax_amd import sms_attention_forward
+    from attention_softmax_amd.workloads import draw_x
+    from tests.parity import to_np
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, H, S, D, causal = 4, 32, 4096, 128, True
+    scale = D ** -0.5
+    q = draw_x((B, H, S, D), "f16", ("normal", 1.0), 11, dev)
+    k = draw_x((B, H, S, D), "f16", ("normal", 1.0), 12, dev)
+    v = draw_x((B, H, S, D), "f16", ("normal", 1.0), 13, dev)
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+    flops = 4.0 * B * H * S * S * D * (0.5 if causal else 1.0)
+    for _ in range(args.warmup):
+        sms_attention_forward(q, k, v, None, scale, causal, o=o, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        sms_attention_forward(q, k, v, None, scale, causal, o=o, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = e0.elapsed_time(e1) / args.steps
+    tflops = flops / (ms * 1e-3) / 1e12
+    sdpa = None
+    try:
+        for _ in range(3):
+            torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal)
+        e0.record(stream)
+        for _ in range(5):
+            torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t2 = e0.elapsed_time(e1) / 5
+        sdpa = {"what": "torch.nn.functional.scaled_dot_product_attention, same tensors",
+                "avg_us": round(t2 * 1e3, 1), "TFLOPs": round(flops / (t2 * 1e-3) / 1e12, 1)}
+    except RuntimeError as ex:  # context only
+        sdpa = {"error": type(ex).__name__}
+    cpu = None
+    if args.cpu_seconds > 0:
+        # the float64 oracle on the first n queries of head (0, 0), n doubling
+        # until the time budget is spent
+        # (one BLAS thread, so that `cores` is what was used)
+        from threadpoolctl import threadpool_limits
+
+        n, spent, done_flops = 16, 0.0, 0.0
+        qn, kn, vn = to_np(q[:1, :1]), to_np(k[:1, :1]), to_np(v[:1, :1])
+        with threadpool_limits(limits=1):
+            while spent < args.cpu_seconds and n <= S:
+                t0 = time.perf_counter()
+                oracle.attention.forward(qn[:, :, :n], kn, vn, "f16", scale=scale,
+                                         is_causal=causal)
+                spent += time.perf_counter() - t0
+                done_flops += 4.0 * n * S * D  # the oracle multiplies every key (no causal skip)
+                n *= 2
+        cpu = {"value": round(done_flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"queries 0..{n // 2 - 1} of head (0,0), {spent:.1f} s, float64 numpy"}
+    out = {
+        "metric": "fused attention forward TFLOP/s, 1 MI355X", "value": round(tflops, 1),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "attention fp16 Q,K,V [4,32,4096,128] N(0,1), causal",
+                   "shape": [B, H, S, D], "causal": causal, "scale": scale},
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": round(tflops, 1),
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None},
+        "torch_reference": sdpa, "cpu_baseline": cpu, "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.ingest:
@@ -293,6 +385,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): rows are "
               "independent, so a multi-GPU run is the same kernel on each GPU's share", file=sys.stderr)
         sys.exit(2)
+    if args.op == "attention":
+        bench_attention(args)
+        return
 
     import torch
 
