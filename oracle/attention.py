@@ -2,8 +2,8 @@
 
     O = softmax(Q K^T * scale + mask) V        (softmax over keys, per query row)
 
-and of its log-sum-exp per row. TEST INFRASTRUCTURE ONLY (see the package
-docstring).
+and of its log-sum-exp per row, and the backward (dQ, dK, dV for an upstream
+gradient dO). TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Sources: the pnsm.cn ScaledMaskSoftmax article, sec. 4.4, proposes fusing the
 QK^T product into the operator (FlashAttention-style tiling), which removes the
@@ -91,3 +91,47 @@ def forward(q, k, v, dtype, mask=None, scale=1.0, is_causal=False, mask_kind="ad
                 P[i], LSE[b, h, i] = S._softmax_and_lse(s)
             O[b, h] = combine(P, vd[b, g])
     return O, LSE
+
+
+def backward(q, k, v, do, dtype, mask=None, scale=1.0, is_causal=False, mask_kind="additive",
+             key_lengths=None):
+    """(dQ, dK, dV) of L = sum(dO * O), in float64.
+
+    Chain rule through O = P V and P = softmax(S * scale + mask), S = Q K^T:
+    dV = P^T dO; dP = dO V^T; the softmax backward of the softmax oracle gives
+    dS = scale * P * (dP - sum_j dP_j P_j) row by row (lmnt.cn page sec. 3.3,
+    the scale entering as the derivative of S * scale); dQ = dS K; dK = dS^T Q.
+    Key/value heads shared by several query heads sum their contributions.
+    """
+    qd, kd, vd = _decode4(q, dtype), _decode4(k, dtype), _decode4(v, dtype)
+    dod = _decode4(do, dtype)
+    B, H, Sq, D = qd.shape
+    Hk, Sk = kd.shape[1], kd.shape[2]
+    S._check_mask_shape(mask, (B, H, Sq, Sk))
+    off = S.causal_offset(is_causal, Sq, Sk)
+    maskd = None
+    if mask is not None:
+        maskd = S.decode(mask, dtype) if mask_kind == "additive" else np.asarray(mask)
+    sc = S._fp32(scale)
+    dQ = np.zeros(qd.shape)
+    dK = np.zeros(kd.shape)
+    dV = np.zeros(vd.shape)
+    for b in range(B):
+        for h in range(H):
+            g = kv_head(h, H, Hk)
+            scores = head_scores(qd[b, h], kd[b, g])
+            P = np.empty((Sq, Sk))
+            for i in range(Sq):
+                mrow = S._mask_row(maskd, b, h, i) if maskd is not None else None
+                add = mrow if mask_kind == "additive" else None
+                ex = S._excluded(Sk, mrow if mask_kind == "bool" else None,
+                                 key_lengths[b] if key_lengths is not None else None)
+                s = S._scores_one_row(scores[i], add, sc, off is not None, i, ex, off or 0)
+                P[i] = S._softmax_and_lse(s)[0]
+            dV[b, g] += P.T @ dod[b, h]
+            dP = dod[b, h] @ vd[b, g].T
+            dS = np.stack([S._backward_one_row(P[i], dP[i], sc) for i in range(Sq)])
+            dQ[b, h] = dS @ kd[b, g]
+            dK[b, g] += dS.T @ qd[b, h]
+    return dQ, dK, dV
+

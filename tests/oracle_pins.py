@@ -536,9 +536,57 @@ def pin_attention_heads_and_masks():
             _close(O, want, atol=1e-16, rtol=1e-14, what=f"V=I {kind} {causal}")
 
 
+def pin_attention_backward_finite_differences():
+    """dQ, dK, dV against central differences of L = sum(dO * O) computed with
+    the forward oracle, on tiny float64 inputs: grouped heads (H = 2 over
+    Hk = 1), an additive mask, a boolean mask with the causal rule, key lengths."""
+    r = _rng(21)
+    B, H, Hk, Sq, Sk, D = 1, 2, 1, 3, 4, 2
+    q = r.standard_normal((B, H, Sq, D))
+    k = r.standard_normal((B, Hk, Sk, D))
+    v = r.standard_normal((B, Hk, Sk, D))
+    do = r.standard_normal((B, H, Sq, D))
+    add = r.standard_normal((1, 1, Sq, Sk))
+    boolm = np.array([[[[0, 1, 0, 0], [0, 0, 1, 0], [1, 0, 0, 0]]]], bool)
+    cases = [dict(), dict(mask=add), dict(mask=boolm, mask_kind="bool", is_causal=True),
+             dict(mask_kind="lengths", key_lengths=[3], is_causal="bottom_right")]
+    for kw in cases:
+        def loss(qq, kk, vv):
+            return float((A.forward(qq, kk, vv, "f64", scale=0.7, **kw)[0] * do).sum())
+        dq, dk, dv = A.backward(q, k, v, do, "f64", scale=0.7, **kw)
+        for arr, grad, name in ((q, dq, "dQ"), (k, dk, "dK"), (v, dv, "dV")):
+            for idx in itertools.product(*[range(n) for n in arr.shape]):
+                hstep = 1e-6
+                a1, a2 = arr.copy(), arr.copy()
+                a1[idx] += hstep
+                a2[idx] -= hstep
+                args1 = [a1 if x is arr else x for x in (q, k, v)]
+                args2 = [a2 if x is arr else x for x in (q, k, v)]
+                fd = (loss(*args1) - loss(*args2)) / (2 * hstep)
+                _close(grad[idx], fd, atol=1e-8, rtol=1e-6, what=f"{name}{idx} {kw}")
+
+
+def pin_attention_backward_structure():
+    """Keys no query sees (key lengths) get dK = dV = 0; grouped heads sum
+    their heads' gradients (equal to repeating K and V and adding the copies)."""
+    q, k, v = _ints(22, (2, 2, 3, 4)), _ints(23, (2, 2, 5, 4)), _ints(24, (2, 2, 5, 4))
+    do = _ints(25, (2, 2, 3, 4))
+    dq, dk, dv = A.backward(q, k, v, do, "f32", scale=0.3, mask_kind="lengths", key_lengths=[2, 4])
+    assert (dk[0, :, 2:] == 0).all() and (dv[0, :, 2:] == 0).all()
+    assert (dk[1, :, 4:] == 0).all() and (dv[1, :, 4:] == 0).all()
+    kq, vq = _ints(26, (2, 1, 5, 4)), _ints(27, (2, 1, 5, 4))
+    dq1, dk1, dv1 = A.backward(q, kq, vq, do, "f32", scale=0.3)
+    dq2, dk2, dv2 = A.backward(q, np.repeat(kq, 2, axis=1), np.repeat(vq, 2, axis=1), do, "f32",
+                               scale=0.3)
+    _close(dq1, dq2, rtol=0, what="GQA dQ")
+    _close(dk1[:, 0], dk2.sum(axis=1), atol=1e-14, rtol=1e-14, what="GQA dK")
+    _close(dv1[:, 0], dv2.sum(axis=1), atol=1e-14, rtol=1e-14, what="GQA dV")
+
+
 ATTENTION_PINS = [pin_attention_one_and_two_keys, pin_attention_equal_scores,
                   pin_attention_brute_force, pin_attention_invariants,
-                  pin_attention_heads_and_masks]
+                  pin_attention_heads_and_masks, pin_attention_backward_finite_differences,
+                  pin_attention_backward_structure]
 
 
 FORWARD_PINS = [pin_two_element_closed_form, pin_hand_rows, pin_fully_masked_rows,

@@ -193,9 +193,12 @@ def _attention_pins_fail():
     return False
 
 
+_orig_bwd_row = S._backward_one_row
+
+
 @pytest.mark.parametrize("mistake", [
     "gqa_modulo", "scores_transposed", "probs_transposed", "values_unweighted",
-    "lse_without_max", "no_scale",
+    "lse_without_max", "no_scale", "softmax_backward_unscaled", "softmax_backward_no_dot",
 ])
 def test_planted_attention_mistakes_are_caught(mistake, monkeypatch):
     if mistake == "gqa_modulo":  # query head h reads kv head h % Hk
@@ -214,4 +217,8 @@ def test_planted_attention_mistakes_are_caught(mistake, monkeypatch):
         monkeypatch.setattr(S, "_softmax_and_lse", lse_bad)
     elif mistake == "no_scale":
         monkeypatch.setattr(S, "_fp32", lambda v: 1.0)
+    elif mistake == "softmax_backward_unscaled":  # dS without the scale factor
+        monkeypatch.setattr(S, "_backward_one_row", lambda y, dy, sc: _orig_bwd_row(y, dy, 1.0))
+    elif mistake == "softmax_backward_no_dot":  # dS = scale * P * dP
+        monkeypatch.setattr(S, "_backward_one_row", lambda y, dy, sc: sc * y * dy)
     assert _attention_pins_fail(), mistake
