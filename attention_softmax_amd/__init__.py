@@ -9,16 +9,24 @@ functions of the same names in libsms.so (include/sms.h): every step of the
 computation runs in the HIP kernels. ``scaled_mask_softmax`` wraps them in a
 ``torch.autograd.Function`` that saves only y for the backward, as in lmnt.cn
 "Custom fused Softmax operator in CUDA, wrapped into PyTorch", sec. 4.3.
+
+``sms_attention_forward`` / ``sms_attention_backward`` run the fused attention
+softmax(Q K^T * scale + mask) V and its gradients on the matrix cores;
+``attention`` is the differentiable wrapper.
 """
 
 from ._lib import SmsError, lib  # noqa: F401
 from .ops import (  # noqa: F401
+    AttentionFunction,
     ScaledMaskSoftmaxFunction,
+    attention,
     causal_code,
     mask_kind_of,
     mask_mode_of,
     scaled_mask_softmax,
+    sms_attention_backward,
     sms_attention_forward,
+    sms_attention_workspace_bytes,
     sms_backward,
     sms_forward,
     sms_max_sk,

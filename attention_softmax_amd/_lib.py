@@ -25,9 +25,10 @@ MASK_MODES = {"none": 0, "sq_sk": 1, "b_sq_sk": 2, "b_1_sk": 3, "full": 4, "key_
 MASK_BOOL = 0x10
 CAUSAL_CODES = {"none": 0, "top_left": 1, "bottom_right": 2}
 EXPORTS = ("sms_forward", "sms_backward", "sms_forward_ws", "sms_backward_ws",
-           "sms_workspace_bytes", "sms_attention_forward", "sms_max_sk", "sms_path",
+           "sms_workspace_bytes", "sms_attention_forward", "sms_attention_backward",
+           "sms_attention_workspace_bytes", "sms_max_sk", "sms_path",
            "sms_status_str", "sms_abi_version")
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _lock = threading.Lock()
 _lib = None
@@ -60,6 +61,13 @@ def _declare(L):
                                         strides, vp, i32, i64, i64, i64, i64, i64, i64, f32, i32,
                                         vp]
     L.sms_attention_forward.restype = i32
+    L.sms_attention_backward.argtypes = [vp, strides, vp, strides, vp, strides, vp, strides, vp,
+                                         strides, vp, vp, i32, vp, strides, vp, strides, vp,
+                                         strides, i32, i64, i64, i64, i64, i64, i64, f32, i32, vp,
+                                         i64, vp]
+    L.sms_attention_backward.restype = i32
+    L.sms_attention_workspace_bytes.argtypes = [i64, i64, i64]
+    L.sms_attention_workspace_bytes.restype = i64
     L.sms_workspace_bytes.argtypes = [i32, i64, i64, i64, i64, i32]
     L.sms_workspace_bytes.restype = i64
     L.sms_max_sk.argtypes = [i32]

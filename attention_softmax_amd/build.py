@@ -19,8 +19,15 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsms.so")
 
 SOURCES = ["api.hip", "inst_f32.hip", "inst_f16.hip", "inst_bf16.hip", "inst_f64.hip",
-           "attention.hip"]
+           "attention.hip", "attention_bwd.hip"]
 ARCH = "gfx950"
+
+# Per-source flags. The attention backward's MFMAs keep their accumulators in
+# ordinary VGPRs: with the compiler's default (AGPR accumulators) the D = 64
+# dK/dV kernel copied an accumulator out of AGPRs at its loop head three wait
+# states after the MFMA that wrote it (an 8-pass MFMA needs 11), and the copy
+# read a stale value (isa_check.py finds such reads).
+EXTRA_FLAGS = {"attention_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc():
@@ -43,9 +50,25 @@ def common_flags():
     ]
 
 
+def source_flags(src):
+    """Every hipcc flag the build uses for one source file."""
+    return common_flags() + EXTRA_FLAGS.get(src, [])
+
+
+def device_asm(src, out):
+    """Compile one source's gfx950 device code to assembly at ``out``, with the
+    build's flags (for inspection; the build itself does not need it)."""
+    cmd = [hipcc()] + source_flags(src) + ["--cuda-device-only", "-S", os.path.join(CSRC, src),
+                                           "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stderr}")
+    return out
+
+
 def _compile(src):
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + source_flags(src) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature and says so; drop that line.
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)

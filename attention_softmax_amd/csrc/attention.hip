@@ -28,69 +28,7 @@
 namespace sms {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
-constexpr float kLog2eA = 1.4426950408889634f;
-constexpr float kLn2A = 0.6931471805599453f;
-constexpr float kNegInfA = -__builtin_inff();
-// Growth of the row maximum (log2 units) that the running output absorbs
-// before it is rescaled; probabilities stay below 2^kLazy.
-constexpr float kLazy = 8.0f;
-
-template <bool BF16>
-__device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
-  if constexpr (BF16)
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
-
-// Two fp32 values to a packed pair of 16-bit values, round to nearest even.
-template <bool BF16>
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-  if constexpr (BF16) {
-    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-    b2 v;
-    v.x = (__bf16)a;
-    v.y = (__bf16)b;
-    return __builtin_bit_cast(uint32_t, v);
-  } else {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    h2 v;
-    v.x = (_Float16)a;
-    v.y = (_Float16)b;
-    return __builtin_bit_cast(uint32_t, v);
-  }
-}
-
-template <bool BF16>
-__device__ __forceinline__ float to_float(uint32_t bits16) {
-  if constexpr (BF16) return __uint_as_float(bits16 << 16);
-  else return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
-}
-
-// The value of lane l ^ 32 (same query, the other 16 keys of a 32-key block).
-__device__ __forceinline__ float other_half_max(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float other_half_sum(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// 16-bit element j (0..7) of an 8-element vector.
-__device__ __forceinline__ uint32_t elem(const u32x4& v, int j) {
-  return (v[j >> 1] >> ((j & 1) * 16)) & 0xffffu;
-}
+using namespace attn;
 
 template <bool BF16, int D, int KIND>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))

@@ -35,12 +35,121 @@ struct AttnParams {
 
 enum : int { ATTN_MASK_NONE = 0, ATTN_MASK_ADD = 1, ATTN_MASK_BOOL = 2, ATTN_MASK_LEN = 3 };
 
+// Backward: dQ, dK, dV of L = sum(dO * O) given the forward's O and LSE.
+struct AttnBwdParams {
+  const char* q;
+  const char* k;
+  const char* v;
+  const char* o;
+  const char* dout;  // dO
+  const char* mask;  // as in AttnParams
+  const float* lse;  // [B, H, Sq] from the forward
+  float* delta;      // workspace [B, H, Sq]: rowsum(dO * O)
+  char* dq;
+  char* dk;
+  char* dv;
+  int64_t sq_b, sq_h, sq_s;
+  int64_t sk_b, sk_h, sk_s;
+  int64_t sv_b, sv_h, sv_s;
+  int64_t so_b, so_h, so_s;    // O
+  int64_t sdo_b, sdo_h, sdo_s; // dO
+  int64_t sdq_b, sdq_h, sdq_s;
+  int64_t sdk_b, sdk_h, sdk_s;
+  int64_t sdv_b, sdv_h, sdv_s;
+  int64_t sm_b, sm_h, sm_q;
+  uint32_t B, H, Hk, Sq, Sk;
+  uint32_t group;
+  float scale;       // the forward's scale
+  float scale_log2;  // scale * log2(e)
+  int causal;
+  int mask_kind;
+};
+
+// Keys per workgroup of the dK / dV kernel (four wavefronts x 32) and queries
+// per tile it streams.
+constexpr int kAttnBwdBk = 128;
+constexpr int kAttnBwdBq = 32;
+
 // Queries per workgroup (four wavefronts of 32 queries) and keys per tile.
 constexpr int kAttnBq = 128;
 constexpr int kAttnBk = 64;
+
+// Device helpers shared by the forward and backward kernels.
+namespace attn {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2eA = 1.4426950408889634f;
+constexpr float kLn2A = 0.6931471805599453f;
+constexpr float kNegInfA = -__builtin_inff();
+// Growth of the row maximum (log2 units) that the running output absorbs
+// before it is rescaled; probabilities stay below 2^kLazy.
+constexpr float kLazy = 8.0f;
+
+template <bool BF16>
+__device__ inline __attribute__((always_inline)) f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Two fp32 values to a packed pair of 16-bit values, round to nearest even.
+template <bool BF16>
+__device__ inline __attribute__((always_inline)) uint32_t pack2(float a, float b) {
+  if constexpr (BF16) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    b2 v;
+    v.x = (__bf16)a;
+    v.y = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    h2 v;
+    v.x = (_Float16)a;
+    v.y = (_Float16)b;
+    return __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+template <bool BF16>
+__device__ inline __attribute__((always_inline)) float to_float(uint32_t bits16) {
+  if constexpr (BF16) return __uint_as_float(bits16 << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// The value of lane l ^ 32 (same query, the other 16 keys of a 32-key block).
+__device__ inline __attribute__((always_inline)) float other_half_max(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline __attribute__((always_inline)) float other_half_sum(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 16-bit element j (0..7) of an 8-element vector.
+__device__ inline __attribute__((always_inline)) uint32_t elem(const u32x4& v, int j) {
+  return (v[j >> 1] >> ((j & 1) * 16)) & 0xffffu;
+}
+
+}  // namespace attn
 
 }  // namespace sms
 
 // Launch of the forward for dtype 1 (fp16) or 2 (bf16) and head dim 64 or 128;
 // hipErrorInvalidValue for anything else. Grid: H * B * ceil(Sq / 128).
 hipError_t sms_attn_launch(const sms::AttnParams* p, int dtype, int head_dim, hipStream_t st);
+
+// The backward's three launches (rowsum(dO * O) into the workspace; dQ; dK and
+// dV), same dtype / head-dim rules.
+hipError_t sms_attn_bwd_launch(const sms::AttnBwdParams* p, int dtype, int head_dim,
+                               hipStream_t st);

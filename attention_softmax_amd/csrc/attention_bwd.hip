@@ -1,0 +1,486 @@
+// attention_bwd.hip -- fused attention backward on the gfx950 matrix cores:
+// dQ, dK, dV of L = sum(dO * O) for O = softmax(Q K^T * scale + mask) V,
+// recomputing the probabilities from the forward's log-sum-exp instead of
+// storing them (the FlashAttention-style scheme the pnsm.cn article's sec. 4.4
+// points to; the softmax gradient itself is the lmnt.cn page's sec. 3.3 rule,
+// dS = P * (dP - rowsum(dP * P)), with rowsum(dP * P) = rowsum(dO * O)).
+//
+// Three launches, all deterministic (no atomics):
+//  1. delta = rowsum(dO * O) per query row, fp32, into the workspace;
+//  2. dQ, one workgroup per 128 queries (query-stationary, as the forward):
+//     S^T = K Q^T and dP^T = V dO^T leave each lane 16 keys of one query;
+//     P = exp(S*scale + mask - LSE); dS^T = P (dP^T - delta); dQ^T += K^T dS^T
+//     with the dS registers as the B operand (keys contracted in the order the
+//     S^T layout holds them, K^T read from a transposed LDS tile);
+//  3. dK and dV, one workgroup per 128 keys of one key/value head
+//     (key-stationary): for every query head of its group and every tile of
+//     32 queries, S = Q K^T and dP = dO V^T leave each lane 16 queries of one
+//     key; dV^T += dO^T P and dK^T += Q^T dS with P and dS as B operands.
+// Lane layouts of v_mfma_f32_32x32x16: see attention.hip.
+
+#include <algorithm>
+
+#include "attention.hpp"
+
+namespace sms {
+namespace {
+
+using namespace attn;
+
+// ------------------------------------------------------------ 1. delta
+
+template <bool BF16, int D>
+__global__ void __launch_bounds__(256) attn_delta_kernel(AttnBwdParams p) {
+  constexpr int LPR = D / 8;       // lanes per row: 16 bytes each
+  constexpr int RPB = 256 / LPR;   // rows per workgroup and pass
+  const int lane = (int)(threadIdx.x % LPR);
+  const int64_t rows = (int64_t)p.B * p.H * p.Sq;
+  // Grid-stride over rows (the grid is capped); the bound is uniform per
+  // workgroup, so every lane reaches the shuffles.
+  for (int64_t row0 = (int64_t)blockIdx.x * RPB; row0 < rows; row0 += (int64_t)gridDim.x * RPB) {
+    const int64_t row = row0 + threadIdx.x / LPR;
+    float acc = 0.0f;
+    if (row < rows) {
+      const uint32_t i = (uint32_t)(row % p.Sq);
+      const uint32_t bh = (uint32_t)(row / p.Sq);
+      const uint32_t h = bh % p.H, b = bh / p.H;
+      const u32x4 g = *reinterpret_cast<const u32x4*>(
+          p.dout + ((int64_t)b * p.sdo_b + (int64_t)h * p.sdo_h + (int64_t)i * p.sdo_s + 8 * lane) * 2);
+      const u32x4 o = *reinterpret_cast<const u32x4*>(
+          p.o + ((int64_t)b * p.so_b + (int64_t)h * p.so_h + (int64_t)i * p.so_s + 8 * lane) * 2);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        acc = fmaf(to_float<BF16>(elem(g, j)), to_float<BF16>(elem(o, j)), acc);
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (row < rows && lane == 0) p.delta[row] = acc;
+  }
+}
+
+// ---------------------------------------------------------------- 2. dQ
+
+template <bool BF16, int D, int KIND>
+__global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdParams p) {
+  constexpr int BK = kAttnBk;
+  constexpr int KP = D + 8;   // row-major tile pitch, elements
+  constexpr int TP = BK + 4;  // transposed tile pitch, elements
+  __shared__ __align__(16) uint16_t ks[BK * KP];   // K, row-major: A of S^T = K Q^T
+  __shared__ __align__(16) uint16_t kts[D * TP];   // K^T: A of dQ^T += K^T dS^T
+  __shared__ __align__(16) uint16_t vs[BK * KP];   // V, row-major: A of dP^T = V dO^T
+
+  const int tid = (int)threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
+  // Same workgroup order as the forward.
+  const uint32_t N = gridDim.x, per = N / 8, HB = p.H * p.B;
+  const uint32_t ntq = N / HB;
+  uint32_t t = blockIdx.x, hb, qt;
+  if (p.causal) {
+    hb = t % HB;
+    qt = ntq - 1 - t / HB;
+  } else {
+    if (t < per * 8) t = (t % 8) * per + t / 8;
+    hb = t / ntq;
+    qt = t % ntq;
+  }
+  const uint32_t h = hb % p.H, b = hb / p.H;
+  const int q0 = (int)(qt * kAttnBq);
+  const int qi = q0 + wave * 32 + c;
+  const int Sq = (int)p.Sq, Sk = (int)p.Sk;
+  const uint32_t hk = h / p.group;
+  const char* kbase = p.k + ((int64_t)b * p.sk_b + (int64_t)hk * p.sk_h) * 2;
+  const char* vbase = p.v + ((int64_t)b * p.sv_b + (int64_t)hk * p.sv_h) * 2;
+
+  const int off = p.causal == 2 ? Sk - Sq : 0;
+  int klen = Sk;
+  if constexpr (KIND == ATTN_MASK_LEN)
+    klen = max(min(reinterpret_cast<const int32_t*>(p.mask)[b], Sk), 0);
+  int kend = klen;
+  if (p.causal) kend = min(kend, max(q0 + kAttnBq + off, 0));
+  int kq = klen;
+  if (p.causal) kq = min(kq, max(qi + off + 1, 0));
+  const bool qvalid = qi < Sq;
+  const int64_t mrow = (int64_t)b * p.sm_b + (int64_t)h * p.sm_h + (int64_t)qi * p.sm_q;
+  const int64_t lrow = ((int64_t)b * p.H + h) * Sq + qi;
+  const float lse = qvalid ? p.lse[lrow] : kNegInfA;
+  const bool live = lse != kNegInfA;  // a query that sees no key has no gradient
+  const float lse2 = live ? lse * kLog2eA : 0.0f;
+  const float delta = qvalid ? p.delta[lrow] : 0.0f;
+
+  // Q and dO fragments: the B operands of S^T = K Q^T and dP^T = V dO^T.
+  u32x4 qf[D / 16], df[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    qf[s] = u32x4{0, 0, 0, 0};
+    df[s] = u32x4{0, 0, 0, 0};
+    if (qvalid) {
+      qf[s] = *reinterpret_cast<const u32x4*>(
+          p.q + ((int64_t)b * p.sq_b + (int64_t)h * p.sq_h + (int64_t)qi * p.sq_s + s * 16 + 8 * g) * 2);
+      df[s] = *reinterpret_cast<const u32x4*>(
+          p.dout + ((int64_t)b * p.sdo_b + (int64_t)h * p.sdo_h + (int64_t)qi * p.sdo_s + s * 16 + 8 * g) * 2);
+    }
+  }
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[db][r] = 0.0f;
+
+  // Tiles fetched one ahead: K as (4 keys x 8 dims) per thread, staged
+  // row-major and transposed; V as 16-byte chunks, staged row-major.
+  constexpr int KITEMS = (BK / 4) * (D / 8);
+  constexpr int KCH = D / 8;
+  constexpr int VC = BK * KCH / 256;
+  const int kdg = tid % (D / 8), kkg = tid / (D / 8);
+  const bool kthread = tid < KITEMS;
+  u32x4 kreg[4], vreg[VC];
+  auto fetch = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = kt + 4 * kkg + i;
+      kreg[i] = u32x4{0, 0, 0, 0};
+      if (kthread && key < Sk)
+        kreg[i] = *reinterpret_cast<const u32x4*>(kbase + ((int64_t)key * p.sk_s + kdg * 8) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < VC; ++i) {
+      const int idx = tid + 256 * i, row = idx / KCH, ch = idx - row * KCH;
+      vreg[i] = u32x4{0, 0, 0, 0};
+      if (kt + row < Sk)
+        vreg[i] = *reinterpret_cast<const u32x4*>(vbase + ((int64_t)(kt + row) * p.sv_s + ch * 8) * 2);
+    }
+  };
+  auto stage = [&]() {
+    if (kthread) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4*>(&ks[(4 * kkg + i) * KP + 8 * kdg]) = kreg[i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const u32x2 w{elem(kreg[0], j) | (elem(kreg[1], j) << 16),
+                      elem(kreg[2], j) | (elem(kreg[3], j) << 16)};
+        *reinterpret_cast<u32x2*>(&kts[(8 * kdg + j) * TP + 4 * kkg]) = w;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VC; ++i) {
+      const int idx = tid + 256 * i, row = idx / KCH, ch = idx - row * KCH;
+      *reinterpret_cast<u32x4*>(&vs[row * KP + ch * 8]) = vreg[i];
+    }
+  };
+  if (kend > 0) fetch(0);
+
+  for (int kt = 0; kt < kend; kt += BK) {
+    __syncthreads();
+    stage();
+    __syncthreads();
+    if (kt + BK < kend) fetch(kt + BK);
+
+    f32x16 sacc[2], dpacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sacc[kb][r] = 0.0f;
+        dpacc[kb][r] = 0.0f;
+      }
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(&ks[(kb * 32 + c) * KP + s * 16 + 8 * g]);
+        sacc[kb] = mfma_32x32x16<BF16>(a, qf[s], sacc[kb]);
+        const u32x4 av = *reinterpret_cast<const u32x4*>(&vs[(kb * 32 + c) * KP + s * 16 + 8 * g]);
+        dpacc[kb] = mfma_32x32x16<BF16>(av, df[s], dpacc[kb]);
+      }
+    }
+    // dS^T = P (dP^T - delta), P recomputed from the forward's LSE.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        float tv = sacc[kb][r] * p.scale_log2;
+        bool excluded = key >= kq || key >= Sk || !live;
+        if constexpr (KIND == ATTN_MASK_ADD) {
+          if (!excluded) {
+            const uint32_t bits = *reinterpret_cast<const uint16_t*>(p.mask + (mrow + key) * 2);
+            tv = fmaf(to_float<BF16>(bits), kLog2eA, tv);
+          }
+        } else if constexpr (KIND == ATTN_MASK_BOOL) {
+          if (!excluded && p.mask[mrow + key] != 0) excluded = true;
+        }
+        const float pv = excluded ? 0.0f : __builtin_amdgcn_exp2f(tv - lse2);
+        sacc[kb][r] = pv * (dpacc[kb][r] - delta);
+      }
+    }
+    u32x4 pb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int kb = s >> 1, base = 8 * (s & 1);
+      pb[s] = u32x4{pack2<BF16>(sacc[kb][base + 0], sacc[kb][base + 1]),
+                    pack2<BF16>(sacc[kb][base + 2], sacc[kb][base + 3]),
+                    pack2<BF16>(sacc[kb][base + 4], sacc[kb][base + 5]),
+                    pack2<BF16>(sacc[kb][base + 6], sacc[kb][base + 7])};
+    }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const uint16_t* krow = &kts[(db * 32 + c) * TP];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x2 a0 = *reinterpret_cast<const u32x2*>(krow + 16 * s + 4 * g);
+        const u32x2 a1 = *reinterpret_cast<const u32x2*>(krow + 16 * s + 8 + 4 * g);
+        dq[db] = mfma_32x32x16<BF16>(u32x4{a0.x, a0.y, a1.x, a1.y}, pb[s], dq[db]);
+      }
+    }
+  }
+
+  if (!qvalid) return;
+  char* orow = p.dq + ((int64_t)b * p.sdq_b + (int64_t)h * p.sdq_h + (int64_t)qi * p.sdq_s) * 2;
+  const float sc = p.scale;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const u32x2 w{pack2<BF16>(dq[db][4 * rg] * sc, dq[db][4 * rg + 1] * sc),
+                    pack2<BF16>(dq[db][4 * rg + 2] * sc, dq[db][4 * rg + 3] * sc)};
+      *reinterpret_cast<u32x2*>(orow + (db * 32 + 8 * rg + 4 * g) * 2) = w;
+    }
+}
+
+// ------------------------------------------------------------ 3. dK, dV
+
+template <bool BF16, int D, int KIND>
+__global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdParams p) {
+  constexpr int BQ = kAttnBwdBq;
+  constexpr int RP = D + 8;   // row-major tile pitch, elements
+  constexpr int TP = BQ + 4;  // transposed tile pitch, elements (18 dwords)
+  __shared__ __align__(16) uint16_t qs[BQ * RP];    // Q: A of S = Q K^T
+  __shared__ __align__(16) uint16_t qts[D * TP];    // Q^T: A of dK^T += Q^T dS
+  __shared__ __align__(16) uint16_t dos[BQ * RP];   // dO: A of dP = dO V^T
+  __shared__ __align__(16) uint16_t dots[D * TP];   // dO^T: A of dV^T += dO^T P
+  __shared__ float lses[BQ], dels[BQ];
+
+  const int tid = (int)threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
+  const int Sq = (int)p.Sq, Sk = (int)p.Sk;
+  const uint32_t nkt = (p.Sk + kAttnBwdBk - 1) / kAttnBwdBk;
+  const uint32_t kti = blockIdx.x % nkt, hkb = blockIdx.x / nkt;
+  const uint32_t hk = hkb % p.Hk, b = hkb / p.Hk;
+  const int k0 = (int)(kti * kAttnBwdBk);
+  const int kj = k0 + wave * 32 + c;  // this lane's key
+  const bool kvalid = kj < Sk;
+  const char* kbase = p.k + ((int64_t)b * p.sk_b + (int64_t)hk * p.sk_h) * 2;
+  const char* vbase = p.v + ((int64_t)b * p.sv_b + (int64_t)hk * p.sv_h) * 2;
+
+  // K and V fragments: the B operands of S = Q K^T and dP = dO V^T.
+  u32x4 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    kf[s] = u32x4{0, 0, 0, 0};
+    vf[s] = u32x4{0, 0, 0, 0};
+    if (kvalid) {
+      kf[s] = *reinterpret_cast<const u32x4*>(kbase + ((int64_t)kj * p.sk_s + s * 16 + 8 * g) * 2);
+      vf[s] = *reinterpret_cast<const u32x4*>(vbase + ((int64_t)kj * p.sv_s + s * 16 + 8 * g) * 2);
+    }
+  }
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[db][r] = 0.0f;
+      dv[db][r] = 0.0f;
+    }
+
+  const int off = p.causal == 2 ? Sk - Sq : 0;
+  int klen = Sk;
+  if constexpr (KIND == ATTN_MASK_LEN)
+    klen = max(min(reinterpret_cast<const int32_t*>(p.mask)[b], Sk), 0);
+  // Queries that may see one of the workgroup's keys: i >= k0 - off (causal).
+  int qstart = p.causal ? max(k0 - off, 0) : 0;
+  qstart = qstart / BQ * BQ;
+  const bool any = k0 < klen;
+
+  // Tiles of BQ queries fetched one ahead: (4 queries x 8 dims) of Q by the
+  // first QITEMS threads and of dO by the next QITEMS, staged row-major and
+  // transposed; LSE and delta by 2 * BQ threads.
+  constexpr int QITEMS = (BQ / 4) * (D / 8);
+  const int item = tid < QITEMS ? tid : tid - QITEMS;
+  const bool is_q = tid < QITEMS, is_do = tid >= QITEMS && tid < 2 * QITEMS;
+  const int qdg = item % (D / 8), qqg = item / (D / 8);
+  u32x4 treg[4];
+  float sreg = 0.0f;
+  auto fetch = [&](uint32_t h, int qt) {
+    const char* base = is_q ? p.q + ((int64_t)b * p.sq_b + (int64_t)h * p.sq_h) * 2
+                            : p.dout + ((int64_t)b * p.sdo_b + (int64_t)h * p.sdo_h) * 2;
+    const int64_t rs = is_q ? p.sq_s : p.sdo_s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = qt + 4 * qqg + i;
+      treg[i] = u32x4{0, 0, 0, 0};
+      if ((is_q || is_do) && q < Sq)
+        treg[i] = *reinterpret_cast<const u32x4*>(base + ((int64_t)q * rs + qdg * 8) * 2);
+    }
+    if (tid < 2 * BQ) {
+      const int q = qt + (tid % BQ);
+      const int64_t lrow = ((int64_t)b * p.H + h) * Sq + q;
+      sreg = tid < BQ ? kNegInfA : 0.0f;
+      if (q < Sq) sreg = tid < BQ ? p.lse[lrow] : p.delta[lrow];
+    }
+  };
+  auto stage = [&]() {
+    if (is_q || is_do) {
+      uint16_t* rm = is_q ? qs : dos;
+      uint16_t* tr = is_q ? qts : dots;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4*>(&rm[(4 * qqg + i) * RP + 8 * qdg]) = treg[i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const u32x2 w{elem(treg[0], j) | (elem(treg[1], j) << 16),
+                      elem(treg[2], j) | (elem(treg[3], j) << 16)};
+        *reinterpret_cast<u32x2*>(&tr[(8 * qdg + j) * TP + 4 * qqg]) = w;
+      }
+    }
+    if (tid < BQ) lses[tid] = sreg;
+    else if (tid < 2 * BQ) dels[tid - BQ] = sreg;
+  };
+
+  if (any) {
+    const uint32_t h0 = hk * p.group, h1 = h0 + p.group;
+    if (qstart < Sq) fetch(h0, qstart);
+    for (uint32_t h = h0; h < h1; ++h) {
+      const int64_t mbase = (int64_t)b * p.sm_b + (int64_t)h * p.sm_h;
+      for (int qt = qstart; qt < Sq; qt += BQ) {
+        __syncthreads();
+        stage();
+        __syncthreads();
+        if (qt + BQ < Sq) fetch(h, qt + BQ);
+        else if (h + 1 < h1) fetch(h + 1, qstart);
+
+        f32x16 sacc, dpacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sacc[r] = 0.0f;
+          dpacc[r] = 0.0f;
+        }
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(&qs[c * RP + s * 16 + 8 * g]);
+          sacc = mfma_32x32x16<BF16>(a, kf[s], sacc);
+          const u32x4 ad = *reinterpret_cast<const u32x4*>(&dos[c * RP + s * 16 + 8 * g]);
+          dpacc = mfma_32x32x16<BF16>(ad, vf[s], dpacc);
+        }
+        // Register r holds query qt + 8*(r/4) + 4g + r%4 of this lane's key.
+        float pr[16], dsr[16];
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int ql = 8 * rg + 4 * g;  // first of 4 consecutive queries
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * rg + e, qq = qt + ql + e;
+            const float lse = lses[ql + e];
+            float tv = sacc[r] * p.scale_log2;
+            bool excluded = qq >= Sq || kj >= klen || !kvalid || lse == kNegInfA ||
+                            (p.causal && kj > qq + off);
+            if constexpr (KIND == ATTN_MASK_ADD) {
+              if (!excluded) {
+                const uint32_t bits = *reinterpret_cast<const uint16_t*>(
+                    p.mask + (mbase + (int64_t)qq * p.sm_q + kj) * 2);
+                tv = fmaf(to_float<BF16>(bits), kLog2eA, tv);
+              }
+            } else if constexpr (KIND == ATTN_MASK_BOOL) {
+              if (!excluded && p.mask[mbase + (int64_t)qq * p.sm_q + kj] != 0) excluded = true;
+            }
+            const float pv = excluded ? 0.0f : __builtin_amdgcn_exp2f(tv - lse * kLog2eA);
+            pr[r] = pv;
+            dsr[r] = pv * (dpacc[r] - dels[ql + e]);
+          }
+        }
+        // B operands: k-step s takes registers 8s .. 8s+7 (queries
+        // 16s + 8*(j/4) + 4g + j%4 for element j).
+        u32x4 pb[2], sb[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          pb[s] = u32x4{pack2<BF16>(pr[8 * s + 0], pr[8 * s + 1]), pack2<BF16>(pr[8 * s + 2], pr[8 * s + 3]),
+                        pack2<BF16>(pr[8 * s + 4], pr[8 * s + 5]), pack2<BF16>(pr[8 * s + 6], pr[8 * s + 7])};
+          sb[s] = u32x4{pack2<BF16>(dsr[8 * s + 0], dsr[8 * s + 1]), pack2<BF16>(dsr[8 * s + 2], dsr[8 * s + 3]),
+                        pack2<BF16>(dsr[8 * s + 4], dsr[8 * s + 5]), pack2<BF16>(dsr[8 * s + 6], dsr[8 * s + 7])};
+        }
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const uint16_t* dorow = &dots[(db * 32 + c) * TP];
+          const uint16_t* qrow = &qts[(db * 32 + c) * TP];
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const u32x2 a0 = *reinterpret_cast<const u32x2*>(dorow + 16 * s + 4 * g);
+            const u32x2 a1 = *reinterpret_cast<const u32x2*>(dorow + 16 * s + 8 + 4 * g);
+            dv[db] = mfma_32x32x16<BF16>(u32x4{a0.x, a0.y, a1.x, a1.y}, pb[s], dv[db]);
+            const u32x2 b0 = *reinterpret_cast<const u32x2*>(qrow + 16 * s + 4 * g);
+            const u32x2 b1 = *reinterpret_cast<const u32x2*>(qrow + 16 * s + 8 + 4 * g);
+            dk[db] = mfma_32x32x16<BF16>(u32x4{b0.x, b0.y, b1.x, b1.y}, sb[s], dk[db]);
+          }
+        }
+      }
+    }
+  }
+
+  if (!kvalid) return;
+  char* dkrow = p.dk + ((int64_t)b * p.sdk_b + (int64_t)hk * p.sdk_h + (int64_t)kj * p.sdk_s) * 2;
+  char* dvrow = p.dv + ((int64_t)b * p.sdv_b + (int64_t)hk * p.sdv_h + (int64_t)kj * p.sdv_s) * 2;
+  const float sc = p.scale;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d = db * 32 + 8 * rg + 4 * g;
+      const u32x2 wk{pack2<BF16>(dk[db][4 * rg] * sc, dk[db][4 * rg + 1] * sc),
+                     pack2<BF16>(dk[db][4 * rg + 2] * sc, dk[db][4 * rg + 3] * sc)};
+      const u32x2 wv{pack2<BF16>(dv[db][4 * rg], dv[db][4 * rg + 1]),
+                     pack2<BF16>(dv[db][4 * rg + 2], dv[db][4 * rg + 3])};
+      *reinterpret_cast<u32x2*>(dkrow + d * 2) = wk;
+      *reinterpret_cast<u32x2*>(dvrow + d * 2) = wv;
+    }
+}
+
+template <bool BF16, int D, int KIND>
+hipError_t launch_bwd_kind(const AttnBwdParams& p, hipStream_t st) {
+  const dim3 block(256);
+  if (p.Sq > 0) {
+    const int64_t rows = (int64_t)p.B * p.H * p.Sq;
+    const int rpb = 256 / (D / 8);
+    const int64_t wgs = std::min<int64_t>((rows + rpb - 1) / rpb, 65536);
+    hipLaunchKernelGGL((attn_delta_kernel<BF16, D>), dim3((uint32_t)wgs), block, 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, KIND>),
+                       dim3(p.H * p.B * ((p.Sq + kAttnBq - 1) / kAttnBq)), block, 0, st, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (p.Sk > 0)
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<BF16, D, KIND>),
+                       dim3(p.Hk * p.B * ((p.Sk + kAttnBwdBk - 1) / kAttnBwdBk)), block, 0, st, p);
+  return hipGetLastError();
+}
+
+template <bool BF16, int D>
+hipError_t launch_bwd(const AttnBwdParams& p, hipStream_t st) {
+  switch (p.mask_kind) {
+    case ATTN_MASK_NONE: return launch_bwd_kind<BF16, D, ATTN_MASK_NONE>(p, st);
+    case ATTN_MASK_ADD: return launch_bwd_kind<BF16, D, ATTN_MASK_ADD>(p, st);
+    case ATTN_MASK_BOOL: return launch_bwd_kind<BF16, D, ATTN_MASK_BOOL>(p, st);
+    case ATTN_MASK_LEN: return launch_bwd_kind<BF16, D, ATTN_MASK_LEN>(p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+}  // namespace sms
+
+hipError_t sms_attn_bwd_launch(const sms::AttnBwdParams* p, int dtype, int head_dim,
+                               hipStream_t st) {
+  if (dtype == 1 && head_dim == 64) return sms::launch_bwd<false, 64>(*p, st);
+  if (dtype == 1 && head_dim == 128) return sms::launch_bwd<false, 128>(*p, st);
+  if (dtype == 2 && head_dim == 64) return sms::launch_bwd<true, 64>(*p, st);
+  if (dtype == 2 && head_dim == 128) return sms::launch_bwd<true, 128>(*p, st);
+  return hipErrorInvalidValue;
+}

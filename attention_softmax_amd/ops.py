@@ -211,10 +211,47 @@ def sms_backward(y, dy, dx, scale=1.0, is_causal=False, stream=None, workspace=N
     return dx
 
 
+def _attn_check(tensors, q):
+    for t, n in tensors:
+        _require_gpu(t, n)
+        if t.dim() != 4 or t.stride(-1) != 1:
+            raise ValueError(f"{n} must be 4-D with a contiguous last axis")
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{n} must share q's dtype and device")
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("attention takes float16 or bfloat16")
+
+
+def _attn_shapes(q, k, v):
+    B, H, Sq, D = q.shape
+    Bk, Hk, Sk, Dk = k.shape
+    if tuple(v.shape) != (Bk, Hk, Sk, Dk) or Bk != B or Dk != D:
+        raise ValueError(f"shapes q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    return B, H, Hk, Sq, Sk, D
+
+
+def _attn_mask(mask, q, scores_shape):
+    """(pointer, C mask mode) of an attention mask over [B, H, Sq, Sk] scores."""
+    mode_code = _lib.MASK_MODES[mask_mode_of(mask, scores_shape)]
+    if mask is None:
+        return None, mode_code
+    _require_gpu(mask, "mask")
+    kind = mask_kind_of(mask)
+    if kind == "additive" and mask.dtype != q.dtype:
+        raise TypeError("additive mask dtype must equal q's")
+    if kind == "lengths" and mask.dtype != torch.int32:
+        raise TypeError("key lengths must be int32")
+    if kind == "bool":
+        mode_code |= _lib.MASK_BOOL
+    if not mask.is_contiguous():
+        raise ValueError("mask must be contiguous in its own shape")
+    return mask.data_ptr(), mode_code
+
+
 def sms_attention_forward(q, k, v, mask=None, scale=None, is_causal=False, o=None,
                           return_lse=False, stream=None):
     """O = softmax(Q K^T * scale + mask) V, fused on the matrix cores (C ABI
-    sms_attention_forward); forward only.
+    sms_attention_forward).
 
     q [B,H,Sq,D], k and v [B,Hk,Sk,D] (Hk divides H), float16 or bfloat16 GPU
     tensors with the head dim contiguous and every row 16-byte aligned; D = 64
@@ -223,39 +260,15 @@ def sms_attention_forward(q, k, v, mask=None, scale=None, is_causal=False, o=Non
     1/sqrt(D). Returns O (``o`` if given), and the fp32 log-sum-exp [B,H,Sq]
     too when ``return_lse``.
     """
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _require_gpu(t, n)
-        if t.dim() != 4 or t.stride(-1) != 1:
-            raise ValueError(f"{n} must be 4-D with a contiguous last axis")
-        if t.dtype != q.dtype or t.device != q.device:
-            raise ValueError("q, k and v must share dtype and device")
-    if q.dtype not in (torch.float16, torch.bfloat16):
-        raise TypeError("attention takes float16 or bfloat16")
-    B, H, Sq, D = q.shape
-    Bk, Hk, Sk, Dk = k.shape
-    if tuple(v.shape) != (Bk, Hk, Sk, Dk) or Bk != B or Dk != D:
-        raise ValueError(f"shapes q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    _attn_check(((q, "q"), (k, "k"), (v, "v")), q)
+    B, H, Hk, Sq, Sk, D = _attn_shapes(q, k, v)
     if o is None:
         o = torch.empty_like(q, memory_format=torch.contiguous_format)
     _require_gpu(o, "o")
     if o.shape != q.shape or o.dtype != q.dtype or o.stride(-1) != 1:
         raise ValueError("o must have q's shape and dtype, last axis contiguous")
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device) if return_lse else None
-    mode = mask_mode_of(mask, (B, H, Sq, Sk))
-    mode_code = _lib.MASK_MODES[mode]
-    mptr = None
-    if mask is not None:
-        _require_gpu(mask, "mask")
-        kind = mask_kind_of(mask)
-        if kind == "additive" and mask.dtype != q.dtype:
-            raise TypeError("additive mask dtype must equal q's")
-        if kind == "lengths" and mask.dtype != torch.int32:
-            raise TypeError("key lengths must be int32")
-        if kind == "bool":
-            mode_code |= _lib.MASK_BOOL
-        if not mask.is_contiguous():
-            raise ValueError("mask must be contiguous in its own shape")
-        mptr = mask.data_ptr()
+    mptr, mode_code = _attn_mask(mask, q, (B, H, Sq, Sk))
     if scale is None:
         scale = 1.0 / float(D) ** 0.5
     L = _lib.lib()
@@ -268,6 +281,64 @@ def sms_attention_forward(q, k, v, mask=None, scale=None, is_causal=False, o=Non
             D, float(scale), causal_code(is_causal), s.cuda_stream)
     _lib.check("sms_attention_forward", st)
     return (o, lse) if return_lse else o
+
+
+def sms_attention_workspace_bytes(B, H, Sq):
+    """Bytes of device workspace ``sms_attention_backward`` needs (4 * B * H * Sq)."""
+    n = int(_lib.lib().sms_attention_workspace_bytes(int(B), int(H), int(Sq)))
+    if n < 0:
+        raise ValueError(f"invalid attention sizes B={B} H={H} Sq={Sq}")
+    return n
+
+
+def sms_attention_backward(q, k, v, o, lse, do, mask=None, scale=None, is_causal=False,
+                           dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """(dQ, dK, dV) of the fused attention (C ABI sms_attention_backward).
+
+    q, k, v, mask, scale, is_causal: as passed to ``sms_attention_forward``;
+    o and lse: its output and fp32 log-sum-exp; do: the upstream gradient
+    (q's shape and dtype). The probabilities are recomputed from lse. Outputs
+    are allocated unless given; ``workspace`` (a GPU tensor of at least
+    ``sms_attention_workspace_bytes(B, H, Sq)`` bytes) likewise.
+    """
+    _attn_check(((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")), q)
+    B, H, Hk, Sq, Sk, D = _attn_shapes(q, k, v)
+    if o.shape != q.shape or do.shape != q.shape:
+        raise ValueError("o and do must have q's shape")
+    _require_gpu(lse, "lse")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Sq) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, Sq] tensor")
+    outs = []
+    for t, like, n in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        if t is None:
+            t = torch.empty_like(like, memory_format=torch.contiguous_format)
+        _require_gpu(t, n)
+        if t.shape != like.shape or t.dtype != like.dtype or t.stride(-1) != 1:
+            raise ValueError(f"{n} must match its input's shape and dtype, last axis contiguous")
+        outs.append(t)
+    dq, dk, dv = outs
+    mptr, mode_code = _attn_mask(mask, q, (B, H, Sq, Sk))
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    L = _lib.lib()
+    need = sms_attention_workspace_bytes(B, H, Sq)
+    with torch.cuda.device(q.device):
+        s = _stream_of(q.device, stream)
+        if workspace is None and need > 0:
+            with torch.cuda.stream(s):
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        wptr, wbytes = None, 0
+        if workspace is not None:
+            _require_gpu(workspace, "workspace")
+            wptr, wbytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        st = L.sms_attention_backward(
+            q.data_ptr(), _strides(q), k.data_ptr(), _strides(k), v.data_ptr(), _strides(v),
+            o.data_ptr(), _strides(o), do.data_ptr(), _strides(do), lse.data_ptr(), mptr,
+            mode_code, dq.data_ptr(), _strides(dq), dk.data_ptr(), _strides(dk), dv.data_ptr(),
+            _strides(dv), _dtype_code(q, "q"), B, H, Hk, Sq, Sk, D, float(scale),
+            causal_code(is_causal), wptr, wbytes, s.cuda_stream)
+    _lib.check("sms_attention_backward", st)
+    return dq, dk, dv
 
 
 def sms_max_sk(dtype):
@@ -320,3 +391,40 @@ def scaled_mask_softmax(x, mask=None, scale=1.0, is_causal=False):
     "bottom_right".
     """
     return ScaledMaskSoftmaxFunction.apply(x, mask, scale, is_causal)
+
+
+class AttentionFunction(torch.autograd.Function):
+    """Autograd wrapper of the fused attention: forward saves q, k, v, O and
+    the log-sum-exp (no probabilities); backward returns (dQ, dK, dV, None...)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, mask, scale, is_causal):
+        if mask is not None:
+            if mask.dtype == torch.int64:  # key lengths: the C ABI takes int32
+                mask = mask.to(torch.int32)
+            if not mask.is_contiguous():
+                mask = mask.contiguous()
+        if scale is None:
+            scale = 1.0 / float(q.shape[-1]) ** 0.5
+        o, lse = sms_attention_forward(q, k, v, mask, scale, is_causal, return_lse=True)
+        ctx.scale = float(scale)
+        ctx.is_causal = causal_code(is_causal)
+        ctx.save_for_backward(q, k, v, o, lse, mask)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse, mask = ctx.saved_tensors
+        if do.stride(-1) != 1 or do.data_ptr() % 16:
+            do = do.contiguous()
+        dq, dk, dv = sms_attention_backward(q, k, v, o, lse, do, mask, ctx.scale, ctx.is_causal)
+        return dq, dk, dv, None, None, None
+
+
+def attention(q, k, v, mask=None, scale=None, is_causal=False):
+    """softmax(Q K^T * scale + mask) V on the fused kernels, differentiable in q, k and v.
+
+    Shapes and mask forms as for ``sms_attention_forward``; ``scale`` defaults
+    to 1/sqrt(D).
+    """
+    return AttentionFunction.apply(q, k, v, mask, scale, is_causal)

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SMS_ABI_VERSION 4
+#define SMS_ABI_VERSION 5
 
 typedef enum {
   SMS_OK = 0,
@@ -243,8 +243,10 @@ sms_status sms_backward_ws(const void* y, const int64_t y_strides[4],
  *
  * Every row of q, k, v and o must start on a 16-byte boundary (base 16-byte
  * aligned, strides multiples of 8 elements; else SMS_ERR_ALIGN); the head dim
- * is contiguous (stride[3] == 1). Limits: ceil(Sq / 128) * H * B < 2^31.
- * Forward only.
+ * is contiguous (stride[3] == 1). With Sk == 0, k, v and a mask other than
+ * key lengths are never read and may be NULL. Limits: Sq, Sk < 2^31 and
+ * ceil(Sq / 128) * H * B < 2^24 (one 256-thread workgroup per 128 queries of a
+ * head; else SMS_ERR_SHAPE). The backward is sms_attention_backward.
  */
 sms_status sms_attention_forward(const void* q, const int64_t q_strides[4],
                                  const void* k, const int64_t k_strides[4],
@@ -254,6 +256,63 @@ sms_status sms_attention_forward(const void* q, const int64_t q_strides[4],
                                  sms_dtype dtype, int64_t B, int64_t H, int64_t Hk,
                                  int64_t Sq, int64_t Sk, int64_t D,
                                  float scale, int is_causal, void* stream);
+
+/*
+ * sms_attention_workspace_bytes -- bytes of device workspace
+ * sms_attention_backward needs: 4 * B * H * Sq (one fp32 per query row); -1
+ * for negative or oversized arguments.
+ */
+int64_t sms_attention_workspace_bytes(int64_t B, int64_t H, int64_t Sq);
+
+/*
+ * sms_attention_backward -- gradients of the fused attention forward,
+ *
+ *     dV = P^T dO,  dP = dO V^T,  dS = scale * P * (dP - rowsum(dO * O)),
+ *     dQ = dS K,    dK = dS^T Q
+ *
+ * for P = softmax(Q K^T * scale + mask): the probabilities are recomputed from
+ * Q, K and the forward's log-sum-exp (never stored), FlashAttention-style, the
+ * scheme the pnsm.cn ScaledMaskSoftmax article, sec. 4.4, points to; the dS
+ * step is the softmax gradient of the lmnt.cn custom-softmax page, sec. 3.3,
+ * with sum_j dP_j P_j computed as rowsum(dO * O). A key/value head shared by
+ * several query heads receives the sum of their contributions. Deterministic:
+ * no atomics, every gradient element written once (zeros where no visible
+ * score reaches it).
+ *
+ *   q, k, v, mask, mask_mode, dtype, B, H, Hk, Sq, Sk, D, scale, is_causal
+ *                  exactly as passed to sms_attention_forward
+ *   o, o_strides   the forward's output O [B, H, Sq, D]
+ *   dout, dout_strides   upstream gradient dO [B, H, Sq, D] (dtype)
+ *   lse            the forward's fp32 log-sum-exp [B, H, Sq], contiguous
+ *                  (may be NULL only when Sq == 0)
+ *   dq, dk, dv (+ strides)   outputs [B, H, Sq, D], [B, Hk, Sk, D],
+ *                  [B, Hk, Sk, D] (dtype), fp32-accumulated and rounded once;
+ *                  they must not overlap the inputs
+ *   workspace, workspace_bytes   device memory of at least
+ *                  sms_attention_workspace_bytes(B, H, Sq) bytes, 4-byte
+ *                  aligned, owned by the caller and not used by any call that
+ *                  may run at the same time (else SMS_ERR_WORKSPACE); its
+ *                  contents on entry do not matter
+ *   stream         hipStream_t to enqueue on (three kernel launches)
+ *
+ * Row alignment and limits as for sms_attention_forward, and also
+ * ceil(Sk / 128) * Hk * B < 2^24. Pointers to tensors over queries (q, o,
+ * dout, lse, dq) may be NULL when Sq == 0, those over keys (k, v, dk, dv)
+ * when Sk == 0, and a mask other than key lengths when either is 0.
+ */
+sms_status sms_attention_backward(const void* q, const int64_t q_strides[4],
+                                  const void* k, const int64_t k_strides[4],
+                                  const void* v, const int64_t v_strides[4],
+                                  const void* o, const int64_t o_strides[4],
+                                  const void* dout, const int64_t dout_strides[4],
+                                  const float* lse, const void* mask, int mask_mode,
+                                  void* dq, const int64_t dq_strides[4],
+                                  void* dk, const int64_t dk_strides[4],
+                                  void* dv, const int64_t dv_strides[4],
+                                  sms_dtype dtype, int64_t B, int64_t H, int64_t Hk,
+                                  int64_t Sq, int64_t Sk, int64_t D, float scale,
+                                  int is_causal, void* workspace, int64_t workspace_bytes,
+                                  void* stream);
 
 /* Largest key length Sk the library runs for `dtype` (2^30; 0 for an unknown
  * dtype). */

@@ -60,35 +60,75 @@ def _decode4(a, dtype):
     return S.decode(a, dtype)
 
 
-def forward(q, k, v, dtype, mask=None, scale=1.0, is_causal=False, mask_kind="additive",
-            key_lengths=None):
-    """(O, LSE) of the fused attention forward, in float64."""
+def _prepare(q, k, v, dtype, mask, mask_kind):
     qd, kd, vd = _decode4(q, dtype), _decode4(k, dtype), _decode4(v, dtype)
     B, H, Sq, D = qd.shape
     Bk, Hk, Sk, Dk = kd.shape
-    Dv = vd.shape[3]
     if vd.shape[:3] != kd.shape[:3] or Bk != B or Dk != D:
         raise ValueError(f"shapes q {qd.shape}, k {kd.shape}, v {vd.shape} do not match")
     S._check_mask_shape(mask, (B, H, Sq, Sk))
-    off = S.causal_offset(is_causal, Sq, Sk)
     maskd = None
     if mask is not None:
         maskd = S.decode(mask, dtype) if mask_kind == "additive" else np.asarray(mask)
+    return qd, kd, vd, maskd
+
+
+def _head_probabilities(qh, kh, maskd, b, h, sc, off, mask_kind, key_lengths):
+    """(P, LSE) of one (batch, head): the scaled-masked softmax of each row of
+    S = Q K^T, by the softmax oracle's score rule and normalisation."""
+    scores = head_scores(qh, kh)  # [Sq, Sk]
+    Sq, Sk = scores.shape
+    P = np.empty((Sq, Sk), dtype=np.float64)
+    LSE = np.empty(Sq, dtype=np.float64)
+    for i in range(Sq):
+        mrow = S._mask_row(maskd, b, h, i) if maskd is not None else None
+        add = mrow if mask_kind == "additive" else None
+        ex = S._excluded(Sk, mrow if mask_kind == "bool" else None,
+                         key_lengths[b] if key_lengths is not None else None)
+        s = S._scores_one_row(scores[i], add, sc, off is not None, i, ex, off or 0)
+        P[i], LSE[i] = S._softmax_and_lse(s)
+    return P, LSE
+
+
+def probabilities(q, k, dtype, mask=None, scale=1.0, is_causal=False, mask_kind="additive",
+                  key_lengths=None):
+    """(P, LSE): P [B, H, Sq, Sk] = softmax(Q K^T * scale + mask) over keys, in
+    float64, and its log-sum-exp [B, H, Sq]."""
+    qd, kd = _decode4(q, dtype), _decode4(k, dtype)
+    B, H, Sq, D = qd.shape
+    Hk, Sk = kd.shape[1], kd.shape[2]
+    if kd.shape[0] != B or kd.shape[3] != D:
+        raise ValueError(f"shapes q {qd.shape}, k {kd.shape} do not match")
+    S._check_mask_shape(mask, (B, H, Sq, Sk))
+    maskd = None
+    if mask is not None:
+        maskd = S.decode(mask, dtype) if mask_kind == "additive" else np.asarray(mask)
+    off = S.causal_offset(is_causal, Sq, Sk)
+    sc = S._fp32(scale)
+    P = np.empty((B, H, Sq, Sk), dtype=np.float64)
+    LSE = np.empty((B, H, Sq), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            P[b, h], LSE[b, h] = _head_probabilities(qd[b, h], kd[b, kv_head(h, H, Hk)], maskd,
+                                                     b, h, sc, off, mask_kind, key_lengths)
+    return P, LSE
+
+
+def forward(q, k, v, dtype, mask=None, scale=1.0, is_causal=False, mask_kind="additive",
+            key_lengths=None):
+    """(O, LSE) of the fused attention forward, in float64."""
+    qd, kd, vd, maskd = _prepare(q, k, v, dtype, mask, mask_kind)
+    B, H, Sq, D = qd.shape
+    Hk, Sk, Dv = kd.shape[1], kd.shape[2], vd.shape[3]
+    off = S.causal_offset(is_causal, Sq, Sk)
     sc = S._fp32(scale)
     O = np.zeros((B, H, Sq, Dv), dtype=np.float64)
     LSE = np.empty((B, H, Sq), dtype=np.float64)
     for b in range(B):
         for h in range(H):
             g = kv_head(h, H, Hk)
-            scores = head_scores(qd[b, h], kd[b, g])  # [Sq, Sk]
-            P = np.empty((Sq, Sk), dtype=np.float64)
-            for i in range(Sq):
-                mrow = S._mask_row(maskd, b, h, i) if maskd is not None else None
-                add = mrow if mask_kind == "additive" else None
-                ex = S._excluded(Sk, mrow if mask_kind == "bool" else None,
-                                 key_lengths[b] if key_lengths is not None else None)
-                s = S._scores_one_row(scores[i], add, sc, off is not None, i, ex, off or 0)
-                P[i], LSE[b, h, i] = S._softmax_and_lse(s)
+            P, LSE[b, h] = _head_probabilities(qd[b, h], kd[b, g], maskd, b, h, sc, off,
+                                               mask_kind, key_lengths)
             O[b, h] = combine(P, vd[b, g])
     return O, LSE
 
@@ -103,15 +143,11 @@ def backward(q, k, v, do, dtype, mask=None, scale=1.0, is_causal=False, mask_kin
     the scale entering as the derivative of S * scale); dQ = dS K; dK = dS^T Q.
     Key/value heads shared by several query heads sum their contributions.
     """
-    qd, kd, vd = _decode4(q, dtype), _decode4(k, dtype), _decode4(v, dtype)
+    qd, kd, vd, maskd = _prepare(q, k, v, dtype, mask, mask_kind)
     dod = _decode4(do, dtype)
     B, H, Sq, D = qd.shape
     Hk, Sk = kd.shape[1], kd.shape[2]
-    S._check_mask_shape(mask, (B, H, Sq, Sk))
     off = S.causal_offset(is_causal, Sq, Sk)
-    maskd = None
-    if mask is not None:
-        maskd = S.decode(mask, dtype) if mask_kind == "additive" else np.asarray(mask)
     sc = S._fp32(scale)
     dQ = np.zeros(qd.shape)
     dK = np.zeros(kd.shape)
@@ -119,19 +155,13 @@ def backward(q, k, v, do, dtype, mask=None, scale=1.0, is_causal=False, mask_kin
     for b in range(B):
         for h in range(H):
             g = kv_head(h, H, Hk)
-            scores = head_scores(qd[b, h], kd[b, g])
-            P = np.empty((Sq, Sk))
-            for i in range(Sq):
-                mrow = S._mask_row(maskd, b, h, i) if maskd is not None else None
-                add = mrow if mask_kind == "additive" else None
-                ex = S._excluded(Sk, mrow if mask_kind == "bool" else None,
-                                 key_lengths[b] if key_lengths is not None else None)
-                s = S._scores_one_row(scores[i], add, sc, off is not None, i, ex, off or 0)
-                P[i] = S._softmax_and_lse(s)[0]
+            P, _ = _head_probabilities(qd[b, h], kd[b, g], maskd, b, h, sc, off, mask_kind,
+                                       key_lengths)
             dV[b, g] += P.T @ dod[b, h]
             dP = dod[b, h] @ vd[b, g].T
-            dS = np.stack([S._backward_one_row(P[i], dP[i], sc) for i in range(Sq)])
+            dS = np.zeros((Sq, Sk))
+            for i in range(Sq):
+                dS[i] = S._backward_one_row(P[i], dP[i], sc)
             dQ[b, h] = dS @ kd[b, g]
             dK[b, g] += dS.T @ qd[b, h]
     return dQ, dK, dV
-

@@ -490,6 +490,14 @@ def pin_attention_brute_force():
         Ob, Lb = _attn_brute(q, k, v, float(np.float32(0.6)), off)
         _close(O, Ob, atol=1e-14, rtol=1e-12, what=f"brute O {causal}")
         _close(L, Lb, atol=1e-14, rtol=1e-12, what=f"brute LSE {causal}")
+        # The probabilities themselves: P V is the brute-force output, the
+        # log-sum-exp is the brute-force one, and every row sums to 1.
+        P, LP = A.probabilities(q, k, "f64", scale=0.6, is_causal=causal)
+        _close(LP, Lb, atol=1e-14, rtol=1e-12, what=f"probabilities LSE {causal}")
+        _close(P.sum(axis=3), np.ones((B, H, Sq)), atol=1e-14, what="probability rows")
+        PV = np.stack([np.stack([P[b, h] @ v[b, h // (H // Hk)] for h in range(H)])
+                       for b in range(B)])
+        _close(PV, Ob, atol=1e-14, rtol=1e-12, what=f"probabilities P V {causal}")
 
 
 def pin_attention_invariants():
@@ -581,6 +589,9 @@ def pin_attention_backward_structure():
     _close(dq1, dq2, rtol=0, what="GQA dQ")
     _close(dk1[:, 0], dk2.sum(axis=1), atol=1e-14, rtol=1e-14, what="GQA dK")
     _close(dv1[:, 0], dv2.sum(axis=1), atol=1e-14, rtol=1e-14, what="GQA dV")
+    # No query: no gradient reaches K or V.
+    dq0, dk0, dv0 = A.backward(q[:, :, :0], k, v, do[:, :, :0], "f32", scale=0.3)
+    assert dq0.shape == (2, 2, 0, 4) and not dk0.any() and not dv0.any()
 
 
 ATTENTION_PINS = [pin_attention_one_and_two_keys, pin_attention_equal_scores,

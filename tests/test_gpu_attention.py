@@ -1,7 +1,7 @@
-"""Fused attention forward (C ABI sms_attention_forward) against the float64
-oracle (oracle.attention), element by element, with the tolerance derived in
-tests/tolerance.py; masks, causal rules, grouped heads, tails, strides,
-errors."""
+"""Fused attention forward and backward (C ABI sms_attention_forward /
+sms_attention_backward) against the float64 oracle (oracle.attention), element
+by element, with the tolerances derived in tests/tolerance.py; masks, causal
+rules, grouped heads, tails, strides, empty sizes, autograd, errors."""
 
 import sys
 import zlib
@@ -11,10 +11,11 @@ import pytest
 import torch
 
 import oracle
-from attention_softmax_amd import SmsError, sms_attention_forward
+from attention_softmax_amd import (SmsError, attention, sms_attention_backward,
+                                   sms_attention_forward, sms_attention_workspace_bytes)
 from attention_softmax_amd.workloads import TORCH_DTYPE, draw_lengths, draw_mask, draw_x
 from tests.parity import DTYPE_OF, mask_4d, to_np
-from tests.tolerance import compare_attention
+from tests.tolerance import attention_grad_tolerances, compare_attention, compare_grads
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -130,3 +131,170 @@ def test_attention_errors():
         sms_attention_forward(big, q, q)
     empty = torch.zeros(1, 1, 0, 64, dtype=torch.float16, device=DEV)
     sms_attention_forward(empty, q, q)  # no query: a no-op
+
+
+# ------------------------------------------------------------------ backward
+
+def check_bwd(q, k, v, mask, mode, kind, scale, causal, what, seed, do=None, chain=False):
+    """The GPU backward against the oracle's gradients; returns the worst
+    elementwise error / tolerance over dQ, dK, dV.
+
+    The backward is given the oracle's O rounded to the I/O dtype and its LSE
+    rounded to fp32 (so the tolerance knows their deviation exactly), or with
+    ``chain`` the GPU forward's O and LSE (tolerance from the forward's bound)."""
+    dt = DTYPE_OF[q.dtype]
+    okind = {"bool": "bool", "lengths": "lengths"}.get(kind, "additive")
+    kw = dict(mask=None if kind in ("none", "lengths") else mask_4d(mask, mode),
+              scale=scale, is_causal=causal, mask_kind=okind,
+              key_lengths=to_np(mask) if kind == "lengths" else None)
+    if do is None:
+        do = draw_x(tuple(q.shape), dt, ("normal", 1.0), seed, DEV)
+    qn, kn, vn, don = (to_np(t.contiguous()) for t in (q, k, v, do))
+    refs = oracle.attention.backward(qn, kn, vn, don, dt, **kw)
+    P, ref_lse = oracle.attention.probabilities(qn, kn, dt, **kw)
+    o_ref, _ = oracle.attention.forward(qn, kn, vn, dt, **kw)
+    if chain:
+        o, lse = sms_attention_forward(q, k, v, mask, scale, causal, return_lse=True)
+        o_in = lse_in = None
+    else:
+        o = torch.from_numpy(o_ref).to(DEV).to(q.dtype)
+        lse = torch.from_numpy(ref_lse).to(DEV).to(torch.float32)
+        o_in = oracle.decode(to_np(o), dt)
+        lse_in = to_np(lse).astype(np.float64)
+    dq, dk, dv = sms_attention_backward(q, k, v, o, lse, do, mask, scale, causal)
+    torch.cuda.synchronize()
+    qd, kd, vd, dod = (oracle.decode(a, dt) for a in (qn, kn, vn, don))
+    B, H = q.shape[:2]
+    group = H // k.shape[1]
+    vrep = np.repeat(vd, group, axis=1)
+    dP = dod @ np.swapaxes(vrep, 2, 3)
+    vmax = np.abs(vrep).max(axis=(2, 3)) if vrep.size else np.zeros((B, H))
+    tols, rms = attention_grad_tolerances(P, dP, qd, kd, dod, vmax, ref_lse,
+                                          float(np.float32(scale)), dt, refs, o_in, o_ref, lse_in)
+    worst = 0.0
+    for name, got, ref, tol, rm in zip(("dQ", "dK", "dV"), (dq, dk, dv), refs, tols, rms):
+        worst = max(worst, compare_grads(oracle.decode(to_np(got.contiguous()), dt), ref, tol,
+                                         f"{what} {name}", rm))
+    return worst
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Sq,Sk", SHAPES)
+def test_attention_backward_sweep(dtype, D, Sq, Sk):
+    """dQ, dK, dV for every mask shape and kind and causal rule on tails of the
+    tiles (128 queries of the dQ kernel, 128 keys of the dK/dV kernel, 64-key
+    and 32-query inner tiles), grouped heads (H = 4 over Hk = 2)."""
+    say(f"attention backward dtype={dtype} D={D} Sq={Sq} Sk={Sk}")
+    B, H, Hk = 2, 4, 2
+    worst = 0.0
+    for mode, kind in MASKS:
+        for causal in (False, True, "bottom_right"):
+            seed = zlib.crc32(f"ab/{dtype}/{D}/{Sq}/{Sk}/{mode}/{kind}/{causal}".encode()) % 10000
+            q = draw_x((B, H, Sq, D), dtype, ("normal", 1.0), seed, DEV)
+            k = draw_x((B, Hk, Sk, D), dtype, ("normal", 1.0), seed + 1, DEV)
+            v = draw_x((B, Hk, Sk, D), dtype, ("normal", 1.0), seed + 2, DEV)
+            mask = make_mask((B, H, Sq, Sk), mode, kind, dtype, seed + 3)
+            w = check_bwd(q, k, v, mask, mode, kind, D ** -0.5, causal,
+                          f"bwd {dtype} D={D} {Sq}x{Sk} {mode}/{kind} causal={causal}", seed + 4)
+            worst = max(worst, w)
+    say(f"  worst error / tolerance {worst:.3f}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_attention_backward_strided_mha_and_scale(dtype):
+    """Q, K, V, dO as [B, S, H, D] storage viewed as [B, H, S, D], gradients
+    written into strided views; plain multi-head (Hk = H) and 8 query heads on
+    one key/value head; scale 1."""
+    say(f"attention backward strided dtype={dtype}")
+    B, H, Sq, Sk, D = 2, 3, 150, 170, 64
+    td = TORCH_DTYPE[dtype]
+    q = draw_x((B, Sq, H, D), dtype, ("normal", 1.0), 11, DEV).permute(0, 2, 1, 3)
+    k = draw_x((B, Sk, H, D), dtype, ("normal", 1.0), 12, DEV).permute(0, 2, 1, 3)
+    v = draw_x((B, Sk, H, D), dtype, ("normal", 1.0), 13, DEV).permute(0, 2, 1, 3)
+    do = draw_x((B, Sq, H, D), dtype, ("normal", 1.0), 14, DEV).permute(0, 2, 1, 3)
+    o, lse = sms_attention_forward(q, k, v, None, 0.25, True, return_lse=True)
+    bufs = [torch.full((B, S, H, D), 7.0, dtype=td, device=DEV) for S in (Sq, Sk, Sk)]
+    dq, dk, dv = (t.permute(0, 2, 1, 3) for t in bufs)
+    sms_attention_backward(q, k, v, o, lse, do, None, 0.25, True, dq=dq, dk=dk, dv=dv)
+    rq, rk, rv = sms_attention_backward(q.contiguous(), k.contiguous(), v.contiguous(),
+                                        o.contiguous(), lse, do.contiguous(), None, 0.25, True)
+    torch.cuda.synchronize()
+    for a, b_, n in ((dq, rq, "dQ"), (dk, rk, "dK"), (dv, rv, "dV")):
+        assert torch.equal(a.contiguous(), b_), f"strided {n} differs from contiguous"
+    check_bwd(q.contiguous(), k.contiguous(), v.contiguous(), None, "none", "none", 0.25, True,
+              "strided", 0, do=do.contiguous())
+    q8 = draw_x((1, 8, 97, 128), dtype, ("normal", 1.0), 15, DEV)
+    k1 = draw_x((1, 1, 300, 128), dtype, ("normal", 1.0), 16, DEV)
+    v1 = draw_x((1, 1, 300, 128), dtype, ("normal", 1.0), 17, DEV)
+    check_bwd(q8, k1, v1, None, "none", "none", 1.0, False, "8 heads on 1, scale 1", 18)
+
+
+def test_attention_backward_long_causal():
+    """fp16 [1, 2, 1024, 1024], D = 128, causal, every gradient element; once
+    from the oracle's O and LSE, once from the GPU forward's."""
+    say("attention backward 1024 x 1024")
+    q = draw_x((1, 2, 1024, 128), "f16", ("normal", 1.0), 21, DEV)
+    k = draw_x((1, 2, 1024, 128), "f16", ("normal", 1.0), 22, DEV)
+    v = draw_x((1, 2, 1024, 128), "f16", ("normal", 1.0), 23, DEV)
+    w = check_bwd(q, k, v, None, "none", "none", 128 ** -0.5, True, "1024 causal", 24)
+    w2 = check_bwd(q, k, v, None, "none", "none", 128 ** -0.5, True, "1024 causal chain", 24,
+                   chain=True)
+    say(f"  worst error / tolerance {w:.3f}, from the GPU forward {w2:.3f}")
+
+
+def test_attention_backward_empty_sides():
+    """No key: dQ = 0 and nothing else; no query: dK = dV = 0."""
+    say("attention backward empty sides")
+    q = draw_x((1, 2, 40, 64), "bf16", ("normal", 1.0), 31, DEV)
+    k0 = torch.empty((1, 2, 0, 64), dtype=torch.bfloat16, device=DEV)
+    o, lse = sms_attention_forward(q, k0, k0, None, 0.125, False, return_lse=True)
+    assert (o == 0).all() and (lse == -float("inf")).all()
+    dq = torch.full_like(q, 3.0)
+    sms_attention_backward(q, k0, k0, o, lse, q, None, 0.125, False, dq=dq)
+    torch.cuda.synchronize()
+    assert (dq == 0).all()
+    k = draw_x((1, 2, 70, 64), "bf16", ("normal", 1.0), 32, DEV)
+    q0 = torch.empty((1, 2, 0, 64), dtype=torch.bfloat16, device=DEV)
+    lse0 = torch.empty((1, 2, 0), dtype=torch.float32, device=DEV)
+    dk, dv = torch.full_like(k, 3.0), torch.full_like(k, 3.0)
+    sms_attention_backward(q0, k, k, q0, lse0, q0, None, 0.125, True, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert (dk == 0).all() and (dv == 0).all()
+
+
+def test_attention_autograd():
+    """attention() under autograd: the gradients are the backward entry
+    point's, bit for bit, and agree with the oracle."""
+    say("attention autograd")
+    q = draw_x((2, 4, 77, 64), "f16", ("normal", 1.0), 41, DEV).requires_grad_()
+    k = draw_x((2, 2, 90, 64), "f16", ("normal", 1.0), 42, DEV).requires_grad_()
+    v = draw_x((2, 2, 90, 64), "f16", ("normal", 1.0), 43, DEV).requires_grad_()
+    do = draw_x((2, 4, 77, 64), "f16", ("normal", 1.0), 44, DEV)
+    lengths = torch.tensor([50, 90], dtype=torch.int64, device=DEV)
+    o = attention(q, k, v, lengths, None, True)
+    o.backward(do)
+    o2, lse = sms_attention_forward(q.detach(), k.detach(), v.detach(),
+                                    lengths.to(torch.int32), 64 ** -0.5, True, return_lse=True)
+    gq, gk, gv = sms_attention_backward(q.detach(), k.detach(), v.detach(), o2, lse, do,
+                                        lengths.to(torch.int32), 64 ** -0.5, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), o2)
+    for a, b_ in ((q.grad, gq), (k.grad, gk), (v.grad, gv)):
+        assert torch.equal(a, b_)
+    check_bwd(q.detach(), k.detach(), v.detach(), lengths.to(torch.int32), "key_lengths",
+              "lengths", 64 ** -0.5, True, "autograd case", 0, do=do, chain=True)
+
+
+def test_attention_backward_errors():
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.float16, device=DEV)
+    lse = torch.zeros(1, 1, 4, dtype=torch.float32, device=DEV)
+    assert sms_attention_workspace_bytes(2, 3, 5) == 4 * 2 * 3 * 5
+    with pytest.raises(SmsError, match="WORKSPACE"):
+        ws = torch.empty(8, dtype=torch.uint8, device=DEV)
+        sms_attention_backward(q, q, q, q, lse, q, workspace=ws)
+    with pytest.raises(SmsError, match="SHAPE"):  # head dim 96
+        z = torch.zeros(1, 1, 4, 96, dtype=torch.float16, device=DEV)
+        sms_attention_backward(z, z, z, z, lse, z)
+    with pytest.raises(ValueError):  # lse of the wrong shape
+        sms_attention_backward(q, q, q, q, lse[..., :3], q)

@@ -1,0 +1,46 @@
+"""The fused attention kernels' device assembly, compiled with the build's
+flags, has no read of a matrix-core (MFMA) result fewer wait states after the
+MFMA than the hardware needs, including across loop back edges
+(attention_softmax_amd.isa_check). CPU only: hipcc cross-compiles."""
+
+import os
+import shutil
+
+import pytest
+
+from attention_softmax_amd import build, isa_check
+
+pytestmark = pytest.mark.skipif(not os.path.exists(build.hipcc()), reason="hipcc not installed")
+
+
+def test_checker_finds_a_loop_carried_early_read():
+    """A read at a loop head 3 wait states after the MFMA at the loop's end is
+    found; the same read behind 8 more wait states, or after a rewrite of the
+    register, is not."""
+    early = """_Zk:
+\tv_mov_b32 v0, 0
+.LBB0_1:
+\tv_accvgpr_read_b32 v20, a15
+\tv_mfma_f32_32x32x16_f16 a[0:15], v[0:3], v[4:7], a[0:15]
+\ts_add_u32 s0, s0, 1
+\ts_cmp_lg_u32 s0, s1
+\ts_cbranch_scc1 .LBB0_1
+\ts_endpgm
+.Lfunc_end0:
+"""
+    found = isa_check.check_text(early)
+    assert list(found) == ["_Zk"] and found["_Zk"][0][2] == 3
+    padded = early.replace("\ts_cbranch_scc1", "\ts_nop 7\n\ts_cbranch_scc1")
+    assert not isa_check.check_text(padded)
+    rewritten = early.replace("\ts_cmp_lg_u32", "\tv_mov_b32 v99, 0\n\tv_accvgpr_write_b32 a15, v99\n"
+                              "\ts_cmp_lg_u32")
+    assert not isa_check.check_text(rewritten)
+
+
+@pytest.mark.parametrize("src", ["attention.hip", "attention_bwd.hip"])
+def test_attention_kernels_have_no_early_mfma_reads(src, tmp_path):
+    out = build.device_asm(src, str(tmp_path / (src + ".s")))
+    with open(out) as fh:
+        found = isa_check.check_text(fh.read())
+    assert not found, {k: v[:2] for k, v in found.items()}
+    shutil.rmtree(tmp_path, ignore_errors=True)

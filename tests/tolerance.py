@@ -115,3 +115,119 @@ def compare_attention(got_o, ref_o, vmax, dtype, what="", got_lse=None, ref_lse=
         assert (d <= ltol).all(), f"{what}: LSE off by {d.max():.3g}"
         stats["lse_max_abs"] = float(d.max()) if d.size else 0.0
     return stats
+
+
+# -------------------------------------------------- fused attention backward
+#
+# The backward takes O (dtype T) and the fp32 LSE as inputs, recomputes
+# P = exp(s*scale + mask - LSE) in fp32, takes delta_i = sum_d dO_id O_id,
+# forms dS = P (dP - delta) with dP = dO V^T in fp32, rounds P and dS to T for
+# the products dV = P^T dO, dQ = scale dS K, dK = scale dS^T Q (fp32
+# accumulation), and rounds the results to T once. Given O_in and LSE_in, the
+# first-order error terms per element, with the oracle's exact P, dP, delta:
+#  * P's relative error E_ij: the LSE input's deviation |LSE_in - LSE| plus
+#    fp32 rounding of the exponent (2^-22 (1 + |LSE_i| + |z_ij|), z the masked
+#    scaled score) and of the score sum (D 2^-24 scale (|Q||K|^T)_ij);
+#  * delta's absolute error e_i: |sum_d dO_id (O_in - O)_id| plus the fp32
+#    sums of delta and dP (D 2^-24 (|dO_i|.|O_in,i| + ||dO_i||_1 max|v|));
+#  * rounding P or dS to T: relative u_T; fp32 accumulation over n terms:
+#    n 2^-24 relative to the sum of absolute values (n = Sk for dQ,
+#    Sq * group for dK and dV); the final rounding: half an ulp.
+# Elementwise (worst case, every rounding error aligned), summed over the
+# query heads that share a key/value head, the bound allows twice
+#   dQ_id:  scale [ (u + gk) (|dS||K|)_id + ((|dS| o E)|K|)_id + e_i (P|K|)_id ]
+#   dK_jd:  scale [ (u + gq) (|dS|^T|Q|)_jd + ((|dS| o E)^T|Q|)_jd + (P^T (e o |Q|))_jd ]
+#   dV_jd:  (u + gq) (P^T|dO|)_jd + ((P o E)^T|dO|)_jd
+# plus 2 ulp_T of the reference value. With cancellation in the sums this is
+# loose (a 1% error in dQ can hide under it), so a second bound applies to
+# the whole tensor: the rounding errors of P and dS are independent from
+# element to element, so their contribution to ||err||_F is at most
+# u sqrt(sum (dS^2 K^2)) (etc.) in expectation; the test allows three times
+# the root-sum-square of that and of the final rounding (u |ref|), plus twice
+# the Frobenius norm of the remaining (systematic) terms.
+
+
+def attention_grad_tolerances(P, dP, q, k, do, vmax, lse, scale, dtype, refs, o_in=None,
+                              o_ref=None, lse_in=None):
+    """(elementwise tolerances (tol_dq, tol_dk, tol_dv), Frobenius bounds
+    (rms_dq, rms_dk, rms_dv)) of the attention backward.
+
+    P, dP [B, H, Sq, Sk] (oracle, float64; dP = dO V^T per query head),
+    q/do [B, H, Sq, D], k [B, Hk, Sk, D], vmax [B, H] (max |v| over the head's
+    keys), lse [B, H, Sq] (oracle), refs = oracle (dQ, dK, dV). o_in / lse_in:
+    the O and LSE the backward was given, o_ref: the oracle's O; without them
+    O_in is only known to satisfy the forward's bound 2 u max|v| + 2 ulp(O)
+    (<= 6 u max|v|) and LSE_in its 2^-18 (1 + |LSE|)."""
+    u = ATTN_U[dtype]
+    B, H, Sq, Sk = P.shape
+    Hk, D = k.shape[1], k.shape[3]
+    group = H // Hk
+    gk, gq = Sk * 2.0 ** -24, Sq * group * 2.0 ** -24
+    aq, ak, ado = np.abs(q), np.abs(k), np.abs(do)
+    shape_v = k.shape[:3] + (do.shape[3],)
+    # w*: aligned rounding of P / dS (u times sums of absolute values);
+    # s*: the other (systematic) terms; r*: expected squared rounding error.
+    wq, sq_, rq = np.zeros(q.shape), np.zeros(q.shape), np.zeros(q.shape)
+    wk, sk_, rk = np.zeros(k.shape), np.zeros(k.shape), np.zeros(k.shape)
+    wv, sv_, rv = np.zeros(shape_v), np.zeros(shape_v), np.zeros(shape_v)
+    for b in range(B):
+        for h in range(H):
+            g = h // group
+            p = P[b, h]
+            fin = np.isfinite(lse[b, h])
+            lz = np.where(fin, np.abs(lse[b, h]), 0.0)
+            lsef = np.where(fin, lse[b, h], 0.0)
+            delta = (p * dP[b, h]).sum(axis=1)
+            ads = p * np.abs(dP[b, h] - delta[:, None])
+            live = p > 0
+            z = np.where(live, np.abs(np.log(np.where(live, p, 1.0)) + lsef[:, None]), 0.0)
+            qk = scale * (aq[b, h] @ ak[b, g].T)
+            if lse_in is None:
+                dl = 2.0 ** -18 * (1 + lz)
+            else:
+                dl = np.where(fin, np.abs(np.where(fin, lse_in[b, h], 0.0) - lsef), 0.0)
+            E = (dl + 2.0 ** -22 * (1 + lz))[:, None] + 2.0 ** -22 * z + (D + 4) * 2.0 ** -24 * qk
+            l1 = ado[b, h].sum(axis=1)
+            if o_in is None:
+                e = l1 * vmax[b, h] * (6 * u + 2 * D * 2.0 ** -24)
+            else:
+                e = (np.abs((do[b, h] * (o_in[b, h] - o_ref[b, h])).sum(axis=1))
+                     + D * 2.0 ** -24 * ((ado[b, h] * np.abs(o_in[b, h])).sum(axis=1)
+                                         + l1 * vmax[b, h]))
+            wq[b, h] = u * scale * (ads @ ak[b, g])
+            wk[b, g] += u * scale * (ads.T @ aq[b, h])
+            wv[b, g] += u * (p.T @ ado[b, h])
+            sq_[b, h] = scale * (gk * (ads @ ak[b, g]) + (ads * E) @ ak[b, g]
+                                 + e[:, None] * (p @ ak[b, g]))
+            sk_[b, g] += scale * (gq * (ads.T @ aq[b, h]) + (ads * E).T @ aq[b, h]
+                                  + p.T @ (e[:, None] * aq[b, h]))
+            sv_[b, g] += gq * (p.T @ ado[b, h]) + (p * E).T @ ado[b, h]
+            rq[b, h] = (u * scale) ** 2 * ((ads ** 2) @ (ak[b, g] ** 2))
+            rk[b, g] += (u * scale) ** 2 * ((ads ** 2).T @ (aq[b, h] ** 2))
+            rv[b, g] += u ** 2 * ((p ** 2).T @ (ado[b, h] ** 2))
+    refs = [np.asarray(r, dtype=np.float64) for r in refs]
+    tols = tuple(2 * (w + s_) + 2 * ulp(r, dtype)
+                 for w, s_, r in zip((wq, wk, wv), (sq_, sk_, sv_), refs))
+    rms = tuple(3 * np.sqrt(rr.sum() + ((u * r) ** 2).sum()) + 2 * np.sqrt((s_ ** 2).sum())
+                for rr, s_, r in zip((rq, rk, rv), (sq_, sk_, sv_), refs))
+    return tols, rms
+
+
+def compare_grads(got, ref, tol, what="", rms=None):
+    """Raise unless |got - ref| <= tol everywhere and, if given, the Frobenius
+    norm of got - ref is at most ``rms``; returns max(err / tol)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    r = err / tol
+    if r.size and (r > 1).any():
+        i = np.argmax(r)
+        raise AssertionError(f"{what}: {int((r > 1).sum())} elements beyond tolerance; worst at "
+                             f"{np.unravel_index(i, got.shape)}: got {got.flat[i]!r} want "
+                             f"{ref.flat[i]!r} tol {tol.flat[i]:.3g}")
+    if rms is not None:
+        f = float(np.sqrt((err ** 2).sum()))
+        assert f <= rms, f"{what}: ||err||_F = {f:.4g} above its bound {rms:.4g}"
+    return float(r.max()) if r.size else 0.0
