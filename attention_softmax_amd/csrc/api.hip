@@ -150,6 +150,28 @@ bool choose_plan(int64_t nvec, bool backward, bool causal, Plan& out) {
   return false;
 }
 
+// Heads per workgroup for an aligned forward plan (1: one row per
+// workgroup). A group takes query q of G heads that read the same mask row,
+// so the mask (a stride of 0 over heads) is read once for them and their
+// reductions share two barriers. Needs G | H and a plan the head-group kernels
+// are built for (heads_built). Automatic choice: two heads for rows of 65 to
+// 128 vectors (128 lanes, one vector each), where the per-row fixed cost is
+// largest: measured on MI355X (us, one row per workgroup -> two heads) fp16
+// [8,32,1024,1024] 183 -> 164, causal 159 -> 128; bf16 [16,16,1000,1000]
+// with a [1000,1000] mask 185 -> 175, causal 179 -> 139; fp16
+// [8,16,800,800] with key padding 69 -> 59. Longer rows gain at most 2 % and
+// some lose (fp32 [8,32,1024,1024] with key padding 319 -> 343; fp16
+// [4,32,4096,4096] with a [4,4096,4096] mask, causal, 1095 -> 1153), so they
+// keep one row per workgroup. SMS_HEADS=<1|2|4> overrides the choice.
+int heads_per_group(const Plan& pl, int64_t H, int64_t mask_head_stride) {
+  if (mask_head_stride != 0) return 1;
+  int want = env_int("SMS_HEADS", 0);
+  if (want == 0) want = (pl.tpr == 128 && pl.nv == 1) ? 2 : 1;
+  for (int g : sms::kHeadsList)
+    if (g == want && H % g == 0 && sms::heads_built(pl.tpr, pl.nv, g)) return g;
+  return 1;
+}
+
 bool rows_aligned16(const void* base, const int64_t st[4], int64_t B, int64_t H, int64_t Sq,
                     int bytes) {
   if ((uintptr_t)base & 15) return false;
@@ -375,6 +397,8 @@ sms_status sms_forward_ws(const void* x, const int64_t x_strides[4], const void*
   p.chunks = (uint32_t)pl.chunks;
   p.chunk_vec = (uint32_t)pl.chunk_vec;
   p.ws = static_cast<float2*>(workspace);
+  p.heads = 1;
+  p.div_hg = sms::make_fastdiv(1);
 
   if (pl.family != sms::FAMILY_STREAM && pl.family != sms::FAMILY_SPLIT && !f64) {
     // Aligned-row kernels: every operand's rows on 16-byte lines, whole vectors.
@@ -388,6 +412,13 @@ sms_status sms_forward_ws(const void* x, const int64_t x_strides[4], const void*
 
   uint32_t blocks = 0;
   if (!grid_for(p.g.rows, pl, blocks)) return SMS_ERR_SHAPE;
+  const int heads = pl.family == sms::FAMILY_ALIGNED ? heads_per_group(pl, H, p.sm_h) : 1;
+  if (heads > 1) {
+    pl.family = sms::FAMILY_HEADS;
+    p.heads = (uint32_t)heads;
+    p.div_hg = sms::make_fastdiv((uint32_t)(H / heads));
+    blocks = p.g.rows / (uint32_t)heads;
+  }
   const hipError_t e = launch(dtype, &p, nullptr, pl, blocks, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SMS_OK : SMS_ERR_HIP;
 }

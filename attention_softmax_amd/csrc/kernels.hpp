@@ -321,6 +321,9 @@ struct FwdParams {
   // workspace of rows * chunks (max, sum) pairs.
   uint32_t chunks, chunk_vec;
   float2* ws;
+  // Head groups (FAMILY_HEADS): heads per workgroup, and division by H / heads.
+  uint32_t heads;
+  FastDiv div_hg;
 };
 
 struct BwdParams {
@@ -806,6 +809,161 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_fwd_fast_kernel(FwdParams p
   }
 }
 
+// Reduction of G values per lane over the TPR (>= 128) lanes of a
+// workgroup that owns G rows: one LDS slot per row and wavefront, one barrier
+// for all G rows.
+template <int TPR, int G, class Op>
+SMS_DEV void rows_reduce(float (&v)[G], Op op, float (*slots)[TPR / 64]) {
+  constexpr int W = TPR / 64;
+#pragma unroll
+  for (int i = 0; i < G; ++i) v[i] = group_reduce<64>(v[i], op);
+  if constexpr (W > 1) {
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+      for (int i = 0; i < G; ++i) slots[i][wave] = v[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      float r = slots[i][0];
+#pragma unroll
+      for (int k = 1; k < W; ++k) r = op(r, slots[i][k]);
+      v[i] = r;
+    }
+  }
+}
+
+// Aligned forward over head groups: one workgroup takes query q of heads
+// h0 .. h0 + G - 1 of batch b, for masks that do not depend on the head
+// (mask shapes [Sq,Sk], [B,Sq,Sk], [B,1,Sk], key lengths, or none). The mask
+// row is read once for the G rows, and the G rows' maxima and sums meet in
+// LDS behind the same two barriers. Workgroups run q fastest, then head
+// group, then batch, so each of the G x and y streams stays contiguous.
+template <class F, int TPR, int NV, int KIND, int G>
+__global__ void __launch_bounds__(TPR) sms_fwd_heads_kernel(FwdParams p) {
+  static_assert(TPR >= 64, "one row per workgroup");
+  constexpr int E = F::kE;
+  constexpr int BY = F::kBytes;
+  __shared__ float red[2][G][TPR / 64];
+  const int lane = (int)threadIdx.x;
+  // Host-checked: H % G == 0 and grid = B * (H / G) * Sq.
+  const uint32_t w = blockIdx.x;
+  const uint32_t t = fast_div(w, p.g.div_sq);
+  const uint32_t q = w - t * p.g.Sq;
+  const uint32_t b = fast_div(t, p.div_hg);
+  const uint32_t h0 = (t - b * (p.g.H / G)) * G;
+  const int Sk = (int)p.g.Sk;
+  int kload = p.causal ? causal_bound(p.causal, q, p.g.Sq, Sk) : Sk;
+  const char* mrow = nullptr;
+  if constexpr (KIND != FAST_PLAIN) {
+    const int64_t moff = (int64_t)b * p.sm_b + (int64_t)q * p.sm_q;  // sm_h == 0
+    mrow = p.mask + moff * (KIND == FAST_ADD ? BY : 1);
+  } else {
+    if (p.mask_kind == MASK_LEN)
+      kload = min(kload, max(reinterpret_cast<const int32_t*>(p.mask)[b], 0));
+  }
+  const char* xrow[G];
+  char* yrow[G];
+  RowStream xs[G], ys[G];
+  const bool exact = p.lines != 0;
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    xrow[i] = p.x + row_offset(b, h0 + i, q, p.sx_b, p.sx_h, p.sx_q) * BY;
+    yrow[i] = p.y + row_offset(b, h0 + i, q, p.sy_b, p.sy_h, p.sy_q) * BY;
+    if constexpr (kBufRows) {
+      xs[i] = row_stream(xrow[i], (uint32_t)Sk * BY);
+      ys[i] = row_stream(yrow[i], (uint32_t)Sk * BY);
+    }
+  }
+  u32x4 xr[G][NV], mr[NV];
+  uint64_t mb[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int v = j * TPR + lane;
+    if (v * E < kload) {
+      if constexpr (KIND == FAST_ADD) mr[j] = ld_cached(mrow + (int64_t)v * 16);
+      if constexpr (KIND == FAST_BOOL) mb[j] = ld_bits<E>(mrow + (int64_t)v * E);
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        if (kBufRows && !exact) xr[i][j] = rs_load(xs[i], (uint32_t)v * 16);
+        else xr[i][j] = ld_stream(xrow[i] + (int64_t)v * 16);
+      }
+    }
+  }
+  const float scale = p.scale;
+  float s[G][NV][E];
+  float mx[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) mx[i] = kNegInf;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int k0 = (j * TPR + lane) * E;
+    float m[E];
+    if constexpr (KIND == FAST_ADD) {
+      if (k0 < kload) F::unpack(mr[j], m);
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (k0 < kload) {
+        F::unpack(xr[i][j], s[i][j]);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if constexpr (KIND == FAST_ADD) s[i][j][e] = fmaf(s[i][j][e], scale, m[e]);
+          else if constexpr (KIND == FAST_BOOL)
+            s[i][j][e] = bit_set(mb[j], e) ? kNegInf : s[i][j][e] * scale;
+          else s[i][j][e] *= scale;
+        }
+        if (k0 + E > kload) {  // the vector that holds the row's key bound
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            if (k0 + e >= kload) s[i][j][e] = kNegInf;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[i][j][e] = kNegInf;
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) mx[i] = fmaxf(mx[i], s[i][j][e]);
+    }
+  }
+  rows_reduce<TPR, G>(mx, OpMax(), red[0]);
+  float sum[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    // Every key masked: exponentiate against 0 so every term is exp(-inf) = 0.
+    const float mref = (mx[i] == kNegInf) ? 0.0f : mx[i];
+    sum[i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      if ((j * TPR + lane) * E < kload) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          s[i][j][e] = exp_biased(s[i][j][e], mref);
+          sum[i] += s[i][j][e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[i][j][e] = 0.0f;
+      }
+    }
+  }
+  rows_reduce<TPR, G>(sum, OpAdd(), red[1]);
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const float inv = sum[i] > 0.0f ? 1.0f / sum[i] : 0.0f;  // fully masked row -> zeros
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int v = j * TPR + lane;
+      if (v * E < Sk) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[i][j][e] *= inv;
+        out_store<kBufRows>(ys[i], yrow[i], exact, v, F::pack(s[i][j]));
+      }
+    }
+  }
+}
+
 template <class F, int TPR, int NV>
 __global__ void __launch_bounds__(block_of(TPR)) sms_bwd_fast_kernel(BwdParams p) {
   constexpr int E = F::kE;
@@ -1253,8 +1411,34 @@ enum : int {
   FAMILY_ALIGNED = 1,
   FAMILY_STREAM = 2,
   FAMILY_SPLIT = 3,
-  FAMILY_F64 = 4
+  FAMILY_F64 = 4,
+  FAMILY_HEADS = 5  // aligned forward over head groups (forward only, TPR >= 128)
 };
+
+// Heads per workgroup the head-group forward is built with.
+constexpr int kHeadsList[] = {2, 4};
+
+// Head groups are built for 128 to 512 lanes and heads * NV <= 4 (the G rows
+// then fit in VGPRs without spilling).
+constexpr bool heads_built(int tpr, int nv, int g) { return tpr >= 128 && tpr <= 512 && g * nv <= 4; }
+
+template <class F, int TPR, int NV, int KIND>
+hipError_t launch_heads(const FwdParams* fp, uint32_t blocks, hipStream_t st) {
+  const dim3 grid(blocks), block(TPR);
+  if constexpr (heads_built(TPR, NV, 2)) {
+    if (fp->heads == 2) {
+      hipLaunchKernelGGL((sms_fwd_heads_kernel<F, TPR, NV, KIND, 2>), grid, block, 0, st, *fp);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (heads_built(TPR, NV, 4)) {
+    if (fp->heads == 4) {
+      hipLaunchKernelGGL((sms_fwd_heads_kernel<F, TPR, NV, KIND, 4>), grid, block, 0, st, *fp);
+      return hipGetLastError();
+    }
+  }
+  return hipErrorInvalidValue;
+}
 
 // TPR and NV values the library is built with.
 constexpr int kTprList[] = {4, 8, 16, 32, 64, 128, 256, 512, 1024};
@@ -1265,6 +1449,11 @@ hipError_t launch_nv(const FwdParams* fp, const BwdParams* bp, int family, uint3
                      hipStream_t st) {
   const dim3 grid(blocks), block(block_of(TPR));
   if (fp) {
+    if (family == FAMILY_HEADS) {
+      if (fp->mask_kind == MASK_ADD) return launch_heads<F, TPR, NV, FAST_ADD>(fp, blocks, st);
+      if (fp->mask_kind == MASK_BOOL) return launch_heads<F, TPR, NV, FAST_BOOL>(fp, blocks, st);
+      return launch_heads<F, TPR, NV, FAST_PLAIN>(fp, blocks, st);
+    }
     if (family == FAMILY_ALIGNED) {
       if (fp->mask_kind == MASK_ADD)
         hipLaunchKernelGGL((sms_fwd_fast_kernel<F, TPR, NV, FAST_ADD>), grid, block, 0, st, *fp);

@@ -16,11 +16,12 @@ diagnostics on stderr.
 
     python bench.py --op attention [--steps K] [--warmup W]
 
-times the fused attention forward instead (O = softmax(Q K^T * scale) V, fp16
-[4,32,4096,128] queries, keys and values, causal): value = the two products'
-flops (halved by the causal rule) / time, in TFLOP/s against the MI355X dense
-fp16 matrix peak. It is a diagnostic line for that kernel; the default
-(softmax) line is the headline metric.
+times the fused attention instead (O = softmax(Q K^T * scale) V and its
+gradients, fp16 [4,32,4096,128] queries, keys, values and dO, causal): value =
+the algorithmic flops of the forward's two products and the backward's five
+(halved by the causal rule) / time of a forward + backward, in TFLOP/s against
+the MI355X dense fp16 matrix peak. It is a diagnostic line for those kernels;
+the default (softmax) line is the headline metric.
 """
 
 import argparse
@@ -295,12 +296,25 @@ def torch_reference(torch, w, stream, fwd_b, bwd_b, fwd_ms, bwd_ms):
             "speedup_forward": round(tf / fwd_ms, 2), "speedup_backward": round(tb / bwd_ms, 2)}
 
 
+def _time_launches(torch, fn, stream, n):
+    """Average ms of ``fn()`` over n back-to-back calls, HIP events on ``stream``."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
 def bench_attention(args):
-    """Fused attention forward: fp16 [4,32,4096,128] Q, K, V, causal, scale 1/sqrt(128)."""
+    """Fused attention forward + backward: fp16 [4,32,4096,128] Q, K, V, dO,
+    causal, scale 1/sqrt(128)."""
     import torch
 
     import oracle
-    from attention_softmax_amd import sms_attention_forward
+    from attention_softmax_amd import (sms_attention_backward, sms_attention_forward,
+                                       sms_attention_workspace_bytes)
     from attention_softmax_amd.workloads import draw_x
     from tests.parity import to_np
 
@@ -311,66 +325,106 @@ def bench_attention(args):
     q = draw_x((B, H, S, D), "f16", ("normal", 1.0), 11, dev)
     k = draw_x((B, H, S, D), "f16", ("normal", 1.0), 12, dev)
     v = draw_x((B, H, S, D), "f16", ("normal", 1.0), 13, dev)
+    do = draw_x((B, H, S, D), "f16", ("normal", 1.0), 14, dev)
     o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(sms_attention_workspace_bytes(B, H, S), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-    flops = 4.0 * B * H * S * S * D * (0.5 if causal else 1.0)
+    half = 0.5 if causal else 1.0
+    # Algorithmic flops: forward Q K^T and P V; backward Q K^T (recomputed
+    # once), dO V^T, P^T dO, dS K and dS^T Q.
+    fwd_flops = 4.0 * B * H * S * S * D * half
+    bwd_flops = 10.0 * B * H * S * S * D * half
+
+    def fwd():
+        sms_attention_forward(q, k, v, None, scale, causal, o=o, stream=stream)
+
+    def fwd_lse():
+        lse.copy_(sms_attention_forward(q, k, v, None, scale, causal, o=o, return_lse=True,
+                                        stream=stream)[1])
+
+    def bwd():
+        sms_attention_backward(q, k, v, o, lse, do, None, scale, causal, dq=dq, dk=dk, dv=dv,
+                               workspace=ws, stream=stream)
+
+    fwd_lse()
     for _ in range(args.warmup):
-        sms_attention_forward(q, k, v, None, scale, causal, o=o, stream=stream)
+        fwd()
+        bwd()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        sms_attention_forward(q, k, v, None, scale, causal, o=o, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
+    fwd_ms = _time_launches(torch, fwd, stream, args.steps)
+    bwd_ms = _time_launches(torch, bwd, stream, args.steps)
     wall = time.perf_counter() - wall0
-    ms = e0.elapsed_time(e1) / args.steps
-    tflops = flops / (ms * 1e-3) / 1e12
+    step_ms = fwd_ms + bwd_ms
+    tflops = (fwd_flops + bwd_flops) / (step_ms * 1e-3) / 1e12
+    fwd_tf = fwd_flops / (fwd_ms * 1e-3) / 1e12
+    bwd_tf = bwd_flops / (bwd_ms * 1e-3) / 1e12
     sdpa = None
     try:
+        qg, kg, vg = (t.detach().clone().requires_grad_() for t in (q, k, v))
+        F = torch.nn.functional.scaled_dot_product_attention
+
+        def t_fwd():
+            F(qg, kg, vg, is_causal=causal)
+
+        out = F(qg, kg, vg, is_causal=causal)
+
+        def t_bwd():
+            torch.autograd.grad(out, (qg, kg, vg), do, retain_graph=True)
+
         for _ in range(3):
-            torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal)
-        e0.record(stream)
-        for _ in range(5):
-            torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal)
-        e1.record(stream)
+            t_fwd()
+            t_bwd()
         torch.cuda.synchronize()
-        t2 = e0.elapsed_time(e1) / 5
+        tf_ms = _time_launches(torch, t_fwd, stream, 5)
+        tb_ms = _time_launches(torch, t_bwd, stream, 5)
         sdpa = {"what": "torch.nn.functional.scaled_dot_product_attention, same tensors",
-                "avg_us": round(t2 * 1e3, 1), "TFLOPs": round(flops / (t2 * 1e-3) / 1e12, 1)}
+                "forward_us": round(tf_ms * 1e3, 1),
+                "forward_TFLOPs": round(fwd_flops / (tf_ms * 1e-3) / 1e12, 1),
+                "backward_us": round(tb_ms * 1e3, 1),
+                "backward_TFLOPs": round(bwd_flops / (tb_ms * 1e-3) / 1e12, 1)}
     except RuntimeError as ex:  # context only
         sdpa = {"error": type(ex).__name__}
     cpu = None
     if args.cpu_seconds > 0:
-        # the float64 oracle on the first n queries of head (0, 0), n doubling
-        # until the time budget is spent
-        # (one BLAS thread, so that `cores` is what was used)
+        # the float64 oracle (forward, then backward) on the first n queries of
+        # head (0, 0), n doubling until the time budget is spent (one BLAS
+        # thread, so that `cores` is what was used)
         from threadpoolctl import threadpool_limits
 
         n, spent, done_flops = 16, 0.0, 0.0
-        qn, kn, vn = to_np(q[:1, :1]), to_np(k[:1, :1]), to_np(v[:1, :1])
+        qn, kn, vn, don = (to_np(t[:1, :1]) for t in (q, k, v, do))
         with threadpool_limits(limits=1):
             while spent < args.cpu_seconds and n <= S:
                 t0 = time.perf_counter()
                 oracle.attention.forward(qn[:, :, :n], kn, vn, "f16", scale=scale,
                                          is_causal=causal)
+                oracle.attention.backward(qn[:, :, :n], kn, vn, don[:, :, :n], "f16",
+                                          scale=scale, is_causal=causal)
                 spent += time.perf_counter() - t0
-                done_flops += 4.0 * n * S * D  # the oracle multiplies every key (no causal skip)
+                # the oracle multiplies every key (no causal skip)
+                done_flops += 14.0 * n * S * D
                 n *= 2
         cpu = {"value": round(done_flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
                "kind": "oracle",
-               "sample": f"queries 0..{n // 2 - 1} of head (0,0), {spent:.1f} s, float64 numpy"}
+               "sample": f"forward + backward of queries 0..{n // 2 - 1} of head (0,0) against "
+                         f"all {S} keys, {spent:.1f} s, float64 numpy"}
     out = {
-        "metric": "fused attention forward TFLOP/s, 1 MI355X", "value": round(tflops, 1),
-        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-        "config": {"workload": "attention fp16 Q,K,V [4,32,4096,128] N(0,1), causal",
+        "metric": "fused attention forward + backward TFLOP/s, 1 MI355X",
+        "value": round(tflops, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "attention fp16 Q,K,V,dO [4,32,4096,128] N(0,1), causal",
                    "shape": [B, H, S, D], "causal": causal, "scale": scale},
-        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": round(tflops, 1),
-                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None},
+        "forward": {"us": round(fwd_ms * 1e3, 1), "TFLOPs": round(fwd_tf, 1)},
+        "backward": {"us": round(bwd_ms * 1e3, 1), "TFLOPs": round(bwd_tf, 1),
+                     "launches": "rowsum(dO*O), dQ, dK+dV"},
+        "roofline": {"bound": "mfma", "kernel": "backward (3 launches)",
+                     "achieved": round(bwd_tf, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(bwd_tf / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": None},
         "torch_reference": sdpa, "cpu_baseline": cpu, "wall_s_timed": round(wall, 3),
     }
     print(json.dumps(out), flush=True)

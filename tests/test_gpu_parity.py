@@ -323,6 +323,35 @@ def test_every_lanes_per_row(tpr, dtype, aligned, monkeypatch):
             f"TPR={tpr} bwd")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("tpr,nv", [(128, 1), (256, 1), (512, 1), (128, 2), (256, 2)])
+def test_head_groups(dtype, tpr, nv, monkeypatch):
+    """The forward over head groups (one workgroup takes query q of G heads
+    that share a mask row) against the oracle and bit for bit against one row
+    per workgroup: every mask shape and kind, both causal rules, H = 4 (groups
+    of 2 and 4) and H = 3 (no group divides it). Mask shapes that vary by
+    head, and widths the groups are not built for, fall back to one row."""
+    E = 4 if dtype == "f32" else 8
+    Sk = (tpr * (nv - 1) + tpr // 2 + 3) * E  # nv vectors per lane at tpr lanes
+    say(f"head groups dtype={dtype} TPR={tpr} NV={nv} Sk={Sk}")
+    monkeypatch.setenv("SMS_FORCE_TPR", str(tpr))
+    for H in (4, 3):
+        shape = (2, H, 3, Sk)
+        for mode, kind in MASK_CASES:
+            for causal in CAUSALS:
+                seed = zlib.crc32(f"hg/{dtype}/{tpr}/{nv}/{H}/{mode}/{kind}/{causal}".encode()) % 10000
+                x = draw_x(shape, dtype, ("normal", 3.0), seed, DEV)
+                mask = make_mask(shape, mode, kind, dtype, seed + 1)
+                monkeypatch.setenv("SMS_HEADS", "1")
+                y1 = fwd(x, mask, 0.3, causal)
+                compare(decoded(y1), oracle_fwd(x, mask, mode, 0.3, causal, kind), dtype,
+                        f"H={H} {mode}/{kind} causal={causal}", rowsum=True)
+                for g in ("2", "4", "0"):
+                    monkeypatch.setenv("SMS_HEADS", g)
+                    assert torch.equal(fwd(x, mask, 0.3, causal), y1), \
+                        f"G={g} H={H} {mode}/{kind} causal={causal}"
+
+
 def test_forced_width_too_small_is_an_error(monkeypatch):
     monkeypatch.setenv("SMS_FORCE_TPR", "4")
     x = torch.zeros(1, 1, 2, 4096, device=DEV)
