@@ -155,18 +155,23 @@ bool choose_plan(int64_t nvec, bool backward, bool causal, Plan& out) {
 // so the mask (a stride of 0 over heads) is read once for them and their
 // reductions share two barriers. Needs G | H and a plan the head-group kernels
 // are built for (heads_built). Automatic choice: two heads for rows of 65 to
-// 128 vectors (128 lanes, one vector each), where the per-row fixed cost is
-// largest: measured on MI355X (us, one row per workgroup -> two heads) fp16
-// [8,32,1024,1024] 183 -> 164, causal 159 -> 128; bf16 [16,16,1000,1000]
-// with a [1000,1000] mask 185 -> 175, causal 179 -> 139; fp16
-// [8,16,800,800] with key padding 69 -> 59. Longer rows gain at most 2 % and
-// some lose (fp32 [8,32,1024,1024] with key padding 319 -> 343; fp16
-// [4,32,4096,4096] with a [4,4096,4096] mask, causal, 1095 -> 1153), so they
-// keep one row per workgroup. SMS_HEADS=<1|2|4> overrides the choice.
-int heads_per_group(const Plan& pl, int64_t H, int64_t mask_head_stride) {
+// 128 vectors (128 lanes, one vector each) that have a causal rule or a mask,
+// where the per-row fixed cost is largest: measured on MI355X (us, one row
+// per workgroup -> two heads) fp16 [8,32,1024,1024] causal 158 -> 128; bf16
+// [16,16,1000,1000] with a [1000,1000] mask 185 -> 175, causal 177 -> 138;
+// fp16 [8,16,800,800] with key padding 68 -> 57. Without either the two are
+// within run-to-run noise (fp16 [8,32,1024,1024] 168 / 165, fp32
+// [16,32,512,512] 161 / 166). Longer rows gain at most 2 % and some lose
+// (fp32 [8,32,1024,1024] with key padding 319 -> 340; fp16 [4,32,2048,2048]
+// causal 255 -> 280; fp16 [4,32,4096,4096] with a [4,4096,4096] mask, causal,
+// 1095 -> 1153), so they keep one row per workgroup. Groups of consecutive
+// rows instead of heads, forward or backward, measured no better.
+// SMS_HEADS=<1|2|4> overrides the choice.
+int heads_per_group(const Plan& pl, int64_t H, int64_t mask_head_stride, bool causal,
+                    bool has_mask) {
   if (mask_head_stride != 0) return 1;
   int want = env_int("SMS_HEADS", 0);
-  if (want == 0) want = (pl.tpr == 128 && pl.nv == 1) ? 2 : 1;
+  if (want == 0) want = (pl.tpr == 128 && pl.nv == 1 && (causal || has_mask)) ? 2 : 1;
   for (int g : sms::kHeadsList)
     if (g == want && H % g == 0 && sms::heads_built(pl.tpr, pl.nv, g)) return g;
   return 1;
@@ -412,7 +417,9 @@ sms_status sms_forward_ws(const void* x, const int64_t x_strides[4], const void*
 
   uint32_t blocks = 0;
   if (!grid_for(p.g.rows, pl, blocks)) return SMS_ERR_SHAPE;
-  const int heads = pl.family == sms::FAMILY_ALIGNED ? heads_per_group(pl, H, p.sm_h) : 1;
+  const int heads = pl.family == sms::FAMILY_ALIGNED
+                        ? heads_per_group(pl, H, p.sm_h, is_causal != 0, has_mask)
+                        : 1;
   if (heads > 1) {
     pl.family = sms::FAMILY_HEADS;
     p.heads = (uint32_t)heads;

@@ -192,24 +192,39 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdParams p) {
         dpacc[kb] = mfma_32x32x16<BF16>(av, df[s], dpacc[kb]);
       }
     }
-    // dS^T = P (dP^T - delta), P recomputed from the forward's LSE.
+    // dS^T = P (dP^T - delta), P recomputed from the forward's LSE. A tile
+    // whose every score is visible to every query of the workgroup (keys in
+    // range and before the first query's causal bound, all queries in range,
+    // no per-score mask) skips the exclusion tests.
+    const bool full = KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL && q0 + kAttnBq <= Sq &&
+                      kt + BK <= klen && (!p.causal || kt + BK <= q0 + off + 1);
+    if (full) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        float tv = sacc[kb][r] * p.scale_log2;
-        bool excluded = key >= kq || key >= Sk || !live;
-        if constexpr (KIND == ATTN_MASK_ADD) {
-          if (!excluded) {
-            const uint32_t bits = *reinterpret_cast<const uint16_t*>(p.mask + (mrow + key) * 2);
-            tv = fmaf(to_float<BF16>(bits), kLog2eA, tv);
-          }
-        } else if constexpr (KIND == ATTN_MASK_BOOL) {
-          if (!excluded && p.mask[mrow + key] != 0) excluded = true;
+        for (int r = 0; r < 16; ++r) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.scale_log2, -lse2));
+          sacc[kb][r] = pv * (dpacc[kb][r] - delta);
         }
-        const float pv = excluded ? 0.0f : __builtin_amdgcn_exp2f(tv - lse2);
-        sacc[kb][r] = pv * (dpacc[kb][r] - delta);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          float tv = sacc[kb][r] * p.scale_log2;
+          bool excluded = key >= kq || key >= Sk || !live;
+          if constexpr (KIND == ATTN_MASK_ADD) {
+            if (!excluded) {
+              const uint32_t bits = *reinterpret_cast<const uint16_t*>(p.mask + (mrow + key) * 2);
+              tv = fmaf(to_float<BF16>(bits), kLog2eA, tv);
+            }
+          } else if constexpr (KIND == ATTN_MASK_BOOL) {
+            if (!excluded && p.mask[mrow + key] != 0) excluded = true;
+          }
+          const float pv = excluded ? 0.0f : __builtin_amdgcn_exp2f(tv - lse2);
+          sacc[kb][r] = pv * (dpacc[kb][r] - delta);
+        }
       }
     }
     u32x4 pb[4];
@@ -257,7 +272,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdParams p) {
   __shared__ __align__(16) uint16_t qts[D * TP];    // Q^T: A of dK^T += Q^T dS
   __shared__ __align__(16) uint16_t dos[BQ * RP];   // dO: A of dP = dO V^T
   __shared__ __align__(16) uint16_t dots[D * TP];   // dO^T: A of dV^T += dO^T P
-  __shared__ float lses[BQ], dels[BQ];
+  __shared__ __align__(16) float lses[BQ];  // LSE * log2(e) of the tile's queries
+  __shared__ __align__(16) float dels[BQ];
 
   const int tid = (int)threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
@@ -301,61 +317,83 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdParams p) {
   const bool any = k0 < klen;
 
   // Tiles of BQ queries fetched one ahead: (4 queries x 8 dims) of Q by the
-  // first QITEMS threads and of dO by the next QITEMS, staged row-major and
-  // transposed; LSE and delta by 2 * BQ threads.
-  constexpr int QITEMS = (BQ / 4) * (D / 8);
-  const int item = tid < QITEMS ? tid : tid - QITEMS;
-  const bool is_q = tid < QITEMS, is_do = tid >= QITEMS && tid < 2 * QITEMS;
+  // first QITEMS threads (whole wavefronts) and of dO by the next QITEMS,
+  // staged row-major and transposed; LSE by the first BQ lanes of wavefront 0
+  // and delta by those of wavefront 1. Every choice of source is uniform over
+  // a wavefront and made once here: a per-lane choice between kernel-argument
+  // fields inside the loop made the compiler fetch the fields with vector
+  // loads and wait for every outstanding load, prefetch included.
+  constexpr int QITEMS = (BQ / 4) * (D / 8);  // 64 or 128: whole wavefronts
+  static_assert(QITEMS % 64 == 0, "Q / dO loads by whole wavefronts");
+  const int tile_role = __builtin_amdgcn_readfirstlane(tid / QITEMS);  // 0: Q, 1: dO, 2+: none
+  const bool is_q = tile_role == 0, is_do = tile_role == 1;
+  const int item = tid - tile_role * QITEMS;
   const int qdg = item % (D / 8), qqg = item / (D / 8);
+  const char* tsrc = is_q ? p.q : p.dout;
+  const int64_t ts_b = is_q ? p.sq_b : p.sdo_b;
+  const int64_t ts_h = is_q ? p.sq_h : p.sdo_h;
+  const int64_t ts_s = is_q ? p.sq_s : p.sdo_s;
+  tsrc += (int64_t)b * ts_b * 2;
+  uint16_t* const stage_rm = is_q ? qs : dos;
+  uint16_t* const stage_tr = is_q ? qts : dots;
+  const bool is_stat = wave < 2 && lane < BQ;  // LSE (wavefront 0) or delta (wavefront 1)
+  const float* ssrc = wave == 0 ? p.lse : p.delta;
+  float* const sdst = wave == 0 ? lses : dels;
+  const float sfill = wave == 0 ? kNegInfA : 0.0f;
+  const float smul = wave == 0 ? kLog2eA : 1.0f;  // LSE is staged in log2 units
   u32x4 treg[4];
   float sreg = 0.0f;
   auto fetch = [&](uint32_t h, int qt) {
-    const char* base = is_q ? p.q + ((int64_t)b * p.sq_b + (int64_t)h * p.sq_h) * 2
-                            : p.dout + ((int64_t)b * p.sdo_b + (int64_t)h * p.sdo_h) * 2;
-    const int64_t rs = is_q ? p.sq_s : p.sdo_s;
+    const char* base = tsrc + (int64_t)h * ts_h * 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int q = qt + 4 * qqg + i;
       treg[i] = u32x4{0, 0, 0, 0};
       if ((is_q || is_do) && q < Sq)
-        treg[i] = *reinterpret_cast<const u32x4*>(base + ((int64_t)q * rs + qdg * 8) * 2);
+        treg[i] = *reinterpret_cast<const u32x4*>(base + ((int64_t)q * ts_s + qdg * 8) * 2);
     }
-    if (tid < 2 * BQ) {
-      const int q = qt + (tid % BQ);
-      const int64_t lrow = ((int64_t)b * p.H + h) * Sq + q;
-      sreg = tid < BQ ? kNegInfA : 0.0f;
-      if (q < Sq) sreg = tid < BQ ? p.lse[lrow] : p.delta[lrow];
+    if (is_stat) {
+      const int q = qt + lane;
+      sreg = q < Sq ? ssrc[((int64_t)b * p.H + h) * Sq + q] * smul : sfill;
     }
   };
   auto stage = [&]() {
     if (is_q || is_do) {
-      uint16_t* rm = is_q ? qs : dos;
-      uint16_t* tr = is_q ? qts : dots;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4*>(&rm[(4 * qqg + i) * RP + 8 * qdg]) = treg[i];
+        *reinterpret_cast<u32x4*>(&stage_rm[(4 * qqg + i) * RP + 8 * qdg]) = treg[i];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const u32x2 w{elem(treg[0], j) | (elem(treg[1], j) << 16),
                       elem(treg[2], j) | (elem(treg[3], j) << 16)};
-        *reinterpret_cast<u32x2*>(&tr[(8 * qdg + j) * TP + 4 * qqg]) = w;
+        *reinterpret_cast<u32x2*>(&stage_tr[(8 * qdg + j) * TP + 4 * qqg]) = w;
       }
     }
-    if (tid < BQ) lses[tid] = sreg;
-    else if (tid < 2 * BQ) dels[tid - BQ] = sreg;
+    if (is_stat) sdst[lane] = sreg;
   };
 
-  if (any) {
-    const uint32_t h0 = hk * p.group, h1 = h0 + p.group;
-    if (qstart < Sq) fetch(h0, qstart);
-    for (uint32_t h = h0; h < h1; ++h) {
+  if (any && qstart < Sq) {
+    // One sequence of (query head, query tile) steps over the heads of the
+    // group, so that the next step's fetch is a single code path.
+    const int ntile = (Sq - qstart + BQ - 1) / BQ;
+    const int nstep = ntile * (int)p.group;
+    uint32_t h = hk * p.group, nh = h;
+    int qt = qstart, nqt = qstart;
+    fetch(h, qt);
+    for (int step = 0; step < nstep; ++step) {
+      h = nh;
+      qt = nqt;
+      nqt = qt + BQ;
+      if (nqt >= Sq) {
+        nqt = qstart;
+        ++nh;
+      }
       const int64_t mbase = (int64_t)b * p.sm_b + (int64_t)h * p.sm_h;
-      for (int qt = qstart; qt < Sq; qt += BQ) {
+      {
         __syncthreads();
         stage();
         __syncthreads();
-        if (qt + BQ < Sq) fetch(h, qt + BQ);
-        else if (h + 1 < h1) fetch(h + 1, qstart);
+        if (step + 1 < nstep) fetch(nh, nqt);
 
         f32x16 sacc, dpacc;
 #pragma unroll
@@ -372,28 +410,51 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdParams p) {
         }
         // Register r holds query qt + 8*(r/4) + 4g + r%4 of this lane's key.
         float pr[16], dsr[16];
+        // A tile whose every (query, key) score is visible (all queries and
+        // keys in range, past the causal boundary, no per-score mask) takes
+        // the probabilities without any exclusion test.
+        const bool full = KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL && qt + BQ <= Sq &&
+                          k0 + kAttnBwdBk <= klen &&
+                          (!p.causal || k0 + kAttnBwdBk - 1 <= qt + off);
+        if (full) {
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int ql = 8 * rg + 4 * g;  // first of 4 consecutive queries
+          for (int rg = 0; rg < 4; ++rg) {
+            const int ql = 8 * rg + 4 * g;  // first of 4 consecutive queries
+            const float4 l2 = *reinterpret_cast<const float4*>(&lses[ql]);
+            const float4 dl = *reinterpret_cast<const float4*>(&dels[ql]);
+            const float lv[4] = {l2.x, l2.y, l2.z, l2.w}, dv4[4] = {dl.x, dl.y, dl.z, dl.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * rg + e, qq = qt + ql + e;
-            const float lse = lses[ql + e];
-            float tv = sacc[r] * p.scale_log2;
-            bool excluded = qq >= Sq || kj >= klen || !kvalid || lse == kNegInfA ||
-                            (p.causal && kj > qq + off);
-            if constexpr (KIND == ATTN_MASK_ADD) {
-              if (!excluded) {
-                const uint32_t bits = *reinterpret_cast<const uint16_t*>(
-                    p.mask + (mbase + (int64_t)qq * p.sm_q + kj) * 2);
-                tv = fmaf(to_float<BF16>(bits), kLog2eA, tv);
-              }
-            } else if constexpr (KIND == ATTN_MASK_BOOL) {
-              if (!excluded && p.mask[mbase + (int64_t)qq * p.sm_q + kj] != 0) excluded = true;
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * rg + e;
+              const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], p.scale_log2, -lv[e]));
+              pr[r] = pv;
+              dsr[r] = pv * (dpacc[r] - dv4[e]);
             }
-            const float pv = excluded ? 0.0f : __builtin_amdgcn_exp2f(tv - lse * kLog2eA);
-            pr[r] = pv;
-            dsr[r] = pv * (dpacc[r] - dels[ql + e]);
+          }
+        } else {
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            const int ql = 8 * rg + 4 * g;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * rg + e, qq = qt + ql + e;
+              const float lse2 = lses[ql + e];
+              float tv = sacc[r] * p.scale_log2;
+              bool excluded = qq >= Sq || kj >= klen || !kvalid || lse2 == kNegInfA ||
+                              (p.causal && kj > qq + off);
+              if constexpr (KIND == ATTN_MASK_ADD) {
+                if (!excluded) {
+                  const uint32_t bits = *reinterpret_cast<const uint16_t*>(
+                      p.mask + (mbase + (int64_t)qq * p.sm_q + kj) * 2);
+                  tv = fmaf(to_float<BF16>(bits), kLog2eA, tv);
+                }
+              } else if constexpr (KIND == ATTN_MASK_BOOL) {
+                if (!excluded && p.mask[mbase + (int64_t)qq * p.sm_q + kj] != 0) excluded = true;
+              }
+              const float pv = excluded ? 0.0f : __builtin_amdgcn_exp2f(tv - lse2);
+              pr[r] = pv;
+              dsr[r] = pv * (dpacc[r] - dels[ql + e]);
+            }
           }
         }
         // B operands: k-step s takes registers 8s .. 8s+7 (queries
