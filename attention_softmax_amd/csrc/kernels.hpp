@@ -230,8 +230,10 @@ SMS_DEV T group_reduce(T v, Op op) {
 
 // Reduction over the TPR lanes that own a row. For TPR > 64 the wavefronts of
 // the workgroup meet in LDS (`slots` holds TPR/64 values) behind one barrier.
+// With nw < TPR/64 only the first nw wavefronts take part (the others have
+// ended: a barrier waits only for wavefronts that have not terminated).
 template <int TPR, class T, class Op>
-SMS_DEV T row_reduce(T v, Op op, T* slots) {
+SMS_DEV T row_reduce(T v, Op op, T* slots, int nw = TPR / 64) {
   if constexpr (TPR <= 64) {
     return group_reduce<TPR>(v, op);
   } else {
@@ -242,7 +244,8 @@ SMS_DEV T row_reduce(T v, Op op, T* slots) {
     __syncthreads();
     T r = slots[0];
 #pragma unroll
-    for (int i = 1; i < W; ++i) r = op(r, slots[i]);
+    for (int i = 1; i < W; ++i)
+      if (i < nw) r = op(r, slots[i]);
     return r;
   }
 }
@@ -324,6 +327,7 @@ struct FwdParams {
   // Head groups (FAMILY_HEADS): heads per workgroup, and division by H / heads.
   uint32_t heads;
   FastDiv div_hg;
+  int early;  // aligned kernels: wavefronts holding only keys past the bound exit early
 };
 
 struct BwdParams {
@@ -337,6 +341,7 @@ struct BwdParams {
   float scale;
   int causal;  // CAUSAL_*: a promise that y is 0 past the bound
   int lines;   // every row of y, dy and dx starts on a 128-byte line and fills whole lines
+  int early;   // aligned kernels: wavefronts holding only keys past the bound exit early
   // Split rows (FAMILY_SPLIT): chunks per row, vectors per chunk, and the
   // workspace of rows * chunks partial dot products.
   uint32_t chunks, chunk_vec;
@@ -627,13 +632,13 @@ SMS_DEV void row_store(char* orow, bool ovec, int a, int v, int Sk, const float 
 // the values: s becomes y.
 template <int TPR, int NV, int E>
 SMS_DEV void softmax_in_registers(float (&s)[NV][E], int lane, int a, int kload, float* smax,
-                                  float* ssum) {
+                                  float* ssum, int nw = TPR / 64) {
   float mx = kNegInf;
 #pragma unroll
   for (int j = 0; j < NV; ++j)
 #pragma unroll
     for (int e = 0; e < E; ++e) mx = fmaxf(mx, s[j][e]);
-  mx = row_reduce<TPR>(mx, OpMax(), smax);
+  mx = row_reduce<TPR>(mx, OpMax(), smax, nw);
   // Every key masked: exponentiate against 0 so every term is exp(-inf) = 0.
   const float mref = (mx == kNegInf) ? 0.0f : mx;
   float sum = 0.0f;
@@ -651,7 +656,7 @@ SMS_DEV void softmax_in_registers(float (&s)[NV][E], int lane, int a, int kload,
       for (int e = 0; e < E; ++e) s[j][e] = 0.0f;
     }
   }
-  sum = row_reduce<TPR>(sum, OpAdd(), ssum);
+  sum = row_reduce<TPR>(sum, OpAdd(), ssum, nw);
   const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;  // fully masked row -> zeros
 #pragma unroll
   for (int j = 0; j < NV; ++j)
@@ -760,6 +765,22 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_fwd_fast_kernel(FwdParams p
     xs = row_stream(xrow, (uint32_t)Sk * BY);
     ys = row_stream(yrow, (uint32_t)Sk * BY);
   }
+  // Wavefronts whose every vector lies past the key bound (the causal future,
+  // padding) store zeros and end; the others reduce among themselves.
+  int nw = TPR > 64 ? TPR / 64 : 1;
+  if constexpr (TPR > 64) {
+    if (p.early) {
+      nw = min(TPR / 64, (kload + 64 * E - 1) / (64 * E));
+      if ((int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= nw) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          const int v = j * TPR + lane;
+          if (v * E < Sk) out_store<kBuf>(ys, yrow, exact, v, u32x4{0, 0, 0, 0});
+        }
+        return;
+      }
+    }
+  }
   u32x4 xr[NV], mr[NV];
   uint64_t mb[NV];
 #pragma unroll
@@ -801,7 +822,7 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_fwd_fast_kernel(FwdParams p
       for (int e = 0; e < E; ++e) s[j][e] = kNegInf;
     }
   }
-  softmax_in_registers<TPR, NV, E>(s, lane, 0, kload, red[0], red[1]);
+  softmax_in_registers<TPR, NV, E>(s, lane, 0, kload, red[0], red[1], nw);
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int v = j * TPR + lane;
@@ -982,6 +1003,22 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_bwd_fast_kernel(BwdParams p
     ds = row_stream(r.d, row_bytes);
     xs = row_stream(r.x, row_bytes);
   }
+  // Wavefronts whose every vector lies past the causal bound (y = 0 there)
+  // store zeros and end; the others reduce among themselves.
+  int nw = TPR > 64 ? TPR / 64 : 1;
+  if constexpr (TPR > 64) {
+    if (p.early) {
+      nw = min(TPR / 64, (kload + 64 * E - 1) / (64 * E));
+      if ((int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= nw) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          const int v = j * TPR + lane;
+          if (v * E < (int)p.g.Sk) out_store<kBuf>(xs, r.x, exact, v, u32x4{0, 0, 0, 0});
+        }
+        return;
+      }
+    }
+  }
   u32x4 yr[NV], dr[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
@@ -1013,7 +1050,7 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_bwd_fast_kernel(BwdParams p
       for (int e = 0; e < E; ++e) acc += F::prod(yv[e], gv[e]);
     }
   }
-  acc = row_reduce<TPR>(acc, OpAdd(), red);
+  acc = row_reduce<TPR>(acc, OpAdd(), red, nw);
   const float dot_hi = (float)acc;
   const float dot_lo = (float)(acc - (double)dot_hi);
   const float scale = p.scale;

@@ -352,6 +352,42 @@ def test_head_groups(dtype, tpr, nv, monkeypatch):
                         f"G={g} H={H} {mode}/{kind} causal={causal}"
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("tpr,nv", [(128, 1), (256, 1), (512, 1), (1024, 1), (256, 2), (128, 4)])
+def test_early_exit_of_future_wavefronts(dtype, tpr, nv, monkeypatch):
+    """Aligned rows whose causal bound (both alignments, more queries than
+    keys so that some rows see no key) or key length leaves whole wavefronts
+    of a row with no key to read: those wavefronts end early, forward and
+    backward, and the results are the oracle's and bit for bit those of the
+    kernels without the early exit."""
+    E = 4 if dtype == "f32" else 8
+    Sk = (tpr * (nv - 1) + tpr // 2 + 5) * E  # nv vectors per lane at tpr lanes
+    say(f"early exit dtype={dtype} TPR={tpr} NV={nv} Sk={Sk}")
+    monkeypatch.setenv("SMS_FORCE_TPR", str(tpr))
+    for Sq, causal, kind in ((Sk // 8 + 3, True, "none"), (Sk // 8 + 3, "bottom_right", "none"),
+                             (Sk + 40, "bottom_right", "none"), (5, False, "lengths"),
+                             (5, True, "lengths")):
+        shape = (1, 1, Sq, Sk) if Sq > Sk else (2, 2, Sq, Sk)
+        seed = zlib.crc32(f"ee/{dtype}/{tpr}/{nv}/{Sq}/{causal}/{kind}".encode()) % 10000
+        x = draw_x(shape, dtype, ("normal", 3.0), seed, DEV)
+        mask = (draw_lengths(shape[0], 0, Sk, seed + 1, DEV) if kind == "lengths" else None)
+        dy = draw_x(shape, dtype, ("normal", 1.0), seed + 2, DEV)
+        outs = {}
+        for early in ("0", "1"):
+            monkeypatch.setenv("SMS_EARLY", early)
+            y = fwd(x, mask, 0.3, causal)
+            outs[early] = (y, bwd(y, dy, 0.3, causal))
+        what = f"Sq={Sq} causal={causal} {kind}"
+        assert torch.equal(outs["0"][0], outs["1"][0]), what + " forward"
+        assert torch.equal(outs["0"][1], outs["1"][1]), what + " backward"
+        y, dx = outs["1"]
+        compare(decoded(y), oracle_fwd(x, mask, "key_lengths" if kind == "lengths" else "none",
+                                       0.3, causal, "lengths" if kind == "lengths" else "additive"),
+                dtype, what, rowsum=True)
+        compare(decoded(dx), oracle.backward(to_np(y), to_np(dy), dtype, 0.3), dtype,
+                what + " bwd")
+
+
 def test_forced_width_too_small_is_an_error(monkeypatch):
     monkeypatch.setenv("SMS_FORCE_TPR", "4")
     x = torch.zeros(1, 1, 2, 4096, device=DEV)
