@@ -404,7 +404,8 @@ sms_status sms_forward_ws(const void* x, const int64_t x_strides[4], const void*
   p.ws = static_cast<float2*>(workspace);
   p.heads = 1;
   p.div_hg = sms::make_fastdiv(1);
-  p.early = env_int("SMS_EARLY", 1);
+  // Only a causal rule or key lengths can leave a wavefront with no key.
+  p.early = (is_causal != 0 || p.mask_kind == sms::MASK_LEN) && env_int("SMS_EARLY", 1) != 0;
 
   if (pl.family != sms::FAMILY_STREAM && pl.family != sms::FAMILY_SPLIT && !f64) {
     // Aligned-row kernels: every operand's rows on 16-byte lines, whole vectors.
@@ -490,7 +491,8 @@ sms_status sms_backward_ws(const void* y, const int64_t y_strides[4], const void
   p.chunks = (uint32_t)pl.chunks;
   p.chunk_vec = (uint32_t)pl.chunk_vec;
   p.ws = static_cast<double*>(workspace);
-  p.early = env_int("SMS_EARLY", 1);
+  // Only the causal promise can leave a wavefront with no key.
+  p.early = is_causal != 0 && env_int("SMS_EARLY", 1) != 0;
 
   if (pl.family != sms::FAMILY_STREAM && pl.family != sms::FAMILY_SPLIT && !f64 &&
       ((Sk * bytes) & 15) == 0 &&

@@ -733,7 +733,7 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_bwd_kernel(BwdParams p) {
 // short rows, such as 1000 bf16 keys, measured up to 9 % faster for it).
 enum : int { FAST_PLAIN = 0 /* none, or key lengths */, FAST_ADD = 1, FAST_BOOL = 2 };
 
-template <class F, int TPR, int NV, int KIND>
+template <class F, int TPR, int NV, int KIND, bool EARLY>
 __global__ void __launch_bounds__(block_of(TPR)) sms_fwd_fast_kernel(FwdParams p) {
   constexpr int E = F::kE;
   constexpr int BY = F::kBytes;
@@ -765,22 +765,6 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_fwd_fast_kernel(FwdParams p
     xs = row_stream(xrow, (uint32_t)Sk * BY);
     ys = row_stream(yrow, (uint32_t)Sk * BY);
   }
-  // Wavefronts whose every vector lies past the key bound (the causal future,
-  // padding) store zeros and end; the others reduce among themselves.
-  int nw = TPR > 64 ? TPR / 64 : 1;
-  if constexpr (TPR > 64) {
-    if (p.early) {
-      nw = min(TPR / 64, (kload + 64 * E - 1) / (64 * E));
-      if ((int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= nw) {
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-          const int v = j * TPR + lane;
-          if (v * E < Sk) out_store<kBuf>(ys, yrow, exact, v, u32x4{0, 0, 0, 0});
-        }
-        return;
-      }
-    }
-  }
   u32x4 xr[NV], mr[NV];
   uint64_t mb[NV];
 #pragma unroll
@@ -791,6 +775,25 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_fwd_fast_kernel(FwdParams p
       else xr[j] = ld_stream(xrow + (int64_t)v * 16);
       if constexpr (KIND == FAST_ADD) mr[j] = ld_cached(mrow + (int64_t)v * 16);
       if constexpr (KIND == FAST_BOOL) mb[j] = ld_bits<E>(mrow + (int64_t)v * E);
+    }
+  }
+  // Wavefronts whose every vector lies past the key bound (the causal future,
+  // padding) loaded nothing: they store zeros and end, and the others reduce
+  // among themselves. (Tested after the loads are issued, so that the test
+  // does not delay them.)
+  // (A compile-time choice: the kernels without it are left exactly as they
+  // were, since any change to their code measurably moved the compiler's
+  // schedule of the non-causal fp32 forward.)
+  int nw = TPR > 64 ? TPR / 64 : 1;
+  if constexpr (EARLY && TPR > 64) {
+    nw = min(TPR / 64, (kload + 64 * E - 1) / (64 * E));
+    if ((int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= nw) {
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int v = j * TPR + lane;
+        if (v * E < Sk) out_store<kBuf>(ys, yrow, exact, v, u32x4{0, 0, 0, 0});
+      }
+      return;
     }
   }
   const float scale = p.scale;
@@ -985,7 +988,7 @@ __global__ void __launch_bounds__(TPR) sms_fwd_heads_kernel(FwdParams p) {
   }
 }
 
-template <class F, int TPR, int NV>
+template <class F, int TPR, int NV, bool EARLY>
 __global__ void __launch_bounds__(block_of(TPR)) sms_bwd_fast_kernel(BwdParams p) {
   constexpr int E = F::kE;
   constexpr int RPB = block_of(TPR) / TPR;
@@ -1003,22 +1006,6 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_bwd_fast_kernel(BwdParams p
     ds = row_stream(r.d, row_bytes);
     xs = row_stream(r.x, row_bytes);
   }
-  // Wavefronts whose every vector lies past the causal bound (y = 0 there)
-  // store zeros and end; the others reduce among themselves.
-  int nw = TPR > 64 ? TPR / 64 : 1;
-  if constexpr (TPR > 64) {
-    if (p.early) {
-      nw = min(TPR / 64, (kload + 64 * E - 1) / (64 * E));
-      if ((int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= nw) {
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-          const int v = j * TPR + lane;
-          if (v * E < (int)p.g.Sk) out_store<kBuf>(xs, r.x, exact, v, u32x4{0, 0, 0, 0});
-        }
-        return;
-      }
-    }
-  }
   u32x4 yr[NV], dr[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
@@ -1031,6 +1018,21 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_bwd_fast_kernel(BwdParams p
         yr[j] = ld_stream(r.y + (int64_t)v * 16);
         dr[j] = ld_stream(r.d + (int64_t)v * 16);
       }
+    }
+  }
+  // Wavefronts whose every vector lies past the causal bound (y = 0 there)
+  // loaded nothing: they store zeros and end, and the others reduce among
+  // themselves (tested after the loads are issued, so as not to delay them).
+  int nw = TPR > 64 ? TPR / 64 : 1;
+  if constexpr (EARLY && TPR > 64) {
+    nw = min(TPR / 64, (kload + 64 * E - 1) / (64 * E));
+    if ((int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= nw) {
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int v = j * TPR + lane;
+        if (v * E < (int)p.g.Sk) out_store<kBuf>(xs, r.x, exact, v, u32x4{0, 0, 0, 0});
+      }
+      return;
     }
   }
   double acc = 0.0;
@@ -1481,6 +1483,22 @@ hipError_t launch_heads(const FwdParams* fp, uint32_t blocks, hipStream_t st) {
 constexpr int kTprList[] = {4, 8, 16, 32, 64, 128, 256, 512, 1024};
 constexpr int kNvList[] = {1, 2, 4};
 
+template <class F, int TPR, int NV, bool EARLY>
+hipError_t launch_fwd_fast(const FwdParams* fp, uint32_t blocks, hipStream_t st) {
+  if constexpr (EARLY && TPR <= 64) {
+    return hipErrorInvalidValue;  // rows of one wavefront or less: nothing ends early
+  } else {
+    const dim3 grid(blocks), block(block_of(TPR));
+    if (fp->mask_kind == MASK_ADD)
+      hipLaunchKernelGGL((sms_fwd_fast_kernel<F, TPR, NV, FAST_ADD, EARLY>), grid, block, 0, st, *fp);
+    else if (fp->mask_kind == MASK_BOOL)
+      hipLaunchKernelGGL((sms_fwd_fast_kernel<F, TPR, NV, FAST_BOOL, EARLY>), grid, block, 0, st, *fp);
+    else
+      hipLaunchKernelGGL((sms_fwd_fast_kernel<F, TPR, NV, FAST_PLAIN, EARLY>), grid, block, 0, st, *fp);
+    return hipGetLastError();
+  }
+}
+
 template <class F, int TPR, int NV>
 hipError_t launch_nv(const FwdParams* fp, const BwdParams* bp, int family, uint32_t blocks,
                      hipStream_t st) {
@@ -1492,19 +1510,21 @@ hipError_t launch_nv(const FwdParams* fp, const BwdParams* bp, int family, uint3
       return launch_heads<F, TPR, NV, FAST_PLAIN>(fp, blocks, st);
     }
     if (family == FAMILY_ALIGNED) {
-      if (fp->mask_kind == MASK_ADD)
-        hipLaunchKernelGGL((sms_fwd_fast_kernel<F, TPR, NV, FAST_ADD>), grid, block, 0, st, *fp);
-      else if (fp->mask_kind == MASK_BOOL)
-        hipLaunchKernelGGL((sms_fwd_fast_kernel<F, TPR, NV, FAST_BOOL>), grid, block, 0, st, *fp);
-      else
-        hipLaunchKernelGGL((sms_fwd_fast_kernel<F, TPR, NV, FAST_PLAIN>), grid, block, 0, st, *fp);
+      if (fp->early && TPR > 64) return launch_fwd_fast<F, TPR, NV, true>(fp, blocks, st);
+      return launch_fwd_fast<F, TPR, NV, false>(fp, blocks, st);
     } else {
       hipLaunchKernelGGL((sms_fwd_kernel<F, TPR, NV>), grid, block, 0, st, *fp);
     }
   } else {
-    if (family == FAMILY_ALIGNED)
-      hipLaunchKernelGGL((sms_bwd_fast_kernel<F, TPR, NV>), grid, block, 0, st, *bp);
-    else
+    if (family == FAMILY_ALIGNED) {
+      if constexpr (TPR > 64) {
+        if (bp->early) {
+          hipLaunchKernelGGL((sms_bwd_fast_kernel<F, TPR, NV, true>), grid, block, 0, st, *bp);
+          return hipGetLastError();
+        }
+      }
+      hipLaunchKernelGGL((sms_bwd_fast_kernel<F, TPR, NV, false>), grid, block, 0, st, *bp);
+    } else
       hipLaunchKernelGGL((sms_bwd_kernel<F, TPR, NV>), grid, block, 0, st, *bp);
   }
   return hipGetLastError();
