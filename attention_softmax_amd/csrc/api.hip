@@ -564,6 +564,10 @@ sms_status sms_attention_forward(const void* q, const int64_t q_strides[4], cons
   p.mask_kind = !has_mask ? sms::ATTN_MASK_NONE
                 : shape_mode == SMS_MASK_KEY_LENGTHS ? sms::ATTN_MASK_LEN
                 : is_bool ? sms::ATTN_MASK_BOOL : sms::ATTN_MASK_ADD;
+  // Mask rows start on 4 elements (strides are multiples of Sk) and runs of 4
+  // keys stay inside a row: vector mask loads.
+  p.mask_vec = (p.mask_kind == sms::ATTN_MASK_ADD || p.mask_kind == sms::ATTN_MASK_BOOL) &&
+               Sk % 4 == 0 && aligned_to(mask, p.mask_kind == sms::ATTN_MASK_ADD ? 8 : 4);
   const hipError_t e = sms_attn_launch(&p, (int)dtype, (int)D, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SMS_OK : SMS_ERR_HIP;
 }
@@ -659,6 +663,10 @@ sms_status sms_attention_backward(const void* q, const int64_t q_strides[4], con
   p.mask_kind = !has_mask ? sms::ATTN_MASK_NONE
                 : shape_mode == SMS_MASK_KEY_LENGTHS ? sms::ATTN_MASK_LEN
                 : is_bool ? sms::ATTN_MASK_BOOL : sms::ATTN_MASK_ADD;
+  // Mask rows start on 4 elements (strides are multiples of Sk) and runs of 4
+  // keys stay inside a row: vector mask loads.
+  p.mask_vec = (p.mask_kind == sms::ATTN_MASK_ADD || p.mask_kind == sms::ATTN_MASK_BOOL) &&
+               Sk % 4 == 0 && aligned_to(mask, p.mask_kind == sms::ATTN_MASK_ADD ? 8 : 4);
   const hipError_t e =
       sms_attn_bwd_launch(&p, (int)dtype, (int)D, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SMS_OK : SMS_ERR_HIP;

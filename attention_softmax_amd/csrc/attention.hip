@@ -30,7 +30,9 @@ namespace {
 
 using namespace attn;
 
-template <bool BF16, int D, int KIND>
+// MV: additive / boolean mask rows allow the vector loads of load_mask_runs;
+// otherwise each mask value is read where it is used.
+template <bool BF16, int D, int KIND, bool MV>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(AttnParams p) {
   constexpr int BK = kAttnBk;
@@ -81,6 +83,9 @@ attn_fwd_kernel(AttnParams p) {
   if (p.causal) kq = min(kq, max(qi + off + 1, 0));
   const bool qvalid = qi < Sq;
   const int64_t mrow = (int64_t)b * p.sm_b + (int64_t)h * p.sm_h + (int64_t)qi * p.sm_q;
+  // The same for a query clamped into the mask (unconditional vector loads).
+  const int64_t mrow_c =
+      (int64_t)b * p.sm_b + (int64_t)h * p.sm_h + (int64_t)min(qi, Sq - 1) * p.sm_q;
 
   // Q fragment: the B operand of S^T = K Q^T (query qi, dims ks*16 + 8g .. +7).
   u32x4 qf[D / 16];
@@ -108,20 +113,42 @@ attn_fwd_kernel(AttnParams p) {
   const int vdg = tid % (D / 8), vkg = tid / (D / 8);
   const bool vthread = tid < VITEMS;
   u32x4 kreg[KC], vreg[4];
+  // With per-score mask loads (MV) the fetch is branch-free: every thread
+  // loads, at keys clamped to the last one the workgroup visits (rows past it
+  // hold copies of that row, finite, and their scores are excluded), so that
+  // the waits for this tile's mask values, issued before the fetch, are
+  // counted exactly and leave the fetch in flight. (A branch around the
+  // loads makes the count cover them too.)
+  const int vtid = MV ? tid % VITEMS : tid;
+  const int vdgl = vtid % (D / 8), vkgl = vtid / (D / 8);
   auto fetch = [&](int kt) {
+    if constexpr (MV) {
+      const int klast = kend - 1;
 #pragma unroll
-    for (int i = 0; i < KC; ++i) {
-      const int idx = tid + 256 * i, row = idx / KCH, ch = idx - row * KCH;
-      kreg[i] = u32x4{0, 0, 0, 0};
-      if (kt + row < Sk)
-        kreg[i] = *reinterpret_cast<const u32x4*>(kbase + ((int64_t)(kt + row) * p.sk_s + ch * 8) * 2);
-    }
+      for (int i = 0; i < KC; ++i) {
+        const int idx = tid + 256 * i, row = idx / KCH, ch = idx - row * KCH;
+        kreg[i] = *reinterpret_cast<const u32x4*>(
+            kbase + ((int64_t)min(kt + row, klast) * p.sk_s + ch * 8) * 2);
+      }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kt + 4 * vkg + i;
-      vreg[i] = u32x4{0, 0, 0, 0};
-      if (vthread && key < Sk)
-        vreg[i] = *reinterpret_cast<const u32x4*>(vbase + ((int64_t)key * p.sv_s + vdg * 8) * 2);
+      for (int i = 0; i < 4; ++i)
+        vreg[i] = *reinterpret_cast<const u32x4*>(
+            vbase + ((int64_t)min(kt + 4 * vkgl + i, klast) * p.sv_s + vdgl * 8) * 2);
+    } else {
+#pragma unroll
+      for (int i = 0; i < KC; ++i) {
+        const int idx = tid + 256 * i, row = idx / KCH, ch = idx - row * KCH;
+        kreg[i] = u32x4{0, 0, 0, 0};
+        if (kt + row < Sk)
+          kreg[i] = *reinterpret_cast<const u32x4*>(kbase + ((int64_t)(kt + row) * p.sk_s + ch * 8) * 2);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = kt + 4 * vkg + i;
+        vreg[i] = u32x4{0, 0, 0, 0};
+        if (vthread && key < Sk)
+          vreg[i] = *reinterpret_cast<const u32x4*>(vbase + ((int64_t)key * p.sv_s + vdg * 8) * 2);
+      }
     }
   };
   auto stage = [&]() {
@@ -145,7 +172,16 @@ attn_fwd_kernel(AttnParams p) {
     __syncthreads();  // the previous tile's LDS reads are done
     stage();
     __syncthreads();
-    if (kt + BK < kend) fetch(kt + BK);  // in flight during this tile's products
+    u32x2 mv[8];  // this tile's mask values (additive / boolean masks)
+    if constexpr (MV) {
+      load_mask_runs<KIND>(p.mask, mrow_c, kt, g, Sk, mv);
+      __builtin_amdgcn_sched_barrier(0);  // keep them ahead of the prefetch
+    }
+    if (MV || kt + BK < kend) fetch(kt + BK);  // in flight during this tile's products
+    // Keep the fetch ahead of the products (under register pressure the
+    // scheduler otherwise sinks the loads to the end of the loop, where the
+    // next tile's stage waits for them at once).
+    if constexpr (MV) __builtin_amdgcn_sched_barrier(0);
 
     // S^T for the tile's two 32-key blocks.
     f32x16 sacc[2];
@@ -171,12 +207,15 @@ attn_fwd_kernel(AttnParams p) {
         if (key >= kq || key >= Sk) {
           t = kNegInfA;
         } else if constexpr (KIND == ATTN_MASK_ADD) {
-          if (qvalid) {
-            const uint32_t bits = *reinterpret_cast<const uint16_t*>(p.mask + (mrow + key) * 2);
-            t = fmaf(to_float<BF16>(bits), kLog2eA, t);
-          }
+          uint32_t bits;
+          if constexpr (MV) bits = mask_run_value(mv, kb, r, false);
+          else bits = qvalid ? *reinterpret_cast<const uint16_t*>(p.mask + (mrow + key) * 2) : 0u;
+          t = fmaf(to_float<BF16>(bits), kLog2eA, t);
         } else if constexpr (KIND == ATTN_MASK_BOOL) {
-          if (qvalid && p.mask[mrow + key] != 0) t = kNegInfA;
+          uint32_t byte;
+          if constexpr (MV) byte = mask_run_value(mv, kb, r, true);
+          else byte = qvalid ? (uint32_t)(uint8_t)p.mask[mrow + key] : 0u;
+          if (byte != 0) t = kNegInfA;
         }
         sacc[kb][r] = t;
         mloc = fmaxf(mloc, t);
@@ -255,11 +294,18 @@ attn_fwd_kernel(AttnParams p) {
 template <bool BF16, int D>
 hipError_t launch_kind(const AttnParams& p, hipStream_t st) {
   const dim3 grid(p.H * p.B * ((p.Sq + kAttnBq - 1) / kAttnBq)), block(256);
+  const bool mv = p.mask_vec != 0;
   switch (p.mask_kind) {
-    case ATTN_MASK_NONE: hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_NONE>), grid, block, 0, st, p); break;
-    case ATTN_MASK_ADD: hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_ADD>), grid, block, 0, st, p); break;
-    case ATTN_MASK_BOOL: hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_BOOL>), grid, block, 0, st, p); break;
-    case ATTN_MASK_LEN: hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_LEN>), grid, block, 0, st, p); break;
+    case ATTN_MASK_NONE: hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_NONE, false>), grid, block, 0, st, p); break;
+    case ATTN_MASK_ADD:
+      if (mv) hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_ADD, true>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_ADD, false>), grid, block, 0, st, p);
+      break;
+    case ATTN_MASK_BOOL:
+      if (mv) hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_BOOL, true>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_BOOL, false>), grid, block, 0, st, p);
+      break;
+    case ATTN_MASK_LEN: hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_LEN, false>), grid, block, 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -31,6 +31,7 @@ struct AttnParams {
   float scale_log2;  // scale * log2(e): scores are kept in the log2 domain
   int causal;        // 0 none, 1 key k > q excluded, 2 key k > q + Sk - Sq excluded
   int mask_kind;     // 0 none, 1 additive, 2 bool, 3 key lengths
+  int mask_vec;      // every mask row starts on 4 elements and Sk % 4 == 0 (runs of 4 keys)
 };
 
 enum : int { ATTN_MASK_NONE = 0, ATTN_MASK_ADD = 1, ATTN_MASK_BOOL = 2, ATTN_MASK_LEN = 3 };
@@ -63,6 +64,7 @@ struct AttnBwdParams {
   float scale_log2;  // scale * log2(e)
   int causal;
   int mask_kind;
+  int mask_vec;      // as in AttnParams
 };
 
 // Keys per workgroup of the dK / dV kernel (four wavefronts x 32) and queries
@@ -139,6 +141,43 @@ __device__ inline __attribute__((always_inline)) float other_half_sum(float v) {
 // 16-bit element j (0..7) of an 8-element vector.
 __device__ inline __attribute__((always_inline)) uint32_t elem(const u32x4& v, int j) {
   return (v[j >> 1] >> ((j & 1) * 16)) & 0xffffu;
+}
+
+// Mask values of one lane's 32 keys of a 64-key tile in the query-stationary
+// layout (block kb, register r: key kt + 32 kb + 8 (r / 4) + 4 g + r % 4):
+// run i = 4 kb + r / 4 holds keys kt + 32 kb + 8 (i % 4) + 4 g .. + 3, read
+// as one 8-byte load (additive: four 16-bit values, .x keys 0-1, .y 2-3) or
+// one 4-byte load (boolean: four bytes in .x). Needs every mask row to start
+// on 4 elements and Sk % 4 == 0 (host-checked). The loads are unconditional:
+// `mrow` is the row of a query clamped into the mask and a run past the row
+// is read at the row's last run, so every address is inside the mask; the
+// values of keys the caller excludes (past its bounds) are never used. Being
+// straight-line, the loads are counted exactly by the wait that precedes
+// their first use, and since they are issued at the start of a tile, before
+// the next tile's prefetch, that wait leaves the prefetch in flight.
+template <int KIND>
+__device__ inline __attribute__((always_inline)) void load_mask_runs(
+    const char* mask, int64_t mrow, int kt, int g, int Sk, u32x2 (&mv)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int k0 = min(kt + (i >> 2) * 32 + 8 * (i & 3) + 4 * g, Sk - 4);
+    if constexpr (KIND == 1) {
+      mv[i] = *reinterpret_cast<const u32x2*>(mask + (mrow + k0) * 2);
+    } else {
+      mv[i].x = *reinterpret_cast<const uint32_t*>(mask + mrow + k0);
+      mv[i].y = 0;
+    }
+  }
+}
+
+// Value of register r (0..15) of block kb from load_mask_runs: the 16-bit
+// additive value, or the boolean byte.
+__device__ inline __attribute__((always_inline)) uint32_t mask_run_value(const u32x2 (&mv)[8],
+                                                                         int kb, int r, bool is_bool) {
+  const u32x2 run = mv[4 * kb + (r >> 2)];
+  const int e = r & 3;
+  if (is_bool) return (run.x >> (8 * e)) & 0xffu;
+  return (run[e >> 1] >> (16 * (e & 1))) & 0xffffu;
 }
 
 }  // namespace attn

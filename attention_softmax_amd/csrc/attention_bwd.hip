@@ -60,7 +60,7 @@ __global__ void __launch_bounds__(256) attn_delta_kernel(AttnBwdParams p) {
 
 // ---------------------------------------------------------------- 2. dQ
 
-template <bool BF16, int D, int KIND>
+template <bool BF16, int D, int KIND, bool MV>
 __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdParams p) {
   constexpr int BK = kAttnBk;
   constexpr int KP = D + 8;   // row-major tile pitch, elements
@@ -101,6 +101,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdParams p) {
   if (p.causal) kq = min(kq, max(qi + off + 1, 0));
   const bool qvalid = qi < Sq;
   const int64_t mrow = (int64_t)b * p.sm_b + (int64_t)h * p.sm_h + (int64_t)qi * p.sm_q;
+  // The same for a query clamped into the mask (unconditional vector loads).
+  const int64_t mrow_c =
+      (int64_t)b * p.sm_b + (int64_t)h * p.sm_h + (int64_t)min(qi, Sq - 1) * p.sm_q;
   const int64_t lrow = ((int64_t)b * p.H + h) * Sq + qi;
   const float lse = qvalid ? p.lse[lrow] : kNegInfA;
   const bool live = lse != kNegInfA;  // a query that sees no key has no gradient
@@ -134,20 +137,39 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdParams p) {
   const int kdg = tid % (D / 8), kkg = tid / (D / 8);
   const bool kthread = tid < KITEMS;
   u32x4 kreg[4], vreg[VC];
+  // With per-score mask loads (MV) the fetch is branch-free, at keys clamped
+  // to the last one the workgroup visits (as in the forward), so that the
+  // waits for this tile's mask values leave it in flight.
+  const int ktid = MV ? tid % KITEMS : tid;
+  const int kdgl = ktid % (D / 8), kkgl = ktid / (D / 8);
   auto fetch = [&](int kt) {
+    if constexpr (MV) {
+      const int klast = kend - 1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kt + 4 * kkg + i;
-      kreg[i] = u32x4{0, 0, 0, 0};
-      if (kthread && key < Sk)
-        kreg[i] = *reinterpret_cast<const u32x4*>(kbase + ((int64_t)key * p.sk_s + kdg * 8) * 2);
-    }
+      for (int i = 0; i < 4; ++i)
+        kreg[i] = *reinterpret_cast<const u32x4*>(
+            kbase + ((int64_t)min(kt + 4 * kkgl + i, klast) * p.sk_s + kdgl * 8) * 2);
 #pragma unroll
-    for (int i = 0; i < VC; ++i) {
-      const int idx = tid + 256 * i, row = idx / KCH, ch = idx - row * KCH;
-      vreg[i] = u32x4{0, 0, 0, 0};
-      if (kt + row < Sk)
-        vreg[i] = *reinterpret_cast<const u32x4*>(vbase + ((int64_t)(kt + row) * p.sv_s + ch * 8) * 2);
+      for (int i = 0; i < VC; ++i) {
+        const int idx = tid + 256 * i, row = idx / KCH, ch = idx - row * KCH;
+        vreg[i] = *reinterpret_cast<const u32x4*>(
+            vbase + ((int64_t)min(kt + row, klast) * p.sv_s + ch * 8) * 2);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = kt + 4 * kkg + i;
+        kreg[i] = u32x4{0, 0, 0, 0};
+        if (kthread && key < Sk)
+          kreg[i] = *reinterpret_cast<const u32x4*>(kbase + ((int64_t)key * p.sk_s + kdg * 8) * 2);
+      }
+#pragma unroll
+      for (int i = 0; i < VC; ++i) {
+        const int idx = tid + 256 * i, row = idx / KCH, ch = idx - row * KCH;
+        vreg[i] = u32x4{0, 0, 0, 0};
+        if (kt + row < Sk)
+          vreg[i] = *reinterpret_cast<const u32x4*>(vbase + ((int64_t)(kt + row) * p.sv_s + ch * 8) * 2);
+      }
     }
   };
   auto stage = [&]() {
@@ -174,7 +196,13 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdParams p) {
     __syncthreads();
     stage();
     __syncthreads();
-    if (kt + BK < kend) fetch(kt + BK);
+    u32x2 mv[8];  // this tile's mask values, loaded before the prefetch
+    if constexpr (MV) {
+      load_mask_runs<KIND>(p.mask, mrow_c, kt, g, Sk, mv);
+      __builtin_amdgcn_sched_barrier(0);  // keep them ahead of the prefetch
+    }
+    if (MV || kt + BK < kend) fetch(kt + BK);
+    if constexpr (MV) __builtin_amdgcn_sched_barrier(0);  // keep the fetch ahead of the products
 
     f32x16 sacc[2], dpacc[2];
 #pragma unroll
@@ -216,11 +244,18 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdParams p) {
           bool excluded = key >= kq || key >= Sk || !live;
           if constexpr (KIND == ATTN_MASK_ADD) {
             if (!excluded) {
-              const uint32_t bits = *reinterpret_cast<const uint16_t*>(p.mask + (mrow + key) * 2);
+              uint32_t bits;
+              if constexpr (MV) bits = mask_run_value(mv, kb, r, false);
+              else bits = *reinterpret_cast<const uint16_t*>(p.mask + (mrow + key) * 2);
               tv = fmaf(to_float<BF16>(bits), kLog2eA, tv);
             }
           } else if constexpr (KIND == ATTN_MASK_BOOL) {
-            if (!excluded && p.mask[mrow + key] != 0) excluded = true;
+            if (!excluded) {
+              uint32_t byte;
+              if constexpr (MV) byte = mask_run_value(mv, kb, r, true);
+              else byte = (uint32_t)(uint8_t)p.mask[mrow + key];
+              if (byte != 0) excluded = true;
+            }
           }
           const float pv = excluded ? 0.0f : __builtin_amdgcn_exp2f(tv - lse2);
           sacc[kb][r] = pv * (dpacc[kb][r] - delta);
@@ -343,18 +378,41 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdParams p) {
   const float smul = wave == 0 ? kLog2eA : 1.0f;  // LSE is staged in log2 units
   u32x4 treg[4];
   float sreg = 0.0f;
+  // With per-score mask loads the fetch is branch-free (as in the forward):
+  // every thread loads, at queries clamped to the last one (rows past it hold
+  // copies of it, finite, and their scores are excluded), threads beyond the
+  // Q / dO items and the LSE / delta lanes repeating loads of the first ones;
+  // the stage keeps what it needs.
+  constexpr bool kFlat = KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL;
+  const int fitem = kFlat ? tid % QITEMS : item;
+  const int fqdg = fitem % (D / 8), fqqg = fitem / (D / 8);
+  const char* fsrc = kFlat && tile_role > 1 ? p.q + (int64_t)b * p.sq_b * 2 : tsrc;
+  const int64_t fs_h = kFlat && tile_role > 1 ? p.sq_h : ts_h;
+  const int64_t fs_s = kFlat && tile_role > 1 ? p.sq_s : ts_s;
+  const float* fssrc = kFlat && wave > 1 ? p.lse : ssrc;
+  int sq_staged = 0;  // first query of the staged tile (the fill of LSE / delta past Sq)
   auto fetch = [&](uint32_t h, int qt) {
-    const char* base = tsrc + (int64_t)h * ts_h * 2;
+    if constexpr (kFlat) {
+      const char* base = fsrc + (int64_t)h * fs_h * 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = qt + 4 * qqg + i;
-      treg[i] = u32x4{0, 0, 0, 0};
-      if ((is_q || is_do) && q < Sq)
-        treg[i] = *reinterpret_cast<const u32x4*>(base + ((int64_t)q * ts_s + qdg * 8) * 2);
-    }
-    if (is_stat) {
-      const int q = qt + lane;
-      sreg = q < Sq ? ssrc[((int64_t)b * p.H + h) * Sq + q] * smul : sfill;
+      for (int i = 0; i < 4; ++i)
+        treg[i] = *reinterpret_cast<const u32x4*>(
+            base + ((int64_t)min(qt + 4 * fqqg + i, Sq - 1) * fs_s + fqdg * 8) * 2);
+      sreg = fssrc[((int64_t)b * p.H + h) * Sq + min(qt + (lane & (BQ - 1)), Sq - 1)];
+    } else {
+      const char* base = tsrc + (int64_t)h * ts_h * 2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = qt + 4 * qqg + i;
+        treg[i] = u32x4{0, 0, 0, 0};
+        if ((is_q || is_do) && q < Sq)
+          treg[i] = *reinterpret_cast<const u32x4*>(base + ((int64_t)q * ts_s + qdg * 8) * 2);
+      }
+      if (is_stat) {
+        const int q = qt + lane;
+        sreg = sfill;
+        if (q < Sq) sreg = ssrc[((int64_t)b * p.H + h) * Sq + q];
+      }
     }
   };
   auto stage = [&]() {
@@ -369,7 +427,12 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdParams p) {
         *reinterpret_cast<u32x2*>(&stage_tr[(8 * qdg + j) * TP + 4 * qqg]) = w;
       }
     }
-    if (is_stat) sdst[lane] = sreg;
+    // (LSE scaled to log2 units here, not as it arrives: an operation on the
+    // loaded value in the fetch would wait for it, and with it for the tile.)
+    if (is_stat) {
+      if constexpr (kFlat) sdst[lane] = sq_staged + lane < Sq ? sreg * smul : sfill;
+      else sdst[lane] = sreg * smul;
+    }
   };
 
   if (any && qstart < Sq) {
@@ -391,9 +454,40 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdParams p) {
       const int64_t mbase = (int64_t)b * p.sm_b + (int64_t)h * p.sm_h;
       {
         __syncthreads();
+        sq_staged = qt;
         stage();
         __syncthreads();
-        if (step + 1 < nstep) fetch(nh, nqt);
+        // This step's mask values of the lane's key, one per query (register
+        // r: query qt + 8 (r / 4) + 4 g + r % 4), loaded before the prefetch
+        // so that waiting for them leaves it in flight: 16-bit additive values
+        // two to a register, boolean bytes four to a register.
+        // (Each value in a register of its own until it is used: packing them
+        // as they arrive made the compiler wait for each load in turn.)
+        // The loads are unconditional, at a query and key clamped into the
+        // mask (values of excluded scores are never used), so that the wait
+        // for them is counted exactly instead of for every load in flight.
+        uint32_t mvk[16];
+        if constexpr (KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL) {
+          const int kjc = min(kj, Sk - 1);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qq = min(qt + 8 * (r >> 2) + 4 * g + (r & 3), Sq - 1);
+            const int64_t at = mbase + (int64_t)qq * p.sm_q + kjc;
+            if constexpr (KIND == ATTN_MASK_ADD)
+              mvk[r] = *reinterpret_cast<const uint16_t*>(p.mask + at * 2);
+            else
+              mvk[r] = (uint8_t)p.mask[at];
+          }
+          __builtin_amdgcn_sched_barrier(0);  // keep them ahead of the prefetch
+        }
+        if (kFlat) {
+          // Branch-free: the last step fetches its own tile again.
+          const bool more = step + 1 < nstep;
+          fetch(more ? nh : h, more ? nqt : qt);
+          __builtin_amdgcn_sched_barrier(0);  // keep the fetch ahead of the products
+        } else if (step + 1 < nstep) {
+          fetch(nh, nqt);
+        }
 
         f32x16 sacc, dpacc;
 #pragma unroll
@@ -443,13 +537,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdParams p) {
               bool excluded = qq >= Sq || kj >= klen || !kvalid || lse2 == kNegInfA ||
                               (p.causal && kj > qq + off);
               if constexpr (KIND == ATTN_MASK_ADD) {
-                if (!excluded) {
-                  const uint32_t bits = *reinterpret_cast<const uint16_t*>(
-                      p.mask + (mbase + (int64_t)qq * p.sm_q + kj) * 2);
-                  tv = fmaf(to_float<BF16>(bits), kLog2eA, tv);
-                }
+                if (!excluded) tv = fmaf(to_float<BF16>(mvk[r]), kLog2eA, tv);
               } else if constexpr (KIND == ATTN_MASK_BOOL) {
-                if (!excluded && p.mask[mbase + (int64_t)qq * p.sm_q + kj] != 0) excluded = true;
+                if (!excluded && mvk[r] != 0) excluded = true;
               }
               const float pv = excluded ? 0.0f : __builtin_amdgcn_exp2f(tv - lse2);
               pr[r] = pv;
@@ -513,8 +603,13 @@ hipError_t launch_bwd_kind(const AttnBwdParams& p, hipStream_t st) {
     hipLaunchKernelGGL((attn_delta_kernel<BF16, D>), dim3((uint32_t)wgs), block, 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, KIND>),
-                       dim3(p.H * p.B * ((p.Sq + kAttnBq - 1) / kAttnBq)), block, 0, st, p);
+    const dim3 gq(p.H * p.B * ((p.Sq + kAttnBq - 1) / kAttnBq));
+    if constexpr (KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL) {
+      if (p.mask_vec) hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, KIND, true>), gq, block, 0, st, p);
+      else hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, KIND, false>), gq, block, 0, st, p);
+    } else {
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, KIND, false>), gq, block, 0, st, p);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (p.Sk > 0)
