@@ -61,7 +61,8 @@ __global__ void __launch_bounds__(256) attn_delta_kernel(AttnBwdParams p) {
 // ---------------------------------------------------------------- 2. dQ
 
 template <bool BF16, int D, int KIND, bool MV>
-__global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdParams p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bwd_dq_kernel(AttnBwdParams p) {
   constexpr int BK = kAttnBk;
   constexpr int KP = D + 8;   // row-major tile pitch, elements
   constexpr int TP = BK + 4;  // transposed tile pitch, elements
@@ -204,43 +205,40 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdParams p) {
     if (MV || kt + BK < kend) fetch(kt + BK);
     if constexpr (MV) __builtin_amdgcn_sched_barrier(0);  // keep the fetch ahead of the products
 
-    f32x16 sacc[2], dpacc[2];
+    // dS^T = P (dP^T - delta), P recomputed from the forward's LSE, one
+    // 32-key block at a time (the block's products, probabilities and dQ
+    // contribution before the next block's, which keeps half the score
+    // registers live). A tile whose every score is visible to every query of
+    // the workgroup (keys in range and before the first query's causal bound,
+    // all queries in range, no per-score mask) skips the exclusion tests.
+    const bool full = KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL && q0 + kAttnBq <= Sq &&
+                      kt + BK <= klen && (!p.causal || kt + BK <= q0 + off + 1);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      f32x16 sacc, dpacc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        sacc[kb][r] = 0.0f;
-        dpacc[kb][r] = 0.0f;
+        sacc[r] = 0.0f;
+        dpacc[r] = 0.0f;
       }
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(&ks[(kb * 32 + c) * KP + s * 16 + 8 * g]);
-        sacc[kb] = mfma_32x32x16<BF16>(a, qf[s], sacc[kb]);
+        sacc = mfma_32x32x16<BF16>(a, qf[s], sacc);
         const u32x4 av = *reinterpret_cast<const u32x4*>(&vs[(kb * 32 + c) * KP + s * 16 + 8 * g]);
-        dpacc[kb] = mfma_32x32x16<BF16>(av, df[s], dpacc[kb]);
+        dpacc = mfma_32x32x16<BF16>(av, df[s], dpacc);
       }
-    }
-    // dS^T = P (dP^T - delta), P recomputed from the forward's LSE. A tile
-    // whose every score is visible to every query of the workgroup (keys in
-    // range and before the first query's causal bound, all queries in range,
-    // no per-score mask) skips the exclusion tests.
-    const bool full = KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL && q0 + kAttnBq <= Sq &&
-                      kt + BK <= klen && (!p.causal || kt + BK <= q0 + off + 1);
-    if (full) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      if (full) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.scale_log2, -lse2));
-          sacc[kb][r] = pv * (dpacc[kb][r] - delta);
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], p.scale_log2, -lse2));
+          sacc[r] = pv * (dpacc[r] - delta);
         }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          float tv = sacc[kb][r] * p.scale_log2;
+          float tv = sacc[r] * p.scale_log2;
           bool excluded = key >= kq || key >= Sk || !live;
           if constexpr (KIND == ATTN_MASK_ADD) {
             if (!excluded) {
@@ -258,27 +256,30 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdParams p) {
             }
           }
           const float pv = excluded ? 0.0f : __builtin_amdgcn_exp2f(tv - lse2);
-          sacc[kb][r] = pv * (dpacc[kb][r] - delta);
+          sacc[r] = pv * (dpacc[r] - delta);
         }
       }
-    }
-    u32x4 pb[4];
+      // B operands of the block's two k-steps (keys 16 s2 + 8 (j / 4) + 4 g
+      // + j % 4 of the block for element j).
+      u32x4 pb[2];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int kb = s >> 1, base = 8 * (s & 1);
-      pb[s] = u32x4{pack2<BF16>(sacc[kb][base + 0], sacc[kb][base + 1]),
-                    pack2<BF16>(sacc[kb][base + 2], sacc[kb][base + 3]),
-                    pack2<BF16>(sacc[kb][base + 4], sacc[kb][base + 5]),
-                    pack2<BF16>(sacc[kb][base + 6], sacc[kb][base + 7])};
-    }
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int base = 8 * s2;
+        pb[s2] = u32x4{pack2<BF16>(sacc[base + 0], sacc[base + 1]),
+                       pack2<BF16>(sacc[base + 2], sacc[base + 3]),
+                       pack2<BF16>(sacc[base + 4], sacc[base + 5]),
+                       pack2<BF16>(sacc[base + 6], sacc[base + 7])};
+      }
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const uint16_t* krow = &kts[(db * 32 + c) * TP];
+      for (int db = 0; db < D / 32; ++db) {
+        const uint16_t* krow = &kts[(db * 32 + c) * TP];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const u32x2 a0 = *reinterpret_cast<const u32x2*>(krow + 16 * s + 4 * g);
-        const u32x2 a1 = *reinterpret_cast<const u32x2*>(krow + 16 * s + 8 + 4 * g);
-        dq[db] = mfma_32x32x16<BF16>(u32x4{a0.x, a0.y, a1.x, a1.y}, pb[s], dq[db]);
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int s = 2 * kb + s2;
+          const u32x2 a0 = *reinterpret_cast<const u32x2*>(krow + 16 * s + 4 * g);
+          const u32x2 a1 = *reinterpret_cast<const u32x2*>(krow + 16 * s + 8 + 4 * g);
+          dq[db] = mfma_32x32x16<BF16>(u32x4{a0.x, a0.y, a1.x, a1.y}, pb[s2], dq[db]);
+        }
       }
     }
   }
