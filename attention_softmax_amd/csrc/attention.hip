@@ -162,7 +162,7 @@ attn_fwd_kernel(AttnParams p) {
       for (int j = 0; j < 8; ++j) {
         const u32x2 w{elem(vreg[0], j) | (elem(vreg[1], j) << 16),
                       elem(vreg[2], j) | (elem(vreg[3], j) << 16)};
-        *reinterpret_cast<u32x2*>(&vt[(8 * vdg + j) * VP + 4 * vkg]) = w;
+        *reinterpret_cast<u32x2*>(&vt[(8 * vdg + j) * VP + tcol(8 * vdg + j, vkg)]) = w;
       }
     }
   };
@@ -265,11 +265,12 @@ attn_fwd_kernel(AttnParams p) {
     }
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const uint16_t* vrow = &vt[(db * 32 + c) * VP];
+      const int vr = db * 32 + c;
+      const uint16_t* vrow = &vt[vr * VP];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const u32x2 a0 = *reinterpret_cast<const u32x2*>(vrow + 16 * s + 4 * g);
-        const u32x2 a1 = *reinterpret_cast<const u32x2*>(vrow + 16 * s + 8 + 4 * g);
+        const u32x2 a0 = *reinterpret_cast<const u32x2*>(vrow + tcol(vr, 4 * s + g));
+        const u32x2 a1 = *reinterpret_cast<const u32x2*>(vrow + tcol(vr, 4 * s + 2 + g));
         oacc[db] = mfma_32x32x16<BF16>(u32x4{a0.x, a0.y, a1.x, a1.y}, pb[s], oacc[db]);
       }
     }

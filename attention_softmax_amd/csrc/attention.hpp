@@ -138,6 +138,15 @@ __device__ inline __attribute__((always_inline)) float other_half_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Column (in elements) of the group of 4 consecutive elements qg in row d of
+// a transposed LDS tile. The group index is XOR-ed with (d / 16) % 8: the
+// staging writes (16 rows of one group per 16 lanes) then spread over all
+// banks instead of landing 8 to a bank, while the MFMA operand reads (32
+// consecutive rows, one group) stay conflict-free (32 banks; 2-way with 64).
+__device__ inline __attribute__((always_inline)) int tcol(int d, int qg) {
+  return 4 * (qg ^ ((d >> 4) & 7));
+}
+
 // 16-bit element j (0..7) of an 8-element vector.
 __device__ inline __attribute__((always_inline)) uint32_t elem(const u32x4& v, int j) {
   return (v[j >> 1] >> ((j & 1) * 16)) & 0xffffu;

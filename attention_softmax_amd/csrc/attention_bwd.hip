@@ -182,7 +182,7 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
       for (int j = 0; j < 8; ++j) {
         const u32x2 w{elem(kreg[0], j) | (elem(kreg[1], j) << 16),
                       elem(kreg[2], j) | (elem(kreg[3], j) << 16)};
-        *reinterpret_cast<u32x2*>(&kts[(8 * kdg + j) * TP + 4 * kkg]) = w;
+        *reinterpret_cast<u32x2*>(&kts[(8 * kdg + j) * TP + tcol(8 * kdg + j, kkg)]) = w;
       }
     }
 #pragma unroll
@@ -270,14 +270,21 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
                        pack2<BF16>(sacc[base + 4], sacc[base + 5]),
                        pack2<BF16>(sacc[base + 6], sacc[base + 7])};
       }
+      // The lane's row, opaque to the compiler here: the swizzled column
+      // offsets below are then recomputed per tile (a few VALU operations)
+      // instead of being held in registers across the loop, where they
+      // spilled.
+      int cl = c;
+      asm volatile("" : "+v"(cl));
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const uint16_t* krow = &kts[(db * 32 + c) * TP];
+        const int kr = db * 32 + cl;
+        const uint16_t* krow = &kts[kr * TP];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           const int s = 2 * kb + s2;
-          const u32x2 a0 = *reinterpret_cast<const u32x2*>(krow + 16 * s + 4 * g);
-          const u32x2 a1 = *reinterpret_cast<const u32x2*>(krow + 16 * s + 8 + 4 * g);
+          const u32x2 a0 = *reinterpret_cast<const u32x2*>(krow + tcol(kr, 4 * s + g));
+          const u32x2 a1 = *reinterpret_cast<const u32x2*>(krow + tcol(kr, 4 * s + 2 + g));
           dq[db] = mfma_32x32x16<BF16>(u32x4{a0.x, a0.y, a1.x, a1.y}, pb[s2], dq[db]);
         }
       }
@@ -299,8 +306,13 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
 
 // ------------------------------------------------------------ 3. dK, dV
 
-template <bool BF16, int D, int KIND>
-__global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdParams p) {
+// PASS 2 accumulates dK and dV together; for D = 128 that needs more than 256
+// registers (one wavefront per SIMD), so there PASS 0 (dV alone: S, P) and
+// PASS 1 (dK alone: S, dP, dS) run as two launches, each at two wavefronts
+// per SIMD, recomputing S in both.
+template <bool BF16, int D, int KIND, int PASS>
+__device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdParams& p) {
+  constexpr bool kDV = PASS != 1, kDK = PASS != 0;
   constexpr int BQ = kAttnBwdBq;
   constexpr int RP = D + 8;   // row-major tile pitch, elements
   constexpr int TP = BQ + 4;  // transposed tile pitch, elements (18 dwords)
@@ -331,7 +343,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdParams p) {
     vf[s] = u32x4{0, 0, 0, 0};
     if (kvalid) {
       kf[s] = *reinterpret_cast<const u32x4*>(kbase + ((int64_t)kj * p.sk_s + s * 16 + 8 * g) * 2);
-      vf[s] = *reinterpret_cast<const u32x4*>(vbase + ((int64_t)kj * p.sv_s + s * 16 + 8 * g) * 2);
+      if constexpr (kDK)
+        vf[s] = *reinterpret_cast<const u32x4*>(vbase + ((int64_t)kj * p.sv_s + s * 16 + 8 * g) * 2);
     }
   }
   f32x16 dk[D / 32], dv[D / 32];
@@ -425,7 +438,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdParams p) {
       for (int j = 0; j < 8; ++j) {
         const u32x2 w{elem(treg[0], j) | (elem(treg[1], j) << 16),
                       elem(treg[2], j) | (elem(treg[3], j) << 16)};
-        *reinterpret_cast<u32x2*>(&stage_tr[(8 * qdg + j) * TP + 4 * qqg]) = w;
+        *reinterpret_cast<u32x2*>(&stage_tr[(8 * qdg + j) * TP + tcol(8 * qdg + j, qqg)]) = w;
       }
     }
     // (LSE scaled to log2 units here, not as it arrives: an operation on the
@@ -500,8 +513,10 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdParams p) {
         for (int s = 0; s < D / 16; ++s) {
           const u32x4 a = *reinterpret_cast<const u32x4*>(&qs[c * RP + s * 16 + 8 * g]);
           sacc = mfma_32x32x16<BF16>(a, kf[s], sacc);
-          const u32x4 ad = *reinterpret_cast<const u32x4*>(&dos[c * RP + s * 16 + 8 * g]);
-          dpacc = mfma_32x32x16<BF16>(ad, vf[s], dpacc);
+          if constexpr (kDK) {
+            const u32x4 ad = *reinterpret_cast<const u32x4*>(&dos[c * RP + s * 16 + 8 * g]);
+            dpacc = mfma_32x32x16<BF16>(ad, vf[s], dpacc);
+          }
         }
         // Register r holds query qt + 8*(r/4) + 4g + r%4 of this lane's key.
         float pr[16], dsr[16];
@@ -560,16 +575,21 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdParams p) {
         }
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const uint16_t* dorow = &dots[(db * 32 + c) * TP];
-          const uint16_t* qrow = &qts[(db * 32 + c) * TP];
+          const int tr = db * 32 + c;
+          const uint16_t* dorow = &dots[tr * TP];
+          const uint16_t* qrow = &qts[tr * TP];
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
-            const u32x2 a0 = *reinterpret_cast<const u32x2*>(dorow + 16 * s + 4 * g);
-            const u32x2 a1 = *reinterpret_cast<const u32x2*>(dorow + 16 * s + 8 + 4 * g);
-            dv[db] = mfma_32x32x16<BF16>(u32x4{a0.x, a0.y, a1.x, a1.y}, pb[s], dv[db]);
-            const u32x2 b0 = *reinterpret_cast<const u32x2*>(qrow + 16 * s + 4 * g);
-            const u32x2 b1 = *reinterpret_cast<const u32x2*>(qrow + 16 * s + 8 + 4 * g);
-            dk[db] = mfma_32x32x16<BF16>(u32x4{b0.x, b0.y, b1.x, b1.y}, sb[s], dk[db]);
+            if constexpr (kDV) {
+              const u32x2 a0 = *reinterpret_cast<const u32x2*>(dorow + tcol(tr, 4 * s + g));
+              const u32x2 a1 = *reinterpret_cast<const u32x2*>(dorow + tcol(tr, 4 * s + 2 + g));
+              dv[db] = mfma_32x32x16<BF16>(u32x4{a0.x, a0.y, a1.x, a1.y}, pb[s], dv[db]);
+            }
+            if constexpr (kDK) {
+              const u32x2 b0 = *reinterpret_cast<const u32x2*>(qrow + tcol(tr, 4 * s + g));
+              const u32x2 b1 = *reinterpret_cast<const u32x2*>(qrow + tcol(tr, 4 * s + 2 + g));
+              dk[db] = mfma_32x32x16<BF16>(u32x4{b0.x, b0.y, b1.x, b1.y}, sb[s], dk[db]);
+            }
           }
         }
       }
@@ -585,13 +605,30 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdParams p) {
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
       const int d = db * 32 + 8 * rg + 4 * g;
-      const u32x2 wk{pack2<BF16>(dk[db][4 * rg] * sc, dk[db][4 * rg + 1] * sc),
-                     pack2<BF16>(dk[db][4 * rg + 2] * sc, dk[db][4 * rg + 3] * sc)};
-      const u32x2 wv{pack2<BF16>(dv[db][4 * rg], dv[db][4 * rg + 1]),
-                     pack2<BF16>(dv[db][4 * rg + 2], dv[db][4 * rg + 3])};
-      *reinterpret_cast<u32x2*>(dkrow + d * 2) = wk;
-      *reinterpret_cast<u32x2*>(dvrow + d * 2) = wv;
+      if constexpr (kDK) {
+        const u32x2 wk{pack2<BF16>(dk[db][4 * rg] * sc, dk[db][4 * rg + 1] * sc),
+                       pack2<BF16>(dk[db][4 * rg + 2] * sc, dk[db][4 * rg + 3] * sc)};
+        *reinterpret_cast<u32x2*>(dkrow + d * 2) = wk;
+      }
+      if constexpr (kDV) {
+        const u32x2 wv{pack2<BF16>(dv[db][4 * rg], dv[db][4 * rg + 1]),
+                       pack2<BF16>(dv[db][4 * rg + 2], dv[db][4 * rg + 3])};
+        *reinterpret_cast<u32x2*>(dvrow + d * 2) = wv;
+      }
     }
+}
+
+// Entry points: the single passes at two wavefronts per SIMD; both
+// gradients together with the registers the compiler needs (D = 64 fits two
+// wavefronts per SIMD as it is).
+template <bool BF16, int D, int KIND, int PASS>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bwd_dkdv_kernel(AttnBwdParams p) {
+  dkdv_body<BF16, D, KIND, PASS>(p);
+}
+template <bool BF16, int D, int KIND>
+__global__ void __launch_bounds__(256) attn_bwd_dkdv_both_kernel(AttnBwdParams p) {
+  dkdv_body<BF16, D, KIND, 2>(p);
 }
 
 template <bool BF16, int D, int KIND>
@@ -613,9 +650,20 @@ hipError_t launch_bwd_kind(const AttnBwdParams& p, hipStream_t st) {
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (p.Sk > 0)
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<BF16, D, KIND>),
-                       dim3(p.Hk * p.B * ((p.Sk + kAttnBwdBk - 1) / kAttnBwdBk)), block, 0, st, p);
+  if (p.Sk > 0) {
+    const dim3 gk(p.Hk * p.B * ((p.Sk + kAttnBwdBk - 1) / kAttnBwdBk));
+    // D = 128: two passes at two wavefronts per SIMD, measured faster than
+    // both gradients in one pass at one (fp16 [4,32,4096,128] causal
+    // backward 4.72 against 5.28 ms; not causal 6.02 against 6.66 ms).
+    if constexpr (D == 128) {
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<BF16, D, KIND, 0>), gk, block, 0, st, p);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<BF16, D, KIND, 1>), gk, block, 0, st, p);
+    } else {
+      hipLaunchKernelGGL((attn_bwd_dkdv_both_kernel<BF16, D, KIND>), gk, block, 0, st, p);
+    }
+  }
   return hipGetLastError();
 }
 
