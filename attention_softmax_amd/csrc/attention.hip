@@ -82,6 +82,10 @@ attn_fwd_kernel(AttnParams p) {
   int kq = klen;
   if (p.causal) kq = min(kq, max(qi + off + 1, 0));
   const bool qvalid = qi < Sq;
+  // Tiles may skip the per-score tests (see the loop) without a per-score
+  // mask and with a positive scale. Queries past Sq need no test: their rows
+  // are finite (Q = 0) and never stored.
+  const bool fast_ok = (KIND == ATTN_MASK_NONE || KIND == ATTN_MASK_LEN) && p.scale_log2 > 0.0f;
   const int64_t mrow = (int64_t)b * p.sm_b + (int64_t)h * p.sm_h + (int64_t)qi * p.sm_q;
   // The same for a query clamped into the mask (unconditional vector loads).
   const int64_t mrow_c =
@@ -113,42 +117,28 @@ attn_fwd_kernel(AttnParams p) {
   const int vdg = tid % (D / 8), vkg = tid / (D / 8);
   const bool vthread = tid < VITEMS;
   u32x4 kreg[KC], vreg[4];
-  // With per-score mask loads (MV) the fetch is branch-free: every thread
-  // loads, at keys clamped to the last one the workgroup visits (rows past it
-  // hold copies of that row, finite, and their scores are excluded), so that
-  // the waits for this tile's mask values, issued before the fetch, are
-  // counted exactly and leave the fetch in flight. (A branch around the
-  // loads makes the count cover them too.)
-  const int vtid = MV ? tid % VITEMS : tid;
-  const int vdgl = vtid % (D / 8), vkgl = vtid / (D / 8);
+  // The fetch reads through buffer resources re-based on each tile (scalar
+  // registers) that end at the last key: rows past it read as zero, with no
+  // per-load test or branch, and each thread's byte offsets within a tile
+  // stay fixed. Being unconditional, the loads also keep the wait for a
+  // tile's mask values (issued before the fetch) from covering the fetch.
+  uint32_t koff[KC], voff[4];
+#pragma unroll
+  for (int i = 0; i < KC; ++i) {
+    const int idx = tid + 256 * i, row = idx / KCH, ch = idx - row * KCH;
+    koff[i] = (uint32_t)(row * p.sk_s * 2 + ch * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)((4 * vkg + i) * p.sv_s * 2 + vdg * 16);
   auto fetch = [&](int kt) {
-    if constexpr (MV) {
-      const int klast = kend - 1;
+    const int rows = Sk - kt;
+    const auto kr = rows_rsrc(kbase + (int64_t)kt * p.sk_s * 2, min(rows, BK), p.sk_s * 2, D * 2);
 #pragma unroll
-      for (int i = 0; i < KC; ++i) {
-        const int idx = tid + 256 * i, row = idx / KCH, ch = idx - row * KCH;
-        kreg[i] = *reinterpret_cast<const u32x4*>(
-            kbase + ((int64_t)min(kt + row, klast) * p.sk_s + ch * 8) * 2);
-      }
+    for (int i = 0; i < KC; ++i) kreg[i] = rsrc_load(kr, koff[i]);
+    if (vthread) {
+      const auto vr = rows_rsrc(vbase + (int64_t)kt * p.sv_s * 2, min(rows, BK), p.sv_s * 2, D * 2);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        vreg[i] = *reinterpret_cast<const u32x4*>(
-            vbase + ((int64_t)min(kt + 4 * vkgl + i, klast) * p.sv_s + vdgl * 8) * 2);
-    } else {
-#pragma unroll
-      for (int i = 0; i < KC; ++i) {
-        const int idx = tid + 256 * i, row = idx / KCH, ch = idx - row * KCH;
-        kreg[i] = u32x4{0, 0, 0, 0};
-        if (kt + row < Sk)
-          kreg[i] = *reinterpret_cast<const u32x4*>(kbase + ((int64_t)(kt + row) * p.sk_s + ch * 8) * 2);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kt + 4 * vkg + i;
-        vreg[i] = u32x4{0, 0, 0, 0};
-        if (vthread && key < Sk)
-          vreg[i] = *reinterpret_cast<const u32x4*>(vbase + ((int64_t)key * p.sv_s + vdg * 8) * 2);
-      }
+      for (int i = 0; i < 4; ++i) vreg[i] = rsrc_load(vr, voff[i]);
     }
   };
   auto stage = [&]() {
@@ -167,6 +157,8 @@ attn_fwd_kernel(AttnParams p) {
     }
   };
   if (kend > 0) fetch(0);
+  // This lane's V^T operand rows c, c + 32, ... (tcol's lane part included).
+  const uint16_t* vlane = &vt[c * VP + tcol_lane(c, g)];
 
   for (int kt = 0; kt < kend; kt += BK) {
     __syncthreads();  // the previous tile's LDS reads are done
@@ -183,21 +175,38 @@ attn_fwd_kernel(AttnParams p) {
     // next tile's stage waits for them at once).
     if constexpr (MV) __builtin_amdgcn_sched_barrier(0);
 
-    // S^T for the tile's two 32-key blocks.
+    // S^T for the tile's two 32-key blocks, alternating between the blocks so
+    // that consecutive products are independent (each K fragment's LDS read
+    // then has a product's time to arrive).
     f32x16 sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
+    for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(&ks[(kb * 32 + c) * KP + s * 16 + 8 * g]);
         sacc[kb] = mfma_32x32x16<BF16>(a, qf[s], sacc[kb]);
       }
-    }
 
-    // Scores in the log2 domain, the mask and the key bounds.
+    // Scores in the log2 domain, the mask and the key bounds. A tile whose
+    // every score is visible to every query of the workgroup (keys in range
+    // and, with a causal rule, before the first query's bound; no per-score
+    // mask) skips the exclusion tests, and with a positive scale it takes the
+    // maximum of the raw scores (scaling is monotonic, so the scaled maximum
+    // is the same rounded value) and folds the scale into the exponential's
+    // argument below.
+    const bool full = fast_ok && kt + BK <= klen && (!p.causal || kt + BK <= q0 + off + 1);
     float mloc = kNegInfA;
+    if (full) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[kb][r]);
+      mloc *= p.scale_log2;
+    } else {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -221,6 +230,7 @@ attn_fwd_kernel(AttnParams p) {
         mloc = fmaxf(mloc, t);
       }
     }
+    }
     mloc = other_half_max(mloc);
     // The reference maximum m_i moves only when a score exceeds it by more
     // than kLazy (log2 units): probabilities then stay below 2^kLazy, far
@@ -236,14 +246,25 @@ attn_fwd_kernel(AttnParams p) {
     }
     const float m_use = (m_i == kNegInfA) ? 0.0f : m_i;  // nothing visible yet
     float psum = 0.0f;
+    if (full) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(sacc[kb][r] - m_use);
-        sacc[kb][r] = pv;
-        psum += pv;
-      }
+        for (int r = 0; r < 16; ++r) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.scale_log2, -m_use));
+          sacc[kb][r] = pv;
+          psum += pv;
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = __builtin_amdgcn_exp2f(sacc[kb][r] - m_use);
+          sacc[kb][r] = pv;
+          psum += pv;
+        }
+    }
     l_i += psum;
     const bool rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
     // P as the B operand of O^T += V^T P^T: k-step s takes registers
@@ -263,17 +284,16 @@ attn_fwd_kernel(AttnParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= corr;
     }
+    // (k-steps outer, dimension blocks inner: consecutive products independent.)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int vr = db * 32 + c;
-      const uint16_t* vrow = &vt[vr * VP];
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const u32x2 a0 = *reinterpret_cast<const u32x2*>(vrow + tcol(vr, 4 * s + g));
-        const u32x2 a1 = *reinterpret_cast<const u32x2*>(vrow + tcol(vr, 4 * s + 2 + g));
+      for (int db = 0; db < D / 32; ++db) {
+        const uint16_t* vrow = vlane + db * 32 * VP;
+        const u32x2 a0 = *reinterpret_cast<const u32x2*>(vrow + tcol_const(db, 2 * s));
+        const u32x2 a1 = *reinterpret_cast<const u32x2*>(vrow + tcol_const(db, 2 * s + 1));
         oacc[db] = mfma_32x32x16<BF16>(u32x4{a0.x, a0.y, a1.x, a1.y}, pb[s], oacc[db]);
       }
-    }
   }
 
   const float L = other_half_sum(l_i);  // both halves of the query's keys

@@ -143,9 +143,41 @@ __device__ inline __attribute__((always_inline)) float other_half_sum(float v) {
 // staging writes (16 rows of one group per 16 lanes) then spread over all
 // banks instead of landing 8 to a bank, while the MFMA operand reads (32
 // consecutive rows, one group) stay conflict-free (32 banks; 2-way with 64).
-__device__ inline __attribute__((always_inline)) int tcol(int d, int qg) {
-  return 4 * (qg ^ ((d >> 4) & 7));
+// A raw buffer (stride 0) over `rows` rows of `row_bytes` bytes, `pitch`
+// bytes apart, from `base` (wave-uniform): loads at offsets past the last
+// row's bytes return zero without touching memory. Row pitches are at most
+// 2^25 bytes (checked on the host), so a tile of up to 64 rows fits the
+// 31-bit record count.
+constexpr int kRsrcWord3A = 0x00020000;  // fourth descriptor word of a raw buffer (gfx9)
+__device__ inline __attribute__((always_inline)) __amdgpu_buffer_rsrc_t
+rows_rsrc(const char* base, int rows, int64_t pitch, int row_bytes) {
+  const int bytes = rows > 0 ? (int)((int64_t)(rows - 1) * pitch + row_bytes) : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes, kRsrcWord3A);
 }
+__device__ inline __attribute__((always_inline)) u32x4 rsrc_load(__amdgpu_buffer_rsrc_t r,
+                                                                 uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+__host__ __device__ constexpr int tcol(int d, int qg) { return 4 * (qg ^ ((d >> 4) & 7)); }
+
+// tcol for an operand read of row d = 32 * blk + c (c < 32) and group
+// qg = 2 * h + g (g < 2), split into a part that depends on the lane (c, g)
+// and a part fixed at compile time (blk, h): the lane's bits (g and
+// (c / 16) % 2) make up bit 0 of the group index and the XOR, which the
+// compile-time bits never reach, so the XOR becomes a sum. One address
+// register per lane then serves every read, with immediate offsets.
+__host__ __device__ constexpr int tcol_lane(int c, int g) { return 4 * (g ^ ((c >> 4) & 1)); }
+__host__ __device__ constexpr int tcol_const(int blk, int h) { return 4 * ((2 * h) ^ ((2 * blk) & 7)); }
+constexpr bool tcol_split_holds() {
+  for (int blk = 0; blk < 8; ++blk)
+    for (int c = 0; c < 32; ++c)
+      for (int h = 0; h < 8; ++h)
+        for (int g = 0; g < 2; ++g)
+          if (tcol(32 * blk + c, 2 * h + g) != tcol_lane(c, g) + tcol_const(blk, h)) return false;
+  return true;
+}
+static_assert(tcol_split_holds(), "tcol must split into lane and compile-time parts");
 
 // 16-bit element j (0..7) of an 8-element vector.
 __device__ inline __attribute__((always_inline)) uint32_t elem(const u32x4& v, int j) {

@@ -29,6 +29,10 @@ sms_status check_strides(const int64_t st[4]) {
 
 bool aligned_to(const void* p, int bytes) { return ((uintptr_t)p % (uintptr_t)bytes) == 0; }
 
+// Largest key / value row stride (elements): a tile of 64 rows is read
+// through one buffer range, whose byte count must fit 31 bits.
+constexpr int64_t kMaxRowStride = int64_t(1) << 24;
+
 // A fused attention launch over `rows` rows per (head, batch) in tiles of 128
 // is one workgroup of 256 threads per (tile, head, batch): the dispatch's
 // work-item count must fit 32 bits.
@@ -84,6 +88,7 @@ sms_status sms_attention_forward(const void* q, const int64_t q_strides[4], cons
   for (const int64_t* s : {q_strides, k_strides, v_strides, o_strides})
     if ((st = check_strides(s)) != SMS_OK) return st;
   if (Sq > INT32_MAX || Sk > INT32_MAX || attn_grid_too_large(Sq, H, B)) return SMS_ERR_SHAPE;
+  if (k_strides[2] > kMaxRowStride || v_strides[2] > kMaxRowStride) return SMS_ERR_STRIDE;
   // Every row of Q, K, V and O starts on a 16-byte line (head dims of 8 elements).
   for (const auto& t : {std::make_pair(q, q_strides), std::make_pair(k, k_strides),
                         std::make_pair(v, v_strides),

@@ -246,7 +246,9 @@ sms_status sms_backward_ws(const void* y, const int64_t y_strides[4],
  * is contiguous (stride[3] == 1). With Sk == 0, k, v and a mask other than
  * key lengths are never read and may be NULL. Limits: Sq, Sk < 2^31 and
  * ceil(Sq / 128) * H * B < 2^24 (one 256-thread workgroup per 128 queries of a
- * head; else SMS_ERR_SHAPE). The backward is sms_attention_backward.
+ * head; else SMS_ERR_SHAPE); the key and value row strides k_strides[2] and
+ * v_strides[2] at most 2^24 elements (tiles are read through 32-bit buffer
+ * ranges; else SMS_ERR_STRIDE). The backward is sms_attention_backward.
  */
 sms_status sms_attention_forward(const void* q, const int64_t q_strides[4],
                                  const void* k, const int64_t k_strides[4],

@@ -129,6 +129,11 @@ def test_attention_errors():
     with pytest.raises(SmsError, match="ALIGN"):  # rows not on 16-byte lines
         big = torch.zeros(1, 1, 4, 72, dtype=torch.float16, device=DEV)[..., 4:68]
         sms_attention_forward(big, q, q)
+    with pytest.raises(SmsError, match="STRIDE"):  # key rows more than 2^24 elements apart
+        rs = (1 << 24) + 8
+        kv = torch.zeros(rs + 64, dtype=torch.float16, device=DEV).as_strided(
+            (1, 1, 2, 64), (2 * rs, 2 * rs, rs, 1))
+        sms_attention_forward(torch.zeros(1, 1, 2, 64, dtype=torch.float16, device=DEV), kv, kv)
     empty = torch.zeros(1, 1, 0, 64, dtype=torch.float16, device=DEV)
     sms_attention_forward(empty, q, q)  # no query: a no-op
 
