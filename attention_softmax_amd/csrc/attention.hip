@@ -128,18 +128,20 @@ attn_fwd_kernel(AttnParams p) {
     const int idx = tid + 256 * i, row = idx / KCH, ch = idx - row * KCH;
     koff[i] = (uint32_t)(row * p.sk_s * 2 + ch * 16);
   }
+  // (Threads past the V items, with D = 64, load a copy of another
+  // thread's item: a branch around their loads would make the wait for the
+  // mask values cover the fetch too.)
+  const int vtid = tid % VITEMS, vdgl = vtid % (D / 8), vkgl = vtid / (D / 8);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)((4 * vkg + i) * p.sv_s * 2 + vdg * 16);
+  for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)((4 * vkgl + i) * p.sv_s * 2 + vdgl * 16);
   auto fetch = [&](int kt) {
-    const int rows = Sk - kt;
-    const auto kr = rows_rsrc(kbase + (int64_t)kt * p.sk_s * 2, min(rows, BK), p.sk_s * 2, D * 2);
+    const int rows = min(Sk - kt, BK);
+    const auto kr = rows_rsrc(kbase + (int64_t)kt * p.sk_s * 2, rows, p.sk_s * 2, D * 2);
+    const auto vr = rows_rsrc(vbase + (int64_t)kt * p.sv_s * 2, rows, p.sv_s * 2, D * 2);
 #pragma unroll
     for (int i = 0; i < KC; ++i) kreg[i] = rsrc_load(kr, koff[i]);
-    if (vthread) {
-      const auto vr = rows_rsrc(vbase + (int64_t)kt * p.sv_s * 2, min(rows, BK), p.sv_s * 2, D * 2);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vreg[i] = rsrc_load(vr, voff[i]);
-    }
+    for (int i = 0; i < 4; ++i) vreg[i] = rsrc_load(vr, voff[i]);
   };
   auto stage = [&]() {
 #pragma unroll

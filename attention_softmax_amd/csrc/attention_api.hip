@@ -172,6 +172,8 @@ sms_status sms_attention_backward(const void* q, const int64_t q_strides[4], con
     if ((st = check_strides(s)) != SMS_OK) return st;
   if (Sq > INT32_MAX || Sk > INT32_MAX) return SMS_ERR_SHAPE;
   if (attn_grid_too_large(Sq, H, B) || attn_grid_too_large(Sk, Hk, B)) return SMS_ERR_SHAPE;
+  for (const int64_t* s : {q_strides, k_strides, v_strides, dout_strides})
+    if (s[2] > kMaxRowStride) return SMS_ERR_STRIDE;
   const int64_t need = sms_attention_workspace_bytes(B, H, Sq);
   if (need < 0) return SMS_ERR_SHAPE;
   for (const auto& t :

@@ -138,40 +138,28 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
   const int kdg = tid % (D / 8), kkg = tid / (D / 8);
   const bool kthread = tid < KITEMS;
   u32x4 kreg[4], vreg[VC];
-  // With per-score mask loads (MV) the fetch is branch-free, at keys clamped
-  // to the last one the workgroup visits (as in the forward), so that the
-  // waits for this tile's mask values leave it in flight.
-  const int ktid = MV ? tid % KITEMS : tid;
-  const int kdgl = ktid % (D / 8), kkgl = ktid / (D / 8);
+  // The fetch reads through buffer ranges re-based on each tile that end at
+  // the last key (rows past it read as zero), with fixed per-thread offsets
+  // and no per-load test or branch; threads past the K items (D = 64) load a
+  // copy of another thread's item, so that the wait for a tile's mask values
+  // does not cover the fetch.
+  uint32_t koff[4], voff[VC];
+  const int ktid = tid % KITEMS, kdgl = ktid % (D / 8), kkgl = ktid / (D / 8);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) koff[i] = (uint32_t)((4 * kkgl + i) * p.sk_s * 2 + kdgl * 16);
+#pragma unroll
+  for (int i = 0; i < VC; ++i) {
+    const int idx = tid + 256 * i, row = idx / KCH, ch = idx - row * KCH;
+    voff[i] = (uint32_t)(row * p.sv_s * 2 + ch * 16);
+  }
   auto fetch = [&](int kt) {
-    if constexpr (MV) {
-      const int klast = kend - 1;
+    const int rows = min(Sk - kt, BK);
+    const auto kr = rows_rsrc(kbase + (int64_t)kt * p.sk_s * 2, rows, p.sk_s * 2, D * 2);
+    const auto vr = rows_rsrc(vbase + (int64_t)kt * p.sv_s * 2, rows, p.sv_s * 2, D * 2);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        kreg[i] = *reinterpret_cast<const u32x4*>(
-            kbase + ((int64_t)min(kt + 4 * kkgl + i, klast) * p.sk_s + kdgl * 8) * 2);
+    for (int i = 0; i < 4; ++i) kreg[i] = rsrc_load(kr, koff[i]);
 #pragma unroll
-      for (int i = 0; i < VC; ++i) {
-        const int idx = tid + 256 * i, row = idx / KCH, ch = idx - row * KCH;
-        vreg[i] = *reinterpret_cast<const u32x4*>(
-            vbase + ((int64_t)min(kt + row, klast) * p.sv_s + ch * 8) * 2);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kt + 4 * kkg + i;
-        kreg[i] = u32x4{0, 0, 0, 0};
-        if (kthread && key < Sk)
-          kreg[i] = *reinterpret_cast<const u32x4*>(kbase + ((int64_t)key * p.sk_s + kdg * 8) * 2);
-      }
-#pragma unroll
-      for (int i = 0; i < VC; ++i) {
-        const int idx = tid + 256 * i, row = idx / KCH, ch = idx - row * KCH;
-        vreg[i] = u32x4{0, 0, 0, 0};
-        if (kt + row < Sk)
-          vreg[i] = *reinterpret_cast<const u32x4*>(vbase + ((int64_t)(kt + row) * p.sv_s + ch * 8) * 2);
-      }
-    }
+    for (int i = 0; i < VC; ++i) vreg[i] = rsrc_load(vr, voff[i]);
   };
   auto stage = [&]() {
     if (kthread) {
@@ -378,56 +366,40 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
   const bool is_q = tile_role == 0, is_do = tile_role == 1;
   const int item = tid - tile_role * QITEMS;
   const int qdg = item % (D / 8), qqg = item / (D / 8);
-  const char* tsrc = is_q ? p.q : p.dout;
-  const int64_t ts_b = is_q ? p.sq_b : p.sdo_b;
-  const int64_t ts_h = is_q ? p.sq_h : p.sdo_h;
-  const int64_t ts_s = is_q ? p.sq_s : p.sdo_s;
-  tsrc += (int64_t)b * ts_b * 2;
   uint16_t* const stage_rm = is_q ? qs : dos;
   uint16_t* const stage_tr = is_q ? qts : dots;
   const bool is_stat = wave < 2 && lane < BQ;  // LSE (wavefront 0) or delta (wavefront 1)
-  const float* ssrc = wave == 0 ? p.lse : p.delta;
-  float* const sdst = wave == 0 ? lses : dels;
-  const float sfill = wave == 0 ? kNegInfA : 0.0f;
-  const float smul = wave == 0 ? kLog2eA : 1.0f;  // LSE is staged in log2 units
+  const int swave = __builtin_amdgcn_readfirstlane(wave);
+  float* const sdst = swave == 0 ? lses : dels;
+  const float sfill = swave == 0 ? kNegInfA : 0.0f;
+  const float smul = swave == 0 ? kLog2eA : 1.0f;  // LSE is staged in log2 units
   u32x4 treg[4];
   float sreg = 0.0f;
-  // With per-score mask loads the fetch is branch-free (as in the forward):
-  // every thread loads, at queries clamped to the last one (rows past it hold
-  // copies of it, finite, and their scores are excluded), threads beyond the
-  // Q / dO items and the LSE / delta lanes repeating loads of the first ones;
-  // the stage keeps what it needs.
+  // The fetch reads through buffer ranges re-based on each step (scalar
+  // registers) that end at the last query (rows past it read as zero; the
+  // stage fills LSE / delta there), with fixed per-thread offsets. Every
+  // thread loads: wavefronts past the Q and dO items load a copy of Q, and
+  // those past the LSE / delta lanes a copy of the LSE, so that no branch
+  // makes the wait for a step's mask values cover the fetch.
+  const char* fsrc = is_do ? p.dout + (int64_t)b * p.sdo_b * 2 : p.q + (int64_t)b * p.sq_b * 2;
+  const int64_t fs_h = is_do ? p.sdo_h : p.sq_h;
+  const int64_t fs_s = is_do ? p.sdo_s : p.sq_s;
+  const float* fssrc = swave == 1 ? p.delta : p.lse;
+  uint32_t toff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) toff[i] = (uint32_t)((4 * qqg + i) * fs_s * 2 + qdg * 16);
+  const uint32_t soff = (uint32_t)(lane & (BQ - 1)) * 4;
+  // With per-score mask loads the loop's fetch is unconditional too.
   constexpr bool kFlat = KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL;
-  const int fitem = kFlat ? tid % QITEMS : item;
-  const int fqdg = fitem % (D / 8), fqqg = fitem / (D / 8);
-  const char* fsrc = kFlat && tile_role > 1 ? p.q + (int64_t)b * p.sq_b * 2 : tsrc;
-  const int64_t fs_h = kFlat && tile_role > 1 ? p.sq_h : ts_h;
-  const int64_t fs_s = kFlat && tile_role > 1 ? p.sq_s : ts_s;
-  const float* fssrc = kFlat && wave > 1 ? p.lse : ssrc;
   int sq_staged = 0;  // first query of the staged tile (the fill of LSE / delta past Sq)
   auto fetch = [&](uint32_t h, int qt) {
-    if constexpr (kFlat) {
-      const char* base = fsrc + (int64_t)h * fs_h * 2;
+    const int rows = min(Sq - qt, BQ);
+    const auto tr = rows_rsrc(fsrc + ((int64_t)h * fs_h + (int64_t)qt * fs_s) * 2, rows, fs_s * 2, D * 2);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        treg[i] = *reinterpret_cast<const u32x4*>(
-            base + ((int64_t)min(qt + 4 * fqqg + i, Sq - 1) * fs_s + fqdg * 8) * 2);
-      sreg = fssrc[((int64_t)b * p.H + h) * Sq + min(qt + (lane & (BQ - 1)), Sq - 1)];
-    } else {
-      const char* base = tsrc + (int64_t)h * ts_h * 2;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int q = qt + 4 * qqg + i;
-        treg[i] = u32x4{0, 0, 0, 0};
-        if ((is_q || is_do) && q < Sq)
-          treg[i] = *reinterpret_cast<const u32x4*>(base + ((int64_t)q * ts_s + qdg * 8) * 2);
-      }
-      if (is_stat) {
-        const int q = qt + lane;
-        sreg = sfill;
-        if (q < Sq) sreg = ssrc[((int64_t)b * p.H + h) * Sq + q];
-      }
-    }
+    for (int i = 0; i < 4; ++i) treg[i] = rsrc_load(tr, toff[i]);
+    const auto sr = rows_rsrc(reinterpret_cast<const char*>(fssrc + ((int64_t)b * p.H + h) * Sq + qt),
+                              rows, 4, 4);
+    sreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, (int)soff, 0, 0));
   };
   auto stage = [&]() {
     if (is_q || is_do) {
@@ -443,10 +415,7 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
     }
     // (LSE scaled to log2 units here, not as it arrives: an operation on the
     // loaded value in the fetch would wait for it, and with it for the tile.)
-    if (is_stat) {
-      if constexpr (kFlat) sdst[lane] = sq_staged + lane < Sq ? sreg * smul : sfill;
-      else sdst[lane] = sreg * smul;
-    }
+    if (is_stat) sdst[lane] = sq_staged + lane < Sq ? sreg * smul : sfill;
   };
 
   if (any && qstart < Sq) {

@@ -295,10 +295,12 @@ int64_t sms_attention_workspace_bytes(int64_t B, int64_t H, int64_t Sq);
  *                  aligned, owned by the caller and not used by any call that
  *                  may run at the same time (else SMS_ERR_WORKSPACE); its
  *                  contents on entry do not matter
- *   stream         hipStream_t to enqueue on (three kernel launches)
+ *   stream         hipStream_t to enqueue on (three kernel launches; four
+ *                  with D = 128, where dK and dV take a launch each)
  *
  * Row alignment and limits as for sms_attention_forward, and also
- * ceil(Sk / 128) * Hk * B < 2^24. Pointers to tensors over queries (q, o,
+ * ceil(Sk / 128) * Hk * B < 2^24 and the q and dout row strides at most 2^24
+ * elements (else SMS_ERR_STRIDE). Pointers to tensors over queries (q, o,
  * dout, lse, dq) may be NULL when Sq == 0, those over keys (k, v, dk, dv)
  * when Sk == 0, and a mask other than key lengths when either is 0.
  */
