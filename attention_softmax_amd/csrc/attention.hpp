@@ -138,11 +138,6 @@ __device__ inline __attribute__((always_inline)) float other_half_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Column (in elements) of the group of 4 consecutive elements qg in row d of
-// a transposed LDS tile. The group index is XOR-ed with (d / 16) % 8: the
-// staging writes (16 rows of one group per 16 lanes) then spread over all
-// banks instead of landing 8 to a bank, while the MFMA operand reads (32
-// consecutive rows, one group) stay conflict-free (32 banks; 2-way with 64).
 // A raw buffer (stride 0) over `rows` rows of `row_bytes` bytes, `pitch`
 // bytes apart, from `base` (wave-uniform): loads at offsets past the last
 // row's bytes return zero without touching memory. Row pitches are at most
@@ -159,16 +154,28 @@ __device__ inline __attribute__((always_inline)) u32x4 rsrc_load(__amdgpu_buffer
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
 
-__host__ __device__ constexpr int tcol(int d, int qg) { return 4 * (qg ^ ((d >> 4) & 7)); }
+// Column (in elements) of the group of 4 consecutive elements qg in row d of
+// a transposed LDS tile. Bits 0 and 2 of the group index are XOR-ed with bits
+// 4 and 5 of the row: the staging writes (16 rows of one group per 16 lanes)
+// then land at most 2 to a bank instead of 8, while the MFMA operand reads (32
+// consecutive rows, one group) stay conflict-free (32 banks; 2-way with 64).
+// Bit 1 is left alone, so the two 8-byte halves of an operand (groups 2h and
+// 2h + 1, h even) keep their order in memory and one paired LDS read fills
+// the operand's registers in order. (XOR-ing bits 0-2 with row bits 4-6 made
+// the writes conflict-free, but swapped the halves on every other 32-row
+// block, and the compiler then spent four register moves per operand.)
+__host__ __device__ constexpr int tcol(int d, int qg) {
+  return 4 * (qg ^ (((d >> 4) & 1) | ((d >> 3) & 4)));
+}
 
 // tcol for an operand read of row d = 32 * blk + c (c < 32) and group
 // qg = 2 * h + g (g < 2), split into a part that depends on the lane (c, g)
 // and a part fixed at compile time (blk, h): the lane's bits (g and
-// (c / 16) % 2) make up bit 0 of the group index and the XOR, which the
+// (c / 16) % 2) make up bit 0 of the group index and of the XOR, which the
 // compile-time bits never reach, so the XOR becomes a sum. One address
 // register per lane then serves every read, with immediate offsets.
 __host__ __device__ constexpr int tcol_lane(int c, int g) { return 4 * (g ^ ((c >> 4) & 1)); }
-__host__ __device__ constexpr int tcol_const(int blk, int h) { return 4 * ((2 * h) ^ ((2 * blk) & 7)); }
+__host__ __device__ constexpr int tcol_const(int blk, int h) { return 4 * ((2 * h) ^ (4 * (blk & 1))); }
 constexpr bool tcol_split_holds() {
   for (int blk = 0; blk < 8; ++blk)
     for (int c = 0; c < 32; ++c)

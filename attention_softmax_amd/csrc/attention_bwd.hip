@@ -181,6 +181,8 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
   };
   if (kend > 0) fetch(0);
 
+  // This lane's K^T operand rows c, c + 32, ... (tcol's lane part included).
+  const uint16_t* const klane = &kts[c * TP + tcol_lane(c, g)];
   for (int kt = 0; kt < kend; kt += BK) {
     __syncthreads();
     stage();
@@ -258,21 +260,14 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
                        pack2<BF16>(sacc[base + 4], sacc[base + 5]),
                        pack2<BF16>(sacc[base + 6], sacc[base + 7])};
       }
-      // The lane's row, opaque to the compiler here: the swizzled column
-      // offsets below are then recomputed per tile (a few VALU operations)
-      // instead of being held in registers across the loop, where they
-      // spilled.
-      int cl = c;
-      asm volatile("" : "+v"(cl));
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const int kr = db * 32 + cl;
-        const uint16_t* krow = &kts[kr * TP];
+        const uint16_t* krow = klane + db * 32 * TP;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           const int s = 2 * kb + s2;
-          const u32x2 a0 = *reinterpret_cast<const u32x2*>(krow + tcol(kr, 4 * s + g));
-          const u32x2 a1 = *reinterpret_cast<const u32x2*>(krow + tcol(kr, 4 * s + 2 + g));
+          const u32x2 a0 = *reinterpret_cast<const u32x2*>(krow + tcol_const(db, 2 * s));
+          const u32x2 a1 = *reinterpret_cast<const u32x2*>(krow + tcol_const(db, 2 * s + 1));
           dq[db] = mfma_32x32x16<BF16>(u32x4{a0.x, a0.y, a1.x, a1.y}, pb[s2], dq[db]);
         }
       }
@@ -368,6 +363,9 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
   const int qdg = item % (D / 8), qqg = item / (D / 8);
   uint16_t* const stage_rm = is_q ? qs : dos;
   uint16_t* const stage_tr = is_q ? qts : dots;
+  // This lane's Q^T and dO^T operand rows c, c + 32, ... (tcol's lane part included).
+  const uint16_t* const qlane = &qts[c * TP + tcol_lane(c, g)];
+  const uint16_t* const dolane = &dots[c * TP + tcol_lane(c, g)];
   const bool is_stat = wave < 2 && lane < BQ;  // LSE (wavefront 0) or delta (wavefront 1)
   const int swave = __builtin_amdgcn_readfirstlane(wave);
   float* const sdst = swave == 0 ? lses : dels;
@@ -544,19 +542,18 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
         }
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const int tr = db * 32 + c;
-          const uint16_t* dorow = &dots[tr * TP];
-          const uint16_t* qrow = &qts[tr * TP];
+          const uint16_t* dorow = dolane + db * 32 * TP;
+          const uint16_t* qrow = qlane + db * 32 * TP;
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
             if constexpr (kDV) {
-              const u32x2 a0 = *reinterpret_cast<const u32x2*>(dorow + tcol(tr, 4 * s + g));
-              const u32x2 a1 = *reinterpret_cast<const u32x2*>(dorow + tcol(tr, 4 * s + 2 + g));
+              const u32x2 a0 = *reinterpret_cast<const u32x2*>(dorow + tcol_const(db, 2 * s));
+              const u32x2 a1 = *reinterpret_cast<const u32x2*>(dorow + tcol_const(db, 2 * s + 1));
               dv[db] = mfma_32x32x16<BF16>(u32x4{a0.x, a0.y, a1.x, a1.y}, pb[s], dv[db]);
             }
             if constexpr (kDK) {
-              const u32x2 b0 = *reinterpret_cast<const u32x2*>(qrow + tcol(tr, 4 * s + g));
-              const u32x2 b1 = *reinterpret_cast<const u32x2*>(qrow + tcol(tr, 4 * s + 2 + g));
+              const u32x2 b0 = *reinterpret_cast<const u32x2*>(qrow + tcol_const(db, 2 * s));
+              const u32x2 b1 = *reinterpret_cast<const u32x2*>(qrow + tcol_const(db, 2 * s + 1));
               dk[db] = mfma_32x32x16<BF16>(u32x4{b0.x, b0.y, b1.x, b1.y}, sb[s], dk[db]);
             }
           }
