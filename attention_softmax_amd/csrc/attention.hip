@@ -152,8 +152,7 @@ attn_fwd_kernel(AttnParams p) {
     if (vthread) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const u32x2 w{elem(vreg[0], j) | (elem(vreg[1], j) << 16),
-                      elem(vreg[2], j) | (elem(vreg[3], j) << 16)};
+        const u32x2 w{pair(vreg[0], vreg[1], j), pair(vreg[2], vreg[3], j)};
         *reinterpret_cast<u32x2*>(&vt[(8 * vdg + j) * VP + tcol(8 * vdg + j, vkg)]) = w;
       }
     }

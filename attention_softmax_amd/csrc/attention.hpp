@@ -191,6 +191,13 @@ __device__ inline __attribute__((always_inline)) uint32_t elem(const u32x4& v, i
   return (v[j >> 1] >> ((j & 1) * 16)) & 0xffffu;
 }
 
+// elem(lo, j) | elem(hi, j) << 16 in one byte permute (v_perm_b32: bytes 0-3
+// of the second operand and 4-7 of the first are selectable).
+__device__ inline __attribute__((always_inline)) uint32_t pair(const u32x4& lo, const u32x4& hi,
+                                                               int j) {
+  return __builtin_amdgcn_perm(hi[j >> 1], lo[j >> 1], (j & 1) ? 0x07060302u : 0x05040100u);
+}
+
 // Mask values of one lane's 32 keys of a 64-key tile in the query-stationary
 // layout (block kb, register r: key kt + 32 kb + 8 (r / 4) + 4 g + r % 4):
 // run i = 4 kb + r / 4 holds keys kt + 32 kb + 8 (i % 4) + 4 g .. + 3, read

@@ -168,8 +168,7 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
         *reinterpret_cast<u32x4*>(&ks[(4 * kkg + i) * KP + 8 * kdg]) = kreg[i];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const u32x2 w{elem(kreg[0], j) | (elem(kreg[1], j) << 16),
-                      elem(kreg[2], j) | (elem(kreg[3], j) << 16)};
+        const u32x2 w{pair(kreg[0], kreg[1], j), pair(kreg[2], kreg[3], j)};
         *reinterpret_cast<u32x2*>(&kts[(8 * kdg + j) * TP + tcol(8 * kdg + j, kkg)]) = w;
       }
     }
@@ -293,10 +292,13 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
 // registers (one wavefront per SIMD), so there PASS 0 (dV alone: S, P) and
 // PASS 1 (dK alone: S, dP, dS) run as two launches, each at two wavefronts
 // per SIMD, recomputing S in both.
-template <bool BF16, int D, int KIND, int PASS>
+template <bool BF16, int D, int KIND, int PASS, int BQ>
 __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdParams& p) {
   constexpr bool kDV = PASS != 1, kDK = PASS != 0;
-  constexpr int BQ = kAttnBwdBq;
+  static_assert(BQ == 32 || BQ == 64, "query tiles of one or two 32-query blocks");
+  static_assert(BQ == 32 || (KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL),
+                "per-score masks are loaded for one 32-query block per step");
+  constexpr int NSUB = BQ / 32;
   constexpr int RP = D + 8;   // row-major tile pitch, elements
   constexpr int TP = BQ + 4;  // transposed tile pitch, elements (18 dwords)
   __shared__ __align__(16) uint16_t qs[BQ * RP];    // Q: A of S = Q K^T
@@ -310,7 +312,20 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
   const int Sq = (int)p.Sq, Sk = (int)p.Sk;
   const uint32_t nkt = (p.Sk + kAttnBwdBk - 1) / kAttnBwdBk;
-  const uint32_t kti = blockIdx.x % nkt, hkb = blockIdx.x / nkt;
+  // Workgroup order: with a causal rule a key block's work shrinks with its
+  // position (its first visible query moves up), so every head's first
+  // (longest) block goes first, then every head's second, ...; the short
+  // blocks fill the end. Without one: a head's key blocks together, which
+  // then read the head's Q / dO tiles at about the same time.
+  uint32_t kti, hkb;
+  if (p.causal) {
+    const uint32_t HKB = p.Hk * p.B;
+    kti = blockIdx.x / HKB;
+    hkb = blockIdx.x % HKB;
+  } else {
+    kti = blockIdx.x % nkt;
+    hkb = blockIdx.x / nkt;
+  }
   const uint32_t hk = hkb % p.Hk, b = hkb / p.Hk;
   const int k0 = (int)(kti * kAttnBwdBk);
   const int kj = k0 + wave * 32 + c;  // this lane's key
@@ -348,21 +363,18 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
   qstart = qstart / BQ * BQ;
   const bool any = k0 < klen;
 
-  // Tiles of BQ queries fetched one ahead: (4 queries x 8 dims) of Q by the
-  // first QITEMS threads (whole wavefronts) and of dO by the next QITEMS,
-  // staged row-major and transposed; LSE by the first BQ lanes of wavefront 0
-  // and delta by those of wavefront 1. Every choice of source is uniform over
-  // a wavefront and made once here: a per-lane choice between kernel-argument
-  // fields inside the loop made the compiler fetch the fields with vector
-  // loads and wait for every outstanding load, prefetch included.
-  constexpr int QITEMS = (BQ / 4) * (D / 8);  // 64 or 128: whole wavefronts
+  // Tiles of BQ queries fetched one ahead as items of (4 queries x 8 dims):
+  // the QITEMS items of Q, then those of dO, dealt to the threads in order
+  // (item tid + 256 i is thread tid's i-th), staged row-major and
+  // transposed; LSE by the first BQ lanes of wavefront 0 and delta by those
+  // of wavefront 1. Every choice of source is uniform over a wavefront and
+  // made once here: a per-lane choice between kernel-argument fields inside
+  // the loop made the compiler fetch the fields with vector loads and wait
+  // for every outstanding load, prefetch included.
+  constexpr int QITEMS = (BQ / 4) * (D / 8);  // 64, 128 or 256: whole wavefronts
+  constexpr int NITEMS = 2 * QITEMS;
+  constexpr int NIT = (NITEMS + 255) / 256;    // items per thread
   static_assert(QITEMS % 64 == 0, "Q / dO loads by whole wavefronts");
-  const int tile_role = __builtin_amdgcn_readfirstlane(tid / QITEMS);  // 0: Q, 1: dO, 2+: none
-  const bool is_q = tile_role == 0, is_do = tile_role == 1;
-  const int item = tid - tile_role * QITEMS;
-  const int qdg = item % (D / 8), qqg = item / (D / 8);
-  uint16_t* const stage_rm = is_q ? qs : dos;
-  uint16_t* const stage_tr = is_q ? qts : dots;
   // This lane's Q^T and dO^T operand rows c, c + 32, ... (tcol's lane part included).
   const uint16_t* const qlane = &qts[c * TP + tcol_lane(c, g)];
   const uint16_t* const dolane = &dots[c * TP + tcol_lane(c, g)];
@@ -371,44 +383,65 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
   float* const sdst = swave == 0 ? lses : dels;
   const float sfill = swave == 0 ? kNegInfA : 0.0f;
   const float smul = swave == 0 ? kLog2eA : 1.0f;  // LSE is staged in log2 units
-  u32x4 treg[4];
+  u32x4 treg[NIT][4];
   float sreg = 0.0f;
   // The fetch reads through buffer ranges re-based on each step (scalar
   // registers) that end at the last query (rows past it read as zero; the
   // stage fills LSE / delta there), with fixed per-thread offsets. Every
-  // thread loads: wavefronts past the Q and dO items load a copy of Q, and
-  // those past the LSE / delta lanes a copy of the LSE, so that no branch
+  // thread loads: threads past the last item load a copy of another's, and
+  // wavefronts past the LSE / delta lanes a copy of the LSE, so that no branch
   // makes the wait for a step's mask values cover the fetch.
-  const char* fsrc = is_do ? p.dout + (int64_t)b * p.sdo_b * 2 : p.q + (int64_t)b * p.sq_b * 2;
-  const int64_t fs_h = is_do ? p.sdo_h : p.sq_h;
-  const int64_t fs_s = is_do ? p.sdo_s : p.sq_s;
-  const float* fssrc = swave == 1 ? p.delta : p.lse;
-  uint32_t toff[4];
+  const char* fsrc[NIT];
+  int64_t fs_h[NIT], fs_s[NIT];
+  bool fstage[NIT], fdo[NIT];
+  int fqdg[NIT], fqqg[NIT];
+  uint32_t toff[NIT][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) toff[i] = (uint32_t)((4 * qqg + i) * fs_s * 2 + qdg * 16);
+  for (int i = 0; i < NIT; ++i) {
+    const int it = (tid + 256 * i) % NITEMS;
+    fstage[i] = tid + 256 * i < NITEMS;
+    fdo[i] = __builtin_amdgcn_readfirstlane(it / QITEMS) == 1;
+    const int local = it % QITEMS;
+    fqdg[i] = local % (D / 8);
+    fqqg[i] = local / (D / 8);
+    fsrc[i] = fdo[i] ? p.dout + (int64_t)b * p.sdo_b * 2 : p.q + (int64_t)b * p.sq_b * 2;
+    fs_h[i] = fdo[i] ? p.sdo_h : p.sq_h;
+    fs_s[i] = fdo[i] ? p.sdo_s : p.sq_s;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) toff[i][k] = (uint32_t)((4 * fqqg[i] + k) * fs_s[i] * 2 + fqdg[i] * 16);
+  }
+  const float* fssrc = swave == 1 ? p.delta : p.lse;
   const uint32_t soff = (uint32_t)(lane & (BQ - 1)) * 4;
   // With per-score mask loads the loop's fetch is unconditional too.
   constexpr bool kFlat = KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL;
   int sq_staged = 0;  // first query of the staged tile (the fill of LSE / delta past Sq)
   auto fetch = [&](uint32_t h, int qt) {
     const int rows = min(Sq - qt, BQ);
-    const auto tr = rows_rsrc(fsrc + ((int64_t)h * fs_h + (int64_t)qt * fs_s) * 2, rows, fs_s * 2, D * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) treg[i] = rsrc_load(tr, toff[i]);
+    for (int i = 0; i < NIT; ++i) {
+      const auto tr = rows_rsrc(fsrc[i] + ((int64_t)h * fs_h[i] + (int64_t)qt * fs_s[i]) * 2, rows,
+                                fs_s[i] * 2, D * 2);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) treg[i][k] = rsrc_load(tr, toff[i][k]);
+    }
     const auto sr = rows_rsrc(reinterpret_cast<const char*>(fssrc + ((int64_t)b * p.H + h) * Sq + qt),
                               rows, 4, 4);
     sreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, (int)soff, 0, 0));
   };
   auto stage = [&]() {
-    if (is_q || is_do) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4*>(&stage_rm[(4 * qqg + i) * RP + 8 * qdg]) = treg[i];
+    for (int i = 0; i < NIT; ++i) {
+      if (!fstage[i]) continue;
+      uint16_t* const srm = fdo[i] ? dos : qs;
+      uint16_t* const stp = fdo[i] ? dots : qts;
+      const int qdg = fqdg[i], qqg = fqqg[i];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        *reinterpret_cast<u32x4*>(&srm[(4 * qqg + k) * RP + 8 * qdg]) = treg[i][k];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const u32x2 w{elem(treg[0], j) | (elem(treg[1], j) << 16),
-                      elem(treg[2], j) | (elem(treg[3], j) << 16)};
-        *reinterpret_cast<u32x2*>(&stage_tr[(8 * qdg + j) * TP + tcol(8 * qdg + j, qqg)]) = w;
+        const u32x2 w{pair(treg[i][0], treg[i][1], j), pair(treg[i][2], treg[i][3], j)};
+        *reinterpret_cast<u32x2*>(&stp[(8 * qdg + j) * TP + tcol(8 * qdg + j, qqg)]) = w;
       }
     }
     // (LSE scaled to log2 units here, not as it arrives: an operation on the
@@ -470,91 +503,100 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
           fetch(nh, nqt);
         }
 
-        f32x16 sacc, dpacc;
+        // The tile's 32-query blocks in turn (the block's products,
+        // probabilities and gradient contributions before the next block's).
+        // A block that no key of the workgroup can see (causal) is skipped.
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sacc[r] = 0.0f;
-          dpacc[r] = 0.0f;
-        }
+        for (int qb = 0; qb < NSUB; ++qb) {
+          const int qb0 = qt + 32 * qb;  // the block's first query
+          if (NSUB > 1 && (qb0 >= Sq || (p.causal && k0 > qb0 + 31 + off))) continue;
+          f32x16 sacc, dpacc;
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(&qs[c * RP + s * 16 + 8 * g]);
-          sacc = mfma_32x32x16<BF16>(a, kf[s], sacc);
-          if constexpr (kDK) {
-            const u32x4 ad = *reinterpret_cast<const u32x4*>(&dos[c * RP + s * 16 + 8 * g]);
-            dpacc = mfma_32x32x16<BF16>(ad, vf[s], dpacc);
+          for (int r = 0; r < 16; ++r) {
+            sacc[r] = 0.0f;
+            dpacc[r] = 0.0f;
           }
-        }
-        // Register r holds query qt + 8*(r/4) + 4g + r%4 of this lane's key.
-        float pr[16], dsr[16];
-        // A tile whose every (query, key) score is visible (all queries and
-        // keys in range, past the causal boundary, no per-score mask) takes
-        // the probabilities without any exclusion test.
-        const bool full = KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL && qt + BQ <= Sq &&
-                          k0 + kAttnBwdBk <= klen &&
-                          (!p.causal || k0 + kAttnBwdBk - 1 <= qt + off);
-        if (full) {
 #pragma unroll
-          for (int rg = 0; rg < 4; ++rg) {
-            const int ql = 8 * rg + 4 * g;  // first of 4 consecutive queries
-            const float4 l2 = *reinterpret_cast<const float4*>(&lses[ql]);
-            const float4 dl = *reinterpret_cast<const float4*>(&dels[ql]);
-            const float lv[4] = {l2.x, l2.y, l2.z, l2.w}, dv4[4] = {dl.x, dl.y, dl.z, dl.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * rg + e;
-              const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], p.scale_log2, -lv[e]));
-              pr[r] = pv;
-              dsr[r] = pv * (dpacc[r] - dv4[e]);
+          for (int s = 0; s < D / 16; ++s) {
+            const u32x4 a = *reinterpret_cast<const u32x4*>(&qs[(32 * qb + c) * RP + s * 16 + 8 * g]);
+            sacc = mfma_32x32x16<BF16>(a, kf[s], sacc);
+            if constexpr (kDK) {
+              const u32x4 ad = *reinterpret_cast<const u32x4*>(&dos[(32 * qb + c) * RP + s * 16 + 8 * g]);
+              dpacc = mfma_32x32x16<BF16>(ad, vf[s], dpacc);
             }
           }
-        } else {
+          // Register r holds query qb0 + 8*(r/4) + 4g + r%4 of this lane's key.
+          float pr[16], dsr[16];
+          // A block whose every (query, key) score is visible (all queries and
+          // keys in range, past the causal boundary, no per-score mask) takes
+          // the probabilities without any exclusion test.
+          const bool full = KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL && qb0 + 32 <= Sq &&
+                            k0 + kAttnBwdBk <= klen &&
+                            (!p.causal || k0 + kAttnBwdBk - 1 <= qb0 + off);
+          if (full) {
 #pragma unroll
-          for (int rg = 0; rg < 4; ++rg) {
-            const int ql = 8 * rg + 4 * g;
+            for (int rg = 0; rg < 4; ++rg) {
+              const int ql = 32 * qb + 8 * rg + 4 * g;  // first of 4 consecutive queries
+              const float4 l2 = *reinterpret_cast<const float4*>(&lses[ql]);
+              const float4 dl = *reinterpret_cast<const float4*>(&dels[ql]);
+              const float lv[4] = {l2.x, l2.y, l2.z, l2.w}, dv4[4] = {dl.x, dl.y, dl.z, dl.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * rg + e, qq = qt + ql + e;
-              const float lse2 = lses[ql + e];
-              float tv = sacc[r] * p.scale_log2;
-              bool excluded = qq >= Sq || kj >= klen || !kvalid || lse2 == kNegInfA ||
-                              (p.causal && kj > qq + off);
-              if constexpr (KIND == ATTN_MASK_ADD) {
-                if (!excluded) tv = fmaf(to_float<BF16>(mvk[r]), kLog2eA, tv);
-              } else if constexpr (KIND == ATTN_MASK_BOOL) {
-                if (!excluded && mvk[r] != 0) excluded = true;
+              for (int e = 0; e < 4; ++e) {
+                const int r = 4 * rg + e;
+                const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], p.scale_log2, -lv[e]));
+                pr[r] = pv;
+                dsr[r] = pv * (dpacc[r] - dv4[e]);
               }
-              const float pv = excluded ? 0.0f : __builtin_amdgcn_exp2f(tv - lse2);
-              pr[r] = pv;
-              dsr[r] = pv * (dpacc[r] - dels[ql + e]);
+            }
+          } else {
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+              const int ql = 32 * qb + 8 * rg + 4 * g;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = 4 * rg + e, qq = qt + ql + e;
+                const float lse2 = lses[ql + e];
+                float tv = sacc[r] * p.scale_log2;
+                bool excluded = qq >= Sq || kj >= klen || !kvalid || lse2 == kNegInfA ||
+                                (p.causal && kj > qq + off);
+                if constexpr (KIND == ATTN_MASK_ADD) {
+                  if (!excluded) tv = fmaf(to_float<BF16>(mvk[r]), kLog2eA, tv);
+                } else if constexpr (KIND == ATTN_MASK_BOOL) {
+                  if (!excluded && mvk[r] != 0) excluded = true;
+                }
+                const float pv = excluded ? 0.0f : __builtin_amdgcn_exp2f(tv - lse2);
+                pr[r] = pv;
+                dsr[r] = pv * (dpacc[r] - dels[ql + e]);
+              }
             }
           }
-        }
-        // B operands: k-step s takes registers 8s .. 8s+7 (queries
-        // 16s + 8*(j/4) + 4g + j%4 for element j).
-        u32x4 pb[2], sb[2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          pb[s] = u32x4{pack2<BF16>(pr[8 * s + 0], pr[8 * s + 1]), pack2<BF16>(pr[8 * s + 2], pr[8 * s + 3]),
-                        pack2<BF16>(pr[8 * s + 4], pr[8 * s + 5]), pack2<BF16>(pr[8 * s + 6], pr[8 * s + 7])};
-          sb[s] = u32x4{pack2<BF16>(dsr[8 * s + 0], dsr[8 * s + 1]), pack2<BF16>(dsr[8 * s + 2], dsr[8 * s + 3]),
-                        pack2<BF16>(dsr[8 * s + 4], dsr[8 * s + 5]), pack2<BF16>(dsr[8 * s + 6], dsr[8 * s + 7])};
-        }
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const uint16_t* dorow = dolane + db * 32 * TP;
-          const uint16_t* qrow = qlane + db * 32 * TP;
+          // B operands: k-step s takes registers 8s .. 8s+7 (queries
+          // qb0 + 16s + 8*(j/4) + 4g + j%4 for element j).
+          u32x4 pb[2], sb[2];
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
-            if constexpr (kDV) {
-              const u32x2 a0 = *reinterpret_cast<const u32x2*>(dorow + tcol_const(db, 2 * s));
-              const u32x2 a1 = *reinterpret_cast<const u32x2*>(dorow + tcol_const(db, 2 * s + 1));
-              dv[db] = mfma_32x32x16<BF16>(u32x4{a0.x, a0.y, a1.x, a1.y}, pb[s], dv[db]);
-            }
-            if constexpr (kDK) {
-              const u32x2 b0 = *reinterpret_cast<const u32x2*>(qrow + tcol_const(db, 2 * s));
-              const u32x2 b1 = *reinterpret_cast<const u32x2*>(qrow + tcol_const(db, 2 * s + 1));
-              dk[db] = mfma_32x32x16<BF16>(u32x4{b0.x, b0.y, b1.x, b1.y}, sb[s], dk[db]);
+            pb[s] = u32x4{pack2<BF16>(pr[8 * s + 0], pr[8 * s + 1]), pack2<BF16>(pr[8 * s + 2], pr[8 * s + 3]),
+                          pack2<BF16>(pr[8 * s + 4], pr[8 * s + 5]), pack2<BF16>(pr[8 * s + 6], pr[8 * s + 7])};
+            sb[s] = u32x4{pack2<BF16>(dsr[8 * s + 0], dsr[8 * s + 1]), pack2<BF16>(dsr[8 * s + 2], dsr[8 * s + 3]),
+                          pack2<BF16>(dsr[8 * s + 4], dsr[8 * s + 5]), pack2<BF16>(dsr[8 * s + 6], dsr[8 * s + 7])};
+          }
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const uint16_t* dorow = dolane + db * 32 * TP;
+            const uint16_t* qrow = qlane + db * 32 * TP;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+              const int ks = 2 * qb + s;  // the k-step's 16 queries within the tile
+              if constexpr (kDV) {
+                const u32x2 a0 = *reinterpret_cast<const u32x2*>(dorow + tcol_const(db, 2 * ks));
+                const u32x2 a1 = *reinterpret_cast<const u32x2*>(dorow + tcol_const(db, 2 * ks + 1));
+                dv[db] = mfma_32x32x16<BF16>(u32x4{a0.x, a0.y, a1.x, a1.y}, pb[s], dv[db]);
+              }
+              if constexpr (kDK) {
+                const u32x2 b0 = *reinterpret_cast<const u32x2*>(qrow + tcol_const(db, 2 * ks));
+                const u32x2 b1 = *reinterpret_cast<const u32x2*>(qrow + tcol_const(db, 2 * ks + 1));
+                dk[db] = mfma_32x32x16<BF16>(u32x4{b0.x, b0.y, b1.x, b1.y}, sb[s], dk[db]);
+              }
             }
           }
         }
@@ -587,14 +629,24 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
 // Entry points: the single passes at two wavefronts per SIMD; both
 // gradients together with the registers the compiler needs (D = 64 fits two
 // wavefronts per SIMD as it is).
-template <bool BF16, int D, int KIND, int PASS>
+template <bool BF16, int D, int KIND, int PASS, int BQ>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkdv_kernel(AttnBwdParams p) {
-  dkdv_body<BF16, D, KIND, PASS>(p);
+  dkdv_body<BF16, D, KIND, PASS, BQ>(p);
 }
-template <bool BF16, int D, int KIND>
+template <bool BF16, int D, int KIND, int BQ>
 __global__ void __launch_bounds__(256) attn_bwd_dkdv_both_kernel(AttnBwdParams p) {
-  dkdv_body<BF16, D, KIND, 2>(p);
+  dkdv_body<BF16, D, KIND, 2, BQ>(p);
+}
+
+// Queries per dK/dV step. Two 32-query blocks per staged tile halve the
+// per-step work (barriers, staging, LSE / delta) per product: measured 4 %
+// faster for D = 64 (fp16 [8,32,2048,64] backward), equal within noise for
+// D = 128, where one block keeps the LDS and registers smaller. Per-score
+// masks keep one block (their values take registers per block).
+template <int KIND, int D>
+constexpr int dkdv_bq() {
+  return (KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL || D == 128) ? 32 : 64;
 }
 
 template <bool BF16, int D, int KIND>
@@ -621,13 +673,14 @@ hipError_t launch_bwd_kind(const AttnBwdParams& p, hipStream_t st) {
     // D = 128: two passes at two wavefronts per SIMD, measured faster than
     // both gradients in one pass at one (fp16 [4,32,4096,128] causal
     // backward 4.72 against 5.28 ms; not causal 6.02 against 6.66 ms).
+    constexpr int BQ = dkdv_bq<KIND, D>();
     if constexpr (D == 128) {
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<BF16, D, KIND, 0>), gk, block, 0, st, p);
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<BF16, D, KIND, 0, BQ>), gk, block, 0, st, p);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<BF16, D, KIND, 1>), gk, block, 0, st, p);
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<BF16, D, KIND, 1, BQ>), gk, block, 0, st, p);
     } else {
-      hipLaunchKernelGGL((attn_bwd_dkdv_both_kernel<BF16, D, KIND>), gk, block, 0, st, p);
+      hipLaunchKernelGGL((attn_bwd_dkdv_both_kernel<BF16, D, KIND, BQ>), gk, block, 0, st, p);
     }
   }
   return hipGetLastError();
