@@ -101,13 +101,12 @@ def parse():
 
 def csrc_sha():
     """Hash of the sources the softmax kernels and their launches are built
-    from (the fused attention's own files excluded): counters taken on other
-    sources are stale."""
+    from (every file under csrc/ but the fused attention's own): counters
+    taken on other sources are stale."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "attention_softmax_amd", "csrc")
     files = sorted(f for f in glob.glob(os.path.join(csrc, "*"))
                    if not os.path.basename(f).startswith("attention"))
-    files.append(os.path.join(ROOT, "include", "sms.h"))
     for f in files:
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())
