@@ -248,6 +248,44 @@ def test_attention_backward_long_causal():
     say(f"  worst error / tolerance {w:.3f}, from the GPU forward {w2:.3f}")
 
 
+def test_attention_bench_workload_sampled():
+    """The attention bench's workload at full size, in the launches the bench
+    times: fp16 Q, K, V, dO [4, 32, 4096, 128] ~ N(0, 1) (the bench's seeds),
+    causal, scale 1/sqrt(128); forward and backward over all 128 heads, then
+    two (batch, head) pairs checked element by element against the oracle:
+    O, LSE, dQ, dK and dV of those heads, the backward from the GPU
+    forward's O and LSE."""
+    B, H, S, D = 4, 32, 4096, 128
+    sc = D ** -0.5
+    say("attention bench workload fp16 [4,32,4096,128] causal")
+    q, k, v, do = (draw_x((B, H, S, D), "f16", ("normal", 1.0), 11 + i, DEV) for i in range(4))
+    o, lse = sms_attention_forward(q, k, v, None, sc, True, return_lse=True)
+    dq, dk, dv = sms_attention_backward(q, k, v, o, lse, do, None, sc, True)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (3, 31)):
+        what = f"bench workload (b={b}, h={h})"
+        say(f"  {what}")
+
+        def head(t):
+            return to_np(t[b:b + 1, h:h + 1].contiguous())
+
+        qn, kn, vn, don = head(q), head(k), head(v), head(do)
+        o_ref, lse_ref = oracle.attention.forward(qn, kn, vn, "f16", scale=sc, is_causal=True)
+        vd = oracle.decode(vn, "f16")
+        compare_attention(oracle.decode(head(o), "f16"), o_ref,
+                          np.abs(vd).max(axis=(2, 3))[:, :, None, None], "f16", what + " O",
+                          head(lse), lse_ref)
+        refs = oracle.attention.backward(qn, kn, vn, don, "f16", scale=sc, is_causal=True)
+        P, ref_lse = oracle.attention.probabilities(qn, kn, "f16", scale=sc, is_causal=True)
+        qd, kd, dod = (oracle.decode(a, "f16") for a in (qn, kn, don))
+        dP = dod @ np.swapaxes(vd, 2, 3)
+        tols, rms = attention_grad_tolerances(P, dP, qd, kd, dod, np.abs(vd).max(axis=(2, 3)),
+                                              ref_lse, float(np.float32(sc)), "f16", refs, None,
+                                              o_ref, None)
+        for name, got, ref, tol, rm in zip(("dQ", "dK", "dV"), (dq, dk, dv), refs, tols, rms):
+            compare_grads(oracle.decode(head(got), "f16"), ref, tol, f"{what} {name}", rm)
+
+
 def test_attention_backward_empty_sides():
     """No key: dQ = 0 and nothing else; no query: dK = dV = 0."""
     say("attention backward empty sides")
