@@ -67,10 +67,9 @@ struct AttnBwdParams {
   int mask_vec;      // as in AttnParams
 };
 
-// Keys per workgroup of the dK / dV kernel (four wavefronts x 32) and queries
-// per tile it streams.
+// Keys per workgroup of the dK / dV kernel (four wavefronts x 32); the
+// queries per tile it streams are a template parameter of that kernel.
 constexpr int kAttnBwdBk = 128;
-constexpr int kAttnBwdBq = 32;
 
 // Queries per workgroup (four wavefronts of 32 queries) and keys per tile.
 constexpr int kAttnBq = 128;

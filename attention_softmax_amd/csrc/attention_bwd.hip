@@ -5,7 +5,8 @@
 // points to; the softmax gradient itself is the lmnt.cn page's sec. 3.3 rule,
 // dS = P * (dP - rowsum(dP * P)), with rowsum(dP * P) = rowsum(dO * O)).
 //
-// Three launches, all deterministic (no atomics):
+// Three launches (four for D = 128, where dK and dV take a pass each), all
+// deterministic (no atomics):
 //  1. delta = rowsum(dO * O) per query row, fp32, into the workspace;
 //  2. dQ, one workgroup per 128 queries (query-stationary, as the forward):
 //     S^T = K Q^T and dP^T = V dO^T leave each lane 16 keys of one query;
@@ -14,8 +15,9 @@
 //     S^T layout holds them, K^T read from a transposed LDS tile);
 //  3. dK and dV, one workgroup per 128 keys of one key/value head
 //     (key-stationary): for every query head of its group and every tile of
-//     32 queries, S = Q K^T and dP = dO V^T leave each lane 16 queries of one
-//     key; dV^T += dO^T P and dK^T += Q^T dS with P and dS as B operands.
+//     32 or 64 queries, S = Q K^T and dP = dO V^T leave each lane 16 queries
+//     of one key per 32-query block; dV^T += dO^T P and dK^T += Q^T dS with P
+//     and dS as B operands.
 // Lane layouts of v_mfma_f32_32x32x16: see attention.hip.
 
 #include <algorithm>
@@ -300,7 +302,7 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
                 "per-score masks are loaded for one 32-query block per step");
   constexpr int NSUB = BQ / 32;
   constexpr int RP = D + 8;   // row-major tile pitch, elements
-  constexpr int TP = BQ + 4;  // transposed tile pitch, elements (18 dwords)
+  constexpr int TP = BQ + 4;  // transposed tile pitch, elements (BQ / 2 + 2 dwords)
   __shared__ __align__(16) uint16_t qs[BQ * RP];    // Q: A of S = Q K^T
   __shared__ __align__(16) uint16_t qts[D * TP];    // Q^T: A of dK^T += Q^T dS
   __shared__ __align__(16) uint16_t dos[BQ * RP];   // dO: A of dP = dO V^T
