@@ -30,9 +30,13 @@ namespace {
 
 using namespace attn;
 
-// MV: additive / boolean mask rows allow the vector loads of load_mask_runs;
-// otherwise each mask value is read where it is used.
-template <bool BF16, int D, int KIND, bool MV>
+// MV (additive / boolean masks): 2 when every mask row of the workgroup's
+// queries starts on a 16-byte line, so that a tile's mask values (128 queries
+// x 64 keys) come with its K / V fetch as whole-line 16-byte loads and are
+// staged in LDS; 1 when mask rows start on 4 elements (runs of 4 keys per
+// lane, loaded at the start of each tile by load_mask_runs); 0: each mask
+// value is read where it is used.
+template <bool BF16, int D, int KIND, int MV>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(AttnParams p) {
   constexpr int BK = kAttnBk;
@@ -40,6 +44,14 @@ attn_fwd_kernel(AttnParams p) {
   constexpr int VP = BK + 4;  // V^T tile row pitch, elements (34 dwords: 8-byte reads spread)
   __shared__ __align__(16) uint16_t ks[BK * KP];
   __shared__ __align__(16) uint16_t vt[D * VP];
+  // Mask tile (MV == 2): kAttnBq rows of BK values; row pitch 144 bytes for
+  // 16-bit values, 80 for bytes (16-byte rows for the staging stores; the
+  // lanes' 8- or 4-byte run reads spread over the banks).
+  constexpr int MB = KIND == ATTN_MASK_ADD ? 2 : 1;  // bytes per mask value
+  constexpr int MP = MB == 2 ? 144 : 80;             // mask tile row pitch, bytes
+  constexpr int MCH = BK * MB / 16;                  // 16-byte chunks per row
+  constexpr int MC = MV == 2 ? kAttnBq * MCH / 256 : 1;  // chunks per thread
+  __shared__ __align__(16) uint8_t ms[MV == 2 ? kAttnBq * MP : 16];
 
   const int tid = (int)threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
@@ -116,7 +128,7 @@ attn_fwd_kernel(AttnParams p) {
   constexpr int VITEMS = (BK / 4) * (D / 8);      // (4 keys x 8 dims) items per tile
   const int vdg = tid % (D / 8), vkg = tid / (D / 8);
   const bool vthread = tid < VITEMS;
-  u32x4 kreg[KC], vreg[4];
+  u32x4 kreg[KC], vreg[4], mreg[MC];
   // The fetch reads through buffer resources re-based on each tile (scalar
   // registers) that end at the last key: rows past it read as zero, with no
   // per-load test or branch, and each thread's byte offsets within a tile
@@ -134,6 +146,17 @@ attn_fwd_kernel(AttnParams p) {
   const int vtid = tid % VITEMS, vdgl = vtid % (D / 8), vkgl = vtid / (D / 8);
 #pragma unroll
   for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)((4 * vkgl + i) * p.sv_s * 2 + vdgl * 16);
+  // Mask tile (MV == 2): the workgroup's query rows (past Sq: none) through
+  // one buffer range ending at the last row's last key; keys past Sk of the
+  // other rows read the next row's first values, whose scores are excluded.
+  uint32_t moff[MC];
+  const int64_t mtile = (int64_t)b * p.sm_b + (int64_t)h * p.sm_h + (int64_t)q0 * p.sm_q;
+  const int mrows = min(Sq - q0, kAttnBq);
+#pragma unroll
+  for (int i = 0; i < MC; ++i) {
+    const int idx = tid + 256 * i, row = idx / MCH, ch = idx - row * MCH;
+    moff[i] = (uint32_t)(row * p.sm_q * MB + ch * 16);
+  }
   auto fetch = [&](int kt) {
     const int rows = min(Sk - kt, BK);
     const auto kr = rows_rsrc(kbase + (int64_t)kt * p.sk_s * 2, rows, p.sk_s * 2, D * 2);
@@ -142,6 +165,12 @@ attn_fwd_kernel(AttnParams p) {
     for (int i = 0; i < KC; ++i) kreg[i] = rsrc_load(kr, koff[i]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) vreg[i] = rsrc_load(vr, voff[i]);
+    if constexpr (MV == 2) {
+      const auto mr = rows_rsrc(p.mask + (mtile + kt) * MB, rows > 0 ? mrows : 0, p.sm_q * MB,
+                                max(rows, 0) * MB);
+#pragma unroll
+      for (int i = 0; i < MC; ++i) mreg[i] = rsrc_load(mr, moff[i]);
+    }
   };
   auto stage = [&]() {
 #pragma unroll
@@ -156,6 +185,13 @@ attn_fwd_kernel(AttnParams p) {
         *reinterpret_cast<u32x2*>(&vt[(8 * vdg + j) * VP + tcol(8 * vdg + j, vkg)]) = w;
       }
     }
+    if constexpr (MV == 2) {
+#pragma unroll
+      for (int i = 0; i < MC; ++i) {
+        const int idx = tid + 256 * i, row = idx / MCH, ch = idx - row * MCH;
+        *reinterpret_cast<u32x4*>(&ms[row * MP + ch * 16]) = mreg[i];
+      }
+    }
   };
   if (kend > 0) fetch(0);
   // This lane's V^T operand rows c, c + 32, ... (tcol's lane part included).
@@ -166,15 +202,29 @@ attn_fwd_kernel(AttnParams p) {
     stage();
     __syncthreads();
     u32x2 mv[8];  // this tile's mask values (additive / boolean masks)
-    if constexpr (MV) {
+    if constexpr (MV == 1) {
       load_mask_runs<KIND>(p.mask, mrow_c, kt, g, Sk, mv);
       __builtin_amdgcn_sched_barrier(0);  // keep them ahead of the prefetch
     }
-    if (MV || kt + BK < kend) fetch(kt + BK);  // in flight during this tile's products
+    if (MV == 1 || kt + BK < kend) fetch(kt + BK);  // in flight during this tile's products
     // Keep the fetch ahead of the products (under register pressure the
     // scheduler otherwise sinks the loads to the end of the loop, where the
     // next tile's stage waits for them at once).
-    if constexpr (MV) __builtin_amdgcn_sched_barrier(0);
+    if constexpr (MV == 1) __builtin_amdgcn_sched_barrier(0);
+    if constexpr (MV == 2) {
+      // The lane's runs of 4 keys (the layout of load_mask_runs) from the tile.
+      const uint8_t* mrow_l = &ms[(wave * 32 + c) * MP];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int kk = (i >> 2) * 32 + 8 * (i & 3) + 4 * g;
+        if constexpr (MB == 2) {
+          mv[i] = *reinterpret_cast<const u32x2*>(mrow_l + kk * 2);
+        } else {
+          mv[i].x = *reinterpret_cast<const uint32_t*>(mrow_l + kk);
+          mv[i].y = 0;
+        }
+      }
+    }
 
     // S^T for the tile's two 32-key blocks, alternating between the blocks so
     // that consecutive products are independent (each K fragment's LDS read
@@ -199,7 +249,8 @@ attn_fwd_kernel(AttnParams p) {
     // maximum of the raw scores (scaling is monotonic, so the scaled maximum
     // is the same rounded value) and folds the scale into the exponential's
     // argument below.
-    const bool full = fast_ok && kt + BK <= klen && (!p.causal || kt + BK <= q0 + off + 1);
+    const bool inb = kt + BK <= klen && (!p.causal || kt + BK <= q0 + off + 1);
+    const bool full = fast_ok && inb;
     float mloc = kNegInfA;
     if (full) {
 #pragma unroll
@@ -207,6 +258,35 @@ attn_fwd_kernel(AttnParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[kb][r]);
       mloc *= p.scale_log2;
+    } else if ((KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL) && inb) {
+      // Every key in bounds for every query: the mask alone.
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float t = sacc[kb][r] * p.scale_log2;
+          if constexpr (KIND == ATTN_MASK_ADD) {
+            uint32_t bits;
+            if constexpr (MV != 0) {
+              bits = mask_run_value(mv, kb, r, false);
+            } else {
+              const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+              bits = qvalid ? *reinterpret_cast<const uint16_t*>(p.mask + (mrow + key) * 2) : 0u;
+            }
+            t = fmaf(to_float<BF16>(bits), kLog2eA, t);
+          } else {
+            uint32_t byte;
+            if constexpr (MV != 0) {
+              byte = mask_run_value(mv, kb, r, true);
+            } else {
+              const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+              byte = qvalid ? (uint32_t)(uint8_t)p.mask[mrow + key] : 0u;
+            }
+            if (byte != 0) t = kNegInfA;
+          }
+          sacc[kb][r] = t;
+          mloc = fmaxf(mloc, t);
+        }
     } else {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -218,12 +298,12 @@ attn_fwd_kernel(AttnParams p) {
           t = kNegInfA;
         } else if constexpr (KIND == ATTN_MASK_ADD) {
           uint32_t bits;
-          if constexpr (MV) bits = mask_run_value(mv, kb, r, false);
+          if constexpr (MV != 0) bits = mask_run_value(mv, kb, r, false);
           else bits = qvalid ? *reinterpret_cast<const uint16_t*>(p.mask + (mrow + key) * 2) : 0u;
           t = fmaf(to_float<BF16>(bits), kLog2eA, t);
         } else if constexpr (KIND == ATTN_MASK_BOOL) {
           uint32_t byte;
-          if constexpr (MV) byte = mask_run_value(mv, kb, r, true);
+          if constexpr (MV != 0) byte = mask_run_value(mv, kb, r, true);
           else byte = qvalid ? (uint32_t)(uint8_t)p.mask[mrow + key] : 0u;
           if (byte != 0) t = kNegInfA;
         }
@@ -316,18 +396,20 @@ attn_fwd_kernel(AttnParams p) {
 template <bool BF16, int D>
 hipError_t launch_kind(const AttnParams& p, hipStream_t st) {
   const dim3 grid(p.H * p.B * ((p.Sq + kAttnBq - 1) / kAttnBq)), block(256);
-  const bool mv = p.mask_vec != 0;
+  const int mv = p.mask_tile ? 2 : p.mask_vec ? 1 : 0;
   switch (p.mask_kind) {
-    case ATTN_MASK_NONE: hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_NONE, false>), grid, block, 0, st, p); break;
+    case ATTN_MASK_NONE: hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_NONE, 0>), grid, block, 0, st, p); break;
     case ATTN_MASK_ADD:
-      if (mv) hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_ADD, true>), grid, block, 0, st, p);
-      else hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_ADD, false>), grid, block, 0, st, p);
+      if (mv == 2) hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_ADD, 2>), grid, block, 0, st, p);
+      else if (mv == 1) hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_ADD, 1>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_ADD, 0>), grid, block, 0, st, p);
       break;
     case ATTN_MASK_BOOL:
-      if (mv) hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_BOOL, true>), grid, block, 0, st, p);
-      else hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_BOOL, false>), grid, block, 0, st, p);
+      if (mv == 2) hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_BOOL, 2>), grid, block, 0, st, p);
+      else if (mv == 1) hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_BOOL, 1>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_BOOL, 0>), grid, block, 0, st, p);
       break;
-    case ATTN_MASK_LEN: hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_LEN, false>), grid, block, 0, st, p); break;
+    case ATTN_MASK_LEN: hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_LEN, 0>), grid, block, 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -32,6 +32,7 @@ struct AttnParams {
   int causal;        // 0 none, 1 key k > q excluded, 2 key k > q + Sk - Sq excluded
   int mask_kind;     // 0 none, 1 additive, 2 bool, 3 key lengths
   int mask_vec;      // every mask row starts on 4 elements and Sk % 4 == 0 (runs of 4 keys)
+  int mask_tile;     // every mask row starts on a 16-byte line (tiles of mask rows in LDS)
 };
 
 enum : int { ATTN_MASK_NONE = 0, ATTN_MASK_ADD = 1, ATTN_MASK_BOOL = 2, ATTN_MASK_LEN = 3 };
