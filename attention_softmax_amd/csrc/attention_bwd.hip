@@ -202,8 +202,8 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
     // registers live). A tile whose every score is visible to every query of
     // the workgroup (keys in range and before the first query's causal bound,
     // all queries in range, no per-score mask) skips the exclusion tests.
-    const bool full = KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL && q0 + kAttnBq <= Sq &&
-                      kt + BK <= klen && (!p.causal || kt + BK <= q0 + off + 1);
+    const bool inb = kt + BK <= klen && (!p.causal || kt + BK <= q0 + off + 1);
+    const bool full = KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL && q0 + kAttnBq <= Sq && inb;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 sacc, dpacc;
@@ -223,6 +223,36 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], p.scale_log2, -lse2));
+          sacc[r] = pv * (dpacc[r] - delta);
+        }
+      } else if ((KIND == ATTN_MASK_BOOL || (KIND == ATTN_MASK_ADD && !MV)) && inb) {
+        // Every key in bounds for every query: the mask (and a query without
+        // any visible key) alone. (Not for additive runs: the extra code path
+        // made that variant spill.)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float tv = sacc[r] * p.scale_log2;
+          bool excluded = !live;
+          if constexpr (KIND == ATTN_MASK_ADD) {
+            uint32_t bits;
+            if constexpr (MV) {
+              bits = mask_run_value(mv, kb, r, false);
+            } else {
+              const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+              bits = live ? *reinterpret_cast<const uint16_t*>(p.mask + (mrow + key) * 2) : 0u;
+            }
+            tv = fmaf(to_float<BF16>(bits), kLog2eA, tv);
+          } else {
+            uint32_t byte;
+            if constexpr (MV) {
+              byte = mask_run_value(mv, kb, r, true);
+            } else {
+              const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+              byte = live ? (uint32_t)(uint8_t)p.mask[mrow + key] : 0u;
+            }
+            if (byte != 0) excluded = true;
+          }
+          const float pv = excluded ? 0.0f : __builtin_amdgcn_exp2f(tv - lse2);
           sacc[r] = pv * (dpacc[r] - delta);
         }
       } else {
@@ -532,9 +562,8 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
           // A block whose every (query, key) score is visible (all queries and
           // keys in range, past the causal boundary, no per-score mask) takes
           // the probabilities without any exclusion test.
-          const bool full = KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL && qb0 + 32 <= Sq &&
-                            k0 + kAttnBwdBk <= klen &&
-                            (!p.causal || k0 + kAttnBwdBk - 1 <= qb0 + off);
+          const bool inb = k0 + kAttnBwdBk <= klen && (!p.causal || k0 + kAttnBwdBk - 1 <= qb0 + off);
+          const bool full = KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL && qb0 + 32 <= Sq && inb;
           if (full) {
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
@@ -546,6 +575,27 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
               for (int e = 0; e < 4; ++e) {
                 const int r = 4 * rg + e;
                 const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], p.scale_log2, -lv[e]));
+                pr[r] = pv;
+                dsr[r] = pv * (dpacc[r] - dv4[e]);
+              }
+            }
+          } else if ((KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL) && inb) {
+            // Every key in bounds for every query: the mask alone (a query
+            // past Sq or without any visible key has LSE -inf here).
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+              const int ql = 32 * qb + 8 * rg + 4 * g;
+              const float4 l2 = *reinterpret_cast<const float4*>(&lses[ql]);
+              const float4 dl = *reinterpret_cast<const float4*>(&dels[ql]);
+              const float lv[4] = {l2.x, l2.y, l2.z, l2.w}, dv4[4] = {dl.x, dl.y, dl.z, dl.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = 4 * rg + e;
+                float tv = sacc[r] * p.scale_log2;
+                bool excluded = lv[e] == kNegInfA;
+                if constexpr (KIND == ATTN_MASK_ADD) tv = fmaf(to_float<BF16>(mvk[r]), kLog2eA, tv);
+                else if (mvk[r] != 0) excluded = true;
+                const float pv = excluded ? 0.0f : __builtin_amdgcn_exp2f(tv - lv[e]);
                 pr[r] = pv;
                 dsr[r] = pv * (dpacc[r] - dv4[e]);
               }
