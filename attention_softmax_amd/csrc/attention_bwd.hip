@@ -5,22 +5,21 @@
 // points to; the softmax gradient itself is the lmnt.cn page's sec. 3.3 rule,
 // dS = P * (dP - rowsum(dP * P)), with rowsum(dP * P) = rowsum(dO * O)).
 //
-// Three launches (four for D = 128, where dK and dV take a pass each), all
+// Two launches (three for D = 128, where dK and dV take a pass each), all
 // deterministic (no atomics):
-//  1. delta = rowsum(dO * O) per query row, fp32, into the workspace;
-//  2. dQ, one workgroup per 128 queries (query-stationary, as the forward):
-//     S^T = K Q^T and dP^T = V dO^T leave each lane 16 keys of one query;
+//  1. dQ, one workgroup per 128 queries (query-stationary, as the forward);
+//     it first forms delta = rowsum(dO * O) of its queries in fp32 and stores
+//     it in the workspace for step 2. S^T = K Q^T and dP^T = V dO^T leave
+//     each lane 16 keys of one query;
 //     P = exp(S*scale + mask - LSE); dS^T = P (dP^T - delta); dQ^T += K^T dS^T
 //     with the dS registers as the B operand (keys contracted in the order the
 //     S^T layout holds them, K^T read from a transposed LDS tile);
-//  3. dK and dV, one workgroup per 128 keys of one key/value head
+//  2. dK and dV, one workgroup per 128 keys of one key/value head
 //     (key-stationary): for every query head of its group and every tile of
 //     32 or 64 queries, S = Q K^T and dP = dO V^T leave each lane 16 queries
 //     of one key per 32-query block; dV^T += dO^T P and dK^T += Q^T dS with P
 //     and dS as B operands.
 // Lane layouts of v_mfma_f32_32x32x16: see attention.hip.
-
-#include <algorithm>
 
 #include "attention.hpp"
 
@@ -29,38 +28,7 @@ namespace {
 
 using namespace attn;
 
-// ------------------------------------------------------------ 1. delta
-
-template <bool BF16, int D>
-__global__ void __launch_bounds__(256) attn_delta_kernel(AttnBwdParams p) {
-  constexpr int LPR = D / 8;       // lanes per row: 16 bytes each
-  constexpr int RPB = 256 / LPR;   // rows per workgroup and pass
-  const int lane = (int)(threadIdx.x % LPR);
-  const int64_t rows = (int64_t)p.B * p.H * p.Sq;
-  // Grid-stride over rows (the grid is capped); the bound is uniform per
-  // workgroup, so every lane reaches the shuffles.
-  for (int64_t row0 = (int64_t)blockIdx.x * RPB; row0 < rows; row0 += (int64_t)gridDim.x * RPB) {
-    const int64_t row = row0 + threadIdx.x / LPR;
-    float acc = 0.0f;
-    if (row < rows) {
-      const uint32_t i = (uint32_t)(row % p.Sq);
-      const uint32_t bh = (uint32_t)(row / p.Sq);
-      const uint32_t h = bh % p.H, b = bh / p.H;
-      const u32x4 g = *reinterpret_cast<const u32x4*>(
-          p.dout + ((int64_t)b * p.sdo_b + (int64_t)h * p.sdo_h + (int64_t)i * p.sdo_s + 8 * lane) * 2);
-      const u32x4 o = *reinterpret_cast<const u32x4*>(
-          p.o + ((int64_t)b * p.so_b + (int64_t)h * p.so_h + (int64_t)i * p.so_s + 8 * lane) * 2);
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        acc = fmaf(to_float<BF16>(elem(g, j)), to_float<BF16>(elem(o, j)), acc);
-    }
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (row < rows && lane == 0) p.delta[row] = acc;
-  }
-}
-
-// ---------------------------------------------------------------- 2. dQ
+// ---------------------------------------------------------------- 1. dQ
 
 template <bool BF16, int D, int KIND, bool MV>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -111,10 +79,13 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
   const float lse = qvalid ? p.lse[lrow] : kNegInfA;
   const bool live = lse != kNegInfA;  // a query that sees no key has no gradient
   const float lse2 = live ? lse * kLog2eA : 0.0f;
-  const float delta = qvalid ? p.delta[lrow] : 0.0f;
 
   // Q and dO fragments: the B operands of S^T = K Q^T and dP^T = V dO^T.
+  // Lanes c and c + 32 hold the two halves of query qi's rows, so the same
+  // loads of O give delta = rowsum(dO * O) of the query with one exchange;
+  // lanes of the first half store it for the dK pass.
   u32x4 qf[D / 16], df[D / 16];
+  float dpart = 0.0f;
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
     qf[s] = u32x4{0, 0, 0, 0};
@@ -124,8 +95,15 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
           p.q + ((int64_t)b * p.sq_b + (int64_t)h * p.sq_h + (int64_t)qi * p.sq_s + s * 16 + 8 * g) * 2);
       df[s] = *reinterpret_cast<const u32x4*>(
           p.dout + ((int64_t)b * p.sdo_b + (int64_t)h * p.sdo_h + (int64_t)qi * p.sdo_s + s * 16 + 8 * g) * 2);
+      const u32x4 of = *reinterpret_cast<const u32x4*>(
+          p.o + ((int64_t)b * p.so_b + (int64_t)h * p.so_h + (int64_t)qi * p.so_s + s * 16 + 8 * g) * 2);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        dpart = fmaf(to_float<BF16>(elem(df[s], j)), to_float<BF16>(elem(of, j)), dpart);
     }
   }
+  const float delta = dpart + __shfl_xor(dpart, 32);
+  if (qvalid && g == 0) p.delta[lrow] = delta;
   f32x16 dq[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -318,7 +296,7 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
     }
 }
 
-// ------------------------------------------------------------ 3. dK, dV
+// ------------------------------------------------------------ 2. dK, dV
 
 // PASS 2 accumulates dK and dV together; for D = 128 that needs more than 256
 // registers (one wavefront per SIMD), so there PASS 0 (dV alone: S, P) and
@@ -712,12 +690,6 @@ template <bool BF16, int D, int KIND>
 hipError_t launch_bwd_kind(const AttnBwdParams& p, hipStream_t st) {
   const dim3 block(256);
   if (p.Sq > 0) {
-    const int64_t rows = (int64_t)p.B * p.H * p.Sq;
-    const int rpb = 256 / (D / 8);
-    const int64_t wgs = std::min<int64_t>((rows + rpb - 1) / rpb, 65536);
-    hipLaunchKernelGGL((attn_delta_kernel<BF16, D>), dim3((uint32_t)wgs), block, 0, st, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const dim3 gq(p.H * p.B * ((p.Sq + kAttnBq - 1) / kAttnBq));
     if constexpr (KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL) {
       if (p.mask_vec) hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, KIND, true>), gq, block, 0, st, p);
@@ -725,7 +697,8 @@ hipError_t launch_bwd_kind(const AttnBwdParams& p, hipStream_t st) {
     } else {
       hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, KIND, false>), gq, block, 0, st, p);
     }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
   if (p.Sk > 0) {
     const dim3 gk(p.Hk * p.B * ((p.Sk + kAttnBwdBk - 1) / kAttnBwdBk));

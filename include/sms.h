@@ -295,7 +295,7 @@ int64_t sms_attention_workspace_bytes(int64_t B, int64_t H, int64_t Sq);
  *                  aligned, owned by the caller and not used by any call that
  *                  may run at the same time (else SMS_ERR_WORKSPACE); its
  *                  contents on entry do not matter
- *   stream         hipStream_t to enqueue on (three kernel launches; four
+ *   stream         hipStream_t to enqueue on (two kernel launches; three
  *                  with D = 128, where dK and dV take a launch each)
  *
  * Row alignment and limits as for sms_attention_forward, and also
