@@ -241,6 +241,9 @@ attn_fwd_kernel(AttnParams p) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(&ks[(kb * 32 + c) * KP + s * 16 + 8 * g]);
         sacc[kb] = mfma_32x32x16<BF16>(a, qf[s], sacc[kb]);
       }
+    // K reads ten products ahead: 2-5 % faster than the scheduler's own order
+    // (measured without per-score mask runs, whose loads share the region).
+    if constexpr (MV == 0) pin_reads_ahead<2 * (D / 16), 10, 1>();
 
     // Scores in the log2 domain, the mask and the key bounds. A tile whose
     // every score is visible to every query of the workgroup (keys in range
@@ -375,6 +378,7 @@ attn_fwd_kernel(AttnParams p) {
         const u32x2 a1 = *reinterpret_cast<const u32x2*>(vrow + tcol_const(db, 2 * s + 1));
         oacc[db] = mfma_32x32x16<BF16>(u32x4{a0.x, a0.y, a1.x, a1.y}, pb[s], oacc[db]);
       }
+    if constexpr (MV == 0) pin_reads_ahead<4 * (D / 32), 4, 2>();  // V^T reads, as above
   }
 
   const float L = other_half_sum(l_i);  // both halves of the query's keys

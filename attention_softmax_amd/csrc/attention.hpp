@@ -149,6 +149,24 @@ rows_rsrc(const char* base, int rows, int64_t pitch, int row_bytes) {
   const int bytes = rows > 0 ? (int)((int64_t)(rows - 1) * pitch + row_bytes) : 0;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes, kRsrcWord3A);
 }
+// Scheduling of a run of N matrix products fed from LDS, RPP reads per
+// product: the reads of the first LA products go out together, then each
+// product is followed by the reads of the one LA places later, so that every
+// read has LA products' time to arrive. (Left to itself the scheduler issues
+// each read just before its product and waits on it, holding few registers.)
+// Applies to the scheduling region it is placed in, after the products.
+template <int N, int LA, int RPP>
+__device__ inline __attribute__((always_inline)) void pin_reads_ahead() {
+  constexpr int L = LA < N ? LA : N;
+  __builtin_amdgcn_sched_group_barrier(0x100, RPP * L, 0);  // LDS reads
+#pragma unroll
+  for (int i = 0; i < N - L; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one product
+    __builtin_amdgcn_sched_group_barrier(0x100, RPP, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, L, 0);
+}
+
 __device__ inline __attribute__((always_inline)) u32x4 rsrc_load(__amdgpu_buffer_rsrc_t r,
                                                                  uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);

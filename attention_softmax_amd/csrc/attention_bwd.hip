@@ -197,6 +197,7 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
         const u32x4 av = *reinterpret_cast<const u32x4*>(&vs[(kb * 32 + c) * KP + s * 16 + 8 * g]);
         dpacc = mfma_32x32x16<BF16>(av, df[s], dpacc);
       }
+      pin_reads_ahead<2 * (D / 16), 4, 1>();  // K / V reads four products ahead (1-2 % faster)
       if (full) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -535,6 +536,10 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
               dpacc = mfma_32x32x16<BF16>(ad, vf[s], dpacc);
             }
           }
+          // Q / dO reads four products ahead (1-2 % faster); not with per-score
+          // masks, whose registers are short already.
+          if constexpr (KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL)
+            pin_reads_ahead<(kDK ? 2 : 1) * (D / 16), 4, 1>();
           // Register r holds query qb0 + 8*(r/4) + 4g + r%4 of this lane's key.
           float pr[16], dsr[16];
           // A block whose every (query, key) score is visible (all queries and
