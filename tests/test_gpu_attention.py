@@ -56,7 +56,8 @@ def check(q, k, v, mask, mode, kind, scale, causal, what):
                              to_np(lse), ref_lse)
 
 
-SHAPES = [(1, 1), (37, 63), (128, 64), (129, 65), (200, 300), (64, 1000)]
+# (300, 100): bottom-right causal leaves the first 128-query tile without any key.
+SHAPES = [(1, 1), (37, 63), (128, 64), (129, 65), (200, 300), (64, 1000), (300, 100)]
 MASKS = [("none", "none"), ("sq_sk", "additive"), ("b_sq_sk", "neginf"), ("b_1_sk", "neginf"),
          ("full", "additive"), ("b_sq_sk", "bool"), ("key_lengths", "lengths")]
 
