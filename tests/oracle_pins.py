@@ -341,6 +341,56 @@ def pin_backward_invariants():
                                                      2 * 0.75 * (-1 - (-0.5))], rtol=0)
 
 
+def _bf16_values_torch(bits):
+    """bf16 bit patterns to float64 through torch's own bfloat16 type, a decoder
+    that shares nothing with the oracle's."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16).copy())
+    return t.view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def pin_backward_tensor_gather():
+    """The whole-tensor backward (``backward``) and the row-subset one
+    (``backward_rows``) against the softmax Jacobian applied row by row with
+    explicit (b, h, q) indexing: y and dy differ in every row and along every
+    axis, so a swap of y and dy, a row taken from another (b, h, q) or a wrong
+    decoding of the typed values changes the result (lmnt.cn page sec. 3.3)."""
+    rng = _rng(23)
+    B, H, Sq, Sk = 2, 3, 4, 5
+    for dtype in ("f32", "f16", "bf16"):
+        # y: a distinct positive row per (b, h, q) (a probability-like row that
+        # need not sum to 1: the formula does not assume it); dy: signed.
+        yv = (rng.integers(1, 64, (B, H, Sq, Sk)) / 64.0
+              + np.arange(B * H * Sq).reshape(B, H, Sq, 1) / 1024.0)
+        dyv = rng.integers(-40, 41, (B, H, Sq, Sk)) / 16.0
+        if dtype == "bf16":
+            # values exact in bf16 (8 significant bits): multiples of 1/64 below 4
+            yv = np.round(yv * 64) / 64
+            y = (yv.astype(F32).view(np.uint32) >> 16).astype(np.uint16)
+            dy = (dyv.astype(F32).view(np.uint32) >> 16).astype(np.uint16)
+            yd, dyd = _bf16_values_torch(y), _bf16_values_torch(dy)
+            assert (yd == yv).all() and (dyd == dyv).all()
+        else:
+            t = F32 if dtype == "f32" else F16
+            y, dy = yv.astype(t), dyv.astype(t)
+            yd, dyd = y.astype(np.float64), dy.astype(np.float64)
+        sc = 0.75
+        full = S.backward(y, dy, dtype, scale=sc)
+        assert full.shape == (B, H, Sq, Sk)
+        rows = [5, 0, B * H * Sq - 1, 13, 7]
+        sub = S.backward_rows(y, dy, dtype, rows, scale=sc)
+        for b, h, q in itertools.product(range(B), range(H), range(Sq)):
+            yr, dyr = yd[b, h, q], dyd[b, h, q]
+            J = np.diag(yr) - np.outer(yr, yr)      # d softmax / d s, symmetric
+            want = sc * (J @ dyr)
+            _close(full[b, h, q], want, atol=1e-15, rtol=1e-13,
+                   what=f"backward {dtype} ({b},{h},{q})")
+            r = (b * H + h) * Sq + q
+            if r in rows:
+                _close(sub[rows.index(r)], want, atol=1e-15, rtol=1e-13,
+                       what=f"backward_rows {dtype} row {r}")
+
+
 def pin_bool_masks():
     """Boolean masks: nonzero excludes the key (score -inf); exhaustive brute
     force over every pattern for n <= 6 and a hand row fixing the polarity."""
@@ -605,5 +655,5 @@ FORWARD_PINS = [pin_two_element_closed_form, pin_hand_rows, pin_fully_masked_row
                 pin_tensor_indexing, pin_decode, pin_scale_rounding, pin_bool_masks,
                 pin_key_lengths, pin_causal_alignments]
 BACKWARD_PINS = [pin_backward_finite_differences, pin_backward_jacobian,
-                 pin_backward_invariants]
+                 pin_backward_invariants, pin_backward_tensor_gather]
 ALL_PINS = FORWARD_PINS + BACKWARD_PINS + ATTENTION_PINS

@@ -144,6 +144,55 @@ def test_planted_decode_mistake_is_caught(monkeypatch):
     assert _run_all_pins()
 
 
+_orig_backward_rows = S.backward_rows
+
+
+def _backward_rows_mutant(kind):
+    """A copy of the oracle's row gather with one plausible mistake planted."""
+    def rows_fn(y, dy, dtype, rows, scale=1.0):
+        y, dy = np.asarray(y), np.asarray(dy)
+        B, H, Sq, Sk = y.shape
+        sc = S._fp32(scale)
+        out = np.empty((len(rows), Sk))
+        for i, r in enumerate(rows):
+            b, h, q = S.row_index(y.shape, int(r))
+            yr, dyr = y[b, h, q, :], dy[b, h, q, :]
+            if kind == "swap":            # y and dy exchanged
+                yr, dyr = dyr, yr
+            elif kind == "dy_bqh":        # dy read as if laid out [B, Sq, H, Sk]
+                dyr = dy.reshape(B, Sq, H, Sk)[b, q, h, :]
+            dec = S.decode
+            if kind == "decode" and dtype == "bf16":   # bf16 bits taken as fp16 bits
+                out[i] = S._backward_one_row(dec(yr.view(np.float16), "f16"),
+                                             dec(dyr.view(np.float16), "f16"), sc)
+                continue
+            if kind == "decode" and dtype == "f16":    # fp16 bits taken as bf16 bits
+                out[i] = S._backward_one_row(dec(yr.view(np.uint16), "bf16"),
+                                             dec(dyr.view(np.uint16), "bf16"), sc)
+                continue
+            out[i] = S._backward_one_row(dec(yr, dtype), dec(dyr, dtype), sc)
+        return out
+    return rows_fn
+
+
+@pytest.mark.parametrize("kind", ["swap", "dy_bqh", "decode"])
+def test_planted_backward_gather_mistake_is_caught(kind, monkeypatch):
+    """Mistakes in the tensor-level backward's row gather (y/dy swapped, dy
+    from another (b, h, q), the wrong decoding of typed values): ``backward``
+    goes through ``backward_rows``, so one planted copy covers both."""
+    monkeypatch.setattr(S, "backward_rows", _backward_rows_mutant(kind))
+    failures = _run_all_pins()
+    assert any(n == "pin_backward_tensor_gather" for n, _ in failures), \
+        f"planted gather mistake '{kind}' passed every pin"
+
+
+def test_unplanted_backward_gather_copy_passes(monkeypatch):
+    """The planting copy without a mistake passes every pin (so the failures
+    above come from the mistakes, not from the copy)."""
+    monkeypatch.setattr(S, "backward_rows", _backward_rows_mutant("none"))
+    assert not _run_all_pins()
+
+
 _orig_excluded = S._excluded
 _orig_offset = S.causal_offset
 
