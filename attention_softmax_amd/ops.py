@@ -249,7 +249,7 @@ def _attn_mask(mask, q, scores_shape):
 
 
 def sms_attention_forward(q, k, v, mask=None, scale=None, is_causal=False, o=None,
-                          return_lse=False, stream=None):
+                          return_lse=False, stream=None, lse=None):
     """O = softmax(Q K^T * scale + mask) V, fused on the matrix cores (C ABI
     sms_attention_forward).
 
@@ -258,7 +258,8 @@ def sms_attention_forward(q, k, v, mask=None, scale=None, is_causal=False, o=Non
     or 128. ``mask``: as for ``sms_forward`` (shapes over [B,H,Sq,Sk], additive
     of q's dtype, boolean, or int32 key lengths [B]). ``scale`` defaults to
     1/sqrt(D). Returns O (``o`` if given), and the fp32 log-sum-exp [B,H,Sq]
-    too when ``return_lse``.
+    too when ``return_lse`` (written into ``lse`` if given, a contiguous
+    float32 [B,H,Sq] GPU tensor; giving it implies ``return_lse``).
     """
     _attn_check(((q, "q"), (k, "k"), (v, "v")), q)
     B, H, Hk, Sq, Sk, D = _attn_shapes(q, k, v)
@@ -267,7 +268,14 @@ def sms_attention_forward(q, k, v, mask=None, scale=None, is_causal=False, o=Non
     _require_gpu(o, "o")
     if o.shape != q.shape or o.dtype != q.dtype or o.stride(-1) != 1:
         raise ValueError("o must have q's shape and dtype, last axis contiguous")
-    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device) if return_lse else None
+    if lse is not None:
+        _require_gpu(lse, "lse")
+        if (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Sq)
+                or not lse.is_contiguous() or lse.device != q.device):
+            raise ValueError("lse must be a contiguous float32 [B, H, Sq] tensor on q's device")
+        return_lse = True
+    elif return_lse:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     mptr, mode_code = _attn_mask(mask, q, (B, H, Sq, Sk))
     if scale is None:
         scale = 1.0 / float(D) ** 0.5

@@ -15,7 +15,8 @@ from attention_softmax_amd import (SmsError, attention, sms_attention_backward,
                                    sms_attention_forward, sms_attention_workspace_bytes)
 from attention_softmax_amd.workloads import TORCH_DTYPE, draw_lengths, draw_mask, draw_x
 from tests.parity import DTYPE_OF, mask_4d, to_np
-from tests.tolerance import attention_grad_tolerances, compare_attention, compare_grads
+from tests.tolerance import (attention_forward_bounds, attention_grad_tolerances,
+                             compare_attention, compare_grads)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -38,21 +39,26 @@ def make_mask(shape, mode, kind, dtype, seed):
     return draw_mask(shape, mode, dtype, ("normal", 2.0), seed, DEV)
 
 
+def fwd_bounds(qn, kn, vn, dt, o_ref, lse_ref, scale, **kw):
+    """The forward's error bounds (tests/tolerance.py) from the oracle's
+    probabilities of these typed inputs."""
+    P, _ = oracle.attention.probabilities(qn, kn, dt, scale=scale, **kw)
+    return attention_forward_bounds(P, lse_ref, *(oracle.decode(a, dt) for a in (qn, kn, vn)),
+                                    o_ref, float(np.float32(scale)), dt)
+
+
 def check(q, k, v, mask, mode, kind, scale, causal, what):
     dt = DTYPE_OF[q.dtype]
     o, lse = sms_attention_forward(q, k, v, mask, scale, causal, return_lse=True)
     torch.cuda.synchronize()
     okind = {"bool": "bool", "lengths": "lengths"}.get(kind, "additive")
-    ref, ref_lse = oracle.attention.forward(
-        to_np(q), to_np(k), to_np(v), dt,
-        mask=None if kind in ("none", "lengths") else mask_4d(mask, mode), scale=scale,
-        is_causal=causal, mask_kind=okind,
-        key_lengths=to_np(mask) if kind == "lengths" else None)
-    B, H, Sq, D = q.shape
-    Hk = k.shape[1]
-    vabs = np.abs(oracle.decode(to_np(v), dt)).max(axis=(2, 3))  # [B, Hk]
-    vmax = np.repeat(vabs, H // Hk, axis=1)[:, :, None, None]
-    return compare_attention(oracle.decode(to_np(o), dt), ref, vmax, dt, what,
+    kw = dict(mask=None if kind in ("none", "lengths") else mask_4d(mask, mode),
+              is_causal=causal, mask_kind=okind,
+              key_lengths=to_np(mask) if kind == "lengths" else None)
+    qn, kn, vn = to_np(q), to_np(k), to_np(v)
+    ref, ref_lse = oracle.attention.forward(qn, kn, vn, dt, scale=scale, **kw)
+    bounds = fwd_bounds(qn, kn, vn, dt, ref, ref_lse, scale, **kw)
+    return compare_attention(oracle.decode(to_np(o), dt), ref, bounds, dt, what,
                              to_np(lse), ref_lse)
 
 
@@ -98,10 +104,10 @@ def test_attention_strided_and_large_scores(dtype):
     o = obuf.permute(0, 2, 1, 3)
     sms_attention_forward(q, k, v, None, 0.25, True, o=o)
     torch.cuda.synchronize()
-    ref, _ = oracle.attention.forward(to_np(q.contiguous()), to_np(k.contiguous()),
-                                      to_np(v.contiguous()), dtype, scale=0.25, is_causal=True)
-    vmax = np.abs(oracle.decode(to_np(v.contiguous()), dtype)).max(axis=(2, 3))[:, :, None, None]
-    compare_attention(oracle.decode(to_np(o.contiguous()), dtype), ref, vmax, dtype, "strided")
+    qn, kn, vn = (to_np(t.contiguous()) for t in (q, k, v))
+    ref, ref_lse = oracle.attention.forward(qn, kn, vn, dtype, scale=0.25, is_causal=True)
+    bounds = fwd_bounds(qn, kn, vn, dtype, ref, ref_lse, 0.25, is_causal=True)
+    compare_attention(oracle.decode(to_np(o.contiguous()), dtype), ref, bounds, dtype, "strided")
     check(q.contiguous(), k.contiguous(), v.contiguous(), None, "none", "none", 1.0, False,
           "scale 1")
 
@@ -273,12 +279,14 @@ def test_attention_bench_workload_sampled():
         qn, kn, vn, don = head(q), head(k), head(v), head(do)
         o_ref, lse_ref = oracle.attention.forward(qn, kn, vn, "f16", scale=sc, is_causal=True)
         vd = oracle.decode(vn, "f16")
-        compare_attention(oracle.decode(head(o), "f16"), o_ref,
-                          np.abs(vd).max(axis=(2, 3))[:, :, None, None], "f16", what + " O",
-                          head(lse), lse_ref)
-        refs = oracle.attention.backward(qn, kn, vn, don, "f16", scale=sc, is_causal=True)
         P, ref_lse = oracle.attention.probabilities(qn, kn, "f16", scale=sc, is_causal=True)
         qd, kd, dod = (oracle.decode(a, "f16") for a in (qn, kn, don))
+        bounds = attention_forward_bounds(P, ref_lse, qd, kd, vd, o_ref, float(np.float32(sc)),
+                                          "f16")
+        st = compare_attention(oracle.decode(head(o), "f16"), o_ref, bounds, "f16", what + " O",
+                               head(lse), lse_ref)
+        say(f"    O: {st}")
+        refs = oracle.attention.backward(qn, kn, vn, don, "f16", scale=sc, is_causal=True)
         dP = dod @ np.swapaxes(vd, 2, 3)
         tols, rms = attention_grad_tolerances(P, dP, qd, kd, dod, np.abs(vd).max(axis=(2, 3)),
                                               ref_lse, float(np.float32(sc)), "f16", refs, None,

@@ -75,35 +75,125 @@ def compare(got, ref, dtype, what="", rowsum=False, live_rows=None):
 
 # ------------------------------------------------------- fused attention
 #
-# O = sum_k p_k v_k / L with fp32 scores and sums, the probabilities rounded to
-# the I/O dtype T (unit roundoff u_T = 2^-11 fp16, 2^-8 bf16) for the P V
-# product while L sums them unrounded, and O rounded to T at the end. Per
-# element: |O - O_ref| <= u_T * max_k |v_k| (the rounded probabilities) plus
-# the fp32 score error (below 2^-20 relative for |scores| < 2^4) plus half an
-# ulp of O; the bound allows twice that: 2 u_T max|v| + 2 ulp_T(O_ref). The
-# log-sum-exp is fp32: |LSE - LSE_ref| <= 2^-18 (1 + |LSE_ref|). Rows with no
-# visible key: O exactly 0 and LSE = -inf.
+# The forward computes, per query row i, fp32 scores s_ik = scale q_i.k_k
+# (+ mask), exponentials p~_ik = exp(s_ik - m_i) against a reference maximum
+# m_i no larger than the row's maximum (so the largest p~ is >= 1), their fp32
+# sum L_i, the product acc_id = sum_k RN_T(p~_ik) v_kd with the probabilities
+# rounded to the I/O dtype T (unit roundoff u = 2^-11 fp16, 2^-8 bf16) and
+# accumulated in fp32, and O_id = RN_T(acc_id / L_i). With the oracle's exact
+# probabilities P_ik = p~_ik / L_i and output O, the first-order error terms:
+#  * rounding p~ to T: relative u, or an absolute 2^(e_min - p) in the
+#    subnormal range, which in units of P is at most u 2^e_min max_k P_ik
+#    (because L_i >= 1); so u P'_ik with P'_ik = max(P_ik, 2^e_min max_k P_ik);
+#  * the fp32 arithmetic of p~ (relative E_ik): the dot product over D,
+#    (D + 4) 2^-24 scale (|q_i|.|k_k|), and the shifted exponent and the
+#    exponential, 2^-22 (1 + |s_ik| + |m_i|);
+#  * the fp32 accumulation of acc over n_i visible keys, (n_i + 4) 2^-24
+#    (P|V|)_id, and of L (the same relative size on O);
+#  * the division by L, 2^-22 |O|, and rounding O to T, half an ulp.
+# Three checks, each of which a wrong kernel must pass to go unnoticed:
+#  1. per element, twice the worst case of all terms aligned, plus 2 ulp;
+#  2. the Frobenius norm of the error: the rounding errors of distinct
+#     probabilities, sums and outputs are independent and zero-mean (round to
+#     nearest), so E ||err||^2 <= sum sigma^2 with sigma^2 the squares of the
+#     per-key terms summed over keys; the bound is (1.5 + 4/sqrt(N)) times
+#     its root. Rounding the probabilities to a narrower type, or leaving out
+#     their rounding's tie handling, moves this by its ratio of unit roundoffs;
+#  3. the bias: sum err_id O_id / sum O_id^2 measures a common scaling of O.
+#     Round to nearest leaves it at zero up to the noise (4 sigma); a
+#     truncating rounding of P scales O by about 1 - 0.72 u. Allowed: u/8.
+# The log-sum-exp is fp32: |LSE - LSE_ref| <= 2^-18 (1 + |LSE_ref|). Rows
+# with no visible key: O exactly 0 and LSE = -inf.
 
 ATTN_U = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+_TMIN = {"f16": 2.0 ** -14, "bf16": 2.0 ** -126}
 
 
-def compare_attention(got_o, ref_o, vmax, dtype, what="", got_lse=None, ref_lse=None):
-    """``vmax``: per output row, max |v| over the keys of its (batch, kv head),
-    broadcastable to O's shape. Returns stats."""
+def attention_forward_bounds(P, lse, q, k, v, o_ref, scale, dtype):
+    """Bounds of the fused attention forward's error against the oracle.
+
+    P [B, H, Sq, Sk] and lse [B, H, Sq]: the oracle's probabilities and
+    log-sum-exp; q [B, H, Sq, D], k and v [B, Hk, Sk, D(v)] decoded float64;
+    o_ref [B, H, Sq, Dv]: the oracle's O. Returns a dict: ``tol`` (per
+    element), ``var`` (per-element variance bound sigma^2), ``u``."""
+    u = ATTN_U[dtype]
+    B, H, Sq, Sk = P.shape
+    Hk, D = k.shape[1], k.shape[3]
+    group = H // Hk if Hk else 1
+    o_ref = np.asarray(o_ref, dtype=np.float64)
+    tol = np.zeros(o_ref.shape)
+    var = np.zeros(o_ref.shape)
+    aq, ak, av = np.abs(q), np.abs(k), np.abs(v)
+    for b in range(B):
+        for h in range(H):
+            g = h // group
+            p = P[b, h]
+            if p.size == 0:
+                continue
+            live = p > 0
+            fin = np.isfinite(lse[b, h])
+            lf = np.where(fin, lse[b, h], 0.0)
+            pmax = p.max(axis=1)
+            pp = np.where(live, np.maximum(p, _TMIN[dtype] * pmax[:, None]), 0.0)
+            logp = np.where(live, np.log(np.where(live, p, 1.0)), 0.0)
+            s_abs = np.abs(logp + lf[:, None])              # |masked scaled score|
+            m_abs = np.abs(lf + np.log(np.where(pmax > 0, pmax, 1.0)))   # |row maximum|
+            E = (2.0 ** -22 * (1 + s_abs + m_abs[:, None])
+                 + (D + 4) * 2.0 ** -24 * scale * (aq[b, h] @ ak[b, g].T))
+            E = np.where(live, E, 0.0)
+            n = live.sum(axis=1)[:, None]
+            acc = (n + 4) * 2.0 ** -24
+            pv = p @ av[b, g]
+            pe = (p * E) @ av[b, g]
+            ao = np.abs(o_ref[b, h])
+            pE = (p * E).sum(axis=1)[:, None]
+            tol[b, h] = 2 * (u * (pp @ av[b, g]) + pe + acc * pv
+                             + ao * (pE + acc + 2.0 ** -22))
+            var[b, h] = (u ** 2 * ((pp ** 2) @ (av[b, g] ** 2))
+                         + ((p * E) ** 2) @ (av[b, g] ** 2)
+                         + ao ** 2 * ((p * E) ** 2).sum(axis=1)[:, None]
+                         + ((acc * pv) ** 2 + (acc * ao) ** 2) / np.maximum(n, 1)
+                         + (2.0 ** -22 * ao) ** 2)
+    half = 0.5 * ulp(o_ref, dtype)
+    tol = tol + 2 * ulp(o_ref, dtype)
+    var = var + half ** 2
+    return {"tol": tol, "var": var, "u": u}
+
+
+def compare_attention(got_o, ref_o, bounds, dtype, what="", got_lse=None, ref_lse=None):
+    """Raise unless the GPU's O (float64 of the typed output) meets the three
+    forward checks of ``attention_forward_bounds`` and, if given, its LSE the
+    fp32 bound. Returns stats (each check's value over its bound)."""
     got = np.asarray(got_o, dtype=np.float64)
     ref = np.asarray(ref_o, dtype=np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite output"
-    tol = 2 * ATTN_U[dtype] * np.asarray(vmax, dtype=np.float64) + 2 * ulp(ref, dtype)
-    err = np.abs(got - ref)
-    bad = err > tol
-    stats = {"max_abs": float(err.max()) if err.size else 0.0,
-             "max_err_over_tol": float((err / tol).max()) if err.size else 0.0}
+    tol, var, u = bounds["tol"], bounds["var"], bounds["u"]
+    err = got - ref
+    aerr = np.abs(err)
+    bad = aerr > tol
+    stats = {"max_abs": float(aerr.max()) if err.size else 0.0,
+             "max_err_over_tol": float((aerr / tol).max()) if err.size else 0.0}
     if bad.any():
-        i = np.argmax(err / tol)
+        i = np.argmax(aerr / tol)
         raise AssertionError(f"{what}: {int(bad.sum())} elements beyond tolerance; worst at "
                              f"{np.unravel_index(i, got.shape)}: got {got.flat[i]!r} want "
                              f"{ref.flat[i]!r} tol {tol.flat[i]:.3g}")
+    nz = int(np.count_nonzero(var))
+    if nz:
+        fro = float(np.sqrt((err ** 2).sum()))
+        fro_bound = (1.5 + 4.0 / np.sqrt(nz)) * float(np.sqrt(var.sum()))
+        stats["fro_over_bound"] = fro / fro_bound
+        assert fro <= fro_bound, (f"{what}: ||err||_F = {fro:.4g} above its bound "
+                                  f"{fro_bound:.4g}")
+        oo = float((ref ** 2).sum())
+        if oo > 0:
+            bias = float((err * ref).sum())
+            allow = u / 8 * oo + 4.0 * float(np.sqrt((ref ** 2 * var).sum()))
+            stats["bias"] = bias / oo
+            stats["bias_over_bound"] = abs(bias) / allow
+            assert abs(bias) <= allow, (f"{what}: O is scaled by 1 + {bias / oo:.3g} "
+                                        f"(allowed {allow / oo:.3g})")
     if got_lse is not None:
         gl = np.asarray(got_lse, dtype=np.float64)
         rl = np.asarray(ref_lse, dtype=np.float64)
