@@ -1,18 +1,27 @@
 """Throughput of the fused scaled-masked softmax, forward + backward, on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
 
 A step is one forward (y = softmax(x*scale + mask), causal rule if the workload
 has it) and one backward (dx = scale*y*(dy - sum dy*y)) over the whole synthetic
 batch, through the C ABI, with every input already in HBM. The default workload
-is fp32 x[8,32,1024,1024] ~ N(0,4), scale 1/8, additive key-padding mask
-[8,1,1024] (0 before a per-batch length L_b ~ U{256..1024}, -10000 after);
-dy ~ N(0,1) fp32.
+is the largest: fp16 x[4,32,4096,4096] = 8*N(0,1), scale 1/sqrt(128), additive
+mask [4,4096,4096] with -inf at 10 % of the positions (the diagonal kept), the
+causal rule; dy ~ N(0,1) fp16.
+
+Before the W warm-up steps, the step runs untimed for a fixed wall time
+(``--settle-seconds``) so that the GPU's clocks have left their idle state; the
+JSON line states that time and the number of steps it took. The timed region is
+exactly K steps.
 
 value = algorithmic bytes of a step / time of a step (GB/s), where algorithmic
 bytes count x and the mask once where the result depends on them, y and dy
-where y can be nonzero, and every y and dx written. One JSON line on stdout;
-diagnostics on stderr.
+where y can be nonzero, and every y and dx written. The same line carries the
+per-kernel rate of the other workloads (fp32 [1,2,64,64], fp32 [8,32,1024,1024]
+with key padding, fp16 [4,32,2048,2048] causal, bf16 [16,16,1000,1000] with a
+[1000,1000] mask), each timed after its own settle phase, and the float64
+oracle timed on the host's cores over a sample of the headline workload's rows.
+One JSON line on stdout; diagnostics on stderr.
 
     python bench.py --op attention [--steps K] [--warmup W]
 
@@ -79,15 +88,26 @@ def min_bytes(shape, dtype_bytes, mode, causal):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    # MI355X takes ~25 launches of this size after a start from idle to settle
-    # its clocks (the forward runs up to 15 % slow meanwhile): warm up past it.
-    ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    # From idle, MI355X runs the first launches of this size up to 15 % slow
+    # while its clocks ramp: the settle phase runs the step past that, for a
+    # fixed wall time, before the warm-up steps.
+    ap.add_argument("--settle-seconds", type=float, default=2.0,
+                    help="untimed wall time the step runs before --warmup (0 = none)")
+    ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--others", default="1,2,3,5",
+                    help="workloads whose per-kernel rate the line also reports ('' = none)")
+    ap.add_argument("--other-launches", type=int, default=20,
+                    help="timed launches of each kernel of the other workloads")
     ap.add_argument("--op", default="softmax", choices=["softmax", "attention"],
                     help="softmax (the headline line) or the fused attention forward")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="time budget of the oracle CPU baseline sample (0 = skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=16.0,
+                    help="CPU work (summed over workers) of the oracle CPU baseline sample "
+                         "(0 = skip)")
+    ap.add_argument("--cpu-workers", type=int, default=16,
+                    help="most worker processes of the CPU baseline (one per core, at most "
+                         "the host's CPU count)")
     ap.add_argument("--no-copy", action="store_true", help="skip the plain-copy reference")
     ap.add_argument("--no-torch", action="store_true",
                     help="skip the unfused PyTorch reference (context only)")
@@ -213,39 +233,182 @@ def load_traffic(path, workload, role):
     return e["traffic"]
 
 
-def cpu_baseline(w, y, dy, step_bytes, rows_total, budget_s):
-    """The float64 oracle, as it stands, over a bounded sample of the same rows."""
-    import numpy as np
+_GO = None     # set by the parent when every worker holds its rows
+_READY = None  # number of workers holding their rows
+
+
+def _init_worker(go, ready):
+    global _GO, _READY
+    _GO, _READY = go, ready
+
+
+def _oracle_rows(dt, xr, mr, yr, dyr, qs, scale, causal, wait=True):
+    """Worker side of the CPU baseline: the float64 oracle, as it stands, on a
+    block of rows (forward, then backward on the GPU's y), one BLAS thread.
+    With ``wait`` it reports that it holds its rows and starts when the parent
+    says so. Returns the (start, end) of its work on the system's monotonic
+    clock."""
+    from threadpoolctl import threadpool_limits
 
     import oracle
+
+    with threadpool_limits(limits=1):
+        if wait:
+            with _READY.get_lock():
+                _READY.value += 1
+            _GO.wait()
+        t0 = time.monotonic()
+        for i in range(len(qs)):
+            oracle.forward_row(xr[i], dt, None if mr is None else mr[i], scale, causal, int(qs[i]))
+            oracle.backward_row(yr[i], dyr[i], dt, scale)
+        return t0, time.monotonic()
+
+
+def _worker_ready():
+    import oracle  # noqa: F401  (import cost paid before the timed sample)
+    time.sleep(0.2)  # so that every worker takes one of these
+    return os.getpid()
+
+
+def start_cpu_pool(n_workers):
+    """Worker processes for the CPU baseline, started fresh ("spawn") before
+    this process touches the GPU; each imports numpy and the oracle only."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+
+    ctx = mp.get_context("spawn")
+    go, ready = ctx.Event(), ctx.Value("i", 0)
+    pool = cf.ProcessPoolExecutor(n_workers, mp_context=ctx, initializer=_init_worker,
+                                  initargs=(go, ready))
+    pids = {f.result() for f in [pool.submit(_worker_ready) for _ in range(n_workers)]}
+    return {"pool": pool, "go": go, "ready": ready}, len(pids)
+
+
+def cpu_baseline(cp, n_workers, w, y, dy, fwd_b, bwd_b, cpu_seconds, cap_bytes=6 << 30):
+    """The float64 oracle over a bounded, seeded sample of the workload's rows
+    (forward + backward per row). The sample is sized for about ``cpu_seconds``
+    of CPU work (from a short calibration) and at most ``cap_bytes`` of row
+    data, split evenly over the worker processes, and handed to them before
+    the clock starts; all start together, and the time is from the first
+    start to the last end. GB/s of the same algorithmic bytes per row as the
+    GPU figure."""
+    import concurrent.futures as cf
+
+    import numpy as np
+
     from tests.parity import gather_mask_rows, gather_rows
 
     B, H, Sq, Sk = w["x"].shape
-    dt = w["dtype"]
-    done = 0
-    spent = 0.0
-    chunk = 64
-    r0 = 0
-    while spent < budget_s and r0 < rows_total:
-        rows = list(range(r0, min(r0 + chunk, rows_total)))
-        xr = gather_rows(w["x"], rows)
-        mr = gather_mask_rows(w["mask"], w["mode"], w["x"].shape, rows)
-        yr, dyr = gather_rows(y, rows), gather_rows(dy, rows)
-        t0 = time.perf_counter()
-        for i, r in enumerate(rows):
-            oracle.forward_row(xr[i], dt, None if mr is None else mr[i], w["scale"], w["causal"],
-                               r % Sq)
-            oracle.backward_row(yr[i], dyr[i], dt, w["scale"])
-        spent += time.perf_counter() - t0
-        done += len(rows)
-        r0 += chunk
-    per_row = step_bytes / rows_total
-    gbps = done * per_row / spent / 1e9
-    del np
-    return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"forward+backward of rows 0..{done - 1} ({done} of {rows_total} rows, "
-                      f"{spent:.1f} s, one thread, float64 numpy oracle)",
-            "rows_per_s": round(done / spent, 1)}
+    rows_total = B * H * Sq
+    dt, causal = w["dtype"], w["causal"]
+    esz = w["x"].element_size()
+    # bytes of row r: the x (and mask share) it reads, y written; the backward
+    # reads y and dy where y can be nonzero and writes dx. Summed over every row
+    # these are exactly the forward's and the backward's algorithmic bytes.
+    full = rows_total * Sk
+    kept_all = (fwd_b // esz) - full          # x and mask elements read by the forward
+    x_all = (bwd_b // esz - full) // 2        # x elements read (= y, dy read by the backward)
+    mfrac = kept_all / x_all - 1.0 if x_all else 0.0
+
+    def row_bytes(q):
+        kept = np.minimum(q + 1, Sk) if causal else np.full_like(q, Sk)
+        return ((kept * (1.0 + mfrac) + Sk) + (2 * kept + Sk)) * esz
+
+    def gather(rows):
+        return (gather_rows(w["x"], rows), gather_mask_rows(w["mask"], w["mode"],
+                                                            w["x"].shape, rows),
+                gather_rows(y, rows), gather_rows(dy, rows))
+
+    order = np.random.default_rng(12345).permutation(rows_total)
+    # calibration: one worker, no barrier
+    cal = order[:64].tolist()
+    xr, mr, yr, dyr = gather(cal)
+    t0, t1 = cp["pool"].submit(_oracle_rows, dt, xr, mr, yr, dyr, np.asarray(cal) % Sq,
+                               w["scale"], causal, False).result()
+    per_row = (t1 - t0) / len(cal)
+    n = int(min(rows_total, cpu_seconds / per_row, cap_bytes // (4 * Sk * esz)))
+    n = max(n_workers, n - n % n_workers)
+    rows = order[:n].tolist()
+    xr, mr, yr, dyr = gather(rows)
+    qs = np.asarray(rows) % Sq
+    share = n // n_workers
+    cp["ready"].value = 0
+    cp["go"].clear()
+    futs = []
+    for i in range(n_workers):
+        sl = slice(i * share, (i + 1) * share)
+        futs.append(cp["pool"].submit(_oracle_rows, dt, xr[sl], None if mr is None else mr[sl],
+                                      yr[sl], dyr[sl], qs[sl], w["scale"], causal, True))
+    deadline = time.monotonic() + 300
+    while cp["ready"].value < n_workers and time.monotonic() < deadline:
+        time.sleep(0.01)
+    cp["go"].set()
+    spans = [f.result() for f in cf.as_completed(futs)]
+    wall = max(e for _, e in spans) - min(s for s, _ in spans)
+    cpu_s = sum(e - s for s, e in spans)
+    done = share * n_workers
+    done_bytes = float(row_bytes(qs[:done]).sum())
+    return {"value": round(done_bytes / wall / 1e9, 4), "unit": "GB/s", "cores": n_workers,
+            "kind": "oracle",
+            "sample": f"forward+backward of {done} of {rows_total} rows (seeded random order), "
+                      f"{share} rows per worker process, one thread each, all started together "
+                      f"with their rows in memory: {wall:.2f} s wall, {cpu_s:.1f} s of CPU "
+                      f"work; float64 numpy oracle",
+            "threads": n_workers, "host_cpu_count": os.cpu_count(),
+            "rows_per_s": round(done / wall, 1)}
+
+
+def settle(torch, fn, seconds, sync_every):
+    """Run ``fn`` untimed for ``seconds`` of wall time; returns the number of calls."""
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        fn()
+        n += 1
+        if n % sync_every == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
+def time_workload(torch, cfg_id, dev, stream, launches, settle_s):
+    """Per-kernel rate of one workload: forward and backward (dy ~ N(0,1)),
+    HIP events on the launch stream around each launch, after a settle phase."""
+    from attention_softmax_amd import sms_backward, sms_forward
+    from attention_softmax_amd.workloads import CONFIGS, make_config
+
+    c = CONFIGS[cfg_id]
+    w = make_config(cfg_id, dev, with_dy=True)
+    x, mask, dy = w["x"], w["mask"], w["dy"]
+    fwd_b, bwd_b = min_bytes(x.shape, x.element_size(), w["mode"], w["causal"])
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+
+    def step():
+        sms_forward(x, mask, y, w["scale"], w["causal"], stream=stream)
+        sms_backward(y, dy, dx, w["scale"], w["causal"], stream=stream)
+
+    n_settle = settle(torch, step, settle_s, 64 if x.numel() < 1 << 20 else 4)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(launches)]
+    for e in ev:
+        e[0].record(stream)
+        sms_forward(x, mask, y, w["scale"], w["causal"], stream=stream)
+        e[1].record(stream)
+        sms_backward(y, dy, dx, w["scale"], w["causal"], stream=stream)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    out = {"workload": c["name"].rsplit(", ", 1)[0], "settle_s": settle_s,
+           "settle_steps": n_settle, "launches": launches}
+    for role, b, i in (("forward", fwd_b, 0), ("backward", bwd_b, 1)):
+        ms = sum(e[i].elapsed_time(e[i + 1]) for e in ev) / launches
+        gbps = b / (ms * 1e-3) / 1e9
+        out[role] = {"avg_us": round(ms * 1e3, 2), "bytes": b, "GBps": round(gbps, 1),
+                     "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    S = x.shape[3]
+    out["target"] = ("80 % of HBM peak (S >= 1024)" if S >= 1024 else
+                     "reported only (S < 1024)")
+    del x, mask, dy, y, dx, w
+    torch.cuda.empty_cache()
+    return out
 
 
 def torch_reference(torch, w, stream, fwd_b, bwd_b, fwd_ms, bwd_ms):
@@ -393,13 +556,14 @@ def bench_attention(args):
     cpu = None
     if args.cpu_seconds > 0:
         # the float64 oracle (forward, then backward) on the first n queries of
-        # head (0, 0), n doubling until the time budget is spent (one BLAS
-        # thread, so that `cores` is what was used)
+        # head (0, 0), n doubling until the time budget is spent; its matrix
+        # products run on BLAS threads over the host's cores (at most 16)
         from threadpoolctl import threadpool_limits
 
         n, spent, done_flops = 16, 0.0, 0.0
+        threads = max(1, min(args.cpu_workers, os.cpu_count() or 1))
         qn, kn, vn, don = (to_np(t[:1, :1]) for t in (q, k, v, do))
-        with threadpool_limits(limits=1):
+        with threadpool_limits(limits=threads):
             while spent < args.cpu_seconds and n <= S:
                 t0 = time.perf_counter()
                 oracle.attention.forward(qn[:, :, :n], kn, vn, "f16", scale=scale,
@@ -410,10 +574,11 @@ def bench_attention(args):
                 # the oracle multiplies every key (no causal skip)
                 done_flops += 14.0 * n * S * D
                 n *= 2
-        cpu = {"value": round(done_flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
-               "kind": "oracle",
+        cpu = {"value": round(done_flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+               "kind": "oracle", "threads": threads, "host_cpu_count": os.cpu_count(),
                "sample": f"forward + backward of queries 0..{n // 2 - 1} of head (0,0) against "
-                         f"all {S} keys, {spent:.1f} s, float64 numpy"}
+                         f"all {S} keys, {spent:.1f} s, float64 numpy, BLAS on {threads} "
+                         f"threads"}
     out = {
         "metric": "fused attention forward + backward TFLOP/s, 1 MI355X",
         "value": round(tflops, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -446,6 +611,12 @@ def main():
         bench_attention(args)
         return
 
+    # CPU baseline workers first, while this process has not touched the GPU.
+    pool, n_workers = None, 0
+    if args.cpu_seconds > 0:
+        n_workers = max(1, min(args.cpu_workers, os.cpu_count() or 1))
+        pool, n_workers = start_cpu_pool(n_workers)
+
     import torch
 
     from attention_softmax_amd import sms_backward, sms_forward, sms_path
@@ -470,6 +641,8 @@ def main():
         sms_forward(x, mask, y, w["scale"], w["causal"], stream=stream)
         sms_backward(y, dy, dx, w["scale"], w["causal"], stream=stream)
 
+    n_settle = settle(torch, step, args.settle_seconds, 4) if args.settle_seconds > 0 else 0
+    log(f"settle: {n_settle} steps in {args.settle_seconds} s")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -503,12 +676,13 @@ def main():
     for k in kern.values():
         k["frac_hbm_peak"] = round(k["GBps"] / HBM_PEAK_GBPS, 4)
     dom = "forward" if fwd_ms >= bwd_ms else "backward"
+    log(f"timed: {ms_step:.4f} ms/step, {value:.1f} GB/s; {kern}")
 
     traffic = load_traffic(args.traffic, args.workload, dom)
 
     copy = None
     if not args.no_copy:
-        # A plain device copy moving the forward's byte count: the achievable ceiling.
+        # A plain device copy moving the forward's byte count: a reference ceiling.
         n = fwd_b // 2
         src = torch.empty(n, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -530,8 +704,20 @@ def main():
         torch_ref = torch_reference(torch, w, stream, fwd_b, bwd_b, fwd_ms, bwd_ms)
 
     cpu = None
-    if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, y, dy, step_b, rows, args.cpu_seconds)
+    if pool is not None:
+        cpu = cpu_baseline(pool, n_workers, w, y, dy, fwd_b, bwd_b, args.cpu_seconds)
+        pool["pool"].shutdown()
+        log(f"cpu baseline: {cpu}")
+
+    del x, mask, dy, y, dx, w
+    torch.cuda.empty_cache()
+    others = {}
+    for o in [int(t) for t in args.others.split(",") if t.strip()]:
+        if o == args.workload:
+            continue
+        others[str(o)] = time_workload(torch, o, dev, stream, args.other_launches,
+                                       min(1.0, args.settle_seconds))
+        log(f"workload {o}: {others[str(o)]}")
 
     out = {
         "metric": "fused masked-softmax GB/s and % of HBM peak, fwd+bwd, 1 MI355X",
@@ -544,14 +730,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"f32": "f32", "f16": "f16", "bf16": "bf16"}[w["dtype"]],
+        "dtype": cfg["dtype"],
         "data": "synthetic",
         # The step times both passes on every workload: the name states that
         # instead of the passes the workload's own description lists.
         "config": {"workload": cfg["name"].rsplit(", ", 1)[0] + ", forward+backward step",
-                   "shape": [B, H, Sq, Sk], "mask": w["mode"],
-                   "causal": w["causal"], "scale": w["scale"], "pass": "forward+backward",
+                   "shape": [B, H, Sq, Sk], "mask": cfg["mask"],
+                   "causal": cfg["causal"], "scale": cfg["scale"], "pass": "forward+backward",
                    "dy": "N(0,1)"},
+        "settle": {"seconds": args.settle_seconds, "steps": n_settle,
+                   "what": "untimed steps before the warm-up, for the clocks to leave idle"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "rows_per_s": round(rows / (ms_step * 1e-3), 1),
         "step_bytes": step_b,
@@ -559,6 +747,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["GBps"],
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": kern[dom]["frac_hbm_peak"], "traffic": traffic},
+        "other_workloads": others,
         "copy_reference": copy,
         "torch_reference": torch_ref,
         "cpu_baseline": cpu,
