@@ -29,7 +29,9 @@ from .ops import (  # noqa: F401
     sms_attention_workspace_bytes,
     sms_backward,
     sms_forward,
+    sms_forward_noalloc,
     sms_max_sk,
+    sms_noalloc_scratch_bytes,
     sms_path,
     sms_workspace_bytes,
 )

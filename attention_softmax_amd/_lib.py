@@ -25,10 +25,11 @@ MASK_MODES = {"none": 0, "sq_sk": 1, "b_sq_sk": 2, "b_1_sk": 3, "full": 4, "key_
 MASK_BOOL = 0x10
 CAUSAL_CODES = {"none": 0, "top_left": 1, "bottom_right": 2}
 EXPORTS = ("sms_forward", "sms_backward", "sms_forward_ws", "sms_backward_ws",
+           "sms_forward_noalloc", "sms_noalloc_scratch_bytes",
            "sms_workspace_bytes", "sms_attention_forward", "sms_attention_backward",
            "sms_attention_workspace_bytes", "sms_max_sk", "sms_path",
            "sms_status_str", "sms_abi_version")
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 _lock = threading.Lock()
 _lib = None
@@ -57,6 +58,11 @@ def _declare(L):
     L.sms_backward_ws.argtypes = [vp, strides, vp, strides, vp, strides, i32, i64, i64, i64, i64,
                                   f32, i32, vp, i64, vp]
     L.sms_backward_ws.restype = i32
+    L.sms_forward_noalloc.argtypes = [vp, strides, vp, i32, vp, strides, i32, i64, i64, i64, i64,
+                                      f32, i32, vp]
+    L.sms_forward_noalloc.restype = i32
+    L.sms_noalloc_scratch_bytes.argtypes = []
+    L.sms_noalloc_scratch_bytes.restype = i64
     L.sms_attention_forward.argtypes = [vp, strides, vp, strides, vp, strides, vp, i32, vp,
                                         strides, vp, i32, i64, i64, i64, i64, i64, i64, f32, i32,
                                         vp]

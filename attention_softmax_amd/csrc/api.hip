@@ -12,6 +12,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <mutex>
 #include <utility>
 
 #include "kernels.hpp"
@@ -278,6 +279,33 @@ hipError_t launch(sms_dtype dtype, const FwdParams* fp, const BwdParams* bp, con
   }
 }
 
+// Scratch for sms_forward_noalloc: the split forward's per-(row, chunk)
+// partials live in this file-scope device array instead of a caller
+// workspace. One copy per GPU, held until the process ends. The largest split
+// the plan chooses by itself takes rows * chunks <= 2048 + 255 pairs of 8 bytes
+// (18,424 bytes); 64 KiB leaves room for small forced splits.
+constexpr int64_t kScratchBytes = 64 * 1024;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`. Host code never
+// passes the array's own name (a host-side stand-in) to a kernel or a copy.
+sms_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SMS_ERR_HIP;
+  std::lock_guard<std::mutex> guard(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SMS_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SMS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -329,6 +357,23 @@ sms_status sms_forward(const void* x, const int64_t x_strides[4], const void* ma
                        void* stream) {
   return sms_forward_ws(x, x_strides, mask, mask_mode, y, y_strides, dtype, B, H, Sq, Sk, scale,
                         is_causal, nullptr, 0, stream);
+}
+
+int64_t sms_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+sms_status sms_forward_noalloc(const void* x, const int64_t x_strides[4], const void* mask,
+                               int mask_mode, void* y, const int64_t y_strides[4],
+                               sms_dtype dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk,
+                               float scale, int is_causal, void* stream) {
+  // The same validation and kernels as sms_forward_ws, with this device's
+  // scratch as the workspace: a split that needs more than kScratchBytes is
+  // SMS_ERR_WORKSPACE there, before anything is launched. The split kernels
+  // write every partial they later read, so nothing needs clearing.
+  void* ws = nullptr;
+  const sms_status st = scratch_of_current_device(&ws);
+  if (st != SMS_OK) return st;
+  return sms_forward_ws(x, x_strides, mask, mask_mode, y, y_strides, dtype, B, H, Sq, Sk, scale,
+                        is_causal, ws, kScratchBytes, stream);
 }
 
 sms_status sms_forward_ws(const void* x, const int64_t x_strides[4], const void* mask,

@@ -134,19 +134,8 @@ def _workspace(dtype, shape, backward, device, stream, workspace):
     return ws, ws.data_ptr(), need
 
 
-def sms_forward(x, mask, y, scale=1.0, is_causal=False, stream=None, workspace=None):
-    """y <- softmax(x*scale + mask) over the last axis (C ABI sms_forward_ws).
-
-    x, y: 4-D GPU tensors of one shape and dtype (float32/float16/bfloat16), key
-    axis contiguous; y may be x itself (in place). mask: None; an additive mask
-    of x's dtype; a boolean mask (torch.bool or uint8, nonzero = key excluded);
-    both contiguous, in one of the shapes ``mask_mode_of`` accepts; or int32 key
-    lengths of shape [B]. is_causal: see ``causal_code``. Enqueued on ``stream``
-    (default: the current stream); returns y. Few long rows are split across
-    workgroups through a workspace: ``workspace`` (a GPU tensor of at least
-    ``sms_workspace_bytes`` bytes) or, by default, one taken from torch's
-    allocator on the launch stream.
-    """
+def _forward_args(x, mask, y):
+    """Checks of a forward call's tensors; (dtype code, mask pointer, C mask mode)."""
     _require_gpu(x, "x")
     _require_gpu(y, "y")
     _require_4d_rows(x, "x")
@@ -171,6 +160,23 @@ def sms_forward(x, mask, y, scale=1.0, is_causal=False, stream=None, workspace=N
         if not mask.is_contiguous():
             raise ValueError("mask must be contiguous in its own shape")
         mptr = mask.data_ptr()
+    return code, mptr, mode_code
+
+
+def sms_forward(x, mask, y, scale=1.0, is_causal=False, stream=None, workspace=None):
+    """y <- softmax(x*scale + mask) over the last axis (C ABI sms_forward_ws).
+
+    x, y: 4-D GPU tensors of one shape and dtype (float32/float16/bfloat16), key
+    axis contiguous; y may be x itself (in place). mask: None; an additive mask
+    of x's dtype; a boolean mask (torch.bool or uint8, nonzero = key excluded);
+    both contiguous, in one of the shapes ``mask_mode_of`` accepts; or int32 key
+    lengths of shape [B]. is_causal: see ``causal_code``. Enqueued on ``stream``
+    (default: the current stream); returns y. Few long rows are split across
+    workgroups through a workspace: ``workspace`` (a GPU tensor of at least
+    ``sms_workspace_bytes`` bytes) or, by default, one taken from torch's
+    allocator on the launch stream.
+    """
+    code, mptr, mode_code = _forward_args(x, mask, y)
     B, H, Sq, Sk = x.shape
     L = _lib.lib()
     with torch.cuda.device(x.device):
@@ -182,6 +188,28 @@ def sms_forward(x, mask, y, scale=1.0, is_causal=False, stream=None, workspace=N
         del keep  # torch reuses the block only for later work on this stream, after the launch
     _lib.check("sms_forward", st)
     return y
+
+
+def sms_forward_noalloc(x, mask, y, scale=1.0, is_causal=False, stream=None):
+    """sms_forward that allocates nothing (C ABI sms_forward_noalloc): a split
+    of few long rows keeps its partials in the library's per-GPU scratch
+    instead of a workspace. Arguments as for ``sms_forward``; calls that may
+    overlap on one GPU share that scratch and must be ordered by the caller."""
+    code, mptr, mode_code = _forward_args(x, mask, y)
+    B, H, Sq, Sk = x.shape
+    L = _lib.lib()
+    with torch.cuda.device(x.device):
+        s = _stream_of(x.device, stream)
+        st = L.sms_forward_noalloc(x.data_ptr(), _strides(x), mptr, mode_code, y.data_ptr(),
+                                   _strides(y), code, B, H, Sq, Sk, float(scale),
+                                   causal_code(is_causal), s.cuda_stream)
+    _lib.check("sms_forward_noalloc", st)
+    return y
+
+
+def sms_noalloc_scratch_bytes():
+    """Bytes of the per-GPU scratch ``sms_forward_noalloc`` uses."""
+    return int(_lib.lib().sms_noalloc_scratch_bytes())
 
 
 def sms_backward(y, dy, dx, scale=1.0, is_causal=False, stream=None, workspace=None):

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SMS_ABI_VERSION 5
+#define SMS_ABI_VERSION 6
 
 typedef enum {
   SMS_OK = 0,
@@ -213,6 +213,31 @@ sms_status sms_backward_ws(const void* y, const int64_t y_strides[4],
                            sms_dtype dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk,
                            float scale, int is_causal, void* workspace, int64_t workspace_bytes,
                            void* stream);
+
+/*
+ * sms_forward_noalloc -- sms_forward_ws for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation. It takes no workspace: a split forward keeps its
+ * per-(row, chunk) partials in a scratch array the library holds in device
+ * memory, one copy per GPU, until the process ends; the call itself allocates
+ * nothing (no hipMalloc, no hipFree). Arguments, results and errors are those
+ * of sms_forward_ws given that scratch as its workspace: a call whose split
+ * needs more than sms_noalloc_scratch_bytes() bytes (possible only when
+ * SMS_FORCE_SPLIT forces a large split) returns SMS_ERR_WORKSPACE and launches
+ * nothing. The scratch of the device current at the call is used, so
+ * `stream` must belong to that device. Every call on one GPU shares its
+ * scratch: calls that may overlap on one GPU (different streams, different
+ * host threads) race on it and must be ordered by the caller. Its contents on
+ * entry do not matter.
+ */
+sms_status sms_forward_noalloc(const void* x, const int64_t x_strides[4],
+                               const void* mask, int mask_mode,
+                               void* y, const int64_t y_strides[4],
+                               sms_dtype dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk,
+                               float scale, int is_causal, void* stream);
+
+/* Bytes of the per-GPU scratch sms_forward_noalloc uses (65536). */
+int64_t sms_noalloc_scratch_bytes(void);
 
 /*
  * sms_attention_forward -- fused attention forward on the matrix cores,

@@ -43,6 +43,13 @@ def test_every_declared_symbol_is_exported(L):
         assert hasattr(L, n), n
 
 
+def test_noalloc_scratch_size(L):
+    # a host-only query: the per-GPU scratch of sms_forward_noalloc holds the
+    # largest automatic split (2048 + 255 (row, chunk) pairs of 8 bytes)
+    assert L.sms_noalloc_scratch_bytes() == 65536
+    assert L.sms_noalloc_scratch_bytes() >= (2048 + 255) * 8
+
+
 def test_abi_version_and_status_text(L):
     assert L.sms_abi_version() == _lib.ABI_VERSION
     for code, name in _lib.STATUS_NAMES.items():
