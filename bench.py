@@ -147,9 +147,15 @@ def _kernel_role(name):
 def ingest(args):
     """Counters of one bench run -> HBM bytes per launch of each kernel.
 
-    FETCH_SIZE and WRITE_SIZE (KiB per dispatch, from two --pmc runs) are scaled
-    by what they read for the plain copy kernel of known size in the same run
-    (copy_reference moves n bytes each way).
+    Reads rocprofv3 output under DIR: kt/ (kernel trace and stats), and one
+    --pmc pass per subdirectory: dram/ (TCC_EA0_RDREQ_DRAM_32B_sum and
+    TCC_EA0_WRREQ_WRITE_DRAM_32B_sum: requests from L2 to the memory
+    controller in 32-byte units, a 64-byte request counted twice and a
+    128-byte one four times), and, as cross-checks, fetch/ (FETCH_SIZE, KiB),
+    write/ (WRITE_SIZE, KiB) and rdsize/ (TCC_EA0_RDREQ_{32B,64B,128B}_sum).
+    The traffic of a launch is 32 * (RDREQ_DRAM_32B + WRREQ_WRITE_DRAM_32B); the
+    plain copy kernel of known size in the same run shows what each counter
+    reads for known bytes.
     """
     d = args.ingest
     stats = glob.glob(os.path.join(d, "kt", "*kernel_stats.csv"))
@@ -175,48 +181,70 @@ def ingest(args):
             last = [dt for _, dt in v[-run["steps"]:]]
             timed[role] = sum(last) / len(last) / 1e3
 
-    def counter(sub):
+    def counter(sub, name, unit):
+        """Median per dispatch of counter `name` (times `unit` bytes) by kernel role."""
         vals = {}
         for f in glob.glob(os.path.join(d, sub, "*counter_collection.csv")):
             for row in csv.DictReader(open(f)):
+                if row["Counter_Name"] != name:
+                    continue
                 role = _kernel_role(row["Kernel_Name"])
                 if role:
-                    vals.setdefault(role, []).append(float(row["Counter_Value"]) * 1024.0)
+                    vals.setdefault(role, []).append(float(row["Counter_Value"]) * unit)
         return {k: statistics.median(v) for k, v in vals.items()}
 
-    fetch, write = counter("fetch"), counter("write")
+    rd = counter("dram", "TCC_EA0_RDREQ_DRAM_32B_sum", 32.0)
+    wr = counter("dram", "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum", 32.0)
+    fetch = counter("fetch", "FETCH_SIZE", 1024.0)
+    write = counter("write", "WRITE_SIZE", 1024.0)
+    r32 = counter("rdsize", "TCC_EA0_RDREQ_32B_sum", 32.0)
+    r64 = counter("rdsize", "TCC_EA0_RDREQ_64B_sum", 64.0)
+    r128 = counter("rdsize", "TCC_EA0_RDREQ_128B_sum", 128.0)
+    sized = {k: r32.get(k, 0.0) + r64.get(k, 0.0) + r128.get(k, 0.0) for k in r32}
     copy_bytes = run["copy_reference"]["bytes"] // 2 if run else None
-    fscale = copy_bytes / fetch["copy"] if copy_bytes and fetch.get("copy") else None
-    wscale = copy_bytes / write["copy"] if copy_bytes and write.get("copy") else None
     wl = run["config"]["workload"] if run else "?"
     key_wl = args.workload
     table = json.load(open(args.traffic)) if os.path.exists(args.traffic) else {}
     table.setdefault("workloads", {})
     sha = csrc_sha()
-    lines = [f"workload {key_wl}: {wl}",
-             f"copy kernel {COPY_KERNEL}: {copy_bytes} B each way; FETCH_SIZE scale "
-             f"{fscale:.4f}, WRITE_SIZE scale {wscale:.4f}" if fscale and wscale else "no copy",
+
+    def ratio(v, role="copy"):
+        return v.get(role, 0.0) / copy_bytes if copy_bytes and v.get(role) else float("nan")
+
+    lines = [f"workload {key_wl}: {wl}", "",
+             f"Plain copy kernel `{COPY_KERNEL}`, {copy_bytes} B read and {copy_bytes} B "
+             "written per launch; what each counter reads for it, over the true bytes:", "",
+             "| counter | read | write |", "|---|---|---|",
+             f"| TCC_EA0_RDREQ_DRAM_32B x 32 / TCC_EA0_WRREQ_WRITE_DRAM_32B x 32 | "
+             f"{ratio(rd):.4f} | {ratio(wr):.4f} |",
+             f"| TCC_EA0_RDREQ_{{32B,64B,128B}} x size | {ratio(sized):.4f} | - |",
+             f"| FETCH_SIZE / WRITE_SIZE (KiB x 1024) | {ratio(fetch):.4f} | {ratio(write):.4f} |",
              "", "| kernel | calls | avg us, all calls (rocprofv3) | avg us, timed calls (rocprofv3) "
-             "| avg us (HIP events) | algorithmic B | FETCH B (scaled) | WRITE B (scaled) | "
-             "traffic / algorithmic |", "|---|---|---|---|---|---|---|---|---|"]
+             "| avg us (HIP events) | algorithmic B | DRAM read B | DRAM write B | "
+             "traffic / algorithmic | RDREQ by size B | FETCH_SIZE B | WRITE_SIZE B |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for role in ("forward", "backward"):
         if role not in avg:
             continue
         name, calls, us = avg[role]
-        f_b = fetch.get(role, 0.0) * (fscale or 1.0)
-        w_b = write.get(role, 0.0) * (wscale or 1.0)
+        r_b, w_b = rd.get(role, 0.0), wr.get(role, 0.0)
         alg = run["kernels"][role]["bytes"] if run else None
         ev = run["kernels"][role]["avg_us"] if run else None
         t_us = timed.get(role)
         table["workloads"][f"{key_wl}_{role}"] = {
-            "kernel": name, "fetch_bytes": round(f_b), "write_bytes": round(w_b),
-            "traffic": round(f_b + w_b), "algorithmic_bytes": alg, "rocprof_avg_us": round(us, 2),
+            "kernel": name, "dram_read_bytes": round(r_b), "dram_write_bytes": round(w_b),
+            "traffic": round(r_b + w_b), "algorithmic_bytes": alg,
+            "rocprof_avg_us": round(us, 2),
             "rocprof_timed_avg_us": round(t_us, 2) if t_us else None,
-            "fetch_scale": fscale, "write_scale": wscale, "csrc_sha": sha}
-        ratio = (f_b + w_b) / alg if alg else float("nan")
+            "fetch_size_bytes": round(fetch.get(role, 0.0)),
+            "write_size_bytes": round(write.get(role, 0.0)),
+            "rdreq_sized_bytes": round(sized.get(role, 0.0)),
+            "copy_read_ratio": ratio(rd), "copy_write_ratio": ratio(wr), "csrc_sha": sha}
+        q = (r_b + w_b) / alg if alg else float("nan")
         t_txt = f"{t_us:.2f}" if t_us else "-"
-        lines.append(f"| `{name}` | {calls} | {us:.2f} | {t_txt} | {ev} | {alg} | {f_b:.0f} | "
-                     f"{w_b:.0f} | {ratio:.4f} |")
+        lines.append(f"| `{name}` | {calls} | {us:.2f} | {t_txt} | {ev} | {alg} | {r_b:.0f} | "
+                     f"{w_b:.0f} | {q:.4f} | {sized.get(role, 0.0):.0f} | "
+                     f"{fetch.get(role, 0.0):.0f} | {write.get(role, 0.0):.0f} |")
     os.makedirs(os.path.dirname(args.traffic), exist_ok=True)
     with open(args.traffic, "w") as fh:
         json.dump(table, fh, indent=1, sort_keys=True)
