@@ -197,7 +197,13 @@ attn_fwd_kernel(AttnParams p) {
   // This lane's V^T operand rows c, c + 32, ... (tcol's lane part included).
   const uint16_t* vlane = &vt[c * VP + tcol_lane(c, g)];
 
-  for (int kt = 0; kt < kend; kt += BK) {
+  // One key tile. FULL tiles have every score visible to every query of the
+  // workgroup (see below); the loop over them is compiled apart from the loop
+  // over the other tiles, so that neither carries the other's branches (with
+  // both in one body the compiler copied the 32 score registers between the
+  // products and the softmax of every tile).
+  auto tile = [&](const int kt, auto full_c) {
+    constexpr bool FULL = decltype(full_c)::value;
     __syncthreads();  // the previous tile's LDS reads are done
     stage();
     __syncthreads();
@@ -252,10 +258,9 @@ attn_fwd_kernel(AttnParams p) {
     // maximum of the raw scores (scaling is monotonic, so the scaled maximum
     // is the same rounded value) and folds the scale into the exponential's
     // argument below.
-    const bool inb = kt + BK <= klen && (!p.causal || kt + BK <= q0 + off + 1);
-    const bool full = fast_ok && inb;
+    const bool inb = FULL || (kt + BK <= klen && (!p.causal || kt + BK <= q0 + off + 1));
     float mloc = kNegInfA;
-    if (full) {
+    if constexpr (FULL) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -330,7 +335,7 @@ attn_fwd_kernel(AttnParams p) {
     }
     const float m_use = (m_i == kNegInfA) ? 0.0f : m_i;  // nothing visible yet
     float psum = 0.0f;
-    if (full) {
+    if constexpr (FULL) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -379,7 +384,18 @@ attn_fwd_kernel(AttnParams p) {
         oacc[db] = mfma_32x32x16<BF16>(u32x4{a0.x, a0.y, a1.x, a1.y}, pb[s], oacc[db]);
       }
     if constexpr (MV == 0) pin_reads_ahead<4 * (D / 32), 4, 2>();  // V^T reads, as above
+  };
+  // Tile kt is fully visible when kt + BK <= lim: the tiles before the last
+  // multiple of BK at or below lim, none without the fast path's conditions.
+  int kfull = 0;
+  if (fast_ok) {
+    int lim = klen;
+    if (p.causal) lim = min(lim, q0 + off + 1);
+    kfull = min(max(lim, 0) / BK * BK, kend);
   }
+  int kt = 0;
+  for (; kt < kfull; kt += BK) tile(kt, BoolC<true>{});
+  for (; kt < kend; kt += BK) tile(kt, BoolC<false>{});
 
   const float L = other_half_sum(l_i);  // both halves of the query's keys
   if (!qvalid) return;

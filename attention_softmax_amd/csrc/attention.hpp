@@ -73,6 +73,12 @@ struct AttnBwdParams {
 constexpr int kAttnBwdBk = 128;
 
 // Queries per workgroup (four wavefronts of 32 queries) and keys per tile.
+// A compile-time bool carried by a value (for generic lambdas).
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
 constexpr int kAttnBq = 128;
 constexpr int kAttnBk = 64;
 
