@@ -9,7 +9,9 @@
 // maximum grows.
 //
 // Workgroup: 4 wavefronts x 32 queries = 128 queries of one (batch, head).
-// Keys arrive in tiles of 64 through LDS (K row-major, V transposed). Per tile
+// Keys arrive in tiles of 64 through LDS: without a per-score mask straight
+// from global memory into double-buffered tiles (attn_fwd_dma_kernel), with
+// one through registers (attn_fwd_kernel, V stored transposed). Per tile
 // a wavefront computes S^T = K Q^T (keys x queries) with
 // v_mfma_f32_32x32x16_{f16,bf16}, so each lane holds 16 keys of one query:
 // the row maximum and sum are mostly in-lane plus one swap with the lane 32
@@ -30,7 +32,9 @@ namespace {
 
 using namespace attn;
 
-// MV (additive / boolean masks): 2 when every mask row of the workgroup's
+// Forward with a per-score mask (additive or boolean). K and V tiles pass
+// through registers into LDS (K row-major, V transposed), single-buffered.
+// MV: 2 when every mask row of the workgroup's
 // queries starts on a 16-byte line, so that a tile's mask values (128 queries
 // x 64 keys) come with its K / V fetch as whole-line 16-byte loads and are
 // staged in LDS; 1 when mask rows start on 4 elements (runs of 4 keys per
@@ -39,6 +43,7 @@ using namespace attn;
 template <bool BF16, int D, int KIND, int MV>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(AttnParams p) {
+  static_assert(KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL, "a per-score mask");
   constexpr int BK = kAttnBk;
   constexpr int KP = D + 8;   // K tile row pitch, elements (conflict-free 16-byte reads)
   constexpr int VP = BK + 4;  // V^T tile row pitch, elements (34 dwords: 8-byte reads spread)
@@ -86,18 +91,11 @@ attn_fwd_kernel(AttnParams p) {
 
   // Keys the workgroup visits ([0, kend)) and this lane's query sees ([0, kq)).
   const int off = p.causal == 2 ? Sk - Sq : 0;
-  int klen = Sk;
-  if constexpr (KIND == ATTN_MASK_LEN)
-    klen = max(min(reinterpret_cast<const int32_t*>(p.mask)[b], Sk), 0);
-  int kend = klen;
+  int kend = Sk;
   if (p.causal) kend = min(kend, max(q0 + kAttnBq + off, 0));
-  int kq = klen;
+  int kq = Sk;
   if (p.causal) kq = min(kq, max(qi + off + 1, 0));
   const bool qvalid = qi < Sq;
-  // Tiles may skip the per-score tests (see the loop) without a per-score
-  // mask and with a positive scale. Queries past Sq need no test: their rows
-  // are finite (Q = 0) and never stored.
-  const bool fast_ok = (KIND == ATTN_MASK_NONE || KIND == ATTN_MASK_LEN) && p.scale_log2 > 0.0f;
   const int64_t mrow = (int64_t)b * p.sm_b + (int64_t)h * p.sm_h + (int64_t)qi * p.sm_q;
   // The same for a query clamped into the mask (unconditional vector loads).
   const int64_t mrow_c =
@@ -197,13 +195,8 @@ attn_fwd_kernel(AttnParams p) {
   // This lane's V^T operand rows c, c + 32, ... (tcol's lane part included).
   const uint16_t* vlane = &vt[c * VP + tcol_lane(c, g)];
 
-  // One key tile. FULL tiles have every score visible to every query of the
-  // workgroup (see below); the loop over them is compiled apart from the loop
-  // over the other tiles, so that neither carries the other's branches (with
-  // both in one body the compiler copied the 32 score registers between the
-  // products and the softmax of every tile).
-  auto tile = [&](const int kt, auto full_c) {
-    constexpr bool FULL = decltype(full_c)::value;
+  // One key tile.
+  auto tile = [&](const int kt) {
     __syncthreads();  // the previous tile's LDS reads are done
     stage();
     __syncthreads();
@@ -251,22 +244,12 @@ attn_fwd_kernel(AttnParams p) {
     // (measured without per-score mask runs, whose loads share the region).
     if constexpr (MV == 0) pin_reads_ahead<2 * (D / 16), 10, 1>();
 
-    // Scores in the log2 domain, the mask and the key bounds. A tile whose
-    // every score is visible to every query of the workgroup (keys in range
-    // and, with a causal rule, before the first query's bound; no per-score
-    // mask) skips the exclusion tests, and with a positive scale it takes the
-    // maximum of the raw scores (scaling is monotonic, so the scaled maximum
-    // is the same rounded value) and folds the scale into the exponential's
-    // argument below.
-    const bool inb = FULL || (kt + BK <= klen && (!p.causal || kt + BK <= q0 + off + 1));
+    // Scores in the log2 domain, the mask and the key bounds (tested only on
+    // tiles with a key past Sk or, with a causal rule, past the first query's
+    // bound).
+    const bool inb = kt + BK <= Sk && (!p.causal || kt + BK <= q0 + off + 1);
     float mloc = kNegInfA;
-    if constexpr (FULL) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[kb][r]);
-      mloc *= p.scale_log2;
-    } else if ((KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL) && inb) {
+    if (inb) {
       // Every key in bounds for every query: the mask alone.
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -335,25 +318,14 @@ attn_fwd_kernel(AttnParams p) {
     }
     const float m_use = (m_i == kNegInfA) ? 0.0f : m_i;  // nothing visible yet
     float psum = 0.0f;
-    if constexpr (FULL) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.scale_log2, -m_use));
-          sacc[kb][r] = pv;
-          psum += pv;
-        }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(sacc[kb][r] - m_use);
-          sacc[kb][r] = pv;
-          psum += pv;
-        }
-    }
+      for (int r = 0; r < 16; ++r) {
+        const float pv = __builtin_amdgcn_exp2f(sacc[kb][r] - m_use);
+        sacc[kb][r] = pv;
+        psum += pv;
+      }
     l_i += psum;
     const bool rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
     // P as the B operand of O^T += V^T P^T: k-step s takes registers
@@ -385,21 +357,288 @@ attn_fwd_kernel(AttnParams p) {
       }
     if constexpr (MV == 0) pin_reads_ahead<4 * (D / 32), 4, 2>();  // V^T reads, as above
   };
-  // Tile kt is fully visible when kt + BK <= lim: the tiles before the last
-  // multiple of BK at or below lim, none without the fast path's conditions.
+  for (int kt = 0; kt < kend; kt += BK) tile(kt);
+
+  const float L = other_half_sum(l_i);  // both halves of the query's keys
+  if (!qvalid) return;
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;  // no visible key: zeros
+  char* orow = p.o + ((int64_t)b * p.so_b + (int64_t)h * p.so_h + (int64_t)qi * p.so_s) * 2;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const u32x2 w{pack2<BF16>(oacc[db][4 * rg] * inv, oacc[db][4 * rg + 1] * inv),
+                    pack2<BF16>(oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv)};
+      *reinterpret_cast<u32x2*>(orow + (db * 32 + 8 * rg + 4 * g) * 2) = w;
+    }
+  if (p.lse && g == 0)
+    p.lse[((int64_t)b * p.H + h) * Sq + qi] = L > 0.0f ? (m_i + log2f(L)) * kLn2A : kNegInfA;
+}
+
+// Forward without a per-score mask (none, or key lengths), fed by direct
+// loads from global memory into LDS. The K and V tiles (64 keys x D values,
+// unpadded rows) are double-buffered: each tile starts with one barrier, after
+// which the loads of the next tile go out into the other buffer and stay in
+// flight during this tile's products; the data never passes through
+// registers. Each load instruction fills 1 KB of LDS contiguously (lane n at
+// n * 16 bytes), so the conflict-free read patterns come from the global side:
+// the lane that fills chunk position h of tile row r loads the row's logical
+// chunk h ^ swz(r) (an XOR swizzle, its own inverse).
+//
+// K is read as in attn_fwd_kernel (16 bytes per lane: 16 lanes take one
+// logical chunk of 16 consecutive rows). V stays row-major (keys x dims) and
+// the A operand of O^T += V^T P^T is assembled by transposing LDS reads
+// (ds_read_b64_tr_b16, probed on MI355X: within each 16-lane group, lane 4a + e
+// receives element e of the 8-byte rows addressed by lanes a, a + 4, a + 8,
+// a + 12). A lane group addressing 4 keys x 16 dims (lane j: key j / 4, dims
+// 4 (j % 4) .. + 3) so hands every lane its own dim's 4 consecutive keys.
+template <int D>
+__host__ __device__ constexpr int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__host__ __device__ constexpr int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define SMS_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
+
+template <bool BF16, int D, int KIND>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_fwd_dma_kernel(AttnParams p) {
+  static_assert(KIND == ATTN_MASK_NONE || KIND == ATTN_MASK_LEN, "no per-score mask");
+  constexpr int BK = kAttnBk;
+  constexpr int CH = D / 8;           // 16-byte chunks per row
+  constexpr int TB = BK * D * 2;      // bytes per tile
+  constexpr int NI = TB / 1024 / 4;   // load instructions per wavefront per tile, each of K and V
+  __shared__ __align__(1024) uint8_t ks0[TB];
+  __shared__ __align__(1024) uint8_t ks1[TB];
+  __shared__ __align__(1024) uint8_t vs0[TB];
+  __shared__ __align__(1024) uint8_t vs1[TB];
+
+  const int tid = (int)threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // Grid order as in attn_fwd_kernel.
+  const uint32_t N = gridDim.x, per = N / 8, HB = p.H * p.B;
+  const uint32_t ntq = N / HB;
+  uint32_t t = blockIdx.x, hb, qt;
+  if (p.causal) {
+    hb = t % HB;
+    qt = ntq - 1 - t / HB;
+  } else {
+    if (t < per * 8) t = (t % 8) * per + t / 8;
+    hb = t / ntq;
+    qt = t % ntq;
+  }
+  const uint32_t h = hb % p.H, b = hb / p.H;
+  const int q0 = (int)(qt * kAttnBq);
+  const int qi = q0 + wave * 32 + c;
+  const int Sq = (int)p.Sq, Sk = (int)p.Sk;
+  const uint32_t hk = h / p.group;
+  const char* qbase = p.q + ((int64_t)b * p.sq_b + (int64_t)h * p.sq_h) * 2;
+  const char* kbase = p.k + ((int64_t)b * p.sk_b + (int64_t)hk * p.sk_h) * 2;
+  const char* vbase = p.v + ((int64_t)b * p.sv_b + (int64_t)hk * p.sv_h) * 2;
+
+  const int off = p.causal == 2 ? Sk - Sq : 0;
+  int klen = Sk;
+  if constexpr (KIND == ATTN_MASK_LEN)
+    klen = max(min(reinterpret_cast<const int32_t*>(p.mask)[b], Sk), 0);
+  int kend = klen;
+  if (p.causal) kend = min(kend, max(q0 + kAttnBq + off, 0));
+  int kq = klen;
+  if (p.causal) kq = min(kq, max(qi + off + 1, 0));
+  const bool qvalid = qi < Sq;
+  const bool fast_ok = p.scale_log2 > 0.0f;
+
+  u32x4 qf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    qf[s] = u32x4{0, 0, 0, 0};
+    if (qvalid)
+      qf[s] = *reinterpret_cast<const u32x4*>(qbase + ((int64_t)qi * p.sq_s + s * 16 + 8 * g) * 2);
+  }
+
+  float m_i = kNegInfA, l_i = 0.0f;
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+
+  // Global byte offsets (within a tile) of this lane's chunks: instruction i
+  // of the wavefront fills chunk positions n = (wave * NI + i) * 64 + lane.
+  uint32_t kdo[NI], vdo[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int n = (wave * NI + i) * 64 + lane, r = n / CH, ph = n % CH;
+    kdo[i] = (uint32_t)(r * p.sk_s * 2 + (ph ^ kswz<D>(r)) * 16);
+    vdo[i] = (uint32_t)(r * p.sv_s * 2 + (ph ^ vswz<D>(r)) * 16);
+  }
+  // Rows past the last key read as zero (buffer range ends at the last key).
+  auto dma = [&](int kt, auto buf_c) {
+    constexpr int BUF = decltype(buf_c)::value;
+    uint8_t* kd = BUF ? ks1 : ks0;
+    uint8_t* vd = BUF ? vs1 : vs0;
+    const int rows = min(Sk - kt, BK);
+    const auto kr = rows_rsrc(kbase + (int64_t)kt * p.sk_s * 2, rows, p.sk_s * 2, D * 2);
+    const auto vr = rows_rsrc(vbase + (int64_t)kt * p.sv_s * 2, rows, p.sv_s * 2, D * 2);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, SMS_LDS(void, kd + (wave_u * NI + i) * 1024), 16,
+                                               (int)kdo[i], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, SMS_LDS(void, vd + (wave_u * NI + i) * 1024), 16,
+                                               (int)vdo[i], 0, 0, 0);
+  };
+  if (kend > 0) dma(0, BoolC<false>{});
+
+  // LDS byte offsets of this lane's operand reads. K: row c (+ 32 kb), logical
+  // chunk 2 s + g. V: key 4 g + (c % 16) / 4 (+ 16 s + 8 half), dims
+  // 32 db + 16 ((c / 16) % 2) + 4 (c % 4) .. + 3.
+  uint32_t kao[D / 16], vao[D / 32];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) kao[s] = (uint32_t)(c * D * 2 + (((2 * s + g) ^ kswz<D>(c)) * 16));
+  {
+    const int j = c & 15, vr = 4 * g + (j >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int col = 32 * db + 16 * ((c >> 4) & 1) + 4 * (j & 3);
+      vao[db] = (uint32_t)(vr * D * 2 + (((col >> 3) ^ vswz<D>(vr)) * 16) + (col & 7) * 2);
+    }
+  }
+
+  auto tile = [&](const int kt, auto full_c, auto buf_c) {
+    constexpr bool FULL = decltype(full_c)::value;
+    constexpr int BUF = decltype(buf_c)::value;
+    const uint8_t* kt_lds = BUF ? ks1 : ks0;
+    const uint8_t* vt_lds = BUF ? vs1 : vs0;
+    // This wavefront's loads of the tile have landed; after the barrier every
+    // wavefront's have, and every wavefront is done with the previous tile,
+    // whose buffers the next tile's loads overwrite.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kt + BK < kend) dma(kt + BK, BoolC<BUF == 0>{});
+
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kt_lds + kao[s] + kb * 32 * D * 2);
+        sacc[kb] = mfma_32x32x16<BF16>(a, qf[s], sacc[kb]);
+      }
+    pin_reads_ahead<2 * (D / 16), 10, 1>();
+
+    float mloc = kNegInfA;
+    if constexpr (FULL) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[kb][r]);
+      mloc *= p.scale_log2;
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          float t = sacc[kb][r] * p.scale_log2;
+          if (key >= kq || key >= Sk) t = kNegInfA;
+          sacc[kb][r] = t;
+          mloc = fmaxf(mloc, t);
+        }
+    }
+    mloc = other_half_max(mloc);
+    const bool grow = mloc > m_i + kLazy || (m_i == kNegInfA && mloc != kNegInfA);
+    float corr = 1.0f;
+    if (grow) {
+      corr = __builtin_amdgcn_exp2f(m_i - mloc);
+      m_i = mloc;
+      l_i *= corr;
+    }
+    const float m_use = (m_i == kNegInfA) ? 0.0f : m_i;
+    float psum = 0.0f;
+    if constexpr (FULL) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.scale_log2, -m_use));
+          sacc[kb][r] = pv;
+          psum += pv;
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = __builtin_amdgcn_exp2f(sacc[kb][r] - m_use);
+          sacc[kb][r] = pv;
+          psum += pv;
+        }
+    }
+    l_i += psum;
+    const bool rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
+    u32x4 pb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int kb = s >> 1, base = 8 * (s & 1);
+      pb[s] = u32x4{pack2<BF16>(sacc[kb][base + 0], sacc[kb][base + 1]),
+                    pack2<BF16>(sacc[kb][base + 2], sacc[kb][base + 3]),
+                    pack2<BF16>(sacc[kb][base + 4], sacc[kb][base + 5]),
+                    pack2<BF16>(sacc[kb][base + 6], sacc[kb][base + 7])};
+    }
+    if (rescale) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= corr;
+    }
+    // A operand of k-step s: keys 16 s + 4 g + 0..3 (elements 0-3) and
+    // 16 s + 8 + 4 g + 0..3 (elements 4-7) of the lane's dim.
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const uint8_t* va = vt_lds + vao[db] + 16 * s * D * 2;
+        const s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(SMS_LDS(s16x4, va));
+        const s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(SMS_LDS(s16x4, va + 8 * D * 2));
+        const u32x2 w0 = __builtin_bit_cast(u32x2, a0), w1 = __builtin_bit_cast(u32x2, a1);
+        oacc[db] = mfma_32x32x16<BF16>(u32x4{w0.x, w0.y, w1.x, w1.y}, pb[s], oacc[db]);
+      }
+    pin_reads_ahead<4 * (D / 32), 4, 2>();
+  };
   int kfull = 0;
   if (fast_ok) {
     int lim = klen;
     if (p.causal) lim = min(lim, q0 + off + 1);
     kfull = min(max(lim, 0) / BK * BK, kend);
   }
+  // Tiles go in pairs (buffer 0, then 1), so that each buffer is a separate
+  // LDS object throughout (which keeps the compiler from waiting for the next
+  // tile's loads before this tile's reads) and no branch picks between two
+  // copies of the tile; a fully visible tile left over from an odd count takes
+  // the general path.
+  kfull = kfull / (2 * BK) * (2 * BK);
   int kt = 0;
-  for (; kt < kfull; kt += BK) tile(kt, BoolC<true>{});
-  for (; kt < kend; kt += BK) tile(kt, BoolC<false>{});
+  for (; kt < kfull; kt += 2 * BK) {
+    tile(kt, BoolC<true>{}, BoolC<false>{});
+    tile(kt + BK, BoolC<true>{}, BoolC<true>{});
+  }
+  while (kt < kend) {
+    tile(kt, BoolC<false>{}, BoolC<false>{});
+    kt += BK;
+    if (kt >= kend) break;
+    tile(kt, BoolC<false>{}, BoolC<true>{});
+    kt += BK;
+  }
 
-  const float L = other_half_sum(l_i);  // both halves of the query's keys
+  const float L = other_half_sum(l_i);
   if (!qvalid) return;
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;  // no visible key: zeros
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   char* orow = p.o + ((int64_t)b * p.so_b + (int64_t)h * p.so_h + (int64_t)qi * p.so_s) * 2;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -418,7 +657,7 @@ hipError_t launch_kind(const AttnParams& p, hipStream_t st) {
   const dim3 grid(p.H * p.B * ((p.Sq + kAttnBq - 1) / kAttnBq)), block(256);
   const int mv = p.mask_tile ? 2 : p.mask_vec ? 1 : 0;
   switch (p.mask_kind) {
-    case ATTN_MASK_NONE: hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_NONE, 0>), grid, block, 0, st, p); break;
+    case ATTN_MASK_NONE: hipLaunchKernelGGL((attn_fwd_dma_kernel<BF16, D, ATTN_MASK_NONE>), grid, block, 0, st, p); break;
     case ATTN_MASK_ADD:
       if (mv == 2) hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_ADD, 2>), grid, block, 0, st, p);
       else if (mv == 1) hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_ADD, 1>), grid, block, 0, st, p);
@@ -429,7 +668,7 @@ hipError_t launch_kind(const AttnParams& p, hipStream_t st) {
       else if (mv == 1) hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_BOOL, 1>), grid, block, 0, st, p);
       else hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_BOOL, 0>), grid, block, 0, st, p);
       break;
-    case ATTN_MASK_LEN: hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_LEN, 0>), grid, block, 0, st, p); break;
+    case ATTN_MASK_LEN: hipLaunchKernelGGL((attn_fwd_dma_kernel<BF16, D, ATTN_MASK_LEN>), grid, block, 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
