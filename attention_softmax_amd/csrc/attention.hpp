@@ -210,6 +210,121 @@ constexpr bool tcol_split_holds() {
 }
 static_assert(tcol_split_holds(), "tcol must split into lane and compile-time parts");
 
+// Tiles loaded straight from global memory into LDS (buffer loads with the
+// LDS flag): rows of D 16-bit values in 16-byte chunks, no padding. A load
+// instruction fills 1 KB of LDS in lane order, so the conflict-free layout
+// comes from which chunk each lane fetches: chunk position h of row r holds
+// logical chunk h ^ dswz<D>(r). The swizzle suits both operand read
+// patterns: 16-byte row reads (a 16-lane phase reads one logical chunk of 16
+// consecutive rows, so dswz must be one-to-one on every aligned 16 rows, and
+// for D = 64, where two rows share a 256-byte bank line, on each parity class
+// of them) and transposing 8-byte reads (a 32-lane phase reads 4 consecutive
+// rows x 4 consecutive chunks, so bits 2-3 of dswz -- bit 2 for D = 64 --
+// must differ over every aligned 4 rows).
+template <int D>
+__host__ __device__ constexpr int dswz(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+// Byte offset of logical chunk ch of row r in such a tile.
+template <int D>
+__host__ __device__ constexpr int dtile_off(int r, int ch) {
+  return r * D * 2 + ((ch ^ dswz<D>(r)) * 16);
+}
+template <int D>
+constexpr bool dswz_conflict_free() {
+  constexpr int CH = D / 8;
+  for (int r0 = 0; r0 < 64; r0 += 16)  // row reads: 16 rows, one chunk
+    for (int ch = 0; ch < CH; ++ch) {
+      bool used[16] = {};
+      for (int r = r0; r < r0 + 16; ++r) {
+        const int grp = (dtile_off<D>(r, ch) / 16) % 16;  // 4-bank group of the 64 banks
+        if (used[grp]) return false;
+        used[grp] = true;
+      }
+    }
+  for (int r0 = 0; r0 < 64; r0 += 4)  // transposing reads: 4 rows x 4 chunks
+    for (int c0 = 0; c0 < CH; c0 += 4) {
+      bool used[16] = {};
+      for (int r = r0; r < r0 + 4; ++r)
+        for (int ch = c0; ch < c0 + 4; ++ch) {
+          const int grp = (dtile_off<D>(r, ch) / 16) % 16;
+          if (used[grp]) return false;
+          used[grp] = true;
+        }
+    }
+  return true;
+}
+static_assert(dswz_conflict_free<64>() && dswz_conflict_free<128>(), "dswz must spread both read patterns");
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define SMS_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
+
+// One transposing LDS read (ds_read_b64_tr_b16, probed on MI355X): within each
+// 16-lane group, lane 4a + e receives element e of the 8-byte rows addressed by
+// lanes a, a + 4, a + 8 and a + 12. A group addressing 4 rows x 16 columns
+// (lane j: row j / 4, columns 4 (j % 4) .. + 3) so hands each lane the 4 rows
+// of its own column.
+__device__ inline __attribute__((always_inline)) u32x2 lds_read_tr(const uint8_t* a) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(SMS_LDS(s16x4, a)));
+}
+
+// Loads of a tile of TR rows into LDS in the dswz layout: instruction i of
+// wavefront w fills the RPI rows (1 KB) from R = RPI (w + 4 i), lane n row
+// R + n / (D / 8), chunk position n % (D / 8). In that order the swizzle of a
+// lane's row depends on the lane and w only (dswz reads the row's low 4 bits,
+// which 4 RPI i never reaches), so one offset register per source serves every
+// instruction, the rows' offsets going in the scalar offset. Rows past the
+// buffer range read as zero.
+template <int D>
+__device__ inline __attribute__((always_inline)) uint32_t dma_lane_off(int lane, int w, int64_t pitch) {
+  constexpr int CH = D / 8, RPI = 64 / CH;
+  const int r = lane / CH;
+  return (uint32_t)(r * pitch + 16 * ((lane % CH) ^ dswz<D>(RPI * w + r)));
+}
+// The same loads issued from inline assembly, which the compiler does not
+// see as LDS writes: it then inserts no wait for them before LDS reads of the
+// other buffer (it cannot tell the buffers apart when one code path serves
+// both), and the caller waits for them itself (vmcnt) before its barrier. The
+// compiler keeps no value in m0 here (its only other users are the builtin
+// LDS loads, not used alongside). src: the four descriptor words.
+template <int D, int TR>
+__device__ inline __attribute__((always_inline)) void dma_tile_asm(u32x4 src, uint32_t voff, int64_t pitch,
+                                                                   int w, uint32_t dst) {
+  constexpr int CH = D / 8, RPI = 64 / CH, NI = TR / RPI / 4;
+  static_assert(NI * RPI * 4 == TR, "whole 1 KB loads, four wavefronts");
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int r0 = RPI * (w + 4 * i);
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(src), "s"((uint32_t)(r0 * pitch)), "s"(dst + (uint32_t)(r0 * D * 2))
+                 : "memory");
+  }
+}
+// Descriptor words of rows_rsrc.
+__device__ inline __attribute__((always_inline)) u32x4 rows_desc(const char* base, int rows, int64_t pitch,
+                                                                 int row_bytes) {
+  const uint32_t bytes = rows > 0 ? (uint32_t)((int64_t)(rows - 1) * pitch + row_bytes) : 0u;
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, (uint32_t)kRsrcWord3A};
+}
+// LDS byte address of a __shared__ object.
+__device__ inline __attribute__((always_inline)) uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+template <int D, int TR>
+__device__ inline __attribute__((always_inline)) void dma_tile(__amdgpu_buffer_rsrc_t src, uint32_t voff,
+                                                               int64_t pitch, int w, uint8_t* dst) {
+  constexpr int CH = D / 8, RPI = 64 / CH, NI = TR / RPI / 4;
+  static_assert(NI * RPI * 4 == TR, "whole 1 KB loads, four wavefronts");
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int r0 = RPI * (w + 4 * i);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, SMS_LDS(void, dst + r0 * D * 2), 16, (int)voff,
+                                             (int)(r0 * pitch), 0, 0);
+  }
+}
+
 // 16-bit element j (0..7) of an 8-element vector.
 __device__ inline __attribute__((always_inline)) uint32_t elem(const u32x4& v, int j) {
   return (v[j >> 1] >> ((j & 1) * 16)) & 0xffffu;

@@ -30,18 +30,23 @@ using namespace attn;
 
 // ---------------------------------------------------------------- 1. dQ
 
+// K and V tiles of 64 keys come straight from global memory into
+// double-buffered LDS (dswz layout): one barrier per tile, after which the
+// next tile's loads go out into the other buffer. K serves both the row reads
+// of S^T = K Q^T and the transposing reads that form the K^T operand of
+// dQ^T += K^T dS^T; V the row reads of dP^T = V dO^T.
 template <bool BF16, int D, int KIND, bool MV>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dq_kernel(AttnBwdParams p) {
   constexpr int BK = kAttnBk;
-  constexpr int KP = D + 8;   // row-major tile pitch, elements
-  constexpr int TP = BK + 4;  // transposed tile pitch, elements
-  __shared__ __align__(16) uint16_t ks[BK * KP];   // K, row-major: A of S^T = K Q^T
-  __shared__ __align__(16) uint16_t kts[D * TP];   // K^T: A of dQ^T += K^T dS^T
-  __shared__ __align__(16) uint16_t vs[BK * KP];   // V, row-major: A of dP^T = V dO^T
+  constexpr int TB = BK * D * 2;  // bytes per tile
+  // K tiles at 0 and TB, V tiles at 2 TB and 3 TB; bit TB of the offsets
+  // picks a tile's buffer and flips every tile.
+  __shared__ __align__(1024) uint8_t kv[4 * TB];
 
   const int tid = (int)threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   // Same workgroup order as the forward.
   const uint32_t N = gridDim.x, per = N / 8, HB = p.H * p.B;
   const uint32_t ntq = N / HB;
@@ -110,69 +115,47 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[db][r] = 0.0f;
 
-  // Tiles fetched one ahead: K as (4 keys x 8 dims) per thread, staged
-  // row-major and transposed; V as 16-byte chunks, staged row-major.
-  constexpr int KITEMS = (BK / 4) * (D / 8);
-  constexpr int KCH = D / 8;
-  constexpr int VC = BK * KCH / 256;
-  const int kdg = tid % (D / 8), kkg = tid / (D / 8);
-  const bool kthread = tid < KITEMS;
-  u32x4 kreg[4], vreg[VC];
-  // The fetch reads through buffer ranges re-based on each tile that end at
-  // the last key (rows past it read as zero), with fixed per-thread offsets
-  // and no per-load test or branch; threads past the K items (D = 64) load a
-  // copy of another thread's item, so that the wait for a tile's mask values
-  // does not cover the fetch.
-  uint32_t koff[4], voff[VC];
-  const int ktid = tid % KITEMS, kdgl = ktid % (D / 8), kkgl = ktid / (D / 8);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) koff[i] = (uint32_t)((4 * kkgl + i) * p.sk_s * 2 + kdgl * 16);
-#pragma unroll
-  for (int i = 0; i < VC; ++i) {
-    const int idx = tid + 256 * i, row = idx / KCH, ch = idx - row * KCH;
-    voff[i] = (uint32_t)(row * p.sv_s * 2 + ch * 16);
-  }
-  auto fetch = [&](int kt) {
+  // Tile loads (rows past the last key read as zero; a tile past it loads
+  // nothing but zeros).
+  const uint32_t kdo = dma_lane_off<D>(lane, wave_u, p.sk_s * 2);
+  const uint32_t vdo = dma_lane_off<D>(lane, wave_u, p.sv_s * 2);
+  const uint32_t kv_lds = lds_addr(kv);
+  auto dma = [&](int kt, int buf) {
     const int rows = min(Sk - kt, BK);
-    const auto kr = rows_rsrc(kbase + (int64_t)kt * p.sk_s * 2, rows, p.sk_s * 2, D * 2);
-    const auto vr = rows_rsrc(vbase + (int64_t)kt * p.sv_s * 2, rows, p.sv_s * 2, D * 2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) kreg[i] = rsrc_load(kr, koff[i]);
-#pragma unroll
-    for (int i = 0; i < VC; ++i) vreg[i] = rsrc_load(vr, voff[i]);
+    const u32x4 kr = rows_desc(kbase + (int64_t)kt * p.sk_s * 2, rows, p.sk_s * 2, D * 2);
+    const u32x4 vr = rows_desc(vbase + (int64_t)kt * p.sv_s * 2, rows, p.sv_s * 2, D * 2);
+    dma_tile_asm<D, BK>(kr, kdo, p.sk_s * 2, wave_u, kv_lds + buf * TB);
+    dma_tile_asm<D, BK>(vr, vdo, p.sv_s * 2, wave_u, kv_lds + (2 + buf) * TB);
   };
-  auto stage = [&]() {
-    if (kthread) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4*>(&ks[(4 * kkg + i) * KP + 8 * kdg]) = kreg[i];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const u32x2 w{pair(kreg[0], kreg[1], j), pair(kreg[2], kreg[3], j)};
-        *reinterpret_cast<u32x2*>(&kts[(8 * kdg + j) * TP + tcol(8 * kdg + j, kkg)]) = w;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VC; ++i) {
-      const int idx = tid + 256 * i, row = idx / KCH, ch = idx - row * KCH;
-      *reinterpret_cast<u32x4*>(&vs[row * KP + ch * 8]) = vreg[i];
-    }
-  };
-  if (kend > 0) fetch(0);
+  if (kend > 0) dma(0, 0);
 
-  // This lane's K^T operand rows c, c + 32, ... (tcol's lane part included).
-  const uint16_t* const klane = &kts[c * TP + tcol_lane(c, g)];
+  // LDS byte offsets of this lane's reads. Row reads: row c (+ 32 kb),
+  // logical chunk 2 s + g, at rao ^ 32 s (dswz reads the row's low 4 bits
+  // only; XOR-ing 2 s into the chunk index is XOR-ing 32 s into the offset).
+  // K^T operand (transposing reads): keys 8 hf + 4 g + (c % 16) / 4 (+ 16 s),
+  // dims 32 db + 16 ((c / 16) % 2) + 4 (c % 4) .. + 3, at
+  // (tao ^ 64 db ^ 32 hf) + 8 hf rows (dswz's bits 0-1 hold bits 2-3 of the
+  // key, which hf sets and s leaves).
+  uint32_t rao = (uint32_t)dtile_off<D>(c, g);
+  uint32_t tao =
+      (uint32_t)(dtile_off<D>(4 * g + ((c & 15) >> 2), 2 * ((c >> 4) & 1) + ((c >> 1) & 1)) + 8 * (c & 1));
+
   for (int kt = 0; kt < kend; kt += BK) {
+    const uint8_t* kl = kv;
+    const uint8_t* vl = kv + 2 * TB;
+    const uint32_t ra = rao, ta = tao;
+    // This wavefront's loads of the tile have landed; after the barrier every
+    // wavefront's have, and every wavefront is done with the previous tile,
+    // whose buffers the next loads overwrite.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    stage();
-    __syncthreads();
-    u32x2 mv[8];  // this tile's mask values, loaded before the prefetch
+    u32x2 mv[8];  // this tile's mask values, loaded before the next tile's loads
     if constexpr (MV) {
       load_mask_runs<KIND>(p.mask, mrow_c, kt, g, Sk, mv);
-      __builtin_amdgcn_sched_barrier(0);  // keep them ahead of the prefetch
+      __builtin_amdgcn_sched_barrier(0);  // keep them ahead of the loads
     }
-    if (MV || kt + BK < kend) fetch(kt + BK);
-    if constexpr (MV) __builtin_amdgcn_sched_barrier(0);  // keep the fetch ahead of the products
+    if (MV || kt + BK < kend) dma(kt + BK, ((kt / BK) & 1) ^ 1);
+    if constexpr (MV) __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the products
 
     // dS^T = P (dP^T - delta), P recomputed from the forward's LSE, one
     // 32-key block at a time (the block's products, probabilities and dQ
@@ -192,12 +175,12 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
       }
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&ks[(kb * 32 + c) * KP + s * 16 + 8 * g]);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kl + (ra ^ (32 * s)) + kb * 32 * D * 2);
         sacc = mfma_32x32x16<BF16>(a, qf[s], sacc);
-        const u32x4 av = *reinterpret_cast<const u32x4*>(&vs[(kb * 32 + c) * KP + s * 16 + 8 * g]);
+        const u32x4 av = *reinterpret_cast<const u32x4*>(vl + (ra ^ (32 * s)) + kb * 32 * D * 2);
         dpacc = mfma_32x32x16<BF16>(av, df[s], dpacc);
       }
-      pin_reads_ahead<2 * (D / 16), 4, 1>();  // K / V reads four products ahead (1-2 % faster)
+      pin_reads_ahead<2 * (D / 16), 4, 1>();  // K / V reads four products ahead
       if (full) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -270,21 +253,23 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
                        pack2<BF16>(sacc[base + 4], sacc[base + 5]),
                        pack2<BF16>(sacc[base + 6], sacc[base + 7])};
       }
+      // A operand of k-step s: keys 16 s + 4 g + 0..3 (elements 0-3) and
+      // 16 s + 8 + 4 g + 0..3 (elements 4-7) of the lane's dim of K.
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const uint16_t* krow = klane + db * 32 * TP;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           const int s = 2 * kb + s2;
-          const u32x2 a0 = *reinterpret_cast<const u32x2*>(krow + tcol_const(db, 2 * s));
-          const u32x2 a1 = *reinterpret_cast<const u32x2*>(krow + tcol_const(db, 2 * s + 1));
+          const u32x2 a0 = lds_read_tr(kl + (ta ^ (64 * db)) + 16 * s * D * 2);
+          const u32x2 a1 = lds_read_tr(kl + (ta ^ (64 * db) ^ 32) + (16 * s + 8) * D * 2);
           dq[db] = mfma_32x32x16<BF16>(u32x4{a0.x, a0.y, a1.x, a1.y}, pb[s2], dq[db]);
         }
       }
-      // K^T reads two products ahead for D = 128 (backward 2 % faster; equal
-      // or slower for D = 64).
+      // K^T reads two products ahead for D = 128.
       if constexpr (D == 128) pin_reads_ahead<2 * (D / 32), 2, 2>();
     }
+    rao ^= TB;
+    tao ^= TB;
   }
 
   if (!qvalid) return;
@@ -313,14 +298,14 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
   static_assert(BQ == 32 || (KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL),
                 "per-score masks are loaded for one 32-query block per step");
   constexpr int NSUB = BQ / 32;
-  constexpr int RP = D + 8;   // row-major tile pitch, elements
-  constexpr int TP = BQ + 4;  // transposed tile pitch, elements (BQ / 2 + 2 dwords)
-  __shared__ __align__(16) uint16_t qs[BQ * RP];    // Q: A of S = Q K^T
-  __shared__ __align__(16) uint16_t qts[D * TP];    // Q^T: A of dK^T += Q^T dS
-  __shared__ __align__(16) uint16_t dos[BQ * RP];   // dO: A of dP = dO V^T
-  __shared__ __align__(16) uint16_t dots[D * TP];   // dO^T: A of dV^T += dO^T P
-  __shared__ __align__(16) float lses[BQ];  // LSE * log2(e) of the tile's queries
-  __shared__ __align__(16) float dels[BQ];
+  constexpr int TQ = BQ * D * 2;  // bytes per Q or dO tile
+  // Q and dO tiles of a step (dswz layout) at 0 and TQ, the next step's at
+  // 2 TQ and 3 TQ; bit 2 TQ of the offsets picks a step's buffer. Q serves the
+  // row reads of S = Q K^T and the transposing reads of the Q^T operand of
+  // dK^T += Q^T dS; dO those of dP = dO V^T and dV^T += dO^T P.
+  __shared__ __align__(1024) uint8_t qd[4 * TQ];
+  __shared__ __align__(16) float lses[2][BQ];  // LSE * log2(e) of the step's queries
+  __shared__ __align__(16) float dels[2][BQ];
 
   const int tid = (int)threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
@@ -377,91 +362,43 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
   qstart = qstart / BQ * BQ;
   const bool any = k0 < klen;
 
-  // Tiles of BQ queries fetched one ahead as items of (4 queries x 8 dims):
-  // the QITEMS items of Q, then those of dO, dealt to the threads in order
-  // (item tid + 256 i is thread tid's i-th), staged row-major and
-  // transposed; LSE by the first BQ lanes of wavefront 0 and delta by those
-  // of wavefront 1. Every choice of source is uniform over a wavefront and
-  // made once here: a per-lane choice between kernel-argument fields inside
-  // the loop made the compiler fetch the fields with vector loads and wait
-  // for every outstanding load, prefetch included.
-  constexpr int QITEMS = (BQ / 4) * (D / 8);  // 64, 128 or 256: whole wavefronts
-  constexpr int NITEMS = 2 * QITEMS;
-  constexpr int NIT = (NITEMS + 255) / 256;    // items per thread
-  static_assert(QITEMS % 64 == 0, "Q / dO loads by whole wavefronts");
-  // This lane's Q^T and dO^T operand rows c, c + 32, ... (tcol's lane part included).
-  const uint16_t* const qlane = &qts[c * TP + tcol_lane(c, g)];
-  const uint16_t* const dolane = &dots[c * TP + tcol_lane(c, g)];
-  const bool is_stat = wave < 2 && lane < BQ;  // LSE (wavefront 0) or delta (wavefront 1)
+  // A step's Q and dO tiles are loaded straight into LDS during the step
+  // before (rows past Sq read as zero); LSE and delta through a register of
+  // the first BQ lanes of wavefronts 0 and 1, written to LDS at the start of
+  // the step (scaled, and filled past Sq). Every choice of source is uniform
+  // over a wavefront and made once here.
   const int swave = __builtin_amdgcn_readfirstlane(wave);
-  float* const sdst = swave == 0 ? lses : dels;
+  const bool is_stat = wave < 2 && lane < BQ;  // LSE (wavefront 0) or delta (wavefront 1)
   const float sfill = swave == 0 ? kNegInfA : 0.0f;
   const float smul = swave == 0 ? kLog2eA : 1.0f;  // LSE is staged in log2 units
-  u32x4 treg[NIT][4];
   float sreg = 0.0f;
-  // The fetch reads through buffer ranges re-based on each step (scalar
-  // registers) that end at the last query (rows past it read as zero; the
-  // stage fills LSE / delta there), with fixed per-thread offsets. Every
-  // thread loads: threads past the last item load a copy of another's, and
-  // wavefronts past the LSE / delta lanes a copy of the LSE, so that no branch
-  // makes the wait for a step's mask values cover the fetch.
-  const char* fsrc[NIT];
-  int64_t fs_h[NIT], fs_s[NIT];
-  bool fstage[NIT], fdo[NIT];
-  int fqdg[NIT], fqqg[NIT];
-  uint32_t toff[NIT][4];
-#pragma unroll
-  for (int i = 0; i < NIT; ++i) {
-    const int it = (tid + 256 * i) % NITEMS;
-    fstage[i] = tid + 256 * i < NITEMS;
-    fdo[i] = __builtin_amdgcn_readfirstlane(it / QITEMS) == 1;
-    const int local = it % QITEMS;
-    fqdg[i] = local % (D / 8);
-    fqqg[i] = local / (D / 8);
-    fsrc[i] = fdo[i] ? p.dout + (int64_t)b * p.sdo_b * 2 : p.q + (int64_t)b * p.sq_b * 2;
-    fs_h[i] = fdo[i] ? p.sdo_h : p.sq_h;
-    fs_s[i] = fdo[i] ? p.sdo_s : p.sq_s;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) toff[i][k] = (uint32_t)((4 * fqqg[i] + k) * fs_s[i] * 2 + fqdg[i] * 16);
-  }
   const float* fssrc = swave == 1 ? p.delta : p.lse;
   const uint32_t soff = (uint32_t)(lane & (BQ - 1)) * 4;
-  // With per-score mask loads the loop's fetch is unconditional too.
-  constexpr bool kFlat = KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL;
-  int sq_staged = 0;  // first query of the staged tile (the fill of LSE / delta past Sq)
-  auto fetch = [&](uint32_t h, int qt) {
+  const char* const qsrc = p.q + (int64_t)b * p.sq_b * 2;
+  const char* const dsrc = p.dout + (int64_t)b * p.sdo_b * 2;
+  const uint32_t qdo = dma_lane_off<D>(lane, swave, p.sq_s * 2);
+  const uint32_t ddo = dma_lane_off<D>(lane, swave, p.sdo_s * 2);
+  const uint32_t qd_lds = lds_addr(qd);
+  auto fetch = [&](uint32_t h, int qt, int buf) {
     const int rows = min(Sq - qt, BQ);
-#pragma unroll
-    for (int i = 0; i < NIT; ++i) {
-      const auto tr = rows_rsrc(fsrc[i] + ((int64_t)h * fs_h[i] + (int64_t)qt * fs_s[i]) * 2, rows,
-                                fs_s[i] * 2, D * 2);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) treg[i][k] = rsrc_load(tr, toff[i][k]);
-    }
+    const u32x4 qr = rows_desc(qsrc + ((int64_t)h * p.sq_h + (int64_t)qt * p.sq_s) * 2, rows, p.sq_s * 2, D * 2);
+    const u32x4 dr = rows_desc(dsrc + ((int64_t)h * p.sdo_h + (int64_t)qt * p.sdo_s) * 2, rows, p.sdo_s * 2, D * 2);
+    dma_tile_asm<D, BQ>(qr, qdo, p.sq_s * 2, swave, qd_lds + buf * 2 * TQ);
+    dma_tile_asm<D, BQ>(dr, ddo, p.sdo_s * 2, swave, qd_lds + buf * 2 * TQ + TQ);
     const auto sr = rows_rsrc(reinterpret_cast<const char*>(fssrc + ((int64_t)b * p.H + h) * Sq + qt),
                               rows, 4, 4);
     sreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, (int)soff, 0, 0));
   };
-  auto stage = [&]() {
-#pragma unroll
-    for (int i = 0; i < NIT; ++i) {
-      if (!fstage[i]) continue;
-      uint16_t* const srm = fdo[i] ? dos : qs;
-      uint16_t* const stp = fdo[i] ? dots : qts;
-      const int qdg = fqdg[i], qqg = fqqg[i];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        *reinterpret_cast<u32x4*>(&srm[(4 * qqg + k) * RP + 8 * qdg]) = treg[i][k];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const u32x2 w{pair(treg[i][0], treg[i][1], j), pair(treg[i][2], treg[i][3], j)};
-        *reinterpret_cast<u32x2*>(&stp[(8 * qdg + j) * TP + tcol(8 * qdg + j, qqg)]) = w;
-      }
-    }
-    // (LSE scaled to log2 units here, not as it arrives: an operation on the
-    // loaded value in the fetch would wait for it, and with it for the tile.)
-    if (is_stat) sdst[lane] = sq_staged + lane < Sq ? sreg * smul : sfill;
-  };
+  // With per-score mask loads the loop's fetch is unconditional.
+  constexpr bool kFlat = KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL;
+  // LDS byte offsets of this lane's reads (as in the dQ kernel): row reads
+  // (query 32 qb + c, logical chunk 2 s + g) at (ra ^ 32 s) + 32 qb rows;
+  // transposing reads (queries 8 hf + 4 g + (c % 16) / 4 + 16 ks, dims
+  // 32 db + 16 ((c / 16) % 2) + 4 (c % 4) .. + 3) at (ta ^ 64 db ^ 32 hf)
+  // + (16 ks + 8 hf) rows. Both carry the step's buffer bit.
+  uint32_t rao = (uint32_t)dtile_off<D>(c, g);
+  uint32_t tao =
+      (uint32_t)(dtile_off<D>(4 * g + ((c & 15) >> 2), 2 * ((c >> 4) & 1) + ((c >> 1) & 1)) + 8 * (c & 1));
 
   if (any && qstart < Sq) {
     // One sequence of (query head, query tile) steps over the heads of the
@@ -470,8 +407,9 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
     const int nstep = ntile * (int)p.group;
     uint32_t h = hk * p.group, nh = h;
     int qt = qstart, nqt = qstart;
-    fetch(h, qt);
+    fetch(h, qt, 0);
     for (int step = 0; step < nstep; ++step) {
+      const int buf = step & 1;
       h = nh;
       qt = nqt;
       nqt = qt + BQ;
@@ -481,10 +419,17 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
       }
       const int64_t mbase = (int64_t)b * p.sm_b + (int64_t)h * p.sm_h;
       {
+        // This wavefront's loads of the step have landed; after the barrier
+        // every wavefront's have, and every wavefront is done with the
+        // previous step, whose buffers the next loads overwrite.
+        __builtin_amdgcn_s_waitcnt(0);
+        if (is_stat) (swave == 0 ? lses : dels)[buf][lane] = qt + lane < Sq ? sreg * smul : sfill;
         __syncthreads();
-        sq_staged = qt;
-        stage();
-        __syncthreads();
+        const uint8_t* const ql = qd;
+        const uint8_t* const dl_ = qd + TQ;
+        const float* const lsb = lses[buf];
+        const float* const deb = dels[buf];
+        const uint32_t ra = rao, ta = tao;
         // This step's mask values of the lane's key, one per query (register
         // r: query qt + 8 (r / 4) + 4 g + r % 4), loaded before the prefetch
         // so that waiting for them leaves it in flight: 16-bit additive values
@@ -511,10 +456,10 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
         if (kFlat) {
           // Branch-free: the last step fetches its own tile again.
           const bool more = step + 1 < nstep;
-          fetch(more ? nh : h, more ? nqt : qt);
+          fetch(more ? nh : h, more ? nqt : qt, buf ^ 1);
           __builtin_amdgcn_sched_barrier(0);  // keep the fetch ahead of the products
         } else if (step + 1 < nstep) {
-          fetch(nh, nqt);
+          fetch(nh, nqt, buf ^ 1);
         }
 
         // The tile's 32-query blocks in turn (the block's products,
@@ -532,10 +477,10 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
           }
 #pragma unroll
           for (int s = 0; s < D / 16; ++s) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(&qs[(32 * qb + c) * RP + s * 16 + 8 * g]);
+            const u32x4 a = *reinterpret_cast<const u32x4*>(ql + (ra ^ (32 * s)) + 32 * qb * D * 2);
             sacc = mfma_32x32x16<BF16>(a, kf[s], sacc);
             if constexpr (kDK) {
-              const u32x4 ad = *reinterpret_cast<const u32x4*>(&dos[(32 * qb + c) * RP + s * 16 + 8 * g]);
+              const u32x4 ad = *reinterpret_cast<const u32x4*>(dl_ + (ra ^ (32 * s)) + 32 * qb * D * 2);
               dpacc = mfma_32x32x16<BF16>(ad, vf[s], dpacc);
             }
           }
@@ -553,9 +498,9 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
           if (full) {
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
-              const int ql = 32 * qb + 8 * rg + 4 * g;  // first of 4 consecutive queries
-              const float4 l2 = *reinterpret_cast<const float4*>(&lses[ql]);
-              const float4 dl = *reinterpret_cast<const float4*>(&dels[ql]);
+              const int qo = 32 * qb + 8 * rg + 4 * g;  // first of 4 consecutive queries
+              const float4 l2 = *reinterpret_cast<const float4*>(&lsb[qo]);
+              const float4 dl = *reinterpret_cast<const float4*>(&deb[qo]);
               const float lv[4] = {l2.x, l2.y, l2.z, l2.w}, dv4[4] = {dl.x, dl.y, dl.z, dl.w};
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
@@ -570,9 +515,9 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
             // past Sq or without any visible key has LSE -inf here).
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
-              const int ql = 32 * qb + 8 * rg + 4 * g;
-              const float4 l2 = *reinterpret_cast<const float4*>(&lses[ql]);
-              const float4 dl = *reinterpret_cast<const float4*>(&dels[ql]);
+              const int qo = 32 * qb + 8 * rg + 4 * g;
+              const float4 l2 = *reinterpret_cast<const float4*>(&lsb[qo]);
+              const float4 dl = *reinterpret_cast<const float4*>(&deb[qo]);
               const float lv[4] = {l2.x, l2.y, l2.z, l2.w}, dv4[4] = {dl.x, dl.y, dl.z, dl.w};
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
@@ -589,11 +534,11 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
           } else {
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
-              const int ql = 32 * qb + 8 * rg + 4 * g;
+              const int qo = 32 * qb + 8 * rg + 4 * g;
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                const int r = 4 * rg + e, qq = qt + ql + e;
-                const float lse2 = lses[ql + e];
+                const int r = 4 * rg + e, qq = qt + qo + e;
+                const float lse2 = lsb[qo + e];
                 float tv = sacc[r] * p.scale_log2;
                 bool excluded = qq >= Sq || kj >= klen || !kvalid || lse2 == kNegInfA ||
                                 (p.causal && kj > qq + off);
@@ -604,7 +549,7 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
                 }
                 const float pv = excluded ? 0.0f : __builtin_amdgcn_exp2f(tv - lse2);
                 pr[r] = pv;
-                dsr[r] = pv * (dpacc[r] - dels[ql + e]);
+                dsr[r] = pv * (dpacc[r] - deb[qo + e]);
               }
             }
           }
@@ -618,21 +563,21 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
             sb[s] = u32x4{pack2<BF16>(dsr[8 * s + 0], dsr[8 * s + 1]), pack2<BF16>(dsr[8 * s + 2], dsr[8 * s + 3]),
                           pack2<BF16>(dsr[8 * s + 4], dsr[8 * s + 5]), pack2<BF16>(dsr[8 * s + 6], dsr[8 * s + 7])};
           }
+          // A operands of k-step ks: queries 16 ks + 4 g + 0..3 (elements
+          // 0-3) and 16 ks + 8 + 4 g + 0..3 (elements 4-7) of the lane's dim.
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            const uint16_t* dorow = dolane + db * 32 * TP;
-            const uint16_t* qrow = qlane + db * 32 * TP;
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
               const int ks = 2 * qb + s;  // the k-step's 16 queries within the tile
+              const uint32_t t0 = (ta ^ (64 * db)) + 16 * ks * D * 2;
+              const uint32_t t1 = (ta ^ (64 * db) ^ 32) + (16 * ks + 8) * D * 2;
               if constexpr (kDV) {
-                const u32x2 a0 = *reinterpret_cast<const u32x2*>(dorow + tcol_const(db, 2 * ks));
-                const u32x2 a1 = *reinterpret_cast<const u32x2*>(dorow + tcol_const(db, 2 * ks + 1));
+                const u32x2 a0 = lds_read_tr(dl_ + t0), a1 = lds_read_tr(dl_ + t1);
                 dv[db] = mfma_32x32x16<BF16>(u32x4{a0.x, a0.y, a1.x, a1.y}, pb[s], dv[db]);
               }
               if constexpr (kDK) {
-                const u32x2 b0 = *reinterpret_cast<const u32x2*>(qrow + tcol_const(db, 2 * ks));
-                const u32x2 b1 = *reinterpret_cast<const u32x2*>(qrow + tcol_const(db, 2 * ks + 1));
+                const u32x2 b0 = lds_read_tr(ql + t0), b1 = lds_read_tr(ql + t1);
                 dk[db] = mfma_32x32x16<BF16>(u32x4{b0.x, b0.y, b1.x, b1.y}, sb[s], dk[db]);
               }
             }
@@ -641,6 +586,8 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
           if constexpr (D == 128 && KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL)
             pin_reads_ahead<((kDV ? 1 : 0) + (kDK ? 1 : 0)) * 2 * (D / 32), 2, 2>();
         }
+        rao ^= 2 * TQ;
+        tao ^= 2 * TQ;
       }
     }
   }

@@ -14,7 +14,9 @@ instruction 1; an intervening write of the register ends the search).
 
     python -m attention_softmax_amd.isa_check file.s [...]
 
-Used by the CPU tests on the attention sources as the build compiles them.
+Used by the CPU tests on the attention sources as the build compiles them,
+together with m0_outside_asm (no compiler use of m0 where inline assembly
+sets it).
 """
 
 import re
@@ -131,6 +133,37 @@ def check_text(text, min_wait=MIN_WAIT):
         f = check_function(body, min_wait)
         if f:
             out[name] = f
+    return out
+
+
+def m0_outside_asm(text):
+    """{kernel symbol: [instructions]} of compiler-emitted instructions that
+    name m0, in kernels whose inline assembly sets m0 (the LDS loads issued
+    from inline assembly there rely on the compiler keeping nothing in m0)."""
+    out, cur, in_asm, sets, uses = {}, None, False, False, []
+    def close():
+        if cur is not None and sets and uses:
+            out[cur] = uses
+    for line in text.splitlines():
+        if re.match(r"^_Z\w+:", line):
+            close()
+            cur, in_asm, sets, uses = line.split(":")[0], False, False, []
+            continue
+        s = line.strip()
+        if s.startswith(";;#ASMSTART"):
+            in_asm = True
+            continue
+        if s.startswith(";;#ASMEND"):
+            in_asm = False
+            continue
+        ins = s.split(";")[0].strip()
+        if cur is None or not ins or not re.search(r"\bm0\b", ins):
+            continue
+        if in_asm:
+            sets = True
+        else:
+            uses.append(ins)
+    close()
     return out
 
 
