@@ -271,6 +271,9 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
     rao ^= TB;
     tao ^= TB;
   }
+  // The last tile's loads into LDS (issued unconditionally with per-score
+  // masks) complete before the workgroup, and its LDS, can end.
+  __builtin_amdgcn_s_waitcnt(0);
 
   if (!qvalid) return;
   char* orow = p.dq + ((int64_t)b * p.sdq_b + (int64_t)h * p.sdq_h + (int64_t)qi * p.sdq_s) * 2;
@@ -591,6 +594,9 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
       }
     }
   }
+  // The last step's loads into LDS (issued unconditionally with per-score
+  // masks) complete before the workgroup, and its LDS, can end.
+  __builtin_amdgcn_s_waitcnt(0);
 
   if (!kvalid) return;
   char* dkrow = p.dk + ((int64_t)b * p.sdk_b + (int64_t)hk * p.sdk_h + (int64_t)kj * p.sdk_s) * 2;
