@@ -32,7 +32,7 @@ struct AttnParams {
   int causal;        // 0 none, 1 key k > q excluded, 2 key k > q + Sk - Sq excluded
   int mask_kind;     // 0 none, 1 additive, 2 bool, 3 key lengths
   int mask_vec;      // every mask row starts on 4 elements and Sk % 4 == 0 (runs of 4 keys)
-  int mask_tile;     // every mask row starts on a 16-byte line (tiles of mask rows in LDS)
+  int mask_tile;     // additive, every mask row starts on a 16-byte line (mask tiles in LDS)
 };
 
 enum : int { ATTN_MASK_NONE = 0, ATTN_MASK_ADD = 1, ATTN_MASK_BOOL = 2, ATTN_MASK_LEN = 3 };
@@ -173,43 +173,6 @@ __device__ inline __attribute__((always_inline)) void pin_reads_ahead() {
   __builtin_amdgcn_sched_group_barrier(0x008, L, 0);
 }
 
-__device__ inline __attribute__((always_inline)) u32x4 rsrc_load(__amdgpu_buffer_rsrc_t r,
-                                                                 uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-}
-
-// Column (in elements) of the group of 4 consecutive elements qg in row d of
-// a transposed LDS tile. Bits 0 and 2 of the group index are XOR-ed with bits
-// 4 and 5 of the row: the staging writes (16 rows of one group per 16 lanes)
-// then land at most 2 to a bank instead of 8, while the MFMA operand reads (32
-// consecutive rows, one group) stay conflict-free (32 banks; 2-way with 64).
-// Bit 1 is left alone, so the two 8-byte halves of an operand (groups 2h and
-// 2h + 1, h even) keep their order in memory and one paired LDS read fills
-// the operand's registers in order. (XOR-ing bits 0-2 with row bits 4-6 made
-// the writes conflict-free, but swapped the halves on every other 32-row
-// block, and the compiler then spent four register moves per operand.)
-__host__ __device__ constexpr int tcol(int d, int qg) {
-  return 4 * (qg ^ (((d >> 4) & 1) | ((d >> 3) & 4)));
-}
-
-// tcol for an operand read of row d = 32 * blk + c (c < 32) and group
-// qg = 2 * h + g (g < 2), split into a part that depends on the lane (c, g)
-// and a part fixed at compile time (blk, h): the lane's bits (g and
-// (c / 16) % 2) make up bit 0 of the group index and of the XOR, which the
-// compile-time bits never reach, so the XOR becomes a sum. One address
-// register per lane then serves every read, with immediate offsets.
-__host__ __device__ constexpr int tcol_lane(int c, int g) { return 4 * (g ^ ((c >> 4) & 1)); }
-__host__ __device__ constexpr int tcol_const(int blk, int h) { return 4 * ((2 * h) ^ (4 * (blk & 1))); }
-constexpr bool tcol_split_holds() {
-  for (int blk = 0; blk < 8; ++blk)
-    for (int c = 0; c < 32; ++c)
-      for (int h = 0; h < 8; ++h)
-        for (int g = 0; g < 2; ++g)
-          if (tcol(32 * blk + c, 2 * h + g) != tcol_lane(c, g) + tcol_const(blk, h)) return false;
-  return true;
-}
-static_assert(tcol_split_holds(), "tcol must split into lane and compile-time parts");
-
 // Tiles loaded straight from global memory into LDS (buffer loads with the
 // LDS flag): rows of D 16-bit values in 16-byte chunks, no padding. A load
 // instruction fills 1 KB of LDS in lane order, so the conflict-free layout
@@ -328,13 +291,6 @@ __device__ inline __attribute__((always_inline)) void dma_tile(__amdgpu_buffer_r
 // 16-bit element j (0..7) of an 8-element vector.
 __device__ inline __attribute__((always_inline)) uint32_t elem(const u32x4& v, int j) {
   return (v[j >> 1] >> ((j & 1) * 16)) & 0xffffu;
-}
-
-// elem(lo, j) | elem(hi, j) << 16 in one byte permute (v_perm_b32: bytes 0-3
-// of the second operand and 4-7 of the first are selectable).
-__device__ inline __attribute__((always_inline)) uint32_t pair(const u32x4& lo, const u32x4& hi,
-                                                               int j) {
-  return __builtin_amdgcn_perm(hi[j >> 1], lo[j >> 1], (j & 1) ? 0x07060302u : 0x05040100u);
 }
 
 // Mask values of one lane's 32 keys of a 64-key tile in the query-stationary

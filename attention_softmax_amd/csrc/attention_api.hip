@@ -123,11 +123,10 @@ sms_status sms_attention_forward(const void* q, const int64_t q_strides[4], cons
   // keys stay inside a row: vector mask loads.
   p.mask_vec = (p.mask_kind == sms::ATTN_MASK_ADD || p.mask_kind == sms::ATTN_MASK_BOOL) &&
                Sk % 4 == 0 && aligned_to(mask, p.mask_kind == sms::ATTN_MASK_ADD ? 8 : 4);
-  // Mask rows on 16-byte lines (16 bytes = 8 additive or 16 boolean values),
-  // and a tile of 128 rows within a 31-bit byte range.
-  const int64_t mvb = p.mask_kind == sms::ATTN_MASK_ADD ? 2 : 1;
-  p.mask_tile = (p.mask_kind == sms::ATTN_MASK_ADD || p.mask_kind == sms::ATTN_MASK_BOOL) &&
-                (Sk * mvb) % 16 == 0 && aligned_to(mask, 16) && 128 * Sk * mvb < INT32_MAX;
+  // Additive mask rows on 16-byte lines (8 values), and a tile of 128 rows
+  // within a 31-bit byte range.
+  p.mask_tile = p.mask_kind == sms::ATTN_MASK_ADD && Sk % 8 == 0 && aligned_to(mask, 16) &&
+                128 * Sk * 2 < INT32_MAX;
   const hipError_t e = sms_attn_launch(&p, (int)dtype, (int)D, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SMS_OK : SMS_ERR_HIP;
 }
