@@ -63,7 +63,9 @@ def check(q, k, v, mask, mode, kind, scale, causal, what):
 
 
 # (300, 100): bottom-right causal leaves the first 128-query tile without any key.
-SHAPES = [(1, 1), (37, 63), (128, 64), (129, 65), (200, 300), (64, 1000), (300, 100)]
+# (200, 136): additive masks as LDS tiles (Sk % 8 == 0) over two query tiles and
+# a last key tile of 8 keys.
+SHAPES = [(1, 1), (37, 63), (128, 64), (129, 65), (200, 300), (64, 1000), (300, 100), (200, 136)]
 MASKS = [("none", "none"), ("sq_sk", "additive"), ("b_sq_sk", "neginf"), ("b_1_sk", "neginf"),
          ("full", "additive"), ("b_sq_sk", "bool"), ("key_lengths", "lengths")]
 
