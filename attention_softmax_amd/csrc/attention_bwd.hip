@@ -13,12 +13,16 @@
 //     each lane 16 keys of one query;
 //     P = exp(S*scale + mask - LSE); dS^T = P (dP^T - delta); dQ^T += K^T dS^T
 //     with the dS registers as the B operand (keys contracted in the order the
-//     S^T layout holds them, K^T read from a transposed LDS tile);
+//     S^T layout holds them, K^T read from the row-major K tile by
+//     transposing LDS reads);
 //  2. dK and dV, one workgroup per 128 keys of one key/value head
 //     (key-stationary): for every query head of its group and every tile of
 //     32 or 64 queries, S = Q K^T and dP = dO V^T leave each lane 16 queries
 //     of one key per 32-query block; dV^T += dO^T P and dK^T += Q^T dS with P
 //     and dS as B operands.
+// The tiles (K and V in 1, Q and dO in 2) come from global memory straight
+// into double-buffered LDS (dswz layout, loads issued from inline assembly,
+// dma_tile_asm), one barrier per tile or query step.
 // Lane layouts of v_mfma_f32_32x32x16: see attention.hip.
 
 #include "attention.hpp"
@@ -373,7 +377,7 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
   const int swave = __builtin_amdgcn_readfirstlane(wave);
   const bool is_stat = wave < 2 && lane < BQ;  // LSE (wavefront 0) or delta (wavefront 1)
   const float sfill = swave == 0 ? kNegInfA : 0.0f;
-  const float smul = swave == 0 ? kLog2eA : 1.0f;  // LSE is staged in log2 units
+  const float smul = swave == 0 ? kLog2eA : 1.0f;  // LSE is kept in log2 units
   float sreg = 0.0f;
   const float* fssrc = swave == 1 ? p.delta : p.lse;
   const uint32_t soff = (uint32_t)(lane & (BQ - 1)) * 4;
@@ -640,11 +644,12 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_both_kernel(AttnBwdParams p
   dkdv_body<BF16, D, KIND, 2, BQ>(p);
 }
 
-// Queries per dK/dV step. Two 32-query blocks per staged tile halve the
-// per-step work (barriers, staging, LSE / delta) per product: measured 4 %
-// faster for D = 64 (fp16 [8,32,2048,64] backward), equal within noise for
-// D = 128, where one block keeps the LDS and registers smaller. Per-score
-// masks keep one block (their values take registers per block).
+// Queries per dK/dV step. Two 32-query blocks per loaded tile halve the
+// per-step work (barrier, LSE / delta) per product: measured 4 % faster for
+// D = 64 (fp16 [8,32,2048,64] backward, register-staged tiles); for D = 128
+// 1 % slower with the tiles loaded straight into LDS (the larger tiles fit
+// one fewer dV-pass workgroup per CU). Per-score masks keep one block (their
+// values take registers per block).
 template <int KIND, int D>
 constexpr int dkdv_bq() {
   return (KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL || D == 128) ? 32 : 64;
