@@ -61,8 +61,17 @@ using namespace attn;
 // s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt at their maxima: no wait).
 constexpr int kWaitLgkm0 = 0xF | (7 << 4) | (0 << 8) | (3 << 14);
 
+// Wavefronts per SIMD: three for D = 64 (at most 168 VGPRs: 4-7 % faster
+// than two on fp16 [8,32,2048,64] and [4,32,4096,64]), except with additive
+// mask runs, which spill there; two for D = 128.
+template <int D, int KIND, int MV>
+constexpr int fwd_waves() {
+  return D == 64 && !(KIND == ATTN_MASK_ADD && MV == 1) ? 3 : 2;
+}
+
 template <bool BF16, int D, int KIND, int MV>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(fwd_waves<D, KIND, MV>(), fwd_waves<D, KIND, MV>())))
 attn_fwd_kernel(AttnParams p) {
   constexpr bool MASKED = KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL;
   static_assert(MV == 0 || MASKED, "mask runs need a per-score mask");

@@ -39,8 +39,11 @@ using namespace attn;
 // next tile's loads go out into the other buffer. K serves both the row reads
 // of S^T = K Q^T and the transposing reads that form the K^T operand of
 // dQ^T += K^T dS^T; V the row reads of dP^T = V dO^T.
+// Three wavefronts per SIMD for D = 64 (140-146 VGPRs: the backward 1.5-3 %
+// faster than at two on fp16 [8,32,2048,64] and [4,32,4096,64]), two for D = 128.
 template <bool BF16, int D, int KIND, bool MV>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2, D == 64 ? 3 : 2)))
 attn_bwd_dq_kernel(AttnBwdParams p) {
   constexpr int BK = kAttnBk;
   constexpr int TB = BK * D * 2;  // bytes per tile
