@@ -40,12 +40,15 @@ using namespace attn;
 // O^T += V^T P^T is assembled by transposing LDS reads (lds_read_tr: a lane
 // group addressing 4 keys x 16 dims hands every lane its own dim's 4
 // consecutive keys). The buffers are separate LDS objects and the tiles go
-// in pairs, so that every read has a fixed buffer: the compiler then knows
-// that the reads do not touch the buffer the loads (compiler-visible here)
-// are filling and inserts no wait for them, and the read offsets are
-// loop-invariant registers plus immediates. (The backward kernels issue the
-// loads from inline assembly instead, with one tile body for both buffers;
-// here that measured 1-2 % slower.)
+// in pairs, so that every read has a fixed buffer and the read offsets are
+// loop-invariant registers plus immediates. Without a per-score mask the
+// loads are issued from inline assembly (dma_one), which the compiler does
+// not see (the kernel waits for them itself before each barrier), one after
+// each k-step of the tile's S products instead of all together after the
+// barrier: 2 % faster (fp16 [4,32,4096,128] causal: 618 against 631 us).
+// With a per-score mask they are the compiler-visible builtin loads, issued
+// together; since they fill the other buffer object, the compiler knows that
+// the reads do not touch it and inserts no wait for them.
 //
 // Per-score masks (additive / boolean), MV: 2 (additive masks whose rows
 // start on 16-byte lines): the tile's mask values for the workgroup's 128
@@ -74,6 +77,9 @@ __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(fwd_waves<D, KIND, MV>(), fwd_waves<D, KIND, MV>())))
 attn_fwd_kernel(AttnParams p) {
   constexpr bool MASKED = KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL;
+  // Without a per-score mask the K / V loads are issued from inline assembly,
+  // spread over the tile's S products (below).
+  constexpr bool kSpread = !MASKED;
   static_assert(MV == 0 || MASKED, "mask runs need a per-score mask");
   static_assert(MV != 2 || KIND == ATTN_MASK_ADD, "mask tiles of 16-bit values");
   constexpr int BK = kAttnBk;
@@ -163,6 +169,14 @@ attn_fwd_kernel(AttnParams p) {
     dma_tile<D, BK>(kr, kdo, p.sk_s * 2, wave_u, BUF ? ks1 : ks0);
     dma_tile<D, BK>(vr, vdo, p.sv_s * 2, wave_u, BUF ? vs1 : vs0);
   };
+  // Descriptors of tile kt's K and V rows for the inline-assembly loads
+  // (kSpread); past kend none (the loads then write zeros into a buffer that
+  // no tile reads again).
+  auto tile_desc = [&](int kt, u32x4& kr, u32x4& vr) {
+    const int rows = kt < kend ? min(Sk - kt, BK) : 0;
+    kr = rows_desc(kbase + (int64_t)kt * p.sk_s * 2, rows, p.sk_s * 2, D * 2);
+    vr = rows_desc(vbase + (int64_t)kt * p.sv_s * 2, rows, p.sv_s * 2, D * 2);
+  };
   // Mask tiles (MV == 2): the workgroup's query rows (past Sq: none, or the
   // one broadcast row) through one buffer range ending at the last row's last
   // key; keys past Sk of the other rows read the next row's first values,
@@ -176,7 +190,14 @@ attn_fwd_kernel(AttnParams p) {
     dma_tile<64, kAttnBq>(mr, mdo, p.sm_q * 2, wave_u, ms);
   };
   if (kend > 0) {
-    dma(0, BoolC<false>{});
+    if constexpr (kSpread) {
+      u32x4 kr, vr;
+      tile_desc(0, kr, vr);
+      dma_tile_asm<D, BK>(kr, kdo, p.sk_s * 2, wave_u, lds_addr(ks0));
+      dma_tile_asm<D, BK>(vr, vdo, p.sv_s * 2, wave_u, lds_addr(vs0));
+    } else {
+      dma(0, BoolC<false>{});
+    }
     if constexpr (MV == 2) dma_mask(0);
   }
   u32x2 mv[8], mv_next[8];  // mask runs of this tile and (MV == 1) of the next
@@ -223,8 +244,6 @@ attn_fwd_kernel(AttnParams p) {
       // (Runs past the last key read at the row's last run: never used.)
       load_mask_runs<KIND>(p.mask, mrow_c, kt + BK, g, Sk, mv_next);
       if (kt + BK < kend) dma(kt + BK, BoolC<BUF == 0>{});
-    } else if constexpr (MV == 0 && !MASKED) {
-      if (kt + BK < kend) dma(kt + BK, BoolC<BUF == 0>{});
     }
 
     // S^T for the tile's two 32-key blocks, alternating between the blocks so
@@ -235,16 +254,48 @@ attn_fwd_kernel(AttnParams p) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+    if constexpr (kSpread) {
+      // The next tile's loads, one after each k-step (K and V in turn), in
+      // source order with the K fragments read five k-steps ahead: the loads
+      // are inline assembly with a memory clobber, which no LDS read crosses,
+      // and a scheduling barrier after each keeps the products between them.
+      constexpr int NS = D / 16, AH = NS < 5 ? NS : 5;
+      static_assert(NS == 2 * dma_loads<D, BK>(), "one K or V load per k-step");
+      u32x4 kr, vr;
+      tile_desc(kt + BK, kr, vr);
+      const uint32_t kn = lds_addr(BUF ? ks0 : ks1), vn = lds_addr(BUF ? vs0 : vs1);
+      u32x4 ka[NS][2];
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s)
+      for (int s = 0; s < AH; ++s)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(kt_lds + kao[s] + kb * 32 * D * 2);
-        sacc[kb] = mfma_32x32x16<BF16>(a, qf[s], sacc[kb]);
+        for (int kb = 0; kb < 2; ++kb)
+          ka[s][kb] = *reinterpret_cast<const u32x4*>(kt_lds + kao[s] + kb * 32 * D * 2);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma_32x32x16<BF16>(ka[s][kb], qf[s], sacc[kb]);
+        if (s + AH < NS) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            ka[s + AH][kb] = *reinterpret_cast<const u32x4*>(kt_lds + kao[s + AH] + kb * 32 * D * 2);
+        }
+        if ((s & 1) == 0) dma_one<D>(kr, kdo, p.sk_s * 2, wave_u, kn, s >> 1);
+        else dma_one<D>(vr, vdo, p.sv_s * 2, wave_u, vn, s >> 1);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    // K reads ten products ahead: 2-5 % faster than the scheduler's own order
-    // (measured without per-score mask runs, whose loads share the region).
-    if constexpr (MV == 0) pin_reads_ahead<2 * (D / 16), 10, 1>();
+    } else {
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(kt_lds + kao[s] + kb * 32 * D * 2);
+          sacc[kb] = mfma_32x32x16<BF16>(a, qf[s], sacc[kb]);
+        }
+    }
+    // With mask values read one by one: K reads ten products ahead (2-5 %
+    // faster than the scheduler's own order, measured before the spread loads
+    // above; not with mask runs, whose loads share the region).
+    if constexpr (MV == 0 && MASKED) pin_reads_ahead<2 * (D / 16), 10, 1>();
     if constexpr (MV == 2) {
       // Every wavefront has its runs (LDS reads complete, then the barrier:
       // a plain one, which unlike __syncthreads does not wait for the K / V

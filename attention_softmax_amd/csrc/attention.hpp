@@ -250,19 +250,29 @@ __device__ inline __attribute__((always_inline)) uint32_t dma_lane_off(int lane,
 // both), and the caller waits for them itself (vmcnt) before its barrier. The
 // compiler keeps no value in m0 here (its only other users are the builtin
 // LDS loads, not used alongside). src: the four descriptor words.
+// dma_one issues load i of the wavefront's dma_loads<D, TR>() loads of a tile
+// (rows RPI (w + 4 i) ..); dma_tile_asm issues all of them.
+template <int D, int TR>
+constexpr int dma_loads() {
+  constexpr int CH = D / 8, RPI = 64 / CH, NI = TR / RPI / 4;
+  static_assert(NI * RPI * 4 == TR, "whole 1 KB loads, four wavefronts");
+  return NI;
+}
+template <int D>
+__device__ inline __attribute__((always_inline)) void dma_one(u32x4 src, uint32_t voff, int64_t pitch, int w,
+                                                              uint32_t dst, int i) {
+  constexpr int CH = D / 8, RPI = 64 / CH;
+  const int r0 = RPI * (w + 4 * i);
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(src), "s"((uint32_t)(r0 * pitch)), "s"(dst + (uint32_t)(r0 * D * 2))
+               : "memory");
+}
 template <int D, int TR>
 __device__ inline __attribute__((always_inline)) void dma_tile_asm(u32x4 src, uint32_t voff, int64_t pitch,
                                                                    int w, uint32_t dst) {
-  constexpr int CH = D / 8, RPI = 64 / CH, NI = TR / RPI / 4;
-  static_assert(NI * RPI * 4 == TR, "whole 1 KB loads, four wavefronts");
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int r0 = RPI * (w + 4 * i);
-    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-                 :
-                 : "v"(voff), "s"(src), "s"((uint32_t)(r0 * pitch)), "s"(dst + (uint32_t)(r0 * D * 2))
-                 : "memory");
-  }
+  for (int i = 0; i < dma_loads<D, TR>(); ++i) dma_one<D>(src, voff, pitch, w, dst, i);
 }
 // Descriptor words of rows_rsrc.
 __device__ inline __attribute__((always_inline)) u32x4 rows_desc(const char* base, int rows, int64_t pitch,
