@@ -41,19 +41,21 @@ using namespace attn;
 // group addressing 4 keys x 16 dims hands every lane its own dim's 4
 // consecutive keys). The buffers are separate LDS objects and the tiles go
 // in pairs, so that every read has a fixed buffer and the read offsets are
-// loop-invariant registers plus immediates. Without a per-score mask the
-// loads are issued from inline assembly (dma_one), which the compiler does
-// not see (the kernel waits for them itself before each barrier), one after
-// each k-step of the tile's S products instead of all together after the
-// barrier: 2 % faster (fp16 [4,32,4096,128] causal: 618 against 631 us).
-// With a per-score mask they are the compiler-visible builtin loads, issued
-// together; since they fill the other buffer object, the compiler knows that
-// the reads do not touch it and inserts no wait for them.
+// loop-invariant registers plus immediates. Without a per-score mask, and
+// with mask tiles (MV 2, below), the loads are issued from inline assembly
+// (dma_one), which the compiler does not see (the kernel waits for them
+// itself before each barrier), one after each k-step of the tile's S
+// products instead of all together after the barrier: 2 % faster without a
+// mask (fp16 [4,32,4096,128] causal: 618 against 631 us), 4-6 % with an
+// additive [B,Sq,Sk] mask (723 against 752, 1267 against 1343 not causal).
+// Otherwise they are the compiler-visible builtin loads, issued together;
+// since they fill the other buffer object, the compiler knows that the reads
+// do not touch it and inserts no wait for them.
 //
 // Per-score masks (additive / boolean), MV: 2 (additive masks whose rows
 // start on 16-byte lines): the tile's mask values for the workgroup's 128
 // queries (a 128 x 64 tile of 128-byte rows, the dswz layout of D = 64) come
-// into one LDS buffer by the same loads; each lane reads its runs of 4 keys
+// into one LDS buffer by loads of the same kind; each lane reads its runs of 4 keys
 // from it at the start of the tile, and after a second barrier in the middle
 // of the tile (all runs read) the next tile's mask values go out into it;
 // 1 (mask rows on 4 elements and Sk % 4 == 0): the runs are loaded from
@@ -77,9 +79,10 @@ __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(fwd_waves<D, KIND, MV>(), fwd_waves<D, KIND, MV>())))
 attn_fwd_kernel(AttnParams p) {
   constexpr bool MASKED = KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL;
-  // Without a per-score mask the K / V loads are issued from inline assembly,
-  // spread over the tile's S products (below).
-  constexpr bool kSpread = !MASKED;
+  // Without a per-score mask, and with additive mask tiles, the K / V loads
+  // are issued from inline assembly, spread over the tile's S products
+  // (below).
+  constexpr bool kSpread = !MASKED || MV == 2;
   static_assert(MV == 0 || MASKED, "mask runs need a per-score mask");
   static_assert(MV != 2 || KIND == ATTN_MASK_ADD, "mask tiles of 16-bit values");
   constexpr int BK = kAttnBk;
@@ -186,8 +189,12 @@ attn_fwd_kernel(AttnParams p) {
   const uint32_t mdo = dma_lane_off<64>(lane, wave_u, p.sm_q * 2);
   auto dma_mask = [&](int kt) {
     const int rows = min(Sk - kt, BK);
-    const auto mr = rows_rsrc(p.mask + (mtile + kt) * 2, rows > 0 ? mrows : 0, p.sm_q * 2, max(rows, 0) * 2);
-    dma_tile<64, kAttnBq>(mr, mdo, p.sm_q * 2, wave_u, ms);
+    u32x4 mr = rows_desc(p.mask + (mtile + kt) * 2, rows > 0 ? mrows : 0, p.sm_q * 2, max(rows, 0) * 2);
+    // (Uniform words, which the compiler kept in vector registers here; the
+    // inline assembly takes them in scalar registers.)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mr[j] = __builtin_amdgcn_readfirstlane(mr[j]);
+    dma_tile_asm<64, kAttnBq>(mr, mdo, p.sm_q * 2, wave_u, lds_addr(ms));
   };
   if (kend > 0) {
     if constexpr (kSpread) {
@@ -239,7 +246,6 @@ attn_fwd_kernel(AttnParams p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         mv[i] = *reinterpret_cast<const u32x2*>(ms + dtile_off<64>(wave * 32 + c, 4 * (i >> 2) + (i & 3)) + 8 * g);
-      if (kt + BK < kend) dma(kt + BK, BoolC<BUF == 0>{});
     } else if constexpr (MV == 1) {
       // (Runs past the last key read at the row's last run: never used.)
       load_mask_runs<KIND>(p.mask, mrow_c, kt + BK, g, Sk, mv_next);
