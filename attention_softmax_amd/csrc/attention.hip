@@ -63,8 +63,6 @@ using namespace attn;
 // V, so that they have landed by the barrier that starts their tile; 0: each
 // mask value is read where it is used, and the next tile's loads go out after
 // those reads, so that waiting for them does not wait for the loads.
-// s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt at their maxima: no wait).
-constexpr int kWaitLgkm0 = 0xF | (7 << 4) | (0 << 8) | (3 << 14);
 
 // Wavefronts per SIMD: three for D = 64 (at most 168 VGPRs: 4-7 % faster
 // than two on fp16 [8,32,2048,64] and [4,32,4096,64]), except with additive

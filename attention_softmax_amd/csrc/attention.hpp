@@ -66,6 +66,7 @@ struct AttnBwdParams {
   int causal;
   int mask_kind;
   int mask_vec;      // as in AttnParams
+  int mask_tile;     // as in AttnParams
 };
 
 // Keys per workgroup of the dK / dV kernel (four wavefronts x 32); the
@@ -274,6 +275,8 @@ __device__ inline __attribute__((always_inline)) void dma_tile_asm(u32x4 src, ui
 #pragma unroll
   for (int i = 0; i < dma_loads<D, TR>(); ++i) dma_one<D>(src, voff, pitch, w, dst, i);
 }
+// s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt at their maxima: no wait).
+constexpr int kWaitLgkm0 = 0xF | (7 << 4) | (0 << 8) | (3 << 14);
 // Descriptor words of rows_rsrc.
 __device__ inline __attribute__((always_inline)) u32x4 rows_desc(const char* base, int rows, int64_t pitch,
                                                                  int row_bytes) {

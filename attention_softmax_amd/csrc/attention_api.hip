@@ -228,6 +228,9 @@ sms_status sms_attention_backward(const void* q, const int64_t q_strides[4], con
   // keys stay inside a row: vector mask loads.
   p.mask_vec = (p.mask_kind == sms::ATTN_MASK_ADD || p.mask_kind == sms::ATTN_MASK_BOOL) &&
                Sk % 4 == 0 && aligned_to(mask, p.mask_kind == sms::ATTN_MASK_ADD ? 8 : 4);
+  // Additive mask tiles in LDS, as in the forward.
+  p.mask_tile = p.mask_kind == sms::ATTN_MASK_ADD && Sk % 8 == 0 && aligned_to(mask, 16) &&
+                128 * Sk * 2 < INT32_MAX;
   const hipError_t e =
       sms_attn_bwd_launch(&p, (int)dtype, (int)D, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SMS_OK : SMS_ERR_HIP;

@@ -41,15 +41,26 @@ using namespace attn;
 // dQ^T += K^T dS^T; V the row reads of dP^T = V dO^T.
 // Three wavefronts per SIMD for D = 64 (140-146 VGPRs: the backward 1.5-3 %
 // faster than at two on fp16 [8,32,2048,64] and [4,32,4096,64]), two for D = 128.
-template <bool BF16, int D, int KIND, bool MV>
+// Per-score masks, MV: 2 (additive masks whose rows start on 16-byte lines):
+// the tile's mask values for the workgroup's 128 queries come into one LDS
+// buffer (a 128 x 64 tile, the dswz layout of D = 64), each lane reads its runs
+// at the start of the tile, and after a second barrier (all runs read) the
+// next tile's values go out into it, as in the forward; 1: the runs are
+// loaded from global memory at the start of the tile; 0: each value where it
+// is used.
+template <bool BF16, int D, int KIND, int MV>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2, D == 64 ? 3 : 2)))
 attn_bwd_dq_kernel(AttnBwdParams p) {
+  static_assert(MV == 0 || KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL, "mask runs need a per-score mask");
+  static_assert(MV != 2 || KIND == ATTN_MASK_ADD, "mask tiles of 16-bit values");
   constexpr int BK = kAttnBk;
   constexpr int TB = BK * D * 2;  // bytes per tile
+  constexpr int TM = kAttnBq * BK * 2;  // bytes per mask tile (MV == 2)
   // K tiles at 0 and TB, V tiles at 2 TB and 3 TB; bit TB of the offsets
   // picks a tile's buffer and flips every tile.
   __shared__ __align__(1024) uint8_t kv[4 * TB];
+  __shared__ __align__(1024) uint8_t ms[MV == 2 ? TM : 16];
 
   const int tid = (int)threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
@@ -134,7 +145,23 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
     dma_tile_asm<D, BK>(kr, kdo, p.sk_s * 2, wave_u, kv_lds + buf * TB);
     dma_tile_asm<D, BK>(vr, vdo, p.sv_s * 2, wave_u, kv_lds + (2 + buf) * TB);
   };
-  if (kend > 0) dma(0, 0);
+  // Mask tiles (MV == 2): the workgroup's query rows through one buffer range
+  // ending at the last row's last key; keys past Sk of the other rows read
+  // the next row's first values, whose scores are excluded.
+  const uint32_t mdo = dma_lane_off<64>(lane, wave_u, p.sm_q * 2);
+  const int mrows = min(Sq - q0, kAttnBq);
+  auto dma_mask = [&](int kt) {
+    const int rows = min(Sk - kt, BK);
+    u32x4 mr = rows_desc(p.mask + ((int64_t)b * p.sm_b + (int64_t)h * p.sm_h + (int64_t)q0 * p.sm_q + kt) * 2,
+                         rows > 0 ? mrows : 0, p.sm_q * 2, max(rows, 0) * 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mr[j] = __builtin_amdgcn_readfirstlane(mr[j]);
+    dma_tile_asm<64, kAttnBq>(mr, mdo, p.sm_q * 2, wave_u, lds_addr(ms));
+  };
+  if (kend > 0) {
+    dma(0, 0);
+    if constexpr (MV == 2) dma_mask(0);
+  }
 
   // LDS byte offsets of this lane's reads. Row reads: row c (+ 32 kb),
   // logical chunk 2 s + g, at rao ^ 32 s (dswz reads the row's low 4 bits
@@ -157,12 +184,18 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     u32x2 mv[8];  // this tile's mask values, loaded before the next tile's loads
-    if constexpr (MV) {
+    if constexpr (MV == 2) {
+      // The lane's runs (keys 32 (i / 4) + 8 (i % 4) + 4 g .. + 3 of its
+      // query's row: chunk 4 (i / 4) + i % 4, half g).
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        mv[i] = *reinterpret_cast<const u32x2*>(ms + dtile_off<64>(wave * 32 + c, 4 * (i >> 2) + (i & 3)) + 8 * g);
+    } else if constexpr (MV == 1) {
       load_mask_runs<KIND>(p.mask, mrow_c, kt, g, Sk, mv);
       __builtin_amdgcn_sched_barrier(0);  // keep them ahead of the loads
     }
-    if (MV || kt + BK < kend) dma(kt + BK, ((kt / BK) & 1) ^ 1);
-    if constexpr (MV) __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the products
+    if (MV == 1 || kt + BK < kend) dma(kt + BK, ((kt / BK) & 1) ^ 1);
+    if constexpr (MV == 1) __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the products
 
     // dS^T = P (dP^T - delta), P recomputed from the forward's LSE, one
     // 32-key block at a time (the block's products, probabilities and dQ
@@ -188,13 +221,22 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
         dpacc = mfma_32x32x16<BF16>(av, df[s], dpacc);
       }
       pin_reads_ahead<2 * (D / 16), 4, 1>();  // K / V reads four products ahead
+      if constexpr (MV == 2) {
+        if (kb == 0) {
+          // Every wavefront has its runs; the next tile's mask values may
+          // overwrite them (a plain barrier: it does not wait for the loads).
+          __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+          asm volatile("s_barrier" ::: "memory");
+          if (kt + BK < kend) dma_mask(kt + BK);
+        }
+      }
       if (full) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], p.scale_log2, -lse2));
           sacc[r] = pv * (dpacc[r] - delta);
         }
-      } else if ((KIND == ATTN_MASK_BOOL || (KIND == ATTN_MASK_ADD && !MV)) && inb) {
+      } else if ((KIND == ATTN_MASK_BOOL || (KIND == ATTN_MASK_ADD && MV == 0)) && inb) {
         // Every key in bounds for every query: the mask (and a query without
         // any visible key) alone. (Not for additive runs: the extra code path
         // made that variant spill.)
@@ -204,7 +246,7 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
           bool excluded = !live;
           if constexpr (KIND == ATTN_MASK_ADD) {
             uint32_t bits;
-            if constexpr (MV) {
+            if constexpr (MV != 0) {
               bits = mask_run_value(mv, kb, r, false);
             } else {
               const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
@@ -213,7 +255,7 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
             tv = fmaf(to_float<BF16>(bits), kLog2eA, tv);
           } else {
             uint32_t byte;
-            if constexpr (MV) {
+            if constexpr (MV != 0) {
               byte = mask_run_value(mv, kb, r, true);
             } else {
               const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
@@ -233,14 +275,14 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
           if constexpr (KIND == ATTN_MASK_ADD) {
             if (!excluded) {
               uint32_t bits;
-              if constexpr (MV) bits = mask_run_value(mv, kb, r, false);
+              if constexpr (MV != 0) bits = mask_run_value(mv, kb, r, false);
               else bits = *reinterpret_cast<const uint16_t*>(p.mask + (mrow + key) * 2);
               tv = fmaf(to_float<BF16>(bits), kLog2eA, tv);
             }
           } else if constexpr (KIND == ATTN_MASK_BOOL) {
             if (!excluded) {
               uint32_t byte;
-              if constexpr (MV) byte = mask_run_value(mv, kb, r, true);
+              if constexpr (MV != 0) byte = mask_run_value(mv, kb, r, true);
               else byte = (uint32_t)(uint8_t)p.mask[mrow + key];
               if (byte != 0) excluded = true;
             }
@@ -301,14 +343,20 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
 // registers (one wavefront per SIMD), so there PASS 0 (dV alone: S, P) and
 // PASS 1 (dK alone: S, dP, dS) run as two launches, each at two wavefronts
 // per SIMD, recomputing S in both.
-template <bool BF16, int D, int KIND, int PASS, int BQ>
+// MT: additive mask tiles in LDS (mask rows on 16-byte lines): the step's
+// BQ x 128 values (the dswz layout of D = 128, double-buffered) come with its
+// Q and dO tiles, and each lane takes its key's values for 4 consecutive
+// queries per transposing read, as the forward reads V.
+template <bool BF16, int D, int KIND, int PASS, int BQ, bool MT>
 __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdParams& p) {
   constexpr bool kDV = PASS != 1, kDK = PASS != 0;
   static_assert(BQ == 32 || BQ == 64, "query tiles of one or two 32-query blocks");
   static_assert(BQ == 32 || (KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL),
                 "per-score masks are loaded for one 32-query block per step");
+  static_assert(!MT || KIND == ATTN_MASK_ADD, "mask tiles of 16-bit values");
   constexpr int NSUB = BQ / 32;
   constexpr int TQ = BQ * D * 2;  // bytes per Q or dO tile
+  constexpr int TMQ = BQ * kAttnBwdBk * 2;  // bytes per mask tile (MT)
   // Q and dO tiles of a step (dswz layout) at 0 and TQ, the next step's at
   // 2 TQ and 3 TQ; bit 2 TQ of the offsets picks a step's buffer. Q serves the
   // row reads of S = Q K^T and the transposing reads of the Q^T operand of
@@ -316,6 +364,7 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
   __shared__ __align__(1024) uint8_t qd[4 * TQ];
   __shared__ __align__(16) float lses[2][BQ];  // LSE * log2(e) of the step's queries
   __shared__ __align__(16) float dels[2][BQ];
+  __shared__ __align__(1024) uint8_t mt[MT ? 2 * TMQ : 16];
 
   const int tid = (int)threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
@@ -389,12 +438,23 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
   const uint32_t qdo = dma_lane_off<D>(lane, swave, p.sq_s * 2);
   const uint32_t ddo = dma_lane_off<D>(lane, swave, p.sdo_s * 2);
   const uint32_t qd_lds = lds_addr(qd);
+  const uint32_t mt_lds = lds_addr(mt);
+  const uint32_t mdo = dma_lane_off<kAttnBwdBk>(lane, swave, p.sm_q * 2);
   auto fetch = [&](uint32_t h, int qt, int buf) {
     const int rows = min(Sq - qt, BQ);
     const u32x4 qr = rows_desc(qsrc + ((int64_t)h * p.sq_h + (int64_t)qt * p.sq_s) * 2, rows, p.sq_s * 2, D * 2);
     const u32x4 dr = rows_desc(dsrc + ((int64_t)h * p.sdo_h + (int64_t)qt * p.sdo_s) * 2, rows, p.sdo_s * 2, D * 2);
     dma_tile_asm<D, BQ>(qr, qdo, p.sq_s * 2, swave, qd_lds + buf * 2 * TQ);
     dma_tile_asm<D, BQ>(dr, ddo, p.sdo_s * 2, swave, qd_lds + buf * 2 * TQ + TQ);
+    if constexpr (MT) {
+      // The step's query rows, keys k0 .. k0 + 127 (past Sk: the next row's
+      // first values, or zeros past the last row; those scores are excluded).
+      u32x4 mr = rows_desc(p.mask + ((int64_t)b * p.sm_b + (int64_t)h * p.sm_h + (int64_t)qt * p.sm_q + k0) * 2,
+                           rows, p.sm_q * 2, min(Sk - k0, kAttnBwdBk) * 2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mr[j] = __builtin_amdgcn_readfirstlane(mr[j]);
+      dma_tile_asm<kAttnBwdBk, BQ>(mr, mdo, p.sm_q * 2, swave, mt_lds + buf * TMQ);
+    }
     const auto sr = rows_rsrc(reinterpret_cast<const char*>(fssrc + ((int64_t)b * p.H + h) * Sq + qt),
                               rows, 4, 4);
     sreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, (int)soff, 0, 0));
@@ -409,6 +469,17 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
   uint32_t rao = (uint32_t)dtile_off<D>(c, g);
   uint32_t tao =
       (uint32_t)(dtile_off<D>(4 * g + ((c & 15) >> 2), 2 * ((c >> 4) & 1) + ((c >> 1) & 1)) + 8 * (c & 1));
+  // Mask tile (MT): transposing read m hands the lane its key's values for
+  // queries 8 m + 4 g + 0..3 of the step (registers 4 m .. 4 m + 3): the lane
+  // addresses query 8 m + 4 g + (c % 16) / 4, keys 32 w + 16 ((c / 16) % 2)
+  // + 4 (c % 4) .. + 3, at mao[m % 2] + 16 (m / 2) rows (dswz depends on
+  // bits 0-3 of the row, which 16 rows leave).
+  uint32_t mao[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+    mao[hf] = (uint32_t)(dtile_off<kAttnBwdBk>(8 * hf + 4 * g + ((c & 15) >> 2),
+                                               4 * wave + 2 * ((c >> 4) & 1) + ((c >> 1) & 1)) +
+                         8 * (c & 1));
 
   if (any && qstart < Sq) {
     // One sequence of (query head, query tile) steps over the heads of the
@@ -450,7 +521,17 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
         // mask (values of excluded scores are never used), so that the wait
         // for them is counted exactly instead of for every load in flight.
         uint32_t mvk[16];
-        if constexpr (KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL) {
+        if constexpr (MT) {
+          const uint8_t* const mtb = mt + buf * TMQ;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const u32x2 t = lds_read_tr(mtb + mao[m & 1] + 16 * (m >> 1) * kAttnBwdBk * 2);
+            mvk[4 * m + 0] = t.x & 0xffffu;
+            mvk[4 * m + 1] = t.x >> 16;
+            mvk[4 * m + 2] = t.y & 0xffffu;
+            mvk[4 * m + 3] = t.y >> 16;
+          }
+        } else if constexpr (KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL) {
           const int kjc = min(kj, Sk - 1);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -636,15 +717,15 @@ template <int KIND, int PASS>
 constexpr int dkdv_waves() {
   return PASS == 0 && KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL ? 3 : 2;
 }
-template <bool BF16, int D, int KIND, int PASS, int BQ>
+template <bool BF16, int D, int KIND, int PASS, int BQ, bool MT>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(dkdv_waves<KIND, PASS>(), dkdv_waves<KIND, PASS>())))
 attn_bwd_dkdv_kernel(AttnBwdParams p) {
-  dkdv_body<BF16, D, KIND, PASS, BQ>(p);
+  dkdv_body<BF16, D, KIND, PASS, BQ, MT>(p);
 }
-template <bool BF16, int D, int KIND, int BQ>
+template <bool BF16, int D, int KIND, int BQ, bool MT>
 __global__ void __launch_bounds__(256) attn_bwd_dkdv_both_kernel(AttnBwdParams p) {
-  dkdv_body<BF16, D, KIND, 2, BQ>(p);
+  dkdv_body<BF16, D, KIND, 2, BQ, MT>(p);
 }
 
 // Queries per dK/dV step. Two 32-query blocks per loaded tile halve the
@@ -658,34 +739,48 @@ constexpr int dkdv_bq() {
   return (KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL || D == 128) ? 32 : 64;
 }
 
+template <bool BF16, int D, int KIND, bool MT>
+hipError_t launch_dkdv(const AttnBwdParams& p, hipStream_t st) {
+  const dim3 block(256);
+  const dim3 gk(p.Hk * p.B * ((p.Sk + kAttnBwdBk - 1) / kAttnBwdBk));
+  // D = 128: two passes at two wavefronts per SIMD, measured faster than
+  // both gradients in one pass at one (fp16 [4,32,4096,128] causal
+  // backward 4.72 against 5.28 ms; not causal 6.02 against 6.66 ms).
+  constexpr int BQ = dkdv_bq<KIND, D>();
+  if constexpr (D == 128) {
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<BF16, D, KIND, 0, BQ, MT>), gk, block, 0, st, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<BF16, D, KIND, 1, BQ, MT>), gk, block, 0, st, p);
+  } else {
+    hipLaunchKernelGGL((attn_bwd_dkdv_both_kernel<BF16, D, KIND, BQ, MT>), gk, block, 0, st, p);
+  }
+  return hipGetLastError();
+}
+
 template <bool BF16, int D, int KIND>
 hipError_t launch_bwd_kind(const AttnBwdParams& p, hipStream_t st) {
   const dim3 block(256);
   if (p.Sq > 0) {
     const dim3 gq(p.H * p.B * ((p.Sq + kAttnBq - 1) / kAttnBq));
-    if constexpr (KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL) {
-      if (p.mask_vec) hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, KIND, true>), gq, block, 0, st, p);
-      else hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, KIND, false>), gq, block, 0, st, p);
+    if constexpr (KIND == ATTN_MASK_ADD) {
+      if (p.mask_tile) hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, KIND, 2>), gq, block, 0, st, p);
+      else if (p.mask_vec) hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, KIND, 1>), gq, block, 0, st, p);
+      else hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, KIND, 0>), gq, block, 0, st, p);
+    } else if constexpr (KIND == ATTN_MASK_BOOL) {
+      if (p.mask_vec) hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, KIND, 1>), gq, block, 0, st, p);
+      else hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, KIND, 0>), gq, block, 0, st, p);
     } else {
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, KIND, false>), gq, block, 0, st, p);
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, KIND, 0>), gq, block, 0, st, p);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (p.Sk > 0) {
-    const dim3 gk(p.Hk * p.B * ((p.Sk + kAttnBwdBk - 1) / kAttnBwdBk));
-    // D = 128: two passes at two wavefronts per SIMD, measured faster than
-    // both gradients in one pass at one (fp16 [4,32,4096,128] causal
-    // backward 4.72 against 5.28 ms; not causal 6.02 against 6.66 ms).
-    constexpr int BQ = dkdv_bq<KIND, D>();
-    if constexpr (D == 128) {
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<BF16, D, KIND, 0, BQ>), gk, block, 0, st, p);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<BF16, D, KIND, 1, BQ>), gk, block, 0, st, p);
-    } else {
-      hipLaunchKernelGGL((attn_bwd_dkdv_both_kernel<BF16, D, KIND, BQ>), gk, block, 0, st, p);
+    if constexpr (KIND == ATTN_MASK_ADD) {
+      if (p.mask_tile) return launch_dkdv<BF16, D, KIND, true>(p, st);
     }
+    return launch_dkdv<BF16, D, KIND, false>(p, st);
   }
   return hipGetLastError();
 }
