@@ -709,17 +709,18 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
 }
 
 // Entry points: the single passes at two wavefronts per SIMD, except the dV
-// pass without a per-score mask, which fits three (167 VGPRs, no spills; 1-3 %
-// faster than two; with a mask its values would spill there); both gradients
-// together with the registers the compiler needs (D = 64 fits two wavefronts
-// per SIMD as it is).
-template <int KIND, int PASS>
+// pass without a per-score mask or with mask tiles, which fits three (149-168
+// VGPRs, no spills; 1-3 % faster than two without a mask, 3 % with mask
+// tiles; with mask values from global memory they would spill there); both
+// gradients together with the registers the compiler needs (D = 64 fits two
+// wavefronts per SIMD as it is).
+template <int KIND, int PASS, bool MT>
 constexpr int dkdv_waves() {
-  return PASS == 0 && KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL ? 3 : 2;
+  return PASS == 0 && ((KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL) || MT) ? 3 : 2;
 }
 template <bool BF16, int D, int KIND, int PASS, int BQ, bool MT>
 __global__ void __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(dkdv_waves<KIND, PASS>(), dkdv_waves<KIND, PASS>())))
+__attribute__((amdgpu_waves_per_eu(dkdv_waves<KIND, PASS, MT>(), dkdv_waves<KIND, PASS, MT>())))
 attn_bwd_dkdv_kernel(AttnBwdParams p) {
   dkdv_body<BF16, D, KIND, PASS, BQ, MT>(p);
 }
