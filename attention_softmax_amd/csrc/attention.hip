@@ -80,17 +80,18 @@ attn_fwd_kernel(AttnParams p) {
   // Without a per-score mask, and with additive mask tiles, the K / V loads
   // are issued from inline assembly, spread over the tile's S products
   // (below).
-  constexpr bool kSpread = !MASKED || MV == 2;
+  constexpr bool kSpread = !MASKED || MV >= 2;
   static_assert(MV == 0 || MASKED, "mask runs need a per-score mask");
   static_assert(MV != 2 || KIND == ATTN_MASK_ADD, "mask tiles of 16-bit values");
+  static_assert(MV != 3 || KIND == ATTN_MASK_BOOL, "mask tiles of bytes");
   constexpr int BK = kAttnBk;
   constexpr int TB = BK * D * 2;  // bytes per tile
-  constexpr int TM = kAttnBq * BK * 2;  // bytes per mask tile (MV == 2)
+  constexpr int TM = kAttnBq * BK * (MV == 3 ? 1 : 2);  // bytes per mask tile (MV >= 2)
   __shared__ __align__(1024) uint8_t ks0[TB];
   __shared__ __align__(1024) uint8_t ks1[TB];
   __shared__ __align__(1024) uint8_t vs0[TB];
   __shared__ __align__(1024) uint8_t vs1[TB];
-  __shared__ __align__(1024) uint8_t ms[MV == 2 ? TM : 16];
+  __shared__ __align__(1024) uint8_t ms[MV >= 2 ? TM : 16];
 
   const int tid = (int)threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
@@ -178,21 +179,24 @@ attn_fwd_kernel(AttnParams p) {
     kr = rows_desc(kbase + (int64_t)kt * p.sk_s * 2, rows, p.sk_s * 2, D * 2);
     vr = rows_desc(vbase + (int64_t)kt * p.sv_s * 2, rows, p.sv_s * 2, D * 2);
   };
-  // Mask tiles (MV == 2): the workgroup's query rows (past Sq: none, or the
+  // Mask tiles (MV >= 2): the workgroup's query rows (past Sq: none, or the
   // one broadcast row) through one buffer range ending at the last row's last
   // key; keys past Sk of the other rows read the next row's first values,
-  // whose scores are excluded.
+  // whose scores are excluded. Rows of 64 values: 128 bytes (additive, the
+  // dswz layout of D = 64) or 64 (boolean, that of D = 32).
+  constexpr int MB = MV == 3 ? 1 : 2;  // bytes per mask value
+  constexpr int MD = 32 * MB;          // the tile's dswz layout
   const int64_t mtile = (int64_t)b * p.sm_b + (int64_t)h * p.sm_h + (int64_t)q0 * p.sm_q;
   const int mrows = min(Sq - q0, kAttnBq);
-  const uint32_t mdo = dma_lane_off<64>(lane, wave_u, p.sm_q * 2);
+  const uint32_t mdo = dma_lane_off<MD>(lane, wave_u, p.sm_q * MB);
   auto dma_mask = [&](int kt) {
     const int rows = min(Sk - kt, BK);
-    u32x4 mr = rows_desc(p.mask + (mtile + kt) * 2, rows > 0 ? mrows : 0, p.sm_q * 2, max(rows, 0) * 2);
+    u32x4 mr = rows_desc(p.mask + (mtile + kt) * MB, rows > 0 ? mrows : 0, p.sm_q * MB, max(rows, 0) * MB);
     // (Uniform words, which the compiler kept in vector registers here; the
     // inline assembly takes them in scalar registers.)
 #pragma unroll
     for (int j = 0; j < 4; ++j) mr[j] = __builtin_amdgcn_readfirstlane(mr[j]);
-    dma_tile_asm<64, kAttnBq>(mr, mdo, p.sm_q * 2, wave_u, lds_addr(ms));
+    dma_tile_asm<MD, kAttnBq>(mr, mdo, p.sm_q * MB, wave_u, lds_addr(ms));
   };
   if (kend > 0) {
     if constexpr (kSpread) {
@@ -203,7 +207,7 @@ attn_fwd_kernel(AttnParams p) {
     } else {
       dma(0, BoolC<false>{});
     }
-    if constexpr (MV == 2) dma_mask(0);
+    if constexpr (MV >= 2) dma_mask(0);
   }
   u32x2 mv[8], mv_next[8];  // mask runs of this tile and (MV == 1) of the next
   if constexpr (MV == 1) load_mask_runs<KIND>(p.mask, mrow_c, 0, g, Sk, mv);
@@ -244,6 +248,14 @@ attn_fwd_kernel(AttnParams p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         mv[i] = *reinterpret_cast<const u32x2*>(ms + dtile_off<64>(wave * 32 + c, 4 * (i >> 2) + (i & 3)) + 8 * g);
+    } else if constexpr (MV == 3) {
+      // Boolean runs: run i is the 4 bytes at 8 i + 4 g, in chunk i / 2.
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint8_t* ch = ms + dtile_off<32>(wave * 32 + c, j);
+        mv[2 * j] = u32x2{*reinterpret_cast<const uint32_t*>(ch + 4 * g), 0u};
+        mv[2 * j + 1] = u32x2{*reinterpret_cast<const uint32_t*>(ch + 8 + 4 * g), 0u};
+      }
     } else if constexpr (MV == 1) {
       // (Runs past the last key read at the row's last run: never used.)
       load_mask_runs<KIND>(p.mask, mrow_c, kt + BK, g, Sk, mv_next);
@@ -315,7 +327,7 @@ attn_fwd_kernel(AttnParams p) {
     // faster than the scheduler's own order, measured before the spread loads
     // above; not with mask runs, whose loads share the region).
     if constexpr (MV == 0 && MASKED) pin_reads_ahead<2 * (D / 16), 10, 1>();
-    if constexpr (MV == 2) {
+    if constexpr (MV >= 2) {
       // Every wavefront has its runs (LDS reads complete, then the barrier:
       // a plain one, which unlike __syncthreads does not wait for the K / V
       // loads in flight); the next tile's mask values may overwrite them.
@@ -521,7 +533,8 @@ hipError_t launch_kind(const AttnParams& p, hipStream_t st) {
       else hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_ADD, 0>), grid, block, 0, st, p);
       break;
     case ATTN_MASK_BOOL:
-      if (p.mask_vec) hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_BOOL, 1>), grid, block, 0, st, p);
+      if (p.mask_tile) hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_BOOL, 3>), grid, block, 0, st, p);
+      else if (p.mask_vec) hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_BOOL, 1>), grid, block, 0, st, p);
       else hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_BOOL, 0>), grid, block, 0, st, p);
       break;
     case ATTN_MASK_LEN: hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, ATTN_MASK_LEN, 0>), grid, block, 0, st, p); break;

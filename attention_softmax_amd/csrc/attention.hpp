@@ -185,9 +185,13 @@ __device__ inline __attribute__((always_inline)) void pin_reads_ahead() {
 // of them) and transposing 8-byte reads (a 32-lane phase reads 4 consecutive
 // rows x 4 consecutive chunks, so bits 2-3 of dswz -- bit 2 for D = 64 --
 // must differ over every aligned 4 rows).
+// (D = 32 is the layout of 64-byte rows of bytes, four chunks: a boolean mask
+// tile; its reads are row reads.)
 template <int D>
 __host__ __device__ constexpr int dswz(int r) {
-  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  return D == 128  ? (((r & 3) << 2) | ((r >> 2) & 3))
+         : D == 64 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3))
+                   : ((r >> 2) & 3);
 }
 // Byte offset of logical chunk ch of row r in such a tile.
 template <int D>
@@ -218,7 +222,8 @@ constexpr bool dswz_conflict_free() {
     }
   return true;
 }
-static_assert(dswz_conflict_free<64>() && dswz_conflict_free<128>(), "dswz must spread both read patterns");
+static_assert(dswz_conflict_free<32>() && dswz_conflict_free<64>() && dswz_conflict_free<128>(),
+              "dswz must spread both read patterns");
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define SMS_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))

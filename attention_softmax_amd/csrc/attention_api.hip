@@ -29,6 +29,15 @@ sms_status check_strides(const int64_t st[4]) {
 
 bool aligned_to(const void* p, int bytes) { return ((uintptr_t)p % (uintptr_t)bytes) == 0; }
 
+// Per-score masks whose rows start on 16-byte lines (8 additive values or 16
+// boolean bytes; mask strides are multiples of Sk) go through LDS in tiles of
+// 128 rows, whose byte range must fit 31 bits.
+bool tile_mask(int kind, const void* mask, int64_t Sk) {
+  if (kind == sms::ATTN_MASK_ADD) return Sk % 8 == 0 && aligned_to(mask, 16) && 128 * Sk * 2 < INT32_MAX;
+  if (kind == sms::ATTN_MASK_BOOL) return Sk % 16 == 0 && aligned_to(mask, 16) && 128 * Sk < INT32_MAX;
+  return false;
+}
+
 // Largest key / value row stride (elements): a tile of 64 rows is read
 // through one buffer range, whose byte count must fit 31 bits.
 constexpr int64_t kMaxRowStride = int64_t(1) << 24;
@@ -123,10 +132,9 @@ sms_status sms_attention_forward(const void* q, const int64_t q_strides[4], cons
   // keys stay inside a row: vector mask loads.
   p.mask_vec = (p.mask_kind == sms::ATTN_MASK_ADD || p.mask_kind == sms::ATTN_MASK_BOOL) &&
                Sk % 4 == 0 && aligned_to(mask, p.mask_kind == sms::ATTN_MASK_ADD ? 8 : 4);
-  // Additive mask rows on 16-byte lines (8 values), and a tile of 128 rows
-  // within a 31-bit byte range.
-  p.mask_tile = p.mask_kind == sms::ATTN_MASK_ADD && Sk % 8 == 0 && aligned_to(mask, 16) &&
-                128 * Sk * 2 < INT32_MAX;
+  // Mask rows on 16-byte lines (8 additive values or 16 boolean bytes), and a
+  // tile of 128 rows within a 31-bit byte range.
+  p.mask_tile = tile_mask(p.mask_kind, mask, Sk);
   const hipError_t e = sms_attn_launch(&p, (int)dtype, (int)D, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SMS_OK : SMS_ERR_HIP;
 }
@@ -228,9 +236,8 @@ sms_status sms_attention_backward(const void* q, const int64_t q_strides[4], con
   // keys stay inside a row: vector mask loads.
   p.mask_vec = (p.mask_kind == sms::ATTN_MASK_ADD || p.mask_kind == sms::ATTN_MASK_BOOL) &&
                Sk % 4 == 0 && aligned_to(mask, p.mask_kind == sms::ATTN_MASK_ADD ? 8 : 4);
-  // Additive mask tiles in LDS, as in the forward.
-  p.mask_tile = p.mask_kind == sms::ATTN_MASK_ADD && Sk % 8 == 0 && aligned_to(mask, 16) &&
-                128 * Sk * 2 < INT32_MAX;
+  // Mask tiles in LDS, as in the forward.
+  p.mask_tile = tile_mask(p.mask_kind, mask, Sk);
   const hipError_t e =
       sms_attn_bwd_launch(&p, (int)dtype, (int)D, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SMS_OK : SMS_ERR_HIP;

@@ -41,26 +41,29 @@ using namespace attn;
 // dQ^T += K^T dS^T; V the row reads of dP^T = V dO^T.
 // Three wavefronts per SIMD for D = 64 (140-146 VGPRs: the backward 1.5-3 %
 // faster than at two on fp16 [8,32,2048,64] and [4,32,4096,64]), two for D = 128.
-// Per-score masks, MV: 2 (additive masks whose rows start on 16-byte lines):
-// the tile's mask values for the workgroup's 128 queries come into one LDS
-// buffer (a 128 x 64 tile, the dswz layout of D = 64), each lane reads its runs
-// at the start of the tile, and after a second barrier (all runs read) the
-// next tile's values go out into it, as in the forward; 1: the runs are
-// loaded from global memory at the start of the tile; 0: each value where it
-// is used.
+// Per-score masks, MV: 2 / 3 (additive / boolean masks whose rows start on
+// 16-byte lines): the tile's mask values for the workgroup's 128 queries come
+// into one LDS buffer (a 128 x 64 tile, the dswz layout of D = 64 / 32), each
+// lane reads its runs at the start of the tile, and after a second barrier
+// (all runs read) the next tile's values go out into it, as in the forward;
+// 1: the runs are loaded from global memory at the start of the tile; 0: each
+// value where it is used.
 template <bool BF16, int D, int KIND, int MV>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2, D == 64 ? 3 : 2)))
 attn_bwd_dq_kernel(AttnBwdParams p) {
   static_assert(MV == 0 || KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL, "mask runs need a per-score mask");
   static_assert(MV != 2 || KIND == ATTN_MASK_ADD, "mask tiles of 16-bit values");
+  static_assert(MV != 3 || KIND == ATTN_MASK_BOOL, "mask tiles of bytes");
   constexpr int BK = kAttnBk;
   constexpr int TB = BK * D * 2;  // bytes per tile
-  constexpr int TM = kAttnBq * BK * 2;  // bytes per mask tile (MV == 2)
+  constexpr int MB = MV == 3 ? 1 : 2;  // bytes per mask value
+  constexpr int MD = 32 * MB;          // the mask tile's dswz layout
+  constexpr int TM = kAttnBq * BK * MB;  // bytes per mask tile (MV >= 2)
   // K tiles at 0 and TB, V tiles at 2 TB and 3 TB; bit TB of the offsets
   // picks a tile's buffer and flips every tile.
   __shared__ __align__(1024) uint8_t kv[4 * TB];
-  __shared__ __align__(1024) uint8_t ms[MV == 2 ? TM : 16];
+  __shared__ __align__(1024) uint8_t ms[MV >= 2 ? TM : 16];
 
   const int tid = (int)threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
@@ -145,22 +148,22 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
     dma_tile_asm<D, BK>(kr, kdo, p.sk_s * 2, wave_u, kv_lds + buf * TB);
     dma_tile_asm<D, BK>(vr, vdo, p.sv_s * 2, wave_u, kv_lds + (2 + buf) * TB);
   };
-  // Mask tiles (MV == 2): the workgroup's query rows through one buffer range
+  // Mask tiles (MV >= 2): the workgroup's query rows through one buffer range
   // ending at the last row's last key; keys past Sk of the other rows read
   // the next row's first values, whose scores are excluded.
-  const uint32_t mdo = dma_lane_off<64>(lane, wave_u, p.sm_q * 2);
+  const uint32_t mdo = dma_lane_off<MD>(lane, wave_u, p.sm_q * MB);
   const int mrows = min(Sq - q0, kAttnBq);
   auto dma_mask = [&](int kt) {
     const int rows = min(Sk - kt, BK);
-    u32x4 mr = rows_desc(p.mask + ((int64_t)b * p.sm_b + (int64_t)h * p.sm_h + (int64_t)q0 * p.sm_q + kt) * 2,
-                         rows > 0 ? mrows : 0, p.sm_q * 2, max(rows, 0) * 2);
+    u32x4 mr = rows_desc(p.mask + ((int64_t)b * p.sm_b + (int64_t)h * p.sm_h + (int64_t)q0 * p.sm_q + kt) * MB,
+                         rows > 0 ? mrows : 0, p.sm_q * MB, max(rows, 0) * MB);
 #pragma unroll
     for (int j = 0; j < 4; ++j) mr[j] = __builtin_amdgcn_readfirstlane(mr[j]);
-    dma_tile_asm<64, kAttnBq>(mr, mdo, p.sm_q * 2, wave_u, lds_addr(ms));
+    dma_tile_asm<MD, kAttnBq>(mr, mdo, p.sm_q * MB, wave_u, lds_addr(ms));
   };
   if (kend > 0) {
     dma(0, 0);
-    if constexpr (MV == 2) dma_mask(0);
+    if constexpr (MV >= 2) dma_mask(0);
   }
 
   // LDS byte offsets of this lane's reads. Row reads: row c (+ 32 kb),
@@ -190,6 +193,14 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         mv[i] = *reinterpret_cast<const u32x2*>(ms + dtile_off<64>(wave * 32 + c, 4 * (i >> 2) + (i & 3)) + 8 * g);
+    } else if constexpr (MV == 3) {
+      // Boolean runs: run i is the 4 bytes at 8 i + 4 g, in chunk i / 2.
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint8_t* ch = ms + dtile_off<32>(wave * 32 + c, j);
+        mv[2 * j] = u32x2{*reinterpret_cast<const uint32_t*>(ch + 4 * g), 0u};
+        mv[2 * j + 1] = u32x2{*reinterpret_cast<const uint32_t*>(ch + 8 + 4 * g), 0u};
+      }
     } else if constexpr (MV == 1) {
       load_mask_runs<KIND>(p.mask, mrow_c, kt, g, Sk, mv);
       __builtin_amdgcn_sched_barrier(0);  // keep them ahead of the loads
@@ -221,7 +232,7 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
         dpacc = mfma_32x32x16<BF16>(av, df[s], dpacc);
       }
       pin_reads_ahead<2 * (D / 16), 4, 1>();  // K / V reads four products ahead
-      if constexpr (MV == 2) {
+      if constexpr (MV >= 2) {
         if (kb == 0) {
           // Every wavefront has its runs; the next tile's mask values may
           // overwrite them (a plain barrier: it does not wait for the loads).
@@ -769,7 +780,8 @@ hipError_t launch_bwd_kind(const AttnBwdParams& p, hipStream_t st) {
       else if (p.mask_vec) hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, KIND, 1>), gq, block, 0, st, p);
       else hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, KIND, 0>), gq, block, 0, st, p);
     } else if constexpr (KIND == ATTN_MASK_BOOL) {
-      if (p.mask_vec) hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, KIND, 1>), gq, block, 0, st, p);
+      if (p.mask_tile) hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, KIND, 3>), gq, block, 0, st, p);
+      else if (p.mask_vec) hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, KIND, 1>), gq, block, 0, st, p);
       else hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, KIND, 0>), gq, block, 0, st, p);
     } else {
       hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, KIND, 0>), gq, block, 0, st, p);

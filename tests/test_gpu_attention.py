@@ -64,8 +64,10 @@ def check(q, k, v, mask, mode, kind, scale, causal, what):
 
 # (300, 100): bottom-right causal leaves the first 128-query tile without any key.
 # (200, 136): additive masks as LDS tiles (Sk % 8 == 0) over two query tiles and
-# a last key tile of 8 keys.
-SHAPES = [(1, 1), (37, 63), (128, 64), (129, 65), (200, 300), (64, 1000), (300, 100), (200, 136)]
+# a last key tile of 8 keys. (200, 144): boolean masks as LDS tiles too
+# (Sk % 16 == 0), a last key tile of 16 keys.
+SHAPES = [(1, 1), (37, 63), (128, 64), (129, 65), (200, 300), (64, 1000), (300, 100), (200, 136),
+          (200, 144)]
 MASKS = [("none", "none"), ("sq_sk", "additive"), ("b_sq_sk", "neginf"), ("b_1_sk", "neginf"),
          ("full", "additive"), ("b_sq_sk", "bool"), ("key_lengths", "lengths")]
 
