@@ -42,7 +42,7 @@ using namespace attn;
 // consecutive keys). The buffers are separate LDS objects and the tiles go
 // in pairs, so that every read has a fixed buffer and the read offsets are
 // loop-invariant registers plus immediates. Without a per-score mask, and
-// with mask tiles (MV 2, below), the loads are issued from inline assembly
+// with mask tiles (MV 2 and 3, below), the loads are issued from inline assembly
 // (dma_one), which the compiler does not see (the kernel waits for them
 // itself before each barrier), one after each k-step of the tile's S
 // products instead of all together after the barrier: 2 % faster without a
@@ -52,13 +52,15 @@ using namespace attn;
 // since they fill the other buffer object, the compiler knows that the reads
 // do not touch it and inserts no wait for them.
 //
-// Per-score masks (additive / boolean), MV: 2 (additive masks whose rows
-// start on 16-byte lines): the tile's mask values for the workgroup's 128
-// queries (a 128 x 64 tile of 128-byte rows, the dswz layout of D = 64) come
-// into one LDS buffer by loads of the same kind; each lane reads its runs of 4 keys
-// from it at the start of the tile, and after a second barrier in the middle
-// of the tile (all runs read) the next tile's mask values go out into it;
-// 1 (mask rows on 4 elements and Sk % 4 == 0): the runs are loaded from
+// Per-score masks (additive / boolean), MV: 2 / 3 (additive / boolean masks
+// whose rows start on 16-byte lines): the tile's mask values for the
+// workgroup's 128 queries (a 128 x 64 tile of 128-byte rows, the dswz layout
+// of D = 64, or of 64-byte rows, that of D = 32) come into one LDS buffer by
+// loads of the same kind; each lane reads its runs of 4 keys from it at the
+// start of the tile, and after a second barrier in the middle of the tile
+// (all runs read) the next tile's mask values go out into it (boolean tiles
+// against runs from global memory: 13-25 % faster); 1 (mask rows on 4
+// elements and Sk % 4 == 0): the runs are loaded from
 // global memory one tile ahead (load_mask_runs), before the next tile's K and
 // V, so that they have landed by the barrier that starts their tile; 0: each
 // mask value is read where it is used, and the next tile's loads go out after
@@ -77,9 +79,8 @@ __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(fwd_waves<D, KIND, MV>(), fwd_waves<D, KIND, MV>())))
 attn_fwd_kernel(AttnParams p) {
   constexpr bool MASKED = KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL;
-  // Without a per-score mask, and with additive mask tiles, the K / V loads
-  // are issued from inline assembly, spread over the tile's S products
-  // (below).
+  // Without a per-score mask, and with mask tiles, the K / V loads are
+  // issued from inline assembly, spread over the tile's S products (below).
   constexpr bool kSpread = !MASKED || MV >= 2;
   static_assert(MV == 0 || MASKED, "mask runs need a per-score mask");
   static_assert(MV != 2 || KIND == ATTN_MASK_ADD, "mask tiles of 16-bit values");
