@@ -354,20 +354,23 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
 // registers (one wavefront per SIMD), so there PASS 0 (dV alone: S, P) and
 // PASS 1 (dK alone: S, dP, dS) run as two launches, each at two wavefronts
 // per SIMD, recomputing S in both.
-// MT: additive mask tiles in LDS (mask rows on 16-byte lines): the step's
-// BQ x 128 values (the dswz layout of D = 128, double-buffered) come with its
-// Q and dO tiles, and each lane takes its key's values for 4 consecutive
-// queries per transposing read, as the forward reads V.
+// MT: mask tiles in LDS (mask rows on 16-byte lines): the step's BQ x 128
+// values (additive: the dswz layout of D = 128; boolean: that of D = 64;
+// double-buffered) come with its Q and dO tiles. For additive masks each lane
+// takes its key's values for 4 consecutive queries per transposing read, as
+// the forward reads V; for boolean ones it reads its 16 bytes one by one.
 template <bool BF16, int D, int KIND, int PASS, int BQ, bool MT>
 __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdParams& p) {
   constexpr bool kDV = PASS != 1, kDK = PASS != 0;
   static_assert(BQ == 32 || BQ == 64, "query tiles of one or two 32-query blocks");
   static_assert(BQ == 32 || (KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL),
                 "per-score masks are loaded for one 32-query block per step");
-  static_assert(!MT || KIND == ATTN_MASK_ADD, "mask tiles of 16-bit values");
+  static_assert(!MT || KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL, "mask tiles of a per-score mask");
   constexpr int NSUB = BQ / 32;
   constexpr int TQ = BQ * D * 2;  // bytes per Q or dO tile
-  constexpr int TMQ = BQ * kAttnBwdBk * 2;  // bytes per mask tile (MT)
+  constexpr int MB = KIND == ATTN_MASK_BOOL ? 1 : 2;  // bytes per mask value
+  constexpr int MD = 64 * MB;                            // the mask tile's dswz layout
+  constexpr int TMQ = BQ * kAttnBwdBk * MB;  // bytes per mask tile (MT)
   // Q and dO tiles of a step (dswz layout) at 0 and TQ, the next step's at
   // 2 TQ and 3 TQ; bit 2 TQ of the offsets picks a step's buffer. Q serves the
   // row reads of S = Q K^T and the transposing reads of the Q^T operand of
@@ -450,7 +453,7 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
   const uint32_t ddo = dma_lane_off<D>(lane, swave, p.sdo_s * 2);
   const uint32_t qd_lds = lds_addr(qd);
   const uint32_t mt_lds = lds_addr(mt);
-  const uint32_t mdo = dma_lane_off<kAttnBwdBk>(lane, swave, p.sm_q * 2);
+  const uint32_t mdo = dma_lane_off<MD>(lane, swave, p.sm_q * MB);
   auto fetch = [&](uint32_t h, int qt, int buf) {
     const int rows = min(Sq - qt, BQ);
     const u32x4 qr = rows_desc(qsrc + ((int64_t)h * p.sq_h + (int64_t)qt * p.sq_s) * 2, rows, p.sq_s * 2, D * 2);
@@ -460,11 +463,11 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
     if constexpr (MT) {
       // The step's query rows, keys k0 .. k0 + 127 (past Sk: the next row's
       // first values, or zeros past the last row; those scores are excluded).
-      u32x4 mr = rows_desc(p.mask + ((int64_t)b * p.sm_b + (int64_t)h * p.sm_h + (int64_t)qt * p.sm_q + k0) * 2,
-                           rows, p.sm_q * 2, min(Sk - k0, kAttnBwdBk) * 2);
+      u32x4 mr = rows_desc(p.mask + ((int64_t)b * p.sm_b + (int64_t)h * p.sm_h + (int64_t)qt * p.sm_q + k0) * MB,
+                           rows, p.sm_q * MB, min(Sk - k0, kAttnBwdBk) * MB);
 #pragma unroll
       for (int j = 0; j < 4; ++j) mr[j] = __builtin_amdgcn_readfirstlane(mr[j]);
-      dma_tile_asm<kAttnBwdBk, BQ>(mr, mdo, p.sm_q * 2, swave, mt_lds + buf * TMQ);
+      dma_tile_asm<MD, BQ>(mr, mdo, p.sm_q * MB, swave, mt_lds + buf * TMQ);
     }
     const auto sr = rows_rsrc(reinterpret_cast<const char*>(fssrc + ((int64_t)b * p.H + h) * Sq + qt),
                               rows, 4, 4);
@@ -532,7 +535,14 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
         // mask (values of excluded scores are never used), so that the wait
         // for them is counted exactly instead of for every load in flight.
         uint32_t mvk[16];
-        if constexpr (MT) {
+        if constexpr (MT && KIND == ATTN_MASK_BOOL) {
+          // One byte per query: query 8 (r / 4) + 4 g + r % 4, the lane's key
+          // 32 w + c (chunk 2 w + c / 16, byte c % 16).
+          const uint8_t* const mtb = mt + buf * TMQ;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            mvk[r] = mtb[dtile_off<64>(8 * (r >> 2) + 4 * g + (r & 3), 2 * wave + (c >> 4)) + (c & 15)];
+        } else if constexpr (MT) {
           const uint8_t* const mtb = mt + buf * TMQ;
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
@@ -720,14 +730,15 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
 }
 
 // Entry points: the single passes at two wavefronts per SIMD, except the dV
-// pass without a per-score mask or with mask tiles, which fits three (149-168
-// VGPRs, no spills; 1-3 % faster than two without a mask, 3 % with mask
-// tiles; with mask values from global memory they would spill there); both
+// pass without a per-score mask or with additive mask tiles, which fits three
+// (149-168 VGPRs, no spills; 1-3 % faster than two without a mask, 3 % with
+// mask tiles; with mask values from global memory, or the boolean tile's
+// byte reads, they would spill there); both
 // gradients together with the registers the compiler needs (D = 64 fits two
 // wavefronts per SIMD as it is).
 template <int KIND, int PASS, bool MT>
 constexpr int dkdv_waves() {
-  return PASS == 0 && ((KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL) || MT) ? 3 : 2;
+  return PASS == 0 && ((KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL) || (MT && KIND == ATTN_MASK_ADD)) ? 3 : 2;
 }
 template <bool BF16, int D, int KIND, int PASS, int BQ, bool MT>
 __global__ void __launch_bounds__(256)
@@ -790,7 +801,7 @@ hipError_t launch_bwd_kind(const AttnBwdParams& p, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   if (p.Sk > 0) {
-    if constexpr (KIND == ATTN_MASK_ADD) {
+    if constexpr (KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL) {
       if (p.mask_tile) return launch_dkdv<BF16, D, KIND, true>(p, st);
     }
     return launch_dkdv<BF16, D, KIND, false>(p, st);
