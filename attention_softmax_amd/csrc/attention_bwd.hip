@@ -351,9 +351,9 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
 // ------------------------------------------------------------ 2. dK, dV
 
 // PASS 2 accumulates dK and dV together; for D = 128 that needs more than 256
-// registers (one wavefront per SIMD), so there PASS 0 (dV alone: S, P) and
-// PASS 1 (dK alone: S, dP, dS) run as two launches, each at two wavefronts
-// per SIMD, recomputing S in both.
+// registers (one wavefront per SIMD). PASS 0 (dV alone: S, P) and PASS 1 (dK
+// alone: S, dP, dS) are the same work as two launches at two or three
+// wavefronts per SIMD, recomputing S in both (see launch_dkdv for which).
 // MT: mask tiles in LDS (mask rows on 16-byte lines): the step's BQ x 128
 // values (additive: the dswz layout of D = 128; boolean: that of D = 64;
 // double-buffered) come with its Q and dO tiles. For additive masks each lane
@@ -729,13 +729,13 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
     }
 }
 
-// Entry points: the single passes at two wavefronts per SIMD, except the dV
-// pass without a per-score mask or with additive mask tiles, which fits three
-// (149-168 VGPRs, no spills; 1-3 % faster than two without a mask, 3 % with
-// mask tiles; with mask values from global memory, or the boolean tile's
-// byte reads, they would spill there); both
-// gradients together with the registers the compiler needs (D = 64 fits two
-// wavefronts per SIMD as it is).
+// Entry points: the single passes (per-score masks, D = 128) at two
+// wavefronts per SIMD, except the dV pass with additive mask tiles, which
+// fits three (168 VGPRs, no spills; 3 % faster than two; with mask values
+// from global memory, or the boolean tile's byte reads, they would spill
+// there; without a mask, 149 VGPRs, 1-3 % faster); both gradients together
+// with the registers the compiler needs (one wavefront per SIMD for D = 128;
+// D = 64 fits two as it is).
 template <int KIND, int PASS, bool MT>
 constexpr int dkdv_waves() {
   return PASS == 0 && ((KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL) || (MT && KIND == ATTN_MASK_ADD)) ? 3 : 2;
@@ -762,22 +762,33 @@ constexpr int dkdv_bq() {
   return (KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL || D == 128) ? 32 : 64;
 }
 
+// Workgroups from which masked D = 128 dK / dV take two passes: two per CU of
+// the MI355X's 256.
+constexpr uint32_t kTwoPassGrid = 512;
+
 template <bool BF16, int D, int KIND, bool MT>
 hipError_t launch_dkdv(const AttnBwdParams& p, hipStream_t st) {
   const dim3 block(256);
   const dim3 gk(p.Hk * p.B * ((p.Sk + kAttnBwdBk - 1) / kAttnBwdBk));
-  // D = 128: two passes at two wavefronts per SIMD, measured faster than
-  // both gradients in one pass at one (fp16 [4,32,4096,128] causal
-  // backward 4.72 against 5.28 ms; not causal 6.02 against 6.66 ms).
+  // D = 128: both gradients in one pass at one wavefront per SIMD without a
+  // per-score mask (fp16 [4,32,4096,128] backward: causal 2200 against
+  // 2325 us for the two passes, not causal 3775 against 4070) and on grids
+  // of fewer than two workgroups per CU (bf16 [2,8,1000,128], 128
+  // workgroups: 79 against 103 us, 107 against 131 with an additive mask);
+  // with a per-score mask on larger grids the two passes (fp16
+  // [4,32,4096,128] with an additive mask, causal: 2784 against 2830-3000).
   constexpr int BQ = dkdv_bq<KIND, D>();
-  if constexpr (D == 128) {
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<BF16, D, KIND, 0, BQ, MT>), gk, block, 0, st, p);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<BF16, D, KIND, 1, BQ, MT>), gk, block, 0, st, p);
-  } else {
-    hipLaunchKernelGGL((attn_bwd_dkdv_both_kernel<BF16, D, KIND, BQ, MT>), gk, block, 0, st, p);
+  constexpr bool kPerScore = KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL;
+  if constexpr (D == 128 && kPerScore) {
+    if (gk.x >= kTwoPassGrid) {
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<BF16, D, KIND, 0, BQ, MT>), gk, block, 0, st, p);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<BF16, D, KIND, 1, BQ, MT>), gk, block, 0, st, p);
+      return hipGetLastError();
+    }
   }
+  hipLaunchKernelGGL((attn_bwd_dkdv_both_kernel<BF16, D, KIND, BQ, MT>), gk, block, 0, st, p);
   return hipGetLastError();
 }
 
