@@ -356,7 +356,8 @@ __device__ inline __attribute__((always_inline)) uint32_t mask_run_value(const u
 // hipErrorInvalidValue for anything else. Grid: H * B * ceil(Sq / 128).
 hipError_t sms_attn_launch(const sms::AttnParams* p, int dtype, int head_dim, hipStream_t st);
 
-// The backward's three launches (rowsum(dO * O) into the workspace; dQ; dK and
-// dV), same dtype / head-dim rules.
+// The backward's launches (dQ, which also forms rowsum(dO * O) in the
+// workspace; dK and dV in one launch, or two for D = 128 with a per-score mask
+// on larger grids), same dtype / head-dim rules.
 hipError_t sms_attn_bwd_launch(const sms::AttnBwdParams* p, int dtype, int head_dim,
                                hipStream_t st);

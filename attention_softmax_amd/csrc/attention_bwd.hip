@@ -5,8 +5,9 @@
 // points to; the softmax gradient itself is the lmnt.cn page's sec. 3.3 rule,
 // dS = P * (dP - rowsum(dP * P)), with rowsum(dP * P) = rowsum(dO * O)).
 //
-// Two launches (three for D = 128, where dK and dV take a pass each), all
-// deterministic (no atomics):
+// Two launches (three for D = 128 with a per-score mask on grids of 512 or
+// more dK/dV workgroups, where dK and dV take a pass each), all deterministic
+// (no atomics):
 //  1. dQ, one workgroup per 128 queries (query-stationary, as the forward);
 //     it first forms delta = rowsum(dO * O) of its queries in fp32 and stores
 //     it in the workspace for step 2. S^T = K Q^T and dP^T = V dO^T leave
@@ -753,13 +754,13 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_both_kernel(AttnBwdParams p
 
 // Queries per dK/dV step. Two 32-query blocks per loaded tile halve the
 // per-step work (barrier, LSE / delta) per product: measured 4 % faster for
-// D = 64 (fp16 [8,32,2048,64] backward, register-staged tiles); for D = 128
-// 1 % slower with the tiles loaded straight into LDS (the larger tiles fit
-// one fewer dV-pass workgroup per CU). Per-score masks keep one block (their
-// values take registers per block).
+// D = 64 (fp16 [8,32,2048,64] backward, register-staged tiles) and 2-4 % for
+// the one-pass D = 128 kernel (fp16 [4,32,4096,128] backward, causal 2195
+// against 2250 us). Per-score masks keep one block (their values take
+// registers per block).
 template <int KIND, int D>
 constexpr int dkdv_bq() {
-  return (KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL || D == 128) ? 32 : 64;
+  return (KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL) ? 32 : 64;
 }
 
 // Workgroups from which masked D = 128 dK / dV take two passes: two per CU of

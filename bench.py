@@ -616,7 +616,7 @@ def bench_attention(args):
                    "shape": [B, H, S, D], "causal": causal, "scale": scale},
         "forward": {"us": round(fwd_ms * 1e3, 1), "TFLOPs": round(fwd_tf, 1)},
         "backward": {"us": round(bwd_ms * 1e3, 1), "TFLOPs": round(bwd_tf, 1),
-                     "launches": "dQ with rowsum(dO*O), dK + dV (one pass for D = 64, two for D = 128)"},
+                     "launches": "dQ with rowsum(dO*O), dK + dV in one pass"},
         "roofline": {"bound": "mfma", "kernel": "backward (3 launches)",
                      "achieved": round(bwd_tf, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(bwd_tf / MFMA_F16_PEAK_TFLOPS, 4),

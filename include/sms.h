@@ -321,7 +321,9 @@ int64_t sms_attention_workspace_bytes(int64_t B, int64_t H, int64_t Sq);
  *                  may run at the same time (else SMS_ERR_WORKSPACE); its
  *                  contents on entry do not matter
  *   stream         hipStream_t to enqueue on (two kernel launches; three
- *                  with D = 128, where dK and dV take a launch each)
+ *                  with D = 128, a per-score mask and 512 or more key
+ *                  blocks of 128 (B * Hk * ceil(Sk / 128)), where dK and
+ *                  dV take a launch each)
  *
  * Row alignment and limits as for sms_attention_forward, and also
  * ceil(Sk / 128) * Hk * B < 2^24 and the q and dout row strides at most 2^24
