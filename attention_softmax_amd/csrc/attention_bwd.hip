@@ -360,13 +360,18 @@ attn_bwd_dq_kernel(AttnBwdParams p) {
 // double-buffered) come with its Q and dO tiles. For additive masks each lane
 // takes its key's values for 4 consecutive queries per transposing read, as
 // the forward reads V; for boolean ones it reads its 16 bytes one by one.
-template <bool BF16, int D, int KIND, int PASS, int BQ, bool MT>
+// VL (one pass, D = 128, no per-score mask): V read by rows from an LDS copy
+// of the workgroup's 128 keys (32 KB, loaded once) instead of being held in
+// registers, which brings the pass within 256 registers: two wavefronts per
+// SIMD with 32-query steps (two workgroups' LDS fit a CU).
+template <bool BF16, int D, int KIND, int PASS, int BQ, bool MT, bool VL>
 __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdParams& p) {
   constexpr bool kDV = PASS != 1, kDK = PASS != 0;
   static_assert(BQ == 32 || BQ == 64, "query tiles of one or two 32-query blocks");
   static_assert(BQ == 32 || (KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL),
                 "per-score masks are loaded for one 32-query block per step");
   static_assert(!MT || KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL, "mask tiles of a per-score mask");
+  static_assert(!VL || (PASS == 2 && D == 128 && !MT), "the V copy serves the one-pass D = 128 kernel");
   constexpr int NSUB = BQ / 32;
   constexpr int TQ = BQ * D * 2;  // bytes per Q or dO tile
   constexpr int MB = KIND == ATTN_MASK_BOOL ? 1 : 2;  // bytes per mask value
@@ -380,6 +385,7 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
   __shared__ __align__(16) float lses[2][BQ];  // LSE * log2(e) of the step's queries
   __shared__ __align__(16) float dels[2][BQ];
   __shared__ __align__(1024) uint8_t mt[MT ? 2 * TMQ : 16];
+  __shared__ __align__(1024) uint8_t vl[VL ? kAttnBwdBk * D * 2 : 16];
 
   const int tid = (int)threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
@@ -414,7 +420,7 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
     vf[s] = u32x4{0, 0, 0, 0};
     if (kvalid) {
       kf[s] = *reinterpret_cast<const u32x4*>(kbase + ((int64_t)kj * p.sk_s + s * 16 + 8 * g) * 2);
-      if constexpr (kDK)
+      if constexpr (kDK && !VL)
         vf[s] = *reinterpret_cast<const u32x4*>(vbase + ((int64_t)kj * p.sv_s + s * 16 + 8 * g) * 2);
     }
   }
@@ -484,6 +490,15 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
   uint32_t rao = (uint32_t)dtile_off<D>(c, g);
   uint32_t tao =
       (uint32_t)(dtile_off<D>(4 * g + ((c & 15) >> 2), 2 * ((c >> 4) & 1) + ((c >> 1) & 1)) + 8 * (c & 1));
+  // V copy (VL): the lane's key row, logical chunk 2 s + g at vra ^ 32 s; the
+  // first step's barrier covers its loads.
+  const uint32_t vra = rao + 32 * wave * D * 2;
+  if constexpr (VL) {
+    if (any) {
+      const u32x4 vr = rows_desc(vbase + (int64_t)k0 * p.sv_s * 2, min(Sk - k0, kAttnBwdBk), p.sv_s * 2, D * 2);
+      dma_tile_asm<D, kAttnBwdBk>(vr, dma_lane_off<D>(lane, swave, p.sv_s * 2), p.sv_s * 2, swave, lds_addr(vl));
+    }
+  }
   // Mask tile (MT): transposing read m hands the lane its key's values for
   // queries 8 m + 4 g + 0..3 of the step (registers 4 m .. 4 m + 3): the lane
   // addresses query 8 m + 4 g + (c % 16) / 4, keys 32 w + 16 ((c / 16) % 2)
@@ -588,19 +603,38 @@ __device__ inline __attribute__((always_inline)) void dkdv_body(const AttnBwdPar
             sacc[r] = 0.0f;
             dpacc[r] = 0.0f;
           }
+          if constexpr (VL) {
 #pragma unroll
-          for (int s = 0; s < D / 16; ++s) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(ql + (ra ^ (32 * s)) + 32 * qb * D * 2);
-            sacc = mfma_32x32x16<BF16>(a, kf[s], sacc);
-            if constexpr (kDK) {
+            for (int s = 0; s < D / 16; ++s) {
+              const u32x4 a = *reinterpret_cast<const u32x4*>(ql + (ra ^ (32 * s)) + 32 * qb * D * 2);
               const u32x4 ad = *reinterpret_cast<const u32x4*>(dl_ + (ra ^ (32 * s)) + 32 * qb * D * 2);
-              dpacc = mfma_32x32x16<BF16>(ad, vf[s], dpacc);
+              const u32x4 vv = *reinterpret_cast<const u32x4*>(vl + (vra ^ (32 * s)));
+              sacc = mfma_32x32x16<BF16>(a, kf[s], sacc);
+              dpacc = mfma_32x32x16<BF16>(ad, vv, dpacc);
             }
+            // The Q, dO and V reads of a k-step two k-steps ahead of its products.
+            __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+            for (int i = 0; i < D / 16 - 2; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          } else {
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s) {
+              const u32x4 a = *reinterpret_cast<const u32x4*>(ql + (ra ^ (32 * s)) + 32 * qb * D * 2);
+              sacc = mfma_32x32x16<BF16>(a, kf[s], sacc);
+              if constexpr (kDK) {
+                const u32x4 ad = *reinterpret_cast<const u32x4*>(dl_ + (ra ^ (32 * s)) + 32 * qb * D * 2);
+                dpacc = mfma_32x32x16<BF16>(ad, vf[s], dpacc);
+              }
+            }
+            // Q / dO reads four products ahead (1-2 % faster); not with
+            // per-score masks, whose registers are short already.
+            if constexpr (KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL)
+              pin_reads_ahead<(kDK ? 2 : 1) * (D / 16), 4, 1>();
           }
-          // Q / dO reads four products ahead (1-2 % faster); not with per-score
-          // masks, whose registers are short already.
-          if constexpr (KIND != ATTN_MASK_ADD && KIND != ATTN_MASK_BOOL)
-            pin_reads_ahead<(kDK ? 2 : 1) * (D / 16), 4, 1>();
           // Register r holds query qb0 + 8*(r/4) + 4g + r%4 of this lane's key.
           float pr[16], dsr[16];
           // A block whose every (query, key) score is visible (all queries and
@@ -745,11 +779,16 @@ template <bool BF16, int D, int KIND, int PASS, int BQ, bool MT>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(dkdv_waves<KIND, PASS, MT>(), dkdv_waves<KIND, PASS, MT>())))
 attn_bwd_dkdv_kernel(AttnBwdParams p) {
-  dkdv_body<BF16, D, KIND, PASS, BQ, MT>(p);
+  dkdv_body<BF16, D, KIND, PASS, BQ, MT, false>(p);
 }
 template <bool BF16, int D, int KIND, int BQ, bool MT>
 __global__ void __launch_bounds__(256) attn_bwd_dkdv_both_kernel(AttnBwdParams p) {
-  dkdv_body<BF16, D, KIND, 2, BQ, MT>(p);
+  dkdv_body<BF16, D, KIND, 2, BQ, MT, false>(p);
+}
+template <bool BF16, int KIND>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bwd_dkdv_vl_kernel(AttnBwdParams p) {
+  dkdv_body<BF16, 128, KIND, 2, 32, false, true>(p);
 }
 
 // Queries per dK/dV step. Two 32-query blocks per loaded tile halve the
@@ -763,23 +802,32 @@ constexpr int dkdv_bq() {
   return (KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL) ? 32 : 64;
 }
 
-// Workgroups from which masked D = 128 dK / dV take two passes: two per CU of
-// the MI355X's 256.
+// Workgroups from which D = 128 dK / dV run at two wavefronts per SIMD (two
+// passes with a per-score mask, else one pass with the V copy): two per CU
+// of the MI355X's 256.
 constexpr uint32_t kTwoPassGrid = 512;
 
 template <bool BF16, int D, int KIND, bool MT>
 hipError_t launch_dkdv(const AttnBwdParams& p, hipStream_t st) {
   const dim3 block(256);
   const dim3 gk(p.Hk * p.B * ((p.Sk + kAttnBwdBk - 1) / kAttnBwdBk));
-  // D = 128: both gradients in one pass at one wavefront per SIMD without a
-  // per-score mask (fp16 [4,32,4096,128] backward: causal 2200 against
-  // 2325 us for the two passes, not causal 3775 against 4070) and on grids
-  // of fewer than two workgroups per CU (bf16 [2,8,1000,128], 128
-  // workgroups: 79 against 103 us, 107 against 131 with an additive mask);
-  // with a per-score mask on larger grids the two passes (fp16
-  // [4,32,4096,128] with an additive mask, causal: 2784 against 2830-3000).
+  // D = 128 on grids of two workgroups per CU or more: without a per-score
+  // mask one pass with the V copy at two wavefronts per SIMD (fp16
+  // [4,32,4096,128] backward: causal 2028 against 2225 us for one pass at
+  // one wavefront and 2325 for two passes; not causal 3610 against 3795 and
+  // 4070), with one the two passes (additive mask, causal: 2784 against
+  // 2830-3000 for one pass at one wavefront). Smaller grids: one pass at one
+  // wavefront per SIMD (bf16 [2,8,1000,128], 128 workgroups: 78 against 85
+  // with the V copy and 103 for two passes; 107 against 131 with an
+  // additive mask).
   constexpr int BQ = dkdv_bq<KIND, D>();
   constexpr bool kPerScore = KIND == ATTN_MASK_ADD || KIND == ATTN_MASK_BOOL;
+  if constexpr (D == 128 && !kPerScore) {
+    if (gk.x >= kTwoPassGrid) {
+      hipLaunchKernelGGL((attn_bwd_dkdv_vl_kernel<BF16, KIND>), gk, block, 0, st, p);
+      return hipGetLastError();
+    }
+  }
   if constexpr (D == 128 && kPerScore) {
     if (gk.x >= kTwoPassGrid) {
       hipLaunchKernelGGL((attn_bwd_dkdv_kernel<BF16, D, KIND, 0, BQ, MT>), gk, block, 0, st, p);

@@ -246,23 +246,26 @@ def test_attention_backward_strided_mha_and_scale(dtype):
     check_bwd(q8, k1, v1, None, "none", "none", 1.0, False, "8 heads on 1, scale 1", 18)
 
 
-@pytest.mark.parametrize("kind", ["neginf", "bool"])
-def test_attention_backward_masked_two_passes(kind):
-    """D = 128 with a per-score [B,Sq,Sk] mask (LDS tiles) on a grid of 512
-    dK/dV workgroups (two per CU), where dK and dV take a launch each (smaller
-    grids, as in the sweep, take one): B = 2, H = Hk = 32, 64 queries, 1024
-    keys, not causal and bottom-right causal."""
-    say(f"attention backward two-pass dK/dV mask={kind}")
-    B, H, Sq, Sk, D = 2, 32, 64, 1024, 128
+@pytest.mark.parametrize("kind,Sk", [("neginf", 1024), ("bool", 1024), ("none", 1000), ("lengths", 1000)])
+def test_attention_backward_large_grid(kind, Sk):
+    """D = 128 on a grid of 512 dK/dV workgroups (two per CU), where dK and dV
+    run at two wavefronts per SIMD: as two launches with a per-score [B,Sq,Sk]
+    mask (LDS tiles), as one launch with the V copy in LDS without one
+    (smaller grids, as in the sweep, take one launch at one wavefront per
+    SIMD). B = 2, 64 query heads over 32 key/value heads, 64 queries, 1024 or
+    1000 keys (a last key block of 104), not causal and bottom-right causal."""
+    say(f"attention backward large grid mask={kind} Sk={Sk}")
+    B, H, Hk, Sq, D = 2, 64, 32, 64, 128
     worst = 0.0
     for causal in (False, "bottom_right"):
-        seed = zlib.crc32(f"two/{kind}/{causal}".encode()) % 10000
+        seed = zlib.crc32(f"large/{kind}/{Sk}/{causal}".encode()) % 10000
         q = draw_x((B, H, Sq, D), "f16", ("normal", 1.0), seed, DEV)
-        k = draw_x((B, H, Sk, D), "f16", ("normal", 1.0), seed + 1, DEV)
-        v = draw_x((B, H, Sk, D), "f16", ("normal", 1.0), seed + 2, DEV)
-        mask = make_mask((B, H, Sq, Sk), "b_sq_sk", kind, "f16", seed + 3)
-        w = check_bwd(q, k, v, mask, "b_sq_sk", kind, D ** -0.5, causal,
-                      f"two-pass {kind} causal={causal}", seed + 4)
+        k = draw_x((B, Hk, Sk, D), "f16", ("normal", 1.0), seed + 1, DEV)
+        v = draw_x((B, Hk, Sk, D), "f16", ("normal", 1.0), seed + 2, DEV)
+        mode = {"none": "none", "lengths": "key_lengths"}.get(kind, "b_sq_sk")
+        mask = make_mask((B, H, Sq, Sk), mode, kind, "f16", seed + 3)
+        w = check_bwd(q, k, v, mask, mode, kind, D ** -0.5, causal,
+                      f"large grid {kind} Sk={Sk} causal={causal}", seed + 4)
         worst = max(worst, w)
     say(f"  worst error / tolerance {worst:.3f}")
 
