@@ -28,6 +28,7 @@ from .ops import (  # noqa: F401
     sms_attention_forward,
     sms_attention_workspace_bytes,
     sms_backward,
+    sms_copy_reference,
     sms_forward,
     sms_forward_noalloc,
     sms_max_sk,

@@ -28,8 +28,8 @@ EXPORTS = ("sms_forward", "sms_backward", "sms_forward_ws", "sms_backward_ws",
            "sms_forward_noalloc", "sms_noalloc_scratch_bytes",
            "sms_workspace_bytes", "sms_attention_forward", "sms_attention_backward",
            "sms_attention_workspace_bytes", "sms_max_sk", "sms_path",
-           "sms_status_str", "sms_abi_version")
-ABI_VERSION = 6
+           "sms_copy_reference", "sms_status_str", "sms_abi_version")
+ABI_VERSION = 7
 
 _lock = threading.Lock()
 _lib = None
@@ -80,6 +80,8 @@ def _declare(L):
     L.sms_max_sk.restype = i64
     L.sms_path.argtypes = [i32, i64, i32]
     L.sms_path.restype = i32
+    L.sms_copy_reference.argtypes = [vp, vp, i64, vp]
+    L.sms_copy_reference.restype = i32
     L.sms_status_str.argtypes = [i32]
     L.sms_status_str.restype = ctypes.c_char_p
     L.sms_abi_version.argtypes = []

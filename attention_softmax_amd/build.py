@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsms.so")
 
 SOURCES = ["api.hip", "inst_f32.hip", "inst_f16.hip", "inst_bf16.hip", "inst_f64.hip",
-           "attention.hip", "attention_bwd.hip", "attention_api.hip"]
+           "attention.hip", "attention_bwd.hip", "attention_api.hip", "copy_ref.hip"]
 ARCH = "gfx950"
 
 # Per-source flags. The attention backward's MFMAs keep their accumulators in

@@ -387,6 +387,23 @@ def sms_path(dtype, Sk, backward=False):
     return int(_lib.lib().sms_path(_lib.DTYPE_CODES[_DTYPES[dtype]], int(Sk), int(backward)))
 
 
+def sms_copy_reference(src, dst, stream=None):
+    """dst <- src as raw bytes through the library's plain 16-byte copy kernel
+    (C ABI sms_copy_reference): the bandwidth reference for the softmax
+    kernels, not part of the method. Both tensors contiguous, on the GPU, of
+    the same byte size (a multiple of 16)."""
+    _require_gpu(src, "src")
+    _require_gpu(dst, "dst")
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous")
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("src and dst must hold the same number of bytes")
+    s = _stream_of(src.device, stream)
+    _lib.check("sms_copy_reference",
+               _lib.lib().sms_copy_reference(src.data_ptr(), dst.data_ptr(), n, s.cuda_stream))
+
+
 def _rows_view(t):
     """t itself when its key axis is contiguous, else a contiguous copy."""
     return t if (t.shape[-1] <= 1 or t.stride(-1) == 1) else t.contiguous()

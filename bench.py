@@ -19,8 +19,12 @@ bytes count x and the mask once where the result depends on them, y and dy
 where y can be nonzero, and every y and dx written. The same line carries the
 per-kernel rate of the other workloads (fp32 [1,2,64,64], fp32 [8,32,1024,1024]
 with key padding, fp16 [4,32,2048,2048] causal, bf16 [16,16,1000,1000] with a
-[1000,1000] mask), each timed after its own settle phase, and the float64
-oracle timed on the host's cores over a sample of the headline workload's rows.
+[1000,1000] mask), each timed after its own settle phase, the float64
+oracle timed on the host's cores over a sample of the headline workload's rows,
+and two plain device copies of the forward's byte count: torch's and the
+library's 16-byte copy kernel (copy_ceiling: what a kernel that reads and
+writes those bytes once reaches with no arithmetic, and each kernel's rate as a
+fraction of it).
 One JSON line on stdout; diagnostics on stderr.
 
     python bench.py --op attention [--steps K] [--warmup W]
@@ -121,12 +125,12 @@ def parse():
 
 def csrc_sha():
     """Hash of the sources the softmax kernels and their launches are built
-    from (every file under csrc/ but the fused attention's own): counters
-    taken on other sources are stale."""
+    from (every file under csrc/ but the fused attention's own and the copy
+    reference): counters taken on other sources are stale."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "attention_softmax_amd", "csrc")
     files = sorted(f for f in glob.glob(os.path.join(csrc, "*"))
-                   if not os.path.basename(f).startswith("attention"))
+                   if not os.path.basename(f).startswith(("attention", "copy_ref")))
     for f in files:
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())
@@ -647,7 +651,7 @@ def main():
 
     import torch
 
-    from attention_softmax_amd import sms_backward, sms_forward, sms_path
+    from attention_softmax_amd import sms_backward, sms_copy_reference, sms_forward, sms_path
     from attention_softmax_amd.workloads import CONFIGS, make_config
 
     dev = torch.device("cuda:0")
@@ -708,9 +712,10 @@ def main():
 
     traffic = load_traffic(args.traffic, args.workload, dom)
 
-    copy = None
+    copy = ceiling = None
     if not args.no_copy:
-        # A plain device copy moving the forward's byte count: a reference ceiling.
+        # Plain device copies moving the forward's byte count: torch's (whose
+        # counters calibrate the traffic figures) and the library's own.
         n = fwd_b // 2
         src = torch.empty(n, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -724,7 +729,27 @@ def main():
         torch.cuda.synchronize()
         cms = c0.elapsed_time(c1) / 10
         copy = {"bytes": 2 * n, "avg_us": round(cms * 1e3, 2),
-                "GBps": round(2 * n / (cms * 1e-3) / 1e9, 1)}
+                "GBps": round(2 * n / (cms * 1e-3) / 1e9, 1),
+                "kernel": "torch's device copy (" + COPY_KERNEL + ")"}
+        # The library's plain 16-byte copy of the same bytes (no arithmetic):
+        # what a kernel that reads and writes them once reaches on this chip.
+        n16 = n // 16 * 16
+        for _ in range(3):
+            sms_copy_reference(src[:n16], dst[:n16], stream=stream)
+        c0.record(stream)
+        for _ in range(20):
+            sms_copy_reference(src[:n16], dst[:n16], stream=stream)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        cms = c0.elapsed_time(c1) / 20
+        cgb = 2 * n16 / (cms * 1e-3) / 1e9
+        ceiling = {"kernel": "sms_copy_reference (16-byte nontemporal loads and stores, "
+                             "64 lanes per KB)",
+                   "bytes": 2 * n16, "avg_us": round(cms * 1e3, 2), "GBps": round(cgb, 1),
+                   "frac_hbm_peak": round(cgb / HBM_PEAK_GBPS, 4),
+                   "forward_frac_of_copy": round(kern["forward"]["GBps"] / cgb, 4),
+                   "backward_frac_of_copy": round(kern["backward"]["GBps"] / cgb, 4)}
+        log(f"copy ceiling: {ceiling}")
         del src, dst
 
     torch_ref = None
@@ -777,6 +802,7 @@ def main():
                      "frac": kern[dom]["frac_hbm_peak"], "traffic": traffic},
         "other_workloads": others,
         "copy_reference": copy,
+        "copy_ceiling": ceiling,
         "torch_reference": torch_ref,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),

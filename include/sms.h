@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SMS_ABI_VERSION 6
+#define SMS_ABI_VERSION 7
 
 typedef enum {
   SMS_OK = 0,
@@ -358,6 +358,21 @@ int64_t sms_max_sk(sms_dtype dtype);
  * wavefront or 256 lanes per row). -1 for an unsupported size or dtype.
  * `backward` selects the backward's choice. Host-only; launches nothing. */
 int sms_path(sms_dtype dtype, int64_t Sk, int backward);
+
+/*
+ * sms_copy_reference -- dst[0, bytes) = src[0, bytes): a plain device copy,
+ * 16 bytes per lane, nontemporal. Not a step of the method: the bandwidth
+ * reference for the kernels above, which read their inputs once and write their
+ * outputs once where the unfused chain re-reads and re-writes the score tensor
+ * at every step (lmnt.cn page, sec. 1.1 and 1.2); a copy of the same bytes
+ * with no arithmetic bounds what such a kernel can reach on the same chip.
+ *
+ *   src, dst   device memory, 16-byte aligned, not overlapping, caller-owned
+ *   bytes      a multiple of 16 (else SMS_ERR_ALIGN); 0 is a no-op; at most
+ *              2^31 - 1 KiB (else SMS_ERR_SHAPE)
+ *   stream     hipStream_t to enqueue on
+ */
+sms_status sms_copy_reference(const void* src, void* dst, int64_t bytes, void* stream);
 
 /* Static text naming a status code. */
 const char* sms_status_str(sms_status s);

@@ -114,6 +114,18 @@ def test_backward_argument_checks(L):
     assert L.sms_backward(FAKE, s, FAKE, s, FAKE, s, 0, 1, 1, 1, 64, 1.0, 4, None) == 8
 
 
+@no_device
+def test_copy_reference_argument_checks(L):
+    assert L.sms_copy_reference(None, None, 0, None) == 0          # nothing to copy
+    assert L.sms_copy_reference(FAKE, FAKE + 4096, -16, None) == 2  # negative size
+    assert L.sms_copy_reference(None, FAKE, 16, None) == 1
+    assert L.sms_copy_reference(FAKE, None, 16, None) == 1
+    assert L.sms_copy_reference(FAKE + 8, FAKE + 4096, 16, None) == 6   # src not 16-byte aligned
+    assert L.sms_copy_reference(FAKE, FAKE + 4104, 16, None) == 6       # dst not 16-byte aligned
+    assert L.sms_copy_reference(FAKE, FAKE + 4096, 24, None) == 6       # size not a multiple of 16
+    assert L.sms_copy_reference(FAKE, FAKE + 4096, (1 << 41), None) == 2  # 2^31 KiB blocks
+
+
 def test_f64_queries(L):
     assert L.sms_max_sk(3) == 1 << 30
     assert L.sms_path(3, 1000, 0) == 4 and L.sms_path(3, 1 << 20, 1) == 4
