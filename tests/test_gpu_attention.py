@@ -366,6 +366,66 @@ def test_attention_autograd():
               "lengths", 64 ** -0.5, True, "autograd case", 0, do=do, chain=True)
 
 
+@pytest.mark.parametrize("dtype,D,mode,kind,causal", [
+    ("f16", 128, "b_sq_sk", "additive", True),
+    ("bf16", 64, "none", "none", False),
+])
+def test_attention_hip_graph_capture_and_replay(dtype, D, mode, kind, causal):
+    """Forward + backward captured once into a HIP graph and replayed on new
+    inputs copied into the static buffers, with eager work and synchronisation
+    between replays: every replay equals the eager calls bit for bit, and the
+    forward agrees with the oracle (the operator has no host-side control flow
+    that would keep it out of a graph: pnsm.cn ScaledMaskSoftmax article,
+    sec. 4.4)."""
+    say(f"attention graph {dtype} D={D} mask={mode}/{kind} causal={causal}")
+    B, H, Hk, Sq, Sk = 1, 4, 2, 200, 300
+    scale = D ** -0.5
+    shp_q, shp_k = (B, H, Sq, D), (B, Hk, Sk, D)
+
+    def draw(seed):
+        return (draw_x(shp_q, dtype, ("normal", 1.0), seed, DEV),
+                draw_x(shp_k, dtype, ("normal", 1.0), seed + 1, DEV),
+                draw_x(shp_k, dtype, ("normal", 1.0), seed + 2, DEV),
+                draw_x(shp_q, dtype, ("normal", 1.0), seed + 3, DEV))
+
+    q, k, v, do = draw(60)
+    mask = make_mask((B, H, Sq, Sk), mode, kind, dtype, 64)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=DEV)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(sms_attention_workspace_bytes(B, H, Sq), dtype=torch.uint8, device=DEV)
+
+    def run():
+        sms_attention_forward(q, k, v, mask, scale, causal, o=o, lse=lse)
+        sms_attention_backward(q, k, v, o, lse, do, mask, scale, causal, dq=dq, dk=dk, dv=dv,
+                               workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up off the default stream
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(3):
+        qn, kn, vn, don = draw(100 + 10 * rep)
+        for dst, src in ((q, qn), (k, kn), (v, vn), (do, don)):
+            dst.copy_(src)
+        g.replay()
+        torch.cuda.synchronize()
+        oe, lse_e = sms_attention_forward(qn, kn, vn, mask, scale, causal, return_lse=True)
+        gq, gk, gv = sms_attention_backward(qn, kn, vn, oe, lse_e, don, mask, scale, causal)
+        torch.cuda.synchronize()
+        for name, a, b_ in (("O", o, oe), ("LSE", lse, lse_e), ("dQ", dq, gq), ("dK", dk, gk),
+                            ("dV", dv, gv)):
+            assert torch.equal(a, b_), f"replay {rep}: {name} differs from the eager call"
+        if rep == 0:
+            check(qn, kn, vn, mask, mode, kind, scale, causal, f"graph replay {rep}")
+    del g
+
+
 def test_attention_backward_errors():
     q = torch.zeros(1, 1, 4, 64, dtype=torch.float16, device=DEV)
     lse = torch.zeros(1, 1, 4, dtype=torch.float32, device=DEV)
