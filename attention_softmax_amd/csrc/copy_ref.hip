@@ -46,8 +46,9 @@ extern "C" sms_status sms_copy_reference(const void* src, void* dst, int64_t byt
   if (bytes == 0) return SMS_OK;
   if (!src || !dst) return SMS_ERR_NULL;
   if (((uintptr_t)src & 15) || ((uintptr_t)dst & 15) || (bytes & 15)) return SMS_ERR_ALIGN;
+  // One dispatch holds at most 2^32 - 1 work-items: 64 lanes per KiB.
   const int64_t blocks = (bytes + kCopyChunk - 1) / kCopyChunk;
-  if (blocks > INT32_MAX) return SMS_ERR_SHAPE;
+  if (blocks * kCopyLanes > (int64_t)UINT32_MAX) return SMS_ERR_SHAPE;
   hipLaunchKernelGGL(sms_copy_kernel, dim3((uint32_t)blocks), dim3(kCopyLanes), 0,
                      (hipStream_t)stream, static_cast<const char*>(src), static_cast<char*>(dst),
                      (uint64_t)(bytes / 16));

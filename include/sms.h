@@ -369,7 +369,7 @@ int sms_path(sms_dtype dtype, int64_t Sk, int backward);
  *
  *   src, dst   device memory, 16-byte aligned, not overlapping, caller-owned
  *   bytes      a multiple of 16 (else SMS_ERR_ALIGN); 0 is a no-op; at most
- *              2^31 - 1 KiB (else SMS_ERR_SHAPE)
+ *              (2^32 - 1) / 64 KiB, about 64 GiB (else SMS_ERR_SHAPE)
  *   stream     hipStream_t to enqueue on
  */
 sms_status sms_copy_reference(const void* src, void* dst, int64_t bytes, void* stream);

@@ -123,7 +123,7 @@ def test_copy_reference_argument_checks(L):
     assert L.sms_copy_reference(FAKE + 8, FAKE + 4096, 16, None) == 6   # src not 16-byte aligned
     assert L.sms_copy_reference(FAKE, FAKE + 4104, 16, None) == 6       # dst not 16-byte aligned
     assert L.sms_copy_reference(FAKE, FAKE + 4096, 24, None) == 6       # size not a multiple of 16
-    assert L.sms_copy_reference(FAKE, FAKE + 4096, (1 << 41), None) == 2  # 2^31 KiB blocks
+    assert L.sms_copy_reference(FAKE, FAKE + 4096, (1 << 36), None) == 2  # 2^26 KiB: 2^32 lanes
 
 
 def test_f64_queries(L):
