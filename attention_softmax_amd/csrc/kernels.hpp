@@ -291,6 +291,24 @@ SMS_DEV uint32_t local_row() {
   else return threadIdx.x / TPR;
 }
 
+// Work item of this workgroup in the aligned-row kernels. Workgroups are dealt
+// to the 8 XCDs round-robin (workgroup i runs on XCD i % 8, each XCD with its
+// own L2), so consecutive rows land on different XCDs. Where rows share
+// 128-byte lines with their neighbours (a launch that is not line-exact), a
+// line two rows share then reaches HBM as two partial writes from two L2s.
+// For those launches workgroup i takes work item (i % 8) * (N / 8) + i / 8
+// (the tail past 8 * (N / 8) as is): each XCD walks a contiguous range of
+// rows and both halves of a shared line meet in its L2. Measured on MI355X,
+// bf16 [16,16,1000,1000] with a [1000,1000] mask: forward 175.2 -> 172.2 us,
+// backward 234.3 -> 226.0 us. Line-exact launches measured 1-7 % slower with
+// it (eight streams through memory instead of one) and keep the dealt order.
+SMS_DEV uint32_t work_item(int lines) {
+  const uint32_t i = blockIdx.x;
+  if (lines) return i;
+  const uint32_t per = gridDim.x >> 3;
+  return i < (per << 3) ? (i & 7u) * per + (i >> 3) : i;
+}
+
 // ------------------------------------------------------------- parameters
 
 enum : int { MASK_NONE = 0, MASK_ADD = 1, MASK_BOOL = 2, MASK_LEN = 3 };
@@ -749,7 +767,7 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_fwd_fast_kernel(FwdParams p
   // with it, so they keep the default.
   if constexpr (EARLY) __builtin_amdgcn_s_setprio(3);
   const int lane = (int)(threadIdx.x % TPR);
-  const uint32_t row = blockIdx.x * RPB + local_row<TPR>();
+  const uint32_t row = work_item(p.lines) * RPB + local_row<TPR>();
   if (RPB > 1 && row >= p.g.rows) return;  // a tail group of a TPR <= 64 launch (no barrier)
   uint32_t b, h, q;
   row_bhq(p.g, row, b, h, q);
@@ -882,7 +900,7 @@ __global__ void __launch_bounds__(TPR) sms_fwd_heads_kernel(FwdParams p) {
   __shared__ float red[2][G][TPR / 64];
   const int lane = (int)threadIdx.x;
   // Host-checked: H % G == 0 and grid = B * (H / G) * Sq.
-  const uint32_t w = blockIdx.x;
+  const uint32_t w = work_item(p.lines);
   const uint32_t t = fast_div(w, p.g.div_sq);
   const uint32_t q = w - t * p.g.Sq;
   const uint32_t b = fast_div(t, p.div_hg);
@@ -1004,7 +1022,7 @@ __global__ void __launch_bounds__(block_of(TPR)) sms_bwd_fast_kernel(BwdParams p
   constexpr int RPB = block_of(TPR) / TPR;
   __shared__ double red[TPR > 64 ? TPR / 64 : 1];
   const int lane = (int)(threadIdx.x % TPR);
-  const BwdRow r = bwd_row<F, RPB>(p, blockIdx.x, local_row<TPR>());
+  const BwdRow r = bwd_row<F, RPB>(p, work_item(p.lines), local_row<TPR>());
   if (!r.valid) return;
   const int kload = r.kload;
   const uint32_t row_bytes = p.g.Sk * F::kBytes;
