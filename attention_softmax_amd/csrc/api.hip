@@ -82,6 +82,36 @@ bool use_stream(int64_t nvec) {
   return nvec > kMaxVecPerRow || env_int("SMS_FORCE_STREAM", 0) != 0;
 }
 
+// Longest row (16-byte vectors) the aligned backward holds in VGPRs at 1024
+// lanes x 8 vectors: one pass where the streaming kernels take two. Measured
+// on MI355X (us, streaming -> one pass): fp16 rows of 65536 keys (8192 rows)
+// 730 -> 575, causal 719 -> 585; of 40000 keys (13416 rows) 662 -> 550,
+// causal 625 -> 582. The forward at 1024 x 8 measured equal to the streaming
+// kernels (425 against 430 us, 451 against 445) and keeps them.
+// Rows that keep few of their keys (a top-left causal rule over Sq << Sk)
+// are mostly zero stores, which the streaming kernels' two workgroups per CU
+// issue faster: fp16 [1,8,1677,40000] top-left causal 197 us streaming against
+// 265 in one pass. The one pass is taken when the causal rule keeps at least
+// half of the keys overall.
+constexpr int64_t kMaxVecPerRowBwd = 1024 * 8;
+// Sum over t = 1 .. n of min(t, Sk) (0 for n <= 0).
+__int128 kept_prefix(int64_t n, int64_t Sk) {
+  if (n <= 0) return 0;
+  if (n <= Sk) return (__int128)n * (n + 1) / 2;
+  return (__int128)Sk * (Sk + 1) / 2 + (__int128)(n - Sk) * Sk;
+}
+// Keys the causal rule keeps over all Sq rows of a (b, h) plane, at least half of Sq * Sk.
+bool keeps_half(int64_t Sq, int64_t Sk, int causal) {
+  if (causal == SMS_CAUSAL_NONE) return true;
+  const int64_t d = causal == SMS_CAUSAL_BOTTOM_RIGHT ? Sk - Sq : 0;
+  const __int128 kept = kept_prefix(Sq + d, Sk) - kept_prefix(d, Sk);
+  return 2 * kept >= (__int128)Sq * Sk;
+}
+bool bwd_one_pass_long(int64_t nvec) {
+  return nvec > kMaxVecPerRow && nvec <= kMaxVecPerRowBwd && env_int("SMS_FORCE_STREAM", 0) == 0 &&
+         env_int("SMS_FORCE_TPR", 0) == 0;
+}
+
 // Chunks per row for `rows` rows of up to `nvec` vectors: 1 = no split.
 int64_t split_chunks(int64_t rows, int64_t nvec) {
   if (rows > kSplitGridRows || nvec < 1) return 1;
@@ -335,7 +365,9 @@ int sms_path(sms_dtype dtype, int64_t Sk, int backward) {
   if (!bytes || Sk < 0 || Sk > kMaxSk) return -1;
   if (dtype == SMS_F64) return 4;
   Plan pl;
-  if (!choose_plan(vectors_per_row(Sk, 16 / bytes, true), backward != 0, false, pl)) return -1;
+  const int64_t nvec = vectors_per_row(Sk, 16 / bytes, true);
+  if (backward && ((Sk * bytes) & 15) == 0 && bwd_one_pass_long(nvec)) return 2;
+  if (!choose_plan(nvec, backward != 0, false, pl)) return -1;
   if (pl.family == sms::FAMILY_STREAM) return 3;
   return pl.tpr < 64 ? 0 : (pl.tpr == 64 ? 1 : 2);
 }
@@ -499,10 +531,18 @@ sms_status sms_backward_ws(const void* y, const int64_t y_strides[4], const void
 
   const bool aligned = rows_aligned16(y, y_strides, B, H, Sq, bytes);
   const int64_t nvec = vectors_per_row(Sk, E, aligned);
+  // Every operand's rows on 16-byte lines holding whole vectors: the aligned kernels.
+  const bool fast_rows = !f64 && ((Sk * bytes) & 15) == 0 && env_int("SMS_FAST", 1) != 0 &&
+                         aligned && rows_aligned16(dy, dy_strides, B, H, Sq, bytes) &&
+                         rows_aligned16(dx, dx_strides, B, H, Sq, bytes);
   Plan pl;
   if (f64) {
     pl.family = sms::FAMILY_F64;
     pl.tpr = sms::f64_tpr(Sk);
+  } else if (fast_rows && bwd_one_pass_long(nvec) && keeps_half(Sq, Sk, is_causal)) {
+    pl.family = sms::FAMILY_ALIGNED;
+    pl.tpr = 1024;
+    pl.nv = 8;
   } else if (!choose_plan(nvec, true, is_causal != 0, pl)) {
     return SMS_ERR_SHAPE;
   }
@@ -528,11 +568,7 @@ sms_status sms_backward_ws(const void* y, const int64_t y_strides[4], const void
   // Only the causal promise can leave a wavefront with no key.
   p.early = is_causal != 0 && env_int("SMS_EARLY", 1) != 0;
 
-  if (pl.family != sms::FAMILY_STREAM && pl.family != sms::FAMILY_SPLIT && !f64 &&
-      ((Sk * bytes) & 15) == 0 &&
-      env_int("SMS_FAST", 1) != 0 && aligned &&
-      rows_aligned16(dy, dy_strides, B, H, Sq, bytes) &&
-      rows_aligned16(dx, dx_strides, B, H, Sq, bytes))
+  if (pl.family != sms::FAMILY_STREAM && pl.family != sms::FAMILY_SPLIT && fast_rows)
     pl.family = sms::FAMILY_ALIGNED;
 
   uint32_t blocks = 0;

@@ -1585,6 +1585,15 @@ hipError_t launch(const FwdParams* fp, const BwdParams* bp, int family, int tpr,
     else hipLaunchKernelGGL((sms_bwd_split_final_kernel<F>), grid, block, 0, st, *bp);
     return hipGetLastError();
   }
+  if (bp && family == FAMILY_ALIGNED && tpr == 1024 && nv == 8) {
+    // Long rows of the aligned backward, held in VGPRs in one pass (built for
+    // this width only).
+    if (bp->early)
+      hipLaunchKernelGGL((sms_bwd_fast_kernel<F, 1024, 8, true>), dim3(blocks), dim3(1024), 0, st, *bp);
+    else
+      hipLaunchKernelGGL((sms_bwd_fast_kernel<F, 1024, 8, false>), dim3(blocks), dim3(1024), 0, st, *bp);
+    return hipGetLastError();
+  }
   if (family == FAMILY_STREAM) {
     if (fp)
       hipLaunchKernelGGL((sms_fwd_stream_kernel<F>), dim3(blocks), dim3(kStreamTpr), 0, st, *fp);

@@ -136,7 +136,10 @@ typedef enum {
  * Limits: B*H*Sq < 2^32 rows, Sk <= sms_max_sk(dtype) = 2^30, and at most
  * 2^32 - 1 work-items per launch (rows of more than 4096 16-byte vectors take
  * one 1024-lane workgroup each, so at most 4194303 such rows per call).
- * Longer rows cost a second read of the row (two passes). sms_forward never
+ * Longer rows cost a second read of the row (two passes), except in the
+ * backward of rows of up to 8192 vectors whose every operand row starts on a
+ * 16-byte line and holds whole vectors, when the causal rule (if any) keeps at
+ * least half of the keys (one pass). sms_forward never
  * splits a row across workgroups (see sms_forward_ws).
  */
 sms_status sms_forward(const void* x, const int64_t x_strides[4],
@@ -354,7 +357,8 @@ int64_t sms_max_sk(sms_dtype dtype);
  * 0 = several rows per wavefront, 1 = one wavefront per row, 2 = several
  * wavefronts per row (LDS cross-wave reduction), 3 = streaming (one 1024-lane
  * workgroup per row, two passes: online max/sum, then normalise; for rows of
- * more than 4096 16-byte vectors), 4 = the fp64 kernels (two passes, one
+ * more than 4096 16-byte vectors, but the backward of rows of up to 8192
+ * vectors that hold whole vectors stays in 2), 4 = the fp64 kernels (two passes, one
  * wavefront or 256 lanes per row). -1 for an unsupported size or dtype.
  * `backward` selects the backward's choice. Host-only; launches nothing. */
 int sms_path(sms_dtype dtype, int64_t Sk, int backward);

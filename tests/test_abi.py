@@ -190,6 +190,9 @@ def test_max_sk_and_paths(L):
     # rows beyond 4096 16-byte vectors stream; beyond 2^30 keys: unsupported
     assert L.sms_path(0, 4096 * 4, 0) == 2 and L.sms_path(0, 4096 * 4 + 1, 0) == 3
     assert L.sms_path(1, 4096 * 8, 1) == 2 and L.sms_path(1, 4096 * 8 + 1, 1) == 3
+    # the backward keeps whole-vector rows of up to 8192 vectors in one pass
+    assert L.sms_path(1, 4096 * 8 + 8, 1) == 2 and L.sms_path(1, 4096 * 8 + 8, 0) == 3
+    assert L.sms_path(0, 8192 * 4, 1) == 2 and L.sms_path(0, 8192 * 4 + 4, 1) == 3
     assert L.sms_path(2, 1 << 30, 0) == 3 and L.sms_path(2, (1 << 30) + 1, 0) == -1
 
 

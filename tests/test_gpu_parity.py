@@ -580,6 +580,9 @@ def test_streaming_kernels_on_short_rows(dtype, Sk, monkeypatch):
     ("bf16", 50001, "key_lengths", "lengths"),
     ("f16", 140001, "b_sq_sk", "bool"),       # rows of >= 16384 vectors: split when auto
     ("bf16", 262147, "key_lengths", "lengths"),
+    ("f16", 32776, "b_sq_sk", "additive"),   # 4097 vectors: the one-pass long-row backward
+    ("f16", 65536, "sq_sk", "bool"),         # 8192 vectors: its longest row
+    ("f32", 32768, "b_1_sk", "additive"),   # 8192 vectors of fp32
     ("f32", 65537, "full", "additive"),
     ("f64", 70001, "sq_sk", "additive"),     # fp64: two-pass kernels at every length
     ("f64", 40000, "b_1_sk", "bool"),
