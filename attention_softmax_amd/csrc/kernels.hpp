@@ -581,21 +581,34 @@ SMS_DEV void row_scores(const FwdRow& r, int kind, int v, float scale, float (&s
 #pragma unroll
       for (int e = 0; e < E; ++e) s[e] *= scale;
     }
-  } else {
-    // A partial vector (row head or tail, or the key bound inside it), or none
-    // of the vector's keys read: element by element, -inf outside [0, kload).
+  } else if (k0 < r.kload && k0 + E > 0) {
+    // A partial vector (the row's head or tail, or the key bound inside it):
+    // its 16-byte line is loaded whole -- the line holds at least one key of
+    // the row, so it lies in a page the row occupies -- and the keys outside
+    // [0, kload), which belong to other rows or to no row, are set to -inf
+    // whatever was read there. A mask row at another offset inside its line
+    // is read element by element. (Element loads of x measured 2-3 x slower
+    // per row on bf16 rows of 1001 keys.)
+    float xv[E], m[E];
+    F::unpack(ld_stream<NT>(r.x + (int64_t)k0 * BY), xv);
+    if (kind == MASK_ADD && r.mvec) F::unpack(ld_cached(r.m + (int64_t)k0 * BY), m);
+    uint64_t bits = 0;
+    if (kind == MASK_BOOL && r.mvec) bits = ld_bits<E>(r.m + k0);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int k = k0 + e;
       float v2 = kNegInf;
       if (k >= 0 && k < r.kload) {
-        const float xv = F::ld(r.x + (int64_t)k * BY);
-        if (kind == MASK_ADD) v2 = fmaf(xv, scale, F::ld(r.m + (int64_t)k * BY));
-        else if (kind == MASK_BOOL) v2 = r.m[k] ? kNegInf : xv * scale;
-        else v2 = xv * scale;
+        if (kind == MASK_ADD) v2 = fmaf(xv[e], scale, r.mvec ? m[e] : F::ld(r.m + (int64_t)k * BY));
+        else if (kind == MASK_BOOL) v2 = (r.mvec ? bit_set(bits, e) : r.m[k] != 0) ? kNegInf : xv[e] * scale;
+        else v2 = xv[e] * scale;
       }
       s[e] = v2;
     }
+  } else {
+    // None of the vector's keys is read.
+#pragma unroll
+    for (int e = 0; e < E; ++e) s[e] = kNegInf;
   }
 }
 
@@ -613,15 +626,25 @@ SMS_DEV void row_pair(const BwdRow& r, int v, float (&yv)[F::kE], float (&gv)[F:
 #pragma unroll
       for (int e = 0; e < E; ++e) gv[e] = F::ld(r.d + (int64_t)(k0 + e) * BY);
     }
-  } else {
-    // A partial vector (row head or tail, or the key bound inside it), or none
-    // of the vector's keys read: element by element, zeros outside [0, kload).
+  } else if (k0 < r.kload && k0 + E > 0) {
+    // A partial vector: whole 16-byte lines, as in row_scores, and zeros
+    // outside [0, kload) whatever was read there; a dy row at another offset
+    // inside its line element by element.
+    float ya[E], ga[E];
+    F::unpack(ld_stream<NT>(r.y + (int64_t)k0 * BY), ya);
+    if (r.dvec) F::unpack(ld_stream<NT>(r.d + (int64_t)k0 * BY), ga);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int k = k0 + e;
       const bool in = (k >= 0 && k < r.kload);
-      yv[e] = in ? F::ld(r.y + (int64_t)k * BY) : 0.0f;
-      gv[e] = in ? F::ld(r.d + (int64_t)k * BY) : 0.0f;
+      yv[e] = in ? ya[e] : 0.0f;
+      gv[e] = in ? (r.dvec ? ga[e] : F::ld(r.d + (int64_t)k * BY)) : 0.0f;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      yv[e] = 0.0f;
+      gv[e] = 0.0f;
     }
   }
 }
