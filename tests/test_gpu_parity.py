@@ -277,6 +277,53 @@ def test_strided_and_misaligned(dtype, Sk, pad, xoff, yoff, moff):
     compare(decoded(dx), refb, dtype, "strided bwd")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "f64"])
+@pytest.mark.parametrize("Sk,pad,xoff,yoff,moff", [
+    (1000, 0, 1, 1, 0),    # contiguous rows mid-line: NaN before the first, after the last
+    (1000, 0, 1, 0, 0),    # y at another offset
+    (1001, 7, 0, 0, 3),    # NaN in every row's padding, mask at an odd offset
+    (77, 3, 2, 5, 1),
+    (5, 11, 3, 1, 2),      # rows shorter than one vector
+])
+def test_nan_around_rows_is_not_read_into_results(dtype, Sk, pad, xoff, yoff, moff):
+    """Partial 16-byte vectors at a row's ends are loaded as whole aligned
+    lines; the elements of those lines outside the row (other tensors'
+    bytes, padding) must not reach any result even when they are NaN."""
+    say(f"nan-around dtype={dtype} Sk={Sk} pad={pad} xoff={xoff} yoff={yoff} moff={moff}")
+    B, H, Sq = 2, 3, 4
+    td = TORCH_DTYPE[dtype]
+    nan = float("nan")
+    n, tail = B * H * Sq * (Sk + pad), 16
+
+    def framed(off, body):  # body (B,H,Sq,Sk) at element off of a NaN buffer, NaN padding
+        buf = torch.full((off + n + tail,), nan, dtype=td, device=DEV)
+        rows = buf[off:off + n].view(B, H, Sq, Sk + pad)
+        if body is not None:
+            rows[..., :Sk] = body
+        return buf, rows[..., :Sk]
+
+    _, x = framed(xoff, draw_x((B, H, Sq, Sk), dtype, ("normal", 3.0), Sk + 11, DEV))
+    ms = torch.full((moff + B * Sq * Sk + tail,), nan, dtype=td, device=DEV)
+    ms[moff:moff + B * Sq * Sk] = draw_mask((B, 1, Sq, Sk), "b_sq_sk", dtype,
+                                            ("bernoulli_neginf", 0.2), 5, DEV).reshape(-1)
+    mask = ms[moff:moff + B * Sq * Sk].view(B, Sq, Sk)
+    ys, y = framed(yoff, None)
+    fwd(x, mask, 0.5, True, y=y)
+    ref = oracle_fwd(x.contiguous(), mask, "b_sq_sk", 0.5, True)
+    compare(decoded(y), ref, dtype, "nan-around fwd", rowsum=True)
+    _, dy = framed(xoff, draw_x((B, H, Sq, Sk), dtype, ("normal", 1.0), Sk + 12, DEV))
+    dxs, dx = framed(yoff, None)
+    bwd(y, dy, 0.5, True, dx=dx)
+    refb = oracle.backward(to_np(y), to_np(dy), dtype, 0.5)
+    compare(decoded(dx), refb, dtype, "nan-around bwd")
+    # Nothing outside the rows was written: every byte there is still NaN.
+    for buf, rows in ((ys, y), (dxs, dx)):
+        inside = torch.zeros(buf.shape, dtype=torch.bool, device=DEV)
+        off = rows.storage_offset()
+        inside[off:off + n].view(B, H, Sq, Sk + pad)[..., :Sk] = True
+        assert torch.isnan(buf[~inside]).all()
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_permuted_strides_and_in_place(dtype):
     say(f"permuted/in-place dtype={dtype}")
