@@ -553,6 +553,113 @@ SMS_DEV void row_scores(const FwdRow& r, int kind, int v, float scale, float (&s
   constexpr int E = F::kE;
   constexpr int BY = F::kBytes;
   const int k0 = v * E - r.ax;
+  if (k0 < r.kload && k0 + E > 0) {
+    // Every vector holding a key of [0, kload) loads its 16-byte line (x + k0*BY
+    // sits on one: k0 + ax is a multiple of E) before the whole / partial
+    // branch, so that the wavefront issues one load for both kinds of lane
+    // instead of one per branch, each waited for in turn. A partial vector's
+    // line (the row's head or tail, or the key bound inside it) holds at least
+    // one key of the row, so it lies in a page the row occupies; its keys
+    // outside [0, kload), which belong to other rows or to no row, are set to
+    // -inf whatever was read there. A mask row at another offset inside its
+    // line is read element by element. Measured on MI355X, bf16
+    // [16,16,1000,1001] with a [1000,1001] additive mask (128 lanes per row):
+    // forward 294 -> 229 us and backward 304 -> 252 us against a load in
+    // each branch (element loads of x had been 2-3 x slower still).
+    float xv[E], m[E];
+    uint64_t bits = 0;
+    F::unpack(ld_stream<NT>(r.x + (int64_t)k0 * BY), xv);
+    if (kind == MASK_ADD && r.mvec) F::unpack(ld_cached(r.m + (int64_t)k0 * BY), m);
+    if (kind == MASK_BOOL && r.mvec) bits = ld_bits<E>(r.m + k0);
+    if (k0 >= 0 && k0 + E <= r.kload) {
+      if (kind == MASK_ADD) {
+        if (!r.mvec) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) m[e] = F::ld(r.m + (int64_t)(k0 + e) * BY);
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[e] = fmaf(xv[e], scale, m[e]);
+      } else if (kind == MASK_BOOL) {
+        if (!r.mvec) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) bits |= (uint64_t)(uint8_t)r.m[k0 + e] << (8 * e);
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[e] = bit_set(bits, e) ? kNegInf : xv[e] * scale;
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[e] = xv[e] * scale;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int k = k0 + e;
+        float v2 = kNegInf;
+        if (k >= 0 && k < r.kload) {
+          if (kind == MASK_ADD) v2 = fmaf(xv[e], scale, r.mvec ? m[e] : F::ld(r.m + (int64_t)k * BY));
+          else if (kind == MASK_BOOL) v2 = (r.mvec ? bit_set(bits, e) : r.m[k] != 0) ? kNegInf : xv[e] * scale;
+          else v2 = xv[e] * scale;
+        }
+        s[e] = v2;
+      }
+    }
+  } else {
+    // None of the vector's keys is read.
+#pragma unroll
+    for (int e = 0; e < E; ++e) s[e] = kNegInf;
+  }
+}
+
+// y and dy of vector v for keys [0, kload), zeros elsewhere. Any alignment.
+template <class F, bool NT = kNtLoads>
+SMS_DEV void row_pair(const BwdRow& r, int v, float (&yv)[F::kE], float (&gv)[F::kE]) {
+  constexpr int E = F::kE;
+  constexpr int BY = F::kBytes;
+  const int k0 = v * E - r.ay;
+  if (k0 < r.kload && k0 + E > 0) {
+    // One load of each 16-byte line for whole and partial vectors alike, as in
+    // row_scores; a partial vector's keys outside [0, kload) read as zeros
+    // whatever the line held there, and a dy row at another offset inside its
+    // line is read element by element.
+    float ya[E], ga[E];
+    F::unpack(ld_stream<NT>(r.y + (int64_t)k0 * BY), ya);
+    if (r.dvec) F::unpack(ld_stream<NT>(r.d + (int64_t)k0 * BY), ga);
+    if (k0 >= 0 && k0 + E <= r.kload) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        yv[e] = ya[e];
+        gv[e] = r.dvec ? ga[e] : F::ld(r.d + (int64_t)(k0 + e) * BY);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int k = k0 + e;
+        const bool in = (k >= 0 && k < r.kload);
+        yv[e] = in ? ya[e] : 0.0f;
+        gv[e] = in ? (r.dvec ? ga[e] : F::ld(r.d + (int64_t)k * BY)) : 0.0f;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      yv[e] = 0.0f;
+      gv[e] = 0.0f;
+    }
+  }
+}
+
+// The same two reads with each vector's loads inside its whole / partial
+// branch, for the streaming and split kernels: there the loads of a lane's
+// several vectors per chunk are already in flight together, and the shared
+// load measured no better on MI355X (us, branch loads -> shared load; one
+// 1024-lane workgroup per row): fp16 rows of 65536 keys forward 426 -> 440,
+// backward 725 -> 741; fp32 rows of 20000 keys 395 -> 392 and 652 -> 656;
+// fp16 rows of 40001 keys at every offset 489 -> 483 and 698 -> 664.
+template <class F, bool NT = kNtLoads>
+SMS_DEV void row_scores_branch_loads(const FwdRow& r, int kind, int v, float scale, float (&s)[F::kE]) {
+  constexpr int E = F::kE;
+  constexpr int BY = F::kBytes;
+  const int k0 = v * E - r.ax;
   if (k0 >= 0 && k0 + E <= r.kload) {
     // x + k0*BY sits on a 16-byte line: k0 + ax is a multiple of E.
     F::unpack(ld_stream<NT>(r.x + (int64_t)k0 * BY), s);
@@ -612,9 +719,8 @@ SMS_DEV void row_scores(const FwdRow& r, int kind, int v, float scale, float (&s
   }
 }
 
-// y and dy of vector v for keys [0, kload), zeros elsewhere. Any alignment.
 template <class F, bool NT = kNtLoads>
-SMS_DEV void row_pair(const BwdRow& r, int v, float (&yv)[F::kE], float (&gv)[F::kE]) {
+SMS_DEV void row_pair_branch_loads(const BwdRow& r, int v, float (&yv)[F::kE], float (&gv)[F::kE]) {
   constexpr int E = F::kE;
   constexpr int BY = F::kBytes;
   const int k0 = v * E - r.ay;
@@ -1182,7 +1288,7 @@ SMS_DEV void online_ml(const FwdRow& r, int kind, float scale, int v0, int v1, f
     for (int j = 0; j < CV; ++j) {
       const int v = base + j * TPR + lane;
       if (v < v1) {
-        row_scores<F, false>(r, kind, v, scale, s[j]);
+        row_scores_branch_loads<F, false>(r, kind, v, scale, s[j]);
       } else {
 #pragma unroll
         for (int e = 0; e < E; ++e) s[j][e] = kNegInf;
@@ -1223,7 +1329,7 @@ SMS_DEV void write_probs(const FwdRow& r, int kind, float scale, float mref, flo
 #pragma unroll
           for (int e = 0; e < E; ++e) o[e] = 0.0f;
         } else {
-          row_scores<F>(r, kind, v, scale, o);
+          row_scores_branch_loads<F>(r, kind, v, scale, o);
 #pragma unroll
           for (int e = 0; e < E; ++e) o[e] = exp_biased(o[e], mref) * inv;
         }
@@ -1246,7 +1352,7 @@ SMS_DEV double dot_part(const BwdRow& r, int v0, int v1) {
       const int v = base + j * TPR + lane;
       if (v < v1) {
         float yv[E], gv[E];
-        row_pair<F, false>(r, v, yv, gv);
+        row_pair_branch_loads<F, false>(r, v, yv, gv);
 #pragma unroll
         for (int e = 0; e < E; ++e) acc += F::prod(yv[e], gv[e]);
       }
@@ -1274,7 +1380,7 @@ SMS_DEV void write_grads(const BwdRow& r, float scale, double dot, int v0, int v
           for (int e = 0; e < E; ++e) o[e] = 0.0f;
         } else {
           float yv[E], gv[E];
-          row_pair<F>(r, v, yv, gv);
+          row_pair_branch_loads<F>(r, v, yv, gv);
 #pragma unroll
           for (int e = 0; e < E; ++e) o[e] = (yv[e] * scale) * ((gv[e] - dot_hi) - dot_lo);
         }
